@@ -1,0 +1,133 @@
+"""Block pool, per-sequence block tables and slot mapping (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Follows the ARTICLE, §2.2 (block manager): the pool starts with every block
+id free, in the order ``0 .. num_blocks-1`` unless another order is given;
+``allocate(n)`` takes the first ``n`` ids of the free list and fails when
+fewer than ``n`` are free (the comparison operator is lost in the printed
+text; "fewer than" is the only reading under which the allocation that
+follows can succeed); ``free(ids)`` appends the ids to the back of the list in
+the order given.
+
+The LESSON ("The Concept: PagedAttention as a virtual memory system") fixes
+the rest: a sequence's table maps logical token position p to a physical
+block; the token lives in block ``table[p // block_size]`` at offset
+``p % block_size``; when a sequence grows past its blocks, one more block is
+added; when it finishes, its blocks go back to the pool.
+
+Readings taken where the texts are silent or contradict themselves:
+* the ARTICLE raises an error on shortage but its scheduler (§3.1) tests the
+  result for emptiness: here every allocation is all-or-nothing and a failed
+  call leaves the pool and the table untouched (status ``NO_BLOCKS``);
+* the ARTICLE's ``get_block_table`` reads a map that is never defined: here
+  the pool keeps one table per sequence id;
+* a sequence is created with ``ceil(num_tokens / block_size)`` blocks (the
+  ARTICLE's scheduler, §3.1, allocates that many for a prompt at admission);
+* release returns the table to the back of the free list in table order.
+"""
+from __future__ import annotations
+
+from collections import deque
+
+OK = 0
+ERR_INVALID = -1
+ERR_NO_BLOCKS = -2
+ERR_UNKNOWN_SEQ = -3
+ERR_EXISTS = -4
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+class BlockPool:
+    def __init__(self, num_blocks: int, block_size: int, initial_free_order=None):
+        if num_blocks < 0 or block_size <= 0:
+            raise ValueError("bad pool geometry")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        if initial_free_order is None:
+            order = list(range(self.num_blocks))
+        else:
+            order = [int(b) for b in initial_free_order]
+            if sorted(order) != list(range(self.num_blocks)):
+                raise ValueError("initial free order must be a permutation of the pool")
+        self.free = deque(order)
+        self.tables: dict[int, list[int]] = {}
+        self.lengths: dict[int, int] = {}
+
+    # -- ARTICLE §2.2: allocate / free ---------------------------------------
+    def _take(self, n: int):
+        if len(self.free) < n:
+            return None
+        return [self.free.popleft() for _ in range(n)]
+
+    def _give_back(self, ids):
+        self.free.extend(ids)
+
+    # -- sequence-level verbs -------------------------------------------------
+    def num_free(self) -> int:
+        return len(self.free)
+
+    def seq_create(self, seq: int, num_tokens: int) -> int:
+        if num_tokens < 0:
+            return ERR_INVALID
+        if seq in self.tables:
+            return ERR_EXISTS
+        ids = self._take(ceil_div(num_tokens, self.block_size))
+        if ids is None:
+            return ERR_NO_BLOCKS
+        self.tables[seq] = ids
+        self.lengths[seq] = num_tokens
+        return OK
+
+    def seq_append(self, seq: int, n_new: int):
+        """Grow a sequence by ``n_new`` tokens, taking one block per block
+        boundary crossed.  Returns (status, slots of the new tokens)."""
+        if n_new < 0:
+            return ERR_INVALID, []
+        if seq not in self.tables:
+            return ERR_UNKNOWN_SEQ, []
+        old = self.lengths[seq]
+        need = ceil_div(old + n_new, self.block_size) - len(self.tables[seq])
+        if need > 0:
+            ids = self._take(need)
+            if ids is None:
+                return ERR_NO_BLOCKS, []
+            self.tables[seq].extend(ids)
+        self.lengths[seq] = old + n_new
+        return OK, self.slots(seq, old, n_new)
+
+    def seq_release(self, seq: int) -> int:
+        if seq not in self.tables:
+            return ERR_UNKNOWN_SEQ
+        self._give_back(self.tables.pop(seq))
+        del self.lengths[seq]
+        return OK
+
+    def block_table(self, seq: int) -> list[int]:
+        return list(self.tables[seq])
+
+    def slots(self, seq: int, start: int, n: int) -> list[int]:
+        """Flat slot index ``block * block_size + offset`` of positions
+        ``start .. start+n-1``."""
+        t = self.tables[seq]
+        bs = self.block_size
+        return [t[p // bs] * bs + p % bs for p in range(start, start + n)]
+
+    def pack(self, seqs, max_blocks: int):
+        """Dense ``[len(seqs), max_blocks]`` table padded with -1, and the
+        context length of each sequence."""
+        tables = []
+        lens = []
+        for s in seqs:
+            t = self.tables[s]
+            if len(t) > max_blocks:
+                raise ValueError("table wider than max_blocks")
+            tables.append(t + [-1] * (max_blocks - len(t)))
+            lens.append(self.lengths[s])
+        return tables, lens
+
+    def free_list(self) -> list[int]:
+        return list(self.free)

@@ -1,0 +1,159 @@
+"""Iteration-level continuous batching with chunked prefill (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Policy, from the two texts:
+* LESSON, "Continuous batching at the iteration level" and "What the
+  scheduler looks like": the scheduler runs once per iteration; sequences
+  that reached their end leave RUNNING and release their blocks; waiting
+  sequences are admitted in arrival order while the head of the queue fits
+  in the free blocks; every RUNNING sequence then contributes either a
+  prefill slice or exactly one decode token to one batch.
+* LESSON, "Chunked prefill": prefill is cut into fixed-size slices (512
+  tokens by default), each scheduled as a unit, interleaved with decodes.
+* ARTICLE §3.1 (continuous batching): running sequences that need one more
+  block take it first; if none is free the sequence is preempted -- its
+  blocks are freed, its computed-token count reset to zero and it goes to the
+  back of the waiting queue; admission is capped by a maximum number of
+  running sequences and allocates ``ceil(prompt_len / block_size)`` blocks at
+  once; a sequence that does not fit goes back to the front of the queue and
+  admission stops.
+* ARTICLE §3.2: a preempted sequence is recovered by recomputation: it
+  prefills again every token it knows (prompt plus the output produced so
+  far) before decoding resumes.
+
+Readings taken where the texts leave a step open:
+* order inside one iteration: (1) arrivals join the queue, (2) finished
+  sequences are released, (3) decode-phase sequences grow by one token each,
+  in RUNNING order, preempting on shortage, (4) admission, (5) prefill slices
+  are handed out in RUNNING order until the per-iteration prefill budget is
+  spent;
+* the prefill slice that completes a sequence's known tokens produces its
+  next output token; the sequence decodes from the next iteration on; a
+  decode step appends the newest output token (its K/V written, context
+  grows by one) and produces the next;
+* a sequence is finished once it has produced its target number of output
+  tokens; it is released at the start of the following iteration.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+from .allocator import BlockPool, OK, ERR_NO_BLOCKS, ceil_div
+
+
+@dataclass
+class Seq:
+    sid: int
+    prompt_len: int
+    target: int               # output tokens to produce (>= 1)
+    known: int = 0            # tokens to prefill on (re)admission
+    prefilled: int = 0        # of ``known``, tokens whose K/V are cached
+    decoded: int = 0          # output tokens produced so far
+    in_prefill: bool = True
+    preemptions: int = 0
+
+    def cached_len(self) -> int:
+        return self.prefilled if self.in_prefill else self.prompt_len + self.decoded - 1
+
+
+@dataclass
+class Batch:
+    decode: list = field(default_factory=list)    # (sid, position, slot)
+    prefill: list = field(default_factory=list)   # (sid, start, n, slots)
+    finished: list = field(default_factory=list)
+    admitted: list = field(default_factory=list)
+    preempted: list = field(default_factory=list)
+
+
+class Scheduler:
+    def __init__(self, pool: BlockPool, max_running: int = 256, prefill_budget: int = 512):
+        self.pool = pool
+        self.max_running = max_running
+        self.prefill_budget = prefill_budget
+        self.waiting: list[Seq] = []
+        self.running: list[Seq] = []
+        self.done: list[Seq] = []
+
+    def add(self, sid: int, prompt_len: int, target: int):
+        if prompt_len < 1 or target < 1:
+            raise ValueError("prompt and target must be positive")
+        self.waiting.append(Seq(sid, prompt_len, target, known=prompt_len))
+
+    def _preempt(self, s: Seq):
+        self.pool.seq_release(s.sid)
+        s.preemptions += 1
+        s.in_prefill = True
+        s.prefilled = 0
+        s.known = s.prompt_len + s.decoded
+        self.waiting.append(s)
+
+    def step(self) -> Batch:
+        out = Batch()
+        bs = self.pool.block_size
+        # (2) release finished sequences
+        keep = []
+        for s in self.running:
+            if not s.in_prefill and s.decoded >= s.target:
+                self.pool.seq_release(s.sid)
+                out.finished.append(s.sid)
+                self.done.append(s)
+            else:
+                keep.append(s)
+        self.running = keep
+        # (3) one decode token per decode-phase sequence, preempting on shortage
+        keep = []
+        for s in self.running:
+            if s.in_prefill:
+                keep.append(s)
+                continue
+            st, slots = self.pool.seq_append(s.sid, 1)
+            if st == ERR_NO_BLOCKS:
+                self._preempt(s)
+                out.preempted.append(s.sid)
+                continue
+            assert st == OK
+            pos = s.prompt_len + s.decoded - 1
+            out.decode.append((s.sid, pos, slots[0]))
+            s.decoded += 1
+            keep.append(s)
+        self.running = keep
+        # (4) admission, head of line first
+        while self.waiting and len(self.running) < self.max_running:
+            s = self.waiting[0]
+            if self.pool.num_free() < ceil_div(s.known, bs):
+                break
+            st = self.pool.seq_create(s.sid, s.known)
+            assert st == OK
+            self.waiting.pop(0)
+            self.running.append(s)
+            out.admitted.append(s.sid)
+        # (5) prefill slices within the budget
+        budget = self.prefill_budget
+        for s in self.running:
+            if not s.in_prefill or budget == 0:
+                continue
+            n = min(s.known - s.prefilled, budget)
+            if n <= 0:
+                continue
+            slots = self.pool.slots(s.sid, s.prefilled, n)
+            out.prefill.append((s.sid, s.prefilled, n, slots))
+            s.prefilled += n
+            budget -= n
+            if s.prefilled == s.known:
+                s.in_prefill = False
+                s.decoded += 1
+        return out
+
+    # -- accounting -------------------------------------------------------
+    def held(self):
+        """(blocks held, tokens assigned, reserved-unwritten prompt slots)."""
+        blocks = 0
+        assigned = 0
+        unwritten = 0
+        for s in self.running:
+            blocks += len(self.pool.tables[s.sid])
+            assigned += self.pool.lengths[s.sid]
+            if s.in_prefill:
+                unwritten += s.known - s.prefilled
+        return blocks, assigned, unwritten

@@ -1,0 +1,74 @@
+"""Pins of the oracle's continuous-batching scheduler: two hand-worked traces
+and the invariants the texts state, on seeded random traces."""
+import json
+import os
+
+import numpy as np
+
+from oracle.allocator import BlockPool
+from oracle.scheduler import Scheduler
+from workloads import trace as make_trace
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _run_golden(tr):
+    pool = BlockPool(tr["num_blocks"], tr["block_size"])
+    sch = Scheduler(pool, tr["max_running"], tr["prefill_budget"])
+    for it, want in enumerate(tr["iterations"]):
+        for sid, p, o in tr["arrivals"].get(str(it), []):
+            sch.add(sid, p, o)
+        b = sch.step()
+        got = {"finished": b.finished, "admitted": b.admitted, "preempted": b.preempted,
+               "decode": [list(x) for x in b.decode],
+               "prefill": [[s, a, n, list(sl)] for s, a, n, sl in b.prefill],
+               "free": pool.free_list()}
+        assert got == want, (tr["name"], it, got, want)
+
+
+def test_hand_worked_traces():
+    g = json.load(open(os.path.join(GOLDEN, "scheduler_traces.json")))
+    for tr in g["traces"]:
+        _run_golden(tr)
+
+
+def _check_invariants(num_blocks, iters, lam, budget, max_running, seed):
+    w = make_trace(seed=seed, iters=iters, lam=lam, prompt_median=60, prompt_sigma=1.0,
+                   prompt_cap=400, out_mean=20, num_blocks=num_blocks)
+    pool = BlockPool(num_blocks, 16)
+    sch = Scheduler(pool, max_running, budget)
+    produced = {}
+    targets = {}
+    for it in range(iters):
+        for sid, p, o in w.arrivals[it]:
+            sch.add(sid, p, o)
+            targets[sid] = o
+        b = sch.step()
+        assert sum(n for _, _, n, _ in b.prefill) <= budget
+        assert len(sch.running) <= max_running
+        ids = [s for s, _, _ in b.decode] + [s for s, _, _, _ in b.prefill]
+        assert len(ids) == len(set(ids))          # one unit per sequence per iteration
+        for s, pos, slot in b.decode:
+            t = pool.block_table(s)
+            assert slot == t[pos // 16] * 16 + pos % 16
+            assert pool.lengths[s] == pos + 1
+        held = [x for t in pool.tables.values() for x in t]
+        assert sorted(held + pool.free_list()) == list(range(num_blocks))
+        for s in sch.running:
+            assert pool.lengths[s.sid] == (s.known if s.in_prefill else s.cached_len())
+        for s in sch.done:
+            produced[s.sid] = s.decoded
+    for sid, n in produced.items():
+        assert n == targets[sid]
+    return sch
+
+
+def test_invariants_roomy_pool():
+    sch = _check_invariants(num_blocks=4000, iters=300, lam=0.3, budget=64, max_running=16, seed=21)
+    assert len(sch.done) > 20
+
+
+def test_invariants_tiny_pool_forces_preemption():
+    sch = _check_invariants(num_blocks=40, iters=400, lam=0.3, budget=64, max_running=16, seed=22)
+    assert sum(s.preemptions for s in sch.done + sch.running + sch.waiting) > 0
+    assert len(sch.done) > 5
