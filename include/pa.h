@@ -1,0 +1,239 @@
+/*
+ * pa.h -- C ABI of libpa, a paged-attention library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Sources of the operations (cited by title and section):
+ *   LESSON   "vLLM Serving Internals: PagedAttention, Continuous Batching,
+ *            Chunked Prefill" (AI Engineering from Scratch, Phase 17 Lesson
+ *            04), sections "The Concept: PagedAttention as a virtual memory
+ *            system", "Continuous batching at the iteration level",
+ *            "Chunked prefill", "What the scheduler looks like".
+ *   ARTICLE  "vLLM inference engine architecture: the PagedAttention
+ *            mechanism and high-throughput inference" (lpnh.cn), sections
+ *            2.2 (block manager), 2.3 (PagedAttention kernel interface),
+ *            3.1 (continuous batching scheduler).
+ *
+ * General conventions
+ *   - Every call returns a pa_status; PA_OK is 0, errors are negative.  On
+ *     error nothing is launched and no state changes; pa_last_error() gives a
+ *     thread-local description of the most recent error of the calling
+ *     thread.
+ *   - Host pointers are marked [host], device pointers [device].  Device
+ *     buffers and streams belong to the caller; the library never allocates
+ *     or frees device memory.  The only library-owned object is the host
+ *     block pool (pa_pool), created and destroyed through this API.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Kernel calls are asynchronous on that stream: they return after the
+ *     launch, and errors of the launch itself are reported as
+ *     PA_ERR_DEVICE.
+ *   - Element types: PA_F32 (IEEE binary32), PA_BF16 (bfloat16, stored as
+ *     uint16), PA_FP8_E4M3 (OCP e4m3fn: bias 7, no infinities, max 448,
+ *     stored as uint8; values are code * per-tensor fp32 scale).
+ *   - The pool allocator is not thread-safe: one scheduler thread drives it,
+ *     once per iteration (LESSON, "Continuous batching at the iteration
+ *     level").
+ *
+ * KV cache layout (one layer; block size bs, KV heads H_kv, head dim D):
+ *     K cache  [num_blocks][H_kv][bs][D]   a token's key is one row
+ *     V cache  [num_blocks][H_kv][D][bs]   a token's value is one column
+ * Token position p of a sequence lives in physical block table[p / bs] at
+ * offset p % bs (LESSON, "PagedAttention as a virtual memory system"); its
+ * flat slot is table[p / bs] * bs + p % bs.  The ARTICLE (2.2) shapes both
+ * pools [num_blocks, block_size, num_heads, head_dim]; the axis order inside
+ * a pool is this library's choice (each (block, head) pair is one contiguous
+ * tile, and values are stored token-minor so that the P*V contraction reads
+ * contiguous runs of tokens).
+ *
+ * Supported envelope of the attention kernels (else PA_ERR_INVALID):
+ *   bs == 16; D in {64, 128}; H_q % H_kv == 0; (q, cache, out) element types
+ *   (f32, f32, f32), (bf16, bf16, bf16) or (bf16, fp8, bf16).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* bad argument, shape, dtype or envelope */
+  PA_ERR_NO_BLOCKS = -2,   /* not enough free blocks; state unchanged */
+  PA_ERR_UNKNOWN_SEQ = -3, /* sequence id not in the pool */
+  PA_ERR_EXISTS = -4,      /* sequence id already in the pool */
+  PA_ERR_DEVICE = -5,      /* HIP runtime error (launch, device query) */
+  PA_ERR_WORKSPACE = -6    /* workspace missing or smaller than required */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
+
+typedef struct pa_pool pa_pool; /* opaque host object */
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t pa_version(void);
+
+/* Text of the last error of the calling thread ("" if none).  The pointer
+ * stays valid until the thread's next failing call. */
+const char* pa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Host block pool -- ARTICLE 2.2 (block manager) and LESSON "PagedAttention
+ * as a virtual memory system".
+ *
+ * The free list is FIFO: allocation takes ids from its front, release
+ * appends a sequence's table to its back in table order.  Every allocation
+ * is all-or-nothing: PA_ERR_NO_BLOCKS leaves the pool bit-for-bit unchanged.
+ * ---------------------------------------------------------------------- */
+
+/* Create a pool of num_blocks blocks of block_size tokens.
+ * initial_free_order [host, num_blocks, may be NULL]: the initial free-list
+ * order, a permutation of 0..num_blocks-1 (NULL = 0,1,..,num_blocks-1, as in
+ * the ARTICLE).  The array is copied.  *out receives the pool. */
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size,
+                         const int32_t* initial_free_order, pa_pool** out);
+
+/* Destroy a pool (NULL is accepted). */
+void pa_pool_destroy(pa_pool* pool);
+
+/* Number of free blocks (the LESSON's have_free_blocks_for test compares a
+ * request's block count against this); -1 for a NULL pool. */
+int32_t pa_pool_num_free(const pa_pool* pool);
+
+/* Number of live sequences; -1 for a NULL pool. */
+int32_t pa_pool_num_seqs(const pa_pool* pool);
+
+/* Copy the free list, front first, into out [host, cap].  *n receives the
+ * number of free blocks; PA_ERR_INVALID if cap is smaller. */
+pa_status pa_pool_free_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+
+/* Register sequence `seq` holding num_tokens (>= 0) tokens and give it
+ * ceil(num_tokens / block_size) blocks (the LESSON's
+ * allocate_initial_blocks; ARTICLE 3.1 allocates a prompt's blocks at
+ * admission). */
+pa_status pa_seq_create(pa_pool* pool, int64_t seq, int32_t num_tokens);
+
+/* Grow `seq` by n_new (>= 0) tokens, taking one more block each time a block
+ * boundary is crossed (LESSON: "when a sequence grows past its blocks, one
+ * more block is added").  slots_out [host, n_new, may be NULL] receives the
+ * flat slots of the new positions. */
+pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_new, int32_t* slots_out);
+
+/* Flat slots of positions start .. start+n-1 of `seq` (all must be < the
+ * sequence's length) into slots_out [host, n]. */
+pa_status pa_seq_slots(const pa_pool* pool, int64_t seq, int32_t start, int32_t n,
+                       int32_t* slots_out);
+
+/* Release `seq`: its blocks go to the back of the free list in table order
+ * (ARTICLE 2.2 free; LESSON release_blocks on finish). */
+pa_status pa_seq_release(pa_pool* pool, int64_t seq);
+
+/* Current token count of `seq` into *len. */
+pa_status pa_seq_length(const pa_pool* pool, int64_t seq, int32_t* len);
+
+/* Copy the block table of `seq` (ARTICLE 2.2 get_block_table) into out
+ * [host, cap]; *n receives its length; PA_ERR_INVALID if cap is smaller. */
+pa_status pa_seq_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int32_t cap,
+                             int32_t* n);
+
+/* Pack a batch: block_tables [host, n_seqs * max_blocks] row i = table of
+ * seqs[i] padded with -1; context_lens [host, n_seqs] = their lengths (the
+ * ARTICLE 2.3 block_tables and context_lens arguments).  PA_ERR_INVALID if
+ * a table is longer than max_blocks. */
+pa_status pa_pack_batch(const pa_pool* pool, const int64_t* seqs, int32_t n_seqs,
+                        int32_t max_blocks, int32_t* block_tables, int32_t* context_lens);
+
+/* Host check of a packed batch: every entry of the first
+ * ceil(context_lens[i] / block_size) columns of row i lies in
+ * [0, num_blocks), and context_lens[i] <= max_blocks * block_size.  The
+ * kernels do not trust the tables blindly (an out-of-range entry is read as
+ * block 0 and an overlong context is clipped, so no access leaves the
+ * buffers), but the results of such a row are meaningless; call this to
+ * reject them. */
+pa_status pa_validate_tables(const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t n_seqs, int32_t max_blocks, int32_t block_size,
+                             int32_t num_blocks);
+
+/* ------------------------------------------------------------------------
+ * Cache write -- the K/V of token position p go to block table[p / bs],
+ * offset p % bs (LESSON, "PagedAttention as a virtual memory system").
+ *
+ * k_new, v_new [device, n * H_kv * D, dtype new_dt, contiguous [n][H_kv][D]]
+ * slot_mapping [device, n int32]: flat slot of each token; a slot < 0 skips
+ *   the token; slots >= num_blocks * bs are also skipped (never written).
+ *   Slots of one call must be distinct.
+ * k_cache, v_cache [device]: the pools in the layout above, type cache_dt.
+ * new_dt == cache_dt stores the bits unchanged.  new_dt == PA_BF16 with
+ * cache_dt == PA_FP8_E4M3 stores code = e4m3(x * (1/scale)) with
+ * 1/scale computed once in fp32 on the host, one fp32 multiply, round to
+ * nearest even, magnitudes above 448 saturated to 448, NaN kept as NaN.
+ * k_scale / v_scale are ignored for other caches.
+ * ---------------------------------------------------------------------- */
+pa_status pa_cache_write(void* stream, const void* k_new, const void* v_new, pa_dtype new_dt,
+                         const int32_t* slot_mapping, int32_t n, void* k_cache, void* v_cache,
+                         pa_dtype cache_dt, int32_t num_blocks, int32_t H_kv, int32_t D, int32_t bs,
+                         float k_scale, float v_scale);
+
+/* ------------------------------------------------------------------------
+ * Decode attention -- ARTICLE 2.3: one query token per sequence attends the
+ * sequence's K/V found through block_tables up to context_lens
+ * (out = softmax(sm_scale * q K^T) V, per query head; query head h reads KV
+ * head h / (H_q / H_kv)).  context_lens counts the query's own token, whose
+ * K/V must already be written.
+ *
+ * out [device, S*H_q*D, out_dt]   q [device, S*H_q*D, q_dt], both [S][H_q][D]
+ * block_tables [device, S * max_blocks int32], context_lens [device, S int32],
+ *   each context length in [1, max_context_len].
+ * max_context_len: host-side upper bound of context_lens (sizes the split
+ *   grid; no device-to-host read is needed).
+ * sm_scale: softmax scale (normally 1/sqrt(D)).  k_scale, v_scale: fp8
+ *   per-tensor scales (ignored otherwise).
+ * ws [device, ws_bytes]: scratch for split partials, at least
+ *   pa_decode_workspace_bytes(...) bytes (0 bytes may be needed, then ws
+ *   may be NULL); else PA_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+size_t pa_decode_workspace_bytes(int32_t S, int32_t H_q, int32_t H_kv, int32_t D,
+                                 int32_t max_context_len);
+
+pa_status pa_decode(void* stream, void* out, pa_dtype out_dt, const void* q, pa_dtype q_dt,
+                    const void* k_cache, const void* v_cache, pa_dtype cache_dt,
+                    const int32_t* block_tables, int32_t max_blocks, int32_t num_blocks,
+                    const int32_t* context_lens, int32_t S, int32_t H_q, int32_t H_kv, int32_t D,
+                    int32_t bs, int32_t max_context_len, float sm_scale, float k_scale,
+                    float v_scale, void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
+ * Chunked-prefill attention -- LESSON "Chunked prefill": a long prompt is
+ * processed as fixed-size slices (512 tokens by default), each attending
+ * causally to everything before it.  Slice c holds the queries
+ * q[cu_q_lens[c] .. cu_q_lens[c+1]) at absolute positions
+ * start_pos[c] + i; query i sees positions 0 .. start_pos[c] + i inclusive.
+ * The K/V of every one of those positions (the slice's own included) must
+ * already be in the cache, reached through row c of block_tables.
+ *
+ * out, q [device, total_q * H_q * D], layout [total_q][H_q][D]
+ * cu_q_lens [device, n_chunks + 1 int32], cu_q_lens[0] == 0, nondecreasing
+ * start_pos [device, n_chunks int32], >= 0
+ * block_tables [device, n_chunks * max_blocks int32]
+ * max_q_len: host-side bound of the slice lengths; max_context_len: bound
+ *   of start_pos[c] + q_len(c).
+ * ws as for pa_decode, sized by pa_prefill_workspace_bytes.
+ * ---------------------------------------------------------------------- */
+size_t pa_prefill_workspace_bytes(int32_t n_chunks, int32_t max_q_len, int32_t H_q,
+                                  int32_t H_kv, int32_t D, int32_t max_context_len);
+
+pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, const void* q,
+                           pa_dtype q_dt, const int32_t* cu_q_lens, const int32_t* start_pos,
+                           const void* k_cache, const void* v_cache, pa_dtype cache_dt,
+                           const int32_t* block_tables, int32_t max_blocks, int32_t num_blocks,
+                           int32_t n_chunks, int32_t H_q, int32_t H_kv, int32_t D, int32_t bs,
+                           int32_t max_q_len, int32_t max_context_len, float sm_scale,
+                           float k_scale, float v_scale, void* ws, size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,276 @@
+"""ctypes binding of libpa (include/pa.h), same names as the C ABI.
+
+Argument marshalling only: every step runs in the library (host allocator in
+C++, attention and cache writes in HIP kernels).  Device buffers are torch
+tensors on a ROCm device (``tensor.data_ptr()``); streams are torch streams
+(``stream.cuda_stream``) or raw hipStream_t integers.  Importing this module
+fails loudly when libpa.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libpa.so is not built ({LIB_PATH}); run `python -m paged_kv_cache_host_amd.build`")
+_lib = C.CDLL(LIB_PATH)
+
+PA_OK = 0
+PA_ERR_INVALID = -1
+PA_ERR_NO_BLOCKS = -2
+PA_ERR_UNKNOWN_SEQ = -3
+PA_ERR_EXISTS = -4
+PA_ERR_DEVICE = -5
+PA_ERR_WORKSPACE = -6
+
+PA_F32 = 0
+PA_BF16 = 1
+PA_FP8_E4M3 = 2
+
+_i32p = C.POINTER(C.c_int32)
+_i64p = C.POINTER(C.c_int64)
+_vp = C.c_void_p
+_i32 = C.c_int32
+_i64 = C.c_int64
+_f32 = C.c_float
+_sz = C.c_size_t
+
+_SIGS = {
+    "pa_version": (_i32, []),
+    "pa_last_error": (C.c_char_p, []),
+    "pa_pool_create": (_i32, [_i32, _i32, _i32p, C.POINTER(_vp)]),
+    "pa_pool_destroy": (None, [_vp]),
+    "pa_pool_num_free": (_i32, [_vp]),
+    "pa_pool_num_seqs": (_i32, [_vp]),
+    "pa_pool_free_list": (_i32, [_vp, _i32p, _i32, _i32p]),
+    "pa_seq_create": (_i32, [_vp, _i64, _i32]),
+    "pa_seq_append": (_i32, [_vp, _i64, _i32, _i32p]),
+    "pa_seq_slots": (_i32, [_vp, _i64, _i32, _i32, _i32p]),
+    "pa_seq_release": (_i32, [_vp, _i64]),
+    "pa_seq_length": (_i32, [_vp, _i64, _i32p]),
+    "pa_seq_block_table": (_i32, [_vp, _i64, _i32p, _i32, _i32p]),
+    "pa_pack_batch": (_i32, [_vp, _i64p, _i32, _i32, _i32p, _i32p]),
+    "pa_validate_tables": (_i32, [_i32p, _i32p, _i32, _i32, _i32, _i32]),
+    "pa_cache_write": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                              _i32, _f32, _f32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _i32,
+                         _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32, _vp, _sz]),
+    "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_prefill_chunk": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32,
+                                _vp, _sz]),
+}
+
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libpa status {status}: {msg}")
+        self.status = status
+
+
+def pa_version() -> int:
+    return _lib.pa_version()
+
+
+def pa_last_error() -> str:
+    return _lib.pa_last_error().decode()
+
+
+def check(status: int) -> int:
+    """Raise PaError for a non-OK status, else return it."""
+    if status != PA_OK:
+        raise PaError(status, pa_last_error())
+    return status
+
+
+def _i32_array(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr_i32(a: np.ndarray):
+    return a.ctypes.data_as(_i32p)
+
+
+# ---------------------------------------------------------------- pool -----
+
+def pa_pool_create(num_blocks: int, block_size: int = 16, initial_free_order=None):
+    """Returns (status, pool handle or None)."""
+    out = _vp()
+    order = None if initial_free_order is None else _i32_array(initial_free_order)
+    st = _lib.pa_pool_create(num_blocks, block_size, None if order is None else _ptr_i32(order),
+                             C.byref(out))
+    return st, (out.value if st == PA_OK else None)
+
+
+def pa_pool_destroy(pool) -> None:
+    _lib.pa_pool_destroy(pool)
+
+
+def pa_pool_num_free(pool) -> int:
+    return _lib.pa_pool_num_free(pool)
+
+
+def pa_pool_num_seqs(pool) -> int:
+    return _lib.pa_pool_num_seqs(pool)
+
+
+def pa_pool_free_list(pool):
+    n = _i32()
+    cap = max(0, pa_pool_num_free(pool))
+    buf = np.empty(cap, dtype=np.int32)
+    st = _lib.pa_pool_free_list(pool, _ptr_i32(buf), cap, C.byref(n))
+    return st, buf[: n.value]
+
+
+def pa_seq_create(pool, seq: int, num_tokens: int) -> int:
+    return _lib.pa_seq_create(pool, seq, num_tokens)
+
+
+def pa_seq_append(pool, seq: int, n_new: int, want_slots: bool = True):
+    """Returns (status, slots of the new positions or None)."""
+    if want_slots and n_new > 0:
+        buf = np.empty(n_new, dtype=np.int32)
+        st = _lib.pa_seq_append(pool, seq, n_new, _ptr_i32(buf))
+        return st, buf
+    return _lib.pa_seq_append(pool, seq, n_new, None), None
+
+
+def pa_seq_slots(pool, seq: int, start: int, n: int):
+    buf = np.empty(max(n, 0), dtype=np.int32)
+    st = _lib.pa_seq_slots(pool, seq, start, n, _ptr_i32(buf))
+    return st, buf
+
+
+def pa_seq_release(pool, seq: int) -> int:
+    return _lib.pa_seq_release(pool, seq)
+
+
+def pa_seq_length(pool, seq: int):
+    n = _i32()
+    st = _lib.pa_seq_length(pool, seq, C.byref(n))
+    return st, n.value
+
+
+def pa_seq_block_table(pool, seq: int):
+    n = _i32()
+    st = _lib.pa_seq_block_table(pool, seq, None, 0, C.byref(n))
+    if st == PA_ERR_UNKNOWN_SEQ:
+        return st, None
+    buf = np.empty(n.value, dtype=np.int32)
+    st = _lib.pa_seq_block_table(pool, seq, _ptr_i32(buf), n.value, C.byref(n))
+    return st, buf
+
+
+def pa_pack_batch(pool, seqs, max_blocks: int, block_tables: np.ndarray | None = None,
+                  context_lens: np.ndarray | None = None):
+    """Returns (status, block_tables [n, max_blocks] int32, context_lens [n] int32).
+    Caller-provided output arrays (e.g. pinned host tensors' numpy views) are
+    filled in place."""
+    s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+    n = len(s)
+    if block_tables is None:
+        block_tables = np.empty((n, max_blocks), dtype=np.int32)
+    if context_lens is None:
+        context_lens = np.empty(n, dtype=np.int32)
+    assert block_tables.dtype == np.int32 and block_tables.flags.c_contiguous
+    assert block_tables.size >= n * max_blocks and context_lens.size >= n
+    st = _lib.pa_pack_batch(pool, s.ctypes.data_as(_i64p), n, max_blocks, _ptr_i32(block_tables),
+                            _ptr_i32(context_lens))
+    return st, block_tables, context_lens
+
+
+def pa_validate_tables(block_tables, context_lens, max_blocks: int, block_size: int,
+                       num_blocks: int) -> int:
+    t = _i32_array(block_tables)
+    lens = _i32_array(context_lens)
+    return _lib.pa_validate_tables(_ptr_i32(t), _ptr_i32(lens), len(lens), max_blocks, block_size,
+                                   num_blocks)
+
+
+# ------------------------------------------------------------- kernels -----
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dptr(t) -> int:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise PaError(PA_ERR_INVALID, "expected a device tensor")
+    return t.data_ptr()
+
+
+def dtype_of(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3
+    raise PaError(PA_ERR_INVALID, f"unsupported tensor dtype {t.dtype}")
+
+
+def pa_cache_write(stream, k_new, v_new, slot_mapping, k_cache, v_cache, num_blocks: int,
+                   H_kv: int, D: int, bs: int = 16, k_scale: float = 1.0, v_scale: float = 1.0,
+                   n: int | None = None) -> int:
+    n = slot_mapping.numel() if n is None else n
+    return _lib.pa_cache_write(_stream_handle(stream), _dptr(k_new), _dptr(v_new),
+                               dtype_of(k_new), _dptr(slot_mapping), n, _dptr(k_cache),
+                               _dptr(v_cache), dtype_of(k_cache), num_blocks, H_kv, D, bs,
+                               k_scale, v_scale)
+
+
+def pa_decode_workspace_bytes(S: int, H_q: int, H_kv: int, D: int, max_context_len: int) -> int:
+    return _lib.pa_decode_workspace_bytes(S, H_q, H_kv, D, max_context_len)
+
+
+def pa_decode(stream, out, q, k_cache, v_cache, block_tables, context_lens, num_blocks: int,
+              H_kv: int, max_context_len: int, sm_scale: float, k_scale: float = 1.0,
+              v_scale: float = 1.0, ws=None, bs: int = 16) -> int:
+    S, H_q, D = q.shape
+    max_blocks = block_tables.shape[1]
+    return _lib.pa_decode(_stream_handle(stream), _dptr(out), dtype_of(out), _dptr(q), dtype_of(q),
+                          _dptr(k_cache), _dptr(v_cache), dtype_of(k_cache), _dptr(block_tables),
+                          max_blocks, num_blocks, _dptr(context_lens), S, H_q, H_kv, D, bs,
+                          max_context_len, sm_scale, k_scale, v_scale, _dptr(ws),
+                          0 if ws is None else ws.numel() * ws.element_size())
+
+
+def pa_prefill_workspace_bytes(n_chunks: int, max_q_len: int, H_q: int, H_kv: int, D: int,
+                               max_context_len: int) -> int:
+    return _lib.pa_prefill_workspace_bytes(n_chunks, max_q_len, H_q, H_kv, D, max_context_len)
+
+
+def pa_prefill_chunk(stream, out, q, cu_q_lens, start_pos, k_cache, v_cache, block_tables,
+                     num_blocks: int, H_kv: int, max_q_len: int, max_context_len: int,
+                     sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0, ws=None,
+                     bs: int = 16) -> int:
+    _, H_q, D = q.shape
+    n_chunks = start_pos.numel()
+    max_blocks = block_tables.shape[1]
+    return _lib.pa_prefill_chunk(_stream_handle(stream), _dptr(out), dtype_of(out), _dptr(q),
+                                 dtype_of(q), _dptr(cu_q_lens), _dptr(start_pos), _dptr(k_cache),
+                                 _dptr(v_cache), dtype_of(k_cache), _dptr(block_tables),
+                                 max_blocks, num_blocks, n_chunks, H_q, H_kv, D, bs, max_q_len,
+                                 max_context_len, sm_scale, k_scale, v_scale, _dptr(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size())

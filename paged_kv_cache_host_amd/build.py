@@ -1,0 +1,73 @@
+"""Build libpa.so (host allocator + HIP kernels for gfx950) in-tree.
+
+    python -m paged_kv_cache_host_amd.build          # or build() from Python
+
+Every source is compiled with hipcc for gfx950 only.  Packed-fp32 VALU
+instructions are disabled on the device side (-packed-fp32-ops) so that
+float code is never lowered to them.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libpa.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+SOURCES = ["pa_host.cpp", "pa_cache_write.hip", "pa_decode.hip", "pa_generic.hip", "pa_prefill.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(p):
+        raise RuntimeError("hipcc not found (ROCm is required to build libpa)")
+    return p
+
+
+def _flags(src: str) -> list[str]:
+    f = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-I", INCLUDE, "-I", CSRC]
+    if src.endswith(".hip"):
+        f += ["-x", "hip", f"--offload-arch={ARCH}",
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-fno-gpu-rdc"]
+    return f
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *_flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        msg = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
+        if msg.strip():
+            print(msg, file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,283 @@
+// Host side of libpa: the FIFO block pool, per-sequence block tables, batch
+// packing and error reporting.
+//
+// ARTICLE "vLLM inference engine architecture" (lpnh.cn) §2.2, block
+// manager: every block id starts free; allocate(n) takes the first n free ids
+// and fails when fewer than n are free; free(ids) appends them to the back.
+// LESSON "vLLM Serving Internals", "The Concept: PagedAttention as a virtual
+// memory system": a sequence's table maps logical position p to block
+// table[p / bs]; one more block is added when the sequence grows past its
+// blocks; blocks return to the pool when the sequence finishes.
+//
+// The free list is a ring buffer of int32 ids (capacity = pool size, so it
+// can never overflow: a block is either in the ring or in exactly one table).
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Seq {
+  std::vector<int32_t> table;
+  int32_t len = 0;
+};
+
+}  // namespace
+
+struct pa_pool {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> ring;  // free ids, FIFO
+  int32_t head = 0;           // index of the front of the free list
+  int32_t count = 0;          // number of free ids
+  std::unordered_map<int64_t, Seq> seqs;
+
+  int32_t at(int32_t i) const { return ring[(head + i) % num_blocks]; }
+  // Take n ids from the front.  Caller has checked count >= n.
+  void take(int32_t n, std::vector<int32_t>& dst) {
+    for (int32_t i = 0; i < n; ++i) {
+      dst.push_back(ring[head]);
+      head = head + 1 == num_blocks ? 0 : head + 1;
+    }
+    count -= n;
+  }
+  void give_back(const std::vector<int32_t>& ids) {
+    for (int32_t b : ids) {
+      ring[(head + count) % num_blocks] = b;
+      ++count;
+    }
+  }
+};
+
+namespace pa {
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+}  // namespace pa
+
+using pa::fail;
+
+static inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+extern "C" {
+
+int32_t pa_version(void) { return 10000; }
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order,
+                         pa_pool** out) {
+  if (!out) return fail(PA_ERR_INVALID, "pa_pool_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks < 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID, "pa_pool_create: num_blocks=%d block_size=%d", num_blocks,
+                block_size);
+  pa_pool* p = new (std::nothrow) pa_pool;
+  if (!p) return fail(PA_ERR_INVALID, "pa_pool_create: out of host memory");
+  try {
+    p->ring.resize(static_cast<size_t>(num_blocks));
+  } catch (...) {
+    delete p;
+    return fail(PA_ERR_INVALID, "pa_pool_create: out of host memory for %d blocks", num_blocks);
+  }
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  if (initial_free_order) {
+    std::vector<char> seen(static_cast<size_t>(num_blocks), 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = initial_free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete p;
+        return fail(PA_ERR_INVALID,
+                    "pa_pool_create: initial_free_order is not a permutation (entry %d = %d)", i, b);
+      }
+      seen[b] = 1;
+      p->ring[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) p->ring[i] = i;
+  }
+  p->head = 0;
+  p->count = num_blocks;
+  *out = p;
+  return PA_OK;
+}
+
+void pa_pool_destroy(pa_pool* pool) { delete pool; }
+
+int32_t pa_pool_num_free(const pa_pool* pool) { return pool ? pool->count : -1; }
+
+int32_t pa_pool_num_seqs(const pa_pool* pool) {
+  return pool ? static_cast<int32_t>(pool->seqs.size()) : -1;
+}
+
+pa_status pa_pool_free_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n) {
+  if (!pool || !n) return fail(PA_ERR_INVALID, "pa_pool_free_list: NULL argument");
+  *n = pool->count;
+  if (cap < pool->count || (pool->count > 0 && !out))
+    return fail(PA_ERR_INVALID, "pa_pool_free_list: capacity %d < %d free blocks", cap,
+                pool->count);
+  for (int32_t i = 0; i < pool->count; ++i) out[i] = pool->at(i);
+  return PA_OK;
+}
+
+pa_status pa_seq_create(pa_pool* pool, int64_t seq, int32_t num_tokens) {
+  if (!pool) return fail(PA_ERR_INVALID, "pa_seq_create: pool is NULL");
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "pa_seq_create: num_tokens=%d", num_tokens);
+  if (pool->seqs.count(seq))
+    return fail(PA_ERR_EXISTS, "pa_seq_create: sequence %lld exists", (long long)seq);
+  int64_t need = ceil_div64(num_tokens, pool->block_size);
+  if (need > pool->count)
+    return fail(PA_ERR_NO_BLOCKS, "pa_seq_create: need %lld blocks, %d free", (long long)need,
+                pool->count);
+  Seq s;
+  s.table.reserve(static_cast<size_t>(need));
+  pool->take(static_cast<int32_t>(need), s.table);
+  s.len = num_tokens;
+  pool->seqs.emplace(seq, std::move(s));
+  return PA_OK;
+}
+
+pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_new, int32_t* slots_out) {
+  if (!pool) return fail(PA_ERR_INVALID, "pa_seq_append: pool is NULL");
+  if (n_new < 0) return fail(PA_ERR_INVALID, "pa_seq_append: n_new=%d", n_new);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_append: unknown sequence %lld", (long long)seq);
+  Seq& s = it->second;
+  int64_t new_len = static_cast<int64_t>(s.len) + n_new;
+  if (new_len > INT32_MAX) return fail(PA_ERR_INVALID, "pa_seq_append: length overflow");
+  int64_t need = ceil_div64(new_len, pool->block_size) - static_cast<int64_t>(s.table.size());
+  if (need > pool->count)
+    return fail(PA_ERR_NO_BLOCKS, "pa_seq_append: need %lld blocks, %d free", (long long)need,
+                pool->count);
+  if (need > 0) pool->take(static_cast<int32_t>(need), s.table);
+  const int32_t bs = pool->block_size;
+  if (slots_out) {
+    for (int32_t i = 0; i < n_new; ++i) {
+      int32_t p = s.len + i;
+      slots_out[i] = s.table[p / bs] * bs + p % bs;
+    }
+  }
+  s.len = static_cast<int32_t>(new_len);
+  return PA_OK;
+}
+
+pa_status pa_seq_slots(const pa_pool* pool, int64_t seq, int32_t start, int32_t n,
+                       int32_t* slots_out) {
+  if (!pool || (n > 0 && !slots_out)) return fail(PA_ERR_INVALID, "pa_seq_slots: NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_slots: unknown sequence %lld", (long long)seq);
+  const Seq& s = it->second;
+  if (start < 0 || n < 0 || static_cast<int64_t>(start) + n > s.len)
+    return fail(PA_ERR_INVALID, "pa_seq_slots: range [%d, %d) outside length %d", start,
+                start + n, s.len);
+  const int32_t bs = pool->block_size;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t p = start + i;
+    slots_out[i] = s.table[p / bs] * bs + p % bs;
+  }
+  return PA_OK;
+}
+
+pa_status pa_seq_release(pa_pool* pool, int64_t seq) {
+  if (!pool) return fail(PA_ERR_INVALID, "pa_seq_release: pool is NULL");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_release: unknown sequence %lld", (long long)seq);
+  pool->give_back(it->second.table);
+  pool->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_seq_length(const pa_pool* pool, int64_t seq, int32_t* len) {
+  if (!pool || !len) return fail(PA_ERR_INVALID, "pa_seq_length: NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_length: unknown sequence %lld", (long long)seq);
+  *len = it->second.len;
+  return PA_OK;
+}
+
+pa_status pa_seq_block_table(const pa_pool* pool, int64_t seq, int32_t* out, int32_t cap,
+                             int32_t* n) {
+  if (!pool || !n) return fail(PA_ERR_INVALID, "pa_seq_block_table: NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_block_table: unknown sequence %lld", (long long)seq);
+  const auto& t = it->second.table;
+  *n = static_cast<int32_t>(t.size());
+  if (cap < *n || (*n > 0 && !out))
+    return fail(PA_ERR_INVALID, "pa_seq_block_table: capacity %d < %d", cap, *n);
+  if (!t.empty()) std::memcpy(out, t.data(), t.size() * sizeof(int32_t));
+  return PA_OK;
+}
+
+pa_status pa_pack_batch(const pa_pool* pool, const int64_t* seqs, int32_t n_seqs,
+                        int32_t max_blocks, int32_t* block_tables, int32_t* context_lens) {
+  if (!pool || n_seqs < 0 || max_blocks < 0)
+    return fail(PA_ERR_INVALID, "pa_pack_batch: bad arguments");
+  if (n_seqs > 0 && (!seqs || !context_lens || (max_blocks > 0 && !block_tables)))
+    return fail(PA_ERR_INVALID, "pa_pack_batch: NULL argument");
+  // validate first so that a failure writes nothing
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end())
+      return fail(PA_ERR_UNKNOWN_SEQ, "pa_pack_batch: unknown sequence %lld",
+                  (long long)seqs[i]);
+    if (static_cast<int64_t>(it->second.table.size()) > max_blocks)
+      return fail(PA_ERR_INVALID, "pa_pack_batch: sequence %lld holds %zu blocks > max_blocks %d",
+                  (long long)seqs[i], it->second.table.size(), max_blocks);
+  }
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const Seq& s = pool->seqs.find(seqs[i])->second;
+    int32_t* row = block_tables + static_cast<int64_t>(i) * max_blocks;
+    const int32_t nb = static_cast<int32_t>(s.table.size());
+    if (nb) std::memcpy(row, s.table.data(), static_cast<size_t>(nb) * sizeof(int32_t));
+    for (int32_t j = nb; j < max_blocks; ++j) row[j] = -1;
+    context_lens[i] = s.len;
+  }
+  return PA_OK;
+}
+
+pa_status pa_validate_tables(const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t n_seqs, int32_t max_blocks, int32_t block_size,
+                             int32_t num_blocks) {
+  if (n_seqs < 0 || max_blocks < 0 || block_size <= 0 || num_blocks < 0)
+    return fail(PA_ERR_INVALID, "pa_validate_tables: bad sizes");
+  if (n_seqs > 0 && (!context_lens || (max_blocks > 0 && !block_tables)))
+    return fail(PA_ERR_INVALID, "pa_validate_tables: NULL argument");
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    int64_t L = context_lens[i];
+    if (L < 0 || L > static_cast<int64_t>(max_blocks) * block_size)
+      return fail(PA_ERR_INVALID, "pa_validate_tables: row %d context %lld exceeds %d blocks", i,
+                  (long long)L, max_blocks);
+    int64_t nb = ceil_div64(L, block_size);
+    const int32_t* row = block_tables + static_cast<int64_t>(i) * max_blocks;
+    for (int64_t j = 0; j < nb; ++j)
+      if (row[j] < 0 || row[j] >= num_blocks)
+        return fail(PA_ERR_INVALID, "pa_validate_tables: row %d entry %lld = %d out of range", i,
+                    (long long)j, row[j]);
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+"""libpa's host block pool (C++) against the oracle allocator, bit-exactly,
+plus the library's exported symbols.  CPU only: no kernel is launched."""
+import json
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import paged_kv_cache_host_amd as pa
+from oracle import allocator as oa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 20
+    out = subprocess.run(["nm", "-D", "--defined-only", pa._pa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    # and the binding covers the same set
+    assert sorted(pa.EXPORTED) == names
+
+
+def _state(pool):
+    st_, free = pa.pa_pool_free_list(pool)
+    assert st_ == pa.PA_OK
+    return list(free)
+
+
+def test_golden_trace_through_c_abi():
+    g = json.load(open(os.path.join(GOLDEN, "allocator_trace.json")))
+    st_, pool = pa.pa_pool_create(g["num_blocks"], g["block_size"], g["initial_free_order"])
+    assert st_ == pa.PA_OK
+    try:
+        for step in g["steps"]:
+            if step["op"] == "create":
+                s = pa.pa_seq_create(pool, step["seq"], step["n"])
+            elif step["op"] == "append":
+                s, slots = pa.pa_seq_append(pool, step["seq"], step["n"])
+                if "slots" in step:
+                    assert list(slots) == step["slots"]
+            else:
+                s = pa.pa_seq_release(pool, step["seq"])
+            assert s == step["status"], (step, pa.pa_last_error())
+            assert _state(pool) == step["free"]
+            if "table" in step:
+                assert list(pa.pa_seq_block_table(pool, step["seq"])[1]) == step["table"]
+    finally:
+        pa.pa_pool_destroy(pool)
+
+
+ops = st.lists(st.tuples(st.sampled_from(["create", "append", "release", "pack"]),
+                         st.integers(0, 6), st.integers(0, 90)), max_size=80)
+
+
+@settings(max_examples=300, deadline=None)
+@given(ops, st.integers(0, 48), st.randoms(use_true_random=False))
+def test_bit_exact_against_oracle(oplist, nblocks, rnd):
+    order = list(range(nblocks))
+    rnd.shuffle(order)
+    ref = oa.BlockPool(nblocks, 16, order)
+    st_, pool = pa.pa_pool_create(nblocks, 16, order)
+    assert st_ == pa.PA_OK
+    try:
+        for op, seq, n in oplist:
+            if op == "create":
+                assert pa.pa_seq_create(pool, seq, n) == ref.seq_create(seq, n)
+            elif op == "append":
+                s1, slots1 = pa.pa_seq_append(pool, seq, n)
+                s2, slots2 = ref.seq_append(seq, n)
+                assert s1 == s2
+                if s1 == pa.PA_OK and n > 0:
+                    assert list(slots1) == slots2
+            elif op == "release":
+                assert pa.pa_seq_release(pool, seq) == ref.seq_release(seq)
+            else:
+                seqs = sorted(ref.tables)
+                if seqs:
+                    mb = max(1, max(len(t) for t in ref.tables.values()))
+                    s1, t1, l1 = pa.pa_pack_batch(pool, seqs, mb)
+                    t2, l2 = ref.pack(seqs, mb)
+                    assert s1 == pa.PA_OK
+                    assert t1.tolist() == t2 and l1.tolist() == l2
+            assert _state(pool) == ref.free_list()
+            assert pa.pa_pool_num_free(pool) == ref.num_free()
+            assert pa.pa_pool_num_seqs(pool) == len(ref.tables)
+            for s, t in ref.tables.items():
+                st2, tab = pa.pa_seq_block_table(pool, s)
+                assert st2 == pa.PA_OK and list(tab) == t
+                st3, ln = pa.pa_seq_length(pool, s)
+                assert ln == ref.lengths[s]
+                if ref.lengths[s]:
+                    st4, sl = pa.pa_seq_slots(pool, s, 0, ref.lengths[s])
+                    assert list(sl) == ref.slots(s, 0, ref.lengths[s])
+    finally:
+        pa.pa_pool_destroy(pool)
+
+
+def test_error_paths_leave_state_unchanged():
+    st_, pool = pa.pa_pool_create(3, 16, [2, 0, 1])
+    assert st_ == pa.PA_OK
+    try:
+        assert pa.pa_seq_create(pool, 7, 40) == pa.PA_OK        # takes 2, 0, 1
+        before = _state(pool)
+        assert pa.pa_seq_append(pool, 7, 9)[0] == pa.PA_ERR_NO_BLOCKS
+        assert "need 1 blocks, 0 free" in pa.pa_last_error()
+        assert pa.pa_seq_length(pool, 7) == (pa.PA_OK, 40)
+        assert _state(pool) == before
+        assert pa.pa_seq_create(pool, 7, 1) == pa.PA_ERR_EXISTS
+        assert pa.pa_seq_release(pool, 8) == pa.PA_ERR_UNKNOWN_SEQ
+        assert pa.pa_seq_create(pool, 9, -1) == pa.PA_ERR_INVALID
+        assert pa.pa_seq_slots(pool, 7, 39, 2)[0] == pa.PA_ERR_INVALID
+        st2, _, _ = pa.pa_pack_batch(pool, [7], 2)              # table has 3 blocks
+        assert st2 == pa.PA_ERR_INVALID
+        assert pa.pa_seq_release(pool, 7) == pa.PA_OK
+        assert _state(pool) == [2, 0, 1]
+    finally:
+        pa.pa_pool_destroy(pool)
+    assert pa.pa_pool_create(3, 16, [0, 0, 1])[0] == pa.PA_ERR_INVALID
+    assert pa.pa_pool_create(3, 0)[0] == pa.PA_ERR_INVALID
+    assert pa.pa_pool_num_free(None) == -1
+
+
+def test_validate_tables():
+    t = np.array([[0, 1, -1], [2, -1, -1]], dtype=np.int32)
+    assert pa.pa_validate_tables(t, [20, 16], 3, 16, 3) == pa.PA_OK
+    assert pa.pa_validate_tables(t, [20, 17], 3, 16, 3) == pa.PA_ERR_INVALID   # needs entry [1][1]
+    assert pa.pa_validate_tables(t, [49, 1], 3, 16, 3) == pa.PA_ERR_INVALID    # longer than 3 blocks
+    assert pa.pa_validate_tables(t, [20, 16], 3, 16, 2) == pa.PA_ERR_INVALID   # block 2 out of pool
+
+
+def test_argument_validation_of_kernel_entry_points_on_host():
+    # invalid arguments are rejected before anything touches a device
+    assert pa._pa._lib.pa_decode(None, None, 1, None, 1, None, None, 1, None, 4, 4, None,
+                                 1, 64, 8, 128, 8, 100, 0.1, 1.0, 1.0, None, 0) == pa.PA_ERR_INVALID
+    assert "block size" in pa.pa_last_error()
+    assert pa._pa._lib.pa_decode(None, None, 1, None, 1, None, None, 1, None, 4, 4, None,
+                                 1, 64, 7, 128, 16, 100, 0.1, 1.0, 1.0, None, 0) == pa.PA_ERR_INVALID
+    assert pa._pa._lib.pa_decode(None, None, 1, None, 1, None, None, 1, None, 4, 4, None,
+                                 1, 64, 8, 96, 16, 100, 0.1, 1.0, 1.0, None, 0) == pa.PA_ERR_INVALID
+    assert pa._pa._lib.pa_decode(None, None, 1, None, 1, None, None, 0, None, 4, 4, None,
+                                 1, 64, 8, 128, 16, 100, 0.1, 1.0, 1.0, None, 0) == pa.PA_ERR_INVALID
+    assert "dtypes" in pa.pa_last_error()
+    # fp8 cache with a bad scale
+    assert pa._pa._lib.pa_decode(None, None, 1, None, 1, None, None, 2, None, 4, 4, None,
+                                 1, 64, 8, 128, 16, 100, 0.1, 0.0, 1.0, None, 0) == pa.PA_ERR_INVALID
+    # the MFMA path needs its workspace (pointers are never dereferenced on this path)
+    fake = 0x1000
+    assert pa._pa._lib.pa_decode(None, fake, 1, fake, 1, fake, fake, 1, fake, 4, 4, fake,
+                                 1, 64, 8, 128, 16, 100, 0.1, 1.0, 1.0, None, 0) == pa.PA_ERR_WORKSPACE
+    assert pa.pa_decode_workspace_bytes(2, 64, 8, 128, 600) == 2 * 64 * 3 * 130 * 4
+    assert pa._pa._lib.pa_cache_write(None, None, None, 1, None, 4, None, None, 0, 4, 8, 128, 16,
+                                      1.0, 1.0) == pa.PA_ERR_INVALID
+    assert pa._pa._lib.pa_cache_write(None, fake, fake, 1, fake, 4, fake, fake, 2, 4, 8, 128, 16,
+                                      -1.0, 1.0) == pa.PA_ERR_INVALID
+    assert pa._pa._lib.pa_prefill_chunk(None, None, 1, None, 1, None, None, None, None, 1, None, 4,
+                                        4, 1, 64, 8, 128, 8, 512, 512, 0.1, 1.0, 1.0, None,
+                                        0) == pa.PA_ERR_INVALID

@@ -230,3 +230,61 @@ def trace(seed: int = 5, iters: int = 1000, lam: float = 0.5, prompt_median: flo
     if num_blocks is None:
         num_blocks = int(0.9 * 288e9) // (BLOCK * 2 * 8 * 128 * 2)
     return TraceWorkload(f"trace-{iters}it-lam{lam}", iters, arrivals, num_blocks, None)
+
+
+@dataclass
+class PrefillWorkload:
+    """Prompts whose K/V are all written, then attended by prefill slices
+    (sequence, start position, length) in one call."""
+    name: str
+    prompts: np.ndarray          # [n_seq] prompt lengths
+    slices: list                 # [(seq, start, n)]
+    num_blocks: int
+    free_order: np.ndarray
+    h_q: int
+    h_kv: int
+    d: int
+    kv_dtype: str
+    cache_dtype: str
+    q_dtype: str
+    k_tok: np.ndarray            # [sum prompts, H_kv, D] raw, sequence-major
+    v_tok: np.ndarray
+    q_tok: np.ndarray            # [sum prompts, H_q, D] raw
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    sm_scale: float = 0.0
+
+    def token_offsets(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.prompts)]).astype(np.int64)
+
+
+def prefill_workload(name: str, seed: int, prompt_len: int | None = None, chunks=None,
+                     prompts=None, slices=None, h_q: int = 64, h_kv: int = 8, d: int = 128,
+                     dtype: str = "bf16", cache_dtype: str = "bf16",
+                     extra_blocks: int = 9) -> PrefillWorkload:
+    """Either one prompt of ``prompt_len`` tokens cut into ``chunks`` (sizes),
+    or several ``prompts`` with explicit ``slices``."""
+    if prompts is None:
+        prompts = [prompt_len]
+        slices = []
+        start = 0
+        for n in chunks:
+            slices.append((0, start, n))
+            start += n
+        assert start <= prompt_len
+    prompts = np.asarray(prompts, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    num_blocks = blocks_needed(prompts) + extra_blocks
+    free_order = rng.permutation(num_blocks).astype(np.int32)
+    ntok = int(prompts.sum())
+    kvd = "bf16" if cache_dtype == "fp8" else dtype
+    k_tok = normal_raw(rng, (ntok, h_kv, d), kvd)
+    v_tok = normal_raw(rng, (ntok, h_kv, d), kvd)
+    q_dtype = "bf16" if cache_dtype == "fp8" else dtype
+    q_tok = normal_raw(rng, (ntok, h_q, d), q_dtype)
+    w = PrefillWorkload(name, prompts, list(slices), num_blocks, free_order, h_q, h_kv, d, kvd,
+                        cache_dtype, q_dtype, k_tok, v_tok, q_tok, sm_scale=_sm_scale(d))
+    if cache_dtype == "fp8":
+        w.k_scale = _amax_scale(k_tok)
+        w.v_scale = _amax_scale(v_tok)
+    return w
