@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+One step = one continuous-batching decode iteration of one 70B-shaped
+attention layer (128 sequences, 64 query / 8 KV heads, head dim 128, bf16,
+16-token blocks, lognormal contexts of mean 1500):
+
+  a1  host: libpa grows every sequence by one token (one block taken at each
+      block boundary) and packs block tables + context lengths into pinned
+      buffers; the tables go to the device on a copy stream, overlapped with
+      the previous step's kernels (double-buffered);
+  a2  pa_cache_write scatters the new tokens' K/V into their paged slots;
+  a3  pa_decode: split-K paged attention with the split merge fused in.
+
+``value`` is the whole step's algorithmic HBM bytes (decode: every K/V byte
+of every context once per KV head, Q, output, block-table entries and
+context lengths; cache write: new K/V read and written) divided by the wall
+time of the timed steps.  ``roofline`` is the decode kernel alone: the
+same algorithmic decode bytes per launch over its average duration from HIP
+events on its own stream.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+H_Q, H_KV, D, BLOCK = 64, 8, 128, 16
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=32)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("pa_decode.hip", "pa_device.h"):
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_host_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(lens: np.ndarray) -> int:
+    """Algorithmic HBM bytes of one decode launch (bf16)."""
+    lens = lens.astype(np.int64)
+    S = len(lens)
+    kv = int(lens.sum()) * H_KV * D * 2 * 2
+    qo = S * H_Q * D * (2 + 2)
+    tables = int((-(-lens // BLOCK)).sum()) * 4 + 4 * S
+    return kv + qo + tables
+
+
+def cache_write_bytes(n_tok: int) -> int:
+    return n_tok * H_KV * D * 2 * 2 * 2 + 4 * n_tok
+
+
+def traffic_from_profile(digest: str):
+    """Counter-measured HBM bytes per decode launch, if a PMC summary of the
+    current kernel source is committed."""
+    p = os.path.join(PROFILE_DIR, "decode_70b_128seq_pmc.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_digest") != digest:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(n_seqs: int):
+    """The oracle (numpy, fp64) on the first n_seqs sequences of the same
+    workload: gather through the block tables + softmax attention, timed
+    without data generation and cache construction."""
+    from threadpoolctl import threadpool_info
+
+    import workloads
+    from oracle import allocator as oa
+    from oracle import attention as oat
+    from oracle import cache as oc
+    from oracle import codecs
+
+    lengths, _, _ = workloads.decode_70b_layout()
+    L = lengths[:n_seqs]
+    rng = np.random.default_rng(12)
+    nb = workloads.blocks_needed(L) + 8
+    pool = oa.BlockPool(nb, BLOCK, rng.permutation(nb).tolist())
+    kc, vc = oc.new_cache(nb, H_KV, BLOCK, D, "bf16")
+    for s, l in enumerate(L.tolist()):
+        pool.seq_create(s, l)
+        k = workloads.normal_raw(rng, (l, H_KV, D), "bf16")
+        v = workloads.normal_raw(rng, (l, H_KV, D), "bf16")
+        oc.cache_write(kc, vc, k, v, pool.slots(s, 0, l), "bf16", "bf16")
+    q = codecs.decode(workloads.normal_raw(rng, (len(L), H_Q, D), "bf16"), "bf16")
+    tables, lens = pool.pack(range(len(L)), max(-(-int(l) // BLOCK) for l in L))
+    tables = np.asarray(tables)
+    lens = np.asarray(lens)
+    sm = float(np.float32(1.0) / np.float32(math.sqrt(D)))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oat.decode(q, kc, vc, tables, lens, H_KV, sm, "bf16")
+        reps += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": decode_bytes(lens) / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {len(L)} of the 128 sequences ({int(L.sum())} context tokens), "
+                      f"one decode launch's gather + fp64 attention, mean of {reps} runs; "
+                      f"host {model or 'unknown'}, {len(os.sched_getaffinity(0))} cores visible"}
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "launches": 3}))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the paged-attention path shards by sequence or KV head with no exchange, so "
+              "multi-GPU figures are not produced here.", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import torch
+
+    import workloads
+    from paged_kv_cache_host_amd import _pa as pa
+    from paged_kv_cache_host_amd.engine import PagedKV, decode_workspace, sm_scale_for
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, W = args.steps, args.warmup
+
+    lengths, num_blocks, free_order = workloads.decode_70b_layout()
+    S = len(lengths)
+    seqs = np.arange(S, dtype=np.int64)
+    max_ctx = int(lengths.max()) + W + K
+    MB = -(-max_ctx // BLOCK)
+
+    # -- set-up (untimed): pool, contexts of L-1 tokens already cached
+    kv = PagedKV(num_blocks, H_KV, D, "bf16", dev, free_order)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2)
+    fill_slots = []
+    for s in range(S):
+        pa.check(kv.create(s, int(lengths[s]) - 1))
+        if lengths[s] > 1:
+            fill_slots.append(kv.slots(s, 0, int(lengths[s]) - 1))
+    fill_slots = np.concatenate(fill_slots).astype(np.int32)
+    CH = 1 << 16
+    for a in range(0, len(fill_slots), CH):
+        n = min(CH, len(fill_slots) - a)
+        kk = torch.randn((n, H_KV, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        vv = torch.randn((n, H_KV, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        kv.write(kk, vv, torch.from_numpy(fill_slots[a:a + n]).to(dev))
+    R = 4
+    k_ring = [torch.randn((S, H_KV, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    v_ring = [torch.randn((S, H_KV, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    q_ring = [torch.randn((S, H_Q, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    out = torch.empty((S, H_Q, D), dtype=torch.bfloat16, device=dev)
+    ws = decode_workspace(S, H_Q, H_KV, D, max_ctx, dev)
+    sm = sm_scale_for(D)
+
+    slots_pin = [torch.empty((S, 1), dtype=torch.int32).pin_memory() for _ in range(2)]
+    tables_pin = [torch.empty((S, MB), dtype=torch.int32).pin_memory() for _ in range(2)]
+    lens_pin = [torch.empty((S,), dtype=torch.int32).pin_memory() for _ in range(2)]
+    slots_dev = [torch.empty((S, 1), dtype=torch.int32, device=dev) for _ in range(2)]
+    tables_dev = [torch.empty((S, MB), dtype=torch.int32, device=dev) for _ in range(2)]
+    lens_dev = [torch.empty((S,), dtype=torch.int32, device=dev) for _ in range(2)]
+    compute = torch.cuda.Stream(device=dev)
+    copy = torch.cuda.Stream(device=dev)
+    ev_copied = [torch.cuda.Event() for _ in range(2)]
+    ev_consumed = [torch.cuda.Event() for _ in range(2)]
+    for e in ev_consumed:
+        e.record(compute)
+    ev_d0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_d1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ctx_lens = []
+
+    def step(i: int, timed_idx: int | None):
+        X = i & 1
+        ev_consumed[X].synchronize()
+        st, done, _ = pa.pa_batch_append(kv.pool, seqs, 1, slots_pin[X].numpy())
+        pa.check(st)
+        st, _, lens_np = pa.pa_pack_batch(kv.pool, seqs, MB, tables_pin[X].numpy(),
+                                          lens_pin[X].numpy())
+        pa.check(st)
+        with torch.cuda.stream(copy):
+            slots_dev[X].copy_(slots_pin[X], non_blocking=True)
+            tables_dev[X].copy_(tables_pin[X], non_blocking=True)
+            lens_dev[X].copy_(lens_pin[X], non_blocking=True)
+            ev_copied[X].record(copy)
+        compute.wait_event(ev_copied[X])
+        r = i % R
+        pa.check(pa.pa_cache_write(compute, k_ring[r], v_ring[r], slots_dev[X], kv.k, kv.v,
+                                   num_blocks, H_KV, D, BLOCK))
+        if timed_idx is not None:
+            ev_d0[timed_idx].record(compute)
+        pa.check(pa.pa_decode(compute, out, q_ring[r], kv.k, kv.v, tables_dev[X], lens_dev[X],
+                              num_blocks, H_KV, max_ctx, sm, 1.0, 1.0, ws))
+        if timed_idx is not None:
+            ev_d1[timed_idx].record(compute)
+            ctx_lens.append(lens_np.copy())
+        ev_consumed[X].record(compute)
+
+    for i in range(W):
+        step(i, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    dec_ms = [ev_d0[i].elapsed_time(ev_d1[i]) for i in range(K)]
+    dec_bytes = [decode_bytes(l) for l in ctx_lens]
+    cw = cache_write_bytes(S)
+    total_bytes = sum(dec_bytes) + K * cw
+    value = total_bytes / wall / 1e9
+    dec_avg_s = sum(dec_ms) / K / 1e3
+    achieved = (sum(dec_bytes) / K) / dec_avg_s / 1e9
+    digest = kernel_source_digest()
+    traffic = traffic_from_profile(digest)
+
+    result = {
+        "metric": "paged-attn decode HBM GB/s (% peak); mixed decode+prefill tokens/s per layer",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode-70b-shaped: 128 seqs, 64/8 heads, d128, bf16 KV, "
+                               "block 16, lognormal ctx mean 1500 (one layer, one decode "
+                               "iteration per step incl. host append + cache write)",
+                   "num_seqs": S, "mean_context": round(float(np.mean([l.mean() for l in ctx_lens])), 1),
+                   "num_blocks": num_blocks},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "pa_decode (decode_kernel<BF16,128>)",
+                     "kernel_us": round(dec_avg_s * 1e6, 2),
+                     "algorithmic_bytes_per_launch": int(sum(dec_bytes) / K),
+                     "kernel_source_digest": digest},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_sample_seqs)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    kv.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -121,6 +121,16 @@ pa_status pa_seq_create(pa_pool* pool, int64_t seq, int32_t num_tokens);
  * flat slots of the new positions. */
 pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_new, int32_t* slots_out);
 
+/* Grow each of seqs[0 .. n_seqs) by n_new tokens, in order, as
+ * pa_seq_append does (LESSON "Continuous batching at the iteration level":
+ * every running sequence gains one token per iteration).  slots_out [host,
+ * n_seqs * n_new, may be NULL]: row i receives the new slots of seqs[i].
+ * Stops at the first sequence that fails; *n_done [host] receives the number
+ * of sequences grown (all of them on PA_OK), and the status is that
+ * sequence's error, the failing sequence itself being left unchanged. */
+pa_status pa_batch_append(pa_pool* pool, const int64_t* seqs, int32_t n_seqs, int32_t n_new,
+                          int32_t* slots_out, int32_t* n_done);
+
 /* Flat slots of positions start .. start+n-1 of `seq` (all must be < the
  * sequence's length) into slots_out [host, n]. */
 pa_status pa_seq_slots(const pa_pool* pool, int64_t seq, int32_t start, int32_t n,
@@ -191,8 +201,11 @@ pa_status pa_cache_write(void* stream, const void* k_new, const void* v_new, pa_
  * sm_scale: softmax scale (normally 1/sqrt(D)).  k_scale, v_scale: fp8
  *   per-tensor scales (ignored otherwise).
  * ws [device, ws_bytes]: scratch for split partials, at least
- *   pa_decode_workspace_bytes(...) bytes (0 bytes may be needed, then ws
- *   may be NULL); else PA_ERR_WORKSPACE.
+ *   pa_decode_workspace_bytes(...) bytes; else PA_ERR_WORKSPACE.  Its first
+ *   bytes hold per-(sequence, KV head) completion counters: the whole
+ *   workspace must be zero-filled before its first use, and every call
+ *   leaves the counters zero again.  Calls that overlap in time must not
+ *   share a workspace.
  * ---------------------------------------------------------------------- */
 size_t pa_decode_workspace_bytes(int32_t S, int32_t H_q, int32_t H_kv, int32_t D,
                                  int32_t max_context_len);

@@ -2,8 +2,18 @@
 
 The library ``libpa.so`` (C ABI in ``include/pa.h``) holds the host block
 allocator and the HIP kernels; ``paged_kv_cache_host_amd._pa`` is its ctypes
-binding.  Importing the package loads the library and fails loudly if it has
-not been built (``python -m paged_kv_cache_host_amd.build``).
+binding, re-exported here under the C names.  The library is loaded on first
+use of any of those names (so that ``paged_kv_cache_host_amd.build`` can run
+before it exists); a missing library raises ImportError there.
 """
-from . import _pa  # noqa: F401  (loads libpa.so)
-from ._pa import *  # noqa: F401,F403
+import importlib as _importlib
+
+
+def __getattr__(name):
+    if name.startswith("__"):
+        raise AttributeError(name)
+    _pa = _importlib.import_module("._pa", __name__)
+    try:
+        return getattr(_pa, name)
+    except AttributeError:
+        raise AttributeError(f"module {__name__!r} has no attribute {name!r}") from None

@@ -50,6 +50,7 @@ _SIGS = {
     "pa_pool_free_list": (_i32, [_vp, _i32p, _i32, _i32p]),
     "pa_seq_create": (_i32, [_vp, _i64, _i32]),
     "pa_seq_append": (_i32, [_vp, _i64, _i32, _i32p]),
+    "pa_batch_append": (_i32, [_vp, _i64p, _i32, _i32, _i32p, _i32p]),
     "pa_seq_slots": (_i32, [_vp, _i64, _i32, _i32, _i32p]),
     "pa_seq_release": (_i32, [_vp, _i64]),
     "pa_seq_length": (_i32, [_vp, _i64, _i32p]),
@@ -146,6 +147,19 @@ def pa_seq_append(pool, seq: int, n_new: int, want_slots: bool = True):
         st = _lib.pa_seq_append(pool, seq, n_new, _ptr_i32(buf))
         return st, buf
     return _lib.pa_seq_append(pool, seq, n_new, None), None
+
+
+def pa_batch_append(pool, seqs, n_new: int = 1, slots_out: np.ndarray | None = None):
+    """Returns (status, number of sequences grown, slots [n_seqs, n_new])."""
+    s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+    if slots_out is None:
+        slots_out = np.empty((len(s), n_new), dtype=np.int32)
+    assert slots_out.dtype == np.int32 and slots_out.flags.c_contiguous
+    assert slots_out.size >= len(s) * n_new
+    done = _i32()
+    st = _lib.pa_batch_append(pool, s.ctypes.data_as(_i64p), len(s), n_new, _ptr_i32(slots_out),
+                              C.byref(done))
+    return st, done.value, slots_out
 
 
 def pa_seq_slots(pool, seq: int, start: int, n: int):

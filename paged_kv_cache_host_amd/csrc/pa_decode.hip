@@ -131,15 +131,40 @@ __device__ __forceinline__ bf16x8 v_operand(const StepRegs<CacheT, D>& r, int t)
     return fp8x8_to_bf16x8(r.v[t]);
 }
 
+// Workspace of the matrix-core path: completion counters (one int32 per
+// (sequence, KV head), zero between calls), then per (sequence, query head,
+// split) the running max and sum (2 floats) and the unnormalised output
+// (D floats).
+inline size_t decode_counter_bytes(int32_t S, int32_t H_kv) {
+  return (static_cast<size_t>(S) * H_kv * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store_out4(typename OutT::raw* dst, f32x4 v) {
+  if constexpr (sizeof(typename OutT::raw) == 2) {
+    u32x2 w;
+    w[0] = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    w[1] = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    *reinterpret_cast<u32x2*>(dst) = w;
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = v;
+  }
+}
+
 // grid: (ceil(n_splits / kDecodeWaves), H_kv, S); block: 64 * kDecodeWaves.
 // Wave w of work-group x handles split x * kDecodeWaves + w of (seq, kv head).
+// A context that fits one split is finished by its wave directly.  Otherwise
+// each wave stores its partial (m, l, o) and bumps the (seq, kv head)
+// counter; the wave that arrives last merges all partials and writes the
+// output, then clears the counter for the next call.
 template <typename CacheT, int D>
-__global__ __launch_bounds__(kWave* kDecodeWaves) void decode_split_kernel(
-    const uint16_t* __restrict__ q, const typename CacheT::raw* __restrict__ k_cache,
+__global__ __launch_bounds__(kWave* kDecodeWaves) void decode_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
+    const typename CacheT::raw* __restrict__ k_cache,
     const typename CacheT::raw* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     int32_t max_blocks, int32_t num_blocks, const int32_t* __restrict__ context_lens,
-    int32_t H_q, int32_t H_kv, int32_t G, int32_t n_splits, float score_scale,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+    int32_t H_q, int32_t H_kv, int32_t G, int32_t n_splits, float score_scale, float out_scale,
+    int32_t* __restrict__ counters, float* __restrict__ ws_ml, float* __restrict__ ws_o) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int c = lane & 15;
@@ -153,6 +178,7 @@ __global__ __launch_bounds__(kWave* kDecodeWaves) void decode_split_kernel(
   const int32_t nblk = (L + kBlock - 1) / kBlock;
   const int32_t b0 = split * kSplitBlocks;
   if (L <= 0 || b0 >= nblk) return;
+  const int32_t n_valid = min(n_splits, (nblk + kSplitBlocks - 1) / kSplitBlocks);
   const int32_t b1 = (split == n_splits - 1) ? nblk : min(nblk, b0 + kSplitBlocks);
   const int32_t* __restrict__ table = block_tables + static_cast<int64_t>(seq) * max_blocks;
 
@@ -233,56 +259,56 @@ __global__ __launch_bounds__(kWave* kDecodeWaves) void decode_split_kernel(
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
 
+  const int64_t head_row = static_cast<int64_t>(seq) * H_q + kvh * G + c;  // valid if c < G
+  if (n_valid == 1) {
+    if (c < G) {
+      const float inv = out_scale / l_run;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t)
+        store_out4<BF16>(out + head_row * D + 16 * t + 4 * g, o[t] * inv);
+    }
+    return;
+  }
+
+  const int64_t part = head_row * n_splits + split;
   if (c < G) {
-    const int64_t part =
-        (static_cast<int64_t>(seq) * H_q + kvh * G + c) * n_splits + split;
     float* dst = ws_o + part * D;
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * g) = o[t];
+    for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * g) = o[t];
     if (g == 0) {
       ws_ml[part * 2 + 0] = m_run;
       ws_ml[part * 2 + 1] = l_run;
     }
   }
-}
-
-// grid: ceil(S * H_q / 4); block: 256 (one wave per (seq, query head)).
-template <typename OutT, int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
-    typename OutT::raw* __restrict__ out, const float* __restrict__ ws_o,
-    const float* __restrict__ ws_ml, const int32_t* __restrict__ context_lens, int32_t max_blocks,
-    int32_t S, int32_t H_q, int32_t n_splits, float out_scale) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
-  if (idx >= static_cast<int64_t>(S) * H_q) return;
-  const int seq = static_cast<int>(idx / H_q);
-  const int32_t L = min(context_lens[seq], max_blocks * kBlock);
-  const int32_t nblk = (L + kBlock - 1) / kBlock;
-  const int nsp = L <= 0 ? 0 : min(n_splits, (nblk + kSplitBlocks - 1) / kSplitBlocks);
-  const float* ml = ws_ml + idx * n_splits * 2;
-  const float* po = ws_o + idx * n_splits * D;
+  // publish the partial, then count this split as done
+  __threadfence();
+  int32_t* ctr = counters + static_cast<int64_t>(seq) * H_kv + kvh;
+  int32_t prev = 0;
+  if (lane == 0) prev = atomicAdd(ctr, 1);
+  prev = __shfl(prev, 0, kWave);
+  if (prev != n_valid - 1) return;
+  // last arrival: every other split's partial is visible after this fence
+  __threadfence();
+  if (lane == 0) atomicExch(ctr, 0);
+  if (c >= G) return;
+  const int64_t base = head_row * n_splits;
   float M = -__builtin_inff();
-  for (int j = 0; j < nsp; ++j) M = fmaxf(M, ml[2 * j]);
+  for (int j = 0; j < n_valid; ++j) M = fmaxf(M, ws_ml[(base + j) * 2]);
   float tot = 0.f;
-  float acc[D / kWave];
+  f32x4 acc[D / 16];
 #pragma unroll
-  for (int i = 0; i < D / kWave; ++i) acc[i] = 0.f;
-  for (int j = 0; j < nsp; ++j) {
-    const float w = __builtin_amdgcn_exp2f(ml[2 * j] - M);
-    tot += w * ml[2 * j + 1];
+  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < n_valid; ++j) {
+    const float w = __builtin_amdgcn_exp2f(ws_ml[(base + j) * 2] - M);
+    tot += w * ws_ml[(base + j) * 2 + 1];
+    const float* src = ws_o + (base + j) * D;
 #pragma unroll
-    for (int i = 0; i < D / kWave; ++i) acc[i] += w * po[j * D + lane + kWave * i];
+    for (int t = 0; t < D / 16; ++t)
+      acc[t] += w * *reinterpret_cast<const f32x4*>(src + 16 * t + 4 * g);
   }
-  const float inv = nsp ? out_scale / tot : 0.f;
+  const float inv = out_scale / tot;
 #pragma unroll
-  for (int i = 0; i < D / kWave; ++i) {
-    const float v = acc[i] * inv;
-    if constexpr (sizeof(typename OutT::raw) == 2)
-      out[idx * D + lane + kWave * i] = f32_to_bf16(v);
-    else
-      out[idx * D + lane + kWave * i] = v;
-  }
+  for (int t = 0; t < D / 16; ++t) store_out4<BF16>(out + head_row * D + 16 * t + 4 * g, acc[t] * inv);
 }
 
 template <typename CacheT, int D>
@@ -293,26 +319,20 @@ static pa_status launch_decode_mfma(hipStream_t st, void* out, const void* q, co
                                     int32_t H_kv, int32_t max_context_len, float sm_scale,
                                     float k_scale, float v_scale, void* ws) {
   const int32_t n_splits = decode_num_splits(max_context_len);
-  float* ws_o = static_cast<float*>(ws);
-  float* ws_ml = ws_o + static_cast<int64_t>(S) * H_q * n_splits * D;
+  int32_t* counters = static_cast<int32_t*>(ws);
+  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_counter_bytes(S, H_kv));
+  float* ws_o = ws_ml + static_cast<int64_t>(S) * H_q * n_splits * 2;
   const float score_scale = sm_scale * kLog2e * k_scale;
   dim3 grid((n_splits + kDecodeWaves - 1) / kDecodeWaves, H_kv, S);
-  hipLaunchKernelGGL((decode_split_kernel<CacheT, D>), grid, dim3(kWave * kDecodeWaves), 0, st,
-                     static_cast<const uint16_t*>(q),
+  hipLaunchKernelGGL((decode_kernel<CacheT, D>), grid, dim3(kWave * kDecodeWaves), 0, st,
+                     static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
                      static_cast<const typename CacheT::raw*>(k_cache),
                      static_cast<const typename CacheT::raw*>(v_cache), block_tables, max_blocks,
-                     num_blocks, context_lens, H_q, H_kv, H_q / H_kv, n_splits, score_scale, ws_o,
-                     ws_ml);
+                     num_blocks, context_lens, H_q, H_kv, H_q / H_kv, n_splits, score_scale,
+                     v_scale, counters, ws_ml, ws_o);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
-    return fail(PA_ERR_DEVICE, "pa_decode: split launch failed: %s", hipGetErrorString(e));
-  const int64_t rows = static_cast<int64_t>(S) * H_q;
-  hipLaunchKernelGGL((decode_combine_kernel<BF16, D>), dim3((rows + 3) / 4), dim3(256), 0, st,
-                     static_cast<uint16_t*>(out), ws_o, ws_ml, context_lens, max_blocks, S, H_q,
-                     n_splits, v_scale);
-  e = hipGetLastError();
-  if (e != hipSuccess)
-    return fail(PA_ERR_DEVICE, "pa_decode: combine launch failed: %s", hipGetErrorString(e));
+    return fail(PA_ERR_DEVICE, "pa_decode: launch failed: %s", hipGetErrorString(e));
   return PA_OK;
 }
 
@@ -337,9 +357,9 @@ static bool decode_uses_mfma(pa_dtype q_dt, pa_dtype cache_dt, int32_t H_q, int3
 extern "C" size_t pa_decode_workspace_bytes(int32_t S, int32_t H_q, int32_t H_kv, int32_t D,
                                             int32_t max_context_len) {
   if (S <= 0 || H_q <= 0 || D <= 0) return 0;
-  (void)H_kv;
   const int64_t n_splits = decode_num_splits(max_context_len);
-  return static_cast<size_t>(S) * H_q * n_splits * (D + 2) * sizeof(float);
+  return decode_counter_bytes(S, H_kv) +
+         static_cast<size_t>(S) * H_q * n_splits * (D + 2) * sizeof(float);
 }
 
 extern "C" pa_status pa_decode(void* stream, void* out, pa_dtype out_dt, const void* q,

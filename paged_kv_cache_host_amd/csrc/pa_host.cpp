@@ -180,6 +180,21 @@ pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_new, int32_t* slot
   return PA_OK;
 }
 
+pa_status pa_batch_append(pa_pool* pool, const int64_t* seqs, int32_t n_seqs, int32_t n_new,
+                          int32_t* slots_out, int32_t* n_done) {
+  if (!pool || !n_done || n_seqs < 0 || n_new < 0 || (n_seqs > 0 && !seqs))
+    return fail(PA_ERR_INVALID, "pa_batch_append: bad arguments");
+  *n_done = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    pa_status st =
+        pa_seq_append(pool, seqs[i], n_new,
+                      slots_out ? slots_out + static_cast<int64_t>(i) * n_new : nullptr);
+    if (st != PA_OK) return st;
+    *n_done = i + 1;
+  }
+  return PA_OK;
+}
+
 pa_status pa_seq_slots(const pa_pool* pool, int64_t seq, int32_t start, int32_t n,
                        int32_t* slots_out) {
   if (!pool || (n > 0 && !slots_out)) return fail(PA_ERR_INVALID, "pa_seq_slots: NULL argument");

@@ -119,8 +119,10 @@ class PagedKV:
 
 
 def decode_workspace(S, h_q, h_kv, d, max_context_len, device="cuda") -> torch.Tensor | None:
+    """Zero-filled decode workspace (its completion counters must start at
+    zero; the kernel leaves them zero after every call)."""
     n = pa.pa_decode_workspace_bytes(S, h_q, h_kv, d, max_context_len)
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def prefill_workspace(n_chunks, max_q_len, h_q, h_kv, d, max_context_len, device="cuda"):

@@ -109,6 +109,24 @@ def test_bit_exact_against_oracle(oplist, nblocks, rnd):
         pa.pa_pool_destroy(pool)
 
 
+def test_batch_append_matches_oracle_and_stops_at_failure():
+    st_, pool = pa.pa_pool_create(5, 16, [4, 3, 2, 1, 0])
+    ref = oa.BlockPool(5, 16, [4, 3, 2, 1, 0])
+    try:
+        for s, n in [(10, 16), (11, 5), (12, 32)]:
+            assert pa.pa_seq_create(pool, s, n) == ref.seq_create(s, n) == pa.PA_OK
+        # 10 crosses a boundary (takes 1), 11 does not, 12 needs one more: none left
+        st2, done, slots = pa.pa_batch_append(pool, [11, 10, 12], 1)
+        assert st2 == pa.PA_ERR_NO_BLOCKS and done == 2
+        exp = [ref.seq_append(11, 1)[1], ref.seq_append(10, 1)[1]]
+        assert slots[:2].tolist() == exp
+        assert ref.seq_append(12, 1)[0] == oa.ERR_NO_BLOCKS
+        assert _state(pool) == ref.free_list()
+        assert pa.pa_seq_length(pool, 12) == (pa.PA_OK, 32)
+    finally:
+        pa.pa_pool_destroy(pool)
+
+
 def test_error_paths_leave_state_unchanged():
     st_, pool = pa.pa_pool_create(3, 16, [2, 0, 1])
     assert st_ == pa.PA_OK
@@ -161,7 +179,7 @@ def test_argument_validation_of_kernel_entry_points_on_host():
     fake = 0x1000
     assert pa._pa._lib.pa_decode(None, fake, 1, fake, 1, fake, fake, 1, fake, 4, 4, fake,
                                  1, 64, 8, 128, 16, 100, 0.1, 1.0, 1.0, None, 0) == pa.PA_ERR_WORKSPACE
-    assert pa.pa_decode_workspace_bytes(2, 64, 8, 128, 600) == 2 * 64 * 3 * 130 * 4
+    assert pa.pa_decode_workspace_bytes(2, 64, 8, 128, 600) == 256 + 2 * 64 * 3 * 130 * 4
     assert pa._pa._lib.pa_cache_write(None, None, None, 1, None, 4, None, None, 0, 4, 8, 128, 16,
                                       1.0, 1.0) == pa.PA_ERR_INVALID
     assert pa._pa._lib.pa_cache_write(None, fake, fake, 1, fake, 4, fake, fake, 2, 4, 8, 128, 16,

@@ -92,12 +92,19 @@ def _amax_scale(raw_bf16: np.ndarray) -> float:
     return float(np.float32(amax) / np.float32(448.0))
 
 
-def decode_workload(name, seed, lengths_fn, h_q, h_kv, d, kv_dtype, cache_dtype,
-                    pool_fn, q_dtype=None) -> DecodeWorkload:
+def decode_layout(seed, lengths_fn, pool_fn):
+    """The first draws of a decode workload: (lengths, pool size, free
+    order), identical to those of ``decode_workload`` with the same seed."""
     rng = np.random.default_rng(seed)
     lengths = lengths_fn(rng)
     num_blocks = int(pool_fn(lengths))
     free_order = rng.permutation(num_blocks).astype(np.int32)
+    return rng, lengths, num_blocks, free_order
+
+
+def decode_workload(name, seed, lengths_fn, h_q, h_kv, d, kv_dtype, cache_dtype,
+                    pool_fn, q_dtype=None) -> DecodeWorkload:
+    rng, lengths, num_blocks, free_order = decode_layout(seed, lengths_fn, pool_fn)
     ntok = int(lengths.sum())
     k_tok = normal_raw(rng, (ntok, h_kv, d), kv_dtype)
     v_tok = normal_raw(rng, (ntok, h_kv, d), kv_dtype)
@@ -124,6 +131,13 @@ def tiny_decode(seed: int = 1) -> DecodeWorkload:
         "tiny-decode-4seq-4h-d64-f32", seed,
         lambda rng: rng.integers(1, 201, size=4).astype(np.int64),
         4, 4, 64, "f32", "f32", lambda L: 64)
+
+
+def decode_70b_layout(seed: int = 2, num_seqs: int = 128):
+    """(lengths, pool size, free order) of ``decode_70b`` without its data."""
+    _, lengths, nb, order = decode_layout(seed, lambda rng: lognormal_lengths(rng, num_seqs),
+                                          lambda L: math.ceil(1.1 * blocks_needed(L)))
+    return lengths, nb, order
 
 
 def decode_70b(seed: int = 2, num_seqs: int = 128) -> DecodeWorkload:
