@@ -33,16 +33,19 @@
  *     once per iteration (LESSON, "Continuous batching at the iteration
  *     level").
  *
- * KV cache layout (one layer; block size bs, KV heads H_kv, head dim D):
- *     K cache  [num_blocks][H_kv][bs][D]   a token's key is one row
- *     V cache  [num_blocks][H_kv][D][bs]   a token's value is one column
+ * KV cache layout (one layer; block size bs, KV heads H_kv, head dim D;
+ * x = elements per 16 bytes of the cache type: 4 fp32, 8 bf16, 16 fp8):
+ *     K cache  [num_blocks][H_kv][D/x][bs][x]   dims d..d+x-1 of the bs tokens
+ *                                               of a block side by side
+ *     V cache  [num_blocks][H_kv][D][bs]        a token's value is a column
  * Token position p of a sequence lives in physical block table[p / bs] at
  * offset p % bs (LESSON, "PagedAttention as a virtual memory system"); its
  * flat slot is table[p / bs] * bs + p % bs.  The ARTICLE (2.2) shapes both
  * pools [num_blocks, block_size, num_heads, head_dim]; the axis order inside
- * a pool is this library's choice (each (block, head) pair is one contiguous
- * tile, and values are stored token-minor so that the P*V contraction reads
- * contiguous runs of tokens).
+ * a pool is this library's choice: each (block, head) pair is one contiguous
+ * tile, one 16-byte chunk of K for the 16 tokens is 256 contiguous bytes
+ * (the operand of one matrix instruction), and values are stored token-minor
+ * so that the P*V contraction reads contiguous runs of tokens.
  *
  * Supported envelope of the attention kernels (else PA_ERR_INVALID):
  *   bs == 16; D in {64, 128}; H_q % H_kv == 0; (q, cache, out) element types
@@ -200,10 +203,9 @@ pa_status pa_cache_write(void* stream, const void* k_new, const void* v_new, pa_
  *   grid; no device-to-host read is needed).
  * sm_scale: softmax scale (normally 1/sqrt(D)).  k_scale, v_scale: fp8
  *   per-tensor scales (ignored otherwise).
- * ws [device, ws_bytes]: scratch for split partials, at least
- *   pa_decode_workspace_bytes(...) bytes; else PA_ERR_WORKSPACE.  Its first
- *   bytes hold per-(sequence, KV head) completion counters: the whole
- *   workspace must be zero-filled before its first use, and every call
+ * ws [device, ws_bytes]: scratch, at least pa_decode_workspace_bytes(...)
+ *   bytes; else PA_ERR_WORKSPACE.  Its first bytes are work counters: the
+ *   workspace must be zero-filled once before its first use, and every call
  *   leaves the counters zero again.  Calls that overlap in time must not
  *   share a workspace.
  * ---------------------------------------------------------------------- */

@@ -47,14 +47,14 @@ def gather(k_cache, v_cache, table, length: int, kv_head: int, cache_dtype: str,
            k_scale: float = 1.0, v_scale: float = 1.0):
     """Keys and values of positions 0..length-1 of one sequence and KV head,
     fetched through the block table, as fp64 [length, D] arrays."""
-    bs = k_cache.shape[2]
-    d = k_cache.shape[3]
+    bs = k_cache.shape[3]
+    d = v_cache.shape[2]
     pos = np.arange(length)
     blocks = np.asarray(table, dtype=np.int64)[pos // bs]
     if length and blocks.min() < 0:
         raise ValueError("block table shorter than the context")
     offs = pos % bs
-    k_raw = k_cache[blocks, kv_head, offs, :]            # [L, D]
+    k_raw = k_cache[blocks, kv_head, :, offs, :].reshape(length, d)   # [L, D]
     v_raw = v_cache[blocks, kv_head, :, offs]            # [L, D]
     k = codecs.decode(k_raw, cache_dtype)
     v = codecs.decode(v_raw, cache_dtype)

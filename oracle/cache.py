@@ -9,9 +9,10 @@ names one (block, offset) cell; writing a token means storing its K and V
 vectors for every KV head in that cell.
 
 Cache layout (the library's contract, per physical block ``b`` and KV head
-``h``):
-  K cache  [num_blocks][H_kv][bs][D]   -- a token's key is a contiguous row
-  V cache  [num_blocks][H_kv][D][bs]   -- a token's value is a column
+``h``; ``x`` = elements per 16 bytes: 4 for fp32, 8 for bf16, 16 for fp8):
+  K cache  [num_blocks][H_kv][D/x][bs][x]  -- key dims d..d+x-1 of the 16
+                                              tokens of a block are adjacent
+  V cache  [num_blocks][H_kv][D][bs]       -- a token's value is a column
 The ARTICLE (§2.2) shapes both pools ``[num_blocks, block_size, num_heads,
 head_dim]``; the order of the axes inside a pool is a layout choice that does
 not change what is stored, only where.
@@ -27,11 +28,17 @@ import numpy as np
 from . import codecs
 
 
+def chunk_elems(dtype: str) -> int:
+    """Elements per 16-byte chunk of the K layout."""
+    return 16 // np.dtype(codecs.storage_numpy_dtype(dtype)).itemsize
+
+
 def new_cache(num_blocks: int, h_kv: int, bs: int, d: int, dtype: str):
     """Zero-filled K and V pools in storage dtype (ARTICLE §2.2 allocates
     the pools once, zero-initialised)."""
     nd = codecs.storage_numpy_dtype(dtype)
-    k = np.zeros((num_blocks, h_kv, bs, d), dtype=nd)
+    x = chunk_elems(dtype)
+    k = np.zeros((num_blocks, h_kv, d // x, bs, x), dtype=nd)
     v = np.zeros((num_blocks, h_kv, d, bs), dtype=nd)
     return k, v
 
@@ -49,7 +56,8 @@ def encode_for_cache(x_raw: np.ndarray, new_dtype: str, cache_dtype: str, scale:
 def cache_write(k_cache, v_cache, k_new_raw, v_new_raw, slots, new_dtype, cache_dtype,
                 k_scale=1.0, v_scale=1.0):
     """In-place scatter.  ``k_new_raw``, ``v_new_raw``: [n, H_kv, D] raw."""
-    bs = k_cache.shape[2]
+    bs = k_cache.shape[3]
+    h_kv, nchunk, x = k_cache.shape[1], k_cache.shape[2], k_cache.shape[4]
     kq = encode_for_cache(k_new_raw, new_dtype, cache_dtype, k_scale)
     vq = encode_for_cache(v_new_raw, new_dtype, cache_dtype, v_scale)
     slots = np.asarray(slots, dtype=np.int64)
@@ -58,5 +66,5 @@ def cache_write(k_cache, v_cache, k_new_raw, v_new_raw, slots, new_dtype, cache_
     if len(np.unique(live)) != len(live):
         raise ValueError("slots of one write must be distinct")
     b, o = live // bs, live % bs
-    k_cache[b, :, o, :] = kq[keep]
+    k_cache[b, :, :, o, :] = kq[keep].reshape(-1, h_kv, nchunk, x)
     v_cache[b, :, :, o] = vq[keep]

@@ -4,182 +4,250 @@
 // finds a query's K/V blocks through block_tables up to context_lens,
 // computes scores within a block and accumulates across blocks.  Here the
 // accumulation is an online softmax (running max m, running sum l,
-// unnormalised output o) and the blocks of a long context are cut into
-// fixed-length splits processed by different waves; a second kernel merges
-// the split partials exactly:
+// unnormalised output o).  The 2-block steps of a context are spread over
+// the 8 waves of a work-group, whose states are merged exactly through LDS:
 //     m* = max_j m_j,  l* = sum_j l_j 2^(m_j - m*),
 //     out = sum_j o_j 2^(m_j - m*) / l*.
-// (Scores are kept in base 2: s = sm_scale * log2(e) * q.k, so exp becomes
-// the hardware exp2.)
+// A context longer than one work-group's chunk (2048 tokens) is cut into
+// chunks; each leaves one merged partial in the workspace and a small second
+// kernel applies the same merge across chunks.  (Merging inside the
+// work-group keeps partial results off HBM: written in the middle of the
+// read stream they cost far more than their size.)  Scores are kept in base
+// 2 (s = sm_scale * log2(e) * q.k) so that the exponential is the hardware
+// exp2.
 //
-// Grouped-query heads (query head h reads KV head h / G, G = H_q / H_kv) share
-// every K/V byte: one wave computes all G heads of its KV head, so each
+// Grouped-query heads (query head h reads KV head h / G, G = H_q / H_kv)
+// share every K/V byte: one wave computes all G heads of its KV head, so each
 // K/V tile is read from HBM once per KV head.
 //
-// Matrix-core mapping (gfx950 v_mfma_f32_16x16x32_bf16, wave64):
+// Matrix-core mapping (gfx950, wave64), one step = two 16-token blocks:
 //   scores  S^T[token][head] = K[token][:] . Q^T[:][head]
-//           A = K tile (16 tokens x 32 dims per step), B = Q^T (32 dims x 16
-//           head columns, heads >= G zero-padded)
+//           v_mfma_f32_16x16x32_bf16, A = one block's K (16 tokens x 32 dims
+//           per MFMA), B = Q^T (32 dims x 16 head columns; heads >= G are
+//           zero columns).  Lane (c = l % 16, g = l / 16) receives the scores
+//           of tokens 4g..4g+3 for head c.
 //   output  O^T[d][head] += V^T[d][token] . P^T[token][head]
-//           A = V^T (16 dims x 32 tokens) read straight from the token-minor
-//           V tile, B = P^T taken from the score registers without any
-//           lane exchange.
-// Two 16-token blocks (32 tokens) form one step.  Lane l (c = l % 16,
-// g = l / 16) holds, after the score products, the scores of 8 consecutive
-// positions of head column c: block (g < 2 ? first : second), tokens
-// 8 * (g % 2) + 0..7.  The K rows are assigned to MFMA rows so that this
-// holds: score tile X row 4a + r is token 8 * (a % 2) + r of block a / 2,
-// tile Y row 4a + r is that token + 4.
-//
-// Every lane loads 16 contiguous bytes per operand (bf16) straight from HBM
-// into the operand registers; the next step's tiles are loaded while the
-// current step computes.
+//           v_mfma_f32_16x16x16_bf16 per block: A = V^T (16 dims x 16
+//           tokens), B = P^T, which is exactly the score registers (tokens
+//           4g..4g+3 of head c) after the softmax update; no lane exchange.
+// Loads: a block's K tile is stored as 16-byte chunks of its 16 tokens side
+// by side ([D/x][16][x]), so the K operand of one MFMA step is one 1 KiB
+// contiguous read (lane = token, lane group = chunk); the V tile is stored
+// token-minor ([D][16]), so a lane's 4 tokens of one dim are 8 contiguous
+// bytes and a 16-dim slice of the tile is one 512-byte read.  The data is
+// read once, so all K/V loads are non-temporal.
 #include "pa_device.h"
 #include "pa_internal.h"
 
+#include <algorithm>
+
 namespace pa {
 
-constexpr int kDecodeWaves = 4;       // waves per work-group, one split each
-constexpr int kSplitTokens = 256;     // tokens per split (a multiple of 32)
-constexpr int kSplitBlocks = kSplitTokens / kBlock;
+constexpr int kDecodeWaves = 8;                  // waves per work-group
+constexpr int kChunkTokens = 2048;               // tokens per work-group
+constexpr int kChunkBlocks = kChunkTokens / kBlock;
+constexpr int kMaxGroup = 16;                    // query heads per KV head (MFMA columns)
+constexpr int kMaxSeqsPerLaunch = 4096;          // item prefix kept in LDS
+constexpr int kThreads = kWave * kDecodeWaves;
 
-inline int32_t decode_num_splits(int32_t max_context_len) {
+inline int32_t decode_num_chunks(int32_t max_context_len) {
   const int32_t nblk = (max_context_len + kBlock - 1) / kBlock;
-  return nblk <= 0 ? 1 : (nblk + kSplitBlocks - 1) / kSplitBlocks;
+  return nblk <= 0 ? 1 : (nblk + kChunkBlocks - 1) / kChunkBlocks;
 }
 
-// Dimension index of k-slot group (step s, lane group g) in a D-vector: the
-// 8 consecutive dims a lane feeds to one MFMA.  bf16 rows: each step covers a
-// 64-byte run per token row (4 lane groups side by side); fp8 rows: a lane's
-// D/32 steps cover one run of D/4 bytes.
-template <typename CacheT, int D>
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// First dim of the 8 that lane group g feeds to score MFMA step s (the same
+// map is used for K and Q, so any consistent choice gives q.k).
+//   bf16: chunk (4s + g) of 8 dims;
+//   fp8:  16-dim chunk (g + 4 * (s/2)), half (s % 2).
+template <typename CacheT>
 __device__ __forceinline__ int kdim(int s, int g) {
   if constexpr (sizeof(typename CacheT::raw) == 1)
-    return (D / 4) * g + 8 * s;
+    return 16 * (g + 4 * (s >> 1)) + 8 * (s & 1);
   else
     return 32 * s + 8 * g;
 }
 
 template <typename CacheT, int D>
-struct StepRegs;
+struct BlockRegs;
 
 template <int D>
-struct StepRegs<BF16, D> {
-  bf16x8 kx[D / 32], ky[D / 32], v[D / 16];
+struct BlockRegs<BF16, D> {
+  u32x4 k[D / 32];  // one 16-byte chunk per score step
+  u32x2 v[D / 16];  // 4 tokens of one dim per 16-dim slice
 };
 
 template <int D>
-struct StepRegs<FP8, D> {
-  u32x4 kx[D / 64], ky[D / 64];  // D/4 fp8 codes per lane per tile
-  u32x2 v[D / 16];
+struct BlockRegs<FP8, D> {
+  u32x4 k[D / 64];  // one 16-byte chunk per two score steps
+  uint32_t v[D / 16];
 };
 
 template <typename CacheT, int D>
-__device__ __forceinline__ void load_step(StepRegs<CacheT, D>& r,
-                                          const typename CacheT::raw* __restrict__ k_cache,
-                                          const typename CacheT::raw* __restrict__ v_cache,
-                                          int64_t tile_a, int64_t tile_b, int c, int g) {
-  // K rows: tile X row c -> token 8*((c>>2)&1) + (c&3) of block (c>>3 ? b : a)
-  const int krow_blk = c >> 3;
-  const int ktok = 8 * ((c >> 2) & 1) + (c & 3);
-  const int64_t ktile = krow_blk ? tile_b : tile_a;
-  const typename CacheT::raw* kx = k_cache + ktile * (kBlock * D) + ktok * D;
-  const typename CacheT::raw* ky = kx + 4 * D;
-  // V: lane group g reads block (g >> 1), tokens 8*(g&1) .. +8 of row d
-  const int64_t vtile = (g >> 1) ? tile_b : tile_a;
-  const typename CacheT::raw* vp = v_cache + vtile * (kBlock * D) + c * kBlock + 8 * (g & 1);
-  if constexpr (sizeof(typename CacheT::raw) == 2) {
+__device__ __forceinline__ void load_block(BlockRegs<CacheT, D>& r,
+                                           const typename CacheT::raw* __restrict__ k_cache,
+                                           const typename CacheT::raw* __restrict__ v_cache,
+                                           int64_t tile, int c, int g) {
+  using R = typename CacheT::raw;
+  constexpr int X = 16 / sizeof(R);
+  const R* kt = k_cache + tile * (kBlock * D);
+  const R* vt = v_cache + tile * (kBlock * D) + c * kBlock + 4 * g;
+  if constexpr (sizeof(R) == 2) {
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      r.kx[s] = *reinterpret_cast<const bf16x8*>(kx + kdim<CacheT, D>(s, g));
-      r.ky[s] = *reinterpret_cast<const bf16x8*>(ky + kdim<CacheT, D>(s, g));
-    }
+    for (int s = 0; s < D / 32; ++s)
+      r.k[s] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kt + ((4 * s + g) * kBlock + c) * X));
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
-      r.v[t] = *reinterpret_cast<const bf16x8*>(vp + 16 * t * kBlock);
+      r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vt + 16 * t * kBlock));
   } else {
 #pragma unroll
-    for (int s = 0; s < D / 64; ++s) {
-      r.kx[s] = *reinterpret_cast<const u32x4*>(kx + (D / 4) * g + 16 * s);
-      r.ky[s] = *reinterpret_cast<const u32x4*>(ky + (D / 4) * g + 16 * s);
-    }
+    for (int s = 0; s < D / 64; ++s)
+      r.k[s] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kt + ((g + 4 * s) * kBlock + c) * X));
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
-      r.v[t] = *reinterpret_cast<const u32x2*>(vp + 16 * t * kBlock);
+      r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vt + 16 * t * kBlock));
   }
 }
 
 template <typename CacheT, int D>
-__device__ __forceinline__ bf16x8 k_operand(const StepRegs<CacheT, D>& r, bool y, int s) {
+__device__ __forceinline__ bf16x8 k_operand(const BlockRegs<CacheT, D>& r, int s) {
   if constexpr (sizeof(typename CacheT::raw) == 2) {
-    return y ? r.ky[s] : r.kx[s];
+    return __builtin_bit_cast(bf16x8, r.k[s]);
   } else {
-    // fp8: kdim = (D/4)*g + 8*s -> step s is dwords (2s, 2s+1) of the lane's run
-    const u32x4 w = y ? r.ky[s >> 1] : r.kx[s >> 1];
-    u32x2 pair;
-    pair[0] = (s & 1) ? w[2] : w[0];
-    pair[1] = (s & 1) ? w[3] : w[1];
-    return fp8x8_to_bf16x8(pair);
+    const u32x4 w = r.k[s >> 1];
+    u32x2 half;
+    half[0] = (s & 1) ? w[2] : w[0];
+    half[1] = (s & 1) ? w[3] : w[1];
+    return fp8x8_to_bf16x8(half);
   }
 }
 
 template <typename CacheT, int D>
-__device__ __forceinline__ bf16x8 v_operand(const StepRegs<CacheT, D>& r, int t) {
-  if constexpr (sizeof(typename CacheT::raw) == 2)
-    return r.v[t];
-  else
-    return fp8x8_to_bf16x8(r.v[t]);
-}
-
-// Workspace of the matrix-core path: completion counters (one int32 per
-// (sequence, KV head), zero between calls), then per (sequence, query head,
-// split) the running max and sum (2 floats) and the unnormalised output
-// (D floats).
-inline size_t decode_counter_bytes(int32_t S, int32_t H_kv) {
-  return (static_cast<size_t>(S) * H_kv * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+__device__ __forceinline__ bf16x4 v_operand(const BlockRegs<CacheT, D>& r, int t) {
+  if constexpr (sizeof(typename CacheT::raw) == 2) {
+    return __builtin_bit_cast(bf16x4, r.v[t]);
+  } else {
+    bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.v[t], 1.0f, false);
+    bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.v[t], 1.0f, true);
+    bf16x4 o;
+    o[0] = lo[0];
+    o[1] = lo[1];
+    o[2] = hi[0];
+    o[3] = hi[1];
+    return o;
+  }
 }
 
 template <typename OutT>
 __device__ __forceinline__ void store_out4(typename OutT::raw* dst, f32x4 v) {
   if constexpr (sizeof(typename OutT::raw) == 2) {
     u32x2 w;
-    w[0] = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-    w[1] = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    w[0] = static_cast<uint32_t>(f32_to_bf16(v[0])) |
+           (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    w[1] = static_cast<uint32_t>(f32_to_bf16(v[2])) |
+           (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
     *reinterpret_cast<u32x2*>(dst) = w;
   } else {
     *reinterpret_cast<f32x4*>(dst) = v;
   }
 }
 
-// grid: (ceil(n_splits / kDecodeWaves), H_kv, S); block: 64 * kDecodeWaves.
-// Wave w of work-group x handles split x * kDecodeWaves + w of (seq, kv head).
-// A context that fits one split is finished by its wave directly.  Otherwise
-// each wave stores its partial (m, l, o) and bumps the (seq, kv head)
-// counter; the wave that arrives last merges all partials and writes the
-// output, then clears the counter for the next call.
+// Persistent kernel: grid = as many work-groups as fit on the device at once.
+// The work items are (sequence, KV head, chunk) for every chunk that holds
+// part of a context; each work-group computes the item prefix sum over the
+// context lengths in LDS, then takes items in turn from a ticket counter in
+// the workspace (the next ticket is fetched while the current item runs).
+// Its waves take the 2-block steps of the item's chunk in turn (wave w: steps
+// w, w + W, ...) and merge their running (m, l, o) through LDS.  A context
+// that fits one chunk gets its output here; longer ones leave one partial per
+// chunk for the merge kernel.  The last work-group to finish resets the
+// ticket counters, so they are zero again for the next call.
 template <typename CacheT, int D>
-__global__ __launch_bounds__(kWave* kDecodeWaves) void decode_kernel(
+__global__ __launch_bounds__(kThreads) void decode_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const typename CacheT::raw* __restrict__ k_cache,
     const typename CacheT::raw* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    int32_t max_blocks, int32_t num_blocks, const int32_t* __restrict__ context_lens,
-    int32_t H_q, int32_t H_kv, int32_t G, int32_t n_splits, float score_scale, float out_scale,
+    int32_t max_blocks, int32_t num_blocks, const int32_t* __restrict__ context_lens, int32_t S,
+    int32_t H_q, int32_t H_kv, int32_t G, int32_t n_chunks, float score_scale, float out_scale,
     int32_t* __restrict__ counters, float* __restrict__ ws_ml, float* __restrict__ ws_o) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  __shared__ float lds_o[kDecodeWaves][kMaxGroup][D];
+  __shared__ float lds_ml[kDecodeWaves][kMaxGroup][2];
+  __shared__ int32_t pre[kMaxSeqsPerLaunch + 1];
+  __shared__ int32_t wave_sums[kDecodeWaves];
+  __shared__ int32_t s_item;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int c = lane & 15;
   const int g = lane >> 4;
-  const int split = blockIdx.x * kDecodeWaves + wave;
-  const int kvh = blockIdx.y;
-  const int seq = blockIdx.z;
-  if (split >= n_splits) return;
+
+  // items of sequence i: H_kv * (chunks holding part of its context)
+  auto items_of = [&](int32_t i) -> int32_t {
+    const int32_t Li = min(context_lens[i], max_blocks * kBlock);
+    if (Li <= 0) return 0;
+    const int32_t nb = (Li + kBlock - 1) / kBlock;
+    return H_kv * min(n_chunks, (nb + kChunkBlocks - 1) / kChunkBlocks);
+  };
+  // exclusive prefix over the sequences, kThreads at a time
+  int32_t carry = 0;
+  for (int32_t base = 0; base < S; base += kThreads) {
+    const int32_t i = base + tid;
+    int32_t v = i < S ? items_of(i) : 0;
+    int32_t x = v;  // inclusive scan inside the wave
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int32_t y = __shfl_up(x, o, kWave);
+      if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) wave_sums[wave] = x;
+    __syncthreads();
+    int32_t before = carry;
+    for (int w = 0; w < wave; ++w) before += wave_sums[w];
+    if (i < S) pre[i] = before + x - v;
+    int32_t tot = 0;
+    for (int w = 0; w < kDecodeWaves; ++w) tot += wave_sums[w];
+    carry += tot;
+    __syncthreads();
+  }
+  if (tid == 0) pre[S] = carry;
+  const int32_t total = carry;
+
+  int32_t next = 0;
+  if (tid == 0) next = atomicAdd(&counters[0], 1);
+  while (true) {
+    if (tid == 0) s_item = next;
+    __syncthreads();
+    const int32_t item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item >= total) break;
+    if (tid == 0) next = atomicAdd(&counters[0], 1);
+    // item -> (seq, kvh, chunk): last seq with pre[seq] <= item
+    int32_t lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= item)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int seq = __builtin_amdgcn_readfirstlane(lo);
+    const int32_t r = item - pre[seq];
+    const int32_t n_valid = (pre[seq + 1] - pre[seq]) / H_kv;
+    const int kvh = __builtin_amdgcn_readfirstlane(r / n_valid);
+    const int chunk = __builtin_amdgcn_readfirstlane(r % n_valid);
 
   const int32_t L = min(context_lens[seq], max_blocks * kBlock);
   const int32_t nblk = (L + kBlock - 1) / kBlock;
-  const int32_t b0 = split * kSplitBlocks;
-  if (L <= 0 || b0 >= nblk) return;
-  const int32_t n_valid = min(n_splits, (nblk + kSplitBlocks - 1) / kSplitBlocks);
-  const int32_t b1 = (split == n_splits - 1) ? nblk : min(nblk, b0 + kSplitBlocks);
+  const int32_t c0 = chunk * kChunkBlocks;
+  const int32_t b1 = (chunk == n_chunks - 1) ? nblk : min(nblk, c0 + kChunkBlocks);
   const int32_t* __restrict__ table = block_tables + static_cast<int64_t>(seq) * max_blocks;
 
   // Q^T operand: column c = head kvh*G + c, zero for padded columns.
@@ -189,7 +257,7 @@ __global__ __launch_bounds__(kWave* kDecodeWaves) void decode_kernel(
     const uint16_t* qp = q + (static_cast<int64_t>(seq) * H_q + kvh * G + (live ? c : 0)) * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + kdim<CacheT, D>(s, g));
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + kdim<CacheT>(s, g));
       qb[s] = live ? v : bf16x8{};
     }
   }
@@ -204,111 +272,211 @@ __global__ __launch_bounds__(kWave* kDecodeWaves) void decode_kernel(
     return static_cast<int64_t>(safe_block(table[b], num_blocks)) * H_kv + kvh;
   };
 
-  StepRegs<CacheT, D> cur, nxt;
-  int32_t p = b0;
-  {
-    const int64_t ta = tile_of(p);
-    const int64_t tb = (p + 1 < b1) ? tile_of(p + 1) : ta;
-    load_step<CacheT, D>(cur, k_cache, v_cache, ta, tb, c, g);
-  }
-  for (; p < b1; p += 2) {
-    const int32_t pn = p + 2;
-    if (pn < b1) {
-      const int64_t ta = tile_of(pn);
-      const int64_t tb = (pn + 1 < b1) ? tile_of(pn + 1) : ta;
-      load_step<CacheT, D>(nxt, k_cache, v_cache, ta, tb, c, g);
-    }
-    // scores of the 32 tokens of this step
-    f32x4 sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
+  // One step: blocks p and p+1 (the second is absent when p+1 == b1; its
+  // loads then repeat block p's and all its positions are masked).
+  //
+  // Softmax reference: weights are exp2(score - m_run) with a reference
+  // m_run that is only raised when some score of the step exceeds it by more
+  // than kLazy (log2 units).  Softmax does not depend on the reference, so
+  // the result is unchanged up to rounding, while every weight stays below
+  // 2^kLazy; most steps then need neither the cross-lane max nor a rescale of
+  // the accumulators.
+  constexpr float kLazy = 8.0f;
+  auto compute = [&](const BlockRegs<CacheT, D>& ra, const BlockRegs<CacheT, D>& rb, int32_t p) {
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      sx = mfma16x16x32(k_operand(cur, false, s), qb[s], sx);
-      sy = mfma16x16x32(k_operand(cur, true, s), qb[s], sy);
+      sa = mfma16x16x32(k_operand(ra, s), qb[s], sa);
+      sb = mfma16x16x32(k_operand(rb, s), qb[s], sb);
     }
-    const int32_t pos0 = (p + (g >> 1)) * kBlock + 8 * (g & 1);
+    const int32_t pa_ = p * kBlock + 4 * g;
+    const int32_t pb_ = pa_ + kBlock;
+    const bool tail = (p + 2) * kBlock > L;  // wave-uniform
     float sc[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sc[j] = (pos0 + j < L) ? sx[j] * score_scale : -__builtin_inff();
-      sc[j + 4] = (pos0 + 4 + j < L) ? sy[j] * score_scale : -__builtin_inff();
+      sc[j] = sa[j];
+      sc[j + 4] = sb[j];
     }
-    float mx = sc[0];
+    if (tail) {
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    bf16x8 pb;
+      for (int j = 0; j < 4; ++j) {
+        sc[j] = (pa_ + j < L) ? sc[j] : -__builtin_inff();
+        sc[j + 4] = (pb_ + j < L) ? sc[j + 4] : -__builtin_inff();
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    mx *= score_scale;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) o[t] *= alpha;
+      m_run = m_new;
+    }
+    bf16x4 pa4, pb4;
     float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float e = __builtin_amdgcn_exp2f(sc[j] - m_new);
-      psum += e;
-      pb[j] = static_cast<__bf16>(e);
+    for (int j = 0; j < 4; ++j) {
+      const float ea = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j], score_scale, -m_run));
+      const float eb = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j + 4], score_scale, -m_run));
+      psum += ea + eb;
+      pa4[j] = static_cast<__bf16>(ea);
+      pb4[j] = static_cast<__bf16>(eb);
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
+    if (tail) {
+      // positions past the context carry zero weight; their stored values
+      // may be anything (a reused block), so they are zeroed in the operand
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      o[t] *= alpha;
-      o[t] = mfma16x16x32(v_operand(cur, t), pb, o[t]);
+      for (int t = 0; t < D / 16; ++t) {
+        bf16x4 va = v_operand(ra, t), vb = v_operand(rb, t);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          va[j] = (pa_ + j < L) ? va[j] : static_cast<__bf16>(0.f);
+          vb[j] = (pb_ + j < L) ? vb[j] : static_cast<__bf16>(0.f);
+        }
+        o[t] = mfma16x16x16(va, pa4, o[t]);
+        o[t] = mfma16x16x16(vb, pb4, o[t]);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        o[t] = mfma16x16x16(v_operand(ra, t), pa4, o[t]);
+        o[t] = mfma16x16x16(v_operand(rb, t), pb4, o[t]);
+      }
     }
-    cur = nxt;
+  };
+
+  // This wave's steps: blocks p = c0 + 2 * (wave + kDecodeWaves * i).  The
+  // second block's table entry is read at a clamped index (always in
+  // range) so that no load sits behind a branch.
+  for (int32_t p = c0 + 2 * wave; p < b1; p += 2 * kDecodeWaves) {
+    BlockRegs<CacheT, D> xa, xb;
+    load_block<CacheT, D>(xa, k_cache, v_cache, tile_of(p), c, g);
+    load_block<CacheT, D>(xb, k_cache, v_cache, tile_of(min(p + 1, b1 - 1)), c, g);
+    compute(xa, xb, p);
   }
+
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
-
-  const int64_t head_row = static_cast<int64_t>(seq) * H_q + kvh * G + c;  // valid if c < G
-  if (n_valid == 1) {
-    if (c < G) {
-      const float inv = out_scale / l_run;
+  // lane (c, g) holds o^T[d = 16t + 4g + r][head c]; a wave without steps
+  // holds m = -inf, l = 0, o = 0
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t)
-        store_out4<BF16>(out + head_row * D + 16 * t + 4 * g, o[t] * inv);
-    }
-    return;
+  for (int t = 0; t < D / 16; ++t)
+    *reinterpret_cast<f32x4*>(&lds_o[wave][c][16 * t + 4 * g]) = o[t];
+  if (g == 0) {
+    lds_ml[wave][c][0] = m_run;
+    lds_ml[wave][c][1] = l_run;
   }
-
-  const int64_t part = head_row * n_splits + split;
-  if (c < G) {
-    float* dst = ws_o + part * D;
+  __syncthreads();
+  // merge the waves: thread -> (head h, 4 consecutive dims)
+  constexpr int kPerHead = D / 4;
+  for (int item = threadIdx.x; item < G * kPerHead; item += kWave * kDecodeWaves) {
+    const int h = item / kPerHead;
+    const int d0 = 4 * (item % kPerHead);
+    float M = -__builtin_inff();
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * g) = o[t];
-    if (g == 0) {
-      ws_ml[part * 2 + 0] = m_run;
-      ws_ml[part * 2 + 1] = l_run;
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, lds_ml[w][h][0]);
+    float tot = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(lds_ml[w][h][0] - M);
+      tot += wt * lds_ml[w][h][1];
+      acc += wt * *reinterpret_cast<const f32x4*>(&lds_o[w][h][d0]);
+    }
+    const int64_t head_row = static_cast<int64_t>(seq) * H_q + kvh * G + h;
+    if (n_valid == 1) {
+      store_out4<BF16>(out + head_row * D + d0, acc * (out_scale / tot));
+    } else {
+      const int64_t part = head_row * n_chunks + chunk;
+      *reinterpret_cast<f32x4*>(ws_o + part * D + d0) = acc;
+      if (d0 == 0) {
+        ws_ml[part * 2 + 0] = M;
+        ws_ml[part * 2 + 1] = tot;
+      }
     }
   }
-  // publish the partial, then count this split as done
-  __threadfence();
-  int32_t* ctr = counters + static_cast<int64_t>(seq) * H_kv + kvh;
-  int32_t prev = 0;
-  if (lane == 0) prev = atomicAdd(ctr, 1);
-  prev = __shfl(prev, 0, kWave);
-  if (prev != n_valid - 1) return;
-  // last arrival: every other split's partial is visible after this fence
-  __threadfence();
-  if (lane == 0) atomicExch(ctr, 0);
-  if (c >= G) return;
-  const int64_t base = head_row * n_splits;
+  __syncthreads();  // LDS reads done before the next item overwrites it
+  }
+  // the last work-group out resets the counters for the next call
+  if (tid == 0) {
+    const int32_t done = atomicAdd(&counters[1], 1);
+    if (done == static_cast<int32_t>(gridDim.x) - 1) {
+      atomicExch(&counters[0], 0);
+      atomicExch(&counters[1], 0);
+    }
+  }
+}
+
+// grid: ceil(S * H_q / 4); block: 256 (one wave per (sequence, query head)).
+// Merges the chunk partials of sequences whose context spans several chunks.
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(
+    uint16_t* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
+    const int32_t* __restrict__ context_lens, int32_t max_blocks, int32_t S, int32_t H_q,
+    int32_t n_chunks, float out_scale) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (idx >= static_cast<int64_t>(S) * H_q) return;
+  const int seq = static_cast<int>(idx / H_q);
+  const int32_t L = min(context_lens[seq], max_blocks * kBlock);
+  const int32_t nblk = (L + kBlock - 1) / kBlock;
+  const int nsp = L <= 0 ? 0 : min(n_chunks, (nblk + kChunkBlocks - 1) / kChunkBlocks);
+  if (nsp == 1) return;  // written by the attention kernel
+  const float* ml = ws_ml + idx * n_chunks * 2;
+  const float* po = ws_o + idx * n_chunks * D;
   float M = -__builtin_inff();
-  for (int j = 0; j < n_valid; ++j) M = fmaxf(M, ws_ml[(base + j) * 2]);
+  for (int j = 0; j < nsp; ++j) M = fmaxf(M, ml[2 * j]);
   float tot = 0.f;
-  f32x4 acc[D / 16];
+  float acc[D / kWave];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < n_valid; ++j) {
-    const float w = __builtin_amdgcn_exp2f(ws_ml[(base + j) * 2] - M);
-    tot += w * ws_ml[(base + j) * 2 + 1];
-    const float* src = ws_o + (base + j) * D;
+  for (int i = 0; i < D / kWave; ++i) acc[i] = 0.f;
+  for (int j = 0; j < nsp; ++j) {
+    const float w = __builtin_amdgcn_exp2f(ml[2 * j] - M);
+    tot += w * ml[2 * j + 1];
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      acc[t] += w * *reinterpret_cast<const f32x4*>(src + 16 * t + 4 * g);
+    for (int i = 0; i < D / kWave; ++i) acc[i] += w * po[j * D + lane + kWave * i];
   }
-  const float inv = out_scale / tot;
+  const float inv = nsp ? out_scale / tot : 0.f;
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) store_out4<BF16>(out + head_row * D + 16 * t + 4 * g, acc[t] * inv);
+  for (int i = 0; i < D / kWave; ++i) out[idx * D + lane + kWave * i] = f32_to_bf16(acc[i] * inv);
+}
+
+inline int32_t decode_num_batches(int32_t S) {
+  return (S + kMaxSeqsPerLaunch - 1) / kMaxSeqsPerLaunch;
+}
+
+// Bytes of ticket counters at the front of the workspace (two int32 per
+// launch batch of up to kMaxSeqsPerLaunch sequences).
+inline size_t decode_counter_bytes(int32_t S) {
+  return (static_cast<size_t>(decode_num_batches(S)) * 2 * sizeof(int32_t) + 255) &
+         ~static_cast<size_t>(255);
+}
+
+// Work-groups of the persistent kernel that fit on the current device at
+// once (cached per device).
+template <typename CacheT, int D>
+static int32_t resident_work_groups() {
+  static int32_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<CacheT, D>, kThreads,
+                                                   0) != hipSuccess ||
+      cus <= 0 || per_cu <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  cached[dev] = cus * per_cu;
+  return cached[dev];
 }
 
 template <typename CacheT, int D>
@@ -318,21 +486,36 @@ static pa_status launch_decode_mfma(hipStream_t st, void* out, const void* q, co
                                     const int32_t* context_lens, int32_t S, int32_t H_q,
                                     int32_t H_kv, int32_t max_context_len, float sm_scale,
                                     float k_scale, float v_scale, void* ws) {
-  const int32_t n_splits = decode_num_splits(max_context_len);
+  const int32_t n_chunks = decode_num_chunks(max_context_len);
   int32_t* counters = static_cast<int32_t*>(ws);
-  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_counter_bytes(S, H_kv));
-  float* ws_o = ws_ml + static_cast<int64_t>(S) * H_q * n_splits * 2;
+  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_counter_bytes(S));
+  float* ws_o = ws_ml + static_cast<int64_t>(S) * H_q * n_chunks * 2;
   const float score_scale = sm_scale * kLog2e * k_scale;
-  dim3 grid((n_splits + kDecodeWaves - 1) / kDecodeWaves, H_kv, S);
-  hipLaunchKernelGGL((decode_kernel<CacheT, D>), grid, dim3(kWave * kDecodeWaves), 0, st,
-                     static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
-                     static_cast<const typename CacheT::raw*>(k_cache),
-                     static_cast<const typename CacheT::raw*>(v_cache), block_tables, max_blocks,
-                     num_blocks, context_lens, H_q, H_kv, H_q / H_kv, n_splits, score_scale,
-                     v_scale, counters, ws_ml, ws_o);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess)
-    return fail(PA_ERR_DEVICE, "pa_decode: launch failed: %s", hipGetErrorString(e));
+  const int32_t grid = resident_work_groups<CacheT, D>();
+  for (int32_t b = 0; b < decode_num_batches(S); ++b) {
+    const int64_t s0 = static_cast<int64_t>(b) * kMaxSeqsPerLaunch;
+    const int32_t sn = static_cast<int32_t>(std::min<int64_t>(kMaxSeqsPerLaunch, S - s0));
+    hipLaunchKernelGGL((decode_kernel<CacheT, D>), dim3(grid), dim3(kThreads), 0, st,
+                       static_cast<uint16_t*>(out) + s0 * H_q * D,
+                       static_cast<const uint16_t*>(q) + s0 * H_q * D,
+                       static_cast<const typename CacheT::raw*>(k_cache),
+                       static_cast<const typename CacheT::raw*>(v_cache),
+                       block_tables + s0 * max_blocks, max_blocks, num_blocks, context_lens + s0,
+                       sn, H_q, H_kv, H_q / H_kv, n_chunks, score_scale, v_scale, counters + 2 * b,
+                       ws_ml + s0 * H_q * n_chunks * 2, ws_o + s0 * H_q * n_chunks * D);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(PA_ERR_DEVICE, "pa_decode: launch failed: %s", hipGetErrorString(e));
+  }
+  if (n_chunks > 1) {
+    const int64_t rows = static_cast<int64_t>(S) * H_q;
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, st,
+                       static_cast<uint16_t*>(out), ws_ml, ws_o, context_lens, max_blocks, S, H_q,
+                       n_chunks, v_scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(PA_ERR_DEVICE, "pa_decode: merge launch failed: %s", hipGetErrorString(e));
+  }
   return PA_OK;
 }
 
@@ -351,15 +534,15 @@ using namespace pa;
 
 static bool decode_uses_mfma(pa_dtype q_dt, pa_dtype cache_dt, int32_t H_q, int32_t H_kv) {
   return q_dt == PA_BF16 && (cache_dt == PA_BF16 || cache_dt == PA_FP8_E4M3) &&
-         H_q / H_kv <= 16;
+         H_q / H_kv <= kMaxGroup;
 }
 
 extern "C" size_t pa_decode_workspace_bytes(int32_t S, int32_t H_q, int32_t H_kv, int32_t D,
                                             int32_t max_context_len) {
   if (S <= 0 || H_q <= 0 || D <= 0) return 0;
-  const int64_t n_splits = decode_num_splits(max_context_len);
-  return decode_counter_bytes(S, H_kv) +
-         static_cast<size_t>(S) * H_q * n_splits * (D + 2) * sizeof(float);
+  (void)H_kv;
+  const int64_t n_chunks = decode_num_chunks(max_context_len);
+  return decode_counter_bytes(S) + static_cast<size_t>(S) * H_q * n_chunks * (D + 2) * sizeof(float);
 }
 
 extern "C" pa_status pa_decode(void* stream, void* out, pa_dtype out_dt, const void* q,

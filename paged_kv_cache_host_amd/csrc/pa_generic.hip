@@ -71,9 +71,12 @@ __global__ __launch_bounds__(kWave) void attend_generic_kernel(
     if (key < limit) {
       const int64_t tile =
           static_cast<int64_t>(safe_block(table[key / kBlock], num_blocks)) * H_kv + kvh;
-      const int64_t kb = tile * kBlock * D + static_cast<int64_t>(key % kBlock) * D;
+      // K tile layout [D/X][16][X]: dim d of token o at (d/X)*16*X + o*X + d%X
+      constexpr int X = 16 / sizeof(typename CacheT::raw);
+      const int64_t kb = tile * kBlock * D + static_cast<int64_t>(key % kBlock) * X;
       float dot = 0.f;
-      for (int d = 0; d < D; ++d) dot += q_s[d] * load_f<CacheT>(k_cache, kb + d);
+      for (int d = 0; d < D; ++d)
+        dot += q_s[d] * load_f<CacheT>(k_cache, kb + (d / X) * (kBlock * X) + d % X);
       s = dot * score_scale;
     }
     const float m_new = fmaxf(m_run, wave_max(s));

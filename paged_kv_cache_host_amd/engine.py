@@ -59,7 +59,8 @@ class PagedKV:
         self.k_scale = float(k_scale)
         self.v_scale = float(v_scale)
         dt = _TORCH_STORAGE[cache_dtype]
-        self.k = torch.zeros((num_blocks, h_kv, BLOCK, d), dtype=dt, device=device)
+        x = 16 // torch.empty((), dtype=dt).element_size()   # elements per 16-byte chunk
+        self.k = torch.zeros((num_blocks, h_kv, d // x, BLOCK, x), dtype=dt, device=device)
         self.v = torch.zeros((num_blocks, h_kv, d, BLOCK), dtype=dt, device=device)
 
     def close(self):
@@ -119,8 +120,8 @@ class PagedKV:
 
 
 def decode_workspace(S, h_q, h_kv, d, max_context_len, device="cuda") -> torch.Tensor | None:
-    """Zero-filled decode workspace (its completion counters must start at
-    zero; the kernel leaves them zero after every call)."""
+    """Zero-filled decode workspace (its work counters must start at zero;
+    every call leaves them zero)."""
     n = pa.pa_decode_workspace_bytes(S, h_q, h_kv, d, max_context_len)
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
 

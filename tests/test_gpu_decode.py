@@ -126,7 +126,7 @@ def test_fp8_codes_decode_exactly():
     codes = np.arange(256, dtype=np.uint8).reshape(2, 128)
     codes = np.where(np.isnan(codecs.E4M3_TABLE[codes]), 0x38, codes).astype(np.uint8)  # 0x38 = 1.0
     assert kv.create(0, 1) == 0
-    v = torch.zeros((4, h_kv, d, 16), dtype=torch.uint8)
+    v = torch.zeros((4, h_kv, d, 16), dtype=torch.uint8)      # V layout [b][h][D][16]
     st, table = pa.pa_seq_block_table(kv.pool, 0)
     v[int(table[0]), :, :, 0] = torch.from_numpy(codes)
     kv.v.copy_(v.to(DEV))

@@ -179,7 +179,8 @@ def test_argument_validation_of_kernel_entry_points_on_host():
     fake = 0x1000
     assert pa._pa._lib.pa_decode(None, fake, 1, fake, 1, fake, fake, 1, fake, 4, 4, fake,
                                  1, 64, 8, 128, 16, 100, 0.1, 1.0, 1.0, None, 0) == pa.PA_ERR_WORKSPACE
-    assert pa.pa_decode_workspace_bytes(2, 64, 8, 128, 600) == 256 + 2 * 64 * 3 * 130 * 4
+    assert pa.pa_decode_workspace_bytes(2, 64, 8, 128, 600) == 256 + 2 * 64 * 1 * 130 * 4
+    assert pa.pa_decode_workspace_bytes(2, 64, 8, 128, 4097) == 256 + 2 * 64 * 3 * 130 * 4
     assert pa._pa._lib.pa_cache_write(None, None, None, 1, None, 4, None, None, 0, 4, 8, 128, 16,
                                       1.0, 1.0) == pa.PA_ERR_INVALID
     assert pa._pa._lib.pa_cache_write(None, fake, fake, 1, fake, 4, fake, fake, 2, 4, 8, 128, 16,

@@ -266,9 +266,9 @@ def test_decode_closed_forms():
     _, kc, vc, tables, lens, dense = _paged_setup(rng, [50], 1, d)
     qd = np.zeros((1, 1, d))
     qd[0, 0, 0] = 1.0
-    kc[:, :, :, 0] = 0.0
+    kc[:, :, 0, :, 0] = 0.0              # key dim 0 of every token (layout [b][h][d/x][o][x])
     b, o = tables[0][33 // 16], 33 % 16
-    kc[b, 0, o, 0] = 40.0                # score gap 40 * scale(1.0)
+    kc[b, 0, 0, o, 0] = 40.0             # score gap 40 * scale(1.0)
     out = oat.decode(qd, kc, vc, tables, lens, 1, 1.0, "f32")
     np.testing.assert_allclose(out[0, 0], dense[0][1][33, 0], atol=50 * math.exp(-40) * 10)
 
