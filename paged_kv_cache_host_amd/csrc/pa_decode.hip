@@ -163,11 +163,11 @@ __device__ __forceinline__ void store_out4(typename OutT::raw* dst, f32x4 v) {
 
 // Persistent kernel: grid = as many work-groups as fit on the device at once.
 // The work items are (sequence, KV head, chunk) for every chunk that holds
-// part of a context; each work-group computes the item prefix sum over the
-// context lengths in LDS, then takes items in turn from a ticket counter in
-// the workspace (the next ticket is fetched while the current item runs).
-// Its waves take the 2-block steps of the item's chunk in turn (wave w: steps
-// w, w + W, ...) and merge their running (m, l, o) through LDS.  A context
+// part of a context; each work-group derives the item list from the context
+// lengths in LDS, then takes items in turn from a ticket counter in the
+// workspace (the next ticket is fetched while the current item runs).  Its
+// waves share out the 2-block steps of the item's chunk and merge their
+// running (m, l, o) through LDS.  A context
 // that fits one chunk gets its output here; longer ones leave one partial per
 // chunk for the merge kernel.  The last work-group to finish resets the
 // ticket counters, so they are zero again for the next call.
@@ -181,7 +181,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     int32_t* __restrict__ counters, float* __restrict__ ws_ml, float* __restrict__ ws_o) {
   __shared__ float lds_o[kDecodeWaves][kMaxGroup][D];
   __shared__ float lds_ml[kDecodeWaves][kMaxGroup][2];
-  __shared__ int32_t pre[kMaxSeqsPerLaunch + 1];
+  __shared__ int32_t pre[kMaxSeqsPerLaunch + 1];     // full-chunk items before seq i
+  __shared__ int32_t order[kMaxSeqsPerLaunch];       // sequences with a partial chunk
+  __shared__ int32_t key_s[kThreads];
   __shared__ int32_t wave_sums[kDecodeWaves];
   __shared__ int32_t s_item;
   const int tid = threadIdx.x;
@@ -190,19 +192,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   const int c = lane & 15;
   const int g = lane >> 4;
 
-  // items of sequence i: H_kv * (chunks holding part of its context)
-  auto items_of = [&](int32_t i) -> int32_t {
+  // Work items, largest first: every full chunk (kChunkBlocks blocks; the
+  // last chunk index also takes any excess past max_context_len), then the
+  // partial last chunk of each sequence, in decreasing size, so that the
+  // queue ends with its smallest items.
+  auto blocks_of = [&](int32_t i) -> int32_t {
     const int32_t Li = min(context_lens[i], max_blocks * kBlock);
-    if (Li <= 0) return 0;
-    const int32_t nb = (Li + kBlock - 1) / kBlock;
-    return H_kv * min(n_chunks, (nb + kChunkBlocks - 1) / kChunkBlocks);
+    return Li <= 0 ? 0 : (Li + kBlock - 1) / kBlock;
   };
-  // exclusive prefix over the sequences, kThreads at a time
-  int32_t carry = 0;
-  for (int32_t base = 0; base < S; base += kThreads) {
-    const int32_t i = base + tid;
-    int32_t v = i < S ? items_of(i) : 0;
-    int32_t x = v;  // inclusive scan inside the wave
+  auto full_of = [&](int32_t nb) -> int32_t { return min(nb / kChunkBlocks, n_chunks); };
+  auto part_of = [&](int32_t nb) -> int32_t {
+    const int32_t f = full_of(nb);
+    return (f < n_chunks && nb > f * kChunkBlocks) ? nb - f * kChunkBlocks : 0;
+  };
+  // block-wide exclusive scan of v over the launch's sequences, kThreads at
+  // a time; returns this thread's exclusive prefix and updates carry
+  auto scan = [&](int32_t v, int32_t& carry) -> int32_t {
+    int32_t x = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
       const int32_t y = __shfl_up(x, o, kWave);
@@ -210,16 +216,47 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     }
     if (lane == kWave - 1) wave_sums[wave] = x;
     __syncthreads();
-    int32_t before = carry;
-    for (int w = 0; w < wave; ++w) before += wave_sums[w];
-    if (i < S) pre[i] = before + x - v;
-    int32_t tot = 0;
-    for (int w = 0; w < kDecodeWaves; ++w) tot += wave_sums[w];
+    int32_t before = carry, tot = 0;
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      if (w < wave) before += wave_sums[w];
+      tot += wave_sums[w];
+    }
     carry += tot;
     __syncthreads();
+    return before + x - v;
+  };
+  int32_t total_full = 0, n_part = 0;
+  for (int32_t base = 0; base < S; base += kThreads) {
+    const int32_t i = base + tid;
+    const int32_t nb = i < S ? blocks_of(i) : 0;
+    const int32_t full = H_kv * full_of(nb);
+    const int32_t has_part = part_of(nb) > 0 ? 1 : 0;
+    const int32_t e_full = scan(full, total_full);
+    const int32_t e_part = scan(has_part, n_part);
+    if (i < S) {
+      pre[i] = e_full;
+      if (has_part) order[e_part] = i;  // index order; re-sorted below when small
+    }
   }
-  if (tid == 0) pre[S] = carry;
-  const int32_t total = carry;
+  if (tid == 0) pre[S] = total_full;
+  if (S <= kThreads) {
+    // deterministic sort of the partial chunks by size, descending, ties in
+    // sequence order: rank = #larger + #equal with a smaller index
+    const int32_t my = tid < S ? part_of(blocks_of(tid)) : 0;
+    key_s[tid] = my;
+    __syncthreads();
+    int32_t rank = 0;
+    if (my > 0) {
+      for (int32_t j = 0; j < S; ++j) {
+        const int32_t kj = key_s[j];
+        rank += (kj > my) || (kj == my && j < tid);
+      }
+    }
+    __syncthreads();
+    if (my > 0) order[rank] = tid;
+  }
+  __syncthreads();
+  const int32_t total = total_full + n_part * H_kv;
 
   int32_t next = 0;
   if (tid == 0) next = atomicAdd(&counters[0], 1);
@@ -229,20 +266,31 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const int32_t item = __builtin_amdgcn_readfirstlane(s_item);
     if (item >= total) break;
     if (tid == 0) next = atomicAdd(&counters[0], 1);
-    // item -> (seq, kvh, chunk): last seq with pre[seq] <= item
-    int32_t lo = 0, hi = S - 1;
-    while (lo < hi) {
-      const int32_t mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= item)
-        lo = mid;
-      else
-        hi = mid - 1;
+    int32_t seq_, chunk_, kvh_;
+    if (item < total_full) {
+      // last seq with pre[seq] <= item
+      int32_t lo = 0, hi = S - 1;
+      while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= item)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      const int32_t r = item - pre[lo];
+      seq_ = lo;
+      chunk_ = r / H_kv;
+      kvh_ = r % H_kv;
+    } else {
+      const int32_t u = item - total_full;
+      seq_ = order[u / H_kv];
+      kvh_ = u % H_kv;
+      chunk_ = full_of(blocks_of(seq_));
     }
-    const int seq = __builtin_amdgcn_readfirstlane(lo);
-    const int32_t r = item - pre[seq];
-    const int32_t n_valid = (pre[seq + 1] - pre[seq]) / H_kv;
-    const int kvh = __builtin_amdgcn_readfirstlane(r / n_valid);
-    const int chunk = __builtin_amdgcn_readfirstlane(r % n_valid);
+    const int seq = __builtin_amdgcn_readfirstlane(seq_);
+    const int chunk = __builtin_amdgcn_readfirstlane(chunk_);
+    const int kvh = __builtin_amdgcn_readfirstlane(kvh_);
+    const int32_t n_valid = full_of(blocks_of(seq)) + (part_of(blocks_of(seq)) > 0 ? 1 : 0);
 
   const int32_t L = min(context_lens[seq], max_blocks * kBlock);
   const int32_t nblk = (L + kBlock - 1) / kBlock;
@@ -352,10 +400,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     }
   };
 
-  // This wave's steps: blocks p = c0 + 2 * (wave + kDecodeWaves * i).  The
-  // second block's table entry is read at a clamped index (always in
-  // range) so that no load sits behind a branch.
-  for (int32_t p = c0 + 2 * wave; p < b1; p += 2 * kDecodeWaves) {
+  // Wave w takes the chunk's 2-block steps w, w + W, ...  (a fixed
+  // assignment keeps the result independent of timing: runs are
+  // bit-identical).  The second block's table entry is read at a clamped
+  // index (always in range) so that no load sits behind a branch.
+  const int32_t n_steps = (b1 - c0 + 1) / 2;
+  for (int32_t st = wave; st < n_steps; st += kDecodeWaves) {
+    const int32_t p = c0 + 2 * st;
     BlockRegs<CacheT, D> xa, xb;
     load_block<CacheT, D>(xa, k_cache, v_cache, tile_of(p), c, g);
     load_block<CacheT, D>(xb, k_cache, v_cache, tile_of(min(p + 1, b1 - 1)), c, g);
