@@ -50,7 +50,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=32)
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain device copy of known size (HBM counter calibration)")
+                    help="only run a plain streaming kernel of known size (HBM counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR",
+                                                       "CAL_WRITE_DIR"),
+                    help="no GPU work: turn rocprofv3 --pmc CSV runs into per-launch HBM bytes")
     return ap.parse_args()
 
 
@@ -140,18 +143,71 @@ def cpu_baseline(n_seqs: int):
                       f"host {model or 'unknown'}, {len(os.sched_getaffinity(0))} cores visible"}
 
 
+CAL_BYTES = 1 << 30
+
+
 def calibrate_copy():
+    """A plain streaming kernel of known size for the HBM counter
+    calibration: out = -in over 1 GiB of fp32 (reads 1 GiB, writes 1 GiB)."""
     import torch
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty(n, dtype=torch.uint8, device="cuda")
-    a.fill_(1)
+    n = CAL_BYTES // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda")
+    b = torch.empty(n, dtype=torch.float32, device="cuda")
+    a.fill_(1.0)
     torch.cuda.synchronize()
     for _ in range(3):
-        b.copy_(a)
+        torch.neg(a, out=b)
     torch.cuda.synchronize()
-    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
-                      "launches": 3}))
+    print(json.dumps({"calibration": "fp32 negation kernel", "bytes_read": CAL_BYTES,
+                      "bytes_written": CAL_BYTES, "launches": 3}))
+
+
+def _pmc_rows(d: str, counter: str):
+    """(kernel name, value) of every dispatch in a rocprofv3 --pmc CSV run."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {d}")
+    return rows
+
+
+def _pmc_mean(rows, key: str) -> tuple[float, int]:
+    vals = [v for name, v in rows if key in name]
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel named *{key}*: "
+                         f"{sorted(set(n for n, _ in rows))[:20]}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str):
+    """HBM traffic of one decode launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (KiB per dispatch), each scaled by what the same counter reads for
+    the calibration kernel of known size."""
+    f_dec, n_f = _pmc_mean(_pmc_rows(fetch_dir, "FETCH_SIZE"), "decode_kernel")
+    w_dec, n_w = _pmc_mean(_pmc_rows(write_dir, "WRITE_SIZE"), "decode_kernel")
+    f_cal, _ = _pmc_mean(_pmc_rows(cal_fetch_dir, "FETCH_SIZE"), "neg")
+    w_cal, _ = _pmc_mean(_pmc_rows(cal_write_dir, "WRITE_SIZE"), "neg")
+    f_scale = CAL_BYTES / (f_cal * 1024.0)
+    w_scale = CAL_BYTES / (w_cal * 1024.0)
+    out = {
+        "kernel": "decode_kernel<BF16,128>",
+        "workload": "decode-70b-shaped, 128 seqs (bench.py default)",
+        "kernel_source_digest": kernel_source_digest(),
+        "fetch_kib_per_launch_raw": round(f_dec, 1), "fetch_dispatches": n_f,
+        "write_kib_per_launch_raw": round(w_dec, 1), "write_dispatches": n_w,
+        "calibration": {"kernel": "fp32 negation, 1 GiB in / 1 GiB out",
+                        "fetch_kib_raw": round(f_cal, 1), "write_kib_raw": round(w_cal, 1),
+                        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+        "hbm_read_bytes_per_launch": int(f_dec * 1024 * f_scale),
+        "hbm_write_bytes_per_launch": int(w_dec * 1024 * w_scale),
+    }
+    out["hbm_bytes_per_launch"] = out["hbm_read_bytes_per_launch"] + out["hbm_write_bytes_per_launch"]
+    print(json.dumps(out, indent=1))
 
 
 def main():
@@ -164,6 +220,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
         return
 
     import torch
@@ -219,8 +278,6 @@ def main():
     ev_consumed = [torch.cuda.Event() for _ in range(2)]
     for e in ev_consumed:
         e.record(compute)
-    ev_d0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_d1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ctx_lens = []
 
     def step(i: int, timed_idx: int | None):
@@ -240,30 +297,37 @@ def main():
         r = i % R
         pa.check(pa.pa_cache_write(compute, k_ring[r], v_ring[r], slots_dev[X], kv.k, kv.v,
                                    num_blocks, H_KV, D, BLOCK))
-        if timed_idx is not None:
-            ev_d0[timed_idx].record(compute)
         pa.check(pa.pa_decode(compute, out, q_ring[r], kv.k, kv.v, tables_dev[X], lens_dev[X],
                               num_blocks, H_KV, max_ctx, sm, 1.0, 1.0, ws))
         if timed_idx is not None:
-            ev_d1[timed_idx].record(compute)
             ctx_lens.append(lens_np.copy())
         ev_consumed[X].record(compute)
 
     for i in range(W):
         step(i, None)
     torch.cuda.synchronize()
+    # The library brackets each of its kernel launches with HIP events on the
+    # stream it launches on (here `compute`); reset and enable for the timed
+    # steps only.
+    pa.check(pa.pa_timing_enable(True))
     t0 = time.perf_counter()
     for i in range(K):
         step(W + i, i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    timings = {}
+    for name in ("decode", "decode_merge", "cache_write"):
+        st, cnt, mean_us, tot_us = pa.pa_timing_query(name)
+        pa.check(st)
+        timings[name] = (cnt, mean_us)
+    pa.check(pa.pa_timing_enable(False))
+    assert timings["decode"][0] == K, timings
 
-    dec_ms = [ev_d0[i].elapsed_time(ev_d1[i]) for i in range(K)]
     dec_bytes = [decode_bytes(l) for l in ctx_lens]
     cw = cache_write_bytes(S)
     total_bytes = sum(dec_bytes) + K * cw
     value = total_bytes / wall / 1e9
-    dec_avg_s = sum(dec_ms) / K / 1e3
+    dec_avg_s = timings["decode"][1] / 1e6
     achieved = (sum(dec_bytes) / K) / dec_avg_s / 1e9
     digest = kernel_source_digest()
     traffic = traffic_from_profile(digest)
@@ -288,8 +352,10 @@ def main():
                    "num_blocks": num_blocks},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "pa_decode (decode_kernel<BF16,128>)",
+                     "traffic": traffic, "kernel": "decode_kernel<BF16,128>",
                      "kernel_us": round(dec_avg_s * 1e6, 2),
+                     "other_kernels_us": {"decode_merge_kernel": round(timings["decode_merge"][1], 2),
+                                          "cache_write_kernel": round(timings["cache_write"][1], 2)},
                      "algorithmic_bytes_per_launch": int(sum(dec_bytes) / K),
                      "kernel_source_digest": digest},
     }

@@ -247,6 +247,22 @@ pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, const void*
                            int32_t max_q_len, int32_t max_context_len, float sm_scale,
                            float k_scale, float v_scale, void* ws, size_t ws_bytes);
 
+/* ------------------------------------------------------------------------
+ * Kernel timing (instrumentation, off by default).  When enabled, each
+ * kernel launch of the calls above is bracketed by a pair of HIP events
+ * recorded on the caller's stream (up to 4096 launches per kernel between
+ * resets).  Kernel names: "cache_write", "decode", "decode_merge",
+ * "prefill", "generic".
+ * ---------------------------------------------------------------------- */
+
+/* Enable (non-zero) or disable timing; either way the recorded launches are
+ * forgotten. */
+pa_status pa_timing_enable(int32_t enable);
+
+/* Wait for the recorded launches of `kernel` [host string] and report their
+ * number, mean and total duration in microseconds (each [host]). */
+pa_status pa_timing_query(const char* kernel, int32_t* count, float* mean_us, float* total_us);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,6 +62,8 @@ _SIGS = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _i32,
                          _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32, _vp, _sz]),
+    "pa_timing_enable": (_i32, [_i32]),
+    "pa_timing_query": (_i32, [C.c_char_p, _i32p, C.POINTER(_f32), C.POINTER(_f32)]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_prefill_chunk": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                 _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32,
@@ -212,6 +214,21 @@ def pa_validate_tables(block_tables, context_lens, max_blocks: int, block_size: 
     lens = _i32_array(context_lens)
     return _lib.pa_validate_tables(_ptr_i32(t), _ptr_i32(lens), len(lens), max_blocks, block_size,
                                    num_blocks)
+
+
+# -------------------------------------------------------------- timing -----
+
+def pa_timing_enable(enable: bool = True) -> int:
+    return _lib.pa_timing_enable(1 if enable else 0)
+
+
+def pa_timing_query(kernel: str):
+    """Returns (status, count, mean_us, total_us) of the recorded launches."""
+    n = _i32()
+    mean = _f32()
+    tot = _f32()
+    st = _lib.pa_timing_query(kernel.encode(), C.byref(n), C.byref(mean), C.byref(tot))
+    return st, n.value, mean.value, tot.value
 
 
 # ------------------------------------------------------------- kernels -----
