@@ -252,7 +252,7 @@ pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, const void*
  * kernel launch of the calls above is bracketed by a pair of HIP events
  * recorded on the caller's stream (up to 4096 launches per kernel between
  * resets).  Kernel names: "cache_write", "decode", "decode_merge",
- * "prefill", "generic".
+ * "prefill", "prefill_merge", "generic".
  * ---------------------------------------------------------------------- */
 
 /* Enable (non-zero) or disable timing; either way the recorded launches are

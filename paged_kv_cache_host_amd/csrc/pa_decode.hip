@@ -30,6 +30,8 @@
 //           v_mfma_f32_16x16x16_bf16 per block: A = V^T (16 dims x 16
 //           tokens), B = P^T, which is exactly the score registers (tokens
 //           4g..4g+3 of head c) after the softmax update; no lane exchange.
+//           The weights enter as two bf16 terms (rounded value + rounded
+//           remainder), two MFMAs each, for 16 significant bits.
 // Loads: a block's K tile is stored as 16-byte chunks of its 16 tokens side
 // by side ([D/x][16][x]), so the K operand of one MFMA step is one 1 KiB
 // contiguous read (lane = token, lane group = chunk); the V tile is stored
@@ -366,7 +368,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
       for (int t = 0; t < D / 16; ++t) o[t] *= alpha;
       m_run = m_new;
     }
-    bf16x4 pa4, pb4;
+    // weights as a sum of two bf16 (high part + rounded remainder): about 16
+    // significant bits, so that contexts of a few tokens, where one or two
+    // weights dominate, keep the output within tolerance
+    bf16x4 pa4, pb4, pa4l, pb4l;
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -375,6 +380,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
       psum += ea + eb;
       pa4[j] = static_cast<__bf16>(ea);
       pb4[j] = static_cast<__bf16>(eb);
+      pa4l[j] = static_cast<__bf16>(ea - static_cast<float>(pa4[j]));
+      pb4l[j] = static_cast<__bf16>(eb - static_cast<float>(pb4[j]));
     }
     l_run += psum;
     if (tail) {
@@ -390,12 +397,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
         }
         o[t] = mfma16x16x16(va, pa4, o[t]);
         o[t] = mfma16x16x16(vb, pb4, o[t]);
+        o[t] = mfma16x16x16(va, pa4l, o[t]);
+        o[t] = mfma16x16x16(vb, pb4l, o[t]);
       }
     } else {
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        o[t] = mfma16x16x16(v_operand(ra, t), pa4, o[t]);
-        o[t] = mfma16x16x16(v_operand(rb, t), pb4, o[t]);
+        const bf16x4 va = v_operand(ra, t), vb = v_operand(rb, t);
+        o[t] = mfma16x16x16(va, pa4, o[t]);
+        o[t] = mfma16x16x16(vb, pb4, o[t]);
+        o[t] = mfma16x16x16(va, pa4l, o[t]);
+        o[t] = mfma16x16x16(vb, pb4l, o[t]);
       }
     }
   };

@@ -8,6 +8,8 @@ namespace pa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -69,6 +71,24 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 w) {
   return r;
 }
 
+// Eight e4m3fn codes -> eight fp16 (exact: every e4m3fn value is an fp16
+// value).
+__device__ __forceinline__ f16x8 fp8x8_to_f16x8(u32x2 w) {
+  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false);
+  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true);
+  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, false);
+  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true);
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Two bf16 (one dword) -> two fp16, rounding toward zero.  Exact for
+// magnitudes in [2^-14, 65504]; smaller ones keep an absolute error below
+// 2^-24 and larger finite ones saturate at 65504.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
+                                                                 __uint_as_float(w & 0xFFFF0000u)));
+}
+
 // float -> e4m3fn code: nearest value, ties to even mantissa, |x| > 448
 // saturates to 448, NaN stays NaN (0x7F with the sign).  Written from the
 // format definition: 4 exponent bits of bias 7, 3 mantissa bits, subnormal
@@ -113,6 +133,10 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 }  // namespace pa

@@ -8,7 +8,15 @@
 namespace pa {
 
 // Kernels whose launches the optional timing facility can record.
-enum KernelId { kCacheWrite = 0, kDecode, kDecodeMerge, kPrefill, kGeneric, kKernelCount };
+enum KernelId {
+  kCacheWrite = 0,
+  kDecode,
+  kDecodeMerge,
+  kPrefill,
+  kPrefillMerge,
+  kGeneric,
+  kKernelCount
+};
 
 // Record a HIP event before (begin) or after (!begin) a kernel launch on
 // `st` when timing is enabled (pa_timing_enable); a no-op otherwise.

@@ -4,7 +4,41 @@
 // LESSON "vLLM Serving Internals", "Chunked prefill": a long prompt is split
 // into fixed-size slices (512 tokens by default), each scheduled as a unit;
 // a slice's queries attend every earlier position of the prompt and the
-// slice's own positions up to and including their own (causal).
+// slice's own positions up to and including their own (causal).  The keys
+// and values of the prefix and of the slice itself are read from the paged
+// cache through the sequence's block table ("vLLM architecture", section
+// 2.3: compute within a block, accumulate across blocks), so the slice's own
+// K/V are written with pa_cache_write first.
+//
+// bf16 queries with a bf16 or fp8 e4m3fn cache run on the matrix cores; an
+// fp32 problem runs on the generic VALU kernel.  Q K^T multiplies bf16 by
+// bf16 (v_mfma_f32_32x32x16_bf16).  P V multiplies fp16 by fp16
+// (v_mfma_f32_32x32x16_f16): the softmax weights, at most 2^8 here, keep 11
+// significant bits in fp16 against 8 in bf16, which is what keeps a slice
+// whose first rows see only a handful of keys within the output tolerance;
+// V is converted to fp16 on its way into LDS (exact for e4m3 codes and for
+// bf16 magnitudes up to 65504, larger bf16 values saturate).
+//
+// Work decomposition.  A work-group owns one KV head, up to eight of the
+// query heads that share it (one wave each) and 32 consecutive query
+// positions per wave; when a KV head has fewer than eight query heads the
+// spare waves take further 32-position sub-tiles, so every wave of the group
+// consumes the same K/V tile.  K/V arrive in tiles of 64 keys (four cache
+// blocks), staged through LDS in two buffers: the global loads of tile t+1
+// are in flight while tile t is multiplied.  When the slices alone give too
+// few work-groups to fill the chip, the key range is split and a second
+// kernel merges the partial softmax states.
+//
+// Per wave and 32-key half-tile the scores are computed transposed,
+// S^T = K Q^T (keys on the MFMA rows, the wave's 32 queries on its columns),
+// so that a lane holds 16 scores of a single query.  The accumulator O^T =
+// V^T P^T keeps the same orientation: each lane owns one query's column of
+// O^T, so the softmax statistics and the rescaling never leave the lane
+// except for one exchange with the lane 32 away that holds the query's other
+// 16 keys.  The K rows of a 16-key group are stored in LDS with their middle
+// quads swapped; with that permutation the 8 keys a lane holds for each
+// 16-key step of P^T are consecutive, which is what one 16-byte read of the
+// token-minor V layout supplies.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -18,19 +52,532 @@ pa_status launch_attend_generic(hipStream_t st, void* out, pa_dtype out_dt, cons
                                 int32_t n_chunks, int32_t rows, int32_t H_q, int32_t H_kv,
                                 int32_t D, float sm_scale, float k_scale, float v_scale);
 
+namespace {
+
+constexpr int kPfWaves = 8;                 // waves per work-group
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfRows = 32;                 // query positions per wave
+constexpr int kPfKeys = 64;                 // keys per LDS tile (4 blocks)
+constexpr int kPfTargetGroups = 256;        // one work-group per compute unit
+constexpr int kPfMaxSplit = 8;
+constexpr int kPfMinKeysPerSplit = 1024;
+constexpr float kPfLazy = 8.0f;             // log2 headroom of the softmax reference
+
+// LDS bytes of one stage: K [D/8 chunks][64 rows][16 B] + V [D rows][64 keys].
+template <int D>
+constexpr int stage_bytes() {
+  return D * kPfKeys * 2 * 2;
+}
+
+// Position of key `tok` (0..15) of a block among the 16 K rows of that block
+// in LDS: the second and third groups of four trade places.
+__device__ __forceinline__ int krow_of(int tok) {
+  const int quad = tok >> 2;
+  const int swapped = (quad == 1 || quad == 2) ? (3 - quad) : quad;
+  return (swapped << 2) | (tok & 3);
+}
+
+// V row of dimension d holds 8 chunks of 8 keys (16 B); chunk c sits at
+// c ^ (d & 7) so that the 32 dimensions read by one MFMA step spread over
+// all banks.
+__device__ __forceinline__ int vchunk_pos(int d, int c) { return c ^ (d & 7); }
+
+struct PfGeom {
+  int H_kv, G, hpw, psub, n_head_groups, n_pos_tiles, n_split;
+};
+
+// Work split shared by the launcher and the workspace query.
+PfGeom pf_geometry(int32_t n_chunks, int32_t max_q_len, int32_t H_q, int32_t H_kv,
+                   int32_t max_context_len) {
+  PfGeom g;
+  g.H_kv = H_kv;
+  g.G = H_q / H_kv;
+  g.hpw = g.G < kPfWaves ? g.G : kPfWaves;
+  g.psub = kPfWaves / g.hpw;
+  g.n_head_groups = (g.G + kPfWaves - 1) / kPfWaves;
+  const int pos_per_group = kPfRows * g.psub;
+  g.n_pos_tiles = (max_q_len + pos_per_group - 1) / pos_per_group;
+  const int64_t groups =
+      static_cast<int64_t>(n_chunks) * g.n_pos_tiles * H_kv * g.n_head_groups;
+  int split = groups > 0 ? static_cast<int>(kPfTargetGroups / groups) : 1;
+  const int by_keys = max_context_len / kPfMinKeysPerSplit;
+  if (split > by_keys) split = by_keys;
+  if (split > kPfMaxSplit) split = kPfMaxSplit;
+  if (split < 1) split = 1;
+  g.n_split = split;
+  return g;
+}
+
+__device__ __forceinline__ f16x8 pack_f16x8(const float* v) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = static_cast<_Float16>(v[i]);
+  return r;
+}
+
+template <typename CacheT>
+struct TileLoader;
+
+// bf16 cache: a tile is 4 blocks x (K 4 KB + V 4 KB) per KV head at D = 128,
+// moved as 16-byte pieces.
+template <>
+struct TileLoader<BF16> {
+  template <int D>
+  static constexpr int pieces() {
+    return 2 * 4 * D * kBlock * 2 / 16;
+  }
+  template <int D>
+  static constexpr int per_thread() {
+    return pieces<D>() / kPfThreads;
+  }
+  template <int D>
+  __device__ static void load(u32x4* regs, const uint16_t* __restrict__ k_cache,
+                              const uint16_t* __restrict__ v_cache, const int32_t* blk,
+                              int32_t kvh, int32_t H_kv, int tid) {
+    constexpr int kPerBlock = D * kBlock * 2 / 16;  // pieces per (block, head) and tensor
+    constexpr int kHalf = 4 * kPerBlock;
+#pragma unroll
+    for (int i = 0; i < per_thread<D>(); ++i) {
+      const int p = tid + i * kPfThreads;
+      const bool is_v = p >= kHalf;
+      const int pp = is_v ? p - kHalf : p;
+      const int b = pp / kPerBlock, e = pp % kPerBlock;
+      const int32_t bk = blk[b];
+      if (bk >= 0) {
+        const uint16_t* base = (is_v ? v_cache : k_cache) +
+                               (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + e * 8;
+        regs[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base));
+      } else {
+        regs[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  // `valid` = keys of the tile that exist (V beyond them is zeroed).
+  template <int D>
+  __device__ static void store(const u32x4* regs, uint8_t* stage, int valid, int tid) {
+    constexpr int kPerBlock = D * kBlock * 2 / 16;
+    constexpr int kHalf = 4 * kPerBlock;
+    uint8_t* k_lds = stage;
+    uint8_t* v_lds = stage + D * kPfKeys * 2;
+#pragma unroll
+    for (int i = 0; i < per_thread<D>(); ++i) {
+      const int p = tid + i * kPfThreads;
+      if (p < kHalf) {
+        const int b = p / kPerBlock, e = p % kPerBlock;
+        const int ch = e / kBlock, tok = e % kBlock;
+        *reinterpret_cast<u32x4*>(k_lds + ch * (kPfKeys * 16) + (b * kBlock + krow_of(tok)) * 16) =
+            regs[i];
+      } else {
+        const int pp = p - kHalf;
+        const int b = pp / kPerBlock, e = pp % kPerBlock;
+        const int d = e >> 1, h = e & 1;
+        const int key0 = b * kBlock + h * 8;
+        u32x4 w = regs[i];
+        if (key0 + 8 > valid) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int k = key0 + 2 * j;
+            uint32_t m = 0u;
+            if (k < valid) m |= 0xFFFFu;
+            if (k + 1 < valid) m |= 0xFFFF0000u;
+            w[j] &= m;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(w[j]);
+        *reinterpret_cast<u32x4*>(v_lds + d * (kPfKeys * 2) + vchunk_pos(d, 2 * b + h) * 16) = w;
+      }
+    }
+  }
+};
+
+// fp8 cache: pieces of 16 codes, widened to bf16 (exact) on the way to LDS.
+template <>
+struct TileLoader<FP8> {
+  template <int D>
+  static constexpr int pieces() {
+    return 2 * 4 * D * kBlock / 16;
+  }
+  template <int D>
+  static constexpr int per_thread() {
+    return pieces<D>() / kPfThreads;
+  }
+  template <int D>
+  __device__ static void load(u32x4* regs, const uint8_t* __restrict__ k_cache,
+                              const uint8_t* __restrict__ v_cache, const int32_t* blk,
+                              int32_t kvh, int32_t H_kv, int tid) {
+    constexpr int kPerBlock = D * kBlock / 16;
+    constexpr int kHalf = 4 * kPerBlock;
+#pragma unroll
+    for (int i = 0; i < per_thread<D>(); ++i) {
+      const int p = tid + i * kPfThreads;
+      const bool is_v = p >= kHalf;
+      const int pp = is_v ? p - kHalf : p;
+      const int b = pp / kPerBlock, e = pp % kPerBlock;
+      const int32_t bk = blk[b];
+      if (bk >= 0) {
+        const uint8_t* base = (is_v ? v_cache : k_cache) +
+                              (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + e * 16;
+        regs[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base));
+      } else {
+        regs[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  template <int D>
+  __device__ static void store(const u32x4* regs, uint8_t* stage, int valid, int tid) {
+    constexpr int kPerBlock = D * kBlock / 16;
+    constexpr int kHalf = 4 * kPerBlock;
+    uint8_t* k_lds = stage;
+    uint8_t* v_lds = stage + D * kPfKeys * 2;
+#pragma unroll
+    for (int i = 0; i < per_thread<D>(); ++i) {
+      const int p = tid + i * kPfThreads;
+      const u32x4 w = regs[i];
+      if (p < kHalf) {
+        const bf16x8 lo = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
+        const bf16x8 hi = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
+        // 16 codes = dims 16*ch8 .. +15 of token tok -> bf16 chunks 2*ch8, 2*ch8+1
+        const int b = p / kPerBlock, e = p % kPerBlock;
+        const int ch8 = e / kBlock, tok = e % kBlock;
+        const int row = b * kBlock + krow_of(tok);
+        *reinterpret_cast<bf16x8*>(k_lds + (2 * ch8) * (kPfKeys * 16) + row * 16) = lo;
+        *reinterpret_cast<bf16x8*>(k_lds + (2 * ch8 + 1) * (kPfKeys * 16) + row * 16) = hi;
+      } else {
+        // 16 codes = tokens 0..15 of dimension d
+        const int pp = p - kHalf;
+        const int b = pp / kPerBlock, d = pp % kPerBlock;
+        f16x8 v0 = fp8x8_to_f16x8(u32x2{w[0], w[1]});
+        f16x8 v1 = fp8x8_to_f16x8(u32x2{w[2], w[3]});
+        const int key0 = b * kBlock;
+        if (key0 + kBlock > valid) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (key0 + j >= valid) v0[j] = static_cast<_Float16>(0.0f);
+            if (key0 + 8 + j >= valid) v1[j] = static_cast<_Float16>(0.0f);
+          }
+        }
+        *reinterpret_cast<f16x8*>(v_lds + d * (kPfKeys * 2) + vchunk_pos(d, 2 * b) * 16) = v0;
+        *reinterpret_cast<f16x8*>(v_lds + d * (kPfKeys * 2) + vchunk_pos(d, 2 * b + 1) * 16) = v1;
+      }
+    }
+  }
+};
+
+// grid.x = H_kv * n_head_groups * n_split * n_pos_tiles (KV head fastest, so
+// the groups sharing a KV head land on the same XCD's L2); grid.y = slices.
+template <typename CacheT, int D>
+__global__ __launch_bounds__(kPfThreads) void prefill_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ start_pos,
+    const typename CacheT::raw* __restrict__ k_cache,
+    const typename CacheT::raw* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    int32_t max_blocks, int32_t num_blocks, int32_t H_q, PfGeom geo, float score_scale,
+    float v_scale, float* __restrict__ ws_ml, float* __restrict__ ws_o, int32_t ws_rows) {
+  constexpr int NKS = D / 16;  // 16-dim MFMA steps of Q K^T
+  constexpr int NDT = D / 32;  // 32-dim tiles of O^T
+  constexpr int NLD = TileLoader<CacheT>::template per_thread<D>();
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * stage_bytes<D>()];
+  __shared__ int32_t blk_s[2][4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = lane >> 5;   // which half of the wave (MFMA k-group)
+  const int col = lane & 31; // the lane's query within the wave
+
+  int x = blockIdx.x;
+  const int kvh = x % geo.H_kv;
+  x /= geo.H_kv;
+  const int hg = x % geo.n_head_groups;
+  x /= geo.n_head_groups;
+  const int split = x % geo.n_split;
+  const int pt = geo.n_pos_tiles - 1 - x / geo.n_split;  // longest rows first
+  const int c = blockIdx.y;
+
+  const int32_t q0 = cu_q_lens[c];
+  const int32_t qlen = cu_q_lens[c + 1] - q0;
+  const int32_t P0 = start_pos[c];
+  const int pos_per_group = kPfRows * geo.psub;
+  const int grp0 = pt * pos_per_group;
+  if (grp0 >= qlen) return;
+  const int grp_end = min(grp0 + pos_per_group, qlen);
+  const int32_t kv_end = P0 + grp_end;  // keys this group needs: [0, kv_end)
+
+  const int n_tiles = (kv_end + kPfKeys - 1) / kPfKeys;
+  const int per = (n_tiles + geo.n_split - 1) / geo.n_split;
+  const int t0 = split * per;
+  const int t1 = min(n_tiles, t0 + per);
+
+  // this wave's query head and positions
+  const int hi = wave % geo.hpw, ps = wave / geo.hpw;
+  const int hq_in_group = hg * kPfWaves + hi;
+  const bool active = ps < geo.psub && hq_in_group < geo.G;
+  const int head = kvh * geo.G + hq_in_group;
+  const int w0 = grp0 + ps * kPfRows;  // first position (relative to the slice)
+  const bool wave_live = active && w0 < qlen;
+  const int my_rel = min(w0 + col, qlen - 1);
+  const int32_t qpos = P0 + my_rel;   // absolute position (clamped for rows past the end)
+  const bool row_ok = wave_live && (w0 + col) < qlen;
+  const int32_t wave_last_pos = P0 + min(w0 + kPfRows, qlen) - 1;
+  const int32_t wave_first_pos = P0 + w0;
+
+  // Q fragment: query `col`, dims 16 ks + 8 g .. + 7
+  bf16x8 qf[NKS];
+  {
+    const uint16_t* qrow = q + (static_cast<int64_t>(q0 + my_rel) * H_q + head) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 w = u32x4{0u, 0u, 0u, 0u};
+      if (row_ok) w = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+      qf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  f32x16 o[NDT];
+#pragma unroll
+  for (int n = 0; n < NDT; ++n)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[n][j] = 0.f;
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+
+  const int32_t* table = block_tables + static_cast<int64_t>(c) * max_blocks;
+  const int32_t n_blk = min((kv_end + kBlock - 1) / kBlock, max_blocks);
+  auto tile_blocks = [&](int t, int32_t* dst) {
+    if (tid < 4) {
+      const int kb = t * 4 + tid;
+      dst[tid] = kb < n_blk ? safe_block(table[kb], num_blocks) : -1;
+    }
+  };
+
+  u32x4 regs[NLD];
+  if (t0 < t1) {
+    tile_blocks(t0, blk_s[0]);
+    __syncthreads();
+    TileLoader<CacheT>::template load<D>(regs, k_cache, v_cache, blk_s[0], kvh, geo.H_kv, tid);
+    TileLoader<CacheT>::template store<D>(regs, smem, kv_end - t0 * kPfKeys, tid);
+    if (t0 + 1 < t1) tile_blocks(t0 + 1, blk_s[1]);
+    __syncthreads();
+  }
+
+  for (int t = t0; t < t1; ++t) {
+    const int sb = (t - t0) & 1;
+    const bool more = t + 1 < t1;
+    if (more)
+      TileLoader<CacheT>::template load<D>(regs, k_cache, v_cache, blk_s[sb ^ 1], kvh, geo.H_kv,
+                                           tid);
+    const int32_t key0 = t * kPfKeys;
+    if (wave_live && key0 <= wave_last_pos) {
+      const uint8_t* k_lds = smem + sb * stage_bytes<D>();
+      const uint8_t* v_lds = k_lds + D * kPfKeys * 2;
+      f32x16 s[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[h][j] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              k_lds + (2 * ks + g) * (kPfKeys * 16) + (32 * h + col) * 16);
+          s[h] = mfma32x32x16(a, qf[ks], s[h]);
+        }
+      }
+      // scores -> log2 domain, causal mask only where the tile crosses a
+      // query's own position
+      float xv[32];
+      const bool need_mask = key0 + kPfKeys - 1 > wave_first_pos;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float v = s[h][j] * score_scale;
+          if (need_mask) {
+            const int key = key0 + 32 * h + 16 * (j >> 3) + 8 * g + (j & 7);
+            v = key <= qpos ? v : -__builtin_inff();
+          }
+          xv[16 * h + j] = v;
+        }
+      float mx = xv[0];
+#pragma unroll
+      for (int j = 1; j < 32; ++j) mx = fmaxf(mx, xv[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kPfLazy) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < NDT; ++n)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) o[n][j] *= alpha;
+        m_run = m_new;
+      }
+      const float mu = m_run == -__builtin_inff() ? 0.f : m_run;
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        xv[j] = __builtin_amdgcn_exp2f(xv[j] - mu);
+        psum += xv[j];
+      }
+      l_run += psum;
+      // O^T += V^T P^T, four 16-key steps
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f16x8 pb = pack_f16x8(&xv[8 * u]);
+#pragma unroll
+        for (int n = 0; n < NDT; ++n) {
+          const int d = 32 * n + col;
+          const f16x8 a = *reinterpret_cast<const f16x8*>(
+              v_lds + d * (kPfKeys * 2) + vchunk_pos(d, 2 * u + g) * 16);
+          o[n] = mfma32x32x16(a, pb, o[n]);
+        }
+      }
+    }
+    if (more) {
+      TileLoader<CacheT>::template store<D>(regs, smem + (sb ^ 1) * stage_bytes<D>(),
+                                            kv_end - (t + 1) * kPfKeys, tid);
+      if (t + 2 < t1) tile_blocks(t + 2, blk_s[sb]);
+    }
+    __syncthreads();
+  }
+
+  if (!row_ok) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const int64_t row = q0 + w0 + col;
+  if (geo.n_split == 1) {
+    const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
+    uint16_t* orow = out + (row * H_q + head) * D;
+#pragma unroll
+    for (int n = 0; n < NDT; ++n)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int d = 32 * n + 8 * jq + 4 * g;
+        u32x2 w;
+        w[0] = static_cast<uint32_t>(f32_to_bf16(o[n][4 * jq] * inv)) |
+               (static_cast<uint32_t>(f32_to_bf16(o[n][4 * jq + 1] * inv)) << 16);
+        w[1] = static_cast<uint32_t>(f32_to_bf16(o[n][4 * jq + 2] * inv)) |
+               (static_cast<uint32_t>(f32_to_bf16(o[n][4 * jq + 3] * inv)) << 16);
+        *reinterpret_cast<u32x2*>(orow + d) = w;
+      }
+  } else if (row < ws_rows) {
+    const int64_t slot = (static_cast<int64_t>(split) * ws_rows + row) * H_q + head;
+    float* po = ws_o + slot * D;
+#pragma unroll
+    for (int n = 0; n < NDT; ++n)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int d = 32 * n + 8 * jq + 4 * g;
+        *reinterpret_cast<f32x4*>(po + d) =
+            f32x4{o[n][4 * jq], o[n][4 * jq + 1], o[n][4 * jq + 2], o[n][4 * jq + 3]};
+      }
+    if (g == 0) {
+      ws_ml[2 * slot] = m_run;
+      ws_ml[2 * slot + 1] = l_tot;
+    }
+  }
+}
+
+// Merge the key-range partials of each (row, head): one wave per pair.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(
+    uint16_t* __restrict__ out, const int32_t* __restrict__ cu_q_lens, int32_t n_chunks,
+    int32_t H_q, int32_t n_split, const float* __restrict__ ws_ml,
+    const float* __restrict__ ws_o, int32_t ws_rows, float v_scale) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t total = min(static_cast<int64_t>(cu_q_lens[n_chunks]), static_cast<int64_t>(ws_rows)) * H_q;
+  if (pair >= total) return;
+  float M = -__builtin_inff();
+  for (int j = 0; j < n_split; ++j) {
+    const int64_t slot = static_cast<int64_t>(j) * ws_rows * H_q + pair;
+    if (ws_ml[2 * slot + 1] > 0.f) M = fmaxf(M, ws_ml[2 * slot]);
+  }
+  constexpr int PER = D / kWave;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  float L = 0.f;
+  for (int j = 0; j < n_split; ++j) {
+    const int64_t slot = static_cast<int64_t>(j) * ws_rows * H_q + pair;
+    const float l = ws_ml[2 * slot + 1];
+    if (!(l > 0.f)) continue;
+    const float w = __builtin_amdgcn_exp2f(ws_ml[2 * slot] - M);
+    L += w * l;
+    const float* po = ws_o + slot * D + lane * PER;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += w * po[i];
+  }
+  const float inv = L > 0.f ? v_scale / L : 0.f;
+  uint16_t* orow = out + pair * D + lane * PER;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) orow[i] = f32_to_bf16(acc[i] * inv);
+}
+
+template <typename CacheT, int D>
+pa_status launch_prefill_mfma(hipStream_t st, void* out, const void* q, const int32_t* cu_q_lens,
+                              const int32_t* start_pos, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int32_t max_blocks, int32_t num_blocks,
+                              int32_t n_chunks, int32_t H_q, int32_t H_kv, int32_t max_q_len,
+                              int32_t max_context_len, float score_scale, float v_scale, void* ws,
+                              size_t ws_bytes) {
+  const PfGeom geo = pf_geometry(n_chunks, max_q_len, H_q, H_kv, max_context_len);
+  const int64_t gx = static_cast<int64_t>(H_kv) * geo.n_head_groups * geo.n_split * geo.n_pos_tiles;
+  if (gx > INT32_MAX || n_chunks > 65535)
+    return fail(PA_ERR_INVALID, "pa_prefill_chunk: grid too large (%lld x %d)",
+                static_cast<long long>(gx), n_chunks);
+  const int32_t ws_rows = n_chunks * max_q_len;
+  float* ws_ml = nullptr;
+  float* ws_o = nullptr;
+  if (geo.n_split > 1) {
+    const size_t need = static_cast<size_t>(geo.n_split) * ws_rows * H_q * (D + 2) * sizeof(float);
+    if (!ws || ws_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "pa_prefill_chunk: workspace %zu bytes < %zu", ws_bytes, need);
+    ws_o = static_cast<float*>(ws);
+    ws_ml = ws_o + static_cast<size_t>(geo.n_split) * ws_rows * H_q * D;
+  }
+  timing_mark(st, kPrefill, true);
+  hipLaunchKernelGGL((prefill_kernel<CacheT, D>), dim3(static_cast<uint32_t>(gx), n_chunks),
+                     dim3(kPfThreads), 0, st, static_cast<uint16_t*>(out),
+                     static_cast<const uint16_t*>(q), cu_q_lens, start_pos,
+                     static_cast<const typename CacheT::raw*>(k_cache),
+                     static_cast<const typename CacheT::raw*>(v_cache), block_tables, max_blocks,
+                     num_blocks, H_q, geo, score_scale, v_scale, ws_ml, ws_o, ws_rows);
+  timing_mark(st, kPrefill, false);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PA_ERR_DEVICE, "pa_prefill_chunk: launch failed: %s", hipGetErrorString(e));
+  if (geo.n_split > 1) {
+    const int64_t pairs = static_cast<int64_t>(ws_rows) * H_q;
+    timing_mark(st, kPrefillMerge, true);
+    hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3(static_cast<uint32_t>((pairs + 3) / 4)),
+                       dim3(256), 0, st, static_cast<uint16_t*>(out), cu_q_lens, n_chunks, H_q,
+                       geo.n_split, ws_ml, ws_o, ws_rows, v_scale);
+    timing_mark(st, kPrefillMerge, false);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(PA_ERR_DEVICE, "pa_prefill_chunk: merge launch failed: %s",
+                  hipGetErrorString(e));
+  }
+  return PA_OK;
+}
+
+bool prefill_uses_mfma(pa_dtype q_dt, pa_dtype cache_dt) {
+  return q_dt == PA_BF16 && (cache_dt == PA_BF16 || cache_dt == PA_FP8_E4M3);
+}
+
+}  // namespace
 }  // namespace pa
 
 using namespace pa;
 
 extern "C" size_t pa_prefill_workspace_bytes(int32_t n_chunks, int32_t max_q_len, int32_t H_q,
                                              int32_t H_kv, int32_t D, int32_t max_context_len) {
-  (void)n_chunks;
-  (void)max_q_len;
-  (void)H_q;
-  (void)H_kv;
-  (void)D;
-  (void)max_context_len;
-  return 0;
+  if (n_chunks <= 0 || max_q_len <= 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv != 0 ||
+      (D != 64 && D != 128))
+    return 0;
+  const PfGeom geo = pf_geometry(n_chunks, max_q_len, H_q, H_kv, max_context_len);
+  if (geo.n_split <= 1) return 0;
+  return static_cast<size_t>(geo.n_split) * n_chunks * max_q_len * H_q * (D + 2) * sizeof(float);
 }
 
 extern "C" pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, const void* q,
@@ -42,9 +589,6 @@ extern "C" pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, 
                                       int32_t H_kv, int32_t D, int32_t bs, int32_t max_q_len,
                                       int32_t max_context_len, float sm_scale, float k_scale,
                                       float v_scale, void* ws, size_t ws_bytes) {
-  (void)ws;
-  (void)ws_bytes;
-  (void)max_context_len;
   if (bs != kBlock) return fail(PA_ERR_INVALID, "pa_prefill_chunk: block size %d != 16", bs);
   if (n_chunks < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv != 0)
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: n_chunks=%d H_q=%d H_kv=%d", n_chunks, H_q,
@@ -54,6 +598,10 @@ extern "C" pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, 
   if (max_blocks <= 0 || num_blocks <= 0 || max_q_len < 0)
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: max_blocks=%d num_blocks=%d max_q_len=%d",
                 max_blocks, num_blocks, max_q_len);
+  if (max_context_len < max_q_len || static_cast<int64_t>(max_context_len) > 16LL * max_blocks)
+    return fail(PA_ERR_INVALID,
+                "pa_prefill_chunk: max_context_len=%d must lie in [max_q_len=%d, 16*max_blocks=%lld]",
+                max_context_len, max_q_len, 16LL * max_blocks);
   const bool f32 = q_dt == PA_F32 && cache_dt == PA_F32 && out_dt == PA_F32;
   const bool bf = q_dt == PA_BF16 && out_dt == PA_BF16 &&
                   (cache_dt == PA_BF16 || cache_dt == PA_FP8_E4M3);
@@ -67,12 +615,39 @@ extern "C" pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, 
   if (n_chunks == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !cu_q_lens || !start_pos || !k_cache || !v_cache || !block_tables)
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: NULL buffer");
-  if (static_cast<int64_t>(n_chunks) * max_q_len > INT32_MAX)
+  if (static_cast<int64_t>(n_chunks) * max_q_len > INT32_MAX / 64)
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: too many query rows");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // slice lengths live on the device: launch max_q_len rows per slice and let
-  // the rows past each slice's end exit
-  return launch_attend_generic(st, out, out_dt, q, q_dt, k_cache, v_cache, cache_dt, block_tables,
-                               max_blocks, num_blocks, nullptr, cu_q_lens, start_pos, n_chunks,
-                               max_q_len, H_q, H_kv, D, sm_scale, k_scale, v_scale);
+  if (!prefill_uses_mfma(q_dt, cache_dt)) {
+    // slice lengths live on the device: launch max_q_len rows per slice and
+    // let the rows past each slice's end exit
+    return launch_attend_generic(st, out, out_dt, q, q_dt, k_cache, v_cache, cache_dt,
+                                 block_tables, max_blocks, num_blocks, nullptr, cu_q_lens,
+                                 start_pos, n_chunks, max_q_len, H_q, H_kv, D, sm_scale, k_scale,
+                                 v_scale);
+  }
+  // log2-domain score scale; fp8 keys carry k_scale, values v_scale
+  const float kscale = cache_dt == PA_FP8_E4M3 ? k_scale : 1.f;
+  const float vscale = cache_dt == PA_FP8_E4M3 ? v_scale : 1.f;
+  const float score_scale = sm_scale * kscale * kLog2e;
+  if (cache_dt == PA_BF16) {
+    if (D == 128)
+      return launch_prefill_mfma<BF16, 128>(st, out, q, cu_q_lens, start_pos, k_cache, v_cache,
+                                            block_tables, max_blocks, num_blocks, n_chunks, H_q,
+                                            H_kv, max_q_len, max_context_len, score_scale, vscale,
+                                            ws, ws_bytes);
+    return launch_prefill_mfma<BF16, 64>(st, out, q, cu_q_lens, start_pos, k_cache, v_cache,
+                                         block_tables, max_blocks, num_blocks, n_chunks, H_q, H_kv,
+                                         max_q_len, max_context_len, score_scale, vscale, ws,
+                                         ws_bytes);
+  }
+  if (D == 128)
+    return launch_prefill_mfma<FP8, 128>(st, out, q, cu_q_lens, start_pos, k_cache, v_cache,
+                                         block_tables, max_blocks, num_blocks, n_chunks, H_q, H_kv,
+                                         max_q_len, max_context_len, score_scale, vscale, ws,
+                                         ws_bytes);
+  return launch_prefill_mfma<FP8, 64>(st, out, q, cu_q_lens, start_pos, k_cache, v_cache,
+                                      block_tables, max_blocks, num_blocks, n_chunks, H_q, H_kv,
+                                      max_q_len, max_context_len, score_scale, vscale, ws,
+                                      ws_bytes);
 }

@@ -34,7 +34,8 @@ std::mutex g_mu;
 std::atomic<bool> g_enabled{false};
 Track g_tracks[kKernelCount];
 
-const char* kNames[kKernelCount] = {"cache_write", "decode", "decode_merge", "prefill", "generic"};
+const char* kNames[kKernelCount] = {"cache_write", "decode",        "decode_merge",
+                                    "prefill",     "prefill_merge", "generic"};
 
 }  // namespace
 

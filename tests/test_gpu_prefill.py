@@ -50,3 +50,99 @@ def test_slices_f32():
     w = workloads.prefill_workload("f32", 530, prompt_len=150, chunks=[64, 86], h_q=4, h_kv=4, d=64,
                                    dtype="f32", cache_dtype="f32")
     _check(w, "f32")
+
+
+# Work decompositions of the matrix-core kernel: query heads per KV head of
+# 1 (eight 32-position sub-tiles per work-group), 3 (two sub-tiles, six live
+# waves), 4, 8 and 16 (two head groups); head dims 64 and 128.
+@pytest.mark.parametrize("h_q,h_kv,d", [(32, 8, 128), (12, 4, 64), (32, 2, 128), (4, 4, 64)])
+def test_slices_head_groupings(h_q, h_kv, d):
+    w = workloads.prefill_workload("groups", 540 + h_q + d, prompt_len=420,
+                                   chunks=[200, 33, 150, 37], h_q=h_q, h_kv=h_kv, d=d)
+    _check(w, f"bf16 {h_q}/{h_kv} d{d}")
+
+
+# Long prefixes with few query rows: the key range is split over several
+# work-groups and the partial softmax states merged (2, 3 and 4 ranges).
+@pytest.mark.parametrize("prompt,start,n,cache", [(2900, 2600, 300, "bf16"),
+                                                   (5000, 4900, 100, "bf16"),
+                                                   (3100, 2900, 200, "fp8")])
+def test_slices_split_key_range(prompt, start, n, cache):
+    w = workloads.prefill_workload("split", 560 + n, prompts=[prompt], slices=[(0, start, n)],
+                                   cache_dtype=cache)
+    _check(w, f"{cache} split prefix {start}+{n}")
+
+
+def test_slices_split_several_prompts():
+    w = workloads.prefill_workload("split-multi", 575, prompts=[2200, 1300, 2100],
+                                   slices=[(0, 2100, 100), (1, 1280, 20), (2, 1000, 64)])
+    _check(w, "bf16 split, several prompts")
+
+
+def test_slices_single_token_and_block_edges():
+    # slices of 1, 15, 16, 17 and 64 tokens starting on and off block edges
+    w = workloads.prefill_workload("edges", 590, prompt_len=300,
+                                   chunks=[1, 15, 16, 17, 64, 63, 65, 1, 48])
+    _check(w, "bf16 block edges")
+
+
+def _mixed_prefix_run(chunks, sample):
+    """The 32768-token prompt of the mixed chunked-prefill workload, each
+    listed 512-token slice launched alone exactly as the benchmark does;
+    ``sample(c)`` gives the rows compared against the oracle (None = all)."""
+    import torch
+
+    from oracle import allocator as oa
+    from oracle import attention as oat
+    from oracle import cache as oc
+    from oracle import codecs
+    from paged_kv_cache_host_amd.engine import PagedKV, prefill_workspace, to_device_raw, to_host_raw
+
+    w = workloads.mixed_prefill()
+    dev = "cuda"
+    P, C = w.prompt_len, w.chunk
+    kv = PagedKV(w.num_blocks, w.h_kv, w.d, "bf16", dev, w.free_order)
+    assert kv.create(0, P) == 0
+    slots = kv.slots(0, 0, P).astype(np.int32)
+    kv.write(to_device_raw(w.prompt_k, "bf16", dev), to_device_raw(w.prompt_v, "bf16", dev),
+             torch.from_numpy(slots).to(dev))
+    tables, _ = kv.pack([0], P // 16)
+    t_d = torch.from_numpy(tables).to(dev)
+
+    pool = oa.BlockPool(w.num_blocks, 16, w.free_order.tolist())
+    assert pool.seq_create(0, P) == oa.OK
+    assert np.array_equal(np.asarray(pool.block_table(0)), tables[0]), "tables differ"
+    kc, vc = oc.new_cache(w.num_blocks, w.h_kv, 16, w.d, "bf16")
+    oc.cache_write(kc, vc, w.prompt_k, w.prompt_v, pool.slots(0, 0, P), "bf16", "bf16")
+
+    for c in chunks:
+        P0 = c * C
+        say(f"[prefill parity] mixed-prefill chunk {c} (prefix {P0})")
+        q = to_device_raw(w.prompt_q[P0:P0 + C], "bf16", dev)
+        out = torch.full((C, w.h_q, w.d), float("nan"), dtype=torch.bfloat16, device=dev)
+        cu = torch.tensor([0, C], dtype=torch.int32, device=dev)
+        st = torch.tensor([P0], dtype=torch.int32, device=dev)
+        ws = prefill_workspace(1, C, w.h_q, w.h_kv, w.d, P0 + C, dev)
+        kv.prefill(out, q, cu, st, t_d, C, P0 + C, w.sm_scale, ws)
+        torch.cuda.synchronize()
+        got = out_to_f64(to_host_raw(out, "bf16"), "bf16")
+        rows = sample(c)
+        ref = oat.prefill_chunk(codecs.decode(w.prompt_q[P0:P0 + C], "bf16"), P0, kc, vc,
+                                pool.block_table(0), w.h_kv, w.sm_scale, "bf16", rows=rows)
+        err = assert_close(got, ref, "bf16", f"mixed-prefill chunk {c}")
+        if rows is not None:
+            assert not np.isnan(got).any(), "rows left unwritten"
+        say(f"    max|d| = {err:.3g}")
+    kv.close()
+
+
+def test_mixed_prefill_full_size_sampled():
+    rng = np.random.default_rng(77)
+    fixed = np.array([0, 1, 31, 32, 255, 256, 480, 510, 511])
+
+    def sample(c):
+        if c <= 1:
+            return None  # every row
+        return np.unique(np.concatenate([fixed, rng.choice(512, 7, replace=False)]))
+
+    _mixed_prefix_run([0, 1, 31, 63], sample)
