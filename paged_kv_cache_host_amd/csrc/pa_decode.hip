@@ -638,6 +638,8 @@ extern "C" pa_status pa_decode(void* stream, void* out, pa_dtype out_dt, const v
       (!(k_scale > 0.f) || !(v_scale > 0.f) || !__builtin_isfinite(k_scale) ||
        !__builtin_isfinite(v_scale)))
     return fail(PA_ERR_INVALID, "pa_decode: fp8 scales must be finite and > 0");
+  if (!(sm_scale > 0.f) || !__builtin_isfinite(sm_scale))
+    return fail(PA_ERR_INVALID, "pa_decode: sm_scale must be finite and > 0");
   if (S == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID, "pa_decode: NULL buffer");

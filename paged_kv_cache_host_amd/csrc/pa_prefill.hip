@@ -63,7 +63,7 @@ constexpr int kPfMaxSplit = 8;
 constexpr int kPfMinKeysPerSplit = 1024;
 constexpr float kPfLazy = 8.0f;             // log2 headroom of the softmax reference
 
-// LDS bytes of one stage: K [D/8 chunks][64 rows][16 B] + V [D rows][64 keys].
+// LDS bytes of one stage: K [D/8 chunks][64 rows][16 B] + V [D/16][8 chunks][16 dims][16 B].
 template <int D>
 constexpr int stage_bytes() {
   return D * kPfKeys * 2 * 2;
@@ -77,10 +77,12 @@ __device__ __forceinline__ int krow_of(int tok) {
   return (swapped << 2) | (tok & 3);
 }
 
-// V row of dimension d holds 8 chunks of 8 keys (16 B); chunk c sits at
-// c ^ (d & 7) so that the 32 dimensions read by one MFMA step spread over
-// all banks.
-__device__ __forceinline__ int vchunk_pos(int d, int c) { return c ^ (d & 7); }
+// V in LDS: chunk c (8 keys, 16 B) of dimension d.  The 16 dimensions
+// d0..d0+15 of one chunk are 256 contiguous bytes, so the 16 lanes of an
+// MFMA operand read that take consecutive dimensions hit distinct banks.
+__device__ __forceinline__ int v_off(int d, int c) {
+  return (((d >> 4) * (kPfKeys / 8) + c) << 8) | ((d & 15) << 4);
+}
 
 struct PfGeom {
   int H_kv, G, hpw, psub, n_head_groups, n_pos_tiles, n_split;
@@ -185,7 +187,7 @@ struct TileLoader<BF16> {
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(w[j]);
-        *reinterpret_cast<u32x4*>(v_lds + d * (kPfKeys * 2) + vchunk_pos(d, 2 * b + h) * 16) = w;
+        *reinterpret_cast<u32x4*>(v_lds + v_off(d, 2 * b + h)) = w;
       }
     }
   }
@@ -257,8 +259,8 @@ struct TileLoader<FP8> {
             if (key0 + 8 + j >= valid) v1[j] = static_cast<_Float16>(0.0f);
           }
         }
-        *reinterpret_cast<f16x8*>(v_lds + d * (kPfKeys * 2) + vchunk_pos(d, 2 * b) * 16) = v0;
-        *reinterpret_cast<f16x8*>(v_lds + d * (kPfKeys * 2) + vchunk_pos(d, 2 * b + 1) * 16) = v1;
+        *reinterpret_cast<f16x8*>(v_lds + v_off(d, 2 * b)) = v0;
+        *reinterpret_cast<f16x8*>(v_lds + v_off(d, 2 * b + 1)) = v1;
       }
     }
   }
@@ -332,6 +334,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
       if (row_ok) w = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
       qf[ks] = __builtin_bit_cast(bf16x8, w);
     }
+    // Settle the Q loads here: otherwise the counter bookkeeping at the loop
+    // head cannot tell them from the K/V prefetch and waits for all loads
+    // before every tile's first MFMA.
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qf[ks]));
   }
 
   f32x16 o[NDT];
@@ -383,25 +390,26 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
           s[h] = mfma32x32x16(a, qf[ks], s[h]);
         }
       }
-      // scores -> log2 domain, causal mask only where the tile crosses a
-      // query's own position
+      // causal mask, only in the (at most two) tiles that reach past the
+      // wave's first position
       float xv[32];
-      const bool need_mask = key0 + kPfKeys - 1 > wave_first_pos;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float v = s[h][j] * score_scale;
-          if (need_mask) {
-            const int key = key0 + 32 * h + 16 * (j >> 3) + 8 * g + (j & 7);
-            v = key <= qpos ? v : -__builtin_inff();
-          }
-          xv[16 * h + j] = v;
+        for (int j = 0; j < 16; ++j) xv[16 * h + j] = s[h][j];
+      if (key0 + kPfKeys - 1 > wave_first_pos) {
+        const int lim = qpos - key0 - 8 * g;  // largest admissible key offset
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const int off = 32 * (j >> 4) + 16 * ((j >> 3) & 1) + (j & 7);
+          xv[j] = off <= lim ? xv[j] : -__builtin_inff();
         }
+      }
+      // the score scale is positive, so the maximum is taken on raw scores
       float mx = xv[0];
 #pragma unroll
       for (int j = 1; j < 32; ++j) mx = fmaxf(mx, xv[j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * score_scale;
       if (__builtin_amdgcn_ballot_w64(mx > m_run + kPfLazy) != 0) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -416,7 +424,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
-        xv[j] = __builtin_amdgcn_exp2f(xv[j] - mu);
+        xv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(xv[j], score_scale, -mu));
         psum += xv[j];
       }
       l_run += psum;
@@ -428,7 +436,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
         for (int n = 0; n < NDT; ++n) {
           const int d = 32 * n + col;
           const f16x8 a = *reinterpret_cast<const f16x8*>(
-              v_lds + d * (kPfKeys * 2) + vchunk_pos(d, 2 * u + g) * 16);
+              v_lds + v_off(d, 2 * u + g));
           o[n] = mfma32x32x16(a, pb, o[n]);
         }
       }
@@ -477,40 +485,43 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
   }
 }
 
-// Merge the key-range partials of each (row, head): one wave per pair.
+// Merge the key-range partials of each (row, head): D/4 threads per pair,
+// four dimensions each.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(
     uint16_t* __restrict__ out, const int32_t* __restrict__ cu_q_lens, int32_t n_chunks,
     int32_t H_q, int32_t n_split, const float* __restrict__ ws_ml,
     const float* __restrict__ ws_o, int32_t ws_rows, float v_scale) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int64_t total = min(static_cast<int64_t>(cu_q_lens[n_chunks]), static_cast<int64_t>(ws_rows)) * H_q;
+  constexpr int T = D / 4;
+  const int sub = threadIdx.x % T;
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * (256 / T) + threadIdx.x / T;
+  const int64_t total =
+      min(static_cast<int64_t>(cu_q_lens[n_chunks]), static_cast<int64_t>(ws_rows)) * H_q;
   if (pair >= total) return;
+  const int64_t stride = static_cast<int64_t>(ws_rows) * H_q;
   float M = -__builtin_inff();
   for (int j = 0; j < n_split; ++j) {
-    const int64_t slot = static_cast<int64_t>(j) * ws_rows * H_q + pair;
-    if (ws_ml[2 * slot + 1] > 0.f) M = fmaxf(M, ws_ml[2 * slot]);
+    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * (j * stride + pair));
+    if (ml.y > 0.f) M = fmaxf(M, ml.x);
   }
-  constexpr int PER = D / kWave;
-  float acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   for (int j = 0; j < n_split; ++j) {
-    const int64_t slot = static_cast<int64_t>(j) * ws_rows * H_q + pair;
-    const float l = ws_ml[2 * slot + 1];
-    if (!(l > 0.f)) continue;
-    const float w = __builtin_amdgcn_exp2f(ws_ml[2 * slot] - M);
-    L += w * l;
-    const float* po = ws_o + slot * D + lane * PER;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += w * po[i];
+    const int64_t slot = j * stride + pair;
+    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * slot);
+    if (!(ml.y > 0.f)) continue;
+    const float w = __builtin_amdgcn_exp2f(ml.x - M);
+    L += w * ml.y;
+    const f32x4 po = *reinterpret_cast<const f32x4*>(ws_o + slot * D + 4 * sub);
+    acc += w * po;
   }
   const float inv = L > 0.f ? v_scale / L : 0.f;
-  uint16_t* orow = out + pair * D + lane * PER;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) orow[i] = f32_to_bf16(acc[i] * inv);
+  u32x2 w2;
+  w2[0] = static_cast<uint32_t>(f32_to_bf16(acc[0] * inv)) |
+          (static_cast<uint32_t>(f32_to_bf16(acc[1] * inv)) << 16);
+  w2[1] = static_cast<uint32_t>(f32_to_bf16(acc[2] * inv)) |
+          (static_cast<uint32_t>(f32_to_bf16(acc[3] * inv)) << 16);
+  *reinterpret_cast<u32x2*>(out + pair * D + 4 * sub) = w2;
 }
 
 template <typename CacheT, int D>
@@ -549,7 +560,9 @@ pa_status launch_prefill_mfma(hipStream_t st, void* out, const void* q, const in
   if (geo.n_split > 1) {
     const int64_t pairs = static_cast<int64_t>(ws_rows) * H_q;
     timing_mark(st, kPrefillMerge, true);
-    hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3(static_cast<uint32_t>((pairs + 3) / 4)),
+    constexpr int kPairsPerGroup = 256 / (D / 4);
+    hipLaunchKernelGGL((prefill_merge_kernel<D>),
+                       dim3(static_cast<uint32_t>((pairs + kPairsPerGroup - 1) / kPairsPerGroup)),
                        dim3(256), 0, st, static_cast<uint16_t*>(out), cu_q_lens, n_chunks, H_q,
                        geo.n_split, ws_ml, ws_o, ws_rows, v_scale);
     timing_mark(st, kPrefillMerge, false);
@@ -612,6 +625,8 @@ extern "C" pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, 
       (!(k_scale > 0.f) || !(v_scale > 0.f) || !__builtin_isfinite(k_scale) ||
        !__builtin_isfinite(v_scale)))
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: fp8 scales must be finite and > 0");
+  if (!(sm_scale > 0.f) || !__builtin_isfinite(sm_scale))
+    return fail(PA_ERR_INVALID, "pa_prefill_chunk: sm_scale must be finite and > 0");
   if (n_chunks == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !cu_q_lens || !start_pos || !k_cache || !v_cache || !block_tables)
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: NULL buffer");
