@@ -1,25 +1,34 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-attention hot path on one MI355X.
 
-One step = one continuous-batching decode iteration of one 70B-shaped
-attention layer (128 sequences, 64 query / 8 KV heads, head dim 128, bf16,
-16-token blocks, lognormal contexts of mean 1500):
+Headline step (``value``): one continuous-batching decode iteration of one
+70B-shaped attention layer (128 sequences, 64 query / 8 KV heads, head dim
+128, bf16, 16-token blocks, lognormal contexts of mean 1500):
 
   a1  host: libpa grows every sequence by one token (one block taken at each
       block boundary) and packs block tables + context lengths into pinned
       buffers; the tables go to the device on a copy stream, overlapped with
       the previous step's kernels (double-buffered);
   a2  pa_cache_write scatters the new tokens' K/V into their paged slots;
-  a3  pa_decode: split-K paged attention with the split merge fused in.
+  a3  pa_decode: split-K paged attention (+ merge of multi-chunk contexts).
 
-``value`` is the whole step's algorithmic HBM bytes (decode: every K/V byte
-of every context once per KV head, Q, output, block-table entries and
-context lengths; cache write: new K/V read and written) divided by the wall
-time of the timed steps.  ``roofline`` is the decode kernel alone: the
-same algorithmic decode bytes per launch over its average duration from HIP
-events on its own stream.
+``value`` is the step's algorithmic HBM bytes (decode: every K/V byte of
+every context once per KV head, Q, output, block-table entries and context
+lengths; cache write: new K/V read and written) divided by the wall time of
+the timed steps.  ``roofline`` is the decode kernel alone: the same
+algorithmic decode bytes per launch over its mean duration from HIP events
+on its own stream (libpa's pa_timing_* facility).
+
+Secondary legs (skipped with --decode-only):
+  ``mixed``      the chunked-prefill iteration: a 32768-token prompt as 64
+                 causal 512-token slices, each iteration also decoding one
+                 token for 127 sequences; tokens/s per layer over the 64
+                 iterations, and the prefill kernel's bf16 MFMA TFLOP/s on
+                 the algorithmic causal flop count;
+  ``fp8_decode`` 64 sequences at context 8192 with an e4m3fn cache.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+                       [--decode-only]
 """
 from __future__ import annotations
 
@@ -38,6 +47,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 H_Q, H_KV, D, BLOCK = 64, 8, 128, 16
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -48,6 +58,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode step (no mixed chunked-prefill or fp8 legs)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=32)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain streaming kernel of known size (HBM counter calibration)")
@@ -188,8 +200,8 @@ def pmc_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_di
     """HBM traffic of one decode launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
     runs (KiB per dispatch), each scaled by what the same counter reads for
     the calibration kernel of known size."""
-    f_dec, n_f = _pmc_mean(_pmc_rows(fetch_dir, "FETCH_SIZE"), "decode_kernel")
-    w_dec, n_w = _pmc_mean(_pmc_rows(write_dir, "WRITE_SIZE"), "decode_kernel")
+    f_dec, n_f = _pmc_mean(_pmc_rows(fetch_dir, "FETCH_SIZE"), "decode_kernel<pa::BF16, 128>")
+    w_dec, n_w = _pmc_mean(_pmc_rows(write_dir, "WRITE_SIZE"), "decode_kernel<pa::BF16, 128>")
     f_cal, _ = _pmc_mean(_pmc_rows(cal_fetch_dir, "FETCH_SIZE"), "neg")
     w_cal, _ = _pmc_mean(_pmc_rows(cal_write_dir, "WRITE_SIZE"), "neg")
     f_scale = CAL_BYTES / (f_cal * 1024.0)
@@ -210,32 +222,35 @@ def pmc_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_di
     print(json.dumps(out, indent=1))
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the paged-attention path shards by sequence or KV head with no exchange, so "
-              "multi-GPU figures are not produced here.", file=sys.stderr)
-        sys.exit(2)
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    if args.pmc_summary:
-        pmc_summary(*args.pmc_summary)
-        return
+def _fill_random(kv, slots: np.ndarray, gen, dev, chunk: int = 1 << 16):
+    """Untimed set-up: write N(0,1) bf16 K/V for the given slots through
+    pa_cache_write."""
+    import torch
+    for a in range(0, len(slots), chunk):
+        n = min(chunk, len(slots) - a)
+        kk = torch.randn((n, H_KV, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        vv = torch.randn((n, H_KV, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        kv.write(kk, vv, torch.from_numpy(np.ascontiguousarray(slots[a:a + n], dtype=np.int32)).to(dev))
 
+
+def _timings(pa, names):
+    out = {}
+    for name in names:
+        st, cnt, mean_us, tot_us = pa.pa_timing_query(name)
+        pa.check(st)
+        out[name] = (cnt, mean_us, tot_us)
+    return out
+
+
+def decode_leg(args, dev):
+    """The headline step: one decode iteration of the decode-70b layer."""
     import torch
 
     import workloads
     from paged_kv_cache_host_amd import _pa as pa
     from paged_kv_cache_host_amd.engine import PagedKV, decode_workspace, sm_scale_for
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     K, W = args.steps, args.warmup
-
     lengths, num_blocks, free_order = workloads.decode_70b_layout()
     S = len(lengths)
     seqs = np.arange(S, dtype=np.int64)
@@ -251,13 +266,7 @@ def main():
         pa.check(kv.create(s, int(lengths[s]) - 1))
         if lengths[s] > 1:
             fill_slots.append(kv.slots(s, 0, int(lengths[s]) - 1))
-    fill_slots = np.concatenate(fill_slots).astype(np.int32)
-    CH = 1 << 16
-    for a in range(0, len(fill_slots), CH):
-        n = min(CH, len(fill_slots) - a)
-        kk = torch.randn((n, H_KV, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        vv = torch.randn((n, H_KV, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        kv.write(kk, vv, torch.from_numpy(fill_slots[a:a + n]).to(dev))
+    _fill_random(kv, np.concatenate(fill_slots), gen, dev)
     R = 4
     k_ring = [torch.randn((S, H_KV, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
     v_ring = [torch.randn((S, H_KV, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
@@ -280,7 +289,7 @@ def main():
         e.record(compute)
     ctx_lens = []
 
-    def step(i: int, timed_idx: int | None):
+    def step(i: int, timed: bool):
         X = i & 1
         ev_consumed[X].synchronize()
         st, done, _ = pa.pa_batch_append(kv.pool, seqs, 1, slots_pin[X].numpy())
@@ -299,12 +308,12 @@ def main():
                                    num_blocks, H_KV, D, BLOCK))
         pa.check(pa.pa_decode(compute, out, q_ring[r], kv.k, kv.v, tables_dev[X], lens_dev[X],
                               num_blocks, H_KV, max_ctx, sm, 1.0, 1.0, ws))
-        if timed_idx is not None:
+        if timed:
             ctx_lens.append(lens_np.copy())
         ev_consumed[X].record(compute)
 
     for i in range(W):
-        step(i, None)
+        step(i, False)
     torch.cuda.synchronize()
     # The library brackets each of its kernel launches with HIP events on the
     # stream it launches on (here `compute`); reset and enable for the timed
@@ -312,34 +321,276 @@ def main():
     pa.check(pa.pa_timing_enable(True))
     t0 = time.perf_counter()
     for i in range(K):
-        step(W + i, i)
+        step(W + i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    timings = {}
-    for name in ("decode", "decode_merge", "cache_write"):
-        st, cnt, mean_us, tot_us = pa.pa_timing_query(name)
-        pa.check(st)
-        timings[name] = (cnt, mean_us)
+    tm = _timings(pa, ("decode", "decode_merge", "cache_write"))
     pa.check(pa.pa_timing_enable(False))
-    assert timings["decode"][0] == K, timings
+    assert tm["decode"][0] == K, tm
+    kv.close()
 
     dec_bytes = [decode_bytes(l) for l in ctx_lens]
-    cw = cache_write_bytes(S)
-    total_bytes = sum(dec_bytes) + K * cw
-    value = total_bytes / wall / 1e9
-    dec_avg_s = timings["decode"][1] / 1e6
-    achieved = (sum(dec_bytes) / K) / dec_avg_s / 1e9
-    digest = kernel_source_digest()
-    traffic = traffic_from_profile(digest)
+    total_bytes = sum(dec_bytes) + K * cache_write_bytes(S)
+    dec_avg_s = tm["decode"][1] / 1e6
+    return {
+        "value": total_bytes / wall / 1e9,
+        "wall": wall,
+        "mean_context": float(np.mean([l.mean() for l in ctx_lens])),
+        "num_seqs": S, "num_blocks": num_blocks,
+        "achieved": (sum(dec_bytes) / K) / dec_avg_s / 1e9,
+        "kernel_us": dec_avg_s * 1e6,
+        "merge_us": tm["decode_merge"][1], "cache_write_us": tm["cache_write"][1],
+        "bytes_per_launch": int(sum(dec_bytes) / K),
+    }
 
+
+def mixed_leg(args, dev):
+    """The chunked-prefill mixed batch: a 32768-token prompt as 64 causal
+    512-token slices; every iteration also decodes one token for each of 127
+    sequences.  One iteration = host append/pack + one pa_cache_write of the
+    639 new tokens + pa_prefill_chunk of the slice + pa_decode of the 127
+    sequences.  Reported as tokens/s per layer over the 64 iterations, plus
+    the prefill kernel's bf16 MFMA throughput."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_host_amd import _pa as pa
+    from paged_kv_cache_host_amd.engine import (PagedKV, decode_workspace, prefill_workspace,
+                                                sm_scale_for)
+
+    P, C = 32768, 512
+    iters = P // C
+    dec_len, num_blocks, free_order = workloads.mixed_prefill_layout()
+    S = len(dec_len)
+    PROMPT = S  # sequence id of the prompt
+    dec_seqs = np.arange(S, dtype=np.int64)
+    max_dec = int(dec_len.max()) + iters
+    MB = -(-max_dec // BLOCK)
+    PB = P // BLOCK
+    NT = C + S
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    sm = sm_scale_for(D)
+
+    R = 2
+    k_ring = [torch.randn((NT, H_KV, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    v_ring = [torch.randn((NT, H_KV, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    q_prompt = torch.randn((P, H_Q, D), generator=gen, device=dev).to(torch.bfloat16)
+    q_dec = [torch.randn((S, H_Q, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    out_p = torch.empty((C, H_Q, D), dtype=torch.bfloat16, device=dev)
+    out_d = torch.empty((S, H_Q, D), dtype=torch.bfloat16, device=dev)
+    ws_d = decode_workspace(S, H_Q, H_KV, D, max_dec, dev)
+    ws_p = torch.empty(max(1, max(pa.pa_prefill_workspace_bytes(1, C, H_Q, H_KV, D, (c + 1) * C)
+                                  for c in range(iters))), dtype=torch.uint8, device=dev)
+    cu = torch.tensor([0, C], dtype=torch.int32, device=dev)
+
+    slots_pin = [torch.empty((NT,), dtype=torch.int32).pin_memory() for _ in range(2)]
+    start_pin = [torch.empty((1,), dtype=torch.int32).pin_memory() for _ in range(2)]
+    tables_pin = [torch.empty((S, MB), dtype=torch.int32).pin_memory() for _ in range(2)]
+    lens_pin = [torch.empty((S,), dtype=torch.int32).pin_memory() for _ in range(2)]
+    slots_dev = [torch.empty((NT,), dtype=torch.int32, device=dev) for _ in range(2)]
+    start_dev = [torch.empty((1,), dtype=torch.int32, device=dev) for _ in range(2)]
+    tables_dev = [torch.empty((S, MB), dtype=torch.int32, device=dev) for _ in range(2)]
+    lens_dev = [torch.empty((S,), dtype=torch.int32, device=dev) for _ in range(2)]
+    compute = torch.cuda.Stream(device=dev)
+    copy = torch.cuda.Stream(device=dev)
+    ev_copied = [torch.cuda.Event() for _ in range(2)]
+    ev_consumed = [torch.cuda.Event() for _ in range(2)]
+
+    def run_pass(timed: bool, n_iters: int):
+        # fresh pool: decode contexts of L0-1 tokens cached, prompt blocks
+        # allocated at admission (its K/V are written slice by slice)
+        kv = PagedKV(num_blocks, H_KV, D, "bf16", dev, free_order)
+        fill = []
+        for s in range(S):
+            pa.check(kv.create(s, int(dec_len[s]) - 1))
+            fill.append(kv.slots(s, 0, int(dec_len[s]) - 1))
+        _fill_random(kv, np.concatenate(fill), gen, dev)
+        pa.check(kv.create(PROMPT, P))
+        ptab, _ = kv.pack([PROMPT], PB)
+        ptab_dev = torch.from_numpy(ptab).to(dev)
+        torch.cuda.synchronize()
+        for e in ev_consumed:
+            e.record(compute)
+        if timed:
+            pa.check(pa.pa_timing_enable(True))
+        t0 = time.perf_counter()
+        for c in range(n_iters):
+            X = c & 1
+            ev_consumed[X].synchronize()
+            sl = slots_pin[X].numpy()
+            pa.check(pa.pa_seq_slots(kv.pool, PROMPT, c * C, C, sl[:C])[0])
+            st, _, _ = pa.pa_batch_append(kv.pool, dec_seqs, 1, sl[C:].reshape(S, 1))
+            pa.check(st)
+            st, _, _ = pa.pa_pack_batch(kv.pool, dec_seqs, MB, tables_pin[X].numpy(),
+                                        lens_pin[X].numpy())
+            pa.check(st)
+            start_pin[X][0] = c * C
+            with torch.cuda.stream(copy):
+                slots_dev[X].copy_(slots_pin[X], non_blocking=True)
+                start_dev[X].copy_(start_pin[X], non_blocking=True)
+                tables_dev[X].copy_(tables_pin[X], non_blocking=True)
+                lens_dev[X].copy_(lens_pin[X], non_blocking=True)
+                ev_copied[X].record(copy)
+            compute.wait_event(ev_copied[X])
+            r = c % R
+            pa.check(pa.pa_cache_write(compute, k_ring[r], v_ring[r], slots_dev[X], kv.k, kv.v,
+                                       num_blocks, H_KV, D, BLOCK))
+            pa.check(pa.pa_prefill_chunk(compute, out_p, q_prompt[c * C:(c + 1) * C], cu,
+                                         start_dev[X], kv.k, kv.v, ptab_dev, num_blocks, H_KV, C,
+                                         (c + 1) * C, sm, 1.0, 1.0, ws_p))
+            pa.check(pa.pa_decode(compute, out_d, q_dec[r], kv.k, kv.v, tables_dev[X],
+                                  lens_dev[X], num_blocks, H_KV, max_dec, sm, 1.0, 1.0, ws_d))
+            ev_consumed[X].record(compute)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        tm = None
+        if timed:
+            tm = _timings(pa, ("prefill", "prefill_merge", "decode", "decode_merge", "cache_write"))
+            pa.check(pa.pa_timing_enable(False))
+        kv.close()
+        return wall, tm
+
+    run_pass(False, min(iters, max(args.warmup, 1) * 4))
+    wall, tm = run_pass(True, iters)
+    pairs = sum(C * (c * C) + C * (C + 1) // 2 for c in range(iters))
+    flops = 4 * D * H_Q * pairs
+    n_pf, mean_pf, tot_pf = tm["prefill"]
+    assert n_pf == iters, tm
+    achieved = flops / (tot_pf / 1e6) / 1e12
+    return {
+        "tokens_per_s": iters * NT / wall,
+        "ms_per_iteration": wall / iters * 1e3,
+        "iterations": iters,
+        "tokens_per_iteration": NT,
+        "prefill_roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "traffic": None, "kernel": "prefill_kernel<BF16,128>",
+                             "kernel_us_total": round(tot_pf, 1),
+                             "algorithmic_flops": flops},
+        "other_kernels_us_total": {k: round(tm[k][2], 1) for k in
+                                   ("prefill_merge", "decode", "decode_merge", "cache_write")},
+    }
+
+
+def fp8_leg(args, dev):
+    """Long-context fp8 decode: 64 sequences at context 8192, e4m3fn K/V with
+    per-tensor scales, bf16 Q; kernel time of pa_decode over `steps` launches."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_host_amd import _pa as pa
+    from paged_kv_cache_host_amd.engine import PagedKV, decode_workspace, sm_scale_for
+
+    S, L = 64, 8192
+    _, lengths, num_blocks, free_order = workloads.decode_layout(
+        4, lambda rng: np.full(S, L, dtype=np.int64), lambda Ls: workloads.blocks_needed(Ls))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    # amax/448 of an N(0,1) source of this size: the scale is a plain input here
+    kv = PagedKV(num_blocks, H_KV, D, "fp8", dev, free_order, 4.9 / 448.0, 4.9 / 448.0)
+    fill = []
+    for s in range(S):
+        pa.check(kv.create(s, L))
+        fill.append(kv.slots(s, 0, L))
+    _fill_random(kv, np.concatenate(fill), gen, dev)
+    tables, lens = kv.pack(list(range(S)), L // BLOCK)
+    t_d = torch.from_numpy(tables).to(dev)
+    l_d = torch.from_numpy(lens).to(dev)
+    q = torch.randn((S, H_Q, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((S, H_Q, D), dtype=torch.bfloat16, device=dev)
+    ws = decode_workspace(S, H_Q, H_KV, D, L, dev)
+    sm = sm_scale_for(D)
+    for _ in range(args.warmup):
+        kv.decode(out, q, t_d, l_d, L, sm, ws)
+    torch.cuda.synchronize()
+    pa.check(pa.pa_timing_enable(True))
+    for _ in range(args.steps):
+        kv.decode(out, q, t_d, l_d, L, sm, ws)
+    torch.cuda.synchronize()
+    tm = _timings(pa, ("decode", "decode_merge"))
+    pa.check(pa.pa_timing_enable(False))
+    kv.close()
+    nbytes = S * L * H_KV * D * 2 * 1 + S * H_Q * D * 4 + S * (L // BLOCK) * 4 + 4 * S
+    k_us = tm["decode"][1]
+    return {"workload": "fp8 decode: 64 seqs x ctx 8192, 64/8 heads, d128, e4m3fn KV, bf16 Q",
+            "bound": "hbm", "achieved": round(nbytes / (k_us / 1e6) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(nbytes / (k_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel": "decode_kernel<FP8,128>", "kernel_us": round(k_us, 2),
+            "merge_us": round(tm["decode_merge"][1], 2), "algorithmic_bytes_per_launch": nbytes}
+
+
+def cpu_prefill_baseline():
+    """The oracle on one 512-token slice at prefix 512 (gather + fp64 causal
+    attention of all 64 heads), as GFLOP/s on the algorithmic count."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import allocator as oa
+    from oracle import attention as oat
+    from oracle import cache as oc
+    from oracle import codecs
+    import workloads
+
+    rng = np.random.default_rng(13)
+    P0, C = 512, 512
+    n = P0 + C
+    nb = n // BLOCK + 4
+    pool = oa.BlockPool(nb, BLOCK, rng.permutation(nb).tolist())
+    pool.seq_create(0, n)
+    kc, vc = oc.new_cache(nb, H_KV, BLOCK, D, "bf16")
+    oc.cache_write(kc, vc, workloads.normal_raw(rng, (n, H_KV, D), "bf16"),
+                   workloads.normal_raw(rng, (n, H_KV, D), "bf16"), pool.slots(0, 0, n),
+                   "bf16", "bf16")
+    q = codecs.decode(workloads.normal_raw(rng, (C, H_Q, D), "bf16"), "bf16")
+    sm = float(np.float32(1.0) / np.float32(math.sqrt(D)))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oat.prefill_chunk(q, P0, kc, vc, pool.block_table(0), H_KV, sm, "bf16")
+        reps += 1
+        if time.perf_counter() - t0 > 8.0:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    flops = 4 * D * H_Q * (C * P0 + C * (C + 1) // 2)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e9, "unit": "GFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one 512-token slice at prefix 512 (all 64 heads), mean of {reps} runs"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the paged-attention path shards by sequence or KV head with no exchange, so "
+              "multi-GPU figures are not produced here.", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, W = args.steps, args.warmup
+
+    d = decode_leg(args, dev)
+    digest = kernel_source_digest()
     result = {
         "metric": "paged-attn decode HBM GB/s (% peak); mixed decode+prefill tokens/s per layer",
-        "value": round(value, 2),
+        "value": round(d["value"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(wall / K * 1e3, 4),
+        "ms_per_step": round(d["wall"] / K * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -348,23 +599,30 @@ def main():
         "config": {"workload": "decode-70b-shaped: 128 seqs, 64/8 heads, d128, bf16 KV, "
                                "block 16, lognormal ctx mean 1500 (one layer, one decode "
                                "iteration per step incl. host append + cache write)",
-                   "num_seqs": S, "mean_context": round(float(np.mean([l.mean() for l in ctx_lens])), 1),
-                   "num_blocks": num_blocks},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_kernel<BF16,128>",
-                     "kernel_us": round(dec_avg_s * 1e6, 2),
-                     "other_kernels_us": {"decode_merge_kernel": round(timings["decode_merge"][1], 2),
-                                          "cache_write_kernel": round(timings["cache_write"][1], 2)},
-                     "algorithmic_bytes_per_launch": int(sum(dec_bytes) / K),
+                   "num_seqs": d["num_seqs"], "mean_context": round(d["mean_context"], 1),
+                   "num_blocks": d["num_blocks"]},
+        "roofline": {"bound": "hbm", "achieved": round(d["achieved"], 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(d["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(digest), "kernel": "decode_kernel<BF16,128>",
+                     "kernel_us": round(d["kernel_us"], 2),
+                     "other_kernels_us": {"decode_merge_kernel": round(d["merge_us"], 2),
+                                          "cache_write_kernel": round(d["cache_write_us"], 2)},
+                     "algorithmic_bytes_per_launch": d["bytes_per_launch"],
                      "kernel_source_digest": digest},
     }
+    if not args.decode_only:
+        m = mixed_leg(args, dev)
+        m["workload"] = ("mixed chunked prefill: 32768-token prompt as 64 causal 512-token "
+                         "slices + 127 decodes per iteration, 64/8 heads, d128, bf16")
+        result["mixed"] = m
+        result["fp8_decode"] = fp8_leg(args, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample_seqs)
+        if "mixed" in result:
+            result["mixed"]["cpu_baseline"] = cpu_prefill_baseline()
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
-    kv.close()
 
 
 if __name__ == "__main__":

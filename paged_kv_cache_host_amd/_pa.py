@@ -164,8 +164,11 @@ def pa_batch_append(pool, seqs, n_new: int = 1, slots_out: np.ndarray | None = N
     return st, done.value, slots_out
 
 
-def pa_seq_slots(pool, seq: int, start: int, n: int):
-    buf = np.empty(max(n, 0), dtype=np.int32)
+def pa_seq_slots(pool, seq: int, start: int, n: int, out: np.ndarray | None = None):
+    """Returns (status, slots); ``out`` (int32, >= n entries, e.g. a pinned
+    tensor's numpy view) is filled in place when given."""
+    buf = np.empty(max(n, 0), dtype=np.int32) if out is None else out
+    assert buf.dtype == np.int32 and buf.flags.c_contiguous and buf.size >= n
     st = _lib.pa_seq_slots(pool, seq, start, n, _ptr_i32(buf))
     return st, buf
 

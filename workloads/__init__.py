@@ -185,17 +185,30 @@ class MixedWorkload:
         return self.prompt_len // self.chunk
 
 
+def _mixed_layout(rng, prompt_len, chunk, num_decode):
+    lengths = lognormal_lengths(rng, num_decode)
+    iters = prompt_len // chunk
+    need = prompt_len // BLOCK + blocks_needed(lengths + iters)
+    num_blocks = math.ceil(1.1 * need)
+    free_order = rng.permutation(num_blocks).astype(np.int32)
+    return lengths, num_blocks, free_order
+
+
+def mixed_prefill_layout(seed: int = 3, prompt_len: int = 32768, chunk: int = 512,
+                         num_decode: int = 127):
+    """(decode lengths, pool size, free order) of ``mixed_prefill`` without
+    its data."""
+    return _mixed_layout(np.random.default_rng(seed), prompt_len, chunk, num_decode)
+
+
 def mixed_prefill(seed: int = 3, prompt_len: int = 32768, chunk: int = 512,
                   num_decode: int = 127) -> MixedWorkload:
     """A 32768-token prompt as 64 causal 512-token slices, each iteration also
     decoding one token for each of 127 sequences (lengths as the 70B decode
     workload, growing by one per iteration)."""
     rng = np.random.default_rng(seed)
-    lengths = lognormal_lengths(rng, num_decode)
+    lengths, num_blocks, free_order = _mixed_layout(rng, prompt_len, chunk, num_decode)
     iters = prompt_len // chunk
-    need = prompt_len // BLOCK + blocks_needed(lengths + iters)
-    num_blocks = math.ceil(1.1 * need)
-    free_order = rng.permutation(num_blocks).astype(np.int32)
     h_q, h_kv, d = 64, 8, 128
     prompt_k = normal_raw(rng, (prompt_len, h_kv, d), "bf16")
     prompt_v = normal_raw(rng, (prompt_len, h_kv, d), "bf16")
