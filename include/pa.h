@@ -248,6 +248,75 @@ pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, const void*
                            float k_scale, float v_scale, void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * Iteration-level scheduler over a pool (host).
+ *
+ * LESSON "Continuous batching at the iteration level", "What the scheduler
+ * looks like" and "Chunked prefill"; ARTICLE 3.1 (growth before admission,
+ * preemption of the sequence that cannot grow, admission capped by a
+ * running-sequence limit with ceil(prompt/bs) blocks at once, stop at the
+ * first request that does not fit) and 3.2 (recovery by recomputation).
+ *
+ * One pa_sched_step is one iteration: (1) sequences that produced their
+ * target number of tokens are released; (2) every decode-phase sequence
+ * appends one token (its slot is reported; on PA_ERR_NO_BLOCKS the sequence
+ * is preempted: blocks freed, progress reset to prefill all of prompt +
+ * output so far, queued at the back); (3) waiting sequences are admitted in
+ * arrival order while fewer than max_running run and the head fits; (4)
+ * prefill slices are handed out in running order until prefill_budget
+ * tokens are spent.  The slice that completes a sequence's known tokens
+ * yields its next output token.  The caller writes the reported tokens'
+ * K/V (pa_cache_write) and runs attention before the next step.
+ *
+ * The scheduler drives its pool through the pa_seq_* calls; the pool must
+ * not be used for other sequences meanwhile.  Not thread-safe.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_sched pa_sched;
+
+/* Output arrays of one step, owned by the caller (host memory).  Capacities
+ * must be at least max_running (decode_cap, prefill_cap, event_cap) and
+ * prefill_budget (prefill_slots_cap); pa_sched_step checks them before
+ * changing anything. */
+typedef struct pa_sched_batch {
+  int64_t* decode_seq;     /* [decode_cap] sequences given one decode token  */
+  int32_t* decode_pos;     /* [decode_cap] position of that token            */
+  int32_t* decode_slot;    /* [decode_cap] its cache slot                    */
+  int32_t decode_cap;
+  int64_t* prefill_seq;    /* [prefill_cap] sequence of each prefill slice    */
+  int32_t* prefill_start;  /* [prefill_cap] first position of the slice       */
+  int32_t* prefill_len;    /* [prefill_cap] tokens in the slice               */
+  int32_t prefill_cap;
+  int32_t* prefill_slots;  /* [prefill_slots_cap] slots of all slices, in order */
+  int32_t prefill_slots_cap;
+  int64_t* finished;       /* [event_cap] released this step                 */
+  int64_t* admitted;       /* [event_cap] admitted this step                  */
+  int64_t* preempted;      /* [event_cap] preempted this step                 */
+  int32_t event_cap;
+  /* filled by pa_sched_step */
+  int32_t n_decode, n_prefill, n_prefill_tokens, n_finished, n_admitted, n_preempted;
+} pa_sched_batch;
+
+/* Accounting over the running sequences (ARTICLE 2.2 / LESSON "The Concept:
+ * PagedAttention as a virtual memory system"): blocks held, tokens those
+ * blocks are allocated for, and of those the prompt slots not yet handed out
+ * as prefill (reserved at admission, not yet written).  Internal waste =
+ * 1 - tokens_held / (block_size * blocks_held). */
+typedef struct pa_sched_accounting {
+  int32_t running, waiting;
+  int64_t finished, preemptions;
+  int64_t blocks_held, tokens_held, unwritten;
+} pa_sched_accounting;
+
+/* block_size must equal the pool's.  PA_ERR_INVALID on bad sizes. */
+pa_status pa_sched_create(pa_pool* pool, int32_t max_running, int32_t prefill_budget,
+                          int32_t block_size, pa_sched** out);
+void pa_sched_destroy(pa_sched* sched);
+/* Queue a request (prompt_len >= 1 tokens, target >= 1 output tokens);
+ * PA_ERR_EXISTS if the id was ever added. */
+pa_status pa_sched_add(pa_sched* sched, int64_t seq, int32_t prompt_len, int32_t target);
+pa_status pa_sched_step(pa_sched* sched, pa_sched_batch* batch);
+pa_status pa_sched_stats(const pa_sched* sched, pa_sched_accounting* out);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (instrumentation, off by default).  When enabled, each
  * kernel launch of the calls above is bracketed by a pair of HIP events
  * recorded on the caller's stream (up to 4096 launches per kernel between

@@ -40,6 +40,25 @@ _i64 = C.c_int64
 _f32 = C.c_float
 _sz = C.c_size_t
 
+class SchedBatchC(C.Structure):
+    """``pa_sched_batch`` of include/pa.h."""
+    _fields_ = [("decode_seq", _i64p), ("decode_pos", _i32p), ("decode_slot", _i32p),
+                ("decode_cap", _i32),
+                ("prefill_seq", _i64p), ("prefill_start", _i32p), ("prefill_len", _i32p),
+                ("prefill_cap", _i32),
+                ("prefill_slots", _i32p), ("prefill_slots_cap", _i32),
+                ("finished", _i64p), ("admitted", _i64p), ("preempted", _i64p),
+                ("event_cap", _i32),
+                ("n_decode", _i32), ("n_prefill", _i32), ("n_prefill_tokens", _i32),
+                ("n_finished", _i32), ("n_admitted", _i32), ("n_preempted", _i32)]
+
+
+class SchedAccountingC(C.Structure):
+    """``pa_sched_accounting`` of include/pa.h."""
+    _fields_ = [("running", _i32), ("waiting", _i32), ("finished", _i64), ("preemptions", _i64),
+                ("blocks_held", _i64), ("tokens_held", _i64), ("unwritten", _i64)]
+
+
 _SIGS = {
     "pa_version": (_i32, []),
     "pa_last_error": (C.c_char_p, []),
@@ -62,6 +81,11 @@ _SIGS = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _i32,
                          _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32, _vp, _sz]),
+    "pa_sched_create": (_i32, [_vp, _i32, _i32, _i32, C.POINTER(_vp)]),
+    "pa_sched_destroy": (None, [_vp]),
+    "pa_sched_add": (_i32, [_vp, _i64, _i32, _i32]),
+    "pa_sched_step": (_i32, [_vp, C.POINTER(SchedBatchC)]),
+    "pa_sched_stats": (_i32, [_vp, C.POINTER(SchedAccountingC)]),
     "pa_timing_enable": (_i32, [_i32]),
     "pa_timing_query": (_i32, [C.c_char_p, _i32p, C.POINTER(_f32), C.POINTER(_f32)]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -217,6 +241,86 @@ def pa_validate_tables(block_tables, context_lens, max_blocks: int, block_size: 
     lens = _i32_array(context_lens)
     return _lib.pa_validate_tables(_ptr_i32(t), _ptr_i32(lens), len(lens), max_blocks, block_size,
                                    num_blocks)
+
+
+# ----------------------------------------------------------- scheduler -----
+
+def pa_sched_create(pool, max_running: int = 256, prefill_budget: int = 512,
+                    block_size: int = 16):
+    """Returns (status, scheduler handle or None)."""
+    out = _vp()
+    st = _lib.pa_sched_create(pool, max_running, prefill_budget, block_size, C.byref(out))
+    return st, (out.value if st == PA_OK else None)
+
+
+def pa_sched_destroy(sched) -> None:
+    _lib.pa_sched_destroy(sched)
+
+
+def pa_sched_add(sched, seq: int, prompt_len: int, target: int) -> int:
+    return _lib.pa_sched_add(sched, seq, prompt_len, target)
+
+
+class SchedBatch:
+    """Host arrays of one pa_sched_step (numpy views, reused every step)."""
+
+    def __init__(self, max_running: int, prefill_budget: int):
+        R, B = max_running, max(prefill_budget, 1)
+        self.decode_seq = np.zeros(R, np.int64)
+        self.decode_pos = np.zeros(R, np.int32)
+        self.decode_slot = np.zeros(R, np.int32)
+        self.prefill_seq = np.zeros(R, np.int64)
+        self.prefill_start = np.zeros(R, np.int32)
+        self.prefill_len = np.zeros(R, np.int32)
+        self.prefill_slots = np.zeros(B, np.int32)
+        self.finished = np.zeros(R, np.int64)
+        self.admitted = np.zeros(R, np.int64)
+        self.preempted = np.zeros(R, np.int64)
+        p64 = lambda a: a.ctypes.data_as(_i64p)
+        self.c = SchedBatchC(p64(self.decode_seq), _ptr_i32(self.decode_pos),
+                             _ptr_i32(self.decode_slot), R, p64(self.prefill_seq),
+                             _ptr_i32(self.prefill_start), _ptr_i32(self.prefill_len), R,
+                             _ptr_i32(self.prefill_slots), B, p64(self.finished),
+                             p64(self.admitted), p64(self.preempted), R, 0, 0, 0, 0, 0, 0)
+
+    @property
+    def n_decode(self):
+        return self.c.n_decode
+
+    @property
+    def n_prefill(self):
+        return self.c.n_prefill
+
+    @property
+    def n_prefill_tokens(self):
+        return self.c.n_prefill_tokens
+
+    def decode(self):
+        n = self.c.n_decode
+        return self.decode_seq[:n], self.decode_pos[:n], self.decode_slot[:n]
+
+    def prefill(self):
+        n = self.c.n_prefill
+        return self.prefill_seq[:n], self.prefill_start[:n], self.prefill_len[:n]
+
+    def slots(self):
+        return self.prefill_slots[:self.c.n_prefill_tokens]
+
+    def events(self):
+        return (self.finished[:self.c.n_finished].tolist(),
+                self.admitted[:self.c.n_admitted].tolist(),
+                self.preempted[:self.c.n_preempted].tolist())
+
+
+def pa_sched_step(sched, batch: SchedBatch) -> int:
+    return _lib.pa_sched_step(sched, C.byref(batch.c))
+
+
+def pa_sched_stats(sched):
+    """Returns (status, dict of the accounting fields)."""
+    a = SchedAccountingC()
+    st = _lib.pa_sched_stats(sched, C.byref(a))
+    return st, {k: getattr(a, k) for k, _ in SchedAccountingC._fields_}
 
 
 # -------------------------------------------------------------- timing -----
