@@ -25,7 +25,10 @@ Secondary legs (skipped with --decode-only):
                  token for 127 sequences; tokens/s per layer over the 64
                  iterations, and the prefill kernel's bf16 MFMA TFLOP/s on
                  the algorithmic causal flop count;
-  ``fp8_decode`` 64 sequences at context 8192 with an e4m3fn cache.
+  ``fp8_decode`` 64 sequences at context 8192 with an e4m3fn cache;
+  ``trace``      1000 continuous-batching iterations (libpa scheduler +
+                 kernels) with Poisson arrivals: tokens/s per layer and KV
+                 fragmentation.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
                        [--decode-only]
@@ -522,6 +525,98 @@ def fp8_leg(args, dev):
             "merge_us": round(tm["decode_merge"][1], 2), "algorithmic_bytes_per_launch": nbytes}
 
 
+def trace_leg(args, dev):
+    """The continuous-batching trace: Poisson arrivals, lognormal prompts,
+    geometric outputs, 256 running, 512-token prefill budget, 1000
+    iterations of scheduling + cache write + decode/prefill attention for one
+    layer.  Reports tokens/s per layer and KV fragmentation."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_host_amd import _pa as pa
+    from paged_kv_cache_host_amd.iteration import LayerIterations
+
+    w = workloads.trace()
+    max_ctx = max(p + o for row in w.arrivals for _, p, o in row)
+    # Host-only dry run of the same scheduler: the highest block id the trace
+    # touches (the FIFO pool hands out low ids first).
+    st, pool = pa.pa_pool_create(w.num_blocks, BLOCK, None)
+    pa.check(st)
+    st, sch = pa.pa_sched_create(pool, w.max_running, w.prefill_budget, BLOCK)
+    pa.check(st)
+    b = pa.SchedBatch(w.max_running, w.prefill_budget)
+    top = 0
+    for it in range(w.iters):
+        for sid, p_, o in w.arrivals[it]:
+            pa.check(pa.pa_sched_add(sch, sid, p_, o))
+        pa.check(pa.pa_sched_step(sch, b))
+        if b.n_decode:
+            top = max(top, int(b.decode()[2].max()) // BLOCK)
+        if b.n_prefill_tokens:
+            top = max(top, int(b.slots().max()) // BLOCK)
+    pa.pa_sched_destroy(sch)
+    pa.pa_pool_destroy(pool)
+    used_blocks = top + 1
+
+    torch.cuda.empty_cache()
+    ring_n = 8 * (w.max_running + w.prefill_budget)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    k_ring = torch.randn((ring_n, H_KV, D), generator=gen, device=dev).to(torch.bfloat16)
+    v_ring = torch.randn((ring_n, H_KV, D), generator=gen, device=dev).to(torch.bfloat16)
+    q_ring = torch.randn((ring_n, H_Q, D), generator=gen, device=dev).to(torch.bfloat16)
+    pos = [0]
+
+    def provider(seqs, positions):
+        n = len(seqs)
+        a = pos[0]
+        if a + n > ring_n:
+            a = 0
+        pos[0] = a + n
+        return k_ring[a:a + n], v_ring[a:a + n], q_ring[a:a + n]
+
+    cache_note = "whole pool backed on the device"
+    try:
+        run = LayerIterations(w.num_blocks, H_Q, H_KV, D, dev, provider, w.max_running,
+                              w.prefill_budget, max_context=max_ctx)
+    except torch.OutOfMemoryError:
+        torch.cuda.empty_cache()
+        cache_note = (f"device cache backs the {used_blocks} lowest block ids, the only ones "
+                      f"the trace hands out (the host pool has all {w.num_blocks})")
+        run = LayerIterations(w.num_blocks, H_Q, H_KV, D, dev, provider, w.max_running,
+                              w.prefill_budget, max_context=max_ctx, cache_blocks=used_blocks)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_tok = 0
+    for it in range(w.iters):
+        for sid, p_, o in w.arrivals[it]:
+            run.add(sid, p_, o)
+        n_tok += run.step()
+    run.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    waste = np.array(run.waste)
+    unw = np.array(run.unwritten)
+    out = {"workload": f"trace: {w.iters} iterations, Poisson(0.5) arrivals, lognormal prompts "
+                       "(median 1000, sigma 1, cap 32768), geometric outputs (mean 256), "
+                       "<=256 running, 512-token prefill budget, 64/8 heads, d128, bf16",
+           "tokens_per_s": n_tok / wall, "ms_per_iteration": wall / w.iters * 1e3,
+           "decode_tokens": run.totals["decode_tokens"],
+           "prefill_tokens": run.totals["prefill_tokens"],
+           "finished": run.totals["finished"], "preemptions": run.totals["preempted"],
+           "pool_blocks": w.num_blocks, "cache_blocks": run.cache_blocks,
+           "cache_note": cache_note,
+           "fragmentation": {"internal_waste_mean": float(np.nanmean(waste)),
+                             "internal_waste_max": float(np.nanmax(waste)),
+                             "reserved_unwritten_mean": float(np.nanmean(unw)),
+                             "definition": "1 - tokens the held blocks are allocated for / "
+                                           "(16 x blocks held), over running sequences, per "
+                                           "iteration; reserved-but-unwritten prompt slots "
+                                           "reported separately"}}
+    run.close()
+    return out
+
+
 def cpu_prefill_baseline():
     """The oracle on one 512-token slice at prefix 512 (gather + fp64 causal
     attention of all 64 heads), as GFLOP/s on the algorithmic count."""
@@ -616,6 +711,7 @@ def main():
                          "slices + 127 decodes per iteration, 64/8 heads, d128, bf16")
         result["mixed"] = m
         result["fp8_decode"] = fp8_leg(args, dev)
+        result["trace"] = trace_leg(args, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample_seqs)
         if "mixed" in result:

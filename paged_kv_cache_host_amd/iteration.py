@@ -1,0 +1,210 @@
+"""One attention layer driven through continuous-batching iterations.
+
+Each ``step`` is one iteration of the LESSON's loop ("Continuous batching at
+the iteration level", "Chunked prefill"): libpa's scheduler (pa_sched_step)
+grows the decode-phase sequences by one token, admits and hands out prefill
+slices within the budget; the new tokens' K/V are scattered into the paged
+cache (pa_cache_write) and attention runs for the decode tokens (pa_decode)
+and the prefill slices (pa_prefill_chunk), all on one compute stream.  The
+host work of iteration t+1 (scheduling, table packing, copies on a side
+stream into double-buffered pinned memory) overlaps the kernels of
+iteration t.
+
+Token data (new K, V, Q rows) comes from a caller-supplied provider:
+``provider(seqs, positions) -> (k [n, H_kv, D], v [n, H_kv, D], q [n, H_q, D])``
+device tensors, so that a benchmark can feed a pre-generated ring and a test
+can feed per-position data the oracle also sees.
+
+Argument marshalling and buffer management only: every scheduling decision
+is made in libpa's C++ scheduler and every byte of attention in its kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _pa as pa
+from .engine import BLOCK, _TORCH_STORAGE
+
+
+class LayerIterations:
+    def __init__(self, num_blocks: int, h_q: int, h_kv: int, d: int, device, provider,
+                 max_running: int = 256, prefill_budget: int = 512, max_context: int = 40960,
+                 cache_blocks: int | None = None, cache_dtype: str = "bf16",
+                 k_scale: float = 1.0, v_scale: float = 1.0, sm_scale: float | None = None,
+                 free_order=None):
+        self.h_q, self.h_kv, self.d = h_q, h_kv, d
+        self.dev = torch.device(device)
+        self.provider = provider
+        self.R, self.B = max_running, prefill_budget
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        self.sm = sm_scale if sm_scale is not None else float(np.float32(1.0) / np.float32(np.sqrt(d)))
+        st, self.pool = pa.pa_pool_create(num_blocks, BLOCK, free_order)
+        pa.check(st)
+        st, self.sched = pa.pa_sched_create(self.pool, max_running, prefill_budget, BLOCK)
+        pa.check(st)
+        self.batch = pa.SchedBatch(max_running, prefill_budget)
+        # Device cache: blocks [0, cache_blocks) are backed (all of the pool
+        # by default).  The kernels clamp any table entry outside it.
+        self.cache_blocks = num_blocks if cache_blocks is None else int(cache_blocks)
+        dt = _TORCH_STORAGE[cache_dtype]
+        x = 16 // torch.empty((), dtype=dt).element_size()
+        self.k = torch.empty((self.cache_blocks, h_kv, d // x, BLOCK, x), dtype=dt, device=self.dev)
+        self.v = torch.empty((self.cache_blocks, h_kv, d, BLOCK), dtype=dt, device=self.dev)
+        self.max_ctx = max_context
+        mb = -(-max_context // BLOCK)
+        T = max_running + max(prefill_budget, 1)
+        pin = dict(dtype=torch.int32, pin_memory=True)
+        self.slots_pin = [torch.empty(T, **pin) for _ in range(2)]
+        self.dtab_pin = [torch.empty(max_running * mb, **pin) for _ in range(2)]
+        self.dlen_pin = [torch.empty(max_running, **pin) for _ in range(2)]
+        self.ptab_pin = [torch.empty(max_running * mb, **pin) for _ in range(2)]
+        self.pmeta_pin = [torch.empty(2 * max_running + 1, **pin) for _ in range(2)]
+        dv = dict(dtype=torch.int32, device=self.dev)
+        self.slots_dev = [torch.empty(T, **dv) for _ in range(2)]
+        self.dtab_dev = [torch.empty(max_running * mb, **dv) for _ in range(2)]
+        self.dlen_dev = [torch.empty(max_running, **dv) for _ in range(2)]
+        self.ptab_dev = [torch.empty(max_running * mb, **dv) for _ in range(2)]
+        self.pmeta_dev = [torch.empty(2 * max_running + 1, **dv) for _ in range(2)]
+        out_dt = torch.bfloat16
+        self.out_dec = [torch.empty((max_running, h_q, d), dtype=out_dt, device=self.dev) for _ in range(2)]
+        self.out_pf = [torch.empty((max(prefill_budget, 1), h_q, d), dtype=out_dt, device=self.dev)
+                       for _ in range(2)]
+        n = pa.pa_decode_workspace_bytes(max_running, h_q, h_kv, d, max_context)
+        self.ws_dec = torch.zeros(max(n, 1), dtype=torch.uint8, device=self.dev)
+        n = max(pa.pa_prefill_workspace_bytes(c, max(prefill_budget, 1), h_q, h_kv, d, max_context)
+                for c in range(1, max_running + 1))
+        self.ws_pf = torch.empty(max(n, 1), dtype=torch.uint8, device=self.dev)
+        self.compute = torch.cuda.Stream(device=self.dev)
+        self.copy = torch.cuda.Stream(device=self.dev)
+        self.ev_copied = [torch.cuda.Event() for _ in range(2)]
+        self.ev_done = [torch.cuda.Event() for _ in range(2)]
+        for e in self.ev_done:
+            e.record(self.compute)
+        self.it = 0
+        self.totals = {"decode_tokens": 0, "prefill_tokens": 0, "preempted": 0, "finished": 0}
+        self.waste = []        # internal waste per iteration (nan: nothing held)
+        self.unwritten = []    # reserved-unwritten share per iteration (nan: nothing held)
+
+    def close(self):
+        if self.sched is not None:
+            pa.pa_sched_destroy(self.sched)
+            self.sched = None
+        if self.pool is not None:
+            pa.pa_pool_destroy(self.pool)
+            self.pool = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self, seq: int, prompt_len: int, target: int):
+        pa.check(pa.pa_sched_add(self.sched, seq, prompt_len, target))
+
+    def step(self, keep=None):
+        """One iteration.  ``keep``: optional callback(record) receiving the
+        iteration's host-side record (decode/prefill lists) and its output
+        tensors once the kernels have finished (test use)."""
+        X = self.it & 1
+        self.ev_done[X].synchronize()
+        b = self.batch
+        pa.check(pa.pa_sched_step(self.sched, b))
+        ds, dp, dsl = b.decode()
+        ps, pst, pl = b.prefill()
+        n_dec, n_pf, n_pt = b.n_decode, b.n_prefill, b.n_prefill_tokens
+        fin, _, pre = b.events()
+        self.totals["decode_tokens"] += n_dec
+        self.totals["prefill_tokens"] += n_pt
+        self.totals["preempted"] += len(pre)
+        self.totals["finished"] += len(fin)
+        st, acc = pa.pa_sched_stats(self.sched)
+        pa.check(st)
+        held = acc["blocks_held"] * BLOCK
+        self.waste.append(float("nan") if held == 0 else 1.0 - acc["tokens_held"] / held)
+        self.unwritten.append(float("nan") if held == 0 else acc["unwritten"] / held)
+
+        # token data: prefill tokens first, then decode tokens
+        pf_pos = np.concatenate([np.arange(a, a + n) for a, n in zip(pst.tolist(), pl.tolist())]) \
+            if n_pf else np.zeros(0, np.int64)
+        pf_seq = np.repeat(ps, pl) if n_pf else np.zeros(0, np.int64)
+        seqs = np.concatenate([pf_seq, ds]).astype(np.int64)
+        poss = np.concatenate([pf_pos, dp]).astype(np.int64)
+        n_tok = n_pt + n_dec
+        sl = self.slots_pin[X].numpy()
+        sl[:n_pt] = b.slots()
+        sl[n_pt:n_tok] = dsl
+        mbd = mbp = 1
+        if n_dec:
+            max_ctx_d = int(dp.max()) + 1
+            mbd = -(-max_ctx_d // BLOCK)
+            st, _, _ = pa.pa_pack_batch(self.pool, ds, mbd,
+                                        self.dtab_pin[X].numpy()[:n_dec * mbd].reshape(n_dec, mbd),
+                                        self.dlen_pin[X].numpy()[:n_dec])
+            pa.check(st)
+        if n_pf:
+            # a prefilling sequence holds the blocks of all its known tokens
+            held = 0
+            for sq in ps.tolist():
+                st, n = pa.pa_seq_length(self.pool, sq)
+                pa.check(st)
+                held = max(held, n)
+            mbp = -(-held // BLOCK)
+            st, _, _ = pa.pa_pack_batch(self.pool, ps, mbp,
+                                        self.ptab_pin[X].numpy()[:n_pf * mbp].reshape(n_pf, mbp),
+                                        None)
+            pa.check(st)
+            meta = self.pmeta_pin[X].numpy()
+            meta[0] = 0
+            meta[1:n_pf + 1] = np.cumsum(pl)
+            meta[n_pf + 1:2 * n_pf + 1] = pst
+        record = {"decode": (ds.copy(), dp.copy()), "prefill": (ps.copy(), pst.copy(), pl.copy())}
+        k_new = v_new = q_new = None
+        if n_tok:
+            k_new, v_new, q_new = self.provider(seqs, poss)
+        with torch.cuda.stream(self.copy):
+            self.slots_dev[X][:n_tok].copy_(self.slots_pin[X][:n_tok], non_blocking=True)
+            if n_dec:
+                self.dtab_dev[X][:n_dec * mbd].copy_(self.dtab_pin[X][:n_dec * mbd], non_blocking=True)
+                self.dlen_dev[X][:n_dec].copy_(self.dlen_pin[X][:n_dec], non_blocking=True)
+            if n_pf:
+                self.ptab_dev[X][:n_pf * mbp].copy_(self.ptab_pin[X][:n_pf * mbp], non_blocking=True)
+                self.pmeta_dev[X][:2 * n_pf + 1].copy_(self.pmeta_pin[X][:2 * n_pf + 1],
+                                                       non_blocking=True)
+            self.ev_copied[X].record(self.copy)
+        c = self.compute
+        c.wait_event(self.ev_copied[X])
+        if n_tok:
+            # the provider's tensors were produced on the caller's stream
+            c.wait_stream(torch.cuda.current_stream(self.dev))
+            for t in (k_new, v_new, q_new):
+                t.record_stream(c)
+            pa.check(pa.pa_cache_write(c, k_new, v_new, self.slots_dev[X][:n_tok], self.k, self.v,
+                                       self.cache_blocks, self.h_kv, self.d, BLOCK, self.k_scale,
+                                       self.v_scale))
+        if n_pf:
+            meta = self.pmeta_dev[X]
+            pa.check(pa.pa_prefill_chunk(c, self.out_pf[X][:n_pt], q_new[:n_pt], meta[:n_pf + 1],
+                                         meta[n_pf + 1:2 * n_pf + 1],
+                                         self.k, self.v,
+                                         self.ptab_dev[X][:n_pf * mbp].view(n_pf, mbp),
+                                         self.cache_blocks, self.h_kv, int(pl.max()),
+                                         int((pst + pl).max()), self.sm, self.k_scale,
+                                         self.v_scale, self.ws_pf))
+        if n_dec:
+            pa.check(pa.pa_decode(c, self.out_dec[X][:n_dec], q_new[n_pt:n_tok], self.k, self.v,
+                                  self.dtab_dev[X][:n_dec * mbd].view(n_dec, mbd),
+                                  self.dlen_dev[X][:n_dec], self.cache_blocks, self.h_kv,
+                                  int(dp.max()) + 1, self.sm, self.k_scale, self.v_scale,
+                                  self.ws_dec))
+        self.ev_done[X].record(c)
+        if keep is not None:
+            self.ev_done[X].synchronize()
+            keep(record, self.out_dec[X][:n_dec].clone(), self.out_pf[X][:n_pt].clone())
+        self.it += 1
+        return n_tok
+
+    def synchronize(self):
+        for e in self.ev_done:
+            e.synchronize()

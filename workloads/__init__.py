@@ -315,3 +315,14 @@ def prefill_workload(name: str, seed: int, prompt_len: int | None = None, chunks
         w.k_scale = _amax_scale(k_tok)
         w.v_scale = _amax_scale(v_tok)
     return w
+
+
+def seq_token_rows(seed: int, sid: int, length: int, h_q: int, h_kv: int, d: int):
+    """K, V (raw bf16 [length, h_kv, d]) and Q (raw bf16 [length, h_q, d]) of
+    positions 0..length-1 of sequence ``sid``: per-sequence streams, so that a
+    position's data does not depend on when it is scheduled."""
+    rng = np.random.default_rng([seed, sid])
+    k = normal_raw(rng, (length, h_kv, d), "bf16")
+    v = normal_raw(rng, (length, h_kv, d), "bf16")
+    q = normal_raw(rng, (length, h_q, d), "bf16")
+    return k, v, q
