@@ -81,7 +81,7 @@ __device__ __forceinline__ int krow_of(int tok) {
 // d0..d0+15 of one chunk are 256 contiguous bytes, so the 16 lanes of an
 // MFMA operand read that take consecutive dimensions hit distinct banks.
 __device__ __forceinline__ int v_off(int d, int c) {
-  return (((d >> 4) * (kPfKeys / 8) + c) << 8) | ((d & 15) << 4);
+  return (((d >> 4) * (kPfKeys / 8) + c) << 8) + ((d & 15) << 4);
 }
 
 struct PfGeom {
@@ -117,150 +117,121 @@ __device__ __forceinline__ f16x8 pack_f16x8(const float* v) {
   return r;
 }
 
-template <typename CacheT>
-struct TileLoader;
+// Moves one 64-key tile (4 blocks x K and V of one KV head) from the paged
+// cache into an LDS stage as 16-byte pieces spread over the work-group's
+// threads: piece p = wave * 64 + lane + i * threads.  A block-head tile has a
+// multiple of 64 pieces, so which tensor and block a piece belongs to is the
+// same for the whole wave (scalar), and every offset splits into a scalar
+// part and a lane part that does not depend on i.
+template <typename CacheT, int D>
+struct TileLoader {
+  using CR = typename CacheT::raw;
+  static constexpr int kElems = 16 / sizeof(CR);            // cache elements per piece
+  static constexpr int kPerBlock = D * kBlock / kElems;     // pieces per (block, head), K or V
+  static constexpr int kHalf = 4 * kPerBlock;               // K pieces of a tile
+  static constexpr int kPieces = 2 * kHalf;
+  static constexpr int NLD = kPieces / kPfThreads;          // pieces per thread
+  static_assert(kPieces % kPfThreads == 0, "tile pieces must divide over the threads");
+  static_assert(kPerBlock % kWave == 0, "a wave's pieces must share one block");
+  static constexpr bool kWide = sizeof(CR) == 1;            // fp8 pieces widen to two chunks
 
-// bf16 cache: a tile is 4 blocks x (K 4 KB + V 4 KB) per KV head at D = 128,
-// moved as 16-byte pieces.
-template <>
-struct TileLoader<BF16> {
-  template <int D>
-  static constexpr int pieces() {
-    return 2 * 4 * D * kBlock * 2 / 16;
-  }
-  template <int D>
-  static constexpr int per_thread() {
-    return pieces<D>() / kPfThreads;
-  }
-  template <int D>
-  __device__ static void load(u32x4* regs, const uint16_t* __restrict__ k_cache,
-                              const uint16_t* __restrict__ v_cache, const int32_t* blk,
-                              int32_t kvh, int32_t H_kv, int tid) {
-    constexpr int kPerBlock = D * kBlock * 2 / 16;  // pieces per (block, head) and tensor
-    constexpr int kHalf = 4 * kPerBlock;
-#pragma unroll
-    for (int i = 0; i < per_thread<D>(); ++i) {
-      const int p = tid + i * kPfThreads;
-      const bool is_v = p >= kHalf;
-      const int pp = is_v ? p - kHalf : p;
-      const int b = pp / kPerBlock, e = pp % kPerBlock;
-      const int32_t bk = blk[b];
-      if (bk >= 0) {
-        const uint16_t* base = (is_v ? v_cache : k_cache) +
-                               (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + e * 8;
-        regs[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base));
-      } else {
-        regs[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+  int wave;      // scalar
+  int lane;
+  int k_lane;    // LDS offset, lane part, K pieces
+  int v_lane;    // LDS offset, lane part, V pieces
+  int v_key;     // first key of the lane's V piece inside its block
+
+  __device__ TileLoader(int wave_, int lane_) : wave(wave_), lane(lane_) {
+    if (!kWide) {
+      k_lane = (lane >> 4) * (kPfKeys * 16) + krow_of(lane & 15) * 16;
+      v_lane = (lane >> 5) * 2048 + (lane & 1) * 256 + ((lane >> 1) & 15) * 16;
+      v_key = (lane & 1) * 8;
+    } else {
+      k_lane = (lane >> 4) * 2 * (kPfKeys * 16) + krow_of(lane & 15) * 16;
+      v_lane = (lane >> 4) * 2048 + (lane & 15) * 16;
+      v_key = 0;
     }
   }
-  // `valid` = keys of the tile that exist (V beyond them is zeroed).
-  template <int D>
-  __device__ static void store(const u32x4* regs, uint8_t* stage, int valid, int tid) {
-    constexpr int kPerBlock = D * kBlock * 2 / 16;
-    constexpr int kHalf = 4 * kPerBlock;
-    uint8_t* k_lds = stage;
-    uint8_t* v_lds = stage + D * kPfKeys * 2;
+  // scalar description of piece i of this wave
+  struct Piece {
+    bool v;
+    int b;      // block of the tile
+    int e0;     // index of the wave's first piece inside the (block, head) tile
+  };
+  __device__ Piece piece(int i) const {
+    const int p = wave * kWave + i * kPfThreads;
+    Piece q;
+    q.v = p >= kHalf;
+    const int pp = q.v ? p - kHalf : p;
+    q.b = pp / kPerBlock;
+    q.e0 = pp % kPerBlock;
+    return q;
+  }
+
+  // blk: the tile's four block ids (scalars, inside the pool).  Blocks past
+  // the context are loaded too (any valid id): their keys lie beyond
+  // `valid`, so store() zeroes their V and the causal mask drops their
+  // scores.  Loading unconditionally keeps the loads free of any use before
+  // the store, so their latency overlaps the tile's compute.
+  __device__ void load(u32x4* regs, const CR* __restrict__ k_cache, const CR* __restrict__ v_cache,
+                       const int32_t (&blk)[4], int32_t kvh, int32_t H_kv) const {
 #pragma unroll
-    for (int i = 0; i < per_thread<D>(); ++i) {
-      const int p = tid + i * kPfThreads;
-      if (p < kHalf) {
-        const int b = p / kPerBlock, e = p % kPerBlock;
-        const int ch = e / kBlock, tok = e % kBlock;
-        *reinterpret_cast<u32x4*>(k_lds + ch * (kPfKeys * 16) + (b * kBlock + krow_of(tok)) * 16) =
-            regs[i];
-      } else {
-        const int pp = p - kHalf;
-        const int b = pp / kPerBlock, e = pp % kPerBlock;
-        const int d = e >> 1, h = e & 1;
-        const int key0 = b * kBlock + h * 8;
-        u32x4 w = regs[i];
-        if (key0 + 8 > valid) {
+    for (int i = 0; i < NLD; ++i) {
+      const Piece q = piece(i);
+      const int32_t bk = q.b == 0 ? blk[0] : q.b == 1 ? blk[1] : q.b == 2 ? blk[2] : blk[3];
+      const CR* base = (q.v ? v_cache : k_cache) +
+                       (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + q.e0 * kElems;
+      regs[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane * kElems));
+    }
+  }
+
+  // `valid` = keys of the tile that exist; V beyond them is stored as zero.
+  __device__ void store(const u32x4* regs, uint8_t* stage, int valid) const {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int k = key0 + 2 * j;
-            uint32_t m = 0u;
-            if (k < valid) m |= 0xFFFFu;
-            if (k + 1 < valid) m |= 0xFFFF0000u;
-            w[j] &= m;
+    for (int i = 0; i < NLD; ++i) {
+      const Piece q = piece(i);
+      u32x4 w = regs[i];
+      if (!kWide) {
+        if (!q.v) {
+          // e = chunk * 16 + token
+          const int off = (q.e0 >> 4) * (kPfKeys * 16) + q.b * kBlock * 16;
+          *reinterpret_cast<u32x4*>(stage + off + k_lane) = w;
+        } else {
+          // e = dim * 2 + half; v_off(dim, 2 b + half)
+          if (valid < kPfKeys) {  // last tile of the range only
+            const int key0 = q.b * kBlock + v_key;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int k = key0 + 2 * j;
+              const uint32_t m = (k < valid ? 0xFFFFu : 0u) | (k + 1 < valid ? 0xFFFF0000u : 0u);
+              w[j] &= m;
+            }
           }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(w[j]);
+          const int off = D * kPfKeys * 2 + ((q.e0 >> 1) >> 4) * 2048 + 2 * q.b * 256;
+          *reinterpret_cast<u32x4*>(stage + off + v_lane) = w;
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(w[j]);
-        *reinterpret_cast<u32x4*>(v_lds + v_off(d, 2 * b + h)) = w;
-      }
-    }
-  }
-};
-
-// fp8 cache: pieces of 16 codes, widened to bf16 (exact) on the way to LDS.
-template <>
-struct TileLoader<FP8> {
-  template <int D>
-  static constexpr int pieces() {
-    return 2 * 4 * D * kBlock / 16;
-  }
-  template <int D>
-  static constexpr int per_thread() {
-    return pieces<D>() / kPfThreads;
-  }
-  template <int D>
-  __device__ static void load(u32x4* regs, const uint8_t* __restrict__ k_cache,
-                              const uint8_t* __restrict__ v_cache, const int32_t* blk,
-                              int32_t kvh, int32_t H_kv, int tid) {
-    constexpr int kPerBlock = D * kBlock / 16;
-    constexpr int kHalf = 4 * kPerBlock;
-#pragma unroll
-    for (int i = 0; i < per_thread<D>(); ++i) {
-      const int p = tid + i * kPfThreads;
-      const bool is_v = p >= kHalf;
-      const int pp = is_v ? p - kHalf : p;
-      const int b = pp / kPerBlock, e = pp % kPerBlock;
-      const int32_t bk = blk[b];
-      if (bk >= 0) {
-        const uint8_t* base = (is_v ? v_cache : k_cache) +
-                              (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + e * 16;
-        regs[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base));
+      } else if (!q.v) {
+        // e = chunk8 * 16 + token: bf16 chunks 2 chunk8, 2 chunk8 + 1
+        const int off = (q.e0 >> 4) * 2 * (kPfKeys * 16) + q.b * kBlock * 16 + k_lane;
+        *reinterpret_cast<bf16x8*>(stage + off) = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
+        *reinterpret_cast<bf16x8*>(stage + off + kPfKeys * 16) = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
       } else {
-        regs[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  template <int D>
-  __device__ static void store(const u32x4* regs, uint8_t* stage, int valid, int tid) {
-    constexpr int kPerBlock = D * kBlock / 16;
-    constexpr int kHalf = 4 * kPerBlock;
-    uint8_t* k_lds = stage;
-    uint8_t* v_lds = stage + D * kPfKeys * 2;
-#pragma unroll
-    for (int i = 0; i < per_thread<D>(); ++i) {
-      const int p = tid + i * kPfThreads;
-      const u32x4 w = regs[i];
-      if (p < kHalf) {
-        const bf16x8 lo = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
-        const bf16x8 hi = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
-        // 16 codes = dims 16*ch8 .. +15 of token tok -> bf16 chunks 2*ch8, 2*ch8+1
-        const int b = p / kPerBlock, e = p % kPerBlock;
-        const int ch8 = e / kBlock, tok = e % kBlock;
-        const int row = b * kBlock + krow_of(tok);
-        *reinterpret_cast<bf16x8*>(k_lds + (2 * ch8) * (kPfKeys * 16) + row * 16) = lo;
-        *reinterpret_cast<bf16x8*>(k_lds + (2 * ch8 + 1) * (kPfKeys * 16) + row * 16) = hi;
-      } else {
-        // 16 codes = tokens 0..15 of dimension d
-        const int pp = p - kHalf;
-        const int b = pp / kPerBlock, d = pp % kPerBlock;
+        // e = dim: tokens 0..7 -> chunk 2 b, 8..15 -> chunk 2 b + 1
         f16x8 v0 = fp8x8_to_f16x8(u32x2{w[0], w[1]});
         f16x8 v1 = fp8x8_to_f16x8(u32x2{w[2], w[3]});
-        const int key0 = b * kBlock;
-        if (key0 + kBlock > valid) {
+        const int key0 = q.b * kBlock;
+        if (valid < kPfKeys && key0 + kBlock > valid) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             if (key0 + j >= valid) v0[j] = static_cast<_Float16>(0.0f);
             if (key0 + 8 + j >= valid) v1[j] = static_cast<_Float16>(0.0f);
           }
         }
-        *reinterpret_cast<f16x8*>(v_lds + v_off(d, 2 * b)) = v0;
-        *reinterpret_cast<f16x8*>(v_lds + v_off(d, 2 * b + 1)) = v1;
+        const int off = D * kPfKeys * 2 + (q.e0 >> 4) * 2048 + 2 * q.b * 256 + v_lane;
+        *reinterpret_cast<f16x8*>(stage + off) = v0;
+        *reinterpret_cast<f16x8*>(stage + off + 256) = v1;  // chunk 2 b + 1
       }
     }
   }
@@ -278,9 +249,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
     float v_scale, float* __restrict__ ws_ml, float* __restrict__ ws_o, int32_t ws_rows) {
   constexpr int NKS = D / 16;  // 16-dim MFMA steps of Q K^T
   constexpr int NDT = D / 32;  // 32-dim tiles of O^T
-  constexpr int NLD = TileLoader<CacheT>::template per_thread<D>();
+  using Loader = TileLoader<CacheT, D>;
+  constexpr int NLD = Loader::NLD;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * stage_bytes<D>()];
-  __shared__ int32_t blk_s[2][4];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -351,100 +322,126 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
 
   const int32_t* table = block_tables + static_cast<int64_t>(c) * max_blocks;
   const int32_t n_blk = min((kv_end + kBlock - 1) / kBlock, max_blocks);
-  auto tile_blocks = [&](int t, int32_t* dst) {
-    if (tid < 4) {
-      const int kb = t * 4 + tid;
-      dst[tid] = kb < n_blk ? safe_block(table[kb], num_blocks) : -1;
+  // Block ids are fetched one tile ahead of their use by a vector load
+  // (lanes 0..3 take the tile's four entries, raw) and checked as scalars
+  // when used: entries past the context become block 0, any entry outside
+  // the pool is clamped into it.
+  auto fetch_ids = [&](int t) -> int32_t {
+    return table[min(t * 4 + (lane & 3), n_blk - 1)];
+  };
+  auto ids_of = [&](int32_t v, int t, int32_t (&blk)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int32_t e = __builtin_amdgcn_readlane(v, j);
+      blk[j] = t * 4 + j < n_blk ? safe_block(e, num_blocks) : 0;
     }
   };
 
-  u32x4 regs[NLD];
-  if (t0 < t1) {
-    tile_blocks(t0, blk_s[0]);
-    __syncthreads();
-    TileLoader<CacheT>::template load<D>(regs, k_cache, v_cache, blk_s[0], kvh, geo.H_kv, tid);
-    TileLoader<CacheT>::template store<D>(regs, smem, kv_end - t0 * kPfKeys, tid);
-    if (t0 + 1 < t1) tile_blocks(t0 + 1, blk_s[1]);
-    __syncthreads();
-  }
+  const Loader ld(wave, lane);
+  const int v_lane = v_off(col, g);
 
-  for (int t = t0; t < t1; ++t) {
-    const int sb = (t - t0) & 1;
-    const bool more = t + 1 < t1;
-    if (more)
-      TileLoader<CacheT>::template load<D>(regs, k_cache, v_cache, blk_s[sb ^ 1], kvh, geo.H_kv,
-                                           tid);
-    const int32_t key0 = t * kPfKeys;
-    if (wave_live && key0 <= wave_last_pos) {
-      const uint8_t* k_lds = smem + sb * stage_bytes<D>();
-      const uint8_t* v_lds = k_lds + D * kPfKeys * 2;
-      f32x16 s[2];
+  // One tile's phases.  S^T for the 64 keys of a stage:
+  auto qk = [&](const uint8_t* k_lds, f32x16* s) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) s[h][j] = 0.f;
+      for (int j = 0; j < 16; ++j) s[h][j] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              k_lds + (2 * ks + g) * (kPfKeys * 16) + (32 * h + col) * 16);
-          s[h] = mfma32x32x16(a, qf[ks], s[h]);
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            k_lds + (2 * ks + g) * (kPfKeys * 16) + (32 * h + col) * 16);
+        s[h] = mfma32x32x16(a, qf[ks], s[h]);
       }
-      // causal mask, only in the (at most two) tiles that reach past the
-      // wave's first position
-      float xv[32];
+    }
+  };
+  // softmax update of the scores of the tile starting at key0 (in place:
+  // the scores become the weights), then O^T += V^T P^T from the stage's V.
+  auto softmax_pv = [&](f32x16* s, int32_t key0, const uint8_t* v_lds) {
+    // causal mask, only in the (at most two) tiles that reach past the
+    // wave's first position
+    if (key0 + kPfKeys - 1 > wave_first_pos) {
+      const int lim = qpos - key0 - 8 * g;  // largest admissible key offset
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) xv[16 * h + j] = s[h][j];
-      if (key0 + kPfKeys - 1 > wave_first_pos) {
-        const int lim = qpos - key0 - 8 * g;  // largest admissible key offset
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const int off = 32 * (j >> 4) + 16 * ((j >> 3) & 1) + (j & 7);
-          xv[j] = off <= lim ? xv[j] : -__builtin_inff();
+        for (int j = 0; j < 16; ++j) {
+          const int off = 32 * h + 16 * (j >> 3) + (j & 7);
+          s[h][j] = off <= lim ? s[h][j] : -__builtin_inff();
         }
-      }
-      // the score scale is positive, so the maximum is taken on raw scores
-      float mx = xv[0];
+    }
+    // the score scale is positive, so the maximum is taken on raw scores
+    float mx = s[0][0];
 #pragma unroll
-      for (int j = 1; j < 32; ++j) mx = fmaxf(mx, xv[j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * score_scale;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kPfLazy) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int n = 0; n < NDT; ++n)
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[h][j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * score_scale;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kPfLazy) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) o[n][j] *= alpha;
-        m_run = m_new;
-      }
-      const float mu = m_run == -__builtin_inff() ? 0.f : m_run;
-      float psum = 0.f;
+      for (int n = 0; n < NDT; ++n)
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        xv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(xv[j], score_scale, -mu));
-        psum += xv[j];
-      }
-      l_run += psum;
-      // O^T += V^T P^T, four 16-key steps
+        for (int j = 0; j < 16; ++j) o[n][j] *= alpha;
+      m_run = m_new;
+    }
+    const float mu = m_run == -__builtin_inff() ? 0.f : m_run;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f16x8 pb = pack_f16x8(&xv[8 * u]);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int n = 0; n < NDT; ++n) {
-          const int d = 32 * n + col;
-          const f16x8 a = *reinterpret_cast<const f16x8*>(
-              v_lds + v_off(d, 2 * u + g));
-          o[n] = mfma32x32x16(a, pb, o[n]);
-        }
+      for (int j = 0; j < 16; ++j)
+        s[h][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][j], score_scale, -mu));
+    // four 16-key steps: step u takes keys 16u .. 16u + 15, i.e. registers
+    // 8 (u & 1) .. + 7 of half u / 2.  The row sum adds the fp16 weights
+    // exactly as they enter the product (two per dot instruction).
+    const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[i] = static_cast<_Float16>(s[u >> 1][8 * (u & 1) + i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        l_run = __builtin_amdgcn_fdot2(f16x2{pb[2 * i], pb[2 * i + 1]}, ones, l_run, false);
+#pragma unroll
+      for (int n = 0; n < NDT; ++n) {
+        // v_off(32 n + col, 2 u + g) = v_off(col, g) + n * 4096 + u * 512
+        const f16x8 a = *reinterpret_cast<const f16x8*>(v_lds + v_lane + n * 4096 + u * 512);
+        o[n] = mfma32x32x16(a, pb, o[n]);
       }
     }
+  };
+
+  // Two LDS stages: the global loads of tile t+1 are issued before tile t
+  // is multiplied and stored into the other stage after it.
+  auto stage = [&](int t) { return smem + ((t - t0) & 1) * stage_bytes<D>(); };
+  u32x4 regs[NLD];
+  int32_t ids_ahead = 0;
+  if (t0 < t1) {
+    int32_t blk[4];
+    ids_of(fetch_ids(t0), t0, blk);
+    ld.load(regs, k_cache, v_cache, blk, kvh, geo.H_kv);
+    if (t0 + 1 < t1) ids_ahead = fetch_ids(t0 + 1);
+    ld.store(regs, stage(t0), kv_end - t0 * kPfKeys);
+    __syncthreads();
+  }
+  for (int t = t0; t < t1; ++t) {
+    const bool more = t + 1 < t1;
     if (more) {
-      TileLoader<CacheT>::template store<D>(regs, smem + (sb ^ 1) * stage_bytes<D>(),
-                                            kv_end - (t + 1) * kPfKeys, tid);
-      if (t + 2 < t1) tile_blocks(t + 2, blk_s[sb]);
+      int32_t blk[4];
+      ids_of(ids_ahead, t + 1, blk);
+      ld.load(regs, k_cache, v_cache, blk, kvh, geo.H_kv);
+      if (t + 2 < t1) ids_ahead = fetch_ids(t + 2);
+    }
+    const int32_t key0 = t * kPfKeys;
+    if (wave_live && key0 <= wave_last_pos) {
+      f32x16 s[2];
+      qk(stage(t), s);
+      softmax_pv(s, key0, stage(t) + D * kPfKeys * 2);
+    }
+    if (more) {
+      ld.store(regs, stage(t + 1), kv_end - (t + 1) * kPfKeys);
     }
     __syncthreads();
   }
