@@ -6,9 +6,9 @@ Headline step (``value``): one continuous-batching decode iteration of one
 128, bf16, 16-token blocks, lognormal contexts of mean 1500):
 
   a1  host: libpa grows every sequence by one token (one block taken at each
-      block boundary) and packs block tables + context lengths into pinned
-      buffers; the tables go to the device on a copy stream, overlapped with
-      the previous step's kernels (double-buffered);
+      block boundary) and packs slots, block tables and context lengths into
+      one pinned buffer (double-buffered, so this host work overlaps the
+      previous step's kernels); one copy on the compute stream moves it;
   a2  pa_cache_write scatters the new tokens' K/V into their paged slots;
   a3  pa_decode: split-K paged attention (+ merge of multi-chunk contexts).
 
@@ -257,7 +257,7 @@ def decode_leg(args, dev):
     lengths, num_blocks, free_order = workloads.decode_70b_layout()
     S = len(lengths)
     seqs = np.arange(S, dtype=np.int64)
-    max_ctx = int(lengths.max()) + W + K
+    max_ctx = int(lengths.max()) + W + K + 5
     MB = -(-max_ctx // BLOCK)
 
     # -- set-up (untimed): pool, contexts of L-1 tokens already cached
@@ -278,15 +278,18 @@ def decode_leg(args, dev):
     ws = decode_workspace(S, H_Q, H_KV, D, max_ctx, dev)
     sm = sm_scale_for(D)
 
-    slots_pin = [torch.empty((S, 1), dtype=torch.int32).pin_memory() for _ in range(2)]
-    tables_pin = [torch.empty((S, MB), dtype=torch.int32).pin_memory() for _ in range(2)]
-    lens_pin = [torch.empty((S,), dtype=torch.int32).pin_memory() for _ in range(2)]
-    slots_dev = [torch.empty((S, 1), dtype=torch.int32, device=dev) for _ in range(2)]
-    tables_dev = [torch.empty((S, MB), dtype=torch.int32, device=dev) for _ in range(2)]
-    lens_dev = [torch.empty((S,), dtype=torch.int32, device=dev) for _ in range(2)]
+    # One pinned host buffer and one device buffer per parity hold the
+    # step's slots, context lengths and block tables, so that a single copy
+    # on the compute stream carries them (no cross-stream dependency).
+    n_meta = 2 * S + S * MB
+    host_buf = [torch.empty(n_meta, dtype=torch.int32).pin_memory() for _ in range(2)]
+    dev_buf = [torch.empty(n_meta, dtype=torch.int32, device=dev) for _ in range(2)]
+    views = []
+    for X in range(2):
+        h, d_ = host_buf[X].numpy(), dev_buf[X]
+        views.append((h[:S].reshape(S, 1), h[S:2 * S], h[2 * S:].reshape(S, MB),
+                      d_[:S], d_[S:2 * S], d_[2 * S:].view(S, MB)))
     compute = torch.cuda.Stream(device=dev)
-    copy = torch.cuda.Stream(device=dev)
-    ev_copied = [torch.cuda.Event() for _ in range(2)]
     ev_consumed = [torch.cuda.Event() for _ in range(2)]
     for e in ev_consumed:
         e.record(compute)
@@ -294,22 +297,18 @@ def decode_leg(args, dev):
 
     def step(i: int, timed: bool):
         X = i & 1
+        h_slots, h_lens, h_tab, d_slots, d_lens, d_tab = views[X]
         ev_consumed[X].synchronize()
-        st, done, _ = pa.pa_batch_append(kv.pool, seqs, 1, slots_pin[X].numpy())
+        st, done, _ = pa.pa_batch_append(kv.pool, seqs, 1, h_slots)
         pa.check(st)
-        st, _, lens_np = pa.pa_pack_batch(kv.pool, seqs, MB, tables_pin[X].numpy(),
-                                          lens_pin[X].numpy())
+        st, _, lens_np = pa.pa_pack_batch(kv.pool, seqs, MB, h_tab, h_lens)
         pa.check(st)
-        with torch.cuda.stream(copy):
-            slots_dev[X].copy_(slots_pin[X], non_blocking=True)
-            tables_dev[X].copy_(tables_pin[X], non_blocking=True)
-            lens_dev[X].copy_(lens_pin[X], non_blocking=True)
-            ev_copied[X].record(copy)
-        compute.wait_event(ev_copied[X])
+        with torch.cuda.stream(compute):
+            dev_buf[X].copy_(host_buf[X], non_blocking=True)
         r = i % R
-        pa.check(pa.pa_cache_write(compute, k_ring[r], v_ring[r], slots_dev[X], kv.k, kv.v,
+        pa.check(pa.pa_cache_write(compute, k_ring[r], v_ring[r], d_slots, kv.k, kv.v,
                                    num_blocks, H_KV, D, BLOCK))
-        pa.check(pa.pa_decode(compute, out, q_ring[r], kv.k, kv.v, tables_dev[X], lens_dev[X],
+        pa.check(pa.pa_decode(compute, out, q_ring[r], kv.k, kv.v, d_tab, d_lens,
                               num_blocks, H_KV, max_ctx, sm, 1.0, 1.0, ws))
         if timed:
             ctx_lens.append(lens_np.copy())
@@ -318,18 +317,25 @@ def decode_leg(args, dev):
     for i in range(W):
         step(i, False)
     torch.cuda.synchronize()
-    # The library brackets each of its kernel launches with HIP events on the
-    # stream it launches on (here `compute`); reset and enable for the timed
-    # steps only.
-    pa.check(pa.pa_timing_enable(True))
+    # The library brackets its kernel launches with HIP events on the stream
+    # it launches on (here `compute`); reset and enable for the timed
+    # steps; only the decode kernel is bracketed, so that the events add no
+    # gaps around the other kernels of the step.
+    pa.check(pa.pa_timing_enable(["decode"]))
     t0 = time.perf_counter()
     for i in range(K):
         step(W + i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    tm = _timings(pa, ("decode", "decode_merge", "cache_write"))
-    pa.check(pa.pa_timing_enable(False))
+    tm = _timings(pa, ("decode",))
     assert tm["decode"][0] == K, tm
+    # a few more steps, every kernel timed, for the step's other kernels
+    pa.check(pa.pa_timing_enable(True))
+    for i in range(5):
+        step(W + K + i, False)
+    torch.cuda.synchronize()
+    tm.update(_timings(pa, ("decode_merge", "cache_write")))
+    pa.check(pa.pa_timing_enable(False))
     kv.close()
 
     dec_bytes = [decode_bytes(l) for l in ctx_lens]
@@ -387,17 +393,18 @@ def mixed_leg(args, dev):
                                   for c in range(iters))), dtype=torch.uint8, device=dev)
     cu = torch.tensor([0, C], dtype=torch.int32, device=dev)
 
-    slots_pin = [torch.empty((NT,), dtype=torch.int32).pin_memory() for _ in range(2)]
-    start_pin = [torch.empty((1,), dtype=torch.int32).pin_memory() for _ in range(2)]
-    tables_pin = [torch.empty((S, MB), dtype=torch.int32).pin_memory() for _ in range(2)]
-    lens_pin = [torch.empty((S,), dtype=torch.int32).pin_memory() for _ in range(2)]
-    slots_dev = [torch.empty((NT,), dtype=torch.int32, device=dev) for _ in range(2)]
-    start_dev = [torch.empty((1,), dtype=torch.int32, device=dev) for _ in range(2)]
-    tables_dev = [torch.empty((S, MB), dtype=torch.int32, device=dev) for _ in range(2)]
-    lens_dev = [torch.empty((S,), dtype=torch.int32, device=dev) for _ in range(2)]
+    # per parity: one pinned buffer [slots NT | start 1 | lens S | tables S*MB]
+    # and its device twin, copied once per iteration on the compute stream
+    n_meta = NT + 1 + S + S * MB
+    host_buf = [torch.empty(n_meta, dtype=torch.int32).pin_memory() for _ in range(2)]
+    dev_buf = [torch.empty(n_meta, dtype=torch.int32, device=dev) for _ in range(2)]
+    views = []
+    for X in range(2):
+        h, d_ = host_buf[X].numpy(), dev_buf[X]
+        o1, o2, o3 = NT, NT + 1, NT + 1 + S
+        views.append((h[:NT], h[o1:o2], h[o2:o3], h[o3:].reshape(S, MB),
+                      d_[:NT], d_[o1:o2], d_[o2:o3], d_[o3:].view(S, MB)))
     compute = torch.cuda.Stream(device=dev)
-    copy = torch.cuda.Stream(device=dev)
-    ev_copied = [torch.cuda.Event() for _ in range(2)]
     ev_consumed = [torch.cuda.Event() for _ in range(2)]
 
     def run_pass(timed: bool, n_iters: int):
@@ -416,40 +423,34 @@ def mixed_leg(args, dev):
         for e in ev_consumed:
             e.record(compute)
         if timed:
-            pa.check(pa.pa_timing_enable(True))
+            pa.check(pa.pa_timing_enable(["prefill", "prefill_merge"]))
         t0 = time.perf_counter()
         for c in range(n_iters):
             X = c & 1
+            h_sl, h_st, h_len, h_tab, d_sl, d_st, d_len, d_tab = views[X]
             ev_consumed[X].synchronize()
-            sl = slots_pin[X].numpy()
-            pa.check(pa.pa_seq_slots(kv.pool, PROMPT, c * C, C, sl[:C])[0])
-            st, _, _ = pa.pa_batch_append(kv.pool, dec_seqs, 1, sl[C:].reshape(S, 1))
+            pa.check(pa.pa_seq_slots(kv.pool, PROMPT, c * C, C, h_sl[:C])[0])
+            st, _, _ = pa.pa_batch_append(kv.pool, dec_seqs, 1, h_sl[C:].reshape(S, 1))
             pa.check(st)
-            st, _, _ = pa.pa_pack_batch(kv.pool, dec_seqs, MB, tables_pin[X].numpy(),
-                                        lens_pin[X].numpy())
+            st, _, _ = pa.pa_pack_batch(kv.pool, dec_seqs, MB, h_tab, h_len)
             pa.check(st)
-            start_pin[X][0] = c * C
-            with torch.cuda.stream(copy):
-                slots_dev[X].copy_(slots_pin[X], non_blocking=True)
-                start_dev[X].copy_(start_pin[X], non_blocking=True)
-                tables_dev[X].copy_(tables_pin[X], non_blocking=True)
-                lens_dev[X].copy_(lens_pin[X], non_blocking=True)
-                ev_copied[X].record(copy)
-            compute.wait_event(ev_copied[X])
+            h_st[0] = c * C
+            with torch.cuda.stream(compute):
+                dev_buf[X].copy_(host_buf[X], non_blocking=True)
             r = c % R
-            pa.check(pa.pa_cache_write(compute, k_ring[r], v_ring[r], slots_dev[X], kv.k, kv.v,
+            pa.check(pa.pa_cache_write(compute, k_ring[r], v_ring[r], d_sl, kv.k, kv.v,
                                        num_blocks, H_KV, D, BLOCK))
             pa.check(pa.pa_prefill_chunk(compute, out_p, q_prompt[c * C:(c + 1) * C], cu,
-                                         start_dev[X], kv.k, kv.v, ptab_dev, num_blocks, H_KV, C,
+                                         d_st, kv.k, kv.v, ptab_dev, num_blocks, H_KV, C,
                                          (c + 1) * C, sm, 1.0, 1.0, ws_p))
-            pa.check(pa.pa_decode(compute, out_d, q_dec[r], kv.k, kv.v, tables_dev[X],
-                                  lens_dev[X], num_blocks, H_KV, max_dec, sm, 1.0, 1.0, ws_d))
+            pa.check(pa.pa_decode(compute, out_d, q_dec[r], kv.k, kv.v, d_tab,
+                                  d_len, num_blocks, H_KV, max_dec, sm, 1.0, 1.0, ws_d))
             ev_consumed[X].record(compute)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         tm = None
         if timed:
-            tm = _timings(pa, ("prefill", "prefill_merge", "decode", "decode_merge", "cache_write"))
+            tm = _timings(pa, ("prefill", "prefill_merge"))
             pa.check(pa.pa_timing_enable(False))
         kv.close()
         return wall, tm
@@ -472,8 +473,7 @@ def mixed_leg(args, dev):
                              "traffic": None, "kernel": "prefill_kernel<BF16,128>",
                              "kernel_us_total": round(tot_pf, 1),
                              "algorithmic_flops": flops},
-        "other_kernels_us_total": {k: round(tm[k][2], 1) for k in
-                                   ("prefill_merge", "decode", "decode_merge", "cache_write")},
+        "prefill_merge_us_total": round(tm["prefill_merge"][2], 1),
     }
 
 

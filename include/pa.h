@@ -317,16 +317,16 @@ pa_status pa_sched_step(pa_sched* sched, pa_sched_batch* batch);
 pa_status pa_sched_stats(const pa_sched* sched, pa_sched_accounting* out);
 
 /* ------------------------------------------------------------------------
- * Kernel timing (instrumentation, off by default).  When enabled, each
- * kernel launch of the calls above is bracketed by a pair of HIP events
- * recorded on the caller's stream (up to 4096 launches per kernel between
- * resets).  Kernel names: "cache_write", "decode", "decode_merge",
- * "prefill", "prefill_merge", "generic".
+ * Kernel timing (instrumentation, off by default).  Each launch of a
+ * selected kernel is bracketed by a pair of HIP events recorded on the
+ * caller's stream (up to 4096 launches per kernel between resets).  Kernel
+ * names and their bits: "cache_write" 1, "decode" 2, "decode_merge" 4,
+ * "prefill" 8, "prefill_merge" 16, "generic" 32.
  * ---------------------------------------------------------------------- */
 
-/* Enable (non-zero) or disable timing; either way the recorded launches are
- * forgotten. */
-pa_status pa_timing_enable(int32_t enable);
+/* Record the kernels whose bits are set in `mask` (-1: all, 0: none); either
+ * way the recorded launches are forgotten. */
+pa_status pa_timing_enable(int32_t mask);
 
 /* Wait for the recorded launches of `kernel` [host string] and report their
  * number, mean and total duration in microseconds (each [host]). */

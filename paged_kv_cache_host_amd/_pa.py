@@ -325,8 +325,22 @@ def pa_sched_stats(sched):
 
 # -------------------------------------------------------------- timing -----
 
-def pa_timing_enable(enable: bool = True) -> int:
-    return _lib.pa_timing_enable(1 if enable else 0)
+TIMING_BITS = {"cache_write": 1, "decode": 2, "decode_merge": 4, "prefill": 8,
+               "prefill_merge": 16, "generic": 32}
+
+
+def pa_timing_enable(enable=True) -> int:
+    """``enable``: True (all kernels), False (none), or an iterable of kernel
+    names to record."""
+    if enable is True:
+        mask = -1
+    elif not enable:
+        mask = 0
+    else:
+        mask = 0
+        for name in enable:
+            mask |= TIMING_BITS[name]
+    return _lib.pa_timing_enable(mask)
 
 
 def pa_timing_query(kernel: str):

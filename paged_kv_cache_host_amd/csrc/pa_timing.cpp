@@ -1,10 +1,10 @@
 // Optional per-kernel timing of libpa's own launches.
 //
-// When enabled, the launchers record a HIP event before and after each of
-// their kernels on the caller's stream; pa_timing_query waits for the
-// recorded events and reports how many launches of a kernel were recorded and
-// their mean and total duration.  Disabled (the default), the hooks cost one
-// flag test per launch.
+// For the kernels selected by a bit mask, the launchers record a HIP event
+// before and after each launch on the caller's stream; pa_timing_query waits
+// for the recorded events and reports how many launches of a kernel were
+// recorded and their mean and total duration.  Disabled (the default), the
+// hooks cost one flag test per launch.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -31,7 +31,7 @@ struct Track {
 };
 
 std::mutex g_mu;
-std::atomic<bool> g_enabled{false};
+std::atomic<int32_t> g_mask{0};  // bit k: record kernel k
 Track g_tracks[kKernelCount];
 
 const char* kNames[kKernelCount] = {"cache_write", "decode",        "decode_merge",
@@ -40,7 +40,7 @@ const char* kNames[kKernelCount] = {"cache_write", "decode",        "decode_merg
 }  // namespace
 
 void timing_mark(hipStream_t st, KernelId k, bool begin) {
-  if (!g_enabled) return;
+  if (!(g_mask.load(std::memory_order_relaxed) & (1 << k))) return;
   std::lock_guard<std::mutex> lock(g_mu);
   Track& t = g_tracks[k];
   if (begin) {
@@ -65,9 +65,9 @@ void timing_mark(hipStream_t st, KernelId k, bool begin) {
 
 using namespace pa;
 
-extern "C" pa_status pa_timing_enable(int32_t enable) {
+extern "C" pa_status pa_timing_enable(int32_t mask) {
   std::lock_guard<std::mutex> lock(g_mu);
-  g_enabled = enable != 0;
+  g_mask = mask;
   for (auto& t : g_tracks) t.count = 0;
   return PA_OK;
 }

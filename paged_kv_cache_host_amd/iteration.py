@@ -6,9 +6,9 @@ grows the decode-phase sequences by one token, admits and hands out prefill
 slices within the budget; the new tokens' K/V are scattered into the paged
 cache (pa_cache_write) and attention runs for the decode tokens (pa_decode)
 and the prefill slices (pa_prefill_chunk), all on one compute stream.  The
-host work of iteration t+1 (scheduling, table packing, copies on a side
-stream into double-buffered pinned memory) overlaps the kernels of
-iteration t.
+host work of iteration t+1 (scheduling and table packing into
+double-buffered pinned memory) overlaps the kernels of iteration t; one copy
+on the compute stream then moves the packed metadata.
 
 Token data (new K, V, Q rows) comes from a caller-supplied provider:
 ``provider(seqs, positions) -> (k [n, H_kv, D], v [n, H_kv, D], q [n, H_q, D])``
@@ -53,19 +53,14 @@ class LayerIterations:
         self.v = torch.empty((self.cache_blocks, h_kv, d, BLOCK), dtype=dt, device=self.dev)
         self.max_ctx = max_context
         mb = -(-max_context // BLOCK)
+        # Per parity one pinned buffer and its device twin hold the
+        # iteration's slots, decode context lengths and tables, prefill
+        # tables and slice metadata, packed back to back; one copy on the
+        # compute stream moves the used prefix.
         T = max_running + max(prefill_budget, 1)
-        pin = dict(dtype=torch.int32, pin_memory=True)
-        self.slots_pin = [torch.empty(T, **pin) for _ in range(2)]
-        self.dtab_pin = [torch.empty(max_running * mb, **pin) for _ in range(2)]
-        self.dlen_pin = [torch.empty(max_running, **pin) for _ in range(2)]
-        self.ptab_pin = [torch.empty(max_running * mb, **pin) for _ in range(2)]
-        self.pmeta_pin = [torch.empty(2 * max_running + 1, **pin) for _ in range(2)]
-        dv = dict(dtype=torch.int32, device=self.dev)
-        self.slots_dev = [torch.empty(T, **dv) for _ in range(2)]
-        self.dtab_dev = [torch.empty(max_running * mb, **dv) for _ in range(2)]
-        self.dlen_dev = [torch.empty(max_running, **dv) for _ in range(2)]
-        self.ptab_dev = [torch.empty(max_running * mb, **dv) for _ in range(2)]
-        self.pmeta_dev = [torch.empty(2 * max_running + 1, **dv) for _ in range(2)]
+        n_meta = T + max_running + 2 * max_running * mb + 2 * max_running + 1
+        self.host_buf = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.dev_buf = [torch.empty(n_meta, dtype=torch.int32, device=self.dev) for _ in range(2)]
         out_dt = torch.bfloat16
         self.out_dec = [torch.empty((max_running, h_q, d), dtype=out_dt, device=self.dev) for _ in range(2)]
         self.out_pf = [torch.empty((max(prefill_budget, 1), h_q, d), dtype=out_dt, device=self.dev)
@@ -76,8 +71,6 @@ class LayerIterations:
                 for c in range(1, max_running + 1))
         self.ws_pf = torch.empty(max(n, 1), dtype=torch.uint8, device=self.dev)
         self.compute = torch.cuda.Stream(device=self.dev)
-        self.copy = torch.cuda.Stream(device=self.dev)
-        self.ev_copied = [torch.cuda.Event() for _ in range(2)]
         self.ev_done = [torch.cuda.Event() for _ in range(2)]
         for e in self.ev_done:
             e.record(self.compute)
@@ -132,16 +125,26 @@ class LayerIterations:
         seqs = np.concatenate([pf_seq, ds]).astype(np.int64)
         poss = np.concatenate([pf_pos, dp]).astype(np.int64)
         n_tok = n_pt + n_dec
-        sl = self.slots_pin[X].numpy()
-        sl[:n_pt] = b.slots()
-        sl[n_pt:n_tok] = dsl
+        h = self.host_buf[X].numpy()
+        dvb = self.dev_buf[X]
+        off = 0
+
+        def region(n):
+            nonlocal off
+            r = (h[off:off + n], dvb[off:off + n])
+            off += n
+            return r
+
+        h_sl, d_sl = region(n_tok)
+        h_sl[:n_pt] = b.slots()
+        h_sl[n_pt:] = dsl
         mbd = mbp = 1
         if n_dec:
             max_ctx_d = int(dp.max()) + 1
             mbd = -(-max_ctx_d // BLOCK)
-            st, _, _ = pa.pa_pack_batch(self.pool, ds, mbd,
-                                        self.dtab_pin[X].numpy()[:n_dec * mbd].reshape(n_dec, mbd),
-                                        self.dlen_pin[X].numpy()[:n_dec])
+            h_dl, d_dl = region(n_dec)
+            h_dt, d_dt = region(n_dec * mbd)
+            st, _, _ = pa.pa_pack_batch(self.pool, ds, mbd, h_dt.reshape(n_dec, mbd), h_dl)
             pa.check(st)
         if n_pf:
             # a prefilling sequence holds the blocks of all its known tokens
@@ -151,51 +154,38 @@ class LayerIterations:
                 pa.check(st)
                 held = max(held, n)
             mbp = -(-held // BLOCK)
-            st, _, _ = pa.pa_pack_batch(self.pool, ps, mbp,
-                                        self.ptab_pin[X].numpy()[:n_pf * mbp].reshape(n_pf, mbp),
-                                        None)
+            h_pt, d_pt = region(n_pf * mbp)
+            st, _, _ = pa.pa_pack_batch(self.pool, ps, mbp, h_pt.reshape(n_pf, mbp), None)
             pa.check(st)
-            meta = self.pmeta_pin[X].numpy()
-            meta[0] = 0
-            meta[1:n_pf + 1] = np.cumsum(pl)
-            meta[n_pf + 1:2 * n_pf + 1] = pst
+            h_pm, d_pm = region(2 * n_pf + 1)
+            h_pm[0] = 0
+            h_pm[1:n_pf + 1] = np.cumsum(pl)
+            h_pm[n_pf + 1:] = pst
         record = {"decode": (ds.copy(), dp.copy()), "prefill": (ps.copy(), pst.copy(), pl.copy())}
         k_new = v_new = q_new = None
         if n_tok:
             k_new, v_new, q_new = self.provider(seqs, poss)
-        with torch.cuda.stream(self.copy):
-            self.slots_dev[X][:n_tok].copy_(self.slots_pin[X][:n_tok], non_blocking=True)
-            if n_dec:
-                self.dtab_dev[X][:n_dec * mbd].copy_(self.dtab_pin[X][:n_dec * mbd], non_blocking=True)
-                self.dlen_dev[X][:n_dec].copy_(self.dlen_pin[X][:n_dec], non_blocking=True)
-            if n_pf:
-                self.ptab_dev[X][:n_pf * mbp].copy_(self.ptab_pin[X][:n_pf * mbp], non_blocking=True)
-                self.pmeta_dev[X][:2 * n_pf + 1].copy_(self.pmeta_pin[X][:2 * n_pf + 1],
-                                                       non_blocking=True)
-            self.ev_copied[X].record(self.copy)
         c = self.compute
-        c.wait_event(self.ev_copied[X])
         if n_tok:
             # the provider's tensors were produced on the caller's stream
             c.wait_stream(torch.cuda.current_stream(self.dev))
             for t in (k_new, v_new, q_new):
                 t.record_stream(c)
-            pa.check(pa.pa_cache_write(c, k_new, v_new, self.slots_dev[X][:n_tok], self.k, self.v,
+        with torch.cuda.stream(c):
+            dvb[:off].copy_(self.host_buf[X][:off], non_blocking=True)
+        if n_tok:
+            pa.check(pa.pa_cache_write(c, k_new, v_new, d_sl, self.k, self.v,
                                        self.cache_blocks, self.h_kv, self.d, BLOCK, self.k_scale,
                                        self.v_scale))
         if n_pf:
-            meta = self.pmeta_dev[X]
-            pa.check(pa.pa_prefill_chunk(c, self.out_pf[X][:n_pt], q_new[:n_pt], meta[:n_pf + 1],
-                                         meta[n_pf + 1:2 * n_pf + 1],
-                                         self.k, self.v,
-                                         self.ptab_dev[X][:n_pf * mbp].view(n_pf, mbp),
+            pa.check(pa.pa_prefill_chunk(c, self.out_pf[X][:n_pt], q_new[:n_pt], d_pm[:n_pf + 1],
+                                         d_pm[n_pf + 1:], self.k, self.v, d_pt.view(n_pf, mbp),
                                          self.cache_blocks, self.h_kv, int(pl.max()),
                                          int((pst + pl).max()), self.sm, self.k_scale,
                                          self.v_scale, self.ws_pf))
         if n_dec:
             pa.check(pa.pa_decode(c, self.out_dec[X][:n_dec], q_new[n_pt:n_tok], self.k, self.v,
-                                  self.dtab_dev[X][:n_dec * mbd].view(n_dec, mbd),
-                                  self.dlen_dev[X][:n_dec], self.cache_blocks, self.h_kv,
+                                  d_dt.view(n_dec, mbd), d_dl, self.cache_blocks, self.h_kv,
                                   int(dp.max()) + 1, self.sm, self.k_scale, self.v_scale,
                                   self.ws_dec))
         self.ev_done[X].record(c)
