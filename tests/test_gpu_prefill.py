@@ -146,3 +146,36 @@ def test_mixed_prefill_full_size_sampled():
         return np.unique(np.concatenate([fixed, rng.choice(512, 7, replace=False)]))
 
     _mixed_prefix_run([0, 1, 31, 63], sample)
+
+
+def test_slices_with_empty_slice_and_wide_groups_fp8():
+    # a zero-length slice between two others; 16 query heads per KV head
+    # (two head groups per work-group set), fp8 cache, head dim 64
+    w = workloads.prefill_workload("empty-slice", 600, prompts=[500, 300],
+                                   slices=[(0, 100, 77), (1, 50, 0), (1, 50, 130)],
+                                   h_q=32, h_kv=2, d=64, cache_dtype="fp8")
+    _check(w, "fp8 32/2 d64 with an empty slice")
+
+
+def test_zero_work_calls_are_no_ops():
+    import torch
+
+    import paged_kv_cache_host_amd as pa
+    from paged_kv_cache_host_amd.engine import PagedKV
+
+    kv = PagedKV(8, 2, 64, "bf16", "cuda")
+    e = torch.empty((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    sl = torch.empty((0,), dtype=torch.int32, device="cuda")
+    assert pa.pa_cache_write(None, e, e, sl, kv.k, kv.v, 8, 2, 64) == 0
+    q = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    tables = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
+    lens = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    assert pa.pa_decode(None, out, q, kv.k, kv.v, tables, lens, 8, 2, 16,
+                        0.125, 1.0, 1.0, None) == 0
+    cu = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    st = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    assert pa.pa_prefill_chunk(None, out, q, cu, st, kv.k, kv.v, tables, 8, 2, 0, 16,
+                               0.125, 1.0, 1.0, None) == 0
+    torch.cuda.synchronize()
+    kv.close()
