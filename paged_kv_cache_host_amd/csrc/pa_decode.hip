@@ -46,15 +46,27 @@
 namespace pa {
 
 constexpr int kDecodeWaves = 8;                  // waves per work-group
-constexpr int kChunkTokens = 2048;               // tokens per work-group
-constexpr int kChunkBlocks = kChunkTokens / kBlock;
+constexpr int kMinChunkShift = 7;               // smallest chunk: 128 blocks = 2048 tokens
+constexpr int kMaxChunkShift = 9;               // largest chunk: 512 blocks = 8192 tokens
 constexpr int kMaxGroup = 16;                    // query heads per KV head (MFMA columns)
 constexpr int kMaxSeqsPerLaunch = 4096;          // item prefix kept in LDS
 constexpr int kThreads = kWave * kDecodeWaves;
 
-inline int32_t decode_num_chunks(int32_t max_context_len) {
+// Chunk size (log2 of the blocks one work item covers), a function of the
+// launch shape only.  Small chunks spread a few long contexts over the chip;
+// once the launch's KV rows (bounded by S x H_kv x max_context_len) fill
+// two chip-fulls (2 x 256 CUs) of items at a larger size, the larger size
+// wins: fewer items carry less per-item set-up and fewer partials to merge.
+inline int32_t decode_chunk_shift(int32_t S, int32_t H_kv, int32_t max_context_len) {
+  const int64_t work = static_cast<int64_t>(S) * H_kv * max_context_len;
+  for (int32_t sh = kMaxChunkShift; sh > kMinChunkShift; --sh)
+    if (work >= 2 * 256 * (int64_t{kBlock} << sh)) return sh;
+  return kMinChunkShift;
+}
+
+inline int32_t decode_num_chunks(int32_t max_context_len, int32_t shift) {
   const int32_t nblk = (max_context_len + kBlock - 1) / kBlock;
-  return nblk <= 0 ? 1 : (nblk + kChunkBlocks - 1) / kChunkBlocks;
+  return nblk <= 0 ? 1 : ((nblk - 1) >> shift) + 1;
 }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -179,8 +191,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const typename CacheT::raw* __restrict__ k_cache,
     const typename CacheT::raw* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     int32_t max_blocks, int32_t num_blocks, const int32_t* __restrict__ context_lens, int32_t S,
-    int32_t H_q, int32_t H_kv, int32_t G, int32_t n_chunks, float score_scale, float out_scale,
-    int32_t* __restrict__ counters, float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+    int32_t H_q, int32_t H_kv, int32_t G, int32_t n_chunks, int32_t chunk_shift, float score_scale,
+    float out_scale, int32_t* __restrict__ counters, float* __restrict__ ws_ml, float* __restrict__ ws_o) {
   __shared__ float lds_o[kDecodeWaves][kMaxGroup][D];
   __shared__ float lds_ml[kDecodeWaves][kMaxGroup][2];
   __shared__ int32_t pre[kMaxSeqsPerLaunch + 1];     // full-chunk items before seq i
@@ -194,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   const int c = lane & 15;
   const int g = lane >> 4;
 
-  // Work items, largest first: every full chunk (kChunkBlocks blocks; the
+  // Work items, largest first: every full chunk (2^chunk_shift blocks; the
   // last chunk index also takes any excess past max_context_len), then the
   // partial last chunk of each sequence, in decreasing size, so that the
   // queue ends with its smallest items.
@@ -202,10 +214,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const int32_t Li = min(context_lens[i], max_blocks * kBlock);
     return Li <= 0 ? 0 : (Li + kBlock - 1) / kBlock;
   };
-  auto full_of = [&](int32_t nb) -> int32_t { return min(nb / kChunkBlocks, n_chunks); };
+  auto full_of = [&](int32_t nb) -> int32_t { return min(nb >> chunk_shift, n_chunks); };
   auto part_of = [&](int32_t nb) -> int32_t {
     const int32_t f = full_of(nb);
-    return (f < n_chunks && nb > f * kChunkBlocks) ? nb - f * kChunkBlocks : 0;
+    return (f < n_chunks && nb > (f << chunk_shift)) ? nb - (f << chunk_shift) : 0;
   };
   // block-wide exclusive scan of v over the launch's sequences, kThreads at
   // a time; returns this thread's exclusive prefix and updates carry
@@ -296,8 +308,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 
   const int32_t L = min(context_lens[seq], max_blocks * kBlock);
   const int32_t nblk = (L + kBlock - 1) / kBlock;
-  const int32_t c0 = chunk * kChunkBlocks;
-  const int32_t b1 = (chunk == n_chunks - 1) ? nblk : min(nblk, c0 + kChunkBlocks);
+  const int32_t c0 = chunk << chunk_shift;
+  const int32_t b1 = (chunk == n_chunks - 1) ? nblk : min(nblk, c0 + (1 << chunk_shift));
   const int32_t* __restrict__ table = block_tables + static_cast<int64_t>(seq) * max_blocks;
 
   // Q^T operand: column c = head kvh*G + c, zero for padded columns.
@@ -483,14 +495,14 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ context_lens, int32_t max_blocks, int32_t S, int32_t H_q,
-    int32_t n_chunks, float out_scale) {
+    int32_t n_chunks, int32_t chunk_shift, float out_scale) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
   if (idx >= static_cast<int64_t>(S) * H_q) return;
   const int seq = static_cast<int>(idx / H_q);
   const int32_t L = min(context_lens[seq], max_blocks * kBlock);
   const int32_t nblk = (L + kBlock - 1) / kBlock;
-  const int nsp = L <= 0 ? 0 : min(n_chunks, (nblk + kChunkBlocks - 1) / kChunkBlocks);
+  const int nsp = L <= 0 ? 0 : min(n_chunks, ((nblk - 1) >> chunk_shift) + 1);
   if (nsp == 1) return;  // written by the attention kernel
   const float* ml = ws_ml + idx * n_chunks * 2;
   const float* po = ws_o + idx * n_chunks * D;
@@ -549,7 +561,8 @@ static pa_status launch_decode_mfma(hipStream_t st, void* out, const void* q, co
                                     const int32_t* context_lens, int32_t S, int32_t H_q,
                                     int32_t H_kv, int32_t max_context_len, float sm_scale,
                                     float k_scale, float v_scale, void* ws) {
-  const int32_t n_chunks = decode_num_chunks(max_context_len);
+  const int32_t shift = decode_chunk_shift(S, H_kv, max_context_len);
+  const int32_t n_chunks = decode_num_chunks(max_context_len, shift);
   int32_t* counters = static_cast<int32_t*>(ws);
   float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_counter_bytes(S));
   float* ws_o = ws_ml + static_cast<int64_t>(S) * H_q * n_chunks * 2;
@@ -565,7 +578,7 @@ static pa_status launch_decode_mfma(hipStream_t st, void* out, const void* q, co
                        static_cast<const typename CacheT::raw*>(k_cache),
                        static_cast<const typename CacheT::raw*>(v_cache),
                        block_tables + s0 * max_blocks, max_blocks, num_blocks, context_lens + s0,
-                       sn, H_q, H_kv, H_q / H_kv, n_chunks, score_scale, v_scale, counters + 2 * b,
+                       sn, H_q, H_kv, H_q / H_kv, n_chunks, shift, score_scale, v_scale, counters + 2 * b,
                        ws_ml + s0 * H_q * n_chunks * 2, ws_o + s0 * H_q * n_chunks * D);
     timing_mark(st, kDecode, false);
     hipError_t e = hipGetLastError();
@@ -577,7 +590,7 @@ static pa_status launch_decode_mfma(hipStream_t st, void* out, const void* q, co
     timing_mark(st, kDecodeMerge, true);
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, st,
                        static_cast<uint16_t*>(out), ws_ml, ws_o, context_lens, max_blocks, S, H_q,
-                       n_chunks, v_scale);
+                       n_chunks, shift, v_scale);
     timing_mark(st, kDecodeMerge, false);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -608,7 +621,9 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t S, int32_t H_q, int32_t H_kv
                                             int32_t max_context_len) {
   if (S <= 0 || H_q <= 0 || D <= 0) return 0;
   (void)H_kv;
-  const int64_t n_chunks = decode_num_chunks(max_context_len);
+  // sized for the smallest chunk, so that it covers every chunk choice of
+  // any call with at most these S and max_context_len
+  const int64_t n_chunks = decode_num_chunks(max_context_len, kMinChunkShift);
   return decode_counter_bytes(S) + static_cast<size_t>(S) * H_q * n_chunks * (D + 2) * sizeof(float);
 }
 

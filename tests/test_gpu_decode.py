@@ -70,6 +70,33 @@ def test_edge_lengths_fp8(h_q, h_kv, d):
                 f"edge fp8 {h_q}/{h_kv} d{d}")
 
 
+@pytest.mark.parametrize("S,long_lengths", [
+    # 34 x 8 x 9000 ~ 2.4M KV rows in the launch bound: 4096-token work items
+    (34, [2047, 2048, 2049, 4095, 4096, 4097, 8192, 9000]),
+    # 34 x 8 x 16385 ~ 4.5M: 8192-token work items
+    (34, [4097, 8191, 8192, 8193, 16384, 16385]),
+])
+def test_large_work_items(S, long_lengths):
+    """Launches whose size selects the longer work items: contexts that end
+    on and beside the item boundaries (one, two and three items, merged)
+    beside short ones; the oracle runs on the long sequences and two short
+    ones."""
+    rng = np.random.default_rng(500 + max(long_lengths))
+    short = rng.integers(1, 300, S - len(long_lengths))
+    lengths = np.concatenate([long_lengths, short])
+    w = _edge_workload(lengths, 64, 8, 128, "bf16", "bf16", seed=S + max(long_lengths))
+    say(f"[decode parity] large items: {w.name} S={w.num_seqs} maxL={int(w.lengths.max())}")
+    hip = hip_decode_run(w, DEV)
+    seqs = list(range(len(long_lengths))) + [len(long_lengths), S - 1]
+    ref = oracle_decode_run(w, seqs=seqs)
+    assert np.array_equal(hip["tables"], ref["tables"])
+    assert np.array_equal(hip["slots"], ref["slots"])
+    got = out_to_f64(hip["outs"][0], "bf16")
+    err = assert_close(got[seqs], ref["out"][seqs], "bf16", "large items")
+    say(f"    max|d| = {err:.3g}")
+    hip["kv"].close()
+
+
 def test_edge_lengths_f32_gqa():
     _check_full(_edge_workload([1, 16, 17, 100, 300], 8, 2, 64, "f32", "f32", seed=300),
                 "edge f32 8/2 d64")
