@@ -8,7 +8,8 @@ Headline step (``value``): one continuous-batching decode iteration of one
   a1  host: libpa grows every sequence by one token (one block taken at each
       block boundary) and packs slots, block tables and context lengths into
       one pinned buffer (double-buffered, so this host work overlaps the
-      previous step's kernels); one copy on the compute stream moves it;
+      previous step's kernels); one pa_stage kernel on the compute stream
+      moves it to the device;
   a2  pa_cache_write scatters the new tokens' K/V into their paged slots;
   a3  pa_decode: split-K paged attention (+ merge of multi-chunk contexts).
 
@@ -36,6 +37,7 @@ Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -236,6 +238,14 @@ def _fill_random(kv, slots: np.ndarray, gen, dev, chunk: int = 1 << 16):
         kv.write(kk, vv, torch.from_numpy(np.ascontiguousarray(slots[a:a + n], dtype=np.int32)).to(dev))
 
 
+def _settle():
+    """Before a timed loop: collect, then move every live object to the
+    permanent generation, so that no full collection over the interpreter's
+    (torch-sized) heap pauses the host thread inside the loop."""
+    gc.collect()
+    gc.freeze()
+
+
 def _timings(pa, names):
     out = {}
     for name in names:
@@ -257,7 +267,8 @@ def decode_leg(args, dev):
     lengths, num_blocks, free_order = workloads.decode_70b_layout()
     S = len(lengths)
     seqs = np.arange(S, dtype=np.int64)
-    max_ctx = int(lengths.max()) + W + K + 5
+    EXTRA, TIME_EVERY = 4, 4
+    max_ctx = int(lengths.max()) + W + K + EXTRA
     MB = -(-max_ctx // BLOCK)
 
     # -- set-up (untimed): pool, contexts of L-1 tokens already cached
@@ -278,33 +289,39 @@ def decode_leg(args, dev):
     ws = decode_workspace(S, H_Q, H_KV, D, max_ctx, dev)
     sm = sm_scale_for(D)
 
-    # One pinned host buffer and one device buffer per parity hold the
-    # step's slots, context lengths and block tables, so that a single copy
-    # on the compute stream carries them (no cross-stream dependency).
+    # A ring of NBUF pinned host buffers, each with a device twin, holds the
+    # steps' slots, context lengths and block tables; one pa_stage kernel on
+    # the compute stream carries a step's buffer (no copy engine, no
+    # cross-engine wait).  The host may refill a buffer once the stage kernel
+    # that read it has run: one event per GROUP steps tells it so (an event
+    # record costs the stream a few microseconds, so not one per step).
+    NBUF, GROUP = 8, 4
     n_meta = 2 * S + S * MB
-    host_buf = [torch.empty(n_meta, dtype=torch.int32).pin_memory() for _ in range(2)]
-    dev_buf = [torch.empty(n_meta, dtype=torch.int32, device=dev) for _ in range(2)]
+    host_buf = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True) for _ in range(NBUF)]
+    dev_buf = [torch.empty(n_meta, dtype=torch.int32, device=dev) for _ in range(NBUF)]
     views = []
-    for X in range(2):
+    for X in range(NBUF):
         h, d_ = host_buf[X].numpy(), dev_buf[X]
         views.append((h[:S].reshape(S, 1), h[S:2 * S], h[2 * S:].reshape(S, MB),
                       d_[:S], d_[S:2 * S], d_[2 * S:].view(S, MB)))
     compute = torch.cuda.Stream(device=dev)
-    ev_consumed = [torch.cuda.Event() for _ in range(2)]
-    for e in ev_consumed:
+    ev_group = [torch.cuda.Event() for _ in range(2)]
+    for e in ev_group:
         e.record(compute)
     ctx_lens = []
 
     def step(i: int, timed: bool):
-        X = i & 1
+        X = i % NBUF
+        g = i // GROUP
         h_slots, h_lens, h_tab, d_slots, d_lens, d_tab = views[X]
-        ev_consumed[X].synchronize()
+        if i % GROUP == 0:
+            # recorded after group g-2, whose steps last used this group's buffers
+            ev_group[g % 2].synchronize()
         st, done, _ = pa.pa_batch_append(kv.pool, seqs, 1, h_slots)
         pa.check(st)
         st, _, lens_np = pa.pa_pack_batch(kv.pool, seqs, MB, h_tab, h_lens)
         pa.check(st)
-        with torch.cuda.stream(compute):
-            dev_buf[X].copy_(host_buf[X], non_blocking=True)
+        pa.check(pa.pa_stage(compute, dev_buf[X], host_buf[X]))
         r = i % R
         pa.check(pa.pa_cache_write(compute, k_ring[r], v_ring[r], d_slots, kv.k, kv.v,
                                    num_blocks, H_KV, D, BLOCK))
@@ -312,43 +329,48 @@ def decode_leg(args, dev):
                               num_blocks, H_KV, max_ctx, sm, 1.0, 1.0, ws))
         if timed:
             ctx_lens.append(lens_np.copy())
-        ev_consumed[X].record(compute)
+        if i % GROUP == GROUP - 1:
+            ev_group[g % 2].record(compute)
 
     for i in range(W):
         step(i, False)
     torch.cuda.synchronize()
-    # The library brackets its kernel launches with HIP events on the stream
-    # it launches on (here `compute`); reset and enable for the timed
-    # steps; only the decode kernel is bracketed, so that the events add no
-    # gaps around the other kernels of the step.
-    pa.check(pa.pa_timing_enable(["decode"]))
+    # Kernel timing: the library attaches a pair of HIP events to a selected
+    # kernel's launch on the stream it launches on (here `compute`).  Each
+    # timed launch costs the stream a few microseconds, so the timed steps
+    # time every TIME_EVERY-th decode launch only; a few more steps time the
+    # step's other kernels.
+    pa.check(pa.pa_timing_enable(["decode"], every=TIME_EVERY))
+    _settle()
     t0 = time.perf_counter()
     for i in range(K):
         step(W + i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     tm = _timings(pa, ("decode",))
-    assert tm["decode"][0] == K, tm
-    # a few more steps, every kernel timed, for the step's other kernels
-    pa.check(pa.pa_timing_enable(True))
-    for i in range(5):
+    assert tm["decode"][0] == len(range(0, K, TIME_EVERY)), tm
+    pa.check(pa.pa_timing_enable(["decode_merge", "cache_write", "stage"]))
+    for i in range(EXTRA):
         step(W + K + i, False)
     torch.cuda.synchronize()
-    tm.update(_timings(pa, ("decode_merge", "cache_write")))
+    tm.update(_timings(pa, ("decode_merge", "cache_write", "stage")))
     pa.check(pa.pa_timing_enable(False))
     kv.close()
 
     dec_bytes = [decode_bytes(l) for l in ctx_lens]
     total_bytes = sum(dec_bytes) + K * cache_write_bytes(S)
     dec_avg_s = tm["decode"][1] / 1e6
+    timed_bytes = float(np.mean(dec_bytes[::TIME_EVERY]))
     return {
         "value": total_bytes / wall / 1e9,
         "wall": wall,
         "mean_context": float(np.mean([l.mean() for l in ctx_lens])),
         "num_seqs": S, "num_blocks": num_blocks,
-        "achieved": (sum(dec_bytes) / K) / dec_avg_s / 1e9,
+        "achieved": timed_bytes / dec_avg_s / 1e9,
+        "timed_launches": tm["decode"][0],
         "kernel_us": dec_avg_s * 1e6,
         "merge_us": tm["decode_merge"][1], "cache_write_us": tm["cache_write"][1],
+        "stage_us": tm["stage"][1],
         "bytes_per_launch": int(sum(dec_bytes) / K),
     }
 
@@ -393,19 +415,21 @@ def mixed_leg(args, dev):
                                   for c in range(iters))), dtype=torch.uint8, device=dev)
     cu = torch.tensor([0, C], dtype=torch.int32, device=dev)
 
-    # per parity: one pinned buffer [slots NT | start 1 | lens S | tables S*MB]
-    # and its device twin, copied once per iteration on the compute stream
+    # a ring of NBUF pinned buffers [slots NT | start 1 | lens S | tables S*MB],
+    # each with a device twin, staged once per iteration on the compute
+    # stream; one event per GROUP iterations frees them for refilling
+    NBUF, GROUP = 8, 4
     n_meta = NT + 1 + S + S * MB
-    host_buf = [torch.empty(n_meta, dtype=torch.int32).pin_memory() for _ in range(2)]
-    dev_buf = [torch.empty(n_meta, dtype=torch.int32, device=dev) for _ in range(2)]
+    host_buf = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True) for _ in range(NBUF)]
+    dev_buf = [torch.empty(n_meta, dtype=torch.int32, device=dev) for _ in range(NBUF)]
     views = []
-    for X in range(2):
+    for X in range(NBUF):
         h, d_ = host_buf[X].numpy(), dev_buf[X]
         o1, o2, o3 = NT, NT + 1, NT + 1 + S
         views.append((h[:NT], h[o1:o2], h[o2:o3], h[o3:].reshape(S, MB),
                       d_[:NT], d_[o1:o2], d_[o2:o3], d_[o3:].view(S, MB)))
     compute = torch.cuda.Stream(device=dev)
-    ev_consumed = [torch.cuda.Event() for _ in range(2)]
+    ev_group = [torch.cuda.Event() for _ in range(2)]
 
     def run_pass(timed: bool, n_iters: int):
         # fresh pool: decode contexts of L0-1 tokens cached, prompt blocks
@@ -420,23 +444,24 @@ def mixed_leg(args, dev):
         ptab, _ = kv.pack([PROMPT], PB)
         ptab_dev = torch.from_numpy(ptab).to(dev)
         torch.cuda.synchronize()
-        for e in ev_consumed:
+        for e in ev_group:
             e.record(compute)
         if timed:
             pa.check(pa.pa_timing_enable(["prefill", "prefill_merge"]))
+        _settle()
         t0 = time.perf_counter()
         for c in range(n_iters):
-            X = c & 1
+            X = c % NBUF
             h_sl, h_st, h_len, h_tab, d_sl, d_st, d_len, d_tab = views[X]
-            ev_consumed[X].synchronize()
+            if c % GROUP == 0:
+                ev_group[(c // GROUP) % 2].synchronize()
             pa.check(pa.pa_seq_slots(kv.pool, PROMPT, c * C, C, h_sl[:C])[0])
             st, _, _ = pa.pa_batch_append(kv.pool, dec_seqs, 1, h_sl[C:].reshape(S, 1))
             pa.check(st)
             st, _, _ = pa.pa_pack_batch(kv.pool, dec_seqs, MB, h_tab, h_len)
             pa.check(st)
             h_st[0] = c * C
-            with torch.cuda.stream(compute):
-                dev_buf[X].copy_(host_buf[X], non_blocking=True)
+            pa.check(pa.pa_stage(compute, dev_buf[X], host_buf[X]))
             r = c % R
             pa.check(pa.pa_cache_write(compute, k_ring[r], v_ring[r], d_sl, kv.k, kv.v,
                                        num_blocks, H_KV, D, BLOCK))
@@ -445,7 +470,8 @@ def mixed_leg(args, dev):
                                          (c + 1) * C, sm, 1.0, 1.0, ws_p))
             pa.check(pa.pa_decode(compute, out_d, q_dec[r], kv.k, kv.v, d_tab,
                                   d_len, num_blocks, H_KV, max_dec, sm, 1.0, 1.0, ws_d))
-            ev_consumed[X].record(compute)
+            if c % GROUP == GROUP - 1:
+                ev_group[(c // GROUP) % 2].record(compute)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         tm = None
@@ -586,6 +612,7 @@ def trace_leg(args, dev):
         run = LayerIterations(w.num_blocks, H_Q, H_KV, D, dev, provider, w.max_running,
                               w.prefill_budget, max_context=max_ctx, cache_blocks=used_blocks)
     torch.cuda.synchronize()
+    _settle()
     t0 = time.perf_counter()
     n_tok = 0
     for it in range(w.iters):
@@ -701,7 +728,8 @@ def main():
                      "traffic": traffic_from_profile(digest), "kernel": "decode_kernel<BF16,128>",
                      "kernel_us": round(d["kernel_us"], 2),
                      "other_kernels_us": {"decode_merge_kernel": round(d["merge_us"], 2),
-                                          "cache_write_kernel": round(d["cache_write_us"], 2)},
+                                          "cache_write_kernel": round(d["cache_write_us"], 2),
+                                          "stage_kernel": round(d["stage_us"], 2)},
                      "algorithmic_bytes_per_launch": d["bytes_per_launch"],
                      "kernel_source_digest": digest},
     }

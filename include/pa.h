@@ -317,16 +317,40 @@ pa_status pa_sched_step(pa_sched* sched, pa_sched_batch* batch);
 pa_status pa_sched_stats(const pa_sched* sched, pa_sched_accounting* out);
 
 /* ------------------------------------------------------------------------
+ * pa_stage -- copy one iteration's host-built metadata (slot mappings,
+ * context lengths, block tables packed by pa_batch_append / pa_pack_batch /
+ * pa_sched_step) from pinned host memory to the device, as a kernel on
+ * `stream`.  LESSON "Continuous batching at the iteration level": the batch
+ * is rebuilt on the host every iteration; ARTICLE 2.3: the attention kernel
+ * reads the block tables and context lengths from device memory.  Unlike a
+ * copy-engine transfer, the kernel orders with the other kernels of the
+ * stream without cross-engine waits.
+ *
+ * dst      [device, bytes], 4-byte aligned
+ * src_host [host, bytes], 4-byte aligned, inside an allocation of pinned
+ *          host memory (hipHostMalloc); else PA_ERR_INVALID.  It is read
+ *          while the kernel runs: the caller must not rewrite it before the
+ *          stream has passed this call (double-buffer by iteration parity).
+ * bytes    multiple of 4; 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+pa_status pa_stage(void* stream, void* dst, const void* src_host, size_t bytes);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (instrumentation, off by default).  Each launch of a
- * selected kernel is bracketed by a pair of HIP events recorded on the
- * caller's stream (up to 4096 launches per kernel between resets).  Kernel
- * names and their bits: "cache_write" 1, "decode" 2, "decode_merge" 4,
- * "prefill" 8, "prefill_merge" 16, "generic" 32.
+ * selected kernel carries a pair of HIP events attached to the launch
+ * (hipExtLaunchKernel), which take that kernel's start and end times (up to
+ * 4096 launches per kernel between resets).  The events cost the stream a
+ * few microseconds per timed launch.  Kernel names and their bits:
+ * "cache_write" 1, "decode" 2, "decode_merge" 4, "prefill" 8,
+ * "prefill_merge" 16, "generic" 32, "stage" 64.
  * ---------------------------------------------------------------------- */
 
-/* Record the kernels whose bits are set in `mask` (-1: all, 0: none); either
- * way the recorded launches are forgotten. */
-pa_status pa_timing_enable(int32_t mask);
+/* Time the kernels whose bits are set in `mask` (-1: all, 0: none): of each
+ * selected kernel, the launches 0, every, 2 * every, ... counted from this
+ * call (every >= 1, else PA_ERR_INVALID).  Either way the kept launches are
+ * forgotten.  Call it with no timed launch of the previous recording still
+ * in flight (its events are reused). */
+pa_status pa_timing_enable(int32_t mask, int32_t every);
 
 /* Wait for the recorded launches of `kernel` [host string] and report their
  * number, mean and total duration in microseconds (each [host]). */

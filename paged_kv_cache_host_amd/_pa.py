@@ -86,7 +86,8 @@ _SIGS = {
     "pa_sched_add": (_i32, [_vp, _i64, _i32, _i32]),
     "pa_sched_step": (_i32, [_vp, C.POINTER(SchedBatchC)]),
     "pa_sched_stats": (_i32, [_vp, C.POINTER(SchedAccountingC)]),
-    "pa_timing_enable": (_i32, [_i32]),
+    "pa_stage": (_i32, [_vp, _vp, _vp, _sz]),
+    "pa_timing_enable": (_i32, [_i32, _i32]),
     "pa_timing_query": (_i32, [C.c_char_p, _i32p, C.POINTER(_f32), C.POINTER(_f32)]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_prefill_chunk": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
@@ -326,12 +327,12 @@ def pa_sched_stats(sched):
 # -------------------------------------------------------------- timing -----
 
 TIMING_BITS = {"cache_write": 1, "decode": 2, "decode_merge": 4, "prefill": 8,
-               "prefill_merge": 16, "generic": 32}
+               "prefill_merge": 16, "generic": 32, "stage": 64}
 
 
-def pa_timing_enable(enable=True) -> int:
+def pa_timing_enable(enable=True, every: int = 1) -> int:
     """``enable``: True (all kernels), False (none), or an iterable of kernel
-    names to record."""
+    names to record; ``every``: time every n-th launch of each (from 0)."""
     if enable is True:
         mask = -1
     elif not enable:
@@ -340,7 +341,7 @@ def pa_timing_enable(enable=True) -> int:
         mask = 0
         for name in enable:
             mask |= TIMING_BITS[name]
-    return _lib.pa_timing_enable(mask)
+    return _lib.pa_timing_enable(mask, every)
 
 
 def pa_timing_query(kernel: str):
@@ -390,6 +391,17 @@ def pa_cache_write(stream, k_new, v_new, slot_mapping, k_cache, v_cache, num_blo
                                dtype_of(k_new), _dptr(slot_mapping), n, _dptr(k_cache),
                                _dptr(v_cache), dtype_of(k_cache), num_blocks, H_kv, D, bs,
                                k_scale, v_scale)
+
+
+def pa_stage(stream, dst, src_host, nbytes: int | None = None) -> int:
+    """Copy ``nbytes`` (default: all of ``src_host``) from a pinned host
+    tensor into the device tensor ``dst`` with a kernel on ``stream``."""
+    if src_host.is_cuda or not src_host.is_pinned():
+        raise PaError(PA_ERR_INVALID, "pa_stage: source must be a pinned host tensor")
+    n = src_host.numel() * src_host.element_size() if nbytes is None else int(nbytes)
+    if n > src_host.numel() * src_host.element_size() or n > dst.numel() * dst.element_size():
+        raise PaError(PA_ERR_INVALID, "pa_stage: nbytes exceeds a buffer")
+    return _lib.pa_stage(_stream_handle(stream), _dptr(dst), src_host.data_ptr(), n)
 
 
 def pa_decode_workspace_bytes(S: int, H_q: int, H_kv: int, D: int, max_context_len: int) -> int:

@@ -92,14 +92,12 @@ static pa_status launch_cw(hipStream_t st, const void* k_new, const void* v_new,
                            const int32_t* slots, int32_t n, void* k_cache, void* v_cache,
                            int32_t num_blocks, int32_t H_kv, float k_inv, float v_inv) {
   dim3 grid((n + 15) / 16, H_kv);
-  timing_mark(st, kCacheWrite, true);
-  hipLaunchKernelGGL((cache_write_kernel<NewT, CacheT, D>), grid, dim3(256), 0, st,
-                     static_cast<const typename NewT::raw*>(k_new),
-                     static_cast<const typename NewT::raw*>(v_new), slots, n,
-                     static_cast<typename CacheT::raw*>(k_cache),
-                     static_cast<typename CacheT::raw*>(v_cache), num_blocks, H_kv, k_inv, v_inv);
-  timing_mark(st, kCacheWrite, false);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch(kCacheWrite, cache_write_kernel<NewT, CacheT, D>, grid, dim3(256), 0, st,
+                        static_cast<const typename NewT::raw*>(k_new),
+                        static_cast<const typename NewT::raw*>(v_new), slots, n,
+                        static_cast<typename CacheT::raw*>(k_cache),
+                        static_cast<typename CacheT::raw*>(v_cache), num_blocks, H_kv, k_inv,
+                        v_inv);
   if (e != hipSuccess)
     return fail(PA_ERR_DEVICE, "pa_cache_write: launch failed: %s", hipGetErrorString(e));
   return PA_OK;

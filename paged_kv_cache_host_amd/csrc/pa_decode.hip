@@ -571,28 +571,23 @@ static pa_status launch_decode_mfma(hipStream_t st, void* out, const void* q, co
   for (int32_t b = 0; b < decode_num_batches(S); ++b) {
     const int64_t s0 = static_cast<int64_t>(b) * kMaxSeqsPerLaunch;
     const int32_t sn = static_cast<int32_t>(std::min<int64_t>(kMaxSeqsPerLaunch, S - s0));
-    timing_mark(st, kDecode, true);
-    hipLaunchKernelGGL((decode_kernel<CacheT, D>), dim3(grid), dim3(kThreads), 0, st,
-                       static_cast<uint16_t*>(out) + s0 * H_q * D,
-                       static_cast<const uint16_t*>(q) + s0 * H_q * D,
-                       static_cast<const typename CacheT::raw*>(k_cache),
-                       static_cast<const typename CacheT::raw*>(v_cache),
-                       block_tables + s0 * max_blocks, max_blocks, num_blocks, context_lens + s0,
-                       sn, H_q, H_kv, H_q / H_kv, n_chunks, shift, score_scale, v_scale, counters + 2 * b,
-                       ws_ml + s0 * H_q * n_chunks * 2, ws_o + s0 * H_q * n_chunks * D);
-    timing_mark(st, kDecode, false);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch(kDecode, decode_kernel<CacheT, D>, dim3(grid), dim3(kThreads), 0, st,
+                          static_cast<uint16_t*>(out) + s0 * H_q * D,
+                          static_cast<const uint16_t*>(q) + s0 * H_q * D,
+                          static_cast<const typename CacheT::raw*>(k_cache),
+                          static_cast<const typename CacheT::raw*>(v_cache),
+                          block_tables + s0 * max_blocks, max_blocks, num_blocks, context_lens + s0,
+                          sn, H_q, H_kv, H_q / H_kv, n_chunks, shift, score_scale, v_scale,
+                          counters + 2 * b, ws_ml + s0 * H_q * n_chunks * 2,
+                          ws_o + s0 * H_q * n_chunks * D);
     if (e != hipSuccess)
       return fail(PA_ERR_DEVICE, "pa_decode: launch failed: %s", hipGetErrorString(e));
   }
   if (n_chunks > 1) {
     const int64_t rows = static_cast<int64_t>(S) * H_q;
-    timing_mark(st, kDecodeMerge, true);
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, st,
-                       static_cast<uint16_t*>(out), ws_ml, ws_o, context_lens, max_blocks, S, H_q,
-                       n_chunks, shift, v_scale);
-    timing_mark(st, kDecodeMerge, false);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch(kDecodeMerge, decode_merge_kernel<D>, dim3((rows + 3) / 4), dim3(256), 0,
+                          st, static_cast<uint16_t*>(out), ws_ml, ws_o, context_lens, max_blocks, S,
+                          H_q, n_chunks, shift, v_scale);
     if (e != hipSuccess)
       return fail(PA_ERR_DEVICE, "pa_decode: merge launch failed: %s", hipGetErrorString(e));
   }

@@ -124,15 +124,13 @@ static pa_status launch_generic_t(hipStream_t st, void* out, const void* q, cons
                                   float out_scale) {
   // decode: one row per sequence; prefill: rows = longest slice, one z per slice
   const dim3 grid(rows, H_q, cu_q_lens ? n_chunks : 1);
-  timing_mark(st, kGeneric, true);
-  hipLaunchKernelGGL((attend_generic_kernel<QT, CacheT, OutT>), grid, dim3(kWave), 0, st, static_cast<typename OutT::raw*>(out),
-                     static_cast<const typename QT::raw*>(q),
-                     static_cast<const typename CacheT::raw*>(k_cache),
-                     static_cast<const typename CacheT::raw*>(v_cache), block_tables, max_blocks,
-                     num_blocks, context_lens, cu_q_lens, start_pos, H_q, H_kv, D, score_scale,
-                     out_scale);
-  timing_mark(st, kGeneric, false);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch(kGeneric, attend_generic_kernel<QT, CacheT, OutT>, grid, dim3(kWave), 0, st,
+                        static_cast<typename OutT::raw*>(out),
+                        static_cast<const typename QT::raw*>(q),
+                        static_cast<const typename CacheT::raw*>(k_cache),
+                        static_cast<const typename CacheT::raw*>(v_cache), block_tables, max_blocks,
+                        num_blocks, context_lens, cu_q_lens, start_pos, H_q, H_kv, D, score_scale,
+                        out_scale);
   if (e != hipSuccess)
     return fail(PA_ERR_DEVICE, "generic attention launch failed: %s", hipGetErrorString(e));
   return PA_OK;

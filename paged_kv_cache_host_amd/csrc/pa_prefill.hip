@@ -543,27 +543,22 @@ pa_status launch_prefill_mfma(hipStream_t st, void* out, const void* q, const in
     ws_o = static_cast<float*>(ws);
     ws_ml = ws_o + static_cast<size_t>(geo.n_split) * ws_rows * H_q * D;
   }
-  timing_mark(st, kPrefill, true);
-  hipLaunchKernelGGL((prefill_kernel<CacheT, D>), dim3(static_cast<uint32_t>(gx), n_chunks),
-                     dim3(kPfThreads), 0, st, static_cast<uint16_t*>(out),
-                     static_cast<const uint16_t*>(q), cu_q_lens, start_pos,
-                     static_cast<const typename CacheT::raw*>(k_cache),
-                     static_cast<const typename CacheT::raw*>(v_cache), block_tables, max_blocks,
-                     num_blocks, H_q, geo, score_scale, v_scale, ws_ml, ws_o, ws_rows);
-  timing_mark(st, kPrefill, false);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch(kPrefill, prefill_kernel<CacheT, D>,
+                        dim3(static_cast<uint32_t>(gx), n_chunks), dim3(kPfThreads), 0, st,
+                        static_cast<uint16_t*>(out),
+                        static_cast<const uint16_t*>(q), cu_q_lens, start_pos,
+                        static_cast<const typename CacheT::raw*>(k_cache),
+                        static_cast<const typename CacheT::raw*>(v_cache), block_tables, max_blocks,
+                        num_blocks, H_q, geo, score_scale, v_scale, ws_ml, ws_o, ws_rows);
   if (e != hipSuccess)
     return fail(PA_ERR_DEVICE, "pa_prefill_chunk: launch failed: %s", hipGetErrorString(e));
   if (geo.n_split > 1) {
     const int64_t pairs = static_cast<int64_t>(ws_rows) * H_q;
-    timing_mark(st, kPrefillMerge, true);
     constexpr int kPairsPerGroup = 256 / (D / 4);
-    hipLaunchKernelGGL((prefill_merge_kernel<D>),
-                       dim3(static_cast<uint32_t>((pairs + kPairsPerGroup - 1) / kPairsPerGroup)),
-                       dim3(256), 0, st, static_cast<uint16_t*>(out), cu_q_lens, n_chunks, H_q,
-                       geo.n_split, ws_ml, ws_o, ws_rows, v_scale);
-    timing_mark(st, kPrefillMerge, false);
-    e = hipGetLastError();
+    e = launch(kPrefillMerge, prefill_merge_kernel<D>,
+               dim3(static_cast<uint32_t>((pairs + kPairsPerGroup - 1) / kPairsPerGroup)),
+               dim3(256), 0, st, static_cast<uint16_t*>(out), cu_q_lens, n_chunks, H_q,
+               geo.n_split, ws_ml, ws_o, ws_rows, v_scale);
     if (e != hipSuccess)
       return fail(PA_ERR_DEVICE, "pa_prefill_chunk: merge launch failed: %s",
                   hipGetErrorString(e));

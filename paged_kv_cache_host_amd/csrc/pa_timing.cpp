@@ -1,10 +1,15 @@
 // Optional per-kernel timing of libpa's own launches.
 //
-// For the kernels selected by a bit mask, the launchers record a HIP event
-// before and after each launch on the caller's stream; pa_timing_query waits
-// for the recorded events and reports how many launches of a kernel were
-// recorded and their mean and total duration.  Disabled (the default), the
-// hooks cost one flag test per launch.
+// For the kernels selected by a bit mask, each launch carries a pair of HIP
+// events attached to the launch itself (hipExtLaunchKernel), which take the
+// kernel's start and end times; pa_timing_query waits for them and reports
+// how many launches of a kernel were kept and their mean and total
+// duration; a period n times only every n-th launch of a kernel.  Disabled
+// (the default), the hook costs one flag test per launch.  The events are not free: the start event is one more command in
+// the stream, and a kernel whose end is observable from the host makes the
+// device write its dirty cache lines back when it ends (a few microseconds
+// each, measured on MI355X), so only the kernels of interest should be
+// selected.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -19,7 +24,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kCapacity = 4096;  // launches recorded per kernel between resets
+constexpr int kCapacity = 4096;  // launches kept per kernel between resets
 
 struct Slot {
   hipEvent_t start = nullptr, stop = nullptr;
@@ -27,48 +32,59 @@ struct Slot {
 
 struct Track {
   std::vector<Slot> slots;  // events are created on first use and reused
-  int count = 0;
+  int count = 0;            // launches timed since the last reset
+  int64_t seen = 0;         // launches since the last reset
 };
 
 std::mutex g_mu;
-std::atomic<int32_t> g_mask{0};  // bit k: record kernel k
+std::atomic<int32_t> g_mask{0};  // bit k: time kernel k
+int32_t g_every = 1;             // time launches 0, every, 2 * every, ... of a kernel
 Track g_tracks[kKernelCount];
 
-const char* kNames[kKernelCount] = {"cache_write", "decode",        "decode_merge",
-                                    "prefill",     "prefill_merge", "generic"};
+const char* kNames[kKernelCount] = {"cache_write", "decode",        "decode_merge", "prefill",
+                                    "prefill_merge", "generic",     "stage"};
 
 }  // namespace
 
-void timing_mark(hipStream_t st, KernelId k, bool begin) {
+void timing_events(KernelId k, hipStream_t, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
   if (!(g_mask.load(std::memory_order_relaxed) & (1 << k))) return;
   std::lock_guard<std::mutex> lock(g_mu);
   Track& t = g_tracks[k];
-  if (begin) {
-    if (t.count >= kCapacity) return;
-    if (static_cast<int>(t.slots.size()) <= t.count) {
-      Slot s;
-      if (hipEventCreate(&s.start) != hipSuccess || hipEventCreate(&s.stop) != hipSuccess) {
-        (void)hipGetLastError();
-        return;
-      }
-      t.slots.push_back(s);
+  if (t.seen++ % g_every != 0 || t.count >= kCapacity) return;
+  if (static_cast<int>(t.slots.size()) <= t.count) {
+    Slot s;
+    if (hipEventCreate(&s.start) != hipSuccess || hipEventCreate(&s.stop) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
     }
-    (void)hipEventRecord(t.slots[t.count].start, st);
-  } else {
-    if (t.count >= kCapacity || static_cast<int>(t.slots.size()) <= t.count) return;
-    (void)hipEventRecord(t.slots[t.count].stop, st);
-    ++t.count;
+    t.slots.push_back(s);
   }
+  *start = t.slots[t.count].start;
+  *stop = t.slots[t.count].stop;
+  ++t.count;
+}
+
+void timing_rollback(KernelId k, hipStream_t, hipEvent_t stop) {
+  // the launch failed, so its events were never recorded: forget them
+  std::lock_guard<std::mutex> lock(g_mu);
+  Track& t = g_tracks[k];
+  if (t.count > 0 && t.slots[t.count - 1].stop == stop) --t.count;
 }
 
 }  // namespace pa
 
 using namespace pa;
 
-extern "C" pa_status pa_timing_enable(int32_t mask) {
+extern "C" pa_status pa_timing_enable(int32_t mask, int32_t every) {
+  if (every < 1) return fail(PA_ERR_INVALID, "pa_timing_enable: every=%d must be >= 1", every);
   std::lock_guard<std::mutex> lock(g_mu);
   g_mask = mask;
-  for (auto& t : g_tracks) t.count = 0;
+  g_every = every;
+  for (auto& t : g_tracks) {
+    t.count = 0;
+    t.seen = 0;
+  }
   return PA_OK;
 }
 

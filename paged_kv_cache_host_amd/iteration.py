@@ -7,8 +7,8 @@ slices within the budget; the new tokens' K/V are scattered into the paged
 cache (pa_cache_write) and attention runs for the decode tokens (pa_decode)
 and the prefill slices (pa_prefill_chunk), all on one compute stream.  The
 host work of iteration t+1 (scheduling and table packing into
-double-buffered pinned memory) overlaps the kernels of iteration t; one copy
-on the compute stream then moves the packed metadata.
+double-buffered pinned memory) overlaps the kernels of iteration t; one
+pa_stage kernel on the compute stream then moves the packed metadata.
 
 Token data (new K, V, Q rows) comes from a caller-supplied provider:
 ``provider(seqs, positions) -> (k [n, H_kv, D], v [n, H_kv, D], q [n, H_q, D])``
@@ -55,8 +55,8 @@ class LayerIterations:
         mb = -(-max_context // BLOCK)
         # Per parity one pinned buffer and its device twin hold the
         # iteration's slots, decode context lengths and tables, prefill
-        # tables and slice metadata, packed back to back; one copy on the
-        # compute stream moves the used prefix.
+        # tables and slice metadata, packed back to back; one pa_stage on
+        # the compute stream moves the used prefix.
         T = max_running + max(prefill_budget, 1)
         n_meta = T + max_running + 2 * max_running * mb + 2 * max_running + 1
         self.host_buf = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True) for _ in range(2)]
@@ -171,8 +171,7 @@ class LayerIterations:
             c.wait_stream(torch.cuda.current_stream(self.dev))
             for t in (k_new, v_new, q_new):
                 t.record_stream(c)
-        with torch.cuda.stream(c):
-            dvb[:off].copy_(self.host_buf[X][:off], non_blocking=True)
+        pa.check(pa.pa_stage(c, dvb, self.host_buf[X], 4 * off))
         if n_tok:
             pa.check(pa.pa_cache_write(c, k_new, v_new, d_sl, self.k, self.v,
                                        self.cache_blocks, self.h_kv, self.d, BLOCK, self.k_scale,

@@ -188,3 +188,15 @@ def test_argument_validation_of_kernel_entry_points_on_host():
     assert pa._pa._lib.pa_prefill_chunk(None, None, 1, None, 1, None, None, None, None, 1, None, 4,
                                         4, 1, 64, 8, 128, 8, 512, 512, 0.1, 1.0, 1.0, None,
                                         0) == pa.PA_ERR_INVALID
+
+
+def test_stage_and_timing_argument_checks_on_host():
+    # rejected before any HIP call
+    fake = 0x1000
+    assert pa._pa._lib.pa_stage(None, fake, fake, 0) == 0                # no-op
+    assert pa._pa._lib.pa_stage(None, None, fake, 16) == pa.PA_ERR_INVALID
+    assert pa._pa._lib.pa_stage(None, fake, fake, 6) == pa.PA_ERR_INVALID
+    assert pa._pa._lib.pa_stage(None, fake + 2, fake, 8) == pa.PA_ERR_INVALID
+    assert pa._pa._lib.pa_timing_enable(2, 0) == pa.PA_ERR_INVALID
+    assert "every" in pa.pa_last_error()
+    assert pa._pa._lib.pa_timing_enable(0, 1) == 0
