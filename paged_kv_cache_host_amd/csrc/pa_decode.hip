@@ -179,9 +179,10 @@ __device__ __forceinline__ void store_out4(typename OutT::raw* dst, f32x4 v) {
 // The work items are (sequence, KV head, chunk) for every chunk that holds
 // part of a context; each work-group derives the item list from the context
 // lengths in LDS, then takes items in turn from a ticket counter in the
-// workspace (the next ticket is fetched while the current item runs).  Its
-// waves share out the 2-block steps of the item's chunk and merge their
-// running (m, l, o) through LDS.  A context
+// workspace (the next ticket is fetched when the current item's streaming
+// ends, so its latency overlaps the merge).  Its waves share out the 2-block
+// steps of the item's chunk and merge their running (m, l, o) through LDS.
+// A context
 // that fits one chunk gets its output here; longer ones leave one partial per
 // chunk for the merge kernel.  The last work-group to finish resets the
 // ticket counters, so they are zero again for the next call.
@@ -279,7 +280,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     __syncthreads();
     const int32_t item = __builtin_amdgcn_readfirstlane(s_item);
     if (item >= total) break;
-    if (tid == 0) next = atomicAdd(&counters[0], 1);
     int32_t seq_, chunk_, kvh_;
     if (item < total_full) {
       // last seq with pre[seq] <= item
@@ -437,6 +437,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     compute(xa, xb, p);
   }
 
+  // the next ticket is taken once this item's streaming is done, so that a
+  // work-group that runs ahead takes the next item and the queue balances
+  // (taking it earlier would bind it to this work-group behind a long item)
+  if (tid == 0) next = atomicAdd(&counters[0], 1);
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
   // lane (c, g) holds o^T[d = 16t + 4g + r][head c]; a wave without steps
