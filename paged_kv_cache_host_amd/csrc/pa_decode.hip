@@ -240,6 +240,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     __syncthreads();
     return before + x - v;
   };
+  // the first ticket is requested before the item list is built, so that
+  // the atomic's latency overlaps it
+  int32_t next = 0;
+  if (tid == 0) next = atomicAdd(&counters[0], 1);
   int32_t total_full = 0, n_part = 0;
   for (int32_t base = 0; base < S; base += kThreads) {
     const int32_t i = base + tid;
@@ -273,8 +277,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   __syncthreads();
   const int32_t total = total_full + n_part * H_kv;
 
-  int32_t next = 0;
-  if (tid == 0) next = atomicAdd(&counters[0], 1);
   while (true) {
     if (tid == 0) s_item = next;
     __syncthreads();
