@@ -31,7 +31,7 @@ Secondary legs (skipped with --decode-only):
                  kernels) with Poisson arrivals: tokens/s per layer and KV
                  fragmentation.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 5] [--no-cpu-baseline]
                        [--decode-only]
 """
 from __future__ import annotations
@@ -60,7 +60,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
@@ -270,6 +270,12 @@ def decode_leg(args, dev):
     EXTRA, TIME_EVERY = 4, 4
     max_ctx = int(lengths.max()) + W + K + EXTRA
     MB = -(-max_ctx // BLOCK)
+    # the workload's pool (10% free) covers the growth of a default run; a
+    # longer run appends fresh block ids behind the shuffled ones
+    need = int(np.sum(-(-(lengths - 1 + W + K + EXTRA) // BLOCK)))
+    if need > num_blocks:
+        free_order = np.concatenate([free_order, np.arange(num_blocks, need, dtype=np.int32)])
+        num_blocks = need
 
     # -- set-up (untimed): pool, contexts of L-1 tokens already cached
     kv = PagedKV(num_blocks, H_KV, D, "bf16", dev, free_order)

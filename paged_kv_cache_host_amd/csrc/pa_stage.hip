@@ -23,18 +23,20 @@ namespace pa {
 constexpr int kStageThreads = 256;
 constexpr int kStageUnroll = 4;
 
-// grid: min(ceil(n / (256 * 4)), 256); block: 256.  n: 32-bit words.
-__global__ __launch_bounds__(kStageThreads) void stage_kernel(uint32_t* __restrict__ dst,
-                                                              const uint32_t* __restrict__ src,
+// grid: min(ceil(n / (256 * 4)), 256); block: 256.  n: words of type W
+// (8 bytes when both addresses and the size allow it, else 4).
+template <typename W>
+__global__ __launch_bounds__(kStageThreads) void stage_kernel(W* __restrict__ dst,
+                                                              const W* __restrict__ src,
                                                               int64_t n) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kStageThreads;
   for (int64_t base = static_cast<int64_t>(blockIdx.x) * kStageThreads + threadIdx.x; base < n;
        base += stride * kStageUnroll) {
-    uint32_t v[kStageUnroll];
+    W v[kStageUnroll];
 #pragma unroll
     for (int u = 0; u < kStageUnroll; ++u) {
       const int64_t i = base + u * stride;
-      v[u] = i < n ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0u;
+      v[u] = i < n ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : W{0};
     }
 #pragma unroll
     for (int u = 0; u < kStageUnroll; ++u) {
@@ -42,6 +44,18 @@ __global__ __launch_bounds__(kStageThreads) void stage_kernel(uint32_t* __restri
       if (i < n) dst[i] = v[u];
     }
   }
+}
+
+template <typename W>
+pa_status launch_stage(hipStream_t st, void* dst, const void* src_dev, size_t bytes) {
+  const int64_t n = static_cast<int64_t>(bytes / sizeof(W));
+  const int64_t per_group = int64_t{kStageThreads} * kStageUnroll;
+  const int grid = static_cast<int>(std::min<int64_t>((n + per_group - 1) / per_group, 256));
+  const hipError_t e = launch(kStage, stage_kernel<W>, dim3(grid), dim3(kStageThreads), 0, st,
+                              static_cast<W*>(dst), static_cast<const W*>(src_dev), n);
+  if (e != hipSuccess)
+    return fail(PA_ERR_DEVICE, "pa_stage: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
 }
 
 }  // namespace pa
@@ -62,13 +76,9 @@ extern "C" pa_status pa_stage(void* stream, void* dst, const void* src_host, siz
     return fail(PA_ERR_INVALID, "pa_stage: source is not pinned host memory (%s)",
                 hipGetErrorString(e));
   }
-  const int64_t n = static_cast<int64_t>(bytes / 4);
-  const int64_t per_group = int64_t{kStageThreads} * kStageUnroll;
-  const int grid = static_cast<int>(std::min<int64_t>((n + per_group - 1) / per_group, 256));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  e = launch(kStage, stage_kernel, dim3(grid), dim3(kStageThreads), 0, st,
-             static_cast<uint32_t*>(dst), static_cast<const uint32_t*>(src_dev), n);
-  if (e != hipSuccess)
-    return fail(PA_ERR_DEVICE, "pa_stage: launch failed: %s", hipGetErrorString(e));
-  return PA_OK;
+  if (bytes % 8 == 0 && reinterpret_cast<uintptr_t>(dst) % 8 == 0 &&
+      reinterpret_cast<uintptr_t>(src_dev) % 8 == 0)
+    return launch_stage<uint64_t>(st, dst, src_dev, bytes);
+  return launch_stage<uint32_t>(st, dst, src_dev, bytes);
 }
