@@ -8,9 +8,9 @@ Headline step (``value``): one continuous-batching decode iteration of one
   a1  host: libpa grows every sequence by one token (one block taken at each
       block boundary) and packs slots, block tables and context lengths into
       one pinned buffer (double-buffered, so this host work overlaps the
-      previous step's kernels); one pa_stage kernel on the compute stream
-      moves it to the device;
-  a2  pa_cache_write scatters the new tokens' K/V into their paged slots;
+      previous step's kernels);
+  a2  one pa_stage_cache_write launch moves that buffer to the device and
+      scatters the new tokens' K/V into their paged slots;
   a3  pa_decode: split-K paged attention (+ merge of multi-chunk contexts).
 
 ``value`` is the step's algorithmic HBM bytes (decode: every K/V byte of
@@ -327,10 +327,12 @@ def decode_leg(args, dev):
         pa.check(st)
         st, _, lens_np = pa.pa_pack_batch(kv.pool, seqs, MB, h_tab, h_lens)
         pa.check(st)
-        pa.check(pa.pa_stage(compute, dev_buf[X], host_buf[X]))
         r = i % R
-        pa.check(pa.pa_cache_write(compute, k_ring[r], v_ring[r], d_slots, kv.k, kv.v,
-                                   num_blocks, H_KV, D, BLOCK))
+        # one launch stages the buffer and scatters the new tokens, whose
+        # slots lead the buffer
+        pa.check(pa.pa_stage_cache_write(compute, dev_buf[X], host_buf[X], 4 * n_meta, 0, S,
+                                         k_ring[r], v_ring[r], kv.k, kv.v, num_blocks, H_KV, D,
+                                         BLOCK))
         pa.check(pa.pa_decode(compute, out, q_ring[r], kv.k, kv.v, d_tab, d_lens,
                               num_blocks, H_KV, max_ctx, sm, 1.0, 1.0, ws))
         if timed:
@@ -355,11 +357,11 @@ def decode_leg(args, dev):
     wall = time.perf_counter() - t0
     tm = _timings(pa, ("decode",))
     assert tm["decode"][0] == len(range(0, K, TIME_EVERY)), tm
-    pa.check(pa.pa_timing_enable(["decode_merge", "cache_write", "stage"]))
+    pa.check(pa.pa_timing_enable(["decode_merge", "stage_cache_write"]))
     for i in range(EXTRA):
         step(W + K + i, False)
     torch.cuda.synchronize()
-    tm.update(_timings(pa, ("decode_merge", "cache_write", "stage")))
+    tm.update(_timings(pa, ("decode_merge", "stage_cache_write")))
     pa.check(pa.pa_timing_enable(False))
     kv.close()
 
@@ -375,8 +377,7 @@ def decode_leg(args, dev):
         "achieved": timed_bytes / dec_avg_s / 1e9,
         "timed_launches": tm["decode"][0],
         "kernel_us": dec_avg_s * 1e6,
-        "merge_us": tm["decode_merge"][1], "cache_write_us": tm["cache_write"][1],
-        "stage_us": tm["stage"][1],
+        "merge_us": tm["decode_merge"][1], "stage_cache_write_us": tm["stage_cache_write"][1],
         "bytes_per_launch": int(sum(dec_bytes) / K),
     }
 
@@ -467,10 +468,10 @@ def mixed_leg(args, dev):
             st, _, _ = pa.pa_pack_batch(kv.pool, dec_seqs, MB, h_tab, h_len)
             pa.check(st)
             h_st[0] = c * C
-            pa.check(pa.pa_stage(compute, dev_buf[X], host_buf[X]))
             r = c % R
-            pa.check(pa.pa_cache_write(compute, k_ring[r], v_ring[r], d_sl, kv.k, kv.v,
-                                       num_blocks, H_KV, D, BLOCK))
+            pa.check(pa.pa_stage_cache_write(compute, dev_buf[X], host_buf[X], 4 * n_meta, 0, NT,
+                                             k_ring[r], v_ring[r], kv.k, kv.v, num_blocks, H_KV,
+                                             D, BLOCK))
             pa.check(pa.pa_prefill_chunk(compute, out_p, q_prompt[c * C:(c + 1) * C], cu,
                                          d_st, kv.k, kv.v, ptab_dev, num_blocks, H_KV, C,
                                          (c + 1) * C, sm, 1.0, 1.0, ws_p))
@@ -734,8 +735,8 @@ def main():
                      "traffic": traffic_from_profile(digest), "kernel": "decode_kernel<BF16,128>",
                      "kernel_us": round(d["kernel_us"], 2),
                      "other_kernels_us": {"decode_merge_kernel": round(d["merge_us"], 2),
-                                          "cache_write_kernel": round(d["cache_write_us"], 2),
-                                          "stage_kernel": round(d["stage_us"], 2)},
+                                          "stage_cache_write_kernel":
+                                              round(d["stage_cache_write_us"], 2)},
                      "algorithmic_bytes_per_launch": d["bytes_per_launch"],
                      "kernel_source_digest": digest},
     }

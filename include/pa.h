@@ -336,13 +336,37 @@ pa_status pa_sched_stats(const pa_sched* sched, pa_sched_accounting* out);
 pa_status pa_stage(void* stream, void* dst, const void* src_host, size_t bytes);
 
 /* ------------------------------------------------------------------------
+ * pa_stage_cache_write -- pa_stage and pa_cache_write in one launch, for an
+ * iteration whose slot mapping is part of the staged metadata (LESSON
+ * "Continuous batching at the iteration level": the new tokens' K/V are
+ * scattered into their slots before attention reads them).  Work-groups of
+ * the one kernel copy the buffer while others scatter the new tokens, the
+ * latter reading the slot mapping straight from the pinned host buffer.
+ *
+ * dst, src_host, bytes  as for pa_stage (bytes may be 0 only when n == 0)
+ * slot_offset           byte offset of the n int32 slots inside src_host;
+ *                       a multiple of 4 with slot_offset + 4 n <= bytes, else
+ *                       PA_ERR_INVALID.  The device copy at dst + slot_offset
+ *                       holds the same slots afterwards.
+ * the rest              as for pa_cache_write (types, scales, envelope and
+ *                       the treatment of slots outside the pool).
+ * The cache bytes and the device copy equal those of pa_stage followed by
+ * pa_cache_write on the same stream.
+ * ---------------------------------------------------------------------- */
+pa_status pa_stage_cache_write(void* stream, void* dst, const void* src_host, size_t bytes,
+                               size_t slot_offset, const void* k_new, const void* v_new,
+                               pa_dtype new_dt, int32_t n, void* k_cache, void* v_cache,
+                               pa_dtype cache_dt, int32_t num_blocks, int32_t H_kv, int32_t D,
+                               int32_t bs, float k_scale, float v_scale);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (instrumentation, off by default).  Each launch of a
  * selected kernel carries a pair of HIP events attached to the launch
  * (hipExtLaunchKernel), which take that kernel's start and end times (up to
  * 4096 launches per kernel between resets).  The events cost the stream a
  * few microseconds per timed launch.  Kernel names and their bits:
  * "cache_write" 1, "decode" 2, "decode_merge" 4, "prefill" 8,
- * "prefill_merge" 16, "generic" 32, "stage" 64.
+ * "prefill_merge" 16, "generic" 32, "stage" 64, "stage_cache_write" 128.
  * ---------------------------------------------------------------------- */
 
 /* Time the kernels whose bits are set in `mask` (-1: all, 0: none): of each

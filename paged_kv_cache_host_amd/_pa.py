@@ -87,6 +87,8 @@ _SIGS = {
     "pa_sched_step": (_i32, [_vp, C.POINTER(SchedBatchC)]),
     "pa_sched_stats": (_i32, [_vp, C.POINTER(SchedAccountingC)]),
     "pa_stage": (_i32, [_vp, _vp, _vp, _sz]),
+    "pa_stage_cache_write": (_i32, [_vp, _vp, _vp, _sz, _sz, _vp, _vp, _i32, _i32, _vp, _vp, _i32,
+                                    _i32, _i32, _i32, _i32, _f32, _f32]),
     "pa_timing_enable": (_i32, [_i32, _i32]),
     "pa_timing_query": (_i32, [C.c_char_p, _i32p, C.POINTER(_f32), C.POINTER(_f32)]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -327,7 +329,8 @@ def pa_sched_stats(sched):
 # -------------------------------------------------------------- timing -----
 
 TIMING_BITS = {"cache_write": 1, "decode": 2, "decode_merge": 4, "prefill": 8,
-               "prefill_merge": 16, "generic": 32, "stage": 64}
+               "prefill_merge": 16, "generic": 32, "stage": 64,
+               "stage_cache_write": 128}
 
 
 def pa_timing_enable(enable=True, every: int = 1) -> int:
@@ -402,6 +405,23 @@ def pa_stage(stream, dst, src_host, nbytes: int | None = None) -> int:
     if n > src_host.numel() * src_host.element_size() or n > dst.numel() * dst.element_size():
         raise PaError(PA_ERR_INVALID, "pa_stage: nbytes exceeds a buffer")
     return _lib.pa_stage(_stream_handle(stream), _dptr(dst), src_host.data_ptr(), n)
+
+
+def pa_stage_cache_write(stream, dst, src_host, nbytes: int, slot_offset: int, n: int, k_new,
+                         v_new, k_cache, v_cache, num_blocks: int, H_kv: int, D: int,
+                         bs: int = 16, k_scale: float = 1.0, v_scale: float = 1.0) -> int:
+    """pa_stage of the first ``nbytes`` of the pinned tensor ``src_host`` into
+    ``dst`` plus the cache write of ``n`` new tokens whose int32 slots sit at
+    byte ``slot_offset`` of that buffer, in one launch."""
+    if src_host.is_cuda or not src_host.is_pinned():
+        raise PaError(PA_ERR_INVALID, "pa_stage_cache_write: source must be a pinned host tensor")
+    if nbytes > src_host.numel() * src_host.element_size() or \
+            nbytes > dst.numel() * dst.element_size():
+        raise PaError(PA_ERR_INVALID, "pa_stage_cache_write: nbytes exceeds a buffer")
+    return _lib.pa_stage_cache_write(_stream_handle(stream), _dptr(dst), src_host.data_ptr(),
+                                     nbytes, slot_offset, _dptr(k_new), _dptr(v_new),
+                                     dtype_of(k_new), n, _dptr(k_cache), _dptr(v_cache),
+                                     dtype_of(k_cache), num_blocks, H_kv, D, bs, k_scale, v_scale)
 
 
 def pa_decode_workspace_bytes(S: int, H_q: int, H_kv: int, D: int, max_context_len: int) -> int:

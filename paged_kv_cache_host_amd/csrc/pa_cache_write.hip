@@ -14,6 +14,7 @@
 // thread moves one (token, 16-byte chunk); V: the 16 x D tile is staged in
 // LDS and written column-wise, so that when the 16 tokens fill one block in
 // order (the prefill case) every write of a work-group is contiguous.
+#include "pa_copy.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -35,13 +36,18 @@ __device__ __forceinline__ uint8_t encode<BF16, FP8>(uint16_t x, float inv_scale
   return f32_to_e4m3_sat(bf16_to_f32(x) * inv_scale);
 }
 
-// grid: (ceil(n / 16), H_kv); block: 256 threads.
-template <typename NewT, typename CacheT, int D>
-__global__ __launch_bounds__(256) void cache_write_kernel(
-    const typename NewT::raw* __restrict__ k_new, const typename NewT::raw* __restrict__ v_new,
-    const int32_t* __restrict__ slots, int32_t n, typename CacheT::raw* __restrict__ k_cache,
-    typename CacheT::raw* __restrict__ v_cache, int32_t num_blocks, int32_t H_kv, float k_inv,
-    float v_inv) {
+// One work-group's share: 16 consecutive input tokens (from t0 = 16 bx) of
+// KV head h.  HOST_SLOTS: the slot mapping lies in pinned host memory and is
+// read with system-scope loads (the fused staging kernel); otherwise it is
+// device memory.
+template <typename NewT, typename CacheT, int D, bool HOST_SLOTS>
+__device__ __forceinline__ void cw_tile(int bx, int h, const typename NewT::raw* __restrict__ k_new,
+                                        const typename NewT::raw* __restrict__ v_new,
+                                        const int32_t* __restrict__ slots, int32_t n,
+                                        typename CacheT::raw* __restrict__ k_cache,
+                                        typename CacheT::raw* __restrict__ v_cache,
+                                        int32_t num_blocks, int32_t H_kv, float k_inv,
+                                        float v_inv) {
   using NR = typename NewT::raw;
   using CR = typename CacheT::raw;
   constexpr int X = 16 / sizeof(CR);  // cache elements per 16-byte chunk
@@ -49,11 +55,16 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   __shared__ NR v_s[16][D + 2];
   __shared__ int32_t slot_s[16];
   const int tid = threadIdx.x;
-  const int h = blockIdx.y;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t t0 = static_cast<int64_t>(bx) * 16;
   if (tid < 16) {
     const int64_t t = t0 + tid;
-    int32_t sl = t < n ? slots[t] : -1;
+    int32_t sl = -1;
+    if (t < n) {
+      if constexpr (HOST_SLOTS)
+        sl = __hip_atomic_load(slots + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      else
+        sl = slots[t];
+    }
     if (sl >= num_blocks * kBlock) sl = -1;
     slot_s[tid] = sl;
   }
@@ -87,6 +98,39 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   }
 }
 
+// grid: (ceil(n / 16), H_kv); block: 256 threads.
+template <typename NewT, typename CacheT, int D>
+__global__ __launch_bounds__(256) void cache_write_kernel(
+    const typename NewT::raw* __restrict__ k_new, const typename NewT::raw* __restrict__ v_new,
+    const int32_t* __restrict__ slots, int32_t n, typename CacheT::raw* __restrict__ k_cache,
+    typename CacheT::raw* __restrict__ v_cache, int32_t num_blocks, int32_t H_kv, float k_inv,
+    float v_inv) {
+  cw_tile<NewT, CacheT, D, false>(blockIdx.x, blockIdx.y, k_new, v_new, slots, n, k_cache,
+                                  v_cache, num_blocks, H_kv, k_inv, v_inv);
+}
+
+// grid: stage groups + ceil(n / 16) * H_kv; block: 256 threads.  The first
+// `sgroups` work-groups copy the metadata buffer (as pa_stage), the others
+// scatter the new tokens with the slot mapping read from the same pinned
+// buffer, so both run in one launch.
+template <typename NewT, typename CacheT, int D, typename W>
+__global__ __launch_bounds__(256) void stage_cache_write_kernel(
+    W* __restrict__ dst, const W* __restrict__ src, int64_t n_words, int32_t sgroups,
+    const typename NewT::raw* __restrict__ k_new, const typename NewT::raw* __restrict__ v_new,
+    const int32_t* __restrict__ slots_host, int32_t n, typename CacheT::raw* __restrict__ k_cache,
+    typename CacheT::raw* __restrict__ v_cache, int32_t num_blocks, int32_t H_kv, float k_inv,
+    float v_inv) {
+  const int b = blockIdx.x;
+  if (b < sgroups) {
+    stage_words<W>(dst, src, n_words, b, sgroups);
+    return;
+  }
+  const int ntb = (n + 15) / 16;
+  const int r = b - sgroups;
+  cw_tile<NewT, CacheT, D, true>(r % ntb, r / ntb, k_new, v_new, slots_host, n, k_cache, v_cache,
+                                 num_blocks, H_kv, k_inv, v_inv);
+}
+
 template <typename NewT, typename CacheT, int D>
 static pa_status launch_cw(hipStream_t st, const void* k_new, const void* v_new,
                            const int32_t* slots, int32_t n, void* k_cache, void* v_cache,
@@ -115,6 +159,96 @@ static pa_status launch_cache_write(hipStream_t st, const void* k_new, const voi
                                      H_kv, k_inv, v_inv);
 }
 
+// Argument checks shared by pa_cache_write and pa_stage_cache_write (all but
+// the slot mapping); on success `combo` names the (new, cache) types: 0 f32
+// into f32, 1 bf16 into bf16, 2 bf16 into fp8, with the reciprocal scales.
+struct CwPlan {
+  int combo = 0;
+  float k_inv = 1.f, v_inv = 1.f;
+};
+
+static pa_status cw_check(const char* who, const void* k_new, const void* v_new, pa_dtype new_dt,
+                          int32_t n, void* k_cache, void* v_cache, pa_dtype cache_dt,
+                          int32_t num_blocks, int32_t H_kv, int32_t D, int32_t bs, float k_scale,
+                          float v_scale, CwPlan* plan) {
+  if (bs != kBlock) return fail(PA_ERR_INVALID, "%s: block size %d != 16", who, bs);
+  if (n < 0 || H_kv <= 0 || num_blocks < 0)
+    return fail(PA_ERR_INVALID, "%s: n=%d H_kv=%d num_blocks=%d", who, n, H_kv, num_blocks);
+  if (D != 64 && D != 128) return fail(PA_ERR_INVALID, "%s: D=%d not in {64,128}", who, D);
+  if (static_cast<int64_t>(num_blocks) * kBlock > INT32_MAX)
+    return fail(PA_ERR_INVALID, "%s: num_blocks=%d overflows int32 slots", who, num_blocks);
+  if (H_kv > 65535) return fail(PA_ERR_INVALID, "%s: H_kv=%d too large", who, H_kv);
+  if (n > 0 && (!k_new || !v_new || !k_cache || !v_cache))
+    return fail(PA_ERR_INVALID, "%s: NULL buffer", who);
+  if (new_dt == PA_F32 && cache_dt == PA_F32) {
+    plan->combo = 0;
+  } else if (new_dt == PA_BF16 && cache_dt == PA_BF16) {
+    plan->combo = 1;
+  } else if (new_dt == PA_BF16 && cache_dt == PA_FP8_E4M3) {
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !__builtin_isfinite(k_scale) ||
+        !__builtin_isfinite(v_scale))
+      return fail(PA_ERR_INVALID, "%s: fp8 scales must be finite and > 0", who);
+    plan->combo = 2;
+    // one fp32 reciprocal each, computed here once
+    plan->k_inv = 1.0f / k_scale;
+    plan->v_inv = 1.0f / v_scale;
+  } else {
+    return fail(PA_ERR_INVALID, "%s: unsupported dtypes new=%d cache=%d", who, new_dt, cache_dt);
+  }
+  return PA_OK;
+}
+
+template <typename NewT, typename CacheT, int D, typename W>
+static pa_status launch_scw(hipStream_t st, void* dst, const void* src_dev, size_t bytes,
+                            const int32_t* slots_dev, const void* k_new, const void* v_new,
+                            int32_t n, void* k_cache, void* v_cache, int32_t num_blocks,
+                            int32_t H_kv, float k_inv, float v_inv) {
+  const int64_t n_words = static_cast<int64_t>(bytes / sizeof(W));
+  const int sgroups = stage_groups(n_words);
+  const int64_t grid = sgroups + static_cast<int64_t>((n + 15) / 16) * H_kv;
+  if (grid > INT32_MAX)
+    return fail(PA_ERR_INVALID, "pa_stage_cache_write: grid too large (%lld)",
+                static_cast<long long>(grid));
+  hipError_t e = launch(kStageCacheWrite, stage_cache_write_kernel<NewT, CacheT, D, W>,
+                        dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, static_cast<W*>(dst),
+                        static_cast<const W*>(src_dev), n_words, sgroups,
+                        static_cast<const typename NewT::raw*>(k_new),
+                        static_cast<const typename NewT::raw*>(v_new), slots_dev, n,
+                        static_cast<typename CacheT::raw*>(k_cache),
+                        static_cast<typename CacheT::raw*>(v_cache), num_blocks, H_kv, k_inv,
+                        v_inv);
+  if (e != hipSuccess)
+    return fail(PA_ERR_DEVICE, "pa_stage_cache_write: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+template <typename NewT, typename CacheT, typename W>
+static pa_status launch_scw_d(int32_t D, hipStream_t st, void* dst, const void* src_dev,
+                              size_t bytes, const int32_t* slots_dev, const void* k_new,
+                              const void* v_new, int32_t n, void* k_cache, void* v_cache,
+                              int32_t num_blocks, int32_t H_kv, float k_inv, float v_inv) {
+  if (D == 128)
+    return launch_scw<NewT, CacheT, 128, W>(st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
+                                            k_cache, v_cache, num_blocks, H_kv, k_inv, v_inv);
+  return launch_scw<NewT, CacheT, 64, W>(st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
+                                         k_cache, v_cache, num_blocks, H_kv, k_inv, v_inv);
+}
+
+template <typename W>
+static pa_status launch_scw_types(const CwPlan& plan, int32_t D, hipStream_t st, void* dst,
+                                  const void* src_dev, size_t bytes, const int32_t* slots_dev,
+                                  const void* k_new, const void* v_new, int32_t n, void* k_cache,
+                                  void* v_cache, int32_t num_blocks, int32_t H_kv) {
+  if (plan.combo == 0)
+    return launch_scw_d<F32, F32, W>(D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
+                                     k_cache, v_cache, num_blocks, H_kv, 1.f, 1.f);
+  if (plan.combo == 1)
+    return launch_scw_d<BF16, BF16, W>(D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
+                                       k_cache, v_cache, num_blocks, H_kv, 1.f, 1.f);
+  return launch_scw_d<BF16, FP8, W>(D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
+                                    k_cache, v_cache, num_blocks, H_kv, plan.k_inv, plan.v_inv);
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -124,34 +258,60 @@ extern "C" pa_status pa_cache_write(void* stream, const void* k_new, const void*
                                     void* k_cache, void* v_cache, pa_dtype cache_dt,
                                     int32_t num_blocks, int32_t H_kv, int32_t D, int32_t bs,
                                     float k_scale, float v_scale) {
-  if (bs != kBlock) return fail(PA_ERR_INVALID, "pa_cache_write: block size %d != 16", bs);
-  if (n < 0 || H_kv <= 0 || num_blocks < 0)
-    return fail(PA_ERR_INVALID, "pa_cache_write: n=%d H_kv=%d num_blocks=%d", n, H_kv,
-                num_blocks);
-  if (D != 64 && D != 128) return fail(PA_ERR_INVALID, "pa_cache_write: D=%d not in {64,128}", D);
-  if (static_cast<int64_t>(num_blocks) * kBlock > INT32_MAX)
-    return fail(PA_ERR_INVALID, "pa_cache_write: num_blocks=%d overflows int32 slots", num_blocks);
-  if (H_kv > 65535) return fail(PA_ERR_INVALID, "pa_cache_write: H_kv=%d too large", H_kv);
+  CwPlan plan;
+  const pa_status chk = cw_check("pa_cache_write", k_new, v_new, new_dt, n, k_cache, v_cache,
+                                 cache_dt, num_blocks, H_kv, D, bs, k_scale, v_scale, &plan);
+  if (chk != PA_OK) return chk;
   if (n == 0) return PA_OK;
-  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
-    return fail(PA_ERR_INVALID, "pa_cache_write: NULL buffer");
+  if (!slot_mapping) return fail(PA_ERR_INVALID, "pa_cache_write: NULL buffer");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (new_dt == PA_F32 && cache_dt == PA_F32)
+  if (plan.combo == 0)
     return launch_cache_write<F32, F32>(st, k_new, v_new, slot_mapping, n, k_cache, v_cache,
                                         num_blocks, H_kv, D, 1.f, 1.f);
-  if (new_dt == PA_BF16 && cache_dt == PA_BF16)
+  if (plan.combo == 1)
     return launch_cache_write<BF16, BF16>(st, k_new, v_new, slot_mapping, n, k_cache, v_cache,
                                           num_blocks, H_kv, D, 1.f, 1.f);
-  if (new_dt == PA_BF16 && cache_dt == PA_FP8_E4M3) {
-    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !__builtin_isfinite(k_scale) ||
-        !__builtin_isfinite(v_scale))
-      return fail(PA_ERR_INVALID, "pa_cache_write: fp8 scales must be finite and > 0");
-    // one fp32 reciprocal each, computed here once
-    const float k_inv = 1.0f / k_scale;
-    const float v_inv = 1.0f / v_scale;
-    return launch_cache_write<BF16, FP8>(st, k_new, v_new, slot_mapping, n, k_cache, v_cache,
-                                         num_blocks, H_kv, D, k_inv, v_inv);
+  return launch_cache_write<BF16, FP8>(st, k_new, v_new, slot_mapping, n, k_cache, v_cache,
+                                       num_blocks, H_kv, D, plan.k_inv, plan.v_inv);
+}
+
+extern "C" pa_status pa_stage_cache_write(void* stream, void* dst, const void* src_host,
+                                          size_t bytes, size_t slot_offset, const void* k_new,
+                                          const void* v_new, pa_dtype new_dt, int32_t n,
+                                          void* k_cache, void* v_cache, pa_dtype cache_dt,
+                                          int32_t num_blocks, int32_t H_kv, int32_t D, int32_t bs,
+                                          float k_scale, float v_scale) {
+  CwPlan plan;
+  const pa_status chk = cw_check("pa_stage_cache_write", k_new, v_new, new_dt, n, k_cache,
+                                 v_cache, cache_dt, num_blocks, H_kv, D, bs, k_scale, v_scale,
+                                 &plan);
+  if (chk != PA_OK) return chk;
+  if (bytes % 4 != 0 || slot_offset % 4 != 0 || reinterpret_cast<uintptr_t>(dst) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(src_host) % 4 != 0)
+    return fail(PA_ERR_INVALID,
+                "pa_stage_cache_write: bytes=%zu, slot_offset=%zu and both addresses must be "
+                "multiples of 4",
+                bytes, slot_offset);
+  if (n > 0 && (slot_offset > bytes || (bytes - slot_offset) / 4 < static_cast<size_t>(n)))
+    return fail(PA_ERR_INVALID,
+                "pa_stage_cache_write: %d slots at byte %zu do not fit the %zu-byte buffer", n,
+                slot_offset, bytes);
+  if (bytes == 0) return PA_OK;  // and n == 0
+  if (!dst || !src_host) return fail(PA_ERR_INVALID, "pa_stage_cache_write: NULL buffer");
+  void* src_dev = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&src_dev, const_cast<void*>(src_host), 0);
+  if (e != hipSuccess || !src_dev) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID, "pa_stage_cache_write: source is not pinned host memory (%s)",
+                hipGetErrorString(e));
   }
-  return fail(PA_ERR_INVALID, "pa_cache_write: unsupported dtypes new=%d cache=%d", new_dt,
-              cache_dt);
+  const int32_t* slots_dev =
+      reinterpret_cast<const int32_t*>(static_cast<const char*>(src_dev) + slot_offset);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (bytes % 8 == 0 && reinterpret_cast<uintptr_t>(dst) % 8 == 0 &&
+      reinterpret_cast<uintptr_t>(src_dev) % 8 == 0)
+    return launch_scw_types<uint64_t>(plan, D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
+                                      k_cache, v_cache, num_blocks, H_kv);
+  return launch_scw_types<uint32_t>(plan, D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
+                                    k_cache, v_cache, num_blocks, H_kv);
 }

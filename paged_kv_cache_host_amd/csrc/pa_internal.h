@@ -20,6 +20,7 @@ enum KernelId {
   kPrefillMerge,
   kGeneric,
   kStage,
+  kStageCacheWrite,
   kKernelCount
 };
 

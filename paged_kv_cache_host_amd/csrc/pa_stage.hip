@@ -13,44 +13,25 @@
 // The source is read with system-scope loads, which stay coherent with host
 // writes made before the launch whether or not the pinned allocation is
 // fine-grained.
+#include "pa_copy.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
-#include <algorithm>
-
 namespace pa {
 
-constexpr int kStageThreads = 256;
-constexpr int kStageUnroll = 4;
-
-// grid: min(ceil(n / (256 * 4)), 256); block: 256.  n: words of type W
-// (8 bytes when both addresses and the size allow it, else 4).
+// grid: stage_groups(n); block: 256.  n: words of type W (8 bytes when both
+// addresses and the size allow it, else 4).
 template <typename W>
 __global__ __launch_bounds__(kStageThreads) void stage_kernel(W* __restrict__ dst,
                                                               const W* __restrict__ src,
                                                               int64_t n) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kStageThreads;
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kStageThreads + threadIdx.x; base < n;
-       base += stride * kStageUnroll) {
-    W v[kStageUnroll];
-#pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-      const int64_t i = base + u * stride;
-      v[u] = i < n ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : W{0};
-    }
-#pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-      const int64_t i = base + u * stride;
-      if (i < n) dst[i] = v[u];
-    }
-  }
+  stage_words<W>(dst, src, n, blockIdx.x, gridDim.x);
 }
 
 template <typename W>
 pa_status launch_stage(hipStream_t st, void* dst, const void* src_dev, size_t bytes) {
   const int64_t n = static_cast<int64_t>(bytes / sizeof(W));
-  const int64_t per_group = int64_t{kStageThreads} * kStageUnroll;
-  const int grid = static_cast<int>(std::min<int64_t>((n + per_group - 1) / per_group, 256));
+  const int grid = stage_groups(n);
   const hipError_t e = launch(kStage, stage_kernel<W>, dim3(grid), dim3(kStageThreads), 0, st,
                               static_cast<W*>(dst), static_cast<const W*>(src_dev), n);
   if (e != hipSuccess)

@@ -41,8 +41,9 @@ std::atomic<int32_t> g_mask{0};  // bit k: time kernel k
 int32_t g_every = 1;             // time launches 0, every, 2 * every, ... of a kernel
 Track g_tracks[kKernelCount];
 
-const char* kNames[kKernelCount] = {"cache_write", "decode",        "decode_merge", "prefill",
-                                    "prefill_merge", "generic",     "stage"};
+const char* kNames[kKernelCount] = {"cache_write",   "decode",  "decode_merge",
+                                    "prefill",       "prefill_merge", "generic",
+                                    "stage",         "stage_cache_write"};
 
 }  // namespace
 

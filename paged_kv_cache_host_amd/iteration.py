@@ -8,7 +8,8 @@ cache (pa_cache_write) and attention runs for the decode tokens (pa_decode)
 and the prefill slices (pa_prefill_chunk), all on one compute stream.  The
 host work of iteration t+1 (scheduling and table packing into
 double-buffered pinned memory) overlaps the kernels of iteration t; one
-pa_stage kernel on the compute stream then moves the packed metadata.
+pa_stage_cache_write launch on the compute stream then moves the packed
+metadata and scatters the new tokens' K/V.
 
 Token data (new K, V, Q rows) comes from a caller-supplied provider:
 ``provider(seqs, positions) -> (k [n, H_kv, D], v [n, H_kv, D], q [n, H_q, D])``
@@ -171,11 +172,14 @@ class LayerIterations:
             c.wait_stream(torch.cuda.current_stream(self.dev))
             for t in (k_new, v_new, q_new):
                 t.record_stream(c)
-        pa.check(pa.pa_stage(c, dvb, self.host_buf[X], 4 * off))
         if n_tok:
-            pa.check(pa.pa_cache_write(c, k_new, v_new, d_sl, self.k, self.v,
-                                       self.cache_blocks, self.h_kv, self.d, BLOCK, self.k_scale,
-                                       self.v_scale))
+            # the new tokens' slots lead the buffer: one launch stages it and
+            # scatters their K/V
+            pa.check(pa.pa_stage_cache_write(c, dvb, self.host_buf[X], 4 * off, 0, n_tok, k_new,
+                                             v_new, self.k, self.v, self.cache_blocks, self.h_kv,
+                                             self.d, BLOCK, self.k_scale, self.v_scale))
+        else:
+            pa.check(pa.pa_stage(c, dvb, self.host_buf[X], 4 * off))
         if n_pf:
             pa.check(pa.pa_prefill_chunk(c, self.out_pf[X][:n_pt], q_new[:n_pt], d_pm[:n_pf + 1],
                                          d_pm[n_pf + 1:], self.k, self.v, d_pt.view(n_pf, mbp),

@@ -79,3 +79,69 @@ def test_stage_rejects_bad_sources():
     assert (dev.cpu() == 0).all()
     with pytest.raises(pa.PaError):
         pa.pa_stage(None, dev, torch.arange(64, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("new_dt,cache_dt,d", [("bf16", "bf16", 128), ("bf16", "fp8", 128),
+                                               ("bf16", "bf16", 64), ("f32", "f32", 64)])
+def test_stage_cache_write_equals_stage_then_cache_write(new_dt, cache_dt, d):
+    """The fused launch leaves the same device copy and the same cache bytes
+    as pa_stage followed by pa_cache_write: several sizes (whole and partial
+    work-groups of tokens, 4- and 8-byte words), slots that are skipped (-1)
+    or lie outside the pool, on the same buffers twice in a row."""
+    from paged_kv_cache_host_amd.engine import _TORCH_STORAGE
+    rng = np.random.default_rng(902)
+    h_kv, nb = 4, 40
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[new_dt]
+    cdt = _TORCH_STORAGE[cache_dt]
+    x = 16 // torch.empty((), dtype=cdt).element_size()
+    caches = []
+    for _ in range(2):
+        k = torch.zeros((nb, h_kv, d // x, 16, x), dtype=cdt, device=DEV)
+        v = torch.zeros((nb, h_kv, d, 16), dtype=cdt, device=DEV)
+        caches.append((k, v))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(903)
+    for n, pad_words in [(0, 10), (1, 3), (17, 0), (200, 501), (33, 2)]:
+        say(f"[stage_cache_write] {new_dt}->{cache_dt} d{d} n={n} pad={pad_words}")
+        words = pad_words + n + 5
+        slot_off = 4 * pad_words
+        host = torch.empty(words, dtype=torch.int32, pin_memory=True)
+        h = host.numpy()
+        h[:] = rng.integers(-2**31, 2**31 - 1, size=words, dtype=np.int64).astype(np.int32)
+        sl = rng.permutation(nb * 16)[:n].astype(np.int32)
+        if n >= 3:
+            sl[1] = -1
+            sl[2] = nb * 16 + 7        # outside the pool: skipped
+        h[pad_words:pad_words + n] = sl
+        kn = torch.randn((max(n, 1), h_kv, d), generator=g, device=DEV).to(tdt)
+        vn = torch.randn((max(n, 1), h_kv, d), generator=g, device=DEV).to(tdt)
+        outs = []
+        for i, (kc, vc) in enumerate(caches):
+            dst = torch.full((words + 3,), -9, dtype=torch.int32, device=DEV)
+            if i == 0:
+                assert pa.pa_stage(None, dst, host, 4 * words) == 0
+                if n:
+                    assert pa.pa_cache_write(None, kn, vn, dst[pad_words:pad_words + n], kc, vc,
+                                             nb, h_kv, d, 16, 0.03, 0.05) == 0
+            else:
+                assert pa.pa_stage_cache_write(None, dst, host, 4 * words, slot_off, n, kn, vn,
+                                               kc, vc, nb, h_kv, d, 16, 0.03, 0.05) == 0
+            torch.cuda.synchronize()
+            outs.append(dst.cpu())
+        assert torch.equal(outs[0], outs[1])
+        for a, b in zip(caches[0], caches[1]):
+            assert torch.equal(a.view(torch.uint8).cpu(), b.view(torch.uint8).cpu())
+
+
+def test_stage_cache_write_rejects_bad_arguments():
+    fake = 0x1000
+    host = torch.arange(64, dtype=torch.int32).pin_memory()
+    lib = pa._lib
+    # slots past the end of the buffer, misaligned offset, non-pinned source
+    assert lib.pa_stage_cache_write(None, fake, host.data_ptr(), 64, 40, fake, fake, 1, 8, fake,
+                                    fake, 1, 10, 2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
+    assert lib.pa_stage_cache_write(None, fake, host.data_ptr(), 64, 2, fake, fake, 1, 1, fake,
+                                    fake, 1, 10, 2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
+    pageable = np.zeros(64, dtype=np.int32)
+    assert lib.pa_stage_cache_write(None, fake, pageable.ctypes.data, 64, 0, fake, fake, 1, 1,
+                                    fake, fake, 1, 10, 2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID

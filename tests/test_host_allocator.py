@@ -200,3 +200,22 @@ def test_stage_and_timing_argument_checks_on_host():
     assert pa._pa._lib.pa_timing_enable(2, 0) == pa.PA_ERR_INVALID
     assert "every" in pa.pa_last_error()
     assert pa._pa._lib.pa_timing_enable(0, 1) == 0
+
+
+def test_stage_cache_write_argument_checks_on_host():
+    fake = 0x1000
+    lib = pa._pa._lib
+    # block size, dtypes, fp8 scale, slot range and alignment: rejected before any HIP call
+    assert lib.pa_stage_cache_write(None, fake, fake, 64, 0, fake, fake, 1, 4, fake, fake, 1, 10,
+                                    2, 64, 8, 1.0, 1.0) == pa.PA_ERR_INVALID
+    assert lib.pa_stage_cache_write(None, fake, fake, 64, 0, fake, fake, 1, 4, fake, fake, 0, 10,
+                                    2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
+    assert lib.pa_stage_cache_write(None, fake, fake, 64, 0, fake, fake, 1, 4, fake, fake, 2, 10,
+                                    2, 64, 16, 0.0, 1.0) == pa.PA_ERR_INVALID
+    assert lib.pa_stage_cache_write(None, fake, fake, 64, 52, fake, fake, 1, 4, fake, fake, 1, 10,
+                                    2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
+    assert "do not fit" in pa.pa_last_error()
+    assert lib.pa_stage_cache_write(None, fake, fake, 64, 6, fake, fake, 1, 4, fake, fake, 1, 10,
+                                    2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
+    assert lib.pa_stage_cache_write(None, fake, fake, 0, 0, fake, fake, 1, 0, fake, fake, 1, 10,
+                                    2, 64, 16, 1.0, 1.0) == 0          # nothing to do
