@@ -147,6 +147,17 @@ def cpu_baseline(n_seqs: int):
             break
     dt = (time.perf_counter() - t0) / reps
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    # the same on one thread (a shorter sample)
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        reps1 = 0
+        while True:
+            oat.decode(q, kc, vc, tables, lens, H_KV, sm, "bf16")
+            reps1 += 1
+            if time.perf_counter() - t1 > 5.0:
+                break
+        dt1 = (time.perf_counter() - t1) / reps1
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -156,7 +167,7 @@ def cpu_baseline(n_seqs: int):
     except OSError:
         pass
     return {"value": decode_bytes(lens) / dt / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "value_1_thread": decode_bytes(lens) / dt1 / 1e9,
             "sample": f"first {len(L)} of the 128 sequences ({int(L.sum())} context tokens), "
                       f"one decode launch's gather + fp64 attention, mean of {reps} runs; "
                       f"host {model or 'unknown'}, {len(os.sched_getaffinity(0))} cores visible"}
