@@ -25,6 +25,16 @@ Readings taken where the texts are silent or contradict themselves:
 * a sequence is created with ``ceil(num_tokens / block_size)`` blocks (the
   ARTICLE's scheduler, §3.1, allocates that many for a prompt at admission);
 * release returns the table to the back of the free list in table order.
+
+Prefix sharing (ARTICLE §4.3: requests with the same system-prompt prefix
+reuse one set of KV blocks, marked read-only).  Readings taken:
+* only FULL blocks are shared: a sequence created from a prefix of another
+  takes that sequence's first ``shared_tokens // block_size`` blocks, and the
+  rest of its tokens (including the part of the prefix that fills a partial
+  block) go to fresh blocks, so no sequence ever writes into a shared block;
+* a block is counted once for every table that holds it and returns to the
+  back of the free list when the last table holding it is released (in that
+  table's order).
 """
 from __future__ import annotations
 
@@ -56,15 +66,22 @@ class BlockPool:
         self.free = deque(order)
         self.tables: dict[int, list[int]] = {}
         self.lengths: dict[int, int] = {}
+        self.refs = [0] * self.num_blocks   # tables holding each block
 
     # -- ARTICLE §2.2: allocate / free ---------------------------------------
     def _take(self, n: int):
         if len(self.free) < n:
             return None
-        return [self.free.popleft() for _ in range(n)]
+        ids = [self.free.popleft() for _ in range(n)]
+        for b in ids:
+            self.refs[b] = 1
+        return ids
 
     def _give_back(self, ids):
-        self.free.extend(ids)
+        for b in ids:
+            self.refs[b] -= 1
+            if self.refs[b] == 0:
+                self.free.append(b)
 
     # -- sequence-level verbs -------------------------------------------------
     def num_free(self) -> int:
@@ -81,6 +98,31 @@ class BlockPool:
         self.tables[seq] = ids
         self.lengths[seq] = num_tokens
         return OK
+
+    def seq_share(self, seq: int, src: int, shared_tokens: int, num_tokens: int):
+        """Create ``seq`` with ``num_tokens`` tokens whose first
+        ``shared_tokens`` are those of ``src`` (ARTICLE §4.3): the full blocks
+        among them are shared, the rest is fresh.  Returns (status, number of
+        leading tokens that live in shared blocks)."""
+        if seq in self.tables:
+            return ERR_EXISTS, 0
+        if src not in self.tables:
+            return ERR_UNKNOWN_SEQ, 0
+        if not (0 <= shared_tokens <= self.lengths[src]) or num_tokens < shared_tokens:
+            return ERR_INVALID, 0
+        n_shared = shared_tokens // self.block_size
+        fresh = self._take(ceil_div(num_tokens, self.block_size) - n_shared)
+        if fresh is None:
+            return ERR_NO_BLOCKS, 0
+        head = self.tables[src][:n_shared]
+        for b in head:
+            self.refs[b] += 1
+        self.tables[seq] = head + fresh
+        self.lengths[seq] = num_tokens
+        return OK, n_shared * self.block_size
+
+    def block_refs(self, block: int) -> int:
+        return self.refs[block]
 
     def seq_append(self, seq: int, n_new: int):
         """Grow a sequence by ``n_new`` tokens, taking one block per block

@@ -121,6 +121,81 @@ def test_allocator_hand_worked_trace():
             assert pool.block_table(step["seq"]) == step["table"], step
 
 
+def run_sharing_step(pool, step):
+    """Apply one step of the prefix-sharing fixture; returns its status."""
+    if step["op"] == "create":
+        return pool.seq_create(step["seq"], step["n"])
+    if step["op"] == "append":
+        st_, slots = pool.seq_append(step["seq"], step["n"])
+        if "slots" in step:
+            assert slots == step["slots"], step
+        return st_
+    if step["op"] == "share":
+        st_, shared = pool.seq_share(step["seq"], step["src"], step["shared"], step["n"])
+        if "shared_out" in step:
+            assert shared == step["shared_out"], step
+        return st_
+    return pool.seq_release(step["seq"])
+
+
+def test_prefix_sharing_hand_worked_trace():
+    g = json.load(open(os.path.join(GOLDEN, "prefix_sharing_trace.json")))
+    pool = oa.BlockPool(g["num_blocks"], g["block_size"], g["initial_free_order"])
+    for step in g["steps"]:
+        assert run_sharing_step(pool, step) == step["status"], step
+        assert pool.free_list() == step["free"], step
+        if "table" in step:
+            assert pool.block_table(step["seq"]) == step["table"], step
+        if "refs" in step:
+            assert [pool.block_refs(b) for b in range(g["num_blocks"])] == step["refs"], step
+
+
+share_ops = st.lists(st.tuples(st.sampled_from(["create", "append", "release", "share"]),
+                               st.integers(0, 5), st.integers(0, 5), st.integers(0, 70),
+                               st.integers(0, 70)), max_size=60)
+
+
+@settings(max_examples=200, deadline=None)
+@given(share_ops, st.integers(0, 40))
+def test_prefix_sharing_invariants(oplist, nblocks):
+    """Every block is counted once per table holding it; the free blocks are
+    exactly those no table holds, each once; shared blocks are full, so no
+    position a sequence may still write lies in a block another table holds;
+    failed calls change nothing."""
+    pool = oa.BlockPool(nblocks, 16)
+    for op, seq, src, n, shared in oplist:
+        before = (pool.free_list(), {k: list(v) for k, v in pool.tables.items()},
+                  dict(pool.lengths), list(pool.refs))
+        if op == "create":
+            st_ = pool.seq_create(seq, n)
+        elif op == "append":
+            st_, _ = pool.seq_append(seq, n)
+        elif op == "share":
+            st_, got = pool.seq_share(seq, src, shared, max(n, shared))
+            if st_ == oa.OK:
+                assert got == (shared // 16) * 16
+                assert pool.tables[seq][:shared // 16] == before[1][src][:shared // 16]
+        else:
+            st_ = pool.seq_release(seq)
+        if st_ != oa.OK:
+            assert (pool.free_list(), {k: list(v) for k, v in pool.tables.items()},
+                    dict(pool.lengths), list(pool.refs)) == before
+        counts = [0] * nblocks
+        for t in pool.tables.values():
+            assert len(t) == len(set(t))
+            for b in t:
+                counts[b] += 1
+        assert counts == pool.refs
+        assert sorted(pool.free_list()) == [b for b in range(nblocks) if counts[b] == 0]
+        for s, t in pool.tables.items():
+            assert len(t) == -(-pool.lengths[s] // 16)
+            # a sequence writes only at positions >= its length; the block
+            # holding its next position, if it has one, is its own
+            nxt = pool.lengths[s] // 16
+            if nxt < len(t):
+                assert pool.refs[t[nxt]] == 1
+
+
 ops = st.lists(st.tuples(st.sampled_from(["create", "append", "release"]),
                          st.integers(0, 5), st.integers(0, 70)), max_size=60)
 
