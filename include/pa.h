@@ -139,9 +139,30 @@ pa_status pa_batch_append(pa_pool* pool, const int64_t* seqs, int32_t n_seqs, in
 pa_status pa_seq_slots(const pa_pool* pool, int64_t seq, int32_t start, int32_t n,
                        int32_t* slots_out);
 
-/* Release `seq`: its blocks go to the back of the free list in table order
+/* Release `seq`: it drops its hold on each of its blocks, in table order;
+ * a block no other sequence holds goes to the back of the free list
  * (ARTICLE 2.2 free; LESSON release_blocks on finish). */
 pa_status pa_seq_release(pa_pool* pool, int64_t seq);
+
+/* Prefix sharing (ARTICLE 4.3: requests that start with the same
+ * system-prompt prefix reuse one set of KV blocks, read-only).  Create `seq`
+ * with num_tokens tokens whose first shared_tokens are the first
+ * shared_tokens tokens of `src`: the shared_tokens / block_size full blocks
+ * among them are src's own blocks (held by both tables from now on), the
+ * rest of seq's blocks are taken fresh from the front of the free list.
+ * *shared_out [host, optional] = tokens that live in shared blocks
+ * ((shared_tokens / block_size) * block_size): their K/V are already in the
+ * cache and must not be written again; the caller writes positions
+ * shared_out .. num_tokens-1.  No sequence ever writes into a block another
+ * table holds (a shared block is full; appends go to later blocks).
+ * Errors (state unchanged): PA_ERR_EXISTS (seq exists), PA_ERR_UNKNOWN_SEQ
+ * (src unknown), PA_ERR_INVALID (shared_tokens outside [0, length of src] or
+ * above num_tokens), PA_ERR_NO_BLOCKS. */
+pa_status pa_seq_share(pa_pool* pool, int64_t seq, int64_t src, int32_t shared_tokens,
+                       int32_t num_tokens, int32_t* shared_out);
+
+/* Number of sequences holding `block` (0: free) into *refs [host]. */
+pa_status pa_pool_block_refs(const pa_pool* pool, int32_t block, int32_t* refs);
 
 /* Current token count of `seq` into *len. */
 pa_status pa_seq_length(const pa_pool* pool, int64_t seq, int32_t* len);

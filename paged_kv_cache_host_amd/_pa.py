@@ -72,6 +72,8 @@ _SIGS = {
     "pa_batch_append": (_i32, [_vp, _i64p, _i32, _i32, _i32p, _i32p]),
     "pa_seq_slots": (_i32, [_vp, _i64, _i32, _i32, _i32p]),
     "pa_seq_release": (_i32, [_vp, _i64]),
+    "pa_seq_share": (_i32, [_vp, _i64, _i64, _i32, _i32, _i32p]),
+    "pa_pool_block_refs": (_i32, [_vp, _i32, _i32p]),
     "pa_seq_length": (_i32, [_vp, _i64, _i32p]),
     "pa_seq_block_table": (_i32, [_vp, _i64, _i32p, _i32, _i32p]),
     "pa_pack_batch": (_i32, [_vp, _i64p, _i32, _i32, _i32p, _i32p]),
@@ -198,6 +200,20 @@ def pa_seq_slots(pool, seq: int, start: int, n: int, out: np.ndarray | None = No
     assert buf.dtype == np.int32 and buf.flags.c_contiguous and buf.size >= n
     st = _lib.pa_seq_slots(pool, seq, start, n, _ptr_i32(buf))
     return st, buf
+
+
+def pa_seq_share(pool, seq: int, src: int, shared_tokens: int, num_tokens: int):
+    """Returns (status, tokens that live in shared blocks)."""
+    out = _i32(0)
+    st = _lib.pa_seq_share(pool, seq, src, shared_tokens, num_tokens, C.byref(out))
+    return st, out.value
+
+
+def pa_pool_block_refs(pool, block: int):
+    """Returns (status, number of sequences holding the block)."""
+    out = _i32(0)
+    st = _lib.pa_pool_block_refs(pool, block, C.byref(out))
+    return st, out.value
 
 
 def pa_seq_release(pool, seq: int) -> int:

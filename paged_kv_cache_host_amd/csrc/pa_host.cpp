@@ -9,8 +9,16 @@
 // table[p / bs]; one more block is added when the sequence grows past its
 // blocks; blocks return to the pool when the sequence finishes.
 //
+// ARTICLE §4.3, prefix sharing: sequences that start with the same prefix
+// reuse its blocks, read-only.  Only full blocks are shared (the sharer's
+// remaining tokens, including a prefix tail that fills a partial block, get
+// fresh blocks), so no sequence ever writes into a block another table
+// holds.  Each block counts the tables holding it and returns to the back of
+// the free list when the last of them is released.
+//
 // The free list is a ring buffer of int32 ids (capacity = pool size, so it
-// can never overflow: a block is either in the ring or in exactly one table).
+// can never overflow: a block is either in the ring or held by one or more
+// tables).
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -39,19 +47,25 @@ struct pa_pool {
   std::vector<int32_t> ring;  // free ids, FIFO
   int32_t head = 0;           // index of the front of the free list
   int32_t count = 0;          // number of free ids
+  std::vector<int32_t> refs;  // tables holding each block (0: free)
   std::unordered_map<int64_t, Seq> seqs;
 
   int32_t at(int32_t i) const { return ring[(head + i) % num_blocks]; }
   // Take n ids from the front.  Caller has checked count >= n.
   void take(int32_t n, std::vector<int32_t>& dst) {
     for (int32_t i = 0; i < n; ++i) {
-      dst.push_back(ring[head]);
+      const int32_t b = ring[head];
+      dst.push_back(b);
+      refs[b] = 1;
       head = head + 1 == num_blocks ? 0 : head + 1;
     }
     count -= n;
   }
+  // Drop one reference to each id, in order; ids nobody holds any more go to
+  // the back of the free list.
   void give_back(const std::vector<int32_t>& ids) {
     for (int32_t b : ids) {
+      if (--refs[b] > 0) continue;
       ring[(head + count) % num_blocks] = b;
       ++count;
     }
@@ -93,6 +107,7 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* 
   if (!p) return fail(PA_ERR_INVALID, "pa_pool_create: out of host memory");
   try {
     p->ring.resize(static_cast<size_t>(num_blocks));
+    p->refs.assign(static_cast<size_t>(num_blocks), 0);
   } catch (...) {
     delete p;
     return fail(PA_ERR_INVALID, "pa_pool_create: out of host memory for %d blocks", num_blocks);
@@ -152,6 +167,46 @@ pa_status pa_seq_create(pa_pool* pool, int64_t seq, int32_t num_tokens) {
   pool->take(static_cast<int32_t>(need), s.table);
   s.len = num_tokens;
   pool->seqs.emplace(seq, std::move(s));
+  return PA_OK;
+}
+
+pa_status pa_seq_share(pa_pool* pool, int64_t seq, int64_t src, int32_t shared_tokens,
+                       int32_t num_tokens, int32_t* shared_out) {
+  if (!pool) return fail(PA_ERR_INVALID, "pa_seq_share: pool is NULL");
+  if (pool->seqs.count(seq))
+    return fail(PA_ERR_EXISTS, "pa_seq_share: sequence %lld exists", (long long)seq);
+  auto it = pool->seqs.find(src);
+  if (it == pool->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_share: unknown source sequence %lld", (long long)src);
+  const Seq& from = it->second;
+  if (shared_tokens < 0 || shared_tokens > from.len || num_tokens < shared_tokens)
+    return fail(PA_ERR_INVALID,
+                "pa_seq_share: shared_tokens=%d must lie in [0, %d] and not exceed num_tokens=%d",
+                shared_tokens, from.len, num_tokens);
+  const int32_t n_shared = shared_tokens / pool->block_size;
+  const int64_t need = ceil_div64(num_tokens, pool->block_size) - n_shared;
+  if (need > pool->count)
+    return fail(PA_ERR_NO_BLOCKS, "pa_seq_share: need %lld blocks, %d free", (long long)need,
+                pool->count);
+  Seq s;
+  s.table.reserve(static_cast<size_t>(n_shared + need));
+  for (int32_t i = 0; i < n_shared; ++i) {
+    const int32_t b = from.table[i];
+    s.table.push_back(b);
+    ++pool->refs[b];
+  }
+  pool->take(static_cast<int32_t>(need), s.table);
+  s.len = num_tokens;
+  pool->seqs.emplace(seq, std::move(s));
+  if (shared_out) *shared_out = n_shared * pool->block_size;
+  return PA_OK;
+}
+
+pa_status pa_pool_block_refs(const pa_pool* pool, int32_t block, int32_t* refs) {
+  if (!pool || !refs) return fail(PA_ERR_INVALID, "pa_pool_block_refs: NULL argument");
+  if (block < 0 || block >= pool->num_blocks)
+    return fail(PA_ERR_INVALID, "pa_pool_block_refs: block %d outside the pool", block);
+  *refs = pool->refs[block];
   return PA_OK;
 }
 

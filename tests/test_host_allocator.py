@@ -219,3 +219,72 @@ def test_stage_cache_write_argument_checks_on_host():
                                     2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
     assert lib.pa_stage_cache_write(None, fake, fake, 0, 0, fake, fake, 1, 0, fake, fake, 1, 10,
                                     2, 64, 16, 1.0, 1.0) == 0          # nothing to do
+
+
+def test_prefix_sharing_golden_trace_through_c_abi():
+    g = json.load(open(os.path.join(GOLDEN, "prefix_sharing_trace.json")))
+    st_, pool = pa.pa_pool_create(g["num_blocks"], g["block_size"], g["initial_free_order"])
+    assert st_ == pa.PA_OK
+    try:
+        for step in g["steps"]:
+            if step["op"] == "create":
+                s = pa.pa_seq_create(pool, step["seq"], step["n"])
+            elif step["op"] == "append":
+                s, slots = pa.pa_seq_append(pool, step["seq"], step["n"])
+                if "slots" in step:
+                    assert list(slots) == step["slots"]
+            elif step["op"] == "share":
+                s, shared = pa.pa_seq_share(pool, step["seq"], step["src"], step["shared"],
+                                            step["n"])
+                if "shared_out" in step:
+                    assert shared == step["shared_out"]
+            else:
+                s = pa.pa_seq_release(pool, step["seq"])
+            assert s == step["status"], (step, pa.pa_last_error())
+            assert _state(pool) == step["free"]
+            if "table" in step:
+                assert list(pa.pa_seq_block_table(pool, step["seq"])[1]) == step["table"]
+            if "refs" in step:
+                assert [pa.pa_pool_block_refs(pool, b)[1] for b in range(g["num_blocks"])] == \
+                    step["refs"]
+        assert pa.pa_pool_block_refs(pool, g["num_blocks"])[0] == pa.PA_ERR_INVALID
+    finally:
+        pa.pa_pool_destroy(pool)
+
+
+share_ops = st.lists(st.tuples(st.sampled_from(["create", "append", "release", "share"]),
+                               st.integers(0, 6), st.integers(0, 6), st.integers(0, 90),
+                               st.integers(0, 90)), max_size=80)
+
+
+@settings(max_examples=300, deadline=None)
+@given(share_ops, st.integers(0, 48), st.randoms(use_true_random=False))
+def test_prefix_sharing_bit_exact_against_oracle(oplist, nblocks, rnd):
+    order = list(range(nblocks))
+    rnd.shuffle(order)
+    ref = oa.BlockPool(nblocks, 16, order)
+    st_, pool = pa.pa_pool_create(nblocks, 16, order)
+    assert st_ == pa.PA_OK
+    try:
+        for op, seq, src, n, shared in oplist:
+            if op == "create":
+                assert pa.pa_seq_create(pool, seq, n) == ref.seq_create(seq, n)
+            elif op == "append":
+                s1, slots1 = pa.pa_seq_append(pool, seq, n)
+                s2, slots2 = ref.seq_append(seq, n)
+                assert s1 == s2
+                if s1 == pa.PA_OK and n > 0:
+                    assert list(slots1) == slots2
+            elif op == "share":
+                assert pa.pa_seq_share(pool, seq, src, shared, n) == \
+                    ref.seq_share(seq, src, shared, n)
+            else:
+                assert pa.pa_seq_release(pool, seq) == ref.seq_release(seq)
+            assert _state(pool) == ref.free_list()
+            for b in range(nblocks):
+                assert pa.pa_pool_block_refs(pool, b)[1] == ref.block_refs(b)
+            for s, t in ref.tables.items():
+                assert list(pa.pa_seq_block_table(pool, s)[1]) == t
+                assert pa.pa_seq_length(pool, s)[1] == ref.lengths[s]
+    finally:
+        pa.pa_pool_destroy(pool)
