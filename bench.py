@@ -29,6 +29,8 @@ Secondary legs (skipped with --decode-only):
   ``fp8_decode`` 64 sequences at context 8192 with an e4m3fn cache;
   ``fp8_prefill`` the 64 slices of the 32768-token prompt with an e4m3fn
                  cache: prefill kernel TFLOP/s;
+  ``prefix_sharing`` 128 sequences behind one shared 1024-token prompt:
+                 blocks held and decode kernel time, shared vs private;
   ``trace``      1000 continuous-batching iterations (libpa scheduler +
                  kernels) with Poisson arrivals: tokens/s per layer and KV
                  fragmentation.
@@ -624,6 +626,75 @@ def fp8_prefill_leg(args, dev):
             "algorithmic_flops": flops}
 
 
+def prefix_leg(args, dev):
+    """Prefix sharing (ARTICLE 4.3): 128 sequences that start with the same
+    1024-token system prompt, followed by their own lognormal contexts
+    (decode-70b lengths).  The same decode batch runs over two pools: one
+    where every sequence holds the prompt's 64 blocks through pa_seq_share,
+    one where each holds a private copy.  Reports the blocks held and the
+    decode kernel time of both on the same algorithmic bytes."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_host_amd import _pa as pa
+    from paged_kv_cache_host_amd.engine import PagedKV, decode_workspace, sm_scale_for
+
+    PFX = 1024
+    own, _, _ = workloads.decode_70b_layout()
+    S = len(own)
+    lens = PFX + own
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    sm = sm_scale_for(D)
+    q = torch.randn((S, H_Q, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((S, H_Q, D), dtype=torch.bfloat16, device=dev)
+    res = {}
+    for mode in ("shared", "private"):
+        nb = int(np.sum(-(-lens // BLOCK))) + PFX // BLOCK + 8
+        order = np.random.default_rng(7).permutation(nb).astype(np.int32)
+        kv = PagedKV(nb, H_KV, D, "bf16", dev, order)
+        if mode == "shared":
+            pa.check(kv.create(S, PFX))                       # the prompt's owner
+            _fill_random(kv, kv.slots(S, 0, PFX), gen, dev)
+            fill = []
+            for s in range(S):
+                st, shared = pa.pa_seq_share(kv.pool, s, S, PFX, int(lens[s]))
+                pa.check(st)
+                fill.append(kv.slots(s, shared, int(lens[s]) - shared))
+            _fill_random(kv, np.concatenate(fill), gen, dev)
+        else:
+            fill = []
+            for s in range(S):
+                pa.check(kv.create(s, int(lens[s])))
+                fill.append(kv.slots(s, 0, int(lens[s])))
+            _fill_random(kv, np.concatenate(fill), gen, dev)
+        held = nb - pa.pa_pool_num_free(kv.pool)
+        tables, lns = kv.pack(list(range(S)))
+        t_d = torch.from_numpy(tables).to(dev)
+        l_d = torch.from_numpy(lns).to(dev)
+        mc = int(lns.max())
+        ws = decode_workspace(S, H_Q, H_KV, D, mc, dev)
+        for _ in range(args.warmup):
+            kv.decode(out, q, t_d, l_d, mc, sm, ws)
+        torch.cuda.synchronize()
+        pa.check(pa.pa_timing_enable(["decode"]))
+        for _ in range(args.steps):
+            kv.decode(out, q, t_d, l_d, mc, sm, ws)
+        torch.cuda.synchronize()
+        tm = _timings(pa, ("decode",))
+        pa.check(pa.pa_timing_enable(False))
+        kv.close()
+        nbytes = decode_bytes(lns)
+        us = tm["decode"][1]
+        res[mode] = {"blocks_held": int(held), "kernel_us": round(us, 2),
+                     "achieved_GBps": round(nbytes / (us / 1e6) / 1e9, 1)}
+    res["workload"] = ("prefix sharing: 128 seqs = 1024-token shared system prompt + decode-70b "
+                       "lengths, 64/8 heads, d128, bf16; decode kernel on algorithmic bytes")
+    res["algorithmic_bytes_per_launch"] = int(nbytes)
+    res["blocks_saved"] = res["private"]["blocks_held"] - res["shared"]["blocks_held"]
+    return res
+
+
 def trace_leg(args, dev):
     """The continuous-batching trace: Poisson arrivals, lognormal prompts,
     geometric outputs, 256 running, 512-token prefill budget, 1000
@@ -813,6 +884,7 @@ def main():
         result["mixed"] = m
         result["fp8_decode"] = fp8_leg(args, dev)
         result["fp8_prefill"] = fp8_prefill_leg(args, dev)
+        result["prefix_sharing"] = prefix_leg(args, dev)
         result["trace"] = trace_leg(args, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample_seqs)
