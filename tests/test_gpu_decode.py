@@ -97,6 +97,25 @@ def test_large_work_items(S, long_lengths):
     hip["kv"].close()
 
 
+def test_many_sequences_two_launches():
+    """More sequences than one launch takes (4096): the launcher splits the
+    batch; with more than 512 sequences the partial items keep index order.
+    Oracle on sampled sequences of both launches."""
+    rng = np.random.default_rng(600)
+    lengths = rng.integers(1, 40, 5000)
+    w = _edge_workload(lengths, 8, 2, 64, "bf16", "bf16", seed=601, extra_blocks=3)
+    say(f"[decode parity] many sequences: {w.name} S={w.num_seqs}")
+    hip = hip_decode_run(w, DEV)
+    seqs = [0, 1, 511, 512, 4095, 4096, 4097, 4999]
+    ref = oracle_decode_run(w, seqs=seqs)
+    assert np.array_equal(hip["tables"], ref["tables"])
+    assert np.array_equal(hip["slots"], ref["slots"])
+    got = out_to_f64(hip["outs"][0], "bf16")
+    err = assert_close(got[seqs], ref["out"][seqs], "bf16", "many sequences")
+    say(f"    max|d| = {err:.3g}")
+    hip["kv"].close()
+
+
 def test_edge_lengths_f32_gqa():
     _check_full(_edge_workload([1, 16, 17, 100, 300], 8, 2, 64, "f32", "f32", seed=300),
                 "edge f32 8/2 d64")
