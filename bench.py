@@ -748,13 +748,14 @@ def trace_leg(args, dev):
     cache_note = "whole pool backed on the device"
     try:
         run = LayerIterations(w.num_blocks, H_Q, H_KV, D, dev, provider, w.max_running,
-                              w.prefill_budget, max_context=max_ctx)
+                              w.prefill_budget, max_context=max_ctx, provider_syncs=False)
     except torch.OutOfMemoryError:
         torch.cuda.empty_cache()
         cache_note = (f"device cache backs the {used_blocks} lowest block ids, the only ones "
                       f"the trace hands out (the host pool has all {w.num_blocks})")
         run = LayerIterations(w.num_blocks, H_Q, H_KV, D, dev, provider, w.max_running,
-                              w.prefill_budget, max_context=max_ctx, cache_blocks=used_blocks)
+                              w.prefill_budget, max_context=max_ctx, cache_blocks=used_blocks,
+                              provider_syncs=False)
     torch.cuda.synchronize()
     _settle()
     t0 = time.perf_counter()

@@ -33,10 +33,14 @@ class LayerIterations:
                  max_running: int = 256, prefill_budget: int = 512, max_context: int = 40960,
                  cache_blocks: int | None = None, cache_dtype: str = "bf16",
                  k_scale: float = 1.0, v_scale: float = 1.0, sm_scale: float | None = None,
-                 free_order=None):
+                 free_order=None, provider_syncs: bool = True):
         self.h_q, self.h_kv, self.d = h_q, h_kv, d
         self.dev = torch.device(device)
         self.provider = provider
+        # the provider's tensors come from work queued on the caller's
+        # current stream (True) or are already in memory (False: no
+        # cross-stream wait per iteration)
+        self.provider_syncs = bool(provider_syncs)
         self.R, self.B = max_running, prefill_budget
         self.k_scale, self.v_scale = float(k_scale), float(v_scale)
         self.sm = sm_scale if sm_scale is not None else float(np.float32(1.0) / np.float32(np.sqrt(d)))
@@ -54,14 +58,18 @@ class LayerIterations:
         self.v = torch.empty((self.cache_blocks, h_kv, d, BLOCK), dtype=dt, device=self.dev)
         self.max_ctx = max_context
         mb = -(-max_context // BLOCK)
-        # Per parity one pinned buffer and its device twin hold the
-        # iteration's slots, decode context lengths and tables, prefill
-        # tables and slice metadata, packed back to back; one pa_stage on
-        # the compute stream moves the used prefix.
+        # A ring of NBUF pinned buffers, each with a device twin, holds the
+        # iterations' slots, decode context lengths and tables, prefill
+        # tables and slice metadata, packed back to back; one launch on the
+        # compute stream moves the used prefix.  One event per GROUP
+        # iterations tells the host which buffers the kernels have read.
         T = max_running + max(prefill_budget, 1)
         n_meta = T + max_running + 2 * max_running * mb + 2 * max_running + 1
-        self.host_buf = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True) for _ in range(2)]
-        self.dev_buf = [torch.empty(n_meta, dtype=torch.int32, device=self.dev) for _ in range(2)]
+        self.NBUF, self.GROUP = 8, 4
+        self.host_buf = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True)
+                         for _ in range(self.NBUF)]
+        self.dev_buf = [torch.empty(n_meta, dtype=torch.int32, device=self.dev)
+                        for _ in range(self.NBUF)]
         out_dt = torch.bfloat16
         self.out_dec = [torch.empty((max_running, h_q, d), dtype=out_dt, device=self.dev) for _ in range(2)]
         self.out_pf = [torch.empty((max(prefill_budget, 1), h_q, d), dtype=out_dt, device=self.dev)
@@ -72,10 +80,11 @@ class LayerIterations:
                 for c in range(1, max_running + 1))
         self.ws_pf = torch.empty(max(n, 1), dtype=torch.uint8, device=self.dev)
         self.compute = torch.cuda.Stream(device=self.dev)
-        self.ev_done = [torch.cuda.Event() for _ in range(2)]
-        for e in self.ev_done:
+        self.ev_group = [torch.cuda.Event() for _ in range(2)]
+        for e in self.ev_group:
             e.record(self.compute)
         self.it = 0
+        self._last = None
         self.totals = {"decode_tokens": 0, "prefill_tokens": 0, "preempted": 0, "finished": 0}
         self.waste = []        # internal waste per iteration (nan: nothing held)
         self.unwritten = []    # reserved-unwritten share per iteration (nan: nothing held)
@@ -101,8 +110,12 @@ class LayerIterations:
         """One iteration.  ``keep``: optional callback(record) receiving the
         iteration's host-side record (decode/prefill lists) and its output
         tensors once the kernels have finished (test use)."""
-        X = self.it & 1
-        self.ev_done[X].synchronize()
+        X = self.it % self.NBUF
+        g = self.it // self.GROUP
+        if self.it % self.GROUP == 0:
+            # recorded after group g-2, the last user of this group's buffers
+            self.ev_group[g % 2].synchronize()
+        O = self.it & 1    # output buffers: the stream orders their reuse
         b = self.batch
         pa.check(pa.pa_sched_step(self.sched, b))
         ds, dp, dsl = b.decode()
@@ -167,7 +180,7 @@ class LayerIterations:
         if n_tok:
             k_new, v_new, q_new = self.provider(seqs, poss)
         c = self.compute
-        if n_tok:
+        if n_tok and self.provider_syncs:
             # the provider's tensors were produced on the caller's stream
             c.wait_stream(torch.cuda.current_stream(self.dev))
             for t in (k_new, v_new, q_new):
@@ -181,23 +194,31 @@ class LayerIterations:
         else:
             pa.check(pa.pa_stage(c, dvb, self.host_buf[X], 4 * off))
         if n_pf:
-            pa.check(pa.pa_prefill_chunk(c, self.out_pf[X][:n_pt], q_new[:n_pt], d_pm[:n_pf + 1],
+            pa.check(pa.pa_prefill_chunk(c, self.out_pf[O][:n_pt], q_new[:n_pt], d_pm[:n_pf + 1],
                                          d_pm[n_pf + 1:], self.k, self.v, d_pt.view(n_pf, mbp),
                                          self.cache_blocks, self.h_kv, int(pl.max()),
                                          int((pst + pl).max()), self.sm, self.k_scale,
                                          self.v_scale, self.ws_pf))
         if n_dec:
-            pa.check(pa.pa_decode(c, self.out_dec[X][:n_dec], q_new[n_pt:n_tok], self.k, self.v,
+            pa.check(pa.pa_decode(c, self.out_dec[O][:n_dec], q_new[n_pt:n_tok], self.k, self.v,
                                   d_dt.view(n_dec, mbd), d_dl, self.cache_blocks, self.h_kv,
                                   int(dp.max()) + 1, self.sm, self.k_scale, self.v_scale,
                                   self.ws_dec))
-        self.ev_done[X].record(c)
+        if self.it % self.GROUP == self.GROUP - 1:
+            self.ev_group[g % 2].record(c)
+        self._last = (record, self.out_dec[O][:n_dec], self.out_pf[O][:n_pt])
         if keep is not None:
-            self.ev_done[X].synchronize()
-            keep(record, self.out_dec[X][:n_dec].clone(), self.out_pf[X][:n_pt].clone())
+            c.synchronize()
+            keep(record, self.out_dec[O][:n_dec].clone(), self.out_pf[O][:n_pt].clone())
         self.it += 1
         return n_tok
 
+    def outputs(self):
+        """The last iteration's host-side record and its decode and prefill
+        outputs as device views.  The kernels that write them are queued on
+        ``self.compute``, and the iteration after next overwrites them, so
+        read them from work on that stream (or after ``synchronize``)."""
+        return self._last
+
     def synchronize(self):
-        for e in self.ev_done:
-            e.synchronize()
+        self.compute.synchronize()

@@ -24,14 +24,12 @@ def say(msg):
     sys.stdout.flush()
 
 
-def test_trace_iterations_match_oracle():
-    from paged_kv_cache_host_amd.engine import to_device_raw
-    from paged_kv_cache_host_amd.iteration import LayerIterations
+H_Q, H_KV, D, R, B, SEED = 16, 4, 128, 12, 96, 41
 
-    H_Q, H_KV, D, R, B, SEED = 16, 4, 128, 12, 96, 41
+
+def _trace():
     w = workloads.trace(seed=SEED, iters=80, lam=0.5, prompt_median=60, prompt_sigma=0.8,
                         prompt_cap=500, out_mean=30, num_blocks=80)
-    say(f"[trace parity] {w.name} pool={w.num_blocks} running<={R} budget={B}")
     rows = {}
     for row in w.arrivals:
         for sid, p, o in row:
@@ -43,35 +41,27 @@ def test_trace_iterations_match_oracle():
         q = np.stack([rows[s][2][p] for s, p in zip(seqs, positions)])
         return k, v, q
 
-    def provider(seqs, positions):
-        k, v, q = host_rows(seqs, positions)
-        return (to_device_raw(k, "bf16", "cuda"), to_device_raw(v, "bf16", "cuda"),
-                to_device_raw(q, "bf16", "cuda"))
-
     max_ctx = max(p + o for row in w.arrivals for _, p, o in row)
-    run = LayerIterations(w.num_blocks, H_Q, H_KV, D, "cuda", provider, R, B, max_context=max_ctx)
+    return w, host_rows, max_ctx
+
+
+def _replay(w, host_rows, sm, results):
+    """Run the oracle's scheduler, cache scatter and attention over the same
+    trace and compare every iteration's record and outputs (``results[it]``
+    = (record, decode output, prefill output), decoded to float)."""
     pool = oa.BlockPool(w.num_blocks, 16)
     sch = Scheduler(pool, R, B)
     kc, vc = oc.new_cache(w.num_blocks, H_KV, 16, D, "bf16")
-    sm = run.sm
     checked = {"decode": 0, "prefill": 0}
-    worst = [0.0]
-
+    worst = 0.0
+    written = set()
     for it in range(w.iters):
         for sid, p, o in w.arrivals[it]:
-            run.add(sid, p, o)
             sch.add(sid, p, o)
-        got = {}
-
-        def keep(rec, out_dec, out_pf):
-            got["rec"] = rec
-            got["dec"] = codecs.decode(out_dec.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
-            got["pf"] = codecs.decode(out_pf.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
-
-        run.step(keep)
+        rec, dec, pf = results[it]
         ob = sch.step()
-        ds, dp = got["rec"]["decode"]
-        ps, pst, pl = got["rec"]["prefill"]
+        ds, dp = rec["decode"]
+        ps, pst, pl = rec["prefill"]
         assert [(s, p) for s, p, _ in ob.decode] == list(zip(ds.tolist(), dp.tolist())), it
         assert [(s, a, n) for s, a, n, _ in ob.prefill] == \
             list(zip(ps.tolist(), pst.tolist(), pl.tolist())), it
@@ -79,16 +69,18 @@ def test_trace_iterations_match_oracle():
         for s, a, n, slots in ob.prefill:
             k, v, _ = host_rows([s] * n, list(range(a, a + n)))
             oc.cache_write(kc, vc, k, v, slots, "bf16", "bf16")
+            written.update(int(x) for x in slots)
         for s, p, slot in ob.decode:
             k, v, _ = host_rows([s], [p])
             oc.cache_write(kc, vc, k, v, [slot], "bf16", "bf16")
+            written.add(int(slot))
         off = 0
         for s, a, n, _ in ob.prefill:
             _, _, q = host_rows([s] * n, list(range(a, a + n)))
             ref = oat.prefill_chunk(codecs.decode(q, "bf16"), a, kc, vc, pool.block_table(s),
                                     H_KV, sm, "bf16")
-            worst[0] = max(worst[0], assert_close(got["pf"][off:off + n], ref, "bf16",
-                                                  f"iteration {it} prefill seq {s}"))
+            worst = max(worst, assert_close(pf[off:off + n], ref, "bf16",
+                                            f"iteration {it} prefill seq {s}"))
             off += n
             checked["prefill"] += n
         if ob.decode:
@@ -101,9 +93,83 @@ def test_trace_iterations_match_oracle():
                 tables[i, :len(t)] = t
             lens = np.array([p + 1 for _, p, _ in ob.decode])
             ref = oat.decode(codecs.decode(q, "bf16"), kc, vc, tables, lens, H_KV, sm, "bf16")
-            worst[0] = max(worst[0], assert_close(got["dec"], ref, "bf16", f"iteration {it} decode"))
+            worst = max(worst, assert_close(dec, ref, "bf16", f"iteration {it} decode"))
             checked["decode"] += len(seqs)
+    return checked, worst, kc, vc, sorted(written)
+
+
+def _decode_bf16(t):
+    return codecs.decode(t.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+
+
+def test_trace_iterations_match_oracle():
+    """Host waits for every iteration's kernels (the ``keep`` callback)."""
+    from paged_kv_cache_host_amd.engine import to_device_raw
+    from paged_kv_cache_host_amd.iteration import LayerIterations
+
+    w, host_rows, max_ctx = _trace()
+    say(f"[trace parity, synchronous] {w.name} pool={w.num_blocks} running<={R} budget={B}")
+
+    def provider(seqs, positions):
+        k, v, q = host_rows(seqs, positions)
+        return (to_device_raw(k, "bf16", "cuda"), to_device_raw(v, "bf16", "cuda"),
+                to_device_raw(q, "bf16", "cuda"))
+
+    run = LayerIterations(w.num_blocks, H_Q, H_KV, D, "cuda", provider, R, B, max_context=max_ctx)
+    results = []
+    for it in range(w.iters):
+        for sid, p, o in w.arrivals[it]:
+            run.add(sid, p, o)
+
+        def keep(rec, out_dec, out_pf):
+            results.append((rec, _decode_bf16(out_dec), _decode_bf16(out_pf)))
+
+        run.step(keep)
     run.close()
+    checked, worst, _, _, _ = _replay(w, host_rows, run.sm, results)
     say(f"    checked {checked['decode']} decode tokens, {checked['prefill']} prefill tokens, "
-        f"{run.totals['preempted']} preemptions, max|d| = {worst[0]:.3g}")
+        f"{run.totals['preempted']} preemptions, max|d| = {worst:.3g}")
+    assert run.totals["preempted"] > 0 and checked["decode"] > 50 and checked["prefill"] > 500
+
+
+def test_trace_iterations_pipelined_match_oracle():
+    """The host runs ahead of the kernels (metadata ring, one event per group
+    of iterations, provider tensors already resident): outputs are copied on
+    the compute stream, the written cache slots compared byte for byte at
+    the end."""
+    from paged_kv_cache_host_amd.engine import to_device_raw
+    from paged_kv_cache_host_amd.iteration import LayerIterations
+
+    w, host_rows, max_ctx = _trace()
+    say(f"[trace parity, pipelined] {w.name} pool={w.num_blocks} running<={R} budget={B}")
+
+    def provider(seqs, positions):
+        k, v, q = host_rows(seqs, positions)
+        out = (to_device_raw(k, "bf16", "cuda"), to_device_raw(v, "bf16", "cuda"),
+               to_device_raw(q, "bf16", "cuda"))
+        torch.cuda.current_stream().synchronize()
+        return out
+
+    run = LayerIterations(w.num_blocks, H_Q, H_KV, D, "cuda", provider, R, B, max_context=max_ctx,
+                          provider_syncs=False)
+    copies = []
+    for it in range(w.iters):
+        for sid, p, o in w.arrivals[it]:
+            run.add(sid, p, o)
+        run.step()
+        rec, od, op = run.outputs()
+        with torch.cuda.stream(run.compute):
+            copies.append((rec, od.clone(), op.clone()))
+    run.synchronize()
+    results = [(rec, _decode_bf16(od), _decode_bf16(op)) for rec, od, op in copies]
+    k_dev = run.k.view(torch.int16).cpu().numpy().view(np.uint16)
+    v_dev = run.v.view(torch.int16).cpu().numpy().view(np.uint16)
+    run.close()
+    checked, worst, kc, vc, written = _replay(w, host_rows, run.sm, results)
+    blk = np.array(written) // 16
+    off = np.array(written) % 16
+    np.testing.assert_array_equal(k_dev[blk, :, :, off, :], kc[blk, :, :, off, :])
+    np.testing.assert_array_equal(v_dev[blk, :, :, off], vc[blk, :, :, off])
+    say(f"    checked {checked['decode']} decode tokens, {checked['prefill']} prefill tokens, "
+        f"{len(written)} cache slots, {run.totals['preempted']} preemptions, max|d| = {worst:.3g}")
     assert run.totals["preempted"] > 0 and checked["decode"] > 50 and checked["prefill"] > 500
