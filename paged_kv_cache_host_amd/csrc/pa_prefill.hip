@@ -24,10 +24,15 @@
 // positions per wave; when a KV head has fewer than eight query heads the
 // spare waves take further 32-position sub-tiles, so every wave of the group
 // consumes the same K/V tile.  K/V arrive in tiles of 64 keys (four cache
-// blocks), staged through LDS in two buffers: the global loads of tile t+1
-// are in flight while tile t is multiplied.  When the slices alone give too
-// few work-groups to fill the chip, the key range is split and a second
-// kernel merges the partial softmax states.
+// blocks), staged through four LDS stages: the global loads of a tile are
+// issued two iterations before its keys are multiplied, so their latency
+// hides behind a whole iteration of matrix work.  Inside each wave the
+// tiles run as a software pipeline (see the main loop): the MFMAs of one
+// tile's scores and of an older tile's P V product interleave with the
+// exponentials of the tile in between, so that the matrix core and the
+// vector unit work at once.  When the slices alone give too few work-groups
+// to fill the chip, the key range is split and a second kernel merges the
+// partial softmax states.
 //
 // Per wave and 32-key half-tile the scores are computed transposed,
 // S^T = K Q^T (keys on the MFMA rows, the wave's 32 queries on its columns),
@@ -39,6 +44,8 @@
 // quads swapped; with that permutation the 8 keys a lane holds for each
 // 16-key step of P^T are consecutive, which is what one 16-byte read of the
 // token-minor V layout supplies.
+#include <utility>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -161,27 +168,63 @@ struct TileLoader {
   __device__ Piece piece(int i) const {
     const int p = wave * kWave + i * kPfThreads;
     Piece q;
-    q.v = p >= kHalf;
+    // when the K half is a whole number of sweeps over the threads, which
+    // tensor a piece belongs to depends on i alone
+    q.v = kHalf % kPfThreads == 0 ? i * kPfThreads >= kHalf : p >= kHalf;
     const int pp = q.v ? p - kHalf : p;
     q.b = pp / kPerBlock;
     q.e0 = pp % kPerBlock;
     return q;
   }
 
-  // blk: the tile's four block ids (scalars, inside the pool).  Blocks past
-  // the context are loaded too (any valid id): their keys lie beyond
-  // `valid`, so store() zeroes their V and the causal mask drops their
-  // scores.  Loading unconditionally keeps the loads free of any use before
-  // the store, so their latency overlaps the tile's compute.
+  // ids: lanes 0..3 hold the tile's four block ids, already inside the
+  // pool.  Blocks past the context are loaded too (any valid id): their
+  // keys lie beyond `valid`, so store() zeroes their V and the causal mask
+  // drops their scores.  Loading unconditionally keeps the loads free of
+  // any use before the store, so their latency overlaps the tile's compute.
+  __device__ void load1(u32x4& r, int i, const CR* __restrict__ k_cache,
+                        const CR* __restrict__ v_cache, int32_t ids, int32_t kvh,
+                        int32_t H_kv) const {
+    const Piece q = piece(i);
+    const int32_t bk = __builtin_amdgcn_readlane(ids, q.b);
+    const CR* base = (q.v ? v_cache : k_cache) +
+                     (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + q.e0 * kElems;
+    r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane * kElems));
+  }
   __device__ void load(u32x4* regs, const CR* __restrict__ k_cache, const CR* __restrict__ v_cache,
-                       const int32_t (&blk)[4], int32_t kvh, int32_t H_kv) const {
+                       int32_t ids, int32_t kvh, int32_t H_kv) const {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const Piece q = piece(i);
-      const int32_t bk = q.b == 0 ? blk[0] : q.b == 1 ? blk[1] : q.b == 2 ? blk[2] : blk[3];
+      const int32_t bk = __builtin_amdgcn_readlane(ids, q.b);
       const CR* base = (q.v ? v_cache : k_cache) +
                        (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + q.e0 * kElems;
       regs[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane * kElems));
+    }
+  }
+
+  // Piece i of the tile into a stage, V beyond the context not cleared.
+  __device__ void store1(const u32x4& w0, int i, uint8_t* stage) const {
+    const Piece q = piece(i);
+    u32x4 w = w0;
+    if (!kWide) {
+      if (!q.v) {
+        const int off = (q.e0 >> 4) * (kPfKeys * 16) + q.b * kBlock * 16;
+        *reinterpret_cast<u32x4*>(stage + off + k_lane) = w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(w[j]);
+        const int off = D * kPfKeys * 2 + ((q.e0 >> 1) >> 4) * 2048 + 2 * q.b * 256;
+        *reinterpret_cast<u32x4*>(stage + off + v_lane) = w;
+      }
+    } else if (!q.v) {
+      const int off = (q.e0 >> 4) * 2 * (kPfKeys * 16) + q.b * kBlock * 16 + k_lane;
+      *reinterpret_cast<bf16x8*>(stage + off) = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
+      *reinterpret_cast<bf16x8*>(stage + off + kPfKeys * 16) = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
+    } else {
+      const int off = D * kPfKeys * 2 + (q.e0 >> 4) * 2048 + 2 * q.b * 256 + v_lane;
+      *reinterpret_cast<f16x8*>(stage + off) = fp8x8_to_f16x8(u32x2{w[0], w[1]});
+      *reinterpret_cast<f16x8*>(stage + off + 256) = fp8x8_to_f16x8(u32x2{w[2], w[3]});
     }
   }
 
@@ -251,7 +294,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
   constexpr int NDT = D / 32;  // 32-dim tiles of O^T
   using Loader = TileLoader<CacheT, D>;
   constexpr int NLD = Loader::NLD;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * stage_bytes<D>()];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * stage_bytes<D>()];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -322,128 +365,257 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
 
   const int32_t* table = block_tables + static_cast<int64_t>(c) * max_blocks;
   const int32_t n_blk = min((kv_end + kBlock - 1) / kBlock, max_blocks);
-  // Block ids are fetched one tile ahead of their use by a vector load
-  // (lanes 0..3 take the tile's four entries, raw) and checked as scalars
-  // when used: entries past the context become block 0, any entry outside
-  // the pool is clamped into it.
+  // Block ids are fetched two tiles ahead of their use by a vector load:
+  // lanes 0..3 take the tile's four entries (entries past the context
+  // repeat the last one), clamped into the pool.
   auto fetch_ids = [&](int t) -> int32_t {
-    return table[min(t * 4 + (lane & 3), n_blk - 1)];
-  };
-  auto ids_of = [&](int32_t v, int t, int32_t (&blk)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int32_t e = __builtin_amdgcn_readlane(v, j);
-      blk[j] = t * 4 + j < n_blk ? safe_block(e, num_blocks) : 0;
-    }
+    return safe_block(table[min(t * 4 + (lane & 3), n_blk - 1)], num_blocks);
   };
 
   const Loader ld(wave, lane);
   const int v_lane = v_off(col, g);
 
-  // One tile's phases.  S^T for the 64 keys of a stage:
-  auto qk = [&](const uint8_t* k_lds, f32x16* s) {
+  // Software pipeline inside each wave.  Iteration t enters with the fp16
+  // weights P(t-1), the scores S(t) and the softmax reference for S(t)
+  // already settled.  One straight run of 32 MFMAs then computes
+  // S(t+1) = K(t+1) Q^T and O^T += V(t-1)^T P(t-1)^T; none of them waits
+  // for the vector work of the same iteration, which in between turns S(t)
+  // into P(t) and takes the row maxima of S(t+1).  The reference for S(t+1)
+  // is settled after the run; raising it rescales l at once and O^T one
+  // iteration later, once the product with P(t) (formed against the old
+  // reference) is in.  K/V tiles rotate through four LDS stages: tile t is
+  // stored during iteration t-2, read as K in iteration t-1 and as V in
+  // iteration t+1.
+  auto stage = [&](int t) { return smem + ((t - t0) & 3) * stage_bytes<D>(); };
+  constexpr int NQK = 2 * NKS;       // S MFMAs per tile
+  constexpr int NPV = 4 * NDT;       // O MFMAs per tile
+  constexpr int NM = NQK + NPV;
+  constexpr int EPS = 32 / NQK;      // exponentials per S slot
+  static_assert(EPS * NQK == 32, "32 scores per lane and tile");
+  constexpr int PD = 2;              // operand reads issued this many MFMAs ahead
+  constexpr int kLd0 = NLD;          // first slot with a tile load
+  constexpr int kLdEvery = 4;        // one tile load every this many MFMA slots
+  static_assert(kLd0 + kLdEvery * NLD < NM, "the tile loads fit the slots");
+
+  u32x4 regs[NLD];
+  int32_t ids_ahead = fetch_ids(t0);
+  auto load_tile = [&](int t) {  // tiles past the range reload the last one
+    const int tc = min(t, t1 - 1);
+    ld.load(regs, k_cache, v_cache, ids_ahead, kvh, geo.H_kv);
+    ids_ahead = fetch_ids(min(tc + 1, t1 - 1));
+  };
+  auto store_tile = [&](int t) {
+    ld.store(regs, stage(t), kv_end - min(t, t1 - 1) * kPfKeys);
+  };
+  auto zero_v_tail = [&](uint8_t* v_lds, int valid) {
+    for (int idx = tid; idx < D * 8; idx += kPfThreads) {
+      const int d = idx >> 3, c = idx & 7;
+      if (8 * c + 7 >= valid) {
+        f16x8* p = reinterpret_cast<f16x8*>(v_lds + v_off(d, c));
+        f16x8 v = *p;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s[h][j] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            k_lds + (2 * ks + g) * (kPfKeys * 16) + (32 * h + col) * 16);
-        s[h] = mfma32x32x16(a, qf[ks], s[h]);
+        for (int j = 0; j < 8; ++j)
+          if (8 * c + j >= valid) v[j] = static_cast<_Float16>(0.0f);
+        *p = v;
       }
     }
   };
-  // softmax update of the scores of the tile starting at key0 (in place:
-  // the scores become the weights), then O^T += V^T P^T from the stage's V.
-  auto softmax_pv = [&](f32x16* s, int32_t key0, const uint8_t* v_lds) {
-    // causal mask, only in the (at most two) tiles that reach past the
-    // wave's first position
-    if (key0 + kPfKeys - 1 > wave_first_pos) {
-      const int lim = qpos - key0 - 8 * g;  // largest admissible key offset
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int off = 32 * h + 16 * (j >> 3) + (j & 7);
-          s[h][j] = off <= lim ? s[h][j] : -__builtin_inff();
-        }
-    }
-    // the score scale is positive, so the maximum is taken on raw scores
-    float mx = s[0][0];
+  auto mask_scores = [&](f32x16* s, int t) {
+    const int lim = qpos - t * kPfKeys - 8 * g;  // largest admissible key offset
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[h][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * score_scale;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kPfLazy) != 0) {
+      for (int j = 0; j < 16; ++j) {
+        const int off = 32 * h + 16 * (j >> 3) + (j & 7);
+        s[h][j] = off <= lim ? s[h][j] : -__builtin_inff();
+      }
+  };
+  // the score scale is positive, so maxima are taken on raw scores
+  auto half_max = [&](const f32x16& s) {
+    // scores are never NaN: plain three-way maxima, no quieting
+    float m;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(s[0]), "v"(s[1]), "v"(s[2]));
+#pragma unroll
+    for (int j = 3; j < 15; j += 2)
+      asm("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(m), "v"(s[j]), "v"(s[j + 1]));
+    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(m), "v"(s[15]));
+    return m;
+  };
+  float mu = 0.f;                    // reference the exponentials of S(t) use
+  bool carry = false;                // O^T still owes a rescale by alpha_c
+  float alpha_c = 1.f;
+  // settle the reference for scores whose lane maximum (raw) is mx
+  auto settle = [&](float mx) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * score_scale;
+    const bool raise = __builtin_amdgcn_ballot_w64(mx > m_run + kPfLazy) != 0;
+    float alpha = 1.f;
+    if (raise) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
+      m_run = m_new;
+    }
+    mu = m_run == -__builtin_inff() ? 0.f : m_run;
+    return std::pair<bool, float>(raise, alpha);
+  };
+
+  // One iteration.  sc: S(t) in, sn: S(t+1) out, pp: P(t-1) in, pn: P(t) out.
+  auto body = [&](auto masked_next, int t, f32x16* sc, f32x16* sn, const f16x8* pp, f16x8* pn) {
+    // Tile t+2 (loaded during the last iteration) goes into its stage in the
+    // first slots; the global loads of tile t+3 follow, spread over the
+    // slots so that the waves do not queue for the address unit at once,
+    // and have a whole iteration to arrive.
+    const int t_ld = min(t + 3, t1 - 1);
+    uint8_t* st_lds = stage(t + 2);
+    const uint8_t* k_lds = stage(t + 1);
+    const uint8_t* v_lds = stage(t - 1) + D * kPfKeys * 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sn[h][j] = 0.f;
+    // MFMA slot i < NQK: S step i (h = i & 1, ks = i >> 1); slot NQK + j: O
+    // step j (u = j / NDT, n = j % NDT)
+    auto operand = [&](int i) -> u32x4 {
+      if (i < NQK)
+        return *reinterpret_cast<const u32x4*>(k_lds + (2 * (i >> 1) + g) * (kPfKeys * 16) +
+                                                (32 * (i & 1) + col) * 16);
+      const int j = i - NQK;
+      return *reinterpret_cast<const u32x4*>(v_lds + v_lane + (j % NDT) * 4096 + (j / NDT) * 512);
+    };
+    u32x4 opnd[PD + 1];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) opnd[i] = operand(i);
+    const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + PD < NM) opnd[(i + PD) % (PD + 1)] = operand(i + PD);
+      if (i < NLD) ld.store1(regs[i], i, st_lds);
+      if (i >= kLd0 && (i - kLd0) % kLdEvery == 0 && (i - kLd0) / kLdEvery < NLD)
+        ld.load1(regs[(i - kLd0) / kLdEvery], (i - kLd0) / kLdEvery, k_cache, v_cache, ids_ahead,
+                 kvh, geo.H_kv);
+      if (i == kLd0 + kLdEvery * NLD) ids_ahead = fetch_ids(min(t_ld + 1, t1 - 1));
+      if (i < NQK) {
+        sn[i & 1] = mfma32x32x16(__builtin_bit_cast(bf16x8, opnd[i % (PD + 1)]), qf[i >> 1],
+                                 sn[i & 1]);
+        // weights of scores e = EPS i .. (e = 8 u + i8: key 16 u + i8 of
+        // the lane's half), in pairs
+#pragma unroll
+        for (int q2 = 0; q2 < EPS; q2 += 2) {
+          const int e = EPS * i + q2;
+          const int u = e >> 3, i8 = e & 7;
+          const float w0 = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(sc[u >> 1][8 * (u & 1) + i8], score_scale, -mu));
+          const float w1 = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(sc[u >> 1][8 * (u & 1) + i8 + 1], score_scale, -mu));
+          f16x2 h2 = {static_cast<_Float16>(w0), static_cast<_Float16>(w1)};
+          // computed here, between the MFMAs, not where it is next used
+          asm volatile("" : "+v"(h2));
+          pn[u][i8] = h2[0];
+          pn[u][i8 + 1] = h2[1];
+          l_run = __builtin_amdgcn_fdot2(h2, ones, l_run, false);
+          asm volatile("" : "+v"(l_run));
+        }
+      } else {
+        const int j = i - NQK;
+        o[j % NDT] = mfma32x32x16(__builtin_bit_cast(f16x8, opnd[i % (PD + 1)]), pp[j / NDT],
+                                  o[j % NDT]);
+        // S(t+1) is complete two slots after its last MFMA: mask it (where
+        // it reaches the diagonal) and take its lane maximum
+        if (j == 1) {
+          if constexpr (decltype(masked_next)::value) mask_scores(sn, t + 1);
+          mx = half_max(sn[0]);
+          asm volatile("" : "+v"(mx));
+        }
+        if (j == NPV / 2) {
+          mx = fmaxf(mx, half_max(sn[1]));
+          asm volatile("" : "+v"(mx));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the rescale owed since the last iteration applies to O^T as it
+    // stands now, P(t-1) included
+    if (carry) {
 #pragma unroll
       for (int n = 0; n < NDT; ++n)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[n][j] *= alpha;
-      m_run = m_new;
+        for (int j = 0; j < 16; ++j) o[n][j] *= alpha_c;
     }
-    const float mu = m_run == -__builtin_inff() ? 0.f : m_run;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        s[h][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][j], score_scale, -mu));
-    // four 16-key steps: step u takes keys 16u .. 16u + 15, i.e. registers
-    // 8 (u & 1) .. + 7 of half u / 2.  The row sum adds the fp16 weights
-    // exactly as they enter the product (two per dot instruction).
-    const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      f16x8 pb;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = static_cast<_Float16>(s[u >> 1][8 * (u & 1) + i]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        l_run = __builtin_amdgcn_fdot2(f16x2{pb[2 * i], pb[2 * i + 1]}, ones, l_run, false);
-#pragma unroll
-      for (int n = 0; n < NDT; ++n) {
-        // v_off(32 n + col, 2 u + g) = v_off(col, g) + n * 4096 + u * 512
-        const f16x8 a = *reinterpret_cast<const f16x8*>(v_lds + v_lane + n * 4096 + u * 512);
-        o[n] = mfma32x32x16(a, pb, o[n]);
-      }
-    }
+    // the last tile has no successor: its S(t+1) is a stand-in
+    const auto ra = settle(t + 1 < t1 ? mx : -__builtin_inff());
+    carry = ra.first;
+    alpha_c = ra.second;
+    // V of keys past the context must be zero, not stale cache bits
+    const int valid_st = kv_end - min(t + 2, t1 - 1) * kPfKeys;
+    if (valid_st < kPfKeys) zero_v_tail(st_lds + D * kPfKeys * 2, valid_st);
+    __syncthreads();
   };
 
-  // Two LDS stages: the global loads of tile t+1 are issued before tile t
-  // is multiplied and stored into the other stage after it.
-  auto stage = [&](int t) { return smem + ((t - t0) & 1) * stage_bytes<D>(); };
-  u32x4 regs[NLD];
-  int32_t ids_ahead = 0;
   if (t0 < t1) {
-    int32_t blk[4];
-    ids_of(fetch_ids(t0), t0, blk);
-    ld.load(regs, k_cache, v_cache, blk, kvh, geo.H_kv);
-    if (t0 + 1 < t1) ids_ahead = fetch_ids(t0 + 1);
-    ld.store(regs, stage(t0), kv_end - t0 * kPfKeys);
-    __syncthreads();
-  }
-  for (int t = t0; t < t1; ++t) {
-    const bool more = t + 1 < t1;
-    if (more) {
-      int32_t blk[4];
-      ids_of(ids_ahead, t + 1, blk);
-      ld.load(regs, k_cache, v_cache, blk, kvh, geo.H_kv);
-      if (t + 2 < t1) ids_ahead = fetch_ids(t + 2);
-    }
-    const int32_t key0 = t * kPfKeys;
-    if (wave_live && key0 <= wave_last_pos) {
-      f32x16 s[2];
-      qk(stage(t), s);
-      softmax_pv(s, key0, stage(t) + D * kPfKeys * 2);
-    }
-    if (more) {
-      ld.store(regs, stage(t + 1), kv_end - (t + 1) * kPfKeys);
+    load_tile(t0);
+    store_tile(t0);
+    load_tile(t0 + 1);
+    store_tile(t0 + 1);
+    load_tile(t0 + 2);  // stored by iteration t0
+    {
+      // iteration t0 multiplies zero weights by the V half of the stage
+      // before it: clear that half so that no stale bits become NaN
+      uint8_t* vz = stage(t0 - 1) + D * kPfKeys * 2;
+      for (int i = tid; i < D * kPfKeys * 2 / 16; i += kPfThreads)
+        *reinterpret_cast<u32x4*>(vz + 16 * i) = u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
+    f32x16 sA[2], sB[2];
+    f16x8 pA[4], pB[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pA[u][i] = static_cast<_Float16>(0.0f);
+    // S(t0) and its reference
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sA[h][j] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            stage(t0) + (2 * ks + g) * (kPfKeys * 16) + (32 * h + col) * 16);
+        sA[h] = mfma32x32x16(a, qf[ks], sA[h]);
+      }
+    }
+    if (t0 * kPfKeys + kPfKeys - 1 > wave_first_pos) mask_scores(sA, t0);
+    settle(fmaxf(half_max(sA[0]), half_max(sA[1])));
+    // iteration t masks S(t+1) when tile t+1 reaches past the wave's first
+    // position, i.e. from tile t_mask on
+    const int t_mask = (wave_first_pos + 1) / kPfKeys;
+    int t = t0;
+    for (; t + 2 < min(t_mask, t1); t += 2) {
+      body(std::false_type{}, t, sA, sB, pA, pB);
+      body(std::false_type{}, t + 1, sB, sA, pB, pA);
+    }
+    for (; t + 1 < t1; t += 2) {
+      body(std::true_type{}, t, sA, sB, pA, pB);
+      body(std::true_type{}, t + 1, sB, sA, pB, pA);
+    }
+    const f16x8* p_last = pA;
+    int t_last = t - 1;
+    if (t < t1) {
+      body(std::true_type{}, t, sA, sB, pA, pB);
+      p_last = pB;
+      t_last = t;
+    }
+    // O^T += V(last)^T P(last)^T; every owed rescale is already applied
+    const uint8_t* v_lds = stage(t_last) + D * kPfKeys * 2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int n = 0; n < NDT; ++n) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(v_lds + v_lane + n * 4096 + u * 512);
+        o[n] = mfma32x32x16(a, p_last[u], o[n]);
+      }
   }
 
   if (!row_ok) return;
