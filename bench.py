@@ -6,11 +6,12 @@ Headline step (``value``): one continuous-batching decode iteration of one
 128, bf16, 16-token blocks, lognormal contexts of mean 1500):
 
   a1  host: libpa grows every sequence by one token (one block taken at each
-      block boundary) and packs slots, block tables and context lengths into
-      one pinned buffer (double-buffered, so this host work overlaps the
-      previous step's kernels);
-  a2  one pa_stage_cache_write launch moves that buffer to the device and
-      scatters the new tokens' K/V into their paged slots;
+      block boundary) and writes the new slots and context lengths into one
+      pinned buffer (a ring of them, so this host work overlaps the previous
+      steps' kernels); the block tables stay on the device;
+  a2  one pa_stage_decode_append launch moves that buffer to the device,
+      scatters the new tokens' K/V into their paged slots and enters each
+      block a token opens in its sequence's device block table;
   a3  pa_decode: split-K paged attention (+ merge of multi-chunk contexts).
 
 ``value`` is the step's algorithmic HBM bytes (decode: every K/V byte of
@@ -310,21 +311,27 @@ def decode_leg(args, dev):
     ws = decode_workspace(S, H_Q, H_KV, D, max_ctx, dev)
     sm = sm_scale_for(D)
 
-    # A ring of NBUF pinned host buffers, each with a device twin, holds the
-    # steps' slots, context lengths and block tables; one pa_stage kernel on
-    # the compute stream carries a step's buffer (no copy engine, no
-    # cross-engine wait).  The host may refill a buffer once the stage kernel
-    # that read it has run: one event per GROUP steps tells it so (an event
-    # record costs the stream a few microseconds, so not one per step).
+    # The batch's block tables live on the device: packed once at set-up,
+    # then kept up to date by the launch that scatters each step's new
+    # tokens (pa_stage_decode_append enters a token's block in its row when
+    # the token opens one).  A ring of NBUF pinned host buffers, each with a
+    # device twin, holds the steps' slots and context lengths; that same
+    # launch carries a step's buffer (no copy engine, no cross-engine wait).
+    # The host may refill a buffer once the launch that read it has run: one
+    # event per GROUP steps tells it so (an event record costs the stream a
+    # few microseconds, so not one per step).
     NBUF, GROUP = 8, 4
-    n_meta = 2 * S + S * MB
+    n_meta = 2 * S
+    st, tab0, lens_host = pa.pa_pack_batch(kv.pool, seqs, MB)
+    pa.check(st)
+    d_tab = torch.from_numpy(tab0).to(dev)
+    lens_host = lens_host.copy()
     host_buf = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True) for _ in range(NBUF)]
     dev_buf = [torch.empty(n_meta, dtype=torch.int32, device=dev) for _ in range(NBUF)]
     views = []
     for X in range(NBUF):
         h, d_ = host_buf[X].numpy(), dev_buf[X]
-        views.append((h[:S].reshape(S, 1), h[S:2 * S], h[2 * S:].reshape(S, MB),
-                      d_[:S], d_[S:2 * S], d_[2 * S:].view(S, MB)))
+        views.append((h[:S].reshape(S, 1), h[S:2 * S], d_[S:2 * S]))
     compute = torch.cuda.Stream(device=dev)
     ev_group = [torch.cuda.Event() for _ in range(2)]
     for e in ev_group:
@@ -334,20 +341,21 @@ def decode_leg(args, dev):
     def step(i: int, timed: bool):
         X = i % NBUF
         g = i // GROUP
-        h_slots, h_lens, h_tab, d_slots, d_lens, d_tab = views[X]
+        h_slots, h_lens, d_lens = views[X]
         if i % GROUP == 0:
             # recorded after group g-2, whose steps last used this group's buffers
             ev_group[g % 2].synchronize()
         st, done, _ = pa.pa_batch_append(kv.pool, seqs, 1, h_slots)
         pa.check(st)
-        st, _, lens_np = pa.pa_pack_batch(kv.pool, seqs, MB, h_tab, h_lens)
-        pa.check(st)
+        np.add(lens_host, 1, out=lens_host)
+        h_lens[:] = lens_host
+        lens_np = lens_host
         r = i % R
-        # one launch stages the buffer and scatters the new tokens, whose
-        # slots lead the buffer
-        pa.check(pa.pa_stage_cache_write(compute, dev_buf[X], host_buf[X], 4 * n_meta, 0, S,
-                                         k_ring[r], v_ring[r], kv.k, kv.v, num_blocks, H_KV, D,
-                                         BLOCK))
+        # one launch stages the buffer, scatters the new tokens (whose slots
+        # lead the buffer) and enters the blocks they open in the tables
+        pa.check(pa.pa_stage_decode_append(compute, dev_buf[X], host_buf[X], 4 * n_meta, 0, 4 * S,
+                                           S, k_ring[r], v_ring[r], kv.k, kv.v, num_blocks, H_KV,
+                                           D, d_tab, BLOCK))
         pa.check(pa.pa_decode(compute, out, q_ring[r], kv.k, kv.v, d_tab, d_lens,
                               num_blocks, H_KV, max_ctx, sm, 1.0, 1.0, ws))
         if timed:

@@ -381,6 +381,39 @@ pa_status pa_stage_cache_write(void* stream, void* dst, const void* src_host, si
                                int32_t bs, float k_scale, float v_scale);
 
 /* ------------------------------------------------------------------------
+ * pa_stage_decode_append -- pa_stage_cache_write for a decode batch whose
+ * block tables stay on the device from one iteration to the next.  ARTICLE
+ * 2.2: a sequence's block table only grows, by one entry whenever its next
+ * token opens a new block, and the BlockManager hands the attention kernel
+ * the tables of the running sequences (2.3).  Instead of restaging whole
+ * tables every iteration, the launch also enters, for each of the n new
+ * tokens (one per sequence, token i belonging to row i), the block of its
+ * slot at the column of its position:
+ *     block_tables[i * max_blocks + (lens[i] - 1) / bs] = slots[i] / bs
+ * which leaves the row unchanged unless the token opens a block.
+ *
+ * dst, src_host, bytes, slot_offset, k_new ... v_scale
+ *               as for pa_stage_cache_write
+ * lens_offset   byte offset inside src_host of the n int32 context lengths
+ *               (the new token included); a multiple of 4 with
+ *               lens_offset + 4 n <= bytes, else PA_ERR_INVALID.
+ * block_tables  [device, n x max_blocks] int32, the batch's tables as they
+ *               stood before this iteration (owned by the caller, updated in
+ *               place by the kernel); NULL with n > 0 is PA_ERR_INVALID.
+ * max_blocks    row stride, >= 1.
+ * A token whose slot lies outside the pool, or whose length is < 1 or
+ * > max_blocks * bs, leaves its row unchanged (its K/V are dropped as in
+ * pa_cache_write).  Cache bytes and the staged copy equal those of
+ * pa_stage_cache_write.
+ * ---------------------------------------------------------------------- */
+pa_status pa_stage_decode_append(void* stream, void* dst, const void* src_host, size_t bytes,
+                                 size_t slot_offset, size_t lens_offset, const void* k_new,
+                                 const void* v_new, pa_dtype new_dt, int32_t n, void* k_cache,
+                                 void* v_cache, pa_dtype cache_dt, int32_t num_blocks,
+                                 int32_t H_kv, int32_t D, int32_t bs, float k_scale,
+                                 float v_scale, int32_t* block_tables, int32_t max_blocks);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (instrumentation, off by default).  Each launch of a
  * selected kernel carries a pair of HIP events attached to the launch
  * (hipExtLaunchKernel), which take that kernel's start and end times (up to

@@ -91,6 +91,9 @@ _SIGS = {
     "pa_stage": (_i32, [_vp, _vp, _vp, _sz]),
     "pa_stage_cache_write": (_i32, [_vp, _vp, _vp, _sz, _sz, _vp, _vp, _i32, _i32, _vp, _vp, _i32,
                                     _i32, _i32, _i32, _i32, _f32, _f32]),
+    "pa_stage_decode_append": (_i32, [_vp, _vp, _vp, _sz, _sz, _sz, _vp, _vp, _i32, _i32, _vp,
+                                       _vp, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _vp,
+                                       _i32]),
     "pa_timing_enable": (_i32, [_i32, _i32]),
     "pa_timing_query": (_i32, [C.c_char_p, _i32p, C.POINTER(_f32), C.POINTER(_f32)]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -438,6 +441,31 @@ def pa_stage_cache_write(stream, dst, src_host, nbytes: int, slot_offset: int, n
                                      nbytes, slot_offset, _dptr(k_new), _dptr(v_new),
                                      dtype_of(k_new), n, _dptr(k_cache), _dptr(v_cache),
                                      dtype_of(k_cache), num_blocks, H_kv, D, bs, k_scale, v_scale)
+
+
+def pa_stage_decode_append(stream, dst, src_host, nbytes: int, slot_offset: int,
+                           lens_offset: int, n: int, k_new, v_new, k_cache, v_cache,
+                           num_blocks: int, H_kv: int, D: int, block_tables, bs: int = 16,
+                           k_scale: float = 1.0, v_scale: float = 1.0) -> int:
+    """pa_stage_cache_write of a decode batch whose device block tables
+    (``block_tables`` [n, max_blocks] int32 on the device) are kept up to date
+    in the same launch: token i (slot at byte ``slot_offset``, context length
+    at byte ``lens_offset`` of the staged buffer) enters its block in row i."""
+    if src_host.is_cuda or not src_host.is_pinned():
+        raise PaError(PA_ERR_INVALID, "pa_stage_decode_append: source must be a pinned host tensor")
+    if nbytes > src_host.numel() * src_host.element_size() or \
+            nbytes > dst.numel() * dst.element_size():
+        raise PaError(PA_ERR_INVALID, "pa_stage_decode_append: nbytes exceeds a buffer")
+    if str(block_tables.dtype) != "torch.int32" or not block_tables.is_contiguous() or \
+            block_tables.dim() != 2 or block_tables.shape[0] < n:
+        raise PaError(PA_ERR_INVALID, "pa_stage_decode_append: block_tables must be a contiguous "
+                      "int32 [n, max_blocks] tensor")
+    return _lib.pa_stage_decode_append(_stream_handle(stream), _dptr(dst), src_host.data_ptr(),
+                                       nbytes, slot_offset, lens_offset, _dptr(k_new),
+                                       _dptr(v_new), dtype_of(k_new), n, _dptr(k_cache),
+                                       _dptr(v_cache), dtype_of(k_cache), num_blocks, H_kv, D, bs,
+                                       k_scale, v_scale, _dptr(block_tables),
+                                       block_tables.shape[1])
 
 
 def pa_decode_workspace_bytes(S: int, H_q: int, H_kv: int, D: int, max_context_len: int) -> int:

@@ -112,14 +112,18 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
 // grid: stage groups + ceil(n / 16) * H_kv; block: 256 threads.  The first
 // `sgroups` work-groups copy the metadata buffer (as pa_stage), the others
 // scatter the new tokens with the slot mapping read from the same pinned
-// buffer, so both run in one launch.
+// buffer, so both run in one launch.  With `tables`, the work-groups of KV
+// head 0 also enter each token's block in row i of the device block tables
+// at the column of its position (context length - 1, read from the pinned
+// buffer as well).
 template <typename NewT, typename CacheT, int D, typename W>
 __global__ __launch_bounds__(256) void stage_cache_write_kernel(
     W* __restrict__ dst, const W* __restrict__ src, int64_t n_words, int32_t sgroups,
     const typename NewT::raw* __restrict__ k_new, const typename NewT::raw* __restrict__ v_new,
     const int32_t* __restrict__ slots_host, int32_t n, typename CacheT::raw* __restrict__ k_cache,
     typename CacheT::raw* __restrict__ v_cache, int32_t num_blocks, int32_t H_kv, float k_inv,
-    float v_inv) {
+    float v_inv, int32_t* __restrict__ tables, int32_t max_blocks,
+    const int32_t* __restrict__ lens_host) {
   const int b = blockIdx.x;
   if (b < sgroups) {
     stage_words<W>(dst, src, n_words, b, sgroups);
@@ -127,6 +131,18 @@ __global__ __launch_bounds__(256) void stage_cache_write_kernel(
   }
   const int ntb = (n + 15) / 16;
   const int r = b - sgroups;
+  if (tables && r < ntb && threadIdx.x < 16) {
+    const int64_t t = static_cast<int64_t>(r) * 16 + threadIdx.x;
+    if (t < n) {
+      const int32_t sl = __hip_atomic_load(slots_host + t, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM);
+      const int32_t len = __hip_atomic_load(lens_host + t, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_SYSTEM);
+      if (sl >= 0 && sl < num_blocks * kBlock && len >= 1 &&
+          len <= static_cast<int64_t>(max_blocks) * kBlock)
+        tables[t * max_blocks + (len - 1) / kBlock] = sl / kBlock;
+    }
+  }
   cw_tile<NewT, CacheT, D, true>(r % ntb, r / ntb, k_new, v_new, slots_host, n, k_cache, v_cache,
                                  num_blocks, H_kv, k_inv, v_inv);
 }
@@ -198,11 +214,19 @@ static pa_status cw_check(const char* who, const void* k_new, const void* v_new,
   return PA_OK;
 }
 
+// Block-table upkeep of a decode batch (pa_stage_decode_append); none for
+// pa_stage_cache_write.
+struct TableUpkeep {
+  int32_t* tables = nullptr;
+  int32_t max_blocks = 0;
+  const int32_t* lens_dev = nullptr;
+};
+
 template <typename NewT, typename CacheT, int D, typename W>
 static pa_status launch_scw(hipStream_t st, void* dst, const void* src_dev, size_t bytes,
                             const int32_t* slots_dev, const void* k_new, const void* v_new,
                             int32_t n, void* k_cache, void* v_cache, int32_t num_blocks,
-                            int32_t H_kv, float k_inv, float v_inv) {
+                            int32_t H_kv, float k_inv, float v_inv, const TableUpkeep& tu) {
   const int64_t n_words = static_cast<int64_t>(bytes / sizeof(W));
   const int sgroups = stage_groups(n_words);
   const int64_t grid = sgroups + static_cast<int64_t>((n + 15) / 16) * H_kv;
@@ -216,7 +240,7 @@ static pa_status launch_scw(hipStream_t st, void* dst, const void* src_dev, size
                         static_cast<const typename NewT::raw*>(v_new), slots_dev, n,
                         static_cast<typename CacheT::raw*>(k_cache),
                         static_cast<typename CacheT::raw*>(v_cache), num_blocks, H_kv, k_inv,
-                        v_inv);
+                        v_inv, tu.tables, tu.max_blocks, tu.lens_dev);
   if (e != hipSuccess)
     return fail(PA_ERR_DEVICE, "pa_stage_cache_write: launch failed: %s", hipGetErrorString(e));
   return PA_OK;
@@ -226,27 +250,30 @@ template <typename NewT, typename CacheT, typename W>
 static pa_status launch_scw_d(int32_t D, hipStream_t st, void* dst, const void* src_dev,
                               size_t bytes, const int32_t* slots_dev, const void* k_new,
                               const void* v_new, int32_t n, void* k_cache, void* v_cache,
-                              int32_t num_blocks, int32_t H_kv, float k_inv, float v_inv) {
+                              int32_t num_blocks, int32_t H_kv, float k_inv, float v_inv,
+                              const TableUpkeep& tu) {
   if (D == 128)
     return launch_scw<NewT, CacheT, 128, W>(st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
-                                            k_cache, v_cache, num_blocks, H_kv, k_inv, v_inv);
+                                            k_cache, v_cache, num_blocks, H_kv, k_inv, v_inv, tu);
   return launch_scw<NewT, CacheT, 64, W>(st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
-                                         k_cache, v_cache, num_blocks, H_kv, k_inv, v_inv);
+                                         k_cache, v_cache, num_blocks, H_kv, k_inv, v_inv, tu);
 }
 
 template <typename W>
 static pa_status launch_scw_types(const CwPlan& plan, int32_t D, hipStream_t st, void* dst,
                                   const void* src_dev, size_t bytes, const int32_t* slots_dev,
                                   const void* k_new, const void* v_new, int32_t n, void* k_cache,
-                                  void* v_cache, int32_t num_blocks, int32_t H_kv) {
+                                  void* v_cache, int32_t num_blocks, int32_t H_kv,
+                                  const TableUpkeep& tu) {
   if (plan.combo == 0)
     return launch_scw_d<F32, F32, W>(D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
-                                     k_cache, v_cache, num_blocks, H_kv, 1.f, 1.f);
+                                     k_cache, v_cache, num_blocks, H_kv, 1.f, 1.f, tu);
   if (plan.combo == 1)
     return launch_scw_d<BF16, BF16, W>(D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
-                                       k_cache, v_cache, num_blocks, H_kv, 1.f, 1.f);
+                                       k_cache, v_cache, num_blocks, H_kv, 1.f, 1.f, tu);
   return launch_scw_d<BF16, FP8, W>(D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
-                                    k_cache, v_cache, num_blocks, H_kv, plan.k_inv, plan.v_inv);
+                                    k_cache, v_cache, num_blocks, H_kv, plan.k_inv, plan.v_inv,
+                                    tu);
 }
 
 }  // namespace pa
@@ -275,43 +302,87 @@ extern "C" pa_status pa_cache_write(void* stream, const void* k_new, const void*
                                        num_blocks, H_kv, D, plan.k_inv, plan.v_inv);
 }
 
+namespace pa {
+
+static pa_status stage_cache_write_impl(const char* who, void* stream, void* dst,
+                                        const void* src_host, size_t bytes, size_t slot_offset,
+                                        const void* k_new, const void* v_new, pa_dtype new_dt,
+                                        int32_t n, void* k_cache, void* v_cache,
+                                        pa_dtype cache_dt, int32_t num_blocks, int32_t H_kv,
+                                        int32_t D, int32_t bs, float k_scale, float v_scale,
+                                        const size_t* lens_offset, int32_t* block_tables,
+                                        int32_t max_blocks) {
+  CwPlan plan;
+  const pa_status chk = cw_check(who, k_new, v_new, new_dt, n, k_cache, v_cache, cache_dt,
+                                 num_blocks, H_kv, D, bs, k_scale, v_scale, &plan);
+  if (chk != PA_OK) return chk;
+  if (bytes % 4 != 0 || slot_offset % 4 != 0 || reinterpret_cast<uintptr_t>(dst) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(src_host) % 4 != 0)
+    return fail(PA_ERR_INVALID,
+                "%s: bytes=%zu, slot_offset=%zu and both addresses must be multiples of 4", who,
+                bytes, slot_offset);
+  if (n > 0 && (slot_offset > bytes || (bytes - slot_offset) / 4 < static_cast<size_t>(n)))
+    return fail(PA_ERR_INVALID, "%s: %d slots at byte %zu do not fit the %zu-byte buffer", who, n,
+                slot_offset, bytes);
+  if (lens_offset) {
+    if (*lens_offset % 4 != 0)
+      return fail(PA_ERR_INVALID, "%s: lens_offset=%zu must be a multiple of 4", who,
+                  *lens_offset);
+    if (n > 0 && (*lens_offset > bytes || (bytes - *lens_offset) / 4 < static_cast<size_t>(n)))
+      return fail(PA_ERR_INVALID, "%s: %d lengths at byte %zu do not fit the %zu-byte buffer",
+                  who, n, *lens_offset, bytes);
+    if (max_blocks < 1) return fail(PA_ERR_INVALID, "%s: max_blocks=%d < 1", who, max_blocks);
+    if (n > 0 && !block_tables) return fail(PA_ERR_INVALID, "%s: NULL block_tables", who);
+  }
+  if (bytes == 0) return PA_OK;  // and n == 0
+  if (!dst || !src_host) return fail(PA_ERR_INVALID, "%s: NULL buffer", who);
+  void* src_dev = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&src_dev, const_cast<void*>(src_host), 0);
+  if (e != hipSuccess || !src_dev) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID, "%s: source is not pinned host memory (%s)", who,
+                hipGetErrorString(e));
+  }
+  const int32_t* slots_dev =
+      reinterpret_cast<const int32_t*>(static_cast<const char*>(src_dev) + slot_offset);
+  TableUpkeep tu;
+  if (lens_offset && n > 0) {
+    tu.tables = block_tables;
+    tu.max_blocks = max_blocks;
+    tu.lens_dev =
+        reinterpret_cast<const int32_t*>(static_cast<const char*>(src_dev) + *lens_offset);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (bytes % 8 == 0 && reinterpret_cast<uintptr_t>(dst) % 8 == 0 &&
+      reinterpret_cast<uintptr_t>(src_dev) % 8 == 0)
+    return launch_scw_types<uint64_t>(plan, D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
+                                      k_cache, v_cache, num_blocks, H_kv, tu);
+  return launch_scw_types<uint32_t>(plan, D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
+                                    k_cache, v_cache, num_blocks, H_kv, tu);
+}
+
+}  // namespace pa
+
 extern "C" pa_status pa_stage_cache_write(void* stream, void* dst, const void* src_host,
                                           size_t bytes, size_t slot_offset, const void* k_new,
                                           const void* v_new, pa_dtype new_dt, int32_t n,
                                           void* k_cache, void* v_cache, pa_dtype cache_dt,
                                           int32_t num_blocks, int32_t H_kv, int32_t D, int32_t bs,
                                           float k_scale, float v_scale) {
-  CwPlan plan;
-  const pa_status chk = cw_check("pa_stage_cache_write", k_new, v_new, new_dt, n, k_cache,
-                                 v_cache, cache_dt, num_blocks, H_kv, D, bs, k_scale, v_scale,
-                                 &plan);
-  if (chk != PA_OK) return chk;
-  if (bytes % 4 != 0 || slot_offset % 4 != 0 || reinterpret_cast<uintptr_t>(dst) % 4 != 0 ||
-      reinterpret_cast<uintptr_t>(src_host) % 4 != 0)
-    return fail(PA_ERR_INVALID,
-                "pa_stage_cache_write: bytes=%zu, slot_offset=%zu and both addresses must be "
-                "multiples of 4",
-                bytes, slot_offset);
-  if (n > 0 && (slot_offset > bytes || (bytes - slot_offset) / 4 < static_cast<size_t>(n)))
-    return fail(PA_ERR_INVALID,
-                "pa_stage_cache_write: %d slots at byte %zu do not fit the %zu-byte buffer", n,
-                slot_offset, bytes);
-  if (bytes == 0) return PA_OK;  // and n == 0
-  if (!dst || !src_host) return fail(PA_ERR_INVALID, "pa_stage_cache_write: NULL buffer");
-  void* src_dev = nullptr;
-  hipError_t e = hipHostGetDevicePointer(&src_dev, const_cast<void*>(src_host), 0);
-  if (e != hipSuccess || !src_dev) {
-    (void)hipGetLastError();
-    return fail(PA_ERR_INVALID, "pa_stage_cache_write: source is not pinned host memory (%s)",
-                hipGetErrorString(e));
-  }
-  const int32_t* slots_dev =
-      reinterpret_cast<const int32_t*>(static_cast<const char*>(src_dev) + slot_offset);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (bytes % 8 == 0 && reinterpret_cast<uintptr_t>(dst) % 8 == 0 &&
-      reinterpret_cast<uintptr_t>(src_dev) % 8 == 0)
-    return launch_scw_types<uint64_t>(plan, D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
-                                      k_cache, v_cache, num_blocks, H_kv);
-  return launch_scw_types<uint32_t>(plan, D, st, dst, src_dev, bytes, slots_dev, k_new, v_new, n,
-                                    k_cache, v_cache, num_blocks, H_kv);
+  return stage_cache_write_impl("pa_stage_cache_write", stream, dst, src_host, bytes,
+                                slot_offset, k_new, v_new, new_dt, n, k_cache, v_cache, cache_dt,
+                                num_blocks, H_kv, D, bs, k_scale, v_scale, nullptr, nullptr, 0);
+}
+
+extern "C" pa_status pa_stage_decode_append(void* stream, void* dst, const void* src_host,
+                                            size_t bytes, size_t slot_offset, size_t lens_offset,
+                                            const void* k_new, const void* v_new, pa_dtype new_dt,
+                                            int32_t n, void* k_cache, void* v_cache,
+                                            pa_dtype cache_dt, int32_t num_blocks, int32_t H_kv,
+                                            int32_t D, int32_t bs, float k_scale, float v_scale,
+                                            int32_t* block_tables, int32_t max_blocks) {
+  return stage_cache_write_impl("pa_stage_decode_append", stream, dst, src_host, bytes,
+                                slot_offset, k_new, v_new, new_dt, n, k_cache, v_cache, cache_dt,
+                                num_blocks, H_kv, D, bs, k_scale, v_scale, &lens_offset,
+                                block_tables, max_blocks);
 }

@@ -145,3 +145,77 @@ def test_stage_cache_write_rejects_bad_arguments():
     pageable = np.zeros(64, dtype=np.int32)
     assert lib.pa_stage_cache_write(None, fake, pageable.ctypes.data, 64, 0, fake, fake, 1, 1,
                                     fake, fake, 1, 10, 2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
+
+
+@pytest.mark.parametrize("cache_dt,d", [("bf16", 128), ("fp8", 128), ("bf16", 64)])
+def test_stage_decode_append_keeps_device_tables(cache_dt, d):
+    """Decode iterations whose block tables stay on the device: after every
+    iteration each row equals the allocator's table (pa_pack_batch) entry for
+    entry over its context, and the cache bytes and the staged copy equal
+    those of pa_stage_cache_write on the same data.  Contexts start at and
+    around block boundaries; one iteration carries a slot outside the pool
+    and a length beyond the row, which leave their rows unchanged."""
+    from paged_kv_cache_host_amd.engine import _TORCH_STORAGE
+    rng = np.random.default_rng(911)
+    S, h_kv, steps = 37, 2, 40
+    lengths = rng.integers(1, 70, size=S)
+    lengths[:5] = [16, 32, 1, 15, 17]
+    MB = int(-(-(lengths.max() + steps) // 16))
+    nb = int(sum(-(-(L + steps) // 16) for L in lengths)) + 8
+    st_, pool = pa.pa_pool_create(nb, 16, rng.permutation(nb).astype(np.int32))
+    assert st_ == pa.PA_OK
+    seqs = np.arange(S, dtype=np.int64)
+    try:
+        for s, L in enumerate(lengths):
+            assert pa.pa_seq_create(pool, s, int(L) - 1) == pa.PA_OK
+        st_, tab0, lens = pa.pa_pack_batch(pool, seqs, MB)
+        assert st_ == pa.PA_OK
+        d_tab = torch.from_numpy(tab0.copy()).to(DEV)
+        cdt = _TORCH_STORAGE[cache_dt]
+        x = 16 // torch.empty((), dtype=cdt).element_size()
+        caches = [(torch.zeros((nb, h_kv, d // x, 16, x), dtype=cdt, device=DEV),
+                   torch.zeros((nb, h_kv, d, 16), dtype=cdt, device=DEV)) for _ in range(2)]
+        host = torch.empty(2 * S + 3, dtype=torch.int32, pin_memory=True)
+        h = host.numpy()
+        g = torch.Generator(device=DEV)
+        g.manual_seed(912)
+        say(f"[stage_decode_append] {cache_dt} d{d} S={S} steps={steps} max_blocks={MB}")
+        for it in range(steps):
+            st_, done, slots = pa.pa_batch_append(pool, seqs, 1)
+            assert st_ == pa.PA_OK and done == S
+            lens = lens + 1
+            h[:S] = slots[:, 0]
+            h[S:2 * S] = lens
+            h[2 * S:] = it
+            edge = it == steps // 2
+            if edge:
+                h[5] = nb * 16 + 3        # slot outside the pool: row 5 unchanged
+                h[S + 6] = MB * 16 + 1    # length beyond the row: row 6 unchanged
+            before = d_tab.cpu()
+            kn = torch.randn((S, h_kv, d), generator=g, device=DEV).to(torch.bfloat16)
+            vn = torch.randn((S, h_kv, d), generator=g, device=DEV).to(torch.bfloat16)
+            dsts = [torch.full((2 * S + 5,), -7, dtype=torch.int32, device=DEV) for _ in range(2)]
+            assert pa.pa_stage_cache_write(None, dsts[0], host, 4 * (2 * S + 3), 0, S, kn, vn,
+                                           caches[0][0], caches[0][1], nb, h_kv, d, 16, 0.03,
+                                           0.05) == 0
+            assert pa.pa_stage_decode_append(None, dsts[1], host, 4 * (2 * S + 3), 0, 4 * S, S,
+                                             kn, vn, caches[1][0], caches[1][1], nb, h_kv, d,
+                                             d_tab, 16, 0.03, 0.05) == 0
+            torch.cuda.synchronize()
+            assert torch.equal(dsts[0].cpu(), dsts[1].cpu())
+            for a, b in zip(caches[0], caches[1]):
+                assert torch.equal(a.view(torch.uint8).cpu(), b.view(torch.uint8).cpu())
+            got = d_tab.cpu().numpy()
+            st_, ref, _ = pa.pa_pack_batch(pool, seqs, MB)
+            assert st_ == pa.PA_OK
+            for i in range(S):
+                nblk = -(-int(lens[i]) // 16)
+                if edge and i in (5, 6):
+                    assert np.array_equal(got[i], before[i].numpy()), (it, i)
+                    got[i, :nblk] = ref[i, :nblk]      # the host repairs the row
+                    d_tab[i] = torch.from_numpy(ref[i].copy()).to(DEV)
+                assert np.array_equal(got[i, :nblk], ref[i, :nblk]), (it, i)
+                # entries past the context are never written
+                assert np.array_equal(got[i, nblk:], tab0[i, nblk:]), (it, i)
+    finally:
+        pa.pa_pool_destroy(pool)

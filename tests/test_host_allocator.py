@@ -10,6 +10,7 @@ import pytest
 from hypothesis import given, settings, strategies as st
 
 import paged_kv_cache_host_amd as pa
+import paged_kv_cache_host_amd._pa  # noqa: F401  (pa._pa: library path and handle)
 from oracle import allocator as oa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -219,6 +220,35 @@ def test_stage_cache_write_argument_checks_on_host():
                                     2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
     assert lib.pa_stage_cache_write(None, fake, fake, 0, 0, fake, fake, 1, 0, fake, fake, 1, 10,
                                     2, 64, 16, 1.0, 1.0) == 0          # nothing to do
+
+
+def test_stage_decode_append_argument_checks_on_host():
+    fake = 0x1000
+    lib = pa._pa._lib
+    # (stream, dst, src, bytes, slot_off, lens_off, k, v, new_dt, n, kc, vc, cache_dt,
+    #  num_blocks, H_kv, D, bs, k_scale, v_scale, tables, max_blocks)
+    ok = [None, fake, fake, 64, 0, 16, fake, fake, 1, 4, fake, fake, 1, 10, 2, 64, 16, 1.0, 1.0,
+          fake, 8]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["stream", "dst", "src", "nbytes", "slot_off", "lens_off", "k", "v", "new_dt", "n",
+                 "kc", "vc", "cache_dt", "num_blocks", "h_kv", "d", "bs", "k_scale", "v_scale",
+                 "tables", "max_blocks"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return lib.pa_stage_decode_append(*args)
+
+    # all rejected before any HIP call
+    assert call(lens_off=6) == pa.PA_ERR_INVALID                 # misaligned lengths
+    assert call(lens_off=56) == pa.PA_ERR_INVALID                # 4 lengths do not fit 64 bytes
+    assert "do not fit" in pa.pa_last_error()
+    assert call(max_blocks=0) == pa.PA_ERR_INVALID
+    assert call(tables=None) == pa.PA_ERR_INVALID
+    assert "block_tables" in pa.pa_last_error()
+    assert call(bs=8) == pa.PA_ERR_INVALID                       # as pa_stage_cache_write
+    assert call(slot_off=52) == pa.PA_ERR_INVALID
+    assert call(nbytes=0, n=0) == 0                              # nothing to do
 
 
 def test_prefix_sharing_golden_trace_through_c_abi():
