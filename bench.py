@@ -66,6 +66,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--overlap", action="store_true",
+                    help="decode step: the append launch on a second stream")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
@@ -333,6 +335,12 @@ def decode_leg(args, dev):
         h, d_ = host_buf[X].numpy(), dev_buf[X]
         views.append((h[:S].reshape(S, 1), h[S:2 * S], d_[S:2 * S]))
     compute = torch.cuda.Stream(device=dev)
+    # With --overlap the append launch runs on a stream of its own, so that
+    # step i+1's launch overlaps step i's decode: it writes only slots past
+    # step i's contexts and table entries step i does not read (or rewrites
+    # one with its own value), and the decode of step i+1 waits for it.
+    aux = torch.cuda.Stream(device=dev) if getattr(args, "overlap", False) else compute
+    ev_w = [torch.cuda.Event() for _ in range(2)]
     ev_group = [torch.cuda.Event() for _ in range(2)]
     for e in ev_group:
         e.record(compute)
@@ -353,9 +361,12 @@ def decode_leg(args, dev):
         r = i % R
         # one launch stages the buffer, scatters the new tokens (whose slots
         # lead the buffer) and enters the blocks they open in the tables
-        pa.check(pa.pa_stage_decode_append(compute, dev_buf[X], host_buf[X], 4 * n_meta, 0, 4 * S,
+        pa.check(pa.pa_stage_decode_append(aux, dev_buf[X], host_buf[X], 4 * n_meta, 0, 4 * S,
                                            S, k_ring[r], v_ring[r], kv.k, kv.v, num_blocks, H_KV,
                                            D, d_tab, BLOCK))
+        if aux is not compute:
+            ev_w[i % 2].record(aux)
+            compute.wait_event(ev_w[i % 2])
         pa.check(pa.pa_decode(compute, out, q_ring[r], kv.k, kv.v, d_tab, d_lens,
                               num_blocks, H_KV, max_ctx, sm, 1.0, 1.0, ws))
         if timed:
