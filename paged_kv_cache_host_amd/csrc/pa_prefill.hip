@@ -44,7 +44,7 @@
 // quads swapped; with that permutation the 8 keys a lane holds for each
 // 16-key step of P^T are consecutive, which is what one 16-byte read of the
 // token-minor V layout supplies.
-#include <utility>
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -68,7 +68,7 @@ constexpr int kPfKeys = 64;                 // keys per LDS tile (4 blocks)
 constexpr int kPfTargetGroups = 256;        // one work-group per compute unit
 constexpr int kPfMaxSplit = 8;
 constexpr int kPfMinKeysPerSplit = 1024;
-constexpr float kPfLazy = 8.0f;             // log2 headroom of the softmax reference
+constexpr float kPfSafe = 32768.0f;         // bound on a lane's 32 weights of one tile
 
 // LDS bytes of one stage: K [D/8 chunks][64 rows][16 B] + V [D/16][8 chunks][16 dims][16 B].
 template <int D>
@@ -376,16 +376,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
   const int v_lane = v_off(col, g);
 
   // Software pipeline inside each wave.  Iteration t enters with the fp16
-  // weights P(t-1), the scores S(t) and the softmax reference for S(t)
-  // already settled.  One straight run of 32 MFMAs then computes
-  // S(t+1) = K(t+1) Q^T and O^T += V(t-1)^T P(t-1)^T; none of them waits
-  // for the vector work of the same iteration, which in between turns S(t)
-  // into P(t) and takes the row maxima of S(t+1).  The reference for S(t+1)
-  // is settled after the run; raising it rescales l at once and O^T one
-  // iteration later, once the product with P(t) (formed against the old
-  // reference) is in.  K/V tiles rotate through four LDS stages: tile t is
-  // stored during iteration t-2, read as K in iteration t-1 and as V in
-  // iteration t+1.
+  // weights P(t-1) and the scores S(t).  One straight run of 32 MFMAs then
+  // computes S(t+1) = K(t+1) Q^T and O^T += V(t-1)^T P(t-1)^T; none of them
+  // waits for the vector work of the same iteration, which in between turns
+  // S(t) into P(t) against the current softmax reference.  Only when P(t)
+  // would leave fp16 (checked on its row sums after the run, rare) is the
+  // reference raised and P(t) formed again.  K/V tiles rotate through four
+  // LDS stages: tile t is stored during iteration t-2, read as K in
+  // iteration t-1 and as V in iteration t+1.
   auto stage = [&](int t) { return smem + ((t - t0) & 3) * stage_bytes<D>(); };
   constexpr int NQK = 2 * NKS;       // S MFMAs per tile
   constexpr int NPV = 4 * NDT;       // O MFMAs per tile
@@ -431,6 +429,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
       }
   };
   // the score scale is positive, so maxima are taken on raw scores
+  // S^T of the 64 keys of a stage
+  auto qk_stage = [&](const uint8_t* k_lds, f32x16* s) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[h][j] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            k_lds + (2 * ks + g) * (kPfKeys * 16) + (32 * h + col) * 16);
+        s[h] = mfma32x32x16(a, qf[ks], s[h]);
+      }
+    }
+  };
   auto half_max = [&](const f32x16& s) {
     // scores are never NaN: plain three-way maxima, no quieting
     float m;
@@ -441,24 +453,47 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
     asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(m), "v"(s[15]));
     return m;
   };
-  float mu = 0.f;                    // reference the exponentials of S(t) use
-  bool carry = false;                // O^T still owes a rescale by alpha_c
-  float alpha_c = 1.f;
-  // settle the reference for scores whose lane maximum (raw) is mx
-  auto settle = [&](float mx) {
+  // The softmax reference m_run (log2 domain) starts at the maximum of the
+  // first tile and is raised only when a tile's weights would leave fp16:
+  // a lane whose 32 weights of a tile sum beyond kPfSafe (or overflow).
+  // Any reference gives the same normalised result; this one never lies
+  // above the running maximum, so the largest weight seen so far is >= 1.
+  float mu = 0.f;                    // reference the exponentials use
+  // lane maximum of raw scores -> the query's maximum, scaled
+  auto query_max = [&](const f32x16* s) {
+    const float mx = fmaxf(half_max(s[0]), half_max(s[1]));
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                      false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * score_scale;
-    const bool raise = __builtin_amdgcn_ballot_w64(mx > m_run + kPfLazy) != 0;
-    float alpha = 1.f;
-    if (raise) {
-      const float m_new = fmaxf(m_run, mx);
-      alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
-    }
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * score_scale;
+  };
+  // raise the reference to m_new (>= m_run), rescaling l and O^T
+  auto raise_to = [&](float m_new) {
+    const float alpha =
+        m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int n = 0; n < NDT; ++n)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[n][j] *= alpha;
+    m_run = m_new;
     mu = m_run == -__builtin_inff() ? 0.f : m_run;
-    return std::pair<bool, float>(raise, alpha);
+  };
+  // fp16 weights of S (32 per lane) against mu, and their sum
+  auto weights = [&](const f32x16* s, f16x8* p) {
+    const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; e += 2) {
+      const int u = e >> 3, i8 = e & 7;
+      const f16x2 h2 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(
+                            __builtin_fmaf(s[u >> 1][8 * (u & 1) + i8], score_scale, -mu))),
+                        static_cast<_Float16>(__builtin_amdgcn_exp2f(
+                            __builtin_fmaf(s[u >> 1][8 * (u & 1) + i8 + 1], score_scale, -mu)))};
+      p[u][i8] = h2[0];
+      p[u][i8 + 1] = h2[1];
+      sum = __builtin_amdgcn_fdot2(h2, ones, sum, false);
+    }
+    return sum;
   };
 
   // One iteration.  sc: S(t) in, sn: S(t+1) out, pp: P(t-1) in, pn: P(t) out.
@@ -488,7 +523,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
 #pragma unroll
     for (int i = 0; i < PD; ++i) opnd[i] = operand(i);
     const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-    float mx = -__builtin_inff();
+    float l_tile = 0.f;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       if (i + PD < NM) opnd[(i + PD) % (PD + 1)] = operand(i + PD);
@@ -515,39 +550,30 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
           asm volatile("" : "+v"(h2));
           pn[u][i8] = h2[0];
           pn[u][i8 + 1] = h2[1];
-          l_run = __builtin_amdgcn_fdot2(h2, ones, l_run, false);
-          asm volatile("" : "+v"(l_run));
+          l_tile = __builtin_amdgcn_fdot2(h2, ones, l_tile, false);
+          asm volatile("" : "+v"(l_tile));
         }
       } else {
         const int j = i - NQK;
         o[j % NDT] = mfma32x32x16(__builtin_bit_cast(f16x8, opnd[i % (PD + 1)]), pp[j / NDT],
                                   o[j % NDT]);
-        // S(t+1) is complete two slots after its last MFMA: mask it (where
-        // it reaches the diagonal) and take its lane maximum
-        if (j == 1) {
-          if constexpr (decltype(masked_next)::value) mask_scores(sn, t + 1);
-          mx = half_max(sn[0]);
-          asm volatile("" : "+v"(mx));
-        }
-        if (j == NPV / 2) {
-          mx = fmaxf(mx, half_max(sn[1]));
-          asm volatile("" : "+v"(mx));
-        }
+        // S(t+1) is complete two slots after its last MFMA: mask it where
+        // it reaches the diagonal
+        if constexpr (decltype(masked_next)::value)
+          if (j == 1) mask_scores(sn, t + 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the rescale owed since the last iteration applies to O^T as it
-    // stands now, P(t-1) included
-    if (carry) {
-#pragma unroll
-      for (int n = 0; n < NDT; ++n)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[n][j] *= alpha_c;
+    // P(t) left fp16 (rare: S(t) far above the reference): recompute S(t)
+    // from tile t's K, still in its stage, raise the reference to its
+    // maximum (O^T holds P(t-1) V(t-1) by now) and form P(t) again
+    if (__builtin_amdgcn_ballot_w64(!(l_tile <= kPfSafe)) != 0) {
+      qk_stage(stage(t), sc);
+      if (t * kPfKeys + kPfKeys - 1 > wave_first_pos) mask_scores(sc, t);
+      raise_to(fmaxf(m_run, query_max(sc)));
+      l_tile = weights(sc, pn);
     }
-    // the last tile has no successor: its S(t+1) is a stand-in
-    const auto ra = settle(t + 1 < t1 ? mx : -__builtin_inff());
-    carry = ra.first;
-    alpha_c = ra.second;
+    l_run += l_tile;
     // V of keys past the context must be zero, not stale cache bits
     const int valid_st = kv_end - min(t + 2, t1 - 1) * kPfKeys;
     if (valid_st < kPfKeys) zero_v_tail(st_lds + D * kPfKeys * 2, valid_st);
@@ -574,20 +600,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int i = 0; i < 8; ++i) pA[u][i] = static_cast<_Float16>(0.0f);
-    // S(t0) and its reference
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sA[h][j] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            stage(t0) + (2 * ks + g) * (kPfKeys * 16) + (32 * h + col) * 16);
-        sA[h] = mfma32x32x16(a, qf[ks], sA[h]);
-      }
-    }
+    // S(t0) and the first reference, its maximum
+    qk_stage(stage(t0), sA);
     if (t0 * kPfKeys + kPfKeys - 1 > wave_first_pos) mask_scores(sA, t0);
-    settle(fmaxf(half_max(sA[0]), half_max(sA[1])));
+    m_run = query_max(sA);
+    mu = m_run == -__builtin_inff() ? 0.f : m_run;
     // iteration t masks S(t+1) when tile t+1 reaches past the wave's first
     // position, i.e. from tile t_mask on
     const int t_mask = (wave_first_pos + 1) / kPfKeys;

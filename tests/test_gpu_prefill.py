@@ -46,6 +46,18 @@ def test_slices_fp8():
     _check(w, "fp8 cache")
 
 
+@pytest.mark.parametrize("prompt,chunks,h_q,h_kv,ramp",
+                         [(700, [300, 400], 16, 2, 10.0), (2900, [2600, 300], 64, 8, 3.0)])
+def test_slices_rising_scores(prompt, chunks, h_q, h_kv, ramp):
+    """Scores that climb by `ramp` powers of two per 64 keys: each new tile
+    outweighs the softmax reference taken so far, so the kernel keeps
+    raising it (and rescaling what it has accumulated); the second case also
+    splits the key range of the last slice."""
+    w = workloads.prefill_workload("rising", 560 + prompt, prompt_len=prompt, chunks=chunks,
+                                   h_q=h_q, h_kv=h_kv, score_ramp=ramp)
+    _check(w, f"scores rising {ramp} per tile")
+
+
 def test_slices_f32():
     w = workloads.prefill_workload("f32", 530, prompt_len=150, chunks=[64, 86], h_q=4, h_kv=4, d=64,
                                    dtype="f32", cache_dtype="f32")

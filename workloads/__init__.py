@@ -288,9 +288,15 @@ class PrefillWorkload:
 def prefill_workload(name: str, seed: int, prompt_len: int | None = None, chunks=None,
                      prompts=None, slices=None, h_q: int = 64, h_kv: int = 8, d: int = 128,
                      dtype: str = "bf16", cache_dtype: str = "bf16",
-                     extra_blocks: int = 9) -> PrefillWorkload:
+                     extra_blocks: int = 9, score_ramp: float = 0.0) -> PrefillWorkload:
     """Either one prompt of ``prompt_len`` tokens cut into ``chunks`` (sizes),
-    or several ``prompts`` with explicit ``slices``."""
+    or several ``prompts`` with explicit ``slices``.
+
+    ``score_ramp`` > 0 (bf16 only): scores that climb along each prompt by
+    about that many powers of two per 64 keys.  Every query of a KV head's
+    group is one direction u (|u|^2 = d) plus noise, the key at position p
+    is c(p) u plus noise with c(p) growing by one step per 64 positions, so
+    each new tile outweighs the ones before it."""
     if prompts is None:
         prompts = [prompt_len]
         slices = []
@@ -309,6 +315,19 @@ def prefill_workload(name: str, seed: int, prompt_len: int | None = None, chunks
     v_tok = normal_raw(rng, (ntok, h_kv, d), kvd)
     q_dtype = "bf16" if cache_dtype == "fp8" else dtype
     q_tok = normal_raw(rng, (ntok, h_q, d), q_dtype)
+    if score_ramp > 0:
+        assert dtype == "bf16" and cache_dtype == "bf16"
+        u = rng.standard_normal((h_kv, d)).astype(np.float32)
+        u *= np.float32(math.sqrt(d)) / np.linalg.norm(u, axis=1, keepdims=True)
+        step = score_ramp / (math.sqrt(d) * math.log2(math.e))   # c(p) per 64 keys
+        pos = np.concatenate([np.arange(int(n)) for n in prompts])
+        c = (step * (pos // 64)).astype(np.float32)
+        kf = c[:, None, None] * u[None] + \
+            np.float32(0.1) * rng.standard_normal((ntok, h_kv, d), dtype=np.float32)
+        qf = np.repeat(u, h_q // h_kv, axis=0)[None] + \
+            np.float32(0.1) * rng.standard_normal((ntok, h_q, d), dtype=np.float32)
+        k_tok = to_bf16_bits(kf.astype(np.float32))
+        q_tok = to_bf16_bits(qf.astype(np.float32))
     w = PrefillWorkload(name, prompts, list(slices), num_blocks, free_order, h_q, h_kv, d, kvd,
                         cache_dtype, q_dtype, k_tok, v_tok, q_tok, sm_scale=_sm_scale(d))
     if cache_dtype == "fp8":
