@@ -51,6 +51,19 @@ def _check_full(w, what):
     hip["kv"].close()
 
 
+@pytest.mark.parametrize("h_q,h_kv", [(16, 2), (64, 8)])
+def test_rising_scores_bf16(h_q, h_kv):
+    """Scores that climb about 8 powers of two per 64 keys: every step of a
+    context outweighs the running maximum, so each wave keeps raising its
+    reference, and the waves' and chunks' states merge across far apart
+    maxima (the 2500-token context spans two work items)."""
+    lengths = np.array([1, 63, 64, 700, 2500, 130], dtype=np.int64)
+    w = workloads.decode_workload(
+        f"rising-{h_q}q{h_kv}kv", 913 + h_q, lambda rng: lengths, h_q, h_kv, 128, "bf16", "bf16",
+        lambda L: workloads.blocks_needed(L) + 7, score_ramp=8.0)
+    _check_full(w, "scores rising 8 per 64 keys")
+
+
 def test_tiny_decode_f32():
     _check_full(workloads.tiny_decode(), "tiny fp32")
 

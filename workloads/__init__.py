@@ -103,19 +103,45 @@ def decode_layout(seed, lengths_fn, pool_fn):
 
 
 def decode_workload(name, seed, lengths_fn, h_q, h_kv, d, kv_dtype, cache_dtype,
-                    pool_fn, q_dtype=None) -> DecodeWorkload:
+                    pool_fn, q_dtype=None, score_ramp: float = 0.0) -> DecodeWorkload:
+    """``score_ramp`` > 0 (bf16 only): each query's scores climb along its
+    context by about that many powers of two per 64 keys (the construction
+    of ``prefill_workload``)."""
     rng, lengths, num_blocks, free_order = decode_layout(seed, lengths_fn, pool_fn)
     ntok = int(lengths.sum())
     k_tok = normal_raw(rng, (ntok, h_kv, d), kv_dtype)
     v_tok = normal_raw(rng, (ntok, h_kv, d), kv_dtype)
     q_dtype = q_dtype or kv_dtype
     q = normal_raw(rng, (len(lengths), h_q, d), q_dtype)
+    if score_ramp > 0:
+        assert kv_dtype == "bf16" and cache_dtype == "bf16" and q_dtype == "bf16"
+        k_tok, q = _ramped(rng, [int(x) for x in lengths], len(lengths), h_q, h_kv, d,
+                           score_ramp)
     w = DecodeWorkload(name, lengths, num_blocks, free_order, h_q, h_kv, d, kv_dtype,
                        cache_dtype, q_dtype, k_tok, v_tok, q, sm_scale=_sm_scale(d))
     if cache_dtype == "fp8":
         w.k_scale = _amax_scale(k_tok)
         w.v_scale = _amax_scale(v_tok)
     return w
+
+
+def _ramped(rng, lengths, n_q: int, h_q: int, h_kv: int, d: int, ramp: float):
+    """Raw bf16 K rows of sequences of ``lengths`` (concatenated) and ``n_q``
+    raw bf16 Q rows whose scores climb along each sequence: every query of a
+    KV head's group is one direction u (|u|^2 = d) plus noise, the key at
+    position p is c(p) u plus noise, c(p) growing by ramp / (sqrt(d) log2 e)
+    per 64 positions (about ``ramp`` powers of two per 64 keys once scaled
+    by 1/sqrt(d))."""
+    u = rng.standard_normal((h_kv, d)).astype(np.float32)
+    u *= np.float32(math.sqrt(d)) / np.linalg.norm(u, axis=1, keepdims=True)
+    step = ramp / (math.sqrt(d) * math.log2(math.e))
+    pos = np.concatenate([np.arange(n) for n in lengths])
+    c = (step * (pos // 64)).astype(np.float32)
+    kf = c[:, None, None] * u[None] + \
+        np.float32(0.1) * rng.standard_normal((len(pos), h_kv, d), dtype=np.float32)
+    qf = np.repeat(u, h_q // h_kv, axis=0)[None] + \
+        np.float32(0.1) * rng.standard_normal((n_q, h_q, d), dtype=np.float32)
+    return to_bf16_bits(kf.astype(np.float32)), to_bf16_bits(qf.astype(np.float32))
 
 
 def blocks_needed(lengths) -> int:
@@ -317,17 +343,7 @@ def prefill_workload(name: str, seed: int, prompt_len: int | None = None, chunks
     q_tok = normal_raw(rng, (ntok, h_q, d), q_dtype)
     if score_ramp > 0:
         assert dtype == "bf16" and cache_dtype == "bf16"
-        u = rng.standard_normal((h_kv, d)).astype(np.float32)
-        u *= np.float32(math.sqrt(d)) / np.linalg.norm(u, axis=1, keepdims=True)
-        step = score_ramp / (math.sqrt(d) * math.log2(math.e))   # c(p) per 64 keys
-        pos = np.concatenate([np.arange(int(n)) for n in prompts])
-        c = (step * (pos // 64)).astype(np.float32)
-        kf = c[:, None, None] * u[None] + \
-            np.float32(0.1) * rng.standard_normal((ntok, h_kv, d), dtype=np.float32)
-        qf = np.repeat(u, h_q // h_kv, axis=0)[None] + \
-            np.float32(0.1) * rng.standard_normal((ntok, h_q, d), dtype=np.float32)
-        k_tok = to_bf16_bits(kf.astype(np.float32))
-        q_tok = to_bf16_bits(qf.astype(np.float32))
+        k_tok, q_tok = _ramped(rng, [int(n) for n in prompts], ntok, h_q, h_kv, d, score_ramp)
     w = PrefillWorkload(name, prompts, list(slices), num_blocks, free_order, h_q, h_kv, d, kvd,
                         cache_dtype, q_dtype, k_tok, v_tok, q_tok, sm_scale=_sm_scale(d))
     if cache_dtype == "fp8":
