@@ -5,9 +5,11 @@ the iteration level", "Chunked prefill"): libpa's scheduler (pa_sched_step)
 grows the decode-phase sequences by one token, admits and hands out prefill
 slices within the budget; the new tokens' K/V are scattered into the paged
 cache (pa_cache_write) and attention runs for the decode tokens (pa_decode)
-and the prefill slices (pa_prefill_chunk), all on one compute stream.  The
-host work of iteration t+1 (scheduling and table packing into
-double-buffered pinned memory) overlaps the kernels of iteration t; one
+and the prefill slices (pa_prefill_chunk), on one compute stream (or, with
+``two_streams``, the prefill beside the decode on a second stream that the
+compute stream waits for at the end of the iteration).  The
+host work of iteration t+1 (scheduling and table packing into a ring of
+pinned buffers) overlaps the kernels of the iterations before it; one
 pa_stage_cache_write launch on the compute stream then moves the packed
 metadata and scatters the new tokens' K/V.
 
@@ -33,7 +35,7 @@ class LayerIterations:
                  max_running: int = 256, prefill_budget: int = 512, max_context: int = 40960,
                  cache_blocks: int | None = None, cache_dtype: str = "bf16",
                  k_scale: float = 1.0, v_scale: float = 1.0, sm_scale: float | None = None,
-                 free_order=None, provider_syncs: bool = True):
+                 free_order=None, provider_syncs: bool = True, two_streams: bool = False):
         self.h_q, self.h_kv, self.d = h_q, h_kv, d
         self.dev = torch.device(device)
         self.provider = provider
@@ -80,6 +82,12 @@ class LayerIterations:
                 for c in range(1, max_running + 1))
         self.ws_pf = torch.empty(max(n, 1), dtype=torch.uint8, device=self.dev)
         self.compute = torch.cuda.Stream(device=self.dev)
+        # two_streams: the prefill slices run on a second stream, after the
+        # staging launch and beside the decode, and the compute stream waits
+        # for them before the iteration ends (two events per iteration)
+        self.side = torch.cuda.Stream(device=self.dev) if two_streams else None
+        self.ev_staged = torch.cuda.Event()
+        self.ev_prefilled = torch.cuda.Event()
         self.ev_group = [torch.cuda.Event() for _ in range(2)]
         for e in self.ev_group:
             e.record(self.compute)
@@ -194,7 +202,14 @@ class LayerIterations:
         else:
             pa.check(pa.pa_stage(c, dvb, self.host_buf[X], 4 * off))
         if n_pf:
-            pa.check(pa.pa_prefill_chunk(c, self.out_pf[O][:n_pt], q_new[:n_pt], d_pm[:n_pf + 1],
+            pf_stream = c
+            if self.side is not None:
+                self.ev_staged.record(c)
+                self.side.wait_event(self.ev_staged)
+                pf_stream = self.side
+                if self.provider_syncs:
+                    q_new.record_stream(pf_stream)
+            pa.check(pa.pa_prefill_chunk(pf_stream, self.out_pf[O][:n_pt], q_new[:n_pt], d_pm[:n_pf + 1],
                                          d_pm[n_pf + 1:], self.k, self.v, d_pt.view(n_pf, mbp),
                                          self.cache_blocks, self.h_kv, int(pl.max()),
                                          int((pst + pl).max()), self.sm, self.k_scale,
@@ -204,6 +219,10 @@ class LayerIterations:
                                   d_dt.view(n_dec, mbd), d_dl, self.cache_blocks, self.h_kv,
                                   int(dp.max()) + 1, self.sm, self.k_scale, self.v_scale,
                                   self.ws_dec))
+        if n_pf and self.side is not None:
+            # the iteration ends on the compute stream with both kernels done
+            self.ev_prefilled.record(self.side)
+            c.wait_event(self.ev_prefilled)
         if self.it % self.GROUP == self.GROUP - 1:
             self.ev_group[g % 2].record(c)
         self._last = (record, self.out_dec[O][:n_dec], self.out_pf[O][:n_pt])

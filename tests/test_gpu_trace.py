@@ -132,7 +132,8 @@ def test_trace_iterations_match_oracle():
     assert run.totals["preempted"] > 0 and checked["decode"] > 50 and checked["prefill"] > 500
 
 
-def test_trace_iterations_pipelined_match_oracle():
+@pytest.mark.parametrize("two_streams", [False, True])
+def test_trace_iterations_pipelined_match_oracle(two_streams):
     """The host runs ahead of the kernels (metadata ring, one event per group
     of iterations, provider tensors already resident): outputs are copied on
     the compute stream, the written cache slots compared byte for byte at
@@ -141,7 +142,8 @@ def test_trace_iterations_pipelined_match_oracle():
     from paged_kv_cache_host_amd.iteration import LayerIterations
 
     w, host_rows, max_ctx = _trace()
-    say(f"[trace parity, pipelined] {w.name} pool={w.num_blocks} running<={R} budget={B}")
+    say(f"[trace parity, pipelined, two_streams={two_streams}] {w.name} pool={w.num_blocks} "
+        f"running<={R} budget={B}")
 
     def provider(seqs, positions):
         k, v, q = host_rows(seqs, positions)
@@ -151,7 +153,7 @@ def test_trace_iterations_pipelined_match_oracle():
         return out
 
     run = LayerIterations(w.num_blocks, H_Q, H_KV, D, "cuda", provider, R, B, max_context=max_ctx,
-                          provider_syncs=False)
+                          provider_syncs=False, two_streams=two_streams)
     copies = []
     for it in range(w.iters):
         for sid, p, o in w.arrivals[it]:
