@@ -365,9 +365,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
 
   const int32_t* table = block_tables + static_cast<int64_t>(c) * max_blocks;
   const int32_t n_blk = min((kv_end + kBlock - 1) / kBlock, max_blocks);
-  // Block ids are fetched two tiles ahead of their use by a vector load:
-  // lanes 0..3 take the tile's four entries (entries past the context
-  // repeat the last one), clamped into the pool.
+  // A tile's block ids are fetched by a vector load one iteration before
+  // its K/V loads are issued: lanes 0..3 take the tile's four entries
+  // (entries past the context repeat the last one), clamped into the pool.
   auto fetch_ids = [&](int t) -> int32_t {
     return safe_block(table[min(t * 4 + (lane & 3), n_blk - 1)], num_blocks);
   };
