@@ -740,27 +740,35 @@ def trace_leg(args, dev):
     """The continuous-batching trace: Poisson arrivals, lognormal prompts,
     geometric outputs, 256 running, 512-token prefill budget, 1000
     iterations of scheduling + cache write + decode/prefill attention for one
-    layer.  Reports tokens/s per layer and KV fragmentation."""
+    layer.  Reports tokens/s per layer, KV fragmentation and the requests'
+    time to first token and inter-token gaps (iteration clock x measured
+    iteration time)."""
     import torch
 
     import workloads
     from paged_kv_cache_host_amd import _pa as pa
-    from paged_kv_cache_host_amd.iteration import LayerIterations
+    from paged_kv_cache_host_amd.iteration import LatencyLog, LayerIterations
 
     w = workloads.trace()
     max_ctx = max(p + o for row in w.arrivals for _, p, o in row)
     # Host-only dry run of the same scheduler: the highest block id the trace
-    # touches (the FIFO pool hands out low ids first).
+    # touches (the FIFO pool hands out low ids first), and every request's
+    # token times on the iteration clock (the scheduler is deterministic, so
+    # the timed run makes the same decisions).
     st, pool = pa.pa_pool_create(w.num_blocks, BLOCK, None)
     pa.check(st)
     st, sch = pa.pa_sched_create(pool, w.max_running, w.prefill_budget, BLOCK)
     pa.check(st)
     b = pa.SchedBatch(w.max_running, w.prefill_budget)
     top = 0
+    lat = LatencyLog()
     for it in range(w.iters):
         for sid, p_, o in w.arrivals[it]:
             pa.check(pa.pa_sched_add(sch, sid, p_, o))
+            lat.add(it, sid, p_)
         pa.check(pa.pa_sched_step(sch, b))
+        ps, pst, pl = b.prefill()
+        lat.step(it, b.decode()[0], ps, pst, pl)
         if b.n_decode:
             top = max(top, int(b.decode()[2].max()) // BLOCK)
         if b.n_prefill_tokens:
@@ -817,6 +825,7 @@ def trace_leg(args, dev):
            "decode_tokens": run.totals["decode_tokens"],
            "prefill_tokens": run.totals["prefill_tokens"],
            "finished": run.totals["finished"], "preemptions": run.totals["preempted"],
+           "latency": lat.summary(wall / w.iters * 1e3),
            "pool_blocks": w.num_blocks, "cache_blocks": run.cache_blocks,
            "cache_note": cache_note,
            "fragmentation": {"internal_waste_mean": float(np.nanmean(waste)),

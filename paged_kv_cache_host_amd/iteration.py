@@ -241,3 +241,54 @@ class LayerIterations:
 
     def synchronize(self):
         self.compute.synchronize()
+
+
+class LatencyLog:
+    """Token times of a continuous-batching run on the iteration clock (the
+    LESSON runs its scheduler on virtual time, one tick per iteration): a
+    request arrives before iteration a; its first token comes out of the
+    iteration whose prefill slice completes the prompt (TTFT = f - a + 1
+    iterations), each later token out of one decode iteration (inter-token
+    latency = the iterations between consecutive tokens, so a preemption
+    shows as a long gap).  Fed from the scheduler's batches
+    (``pa_sched_step``); converted to milliseconds with a measured iteration
+    time."""
+
+    def __init__(self):
+        self.arrival, self.prompt, self.tokens = {}, {}, {}
+
+    def add(self, it: int, seq: int, prompt_len: int):
+        self.arrival[seq] = it
+        self.prompt[seq] = prompt_len
+
+    def step(self, it: int, decode_seqs, prefill_seqs, prefill_starts, prefill_lens):
+        for s, a, n in zip(prefill_seqs, prefill_starts, prefill_lens):
+            s = int(s)
+            if a + n == self.prompt[s] and s not in self.tokens:
+                self.tokens[s] = [it]
+        for s in decode_seqs:
+            self.tokens[int(s)].append(it)
+
+    def ttft(self) -> np.ndarray:
+        """TTFT in iterations of every request that got its first token."""
+        return np.array([t[0] - self.arrival[s] + 1 for s, t in sorted(self.tokens.items())],
+                        dtype=np.int64)
+
+    def itl(self) -> np.ndarray:
+        """Inter-token gaps in iterations, all requests, in request order."""
+        gaps = [np.diff(np.asarray(t, dtype=np.int64)) for _, t in sorted(self.tokens.items())]
+        return np.concatenate(gaps) if gaps else np.zeros(0, np.int64)
+
+    def summary(self, ms_per_iteration: float) -> dict:
+        t, g = self.ttft(), self.itl()
+
+        def stats(x):
+            if len(x) == 0:
+                return {"n": 0}
+            return {"n": int(len(x)), "mean_it": float(x.mean()),
+                    "p50_it": float(np.percentile(x, 50)), "p99_it": float(np.percentile(x, 99)),
+                    "max_it": int(x.max()), "mean_ms": float(x.mean() * ms_per_iteration),
+                    "p99_ms": float(np.percentile(x, 99) * ms_per_iteration)}
+
+        return {"ttft": stats(t), "itl": stats(g),
+                "clock": f"iterations x {ms_per_iteration:.4f} ms measured per iteration"}

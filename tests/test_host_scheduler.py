@@ -146,3 +146,46 @@ def test_step_rejects_small_capacities_without_change():
     st, _ = pa.pa_sched_create(c.pool, 0, 32, 16)
     assert st == pa.PA_ERR_INVALID
     c.close()
+
+
+def test_latency_log_matches_oracle_token_times():
+    """TTFT and inter-token gaps (iteration clock) from the C scheduler's
+    batches through LatencyLog equal those counted directly, with test-local
+    code, from the oracle scheduler's batches: first token at the iteration
+    whose slice completes the prompt, one more per decode iteration.  The
+    pool is small enough to preempt."""
+    from paged_kv_cache_host_amd.iteration import LatencyLog
+    w = make_trace(seed=33, iters=300, lam=0.3, prompt_median=60, prompt_sigma=1.0,
+                   prompt_cap=400, out_mean=20, num_blocks=60)
+    c = CSide(w.num_blocks, 16, 64)
+    o = Scheduler(BlockPool(w.num_blocks, 16), 16, 64)
+    log = LatencyLog()
+    arrive, prompt, times = {}, {}, {}
+    preempted = 0
+    for it in range(w.iters):
+        for sid, p, n in w.arrivals[it]:
+            c.add(sid, p, n)
+            o.add(sid, p, n)
+            log.add(it, sid, p)
+            arrive[sid], prompt[sid] = it, p
+        c.step()
+        ds, _, _ = c.b.decode()
+        ps, pst, pl = c.b.prefill()
+        log.step(it, ds, ps, pst, pl)
+        b = o.step()
+        preempted += len(b.preempted)
+        for s, a, n, _ in b.prefill:
+            if a + n == prompt[s] and s not in times:
+                times[s] = [it]
+        for s, _, _ in b.decode:
+            times[s].append(it)
+    c.close()
+    want_ttft = [times[s][0] - arrive[s] + 1 for s in sorted(times)]
+    want_gaps = [b_ - a_ for s in sorted(times) for a_, b_ in zip(times[s], times[s][1:])]
+    assert preempted > 0 and len(want_ttft) > 20
+    assert log.ttft().tolist() == want_ttft
+    assert log.itl().tolist() == want_gaps
+    assert max(want_gaps) > 1          # preemption gaps are visible
+    sm = log.summary(0.5)
+    assert sm["ttft"]["n"] == len(want_ttft)
+    assert abs(sm["itl"]["mean_ms"] - 0.5 * np.mean(want_gaps)) < 1e-9
