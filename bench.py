@@ -34,6 +34,8 @@ Secondary legs (skipped with --decode-only):
                  cache: prefill kernel TFLOP/s;
   ``prefix_sharing`` 128 sequences behind one shared 1024-token prompt:
                  blocks held and decode kernel time, shared vs private;
+  ``block_size`` the decode-70b contexts with 8/16/32-token blocks: decode
+                 kernel GB/s, and the trace's fragmentation per block size;
   ``trace``      1000 continuous-batching iterations (libpa scheduler +
                  kernels) with Poisson arrivals: tokens/s per layer and KV
                  fragmentation.
@@ -614,6 +616,94 @@ def fp8_leg(args, dev):
             "merge_us": round(tm["decode_merge"][1], 2), "algorithmic_bytes_per_launch": nbytes}
 
 
+def block_size_leg(args, dev):
+    """Block-size sweep (ARTICLE 4.1: small blocks cost table and kernel
+    overhead, large ones allocation waste): the decode-70b contexts decoded
+    from caches of 8-, 16- and 32-token blocks (pool = 1.1 x the blocks
+    needed, shuffled), kernel GB/s on the same algorithmic bytes; and the
+    continuous-batching trace's internal fragmentation with each block size
+    (host-only scheduler runs)."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_host_amd import _pa as pa
+    from paged_kv_cache_host_amd.engine import decode_workspace, sm_scale_for
+
+    lengths, _, _ = workloads.decode_70b_layout()
+    S = len(lengths)
+    max_ctx = int(lengths.max())
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    q = torch.randn((S, H_Q, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((S, H_Q, D), dtype=torch.bfloat16, device=dev)
+    ws = decode_workspace(S, H_Q, H_KV, D, max_ctx, dev)
+    sm = sm_scale_for(D)
+    res = {}
+    for bs in (8, 16, 32):
+        need = int(sum(-(-int(L) // bs) for L in lengths))
+        nb = -(-11 * need // 10)
+        order = np.random.default_rng(6 + bs).permutation(nb).astype(np.int32)
+        st, pool = pa.pa_pool_create(nb, bs, order)
+        pa.check(st)
+        for s_, L in enumerate(lengths.tolist()):
+            pa.check(pa.pa_seq_create(pool, s_, int(L)))
+        mb = -(-max_ctx // bs)
+        st, tables, lens = pa.pa_pack_batch(pool, np.arange(S), mb)
+        pa.check(st)
+        pa.pa_pool_destroy(pool)
+        # cache contents are random: the kernel's traffic does not depend on them
+        k = torch.randn((nb, H_KV, D // 8, bs, 8), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((nb, H_KV, D, bs), generator=gen, device=dev).to(torch.bfloat16)
+        t_d = torch.from_numpy(tables).to(dev)
+        l_d = torch.from_numpy(lens).to(dev)
+        for _ in range(args.warmup):
+            pa.check(pa.pa_decode(None, out, q, k, v, t_d, l_d, nb, H_KV, max_ctx, sm, ws=ws,
+                                  bs=bs))
+        torch.cuda.synchronize()
+        pa.check(pa.pa_timing_enable(["decode"]))
+        for _ in range(max(args.steps // 4, 5)):
+            pa.check(pa.pa_decode(None, out, q, k, v, t_d, l_d, nb, H_KV, max_ctx, sm, ws=ws,
+                                  bs=bs))
+        torch.cuda.synchronize()
+        tm = _timings(pa, ("decode",))
+        pa.check(pa.pa_timing_enable(False))
+        del k, v
+        torch.cuda.empty_cache()
+        nbytes = int(lens.astype(np.int64).sum()) * H_KV * D * 2 * 2 + S * H_Q * D * 4 + \
+            int((-(-lens.astype(np.int64) // bs)).sum()) * 4 + 4 * S
+        k_us = tm["decode"][1]
+        res[str(bs)] = {"kernel_us": round(k_us, 2),
+                        "achieved_GBps": round(nbytes / (k_us / 1e6) / 1e9, 1),
+                        "frac": round(nbytes / (k_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "blocks_held": need}
+    # fragmentation of the continuous-batching trace per block size
+    w = workloads.trace()
+    for bs in (8, 16, 32):
+        nb = w.num_blocks * BLOCK // bs
+        st, pool = pa.pa_pool_create(nb, bs, None)
+        pa.check(st)
+        st, sch = pa.pa_sched_create(pool, w.max_running, w.prefill_budget, bs)
+        pa.check(st)
+        b = pa.SchedBatch(w.max_running, w.prefill_budget)
+        waste = []
+        for it in range(w.iters):
+            for sid, p_, o in w.arrivals[it]:
+                pa.check(pa.pa_sched_add(sch, sid, p_, o))
+            pa.check(pa.pa_sched_step(sch, b))
+            st, acc = pa.pa_sched_stats(sch)
+            pa.check(st)
+            held = acc["blocks_held"] * bs
+            if held:
+                waste.append(1.0 - acc["tokens_held"] / held)
+        pa.pa_sched_destroy(sch)
+        pa.pa_pool_destroy(pool)
+        res[str(bs)]["trace_internal_waste_mean"] = round(float(np.mean(waste)), 5)
+        res[str(bs)]["trace_internal_waste_max"] = round(float(np.max(waste)), 5)
+    return {"workload": "decode-70b contexts (128 seqs, 64/8 heads, d128, bf16) with 8/16/32-token "
+                        "blocks; trace fragmentation with the same block sizes",
+            "by_block_size": res}
+
+
 def fp8_prefill_leg(args, dev):
     """The chunked-prefill prompt with an fp8 cache: a 32768-token prompt
     (bf16 source K/V stored as e4m3fn with per-tensor scales, bf16 Q) attended
@@ -936,6 +1026,7 @@ def main():
         result["fp8_decode"] = fp8_leg(args, dev)
         result["fp8_prefill"] = fp8_prefill_leg(args, dev)
         result["prefix_sharing"] = prefix_leg(args, dev)
+        result["block_size"] = block_size_leg(args, dev)
         result["trace"] = trace_leg(args, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample_seqs)

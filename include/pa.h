@@ -49,7 +49,10 @@
  *
  * Supported envelope of the attention kernels (else PA_ERR_INVALID):
  *   bs == 16; D in {64, 128}; H_q % H_kv == 0; (q, cache, out) element types
- *   (f32, f32, f32), (bf16, bf16, bf16) or (bf16, fp8, bf16).
+ *   (f32, f32, f32), (bf16, bf16, bf16) or (bf16, fp8, bf16).  pa_decode
+ *   also takes bs 8 or 32 (ARTICLE 4.1: the block size trades fragmentation
+ *   against per-block overhead) with bf16 queries, a bf16 or fp8 cache and at
+ *   most 16 query heads per KV head.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -224,6 +227,8 @@ pa_status pa_cache_write(void* stream, const void* k_new, const void* v_new, pa_
  *   grid; no device-to-host read is needed).
  * sm_scale: softmax scale (normally 1/sqrt(D)).  k_scale, v_scale: fp8
  *   per-tensor scales (ignored otherwise).
+ * bs: tokens per block, 16, or 8 / 32 on the matrix-core path (bf16 q, bf16
+ *   or fp8 cache, H_q / H_kv <= 16); the cache layout above with that bs.
  * ws [device, ws_bytes]: scratch, at least pa_decode_workspace_bytes(...)
  *   bytes; else PA_ERR_WORKSPACE.  Its first bytes are work counters: the
  *   workspace must be zero-filled once before its first use, and every call

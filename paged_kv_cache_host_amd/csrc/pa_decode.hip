@@ -42,6 +42,7 @@
 #include "pa_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace pa {
 
@@ -104,31 +105,69 @@ struct BlockRegs<FP8, D> {
   uint32_t v[D / 16];
 };
 
-template <typename CacheT, int D>
+// Loads 16-token sub-block j of a sequence (tokens 16 j .. 16 j + 15) from a
+// cache of BS-token blocks (BS = 8, 16 or 32): K [blocks][H_kv][D/x][BS][x],
+// V [blocks][H_kv][D][BS].  With BS = 32 the sub-block is one half of block
+// j / 2; with BS = 8 its K rows and V quads come from blocks 2 j and
+// 2 j + 1 (lane by lane).  Table indices are clamped to the last of the
+// sequence's nphys blocks and every entry into the pool.
+template <typename CacheT, int D, int BS>
 __device__ __forceinline__ void load_block(BlockRegs<CacheT, D>& r,
                                            const typename CacheT::raw* __restrict__ k_cache,
                                            const typename CacheT::raw* __restrict__ v_cache,
-                                           int64_t tile, int c, int g) {
+                                           const int32_t* __restrict__ table, int32_t j,
+                                           int32_t nphys, int32_t num_blocks, int32_t H_kv,
+                                           int32_t kvh, int c, int g) {
   using R = typename CacheT::raw;
   constexpr int X = 16 / sizeof(R);
-  const R* kt = k_cache + tile * (kBlock * D);
-  const R* vt = v_cache + tile * (kBlock * D) + c * kBlock + 4 * g;
+  const R* kt;
+  const R* vt;
+  if constexpr (BS >= kBlock) {
+    constexpr int kSubs = BS / kBlock;       // sub-blocks per block
+    const int64_t tile =
+        static_cast<int64_t>(safe_block(table[min(j / kSubs, nphys - 1)], num_blocks)) * H_kv + kvh;
+    const int tok0 = kBlock * (j % kSubs);   // first token of the sub-block in its block
+    kt = k_cache + tile * (BS * D) + (tok0 + c) * X;
+    vt = v_cache + tile * (BS * D) + c * BS + tok0 + 4 * g;
+  } else {
+    static_assert(kBlock % BS == 0, "block size divides 16");
+    constexpr int kPer = kBlock / BS;        // blocks per sub-block
+    const int64_t tk =
+        static_cast<int64_t>(safe_block(table[min(kPer * j + c / BS, nphys - 1)], num_blocks)) *
+            H_kv + kvh;
+    const int64_t tv =
+        static_cast<int64_t>(safe_block(table[min(kPer * j + (4 * g) / BS, nphys - 1)],
+                                        num_blocks)) * H_kv + kvh;
+    kt = k_cache + tk * (BS * D) + (c % BS) * X;
+    vt = v_cache + tv * (BS * D) + c * BS + (4 * g) % BS;
+  }
   if constexpr (sizeof(R) == 2) {
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
       r.k[s] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(kt + ((4 * s + g) * kBlock + c) * X));
+          reinterpret_cast<const u32x4*>(kt + (4 * s + g) * BS * X));
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vt + 16 * t * kBlock));
+    for (int t = 0; t < D / 16; ++t) {
+      // with 32-token blocks a sub-block's values are half of each 64-byte
+      // row; the other half follows in the step's second load, so those rows
+      // are kept in cache
+      if constexpr (BS > kBlock)
+        r.v[t] = *reinterpret_cast<const u32x2*>(vt + 16 * t * BS);
+      else
+        r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vt + 16 * t * BS));
+    }
   } else {
 #pragma unroll
     for (int s = 0; s < D / 64; ++s)
       r.k[s] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(kt + ((g + 4 * s) * kBlock + c) * X));
+          reinterpret_cast<const u32x4*>(kt + (g + 4 * s) * BS * X));
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vt + 16 * t * kBlock));
+    for (int t = 0; t < D / 16; ++t) {
+      if constexpr (BS > kBlock)
+        r.v[t] = *reinterpret_cast<const uint32_t*>(vt + 16 * t * BS);
+      else
+        r.v[t] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vt + 16 * t * BS));
+    }
   }
 }
 
@@ -186,7 +225,7 @@ __device__ __forceinline__ void store_out4(typename OutT::raw* dst, f32x4 v) {
 // that fits one chunk gets its output here; longer ones leave one partial per
 // chunk for the merge kernel.  The last work-group to finish resets the
 // ticket counters, so they are zero again for the next call.
-template <typename CacheT, int D>
+template <typename CacheT, int D, int BS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const typename CacheT::raw* __restrict__ k_cache,
@@ -212,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   // partial last chunk of each sequence, in decreasing size, so that the
   // queue ends with its smallest items.
   auto blocks_of = [&](int32_t i) -> int32_t {
-    const int32_t Li = min(context_lens[i], max_blocks * kBlock);
+    const int32_t Li = min(context_lens[i], max_blocks * BS);
     return Li <= 0 ? 0 : (Li + kBlock - 1) / kBlock;
   };
   auto full_of = [&](int32_t nb) -> int32_t { return min(nb >> chunk_shift, n_chunks); };
@@ -308,8 +347,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const int kvh = __builtin_amdgcn_readfirstlane(kvh_);
     const int32_t n_valid = full_of(blocks_of(seq)) + (part_of(blocks_of(seq)) > 0 ? 1 : 0);
 
-  const int32_t L = min(context_lens[seq], max_blocks * kBlock);
-  const int32_t nblk = (L + kBlock - 1) / kBlock;
+  const int32_t L = min(context_lens[seq], max_blocks * BS);
+  const int32_t nblk = (L + kBlock - 1) / kBlock;     // 16-token sub-blocks
+  const int32_t nphys = (L + BS - 1) / BS;            // table entries in use
   const int32_t c0 = chunk << chunk_shift;
   const int32_t b1 = (chunk == n_chunks - 1) ? nblk : min(nblk, c0 + (1 << chunk_shift));
   const int32_t* __restrict__ table = block_tables + static_cast<int64_t>(seq) * max_blocks;
@@ -332,9 +372,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  auto tile_of = [&](int32_t b) -> int64_t {
-    return static_cast<int64_t>(safe_block(table[b], num_blocks)) * H_kv + kvh;
-  };
 
   // One step: blocks p and p+1 (the second is absent when p+1 == b1; its
   // loads then repeat block p's and all its positions are masked).
@@ -434,8 +471,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   for (int32_t st = wave; st < n_steps; st += kDecodeWaves) {
     const int32_t p = c0 + 2 * st;
     BlockRegs<CacheT, D> xa, xb;
-    load_block<CacheT, D>(xa, k_cache, v_cache, tile_of(p), c, g);
-    load_block<CacheT, D>(xb, k_cache, v_cache, tile_of(min(p + 1, b1 - 1)), c, g);
+    load_block<CacheT, D, BS>(xa, k_cache, v_cache, table, p, nphys, num_blocks, H_kv, kvh, c, g);
+    load_block<CacheT, D, BS>(xb, k_cache, v_cache, table, min(p + 1, b1 - 1), nphys, num_blocks,
+                              H_kv, kvh, c, g);
     compute(xa, xb, p);
   }
 
@@ -500,13 +538,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
-    const int32_t* __restrict__ context_lens, int32_t max_blocks, int32_t S, int32_t H_q,
-    int32_t n_chunks, int32_t chunk_shift, float out_scale) {
+    const int32_t* __restrict__ context_lens, int32_t max_blocks, int32_t bs, int32_t S,
+    int32_t H_q, int32_t n_chunks, int32_t chunk_shift, float out_scale) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
   if (idx >= static_cast<int64_t>(S) * H_q) return;
   const int seq = static_cast<int>(idx / H_q);
-  const int32_t L = min(context_lens[seq], max_blocks * kBlock);
+  const int32_t L = min(context_lens[seq], max_blocks * bs);
   const int32_t nblk = (L + kBlock - 1) / kBlock;
   const int nsp = L <= 0 ? 0 : min(n_chunks, ((nblk - 1) >> chunk_shift) + 1);
   if (nsp == 1) return;  // written by the attention kernel
@@ -542,7 +580,7 @@ inline size_t decode_counter_bytes(int32_t S) {
 
 // Work-groups of the persistent kernel that fit on the current device at
 // once (cached per device).
-template <typename CacheT, int D>
+template <typename CacheT, int D, int BS>
 static int32_t resident_work_groups() {
   static int32_t cached[64] = {0};
   int dev = 0;
@@ -550,7 +588,7 @@ static int32_t resident_work_groups() {
   if (cached[dev] > 0) return cached[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<CacheT, D>, kThreads,
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<CacheT, D, BS>, kThreads,
                                                    0) != hipSuccess ||
       cus <= 0 || per_cu <= 0) {
     (void)hipGetLastError();
@@ -560,7 +598,7 @@ static int32_t resident_work_groups() {
   return cached[dev];
 }
 
-template <typename CacheT, int D>
+template <typename CacheT, int D, int BS>
 static pa_status launch_decode_mfma(hipStream_t st, void* out, const void* q, const void* k_cache,
                                     const void* v_cache, const int32_t* block_tables,
                                     int32_t max_blocks, int32_t num_blocks,
@@ -573,11 +611,11 @@ static pa_status launch_decode_mfma(hipStream_t st, void* out, const void* q, co
   float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_counter_bytes(S));
   float* ws_o = ws_ml + static_cast<int64_t>(S) * H_q * n_chunks * 2;
   const float score_scale = sm_scale * kLog2e * k_scale;
-  const int32_t grid = resident_work_groups<CacheT, D>();
+  const int32_t grid = resident_work_groups<CacheT, D, BS>();
   for (int32_t b = 0; b < decode_num_batches(S); ++b) {
     const int64_t s0 = static_cast<int64_t>(b) * kMaxSeqsPerLaunch;
     const int32_t sn = static_cast<int32_t>(std::min<int64_t>(kMaxSeqsPerLaunch, S - s0));
-    hipError_t e = launch(kDecode, decode_kernel<CacheT, D>, dim3(grid), dim3(kThreads), 0, st,
+    hipError_t e = launch(kDecode, decode_kernel<CacheT, D, BS>, dim3(grid), dim3(kThreads), 0, st,
                           static_cast<uint16_t*>(out) + s0 * H_q * D,
                           static_cast<const uint16_t*>(q) + s0 * H_q * D,
                           static_cast<const typename CacheT::raw*>(k_cache),
@@ -592,8 +630,8 @@ static pa_status launch_decode_mfma(hipStream_t st, void* out, const void* q, co
   if (n_chunks > 1) {
     const int64_t rows = static_cast<int64_t>(S) * H_q;
     hipError_t e = launch(kDecodeMerge, decode_merge_kernel<D>, dim3((rows + 3) / 4), dim3(256), 0,
-                          st, static_cast<uint16_t*>(out), ws_ml, ws_o, context_lens, max_blocks, S,
-                          H_q, n_chunks, shift, v_scale);
+                          st, static_cast<uint16_t*>(out), ws_ml, ws_o, context_lens, max_blocks,
+                          BS, S, H_q, n_chunks, shift, v_scale);
     if (e != hipSuccess)
       return fail(PA_ERR_DEVICE, "pa_decode: merge launch failed: %s", hipGetErrorString(e));
   }
@@ -635,14 +673,15 @@ extern "C" pa_status pa_decode(void* stream, void* out, pa_dtype out_dt, const v
                                int32_t H_q, int32_t H_kv, int32_t D, int32_t bs,
                                int32_t max_context_len, float sm_scale, float k_scale,
                                float v_scale, void* ws, size_t ws_bytes) {
-  if (bs != kBlock) return fail(PA_ERR_INVALID, "pa_decode: block size %d != 16", bs);
+  if (bs != 8 && bs != 16 && bs != 32)
+    return fail(PA_ERR_INVALID, "pa_decode: block size %d not in {8, 16, 32}", bs);
   if (S < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv != 0)
     return fail(PA_ERR_INVALID, "pa_decode: S=%d H_q=%d H_kv=%d", S, H_q, H_kv);
   if (D != 64 && D != 128) return fail(PA_ERR_INVALID, "pa_decode: D=%d not in {64,128}", D);
   if (max_blocks <= 0 || num_blocks <= 0 || max_context_len <= 0)
     return fail(PA_ERR_INVALID, "pa_decode: max_blocks=%d num_blocks=%d max_context_len=%d",
                 max_blocks, num_blocks, max_context_len);
-  if (static_cast<int64_t>(max_blocks) * kBlock > INT32_MAX)
+  if (static_cast<int64_t>(max_blocks) * bs > INT32_MAX)
     return fail(PA_ERR_INVALID, "pa_decode: max_blocks=%d too large", max_blocks);
   const bool f32 = q_dt == PA_F32 && cache_dt == PA_F32 && out_dt == PA_F32;
   const bool bf = q_dt == PA_BF16 && out_dt == PA_BF16 &&
@@ -667,23 +706,32 @@ extern "C" pa_status pa_decode(void* stream, void* out, pa_dtype out_dt, const v
     if (!ws || ws_bytes < need)
       return fail(PA_ERR_WORKSPACE, "pa_decode: workspace %zu bytes < %zu required", ws_bytes,
                   need);
-    if (cache_dt == PA_BF16) {
-      if (D == 128)
-        return launch_decode_mfma<BF16, 128>(st, out, q, k_cache, v_cache, block_tables,
+    auto by_bs = [&](auto cache_tag, auto d_tag, float ks, float vs) -> pa_status {
+      using CT = decltype(cache_tag);
+      constexpr int DD = decltype(d_tag)::value;
+      if (bs == 8)
+        return launch_decode_mfma<CT, DD, 8>(st, out, q, k_cache, v_cache, block_tables,
                                              max_blocks, num_blocks, context_lens, S, H_q, H_kv,
-                                             max_context_len, sm_scale, 1.f, 1.f, ws);
-      return launch_decode_mfma<BF16, 64>(st, out, q, k_cache, v_cache, block_tables, max_blocks,
-                                          num_blocks, context_lens, S, H_q, H_kv, max_context_len,
-                                          sm_scale, 1.f, 1.f, ws);
-    }
-    if (D == 128)
-      return launch_decode_mfma<FP8, 128>(st, out, q, k_cache, v_cache, block_tables, max_blocks,
-                                          num_blocks, context_lens, S, H_q, H_kv, max_context_len,
-                                          sm_scale, k_scale, v_scale, ws);
-    return launch_decode_mfma<FP8, 64>(st, out, q, k_cache, v_cache, block_tables, max_blocks,
-                                       num_blocks, context_lens, S, H_q, H_kv, max_context_len,
-                                       sm_scale, k_scale, v_scale, ws);
+                                             max_context_len, sm_scale, ks, vs, ws);
+      if (bs == 32)
+        return launch_decode_mfma<CT, DD, 32>(st, out, q, k_cache, v_cache, block_tables,
+                                              max_blocks, num_blocks, context_lens, S, H_q, H_kv,
+                                              max_context_len, sm_scale, ks, vs, ws);
+      return launch_decode_mfma<CT, DD, 16>(st, out, q, k_cache, v_cache, block_tables,
+                                            max_blocks, num_blocks, context_lens, S, H_q, H_kv,
+                                            max_context_len, sm_scale, ks, vs, ws);
+    };
+    using D128 = std::integral_constant<int, 128>;
+    using D64 = std::integral_constant<int, 64>;
+    if (cache_dt == PA_BF16)
+      return D == 128 ? by_bs(BF16{}, D128{}, 1.f, 1.f) : by_bs(BF16{}, D64{}, 1.f, 1.f);
+    return D == 128 ? by_bs(FP8{}, D128{}, k_scale, v_scale)
+                    : by_bs(FP8{}, D64{}, k_scale, v_scale);
   }
+  if (bs != kBlock)
+    return fail(PA_ERR_INVALID,
+                "pa_decode: block size %d needs the matrix-core path (bf16 queries, bf16 or fp8 "
+                "cache, at most 16 query heads per KV head)", bs);
   return launch_attend_generic(st, out, out_dt, q, q_dt, k_cache, v_cache, cache_dt, block_tables,
                                max_blocks, num_blocks, context_lens, nullptr, nullptr, 0, S, H_q,
                                H_kv, D, sm_scale, k_scale, v_scale);

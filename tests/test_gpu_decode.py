@@ -199,3 +199,89 @@ def test_fp8_codes_decode_exactly():
     got = out.float().cpu().numpy()[0]
     assert np.array_equal(got.astype(np.float64), codecs.E4M3_TABLE[codes])
     kv.close()
+
+
+@pytest.mark.parametrize("bs,cache_dt", [(8, "bf16"), (32, "bf16"), (8, "fp8"), (32, "fp8")])
+def test_block_sizes_8_and_32(bs, cache_dt):
+    """pa_decode over caches of 8- and 32-token blocks (ARTICLE 4.1): the C
+    allocator's tables for that block size equal the oracle's; the cache is
+    scattered here by layout alone (its bytes equal the oracle's scatter);
+    outputs within tolerance of the oracle.  Contexts around both block
+    sizes and spanning two work items."""
+    from oracle import allocator as oa
+    from oracle import attention as oat
+    from oracle import cache as oc
+    import paged_kv_cache_host_amd._pa as pa
+    rng = np.random.default_rng(1700 + bs + len(cache_dt))
+    lengths = [1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 100, 700, 2500]
+    S, h_q, h_kv, d = len(lengths), 16, 2, 128
+    nb = sum(-(-L // bs) for L in lengths) + 7
+    order = rng.permutation(nb).astype(np.int32)
+    ntok = sum(lengths)
+    if cache_dt == "bf16":
+        k_raw = workloads.normal_raw(rng, (ntok, h_kv, d), "bf16")
+        v_raw = workloads.normal_raw(rng, (ntok, h_kv, d), "bf16")
+        ks = vs = 1.0
+    else:   # e4m3fn codes, NaN codes (0x7F, 0xFF) excluded
+        k_raw = rng.integers(0, 0x7F, size=(ntok, h_kv, d)).astype(np.uint8) | \
+            (rng.integers(0, 2, size=(ntok, h_kv, d)).astype(np.uint8) << 7)
+        v_raw = rng.integers(0, 0x7F, size=(ntok, h_kv, d)).astype(np.uint8) | \
+            (rng.integers(0, 2, size=(ntok, h_kv, d)).astype(np.uint8) << 7)
+        ks, vs = 0.01, 0.02
+    q_raw = workloads.normal_raw(rng, (S, h_q, d), "bf16")
+    # host side: the C allocator with this block size
+    st_, pool = pa.pa_pool_create(nb, bs, order)
+    assert st_ == pa.PA_OK
+    try:
+        slots = []
+        for s, L in enumerate(lengths):
+            assert pa.pa_seq_create(pool, s, L) == pa.PA_OK
+            st_, sl = pa.pa_seq_slots(pool, s, 0, L)
+            assert st_ == pa.PA_OK
+            slots.append(np.asarray(sl, dtype=np.int64))
+        mb = max(-(-L // bs) for L in lengths)
+        st_, tables, lens = pa.pa_pack_batch(pool, np.arange(S), mb)
+        assert st_ == pa.PA_OK
+    finally:
+        pa.pa_pool_destroy(pool)
+    slots = np.concatenate(slots)
+    # oracle allocator: same tables and slots
+    opool = oa.BlockPool(nb, bs, order.tolist())
+    for s, L in enumerate(lengths):
+        assert opool.seq_create(s, L) == 0
+    o_slots = np.concatenate([np.asarray(opool.slots(s, 0, L)) for s, L in enumerate(lengths)])
+    assert np.array_equal(o_slots, slots)
+    for s in range(S):
+        t = opool.block_table(s)
+        assert list(tables[s, :len(t)]) == list(t)
+    # the device cache, scattered by layout only
+    x = 8 if cache_dt == "bf16" else 16
+    sdt = np.uint16 if cache_dt == "bf16" else np.uint8
+    kc = np.zeros((nb, h_kv, d // x, bs, x), dtype=sdt)
+    vc = np.zeros((nb, h_kv, d, bs), dtype=sdt)
+    kc[slots // bs, :, :, slots % bs, :] = k_raw.reshape(ntok, h_kv, d // x, x)
+    vc[slots // bs, :, :, slots % bs] = v_raw
+    okc, ovc = oc.new_cache(nb, h_kv, bs, d, cache_dt)
+    oc.cache_write(okc, ovc, k_raw, v_raw, slots, cache_dt, cache_dt)
+    assert np.array_equal(okc, kc) and np.array_equal(ovc, vc)
+    sm = float(np.float32(1.0) / np.float32(np.sqrt(d)))
+    ref = oat.decode(codecs.decode(q_raw, "bf16"), okc, ovc, tables, lens, h_kv, sm, cache_dt,
+                     ks, vs)
+    k_d = torch.from_numpy(kc.view(np.int16) if cache_dt == "bf16" else kc).to(DEV)
+    v_d = torch.from_numpy(vc.view(np.int16) if cache_dt == "bf16" else vc).to(DEV)
+    if cache_dt == "bf16":
+        k_d, v_d = k_d.view(torch.bfloat16), v_d.view(torch.bfloat16)
+    else:
+        k_d, v_d = k_d.view(torch.float8_e4m3fn), v_d.view(torch.float8_e4m3fn)
+    q_d = torch.from_numpy(q_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
+    out = torch.empty((S, h_q, d), dtype=torch.bfloat16, device=DEV)
+    ws = torch.zeros(pa.pa_decode_workspace_bytes(S, h_q, h_kv, d, max(lengths)),
+                     dtype=torch.uint8, device=DEV)
+    say(f"[decode bs={bs}] {cache_dt} S={S} maxL={max(lengths)} pool={nb}")
+    assert pa.pa_decode(None, out, q_d, k_d, v_d, torch.from_numpy(tables).to(DEV),
+                        torch.from_numpy(lens).to(DEV), nb, h_kv, max(lengths), sm, ks, vs, ws,
+                        bs=bs) == 0
+    torch.cuda.synchronize()
+    got = codecs.decode(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    err = assert_close(got, ref, cache_dt, f"bs={bs} {cache_dt}")
+    say(f"    max|d| = {err:.3g}")

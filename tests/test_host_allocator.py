@@ -164,8 +164,14 @@ def test_validate_tables():
 def test_argument_validation_of_kernel_entry_points_on_host():
     # invalid arguments are rejected before anything touches a device
     assert pa._pa._lib.pa_decode(None, None, 1, None, 1, None, None, 1, None, 4, 4, None,
-                                 1, 64, 8, 128, 8, 100, 0.1, 1.0, 1.0, None, 0) == pa.PA_ERR_INVALID
+                                 1, 64, 8, 128, 12, 100, 0.1, 1.0, 1.0, None, 0) == pa.PA_ERR_INVALID
     assert "block size" in pa.pa_last_error()
+    # blocks of 8 or 32 tokens only on the matrix-core path: an fp32 call is
+    # refused before any launch
+    fake = 0x1000
+    assert pa._pa._lib.pa_decode(None, fake, 0, fake, 0, fake, fake, 0, fake, 4, 4, fake,
+                                 1, 4, 4, 64, 32, 100, 0.1, 1.0, 1.0, None, 0) == pa.PA_ERR_INVALID
+    assert "matrix-core" in pa.pa_last_error()
     assert pa._pa._lib.pa_decode(None, None, 1, None, 1, None, None, 1, None, 4, 4, None,
                                  1, 64, 7, 128, 16, 100, 0.1, 1.0, 1.0, None, 0) == pa.PA_ERR_INVALID
     assert pa._pa._lib.pa_decode(None, None, 1, None, 1, None, None, 1, None, 4, 4, None,
