@@ -227,14 +227,14 @@ def pmc_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_di
     """HBM traffic of one decode launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
     runs (KiB per dispatch), each scaled by what the same counter reads for
     the calibration kernel of known size."""
-    f_dec, n_f = _pmc_mean(_pmc_rows(fetch_dir, "FETCH_SIZE"), "decode_kernel<pa::BF16, 128>")
-    w_dec, n_w = _pmc_mean(_pmc_rows(write_dir, "WRITE_SIZE"), "decode_kernel<pa::BF16, 128>")
+    f_dec, n_f = _pmc_mean(_pmc_rows(fetch_dir, "FETCH_SIZE"), "decode_kernel<pa::BF16, 128, 16>")
+    w_dec, n_w = _pmc_mean(_pmc_rows(write_dir, "WRITE_SIZE"), "decode_kernel<pa::BF16, 128, 16>")
     f_cal, _ = _pmc_mean(_pmc_rows(cal_fetch_dir, "FETCH_SIZE"), "neg")
     w_cal, _ = _pmc_mean(_pmc_rows(cal_write_dir, "WRITE_SIZE"), "neg")
     f_scale = CAL_BYTES / (f_cal * 1024.0)
     w_scale = CAL_BYTES / (w_cal * 1024.0)
     out = {
-        "kernel": "decode_kernel<BF16,128>",
+        "kernel": "decode_kernel<BF16,128,16>",
         "workload": "decode-70b-shaped, 128 seqs (bench.py default)",
         "kernel_source_digest": kernel_source_digest(),
         "fetch_kib_per_launch_raw": round(f_dec, 1), "fetch_dispatches": n_f,
@@ -612,7 +612,7 @@ def fp8_leg(args, dev):
             "bound": "hbm", "achieved": round(nbytes / (k_us / 1e6) / 1e9, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(nbytes / (k_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
-            "kernel": "decode_kernel<FP8,128>", "kernel_us": round(k_us, 2),
+            "kernel": "decode_kernel<FP8,128,16>", "kernel_us": round(k_us, 2),
             "merge_us": round(tm["decode_merge"][1], 2), "algorithmic_bytes_per_launch": nbytes}
 
 
@@ -1010,7 +1010,7 @@ def main():
                    "num_blocks": d["num_blocks"]},
         "roofline": {"bound": "hbm", "achieved": round(d["achieved"], 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(d["achieved"] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(digest), "kernel": "decode_kernel<BF16,128>",
+                     "traffic": traffic_from_profile(digest), "kernel": "decode_kernel<BF16,128,16>",
                      "kernel_us": round(d["kernel_us"], 2),
                      "other_kernels_us": {"decode_merge_kernel": round(d["merge_us"], 2),
                                           "stage_cache_write_kernel":
