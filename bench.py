@@ -855,10 +855,9 @@ def trace_leg(args, dev):
     for it in range(w.iters):
         for sid, p_, o in w.arrivals[it]:
             pa.check(pa.pa_sched_add(sch, sid, p_, o))
-            lat.add(it, sid, p_)
+            lat.add(it, sid, o)
         pa.check(pa.pa_sched_step(sch, b))
-        ps, pst, pl = b.prefill()
-        lat.step(it, b.decode()[0], ps, pst, pl)
+        lat.step(it, b.decode()[0], b.prefill()[0], b.emits())
         if b.n_decode:
             top = max(top, int(b.decode()[2].max()) // BLOCK)
         if b.n_prefill_tokens:

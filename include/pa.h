@@ -310,6 +310,9 @@ typedef struct pa_sched_batch {
   int64_t* prefill_seq;    /* [prefill_cap] sequence of each prefill slice    */
   int32_t* prefill_start;  /* [prefill_cap] first position of the slice       */
   int32_t* prefill_len;    /* [prefill_cap] tokens in the slice               */
+  int32_t* prefill_emits;  /* [prefill_cap] 1 if the slice completes the
+                              sequence's known tokens (it yields an output
+                              token), else 0                                  */
   int32_t prefill_cap;
   int32_t* prefill_slots;  /* [prefill_slots_cap] slots of all slices, in order */
   int32_t prefill_slots_cap;
@@ -332,9 +335,42 @@ typedef struct pa_sched_accounting {
   int64_t blocks_held, tokens_held, unwritten;
 } pa_sched_accounting;
 
-/* block_size must equal the pool's.  PA_ERR_INVALID on bad sizes. */
+/* block_size must equal the pool's.  PA_ERR_INVALID on bad sizes.  The
+ * scheduler of pa_sched_create is the chunked one (PA_SCHED_CHUNKED). */
 pa_status pa_sched_create(pa_pool* pool, int32_t max_running, int32_t prefill_budget,
                           int32_t block_size, pa_sched** out);
+
+/* The four schedules the LESSON's simulator compares ("Use It"):
+ *   PA_SCHED_CHUNKED     continuous batching with chunked prefill (above).
+ *   PA_SCHED_CONTINUOUS  admission and release every iteration, each prompt
+ *                        prefilled whole in the iteration that admits it;
+ *                        admission also stops at the first request whose
+ *                        known tokens exceed what is left of the iteration's
+ *                        prefill_budget (a request longer than the whole
+ *                        budget enters an iteration with no other prefill and
+ *                        is sliced at the budget).
+ *   PA_SCHED_STATIC      a batch is formed only when nothing runs: up to
+ *                        max_running requests in arrival order while
+ *                        count x longest prompt <= prefill_budget (one request
+ *                        always) and the padded blocks fit; every prompt is
+ *                        padded to the longest (padding tokens enter the cache
+ *                        in front of the output: positions and slots include
+ *                        them) and prefilled in that iteration; members that
+ *                        reached their target keep decoding padding until the
+ *                        last one does, then the batch is released together.
+ *   PA_SCHED_NAIVE       PA_SCHED_STATIC with batches of one request.
+ * Preemption and recomputation work as above in every mode; a preempted
+ * member of a static batch keeps its padding.  prefill_budget must be >= 1
+ * outside PA_SCHED_CHUNKED.  The output capacities are those of
+ * pa_sched_step. */
+typedef enum pa_sched_mode {
+  PA_SCHED_CHUNKED = 0,
+  PA_SCHED_CONTINUOUS = 1,
+  PA_SCHED_STATIC = 2,
+  PA_SCHED_NAIVE = 3
+} pa_sched_mode;
+pa_status pa_sched_create_mode(pa_pool* pool, int32_t mode, int32_t max_running,
+                               int32_t prefill_budget, int32_t block_size, pa_sched** out);
 void pa_sched_destroy(pa_sched* sched);
 /* Queue a request (prompt_len >= 1 tokens, target >= 1 output tokens);
  * PA_ERR_EXISTS if the id was ever added. */

@@ -34,6 +34,23 @@ Readings taken where the texts leave a step open:
   grows by one) and produces the next;
 * a sequence is finished once it has produced its target number of output
   tokens; it is released at the start of the following iteration.
+
+The other three schedules of the LESSON's simulator ("Use It": one request
+at a time; padded static batches; iteration-level admission and release
+without chunking), read as follows:
+* ``continuous``: as above, except that a prompt is prefilled whole in the
+  iteration that admits it, so the head of the queue is admitted only if its
+  known tokens fit the budget still unspent in this iteration (or nothing
+  has been prefilled in it yet: a prompt longer than the whole budget then
+  runs in budget-sized slices);
+* ``static``: a new batch is taken only when nothing runs: heads of the
+  queue in order, as long as (members x longest known length) stays within
+  the budget (the first member always) and that many padded blocks are
+  free; each member is padded to the longest (the padding sits before the
+  output, in the cache) and the batch is prefilled at once; a member that
+  reached its target keeps decoding padding until every member has, and the
+  batch leaves together;
+* ``naive``: ``static`` with one request per batch.
 """
 from __future__ import annotations
 
@@ -52,22 +69,32 @@ class Seq:
     decoded: int = 0          # output tokens produced so far
     in_prefill: bool = True
     preemptions: int = 0
+    padding: int = 0          # static batches: padding tokens before the output
 
     def cached_len(self) -> int:
-        return self.prefilled if self.in_prefill else self.prompt_len + self.decoded - 1
+        if self.in_prefill:
+            return self.prefilled
+        return self.prompt_len + self.padding + self.decoded - 1
 
 
 @dataclass
 class Batch:
     decode: list = field(default_factory=list)    # (sid, position, slot)
     prefill: list = field(default_factory=list)   # (sid, start, n, slots)
+    emits: list = field(default_factory=list)     # per slice: yields a token
     finished: list = field(default_factory=list)
     admitted: list = field(default_factory=list)
     preempted: list = field(default_factory=list)
 
 
 class Scheduler:
-    def __init__(self, pool: BlockPool, max_running: int = 256, prefill_budget: int = 512):
+    MODES = ("chunked", "continuous", "static", "naive")
+
+    def __init__(self, pool: BlockPool, max_running: int = 256, prefill_budget: int = 512,
+                 mode: str = "chunked"):
+        if mode not in self.MODES:
+            raise ValueError(mode)
+        self.mode = mode
         self.pool = pool
         self.max_running = max_running
         self.prefill_budget = prefill_budget
@@ -85,16 +112,47 @@ class Scheduler:
         s.preemptions += 1
         s.in_prefill = True
         s.prefilled = 0
-        s.known = s.prompt_len + s.decoded
+        s.known = s.prompt_len + s.padding + s.decoded
         self.waiting.append(s)
+
+    def _prefill(self, out: Batch, seqs, budget: int) -> int:
+        """Hands out slices to the prefill-phase sequences of ``seqs`` in
+        order; returns the budget left."""
+        for s in seqs:
+            if not s.in_prefill or budget == 0:
+                continue
+            n = min(s.known - s.prefilled, budget)
+            if n <= 0:
+                continue
+            slots = self.pool.slots(s.sid, s.prefilled, n)
+            out.prefill.append((s.sid, s.prefilled, n, slots))
+            s.prefilled += n
+            budget -= n
+            done = s.prefilled == s.known
+            out.emits.append(done)
+            if done:
+                s.in_prefill = False
+                s.decoded += 1
+        return budget
+
+    def _admit(self, out: Batch, s: Seq):
+        st = self.pool.seq_create(s.sid, s.known)
+        assert st == OK
+        self.waiting.pop(0)
+        self.running.append(s)
+        out.admitted.append(s.sid)
 
     def step(self) -> Batch:
         out = Batch()
         bs = self.pool.block_size
-        # (2) release finished sequences
+        static = self.mode in ("static", "naive")
+        # (2) release finished sequences; a static batch only all at once
+        over = [not s.in_prefill and s.decoded >= s.target for s in self.running]
+        if static and not all(over):
+            over = [False] * len(self.running)
         keep = []
-        for s in self.running:
-            if not s.in_prefill and s.decoded >= s.target:
+        for s, f in zip(self.running, over):
+            if f:
                 self.pool.seq_release(s.sid)
                 out.finished.append(s.sid)
                 self.done.append(s)
@@ -113,36 +171,48 @@ class Scheduler:
                 out.preempted.append(s.sid)
                 continue
             assert st == OK
-            pos = s.prompt_len + s.decoded - 1
-            out.decode.append((s.sid, pos, slots[0]))
+            out.decode.append((s.sid, s.cached_len(), slots[0]))
             s.decoded += 1
             keep.append(s)
         self.running = keep
-        # (4) admission, head of line first
-        while self.waiting and len(self.running) < self.max_running:
-            s = self.waiting[0]
-            if self.pool.num_free() < ceil_div(s.known, bs):
-                break
-            st = self.pool.seq_create(s.sid, s.known)
-            assert st == OK
-            self.waiting.pop(0)
-            self.running.append(s)
-            out.admitted.append(s.sid)
-        # (5) prefill slices within the budget
+        # (4) admission and (5) prefill slices within the budget
         budget = self.prefill_budget
-        for s in self.running:
-            if not s.in_prefill or budget == 0:
-                continue
-            n = min(s.known - s.prefilled, budget)
-            if n <= 0:
-                continue
-            slots = self.pool.slots(s.sid, s.prefilled, n)
-            out.prefill.append((s.sid, s.prefilled, n, slots))
-            s.prefilled += n
-            budget -= n
-            if s.prefilled == s.known:
-                s.in_prefill = False
-                s.decoded += 1
+        if self.mode == "chunked":
+            while self.waiting and len(self.running) < self.max_running:
+                s = self.waiting[0]
+                if self.pool.num_free() < ceil_div(s.known, bs):
+                    break
+                self._admit(out, s)
+            self._prefill(out, self.running, budget)
+        elif self.mode == "continuous":
+            budget = self._prefill(out, self.running, budget)
+            while self.waiting and len(self.running) < self.max_running:
+                s = self.waiting[0]
+                if self.pool.num_free() < ceil_div(s.known, bs):
+                    break
+                if s.known > budget and budget < self.prefill_budget:
+                    break
+                self._admit(out, s)
+                budget = self._prefill(out, [s], budget)
+        else:
+            if not self.running:
+                size = 1 if self.mode == "naive" else self.max_running
+                members = []
+                for s in self.waiting[:size]:
+                    width = max([m.known for m in members] + [s.known])
+                    n = len(members) + 1
+                    if members and n * width > self.prefill_budget:
+                        break
+                    if n * ceil_div(width, bs) > self.pool.num_free():
+                        break
+                    members.append(s)
+                if members:
+                    width = max(m.known for m in members)
+                    for s in members:
+                        s.padding += width - s.known
+                        s.known = width
+                        self._admit(out, s)
+            self._prefill(out, self.running, budget)
         return out
 
     # -- accounting -------------------------------------------------------

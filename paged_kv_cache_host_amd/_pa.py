@@ -45,6 +45,7 @@ class SchedBatchC(C.Structure):
     _fields_ = [("decode_seq", _i64p), ("decode_pos", _i32p), ("decode_slot", _i32p),
                 ("decode_cap", _i32),
                 ("prefill_seq", _i64p), ("prefill_start", _i32p), ("prefill_len", _i32p),
+                ("prefill_emits", _i32p),
                 ("prefill_cap", _i32),
                 ("prefill_slots", _i32p), ("prefill_slots_cap", _i32),
                 ("finished", _i64p), ("admitted", _i64p), ("preempted", _i64p),
@@ -84,6 +85,7 @@ _SIGS = {
     "pa_decode": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _i32,
                          _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32, _vp, _sz]),
     "pa_sched_create": (_i32, [_vp, _i32, _i32, _i32, C.POINTER(_vp)]),
+    "pa_sched_create_mode": (_i32, [_vp, _i32, _i32, _i32, _i32, C.POINTER(_vp)]),
     "pa_sched_destroy": (None, [_vp]),
     "pa_sched_add": (_i32, [_vp, _i64, _i32, _i32]),
     "pa_sched_step": (_i32, [_vp, C.POINTER(SchedBatchC)]),
@@ -275,6 +277,19 @@ def pa_sched_create(pool, max_running: int = 256, prefill_budget: int = 512,
     return st, (out.value if st == PA_OK else None)
 
 
+SCHED_MODES = {"chunked": 0, "continuous": 1, "static": 2, "naive": 3}
+
+
+def pa_sched_create_mode(pool, mode: str, max_running: int = 256, prefill_budget: int = 512,
+                         block_size: int = 16):
+    """Returns (status, scheduler handle or None); ``mode`` is one of
+    ``SCHED_MODES``."""
+    out = _vp()
+    st = _lib.pa_sched_create_mode(pool, SCHED_MODES[mode], max_running, prefill_budget,
+                                   block_size, C.byref(out))
+    return st, (out.value if st == PA_OK else None)
+
+
 def pa_sched_destroy(sched) -> None:
     _lib.pa_sched_destroy(sched)
 
@@ -294,6 +309,7 @@ class SchedBatch:
         self.prefill_seq = np.zeros(R, np.int64)
         self.prefill_start = np.zeros(R, np.int32)
         self.prefill_len = np.zeros(R, np.int32)
+        self.prefill_emits = np.zeros(R, np.int32)
         self.prefill_slots = np.zeros(B, np.int32)
         self.finished = np.zeros(R, np.int64)
         self.admitted = np.zeros(R, np.int64)
@@ -301,7 +317,8 @@ class SchedBatch:
         p64 = lambda a: a.ctypes.data_as(_i64p)
         self.c = SchedBatchC(p64(self.decode_seq), _ptr_i32(self.decode_pos),
                              _ptr_i32(self.decode_slot), R, p64(self.prefill_seq),
-                             _ptr_i32(self.prefill_start), _ptr_i32(self.prefill_len), R,
+                             _ptr_i32(self.prefill_start), _ptr_i32(self.prefill_len),
+                             _ptr_i32(self.prefill_emits), R,
                              _ptr_i32(self.prefill_slots), B, p64(self.finished),
                              p64(self.admitted), p64(self.preempted), R, 0, 0, 0, 0, 0, 0)
 
@@ -324,6 +341,10 @@ class SchedBatch:
     def prefill(self):
         n = self.c.n_prefill
         return self.prefill_seq[:n], self.prefill_start[:n], self.prefill_len[:n]
+
+    def emits(self):
+        """Per prefill slice: 1 if it yields the sequence's next output token."""
+        return self.prefill_emits[:self.c.n_prefill]
 
     def slots(self):
         return self.prefill_slots[:self.c.n_prefill_tokens]

@@ -22,7 +22,23 @@
 // sequence decodes from the next step on and is finished once it produced
 // its target count, being released at the start of the following step.
 //
+// Modes (LESSON "Use It": the four schedules its simulator compares):
+//  * CHUNKED (the above): admission every iteration, prompts in slices.
+//  * CONTINUOUS: admission and release every iteration, but a prompt is
+//    prefilled whole in the iteration that admits it, so admission also
+//    stops at the first request whose prompt does not fit what is left of
+//    the iteration's token budget.  A prompt longer than the whole budget is
+//    admitted into an iteration with no other prefill and sliced.
+//  * STATIC: a batch is formed only when nothing runs: up to max_running
+//    waiting requests in arrival order, every prompt padded to the longest
+//    of the batch, all prefilled in that iteration (the padded tokens of the
+//    batch may not exceed the budget, a single request excepted); members
+//    that reached their target keep decoding padding tokens until the last
+//    one finishes, and the batch is released together.
+//  * NAIVE: STATIC with batches of one request.
+//
 // The pool is driven through its public C calls only.
+#include <algorithm>
 #include <cstdint>
 #include <deque>
 #include <new>
@@ -38,6 +54,7 @@ struct SSeq {
   int64_t id;
   int32_t prompt;
   int32_t target;
+  int32_t pad;        // padding tokens in front of the output (static batches)
   int32_t known;      // tokens to prefill on (re)admission
   int32_t prefilled;  // of `known`, tokens handed out as prefill slices
   int32_t decoded;    // output tokens produced
@@ -52,6 +69,7 @@ struct pa_sched {
   int32_t max_running = 0;
   int32_t budget = 0;
   int32_t block_size = 16;
+  int32_t mode = PA_SCHED_CHUNKED;
   std::deque<SSeq> waiting;
   std::vector<SSeq> running;
   std::unordered_set<int64_t> known_ids;
@@ -65,21 +83,32 @@ static int32_t ceil_div32(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 extern "C" {
 
-pa_status pa_sched_create(pa_pool* pool, int32_t max_running, int32_t prefill_budget,
-                          int32_t block_size, pa_sched** out) {
+pa_status pa_sched_create_mode(pa_pool* pool, int32_t mode, int32_t max_running,
+                               int32_t prefill_budget, int32_t block_size, pa_sched** out) {
   if (!pool || !out) return fail(PA_ERR_INVALID, "pa_sched_create: NULL argument");
-  if (max_running <= 0 || prefill_budget < 0 || block_size <= 0)
-    return fail(PA_ERR_INVALID, "pa_sched_create: max_running=%d prefill_budget=%d block_size=%d",
-                max_running, prefill_budget, block_size);
+  if (mode < PA_SCHED_CHUNKED || mode > PA_SCHED_NAIVE)
+    return fail(PA_ERR_INVALID, "pa_sched_create: unknown mode %d", mode);
+  if (max_running <= 0 || prefill_budget < 0 || block_size <= 0 ||
+      (mode != PA_SCHED_CHUNKED && prefill_budget == 0))
+    return fail(PA_ERR_INVALID,
+                "pa_sched_create: max_running=%d prefill_budget=%d block_size=%d (mode %d)",
+                max_running, prefill_budget, block_size, mode);
   pa_sched* s = new (std::nothrow) pa_sched;
   if (!s) return fail(PA_ERR_INVALID, "pa_sched_create: out of host memory");
   s->pool = pool;
   s->max_running = max_running;
   s->budget = prefill_budget;
   s->block_size = block_size;
+  s->mode = mode;
   s->running.reserve(static_cast<size_t>(max_running));
   *out = s;
   return PA_OK;
+}
+
+pa_status pa_sched_create(pa_pool* pool, int32_t max_running, int32_t prefill_budget,
+                          int32_t block_size, pa_sched** out) {
+  return pa_sched_create_mode(pool, PA_SCHED_CHUNKED, max_running, prefill_budget, block_size,
+                              out);
 }
 
 void pa_sched_destroy(pa_sched* s) { delete s; }
@@ -92,7 +121,7 @@ pa_status pa_sched_add(pa_sched* s, int64_t seq, int32_t prompt_len, int32_t tar
   if (s->known_ids.count(seq)) return fail(PA_ERR_EXISTS, "pa_sched_add: sequence %lld exists",
                                            static_cast<long long>(seq));
   s->known_ids.insert(seq);
-  s->waiting.push_back(SSeq{seq, prompt_len, target, prompt_len, 0, 0, true, 0});
+  s->waiting.push_back(SSeq{seq, prompt_len, target, 0, prompt_len, 0, 0, true, 0});
   return PA_OK;
 }
 
@@ -107,16 +136,21 @@ pa_status pa_sched_step(pa_sched* s, pa_sched_batch* b) {
                 "max_running=%d / budget=%d",
                 b->decode_cap, b->prefill_cap, b->event_cap, b->prefill_slots_cap, R, s->budget);
   if ((R > 0 && (!b->decode_seq || !b->decode_pos || !b->decode_slot || !b->prefill_seq ||
-                 !b->prefill_start || !b->prefill_len || !b->finished || !b->admitted ||
-                 !b->preempted)) ||
+                 !b->prefill_start || !b->prefill_len || !b->prefill_emits || !b->finished ||
+                 !b->admitted || !b->preempted)) ||
       (s->budget > 0 && !b->prefill_slots))
     return fail(PA_ERR_INVALID, "pa_sched_step: NULL output array");
   b->n_decode = b->n_prefill = b->n_prefill_tokens = 0;
   b->n_finished = b->n_admitted = b->n_preempted = 0;
   pa_pool* pool = s->pool;
 
-  // finished sequences leave and free their blocks
-  {
+  const bool batched = s->mode == PA_SCHED_STATIC || s->mode == PA_SCHED_NAIVE;
+  // finished sequences leave and free their blocks; a static batch leaves
+  // only as a whole
+  bool batch_done = true;
+  if (batched)
+    for (const SSeq& q : s->running) batch_done = batch_done && !q.in_prefill && q.decoded >= q.target;
+  if (batch_done) {
     size_t w = 0;
     for (size_t i = 0; i < s->running.size(); ++i) {
       SSeq& q = s->running[i];
@@ -148,7 +182,7 @@ pa_status pa_sched_step(pa_sched* s, pa_sched_batch* b) {
         ++s->preemptions;
         q.in_prefill = true;
         q.prefilled = 0;
-        q.known = q.prompt + q.decoded;
+        q.known = q.prompt + q.pad + q.decoded;
         s->waiting.push_back(q);
         b->preempted[b->n_preempted++] = q.id;
         continue;
@@ -156,7 +190,7 @@ pa_status pa_sched_step(pa_sched* s, pa_sched_batch* b) {
       if (st != PA_OK) return st;
       const int32_t k = b->n_decode++;
       b->decode_seq[k] = q.id;
-      b->decode_pos[k] = q.prompt + q.decoded - 1;
+      b->decode_pos[k] = q.prompt + q.pad + q.decoded - 1;
       b->decode_slot[k] = slot;
       ++q.decoded;
       s->running[w++] = q;
@@ -164,37 +198,80 @@ pa_status pa_sched_step(pa_sched* s, pa_sched_batch* b) {
     s->running.resize(w);
   }
 
-  // admission, head of the queue first
-  while (!s->waiting.empty() && static_cast<int32_t>(s->running.size()) < R) {
-    SSeq q = s->waiting.front();
-    if (pa_pool_num_free(pool) < ceil_div32(q.known, s->block_size)) break;
-    const pa_status st = pa_seq_create(pool, q.id, q.known);
-    if (st != PA_OK) return st;
-    s->waiting.pop_front();
-    s->running.push_back(q);
-    b->admitted[b->n_admitted++] = q.id;
-  }
-
-  // prefill slices within the budget, in running order
+  // prefill slices within the budget, in running order: first the
+  // sequences that were already running, then the ones admitted below
   int32_t left = s->budget;
-  for (SSeq& q : s->running) {
-    if (!q.in_prefill || left == 0) continue;
-    const int32_t n = q.known - q.prefilled < left ? q.known - q.prefilled : left;
-    if (n <= 0) continue;
-    const pa_status st = pa_seq_slots(pool, q.id, q.prefilled, n,
-                                      b->prefill_slots + b->n_prefill_tokens);
-    if (st != PA_OK) return st;
-    const int32_t k = b->n_prefill++;
-    b->prefill_seq[k] = q.id;
-    b->prefill_start[k] = q.prefilled;
-    b->prefill_len[k] = n;
-    b->n_prefill_tokens += n;
-    q.prefilled += n;
-    left -= n;
-    if (q.prefilled == q.known) {
-      q.in_prefill = false;
-      ++q.decoded;
+  auto slices = [&](size_t from) -> pa_status {
+    for (size_t i = from; i < s->running.size(); ++i) {
+      SSeq& q = s->running[i];
+      if (!q.in_prefill || left == 0) continue;
+      const int32_t n = q.known - q.prefilled < left ? q.known - q.prefilled : left;
+      if (n <= 0) continue;
+      const pa_status st = pa_seq_slots(pool, q.id, q.prefilled, n,
+                                        b->prefill_slots + b->n_prefill_tokens);
+      if (st != PA_OK) return st;
+      const int32_t k = b->n_prefill++;
+      b->prefill_seq[k] = q.id;
+      b->prefill_start[k] = q.prefilled;
+      b->prefill_len[k] = n;
+      b->n_prefill_tokens += n;
+      q.prefilled += n;
+      left -= n;
+      b->prefill_emits[k] = q.prefilled == q.known;
+      if (q.prefilled == q.known) {
+        q.in_prefill = false;
+        ++q.decoded;
+      }
     }
+    return PA_OK;
+  };
+  const size_t n_old = s->running.size();
+  pa_status st = slices(0);
+  if (st != PA_OK) return st;
+
+  // admission, head of the queue first
+  if (!batched) {
+    while (!s->waiting.empty() && static_cast<int32_t>(s->running.size()) < R) {
+      SSeq q = s->waiting.front();
+      if (pa_pool_num_free(pool) < ceil_div32(q.known, s->block_size)) break;
+      // a whole prompt must fit what is left of the iteration's budget
+      if (s->mode == PA_SCHED_CONTINUOUS && q.known > left && left < s->budget) break;
+      st = pa_seq_create(pool, q.id, q.known);
+      if (st != PA_OK) return st;
+      s->waiting.pop_front();
+      s->running.push_back(q);
+      b->admitted[b->n_admitted++] = q.id;
+      if (s->mode == PA_SCHED_CONTINUOUS) {
+        st = slices(s->running.size() - 1);
+        if (st != PA_OK) return st;
+      }
+    }
+  } else if (s->running.empty()) {
+    // a new batch: as many heads of the queue as fit once padded
+    const int32_t cap = s->mode == PA_SCHED_NAIVE ? 1 : R;
+    int32_t count = 0, padded = 0;
+    while (count < cap && count < static_cast<int32_t>(s->waiting.size())) {
+      const int32_t p = std::max(padded, s->waiting[count].known);
+      const int64_t tokens = static_cast<int64_t>(count + 1) * p;
+      const int64_t blocks = static_cast<int64_t>(count + 1) * ceil_div32(p, s->block_size);
+      if (blocks > pa_pool_num_free(pool) || (count > 0 && tokens > s->budget)) break;
+      padded = p;
+      ++count;
+    }
+    for (int32_t i = 0; i < count; ++i) {
+      SSeq q = s->waiting.front();
+      q.pad += padded - q.known;
+      q.known = padded;
+      st = pa_seq_create(pool, q.id, q.known);
+      if (st != PA_OK) return st;
+      s->waiting.pop_front();
+      s->running.push_back(q);
+      b->admitted[b->n_admitted++] = q.id;
+    }
+  }
+  if (s->mode != PA_SCHED_CONTINUOUS) {
+    st = slices(n_old);
+    if (st != PA_OK) return st;
   }
   return PA_OK;
 }

@@ -244,34 +244,42 @@ class LayerIterations:
 
 
 class LatencyLog:
-    """Token times of a continuous-batching run on the iteration clock (the
-    LESSON runs its scheduler on virtual time, one tick per iteration): a
-    request arrives before iteration a; its first token comes out of the
-    iteration whose prefill slice completes the prompt (TTFT = f - a + 1
-    iterations), each later token out of one decode iteration (inter-token
-    latency = the iterations between consecutive tokens, so a preemption
-    shows as a long gap).  Fed from the scheduler's batches
-    (``pa_sched_step``); converted to milliseconds with a measured iteration
-    time."""
+    """Token times of a continuous-batching run (the LESSON's simulator
+    reports mean time to first token and the P99 inter-token latency per
+    schedule).  A request arrives before iteration a; an output token comes
+    out of every iteration whose prefill slice completes the request's known
+    tokens (its first token, or the next one after a preemption's
+    recomputation) and out of every decode iteration, up to the request's
+    target (a static batch's padding tokens past it are not counted).  Fed
+    from the scheduler's batches (``pa_sched_step``).  Two clocks: the
+    iteration clock (TTFT = f - a + 1 iterations, gaps in iterations, times a
+    measured mean iteration time), or measured end times of every iteration
+    with arrival times on the same clock (``timed``)."""
 
     def __init__(self):
-        self.arrival, self.prompt, self.tokens = {}, {}, {}
+        self.arrival, self.target, self.tokens = {}, {}, {}
 
-    def add(self, it: int, seq: int, prompt_len: int):
+    def add(self, it: int, seq: int, target: int | None = None):
         self.arrival[seq] = it
-        self.prompt[seq] = prompt_len
+        self.target[seq] = target
+        self.tokens[seq] = []
 
-    def step(self, it: int, decode_seqs, prefill_seqs, prefill_starts, prefill_lens):
-        for s, a, n in zip(prefill_seqs, prefill_starts, prefill_lens):
-            s = int(s)
-            if a + n == self.prompt[s] and s not in self.tokens:
-                self.tokens[s] = [it]
+    def _token(self, seq: int, it: int):
+        t = self.tokens[seq]
+        cap = self.target[seq]
+        if cap is None or len(t) < cap:
+            t.append(it)
+
+    def step(self, it: int, decode_seqs, prefill_seqs, prefill_emits):
+        for s, e in zip(prefill_seqs, prefill_emits):
+            if e:
+                self._token(int(s), it)
         for s in decode_seqs:
-            self.tokens[int(s)].append(it)
+            self._token(int(s), it)
 
     def ttft(self) -> np.ndarray:
         """TTFT in iterations of every request that got its first token."""
-        return np.array([t[0] - self.arrival[s] + 1 for s, t in sorted(self.tokens.items())],
+        return np.array([t[0] - self.arrival[s] + 1 for s, t in sorted(self.tokens.items()) if t],
                         dtype=np.int64)
 
     def itl(self) -> np.ndarray:
@@ -292,3 +300,41 @@ class LatencyLog:
 
         return {"ttft": stats(t), "itl": stats(g),
                 "clock": f"iterations x {ms_per_iteration:.4f} ms measured per iteration"}
+
+    def timed(self, arrival_ms: dict, end_ms, ttft_slo_ms: float, itl_slo_ms: float,
+              wall_s: float) -> dict:
+        """Latency on measured time: ``end_ms[i]`` is when iteration i's
+        kernels ended and ``arrival_ms[seq]`` when the request arrived, on one
+        clock.  TTFT = end of the first token's iteration - arrival; each
+        inter-token latency = the gap between the ends of consecutive token
+        iterations.  Goodput counts the output tokens of the requests that met
+        both targets (TTFT within ``ttft_slo_ms`` and every inter-token gap
+        within ``itl_slo_ms``) per second of ``wall_s``."""
+        end_ms = np.asarray(end_ms, dtype=np.float64)
+        ttft, gaps, good_tok, good_req, out_tok = [], [], 0, 0, 0
+        for s, t in sorted(self.tokens.items()):
+            if not t:
+                continue
+            e = end_ms[np.asarray(t)]
+            f = float(e[0] - arrival_ms[s])
+            g = np.diff(e)
+            ttft.append(f)
+            gaps.append(g)
+            out_tok += len(t)
+            if f <= ttft_slo_ms and (len(g) == 0 or float(g.max()) <= itl_slo_ms):
+                good_tok += len(t)
+                good_req += 1
+        ttft = np.asarray(ttft)
+        gaps = np.concatenate(gaps) if gaps else np.zeros(0)
+
+        def stats(x):
+            if len(x) == 0:
+                return {"n": 0}
+            return {"n": int(len(x)), "mean_ms": float(x.mean()),
+                    "p50_ms": float(np.percentile(x, 50)), "p99_ms": float(np.percentile(x, 99)),
+                    "max_ms": float(x.max())}
+
+        return {"ttft": stats(ttft), "itl": stats(gaps), "output_tokens": out_tok,
+                "output_tokens_per_s": out_tok / wall_s,
+                "goodput_tokens_per_s": good_tok / wall_s, "slo_met_requests": good_req,
+                "slo": {"ttft_ms": ttft_slo_ms, "itl_ms": itl_slo_ms}}

@@ -18,10 +18,10 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 class CSide:
-    def __init__(self, num_blocks, max_running, budget, free_order=None):
+    def __init__(self, num_blocks, max_running, budget, free_order=None, mode="chunked"):
         st, self.pool = pa.pa_pool_create(num_blocks, 16, free_order)
         pa.check(st)
-        st, self.sch = pa.pa_sched_create(self.pool, max_running, budget, 16)
+        st, self.sch = pa.pa_sched_create_mode(self.pool, mode, max_running, budget, 16)
         pa.check(st)
         self.b = pa.SchedBatch(max_running, budget)
 
@@ -40,7 +40,7 @@ class CSide:
             k += n
         return {"finished": fin, "admitted": adm, "preempted": pre,
                 "decode": [[s, p, sl] for s, p, sl in zip(ds.tolist(), dp.tolist(), dsl.tolist())],
-                "prefill": prefill}
+                "prefill": prefill, "emits": [bool(e) for e in self.b.emits()]}
 
     def free_list(self):
         st, fl = pa.pa_pool_free_list(self.pool)
@@ -60,7 +60,8 @@ class CSide:
 def _oracle_batch(b):
     return {"finished": list(b.finished), "admitted": list(b.admitted),
             "preempted": list(b.preempted), "decode": [list(x) for x in b.decode],
-            "prefill": [[s, a, n, list(sl)] for s, a, n, sl in b.prefill]}
+            "prefill": [[s, a, n, list(sl)] for s, a, n, sl in b.prefill],
+            "emits": list(b.emits)}
 
 
 def test_hand_worked_traces_through_c():
@@ -71,15 +72,16 @@ def test_hand_worked_traces_through_c():
             for sid, p, o in tr["arrivals"].get(str(it), []):
                 c.add(sid, p, o)
             got = c.step()
+            del got["emits"]
             got["free"] = c.free_list()
             assert got == want, (tr["name"], it, got, want)
         c.close()
 
 
-def _compare(w, max_running, budget, check_free_every=1):
-    c = CSide(w.num_blocks, max_running, budget)
+def _compare(w, max_running, budget, check_free_every=1, mode="chunked"):
+    c = CSide(w.num_blocks, max_running, budget, mode=mode)
     pool = BlockPool(w.num_blocks, 16)
-    o = Scheduler(pool, max_running, budget)
+    o = Scheduler(pool, max_running, budget, mode=mode)
     totals = {"decode": 0, "prefill": 0, "preempted": 0}
     for it in range(w.iters):
         for sid, p, n in w.arrivals[it]:
@@ -151,9 +153,11 @@ def test_step_rejects_small_capacities_without_change():
 def test_latency_log_matches_oracle_token_times():
     """TTFT and inter-token gaps (iteration clock) from the C scheduler's
     batches through LatencyLog equal those counted directly, with test-local
-    code, from the oracle scheduler's batches: first token at the iteration
-    whose slice completes the prompt, one more per decode iteration.  The
-    pool is small enough to preempt."""
+    code, from the oracle scheduler's batches: a token at every iteration
+    whose slice completes the sequence's known tokens (the first token, or
+    the one after a recomputation), one more per decode iteration.  The
+    pool is small enough to preempt, and every finished request has exactly
+    its target count of tokens."""
     from paged_kv_cache_host_amd.iteration import LatencyLog
     w = make_trace(seed=33, iters=300, lam=0.3, prompt_median=60, prompt_sigma=1.0,
                    prompt_cap=400, out_mean=20, num_blocks=60)
@@ -166,21 +170,23 @@ def test_latency_log_matches_oracle_token_times():
         for sid, p, n in w.arrivals[it]:
             c.add(sid, p, n)
             o.add(sid, p, n)
-            log.add(it, sid, p)
-            arrive[sid], prompt[sid] = it, p
+            log.add(it, sid, n)
+            arrive[sid], times[sid] = it, []
         c.step()
         ds, _, _ = c.b.decode()
-        ps, pst, pl = c.b.prefill()
-        log.step(it, ds, ps, pst, pl)
+        log.step(it, ds, c.b.prefill()[0], c.b.emits())
         b = o.step()
         preempted += len(b.preempted)
+        o_seq = {x.sid: x for x in o.running + o.done}
         for s, a, n, _ in b.prefill:
-            if a + n == prompt[s] and s not in times:
-                times[s] = [it]
+            if a + n == o_seq[s].known:
+                times[s].append(it)
         for s, _, _ in b.decode:
             times[s].append(it)
     c.close()
-    want_ttft = [times[s][0] - arrive[s] + 1 for s in sorted(times)]
+    for x in o.done:
+        assert len(times[x.sid]) == x.target, x.sid
+    want_ttft = [times[s][0] - arrive[s] + 1 for s in sorted(times) if times[s]]
     want_gaps = [b_ - a_ for s in sorted(times) for a_, b_ in zip(times[s], times[s][1:])]
     assert preempted > 0 and len(want_ttft) > 20
     assert log.ttft().tolist() == want_ttft
