@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode step (no mixed chunked-prefill or fp8 legs)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=32)
+    ap.add_argument("--modes-only", action="store_true",
+                    help="only the four-schedule serving comparison (printed as one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain streaming kernel of known size (HBM counter calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR",
@@ -928,6 +930,66 @@ def trace_leg(args, dev):
     return out
 
 
+def modes_leg(args, dev):
+    """The four schedules of the LESSON's simulator ("Use It": one request at
+    a time, padded static batches, continuous batching with whole-prompt
+    prefill, continuous batching with 512-token chunks) serving the same
+    timed requests on one layer through the paged kernels, on a live clock:
+    requests join when their arrival time has passed, every iteration's end
+    is timed by an event.  Reports per schedule output tokens/s, mean and
+    P99 time to first token, P50/P99/max inter-token latency and goodput
+    (output tokens of the requests whose TTFT and every inter-token gap met
+    the targets: one layer's 1/80 share of 1 s and 50 ms)."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_host_amd.iteration import LayerIterations, serve
+
+    reqs = workloads.timed_requests()
+    R, CAP = 64, 8192
+    budgets = {"naive": CAP, "static": 8 * CAP, "continuous": CAP, "chunked": 512}
+    ttft_slo, itl_slo = 1000.0 / 80, 50.0 / 80
+    max_ctx = max(r[2] for r in reqs) + max(r[3] for r in reqs)
+    num_blocks = 16384
+    ring_n = R + max(budgets.values())
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    k_ring = torch.randn((ring_n, H_KV, D), generator=gen, device=dev).to(torch.bfloat16)
+    v_ring = torch.randn((ring_n, H_KV, D), generator=gen, device=dev).to(torch.bfloat16)
+    q_ring = torch.randn((ring_n, H_Q, D), generator=gen, device=dev).to(torch.bfloat16)
+
+    def provider(seqs, positions):
+        n = len(seqs)
+        return k_ring[:n], v_ring[:n], q_ring[:n]
+
+    out = {"workload": (f"{len(reqs)} requests, Poisson arrivals at 2 per ms, lognormal prompts "
+                        "(median 512, sigma 1.2, cap 8192), geometric outputs (mean 64, cap 512), "
+                        f"<= {R} running, pool {num_blocks} blocks, 64/8 heads, d128, bf16, one "
+                        "layer; live clock"),
+           "prefill_budget": budgets,
+           "slo_ms": {"ttft": ttft_slo, "itl": itl_slo}, "modes": {}}
+    for mode in ("naive", "static", "continuous", "chunked"):
+        run = LayerIterations(num_blocks, H_Q, H_KV, D, dev, provider, R, budgets[mode],
+                              max_context=max_ctx, provider_syncs=False, mode=mode)
+        torch.cuda.synchronize()
+        r = serve(run, reqs, ttft_slo, itl_slo)
+        run.close()
+        del run
+        torch.cuda.empty_cache()
+        out["modes"][mode] = {
+            "output_tokens_per_s": round(r["output_tokens_per_s"], 1),
+            "goodput_tokens_per_s": round(r["goodput_tokens_per_s"], 1),
+            "slo_met_requests": r["slo_met_requests"],
+            "ttft_ms": {k: round(r["ttft"][k], 3) for k in ("mean_ms", "p99_ms")},
+            "itl_ms": {k: round(r["itl"][k], 4) for k in ("p50_ms", "p99_ms", "max_ms")},
+            "iterations": r["iterations"], "wall_s": round(r["wall_s"], 4),
+            "preemptions": r["preemptions"], "prefill_tokens": r["prefill_tokens"],
+            "output_tokens": r["output_tokens"]}
+        print(f"modes leg: {mode} done ({r['iterations']} iterations)", file=sys.stderr,
+              flush=True)
+    return out
+
+
 def cpu_prefill_baseline():
     """The oracle on one 512-token slice at prefix 512 (gather + fp64 causal
     attention of all 64 heads), as GFLOP/s on the algorithmic count."""
@@ -986,6 +1048,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     K, W = args.steps, args.warmup
+    if args.modes_only:
+        print(json.dumps({"schedules": modes_leg(args, dev)}), flush=True)
+        return
 
     d = decode_leg(args, dev)
     digest = kernel_source_digest()
@@ -1027,6 +1092,7 @@ def main():
         result["prefix_sharing"] = prefix_leg(args, dev)
         result["block_size"] = block_size_leg(args, dev)
         result["trace"] = trace_leg(args, dev)
+        result["schedules"] = modes_leg(args, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample_seqs)
         if "mixed" in result:

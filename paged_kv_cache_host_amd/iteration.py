@@ -35,7 +35,8 @@ class LayerIterations:
                  max_running: int = 256, prefill_budget: int = 512, max_context: int = 40960,
                  cache_blocks: int | None = None, cache_dtype: str = "bf16",
                  k_scale: float = 1.0, v_scale: float = 1.0, sm_scale: float | None = None,
-                 free_order=None, provider_syncs: bool = True, two_streams: bool = False):
+                 free_order=None, provider_syncs: bool = True, two_streams: bool = False,
+                 mode: str = "chunked"):
         self.h_q, self.h_kv, self.d = h_q, h_kv, d
         self.dev = torch.device(device)
         self.provider = provider
@@ -48,7 +49,8 @@ class LayerIterations:
         self.sm = sm_scale if sm_scale is not None else float(np.float32(1.0) / np.float32(np.sqrt(d)))
         st, self.pool = pa.pa_pool_create(num_blocks, BLOCK, free_order)
         pa.check(st)
-        st, self.sched = pa.pa_sched_create(self.pool, max_running, prefill_budget, BLOCK)
+        st, self.sched = pa.pa_sched_create_mode(self.pool, mode, max_running, prefill_budget,
+                                                 BLOCK)
         pa.check(st)
         self.batch = pa.SchedBatch(max_running, prefill_budget)
         # Device cache: blocks [0, cache_blocks) are backed (all of the pool
@@ -78,8 +80,15 @@ class LayerIterations:
                        for _ in range(2)]
         n = pa.pa_decode_workspace_bytes(max_running, h_q, h_kv, d, max_context)
         self.ws_dec = torch.zeros(max(n, 1), dtype=torch.uint8, device=self.dev)
-        n = max(pa.pa_prefill_workspace_bytes(c, max(prefill_budget, 1), h_q, h_kv, d, max_context)
-                for c in range(1, max_running + 1))
+        # the launch's key split (hence its workspace) depends on its slice
+        # count and longest slice, through whole 32-row position tiles: cover
+        # every count and every multiple of 32 up to the budget (a slice
+        # longer than 32768 spans more than 128 position tiles and is never
+        # split) and the budget itself
+        top = max(prefill_budget, 1)
+        q_lens = sorted({top} | set(range(32, min(top, 32768) + 1, 32)))
+        n = max(pa.pa_prefill_workspace_bytes(c, q, h_q, h_kv, d, max_context)
+                for c in range(1, max_running + 1) for q in q_lens)
         self.ws_pf = torch.empty(max(n, 1), dtype=torch.uint8, device=self.dev)
         self.compute = torch.cuda.Stream(device=self.dev)
         # two_streams: the prefill slices run on a second stream, after the
@@ -136,6 +145,7 @@ class LayerIterations:
         self.totals["finished"] += len(fin)
         st, acc = pa.pa_sched_stats(self.sched)
         pa.check(st)
+        self.acc = acc
         held = acc["blocks_held"] * BLOCK
         self.waste.append(float("nan") if held == 0 else 1.0 - acc["tokens_held"] / held)
         self.unwritten.append(float("nan") if held == 0 else acc["unwritten"] / held)
@@ -338,3 +348,64 @@ class LatencyLog:
                 "output_tokens_per_s": out_tok / wall_s,
                 "goodput_tokens_per_s": good_tok / wall_s, "slo_met_requests": good_req,
                 "slo": {"ttft_ms": ttft_slo_ms, "itl_ms": itl_slo_ms}}
+
+
+def serve(run: LayerIterations, requests, ttft_slo_ms: float, itl_slo_ms: float,
+          max_iters: int = 1_000_000, timeout_s: float = 120.0) -> dict:
+    """Serves ``requests`` [(arrival_ms, id, prompt_len, output_len)] (in
+    arrival order) through ``run`` on a live clock until every request has
+    been released: before each iteration the requests whose arrival time
+    has passed join the queue; when nothing runs or waits the host sleeps
+    until the next arrival.  The end of every iteration is timed by an event
+    on the compute stream; the host clock starts when a start event on that
+    stream has completed, so arrival and end times share an origin (to the
+    latency of that one synchronisation).  Returns the latency summary of
+    ``LatencyLog.timed`` plus the iteration count and wall time (first
+    arrival to the last iteration's end)."""
+    import time
+
+    log = LatencyLog()
+    arrival = {}
+    ends = []
+    run.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    start.record(run.compute)
+    start.synchronize()
+    t0 = time.perf_counter()
+    i, n, it = 0, len(requests), 0
+    added = False
+    while run.totals["finished"] < n:
+        now = (time.perf_counter() - t0) * 1e3
+        while i < n and requests[i][0] <= now:
+            a, sid, p, o = requests[i]
+            run.add(sid, p, o)
+            log.add(it, sid, o)
+            arrival[sid] = a
+            added = True
+            i += 1
+        idle = it == 0 or (run.acc["running"] == 0 and run.acc["waiting"] == 0)
+        if idle and not added:
+            if i >= n:
+                raise RuntimeError("serve: requests left unfinished with nothing queued")
+            time.sleep(max(0.0, requests[i][0] / 1e3 - (time.perf_counter() - t0)))
+            continue
+        run.step()
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(run.compute)
+        ends.append(ev)
+        b = run.batch
+        log.step(it, b.decode()[0], b.prefill()[0], b.emits())
+        added = False
+        it += 1
+        if it >= max_iters or time.perf_counter() - t0 > timeout_s:
+            raise RuntimeError(f"serve: {run.totals['finished']} of {n} requests finished "
+                               f"after {it} iterations")
+    run.synchronize()
+    end_ms = np.array([start.elapsed_time(e) for e in ends])
+    wall_s = float(end_ms[-1] - requests[0][0]) / 1e3
+    out = log.timed(arrival, end_ms, ttft_slo_ms, itl_slo_ms, wall_s)
+    out.update({"iterations": it, "wall_s": wall_s,
+                "preemptions": run.totals["preempted"],
+                "prefill_tokens": run.totals["prefill_tokens"],
+                "decode_tokens": run.totals["decode_tokens"]})
+    return out

@@ -1,7 +1,7 @@
 """The four schedules of the LESSON's simulator ("Use It": one request at a
 time, padded static batches, iteration-level admission without chunking,
 and chunked continuous batching) in the C scheduler (pa_sched_create_mode):
-bit-exact against the oracle scheduler on random traces, and pinned to
+bit-exact against the oracle scheduler on random traces, and both pinned to
 what the descriptions fix independently of either implementation: a
 hand-worked static batch, the service recurrence of one-at-a-time
 serving, the shape of every static batch, the reduction of the unchunked
@@ -14,7 +14,33 @@ import paged_kv_cache_host_amd._pa as pa
 from paged_kv_cache_host_amd.iteration import LatencyLog
 from workloads import trace as make_trace
 
-from test_host_scheduler import CSide, _compare
+from oracle.allocator import BlockPool
+from oracle.scheduler import Scheduler
+from test_host_scheduler import CSide, _compare, _oracle_batch
+
+
+class OSide:
+    """The oracle scheduler behind CSide's interface, so that every pin
+    below holds the oracle and the C scheduler to the same facts."""
+
+    def __init__(self, num_blocks, max_running, budget, mode="chunked"):
+        self.pool = BlockPool(num_blocks, 16)
+        self.sch = Scheduler(self.pool, max_running, budget, mode=mode)
+
+    def add(self, sid, p, o):
+        self.sch.add(sid, p, o)
+
+    def step(self):
+        return _oracle_batch(self.sch.step())
+
+    def free_list(self):
+        return list(self.pool.free_list())
+
+    def close(self):
+        pass
+
+
+side = pytest.mark.parametrize("make", [CSide, OSide], ids=["c", "oracle"])
 
 
 def _drive(c, w, iters=None):
@@ -40,7 +66,8 @@ def test_modes_match_oracle(mode, budget, max_running, num_blocks):
         assert totals["preempted"] > 0
 
 
-def test_static_hand_worked():
+@side
+def test_static_hand_worked(make):
     """Two slots, budget 100, a 100-block FIFO pool; A (prompt 20, 2 tokens),
     B (40, 1) and C (10, 1) arrive together.  Iteration 0 forms the batch
     [A, B] padded to 40 tokens (2 x 40 <= 100) and prefills both whole (A:
@@ -48,7 +75,7 @@ def test_static_hand_worked():
     is padding: it already has its one token); iteration 2 releases the
     batch (A's blocks then B's go to the back of the free list) and forms
     [C], which takes block 6."""
-    c = CSide(100, 2, 100, mode="static")
+    c = make(100, 2, 100, mode="static")
     for sid, p, n in ((0, 20, 2), (1, 40, 1), (2, 10, 1)):
         c.add(sid, p, n)
     b0, b1, b2, b3 = (c.step() for _ in range(4))
@@ -64,7 +91,8 @@ def test_static_hand_worked():
     c.close()
 
 
-def test_naive_service_recurrence():
+@side
+def test_naive_service_recurrence(make):
     """One request at a time on a roomy pool: request k is admitted at
     a_k = max(arrival_k, a_(k-1) + P_(k-1) + t_(k-1) - 1), where P =
     ceil(prompt / budget) prefill iterations and t its target (its last token
@@ -73,7 +101,7 @@ def test_naive_service_recurrence():
     w = make_trace(seed=43, iters=600, lam=0.05, prompt_median=60, prompt_sigma=1.0,
                    prompt_cap=400, out_mean=8, num_blocks=4000)
     B = 64
-    c = CSide(w.num_blocks, 16, B, mode="naive")
+    c = make(w.num_blocks, 16, B, mode="naive")
     batches = _drive(c, w)
     c.close()
     admitted_at = {s: it for it, b in enumerate(batches) for s in b["admitted"]}
@@ -92,7 +120,8 @@ def test_naive_service_recurrence():
         assert len(b["decode"]) + len({x[0] for x in b["prefill"]}) <= 1
 
 
-def test_static_batch_shape():
+@side
+def test_static_batch_shape(make):
     """Every static batch on a roomy pool: formed only when nothing runs, from
     the heads of the queue; its prompts all prefilled, whole and padded to the
     longest, in the iteration that forms it (members x longest <= budget); the
@@ -100,7 +129,7 @@ def test_static_batch_shape():
     w = make_trace(seed=44, iters=500, lam=0.3, prompt_median=60, prompt_sigma=1.0,
                    prompt_cap=400, out_mean=10, num_blocks=8000)
     R, B = 8, 1600
-    c = CSide(w.num_blocks, R, B, mode="static")
+    c = make(w.num_blocks, R, B, mode="static")
     batches = _drive(c, w)
     c.close()
     req = {sid: (p, n) for row in w.arrivals for sid, p, n in row}
@@ -128,19 +157,21 @@ def test_static_batch_shape():
     assert n_batches > 5
 
 
-def test_continuous_reduces_to_chunked_when_budget_never_binds():
+@side
+def test_continuous_reduces_to_chunked_when_budget_never_binds(make):
     """With a budget above every iteration's prompt tokens, whole-prompt
     admission and chunked admission make the same decisions."""
     w = make_trace(seed=45, iters=300, lam=0.3, prompt_median=60, prompt_sigma=1.0,
                    prompt_cap=400, out_mean=20, num_blocks=4000)
     big = 16 * 400 + 1
-    a, b = CSide(w.num_blocks, 16, big, mode="continuous"), CSide(w.num_blocks, 16, big)
+    a, b = make(w.num_blocks, 16, big, mode="continuous"), make(w.num_blocks, 16, big)
     assert _drive(a, w) == _drive(b, w)
     a.close()
     b.close()
 
 
-def test_continuous_prefills_whole_prompts():
+@side
+def test_continuous_prefills_whole_prompts(make):
     """A binding budget: every prompt that fits the budget is prefilled in one
     slice, in the iteration that admits it; longer ones are sliced at the
     budget in iterations with no other prefill (their last slice may leave
@@ -148,7 +179,7 @@ def test_continuous_prefills_whole_prompts():
     w = make_trace(seed=46, iters=300, lam=0.5, prompt_median=60, prompt_sigma=1.0,
                    prompt_cap=400, out_mean=20, num_blocks=4000)
     B = 128
-    c = CSide(w.num_blocks, 16, B, mode="continuous")
+    c = make(w.num_blocks, 16, B, mode="continuous")
     batches = _drive(c, w)
     c.close()
     req = {sid: p for row in w.arrivals for sid, p, _ in row}

@@ -285,6 +285,24 @@ def trace(seed: int = 5, iters: int = 1000, lam: float = 0.5, prompt_median: flo
     return TraceWorkload(f"trace-{iters}it-lam{lam}", iters, arrivals, num_blocks, None)
 
 
+def timed_requests(seed: int = 7, n: int = 256, rate_per_ms: float = 2.0,
+                   prompt_median: float = 512.0, prompt_sigma: float = 1.2,
+                   prompt_cap: int = 8192, out_mean: float = 64.0, out_cap: int = 512):
+    """Requests on a time axis for serving-schedule comparisons: a Poisson
+    process (``rate_per_ms`` arrivals per millisecond), lognormal prompts
+    (median 512, sigma 1.2, cap 8192), geometric outputs (mean 64, cap 512).
+    Returns [(arrival_ms, id, prompt_len, output_len)] in arrival order."""
+    rng = np.random.default_rng(seed)
+    gaps = rng.exponential(1.0 / rate_per_ms, n)
+    t = np.cumsum(gaps) - gaps[0]
+    out = []
+    for i in range(n):
+        p = int(min(prompt_cap, math.ceil(rng.lognormal(math.log(prompt_median), prompt_sigma))))
+        o = int(min(out_cap, rng.geometric(1.0 / out_mean)))
+        out.append((float(t[i]), i, max(1, p), o))
+    return out
+
+
 @dataclass
 class PrefillWorkload:
     """Prompts whose K/V are all written, then attended by prefill slices
