@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="decode step: the append launch on a second stream")
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--stage-ahead", action="store_true",
+                    help="decode step: stage the metadata on a side stream ahead of the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode step (no mixed chunked-prefill or fp8 legs)")
@@ -346,6 +348,10 @@ def decode_leg(args, dev):
     # step i's contexts and table entries step i does not read (or rewrites
     # one with its own value), and the decode of step i+1 waits for it.
     aux = torch.cuda.Stream(device=dev) if getattr(args, "overlap", False) else compute
+    # With --stage-ahead only the 1 KiB metadata copy runs on a side stream
+    # (pa_stage, one work-group), and pa_decode_append on the compute stream
+    # reads the staged slots and lengths from device memory.
+    ahead = torch.cuda.Stream(device=dev) if getattr(args, "stage_ahead", False) else None
     ev_w = [torch.cuda.Event() for _ in range(2)]
     ev_group = [torch.cuda.Event() for _ in range(2)]
     for e in ev_group:
@@ -365,12 +371,22 @@ def decode_leg(args, dev):
         h_lens[:] = lens_host
         lens_np = lens_host
         r = i % R
-        # one launch stages the buffer, scatters the new tokens (whose slots
-        # lead the buffer) and enters the blocks they open in the tables
-        pa.check(pa.pa_stage_decode_append(aux, dev_buf[X], host_buf[X], 4 * n_meta, 0, 4 * S,
-                                           S, k_ring[r], v_ring[r], kv.k, kv.v, num_blocks, H_KV,
-                                           D, d_tab, BLOCK))
-        if aux is not compute:
+        if ahead is not None:
+            # the buffer is staged on the side stream as soon as it is packed
+            # (during an earlier step's decode); the compute stream then only
+            # scatters the new tokens and enters their blocks
+            pa.check(pa.pa_stage(ahead, dev_buf[X], host_buf[X], 4 * n_meta))
+            ev_w[i % 2].record(ahead)
+            compute.wait_event(ev_w[i % 2])
+            pa.check(pa.pa_decode_append(compute, dev_buf[X][:S], d_lens, S, k_ring[r], v_ring[r],
+                                         kv.k, kv.v, num_blocks, H_KV, D, d_tab, BLOCK))
+        else:
+            # one launch stages the buffer, scatters the new tokens (whose
+            # slots lead the buffer) and enters the blocks they open
+            pa.check(pa.pa_stage_decode_append(aux, dev_buf[X], host_buf[X], 4 * n_meta, 0,
+                                               4 * S, S, k_ring[r], v_ring[r], kv.k, kv.v,
+                                               num_blocks, H_KV, D, d_tab, BLOCK))
+        if ahead is None and aux is not compute:
             ev_w[i % 2].record(aux)
             compute.wait_event(ev_w[i % 2])
         pa.check(pa.pa_decode(compute, out, q_ring[r], kv.k, kv.v, d_tab, d_lens,

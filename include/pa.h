@@ -455,6 +455,27 @@ pa_status pa_stage_decode_append(void* stream, void* dst, const void* src_host, 
                                  float v_scale, int32_t* block_tables, int32_t max_blocks);
 
 /* ------------------------------------------------------------------------
+ * pa_decode_append -- pa_stage_decode_append with the slots and lengths
+ * already in device memory (for instance staged by pa_stage on another
+ * stream while the previous iteration's attention runs), so that the launch
+ * on the compute stream holds no host-memory read.  Same operation (ARTICLE
+ * 2.2 / 2.3: the new tokens' K/V into their slots, a block-table entry for
+ * each token that opens a block) and the same cache bytes and tables.
+ *
+ * slots, lens   [device, n] int32: the tokens' slots and their sequences'
+ *               context lengths (new token included); owned by the caller
+ * block_tables  [device, n x max_blocks] int32, updated in place
+ * k_new ... v_scale as for pa_cache_write; max_blocks >= 1.
+ * NULL buffers with n > 0 and the pa_cache_write argument errors are
+ * PA_ERR_INVALID; n == 0 launches nothing.
+ * ---------------------------------------------------------------------- */
+pa_status pa_decode_append(void* stream, const int32_t* slots, const int32_t* lens, int32_t n,
+                           const void* k_new, const void* v_new, pa_dtype new_dt, void* k_cache,
+                           void* v_cache, pa_dtype cache_dt, int32_t num_blocks, int32_t H_kv,
+                           int32_t D, int32_t bs, float k_scale, float v_scale,
+                           int32_t* block_tables, int32_t max_blocks);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (instrumentation, off by default).  Each launch of a
  * selected kernel carries a pair of HIP events attached to the launch
  * (hipExtLaunchKernel), which take that kernel's start and end times (up to

@@ -96,6 +96,8 @@ _SIGS = {
     "pa_stage_decode_append": (_i32, [_vp, _vp, _vp, _sz, _sz, _sz, _vp, _vp, _i32, _i32, _vp,
                                        _vp, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _vp,
                                        _i32]),
+    "pa_decode_append": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
+                                 _i32, _i32, _f32, _f32, _vp, _i32]),
     "pa_timing_enable": (_i32, [_i32, _i32]),
     "pa_timing_query": (_i32, [C.c_char_p, _i32p, C.POINTER(_f32), C.POINTER(_f32)]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -487,6 +489,25 @@ def pa_stage_decode_append(stream, dst, src_host, nbytes: int, slot_offset: int,
                                        _dptr(v_cache), dtype_of(k_cache), num_blocks, H_kv, D, bs,
                                        k_scale, v_scale, _dptr(block_tables),
                                        block_tables.shape[1])
+
+
+def pa_decode_append(stream, slots, lens, n: int, k_new, v_new, k_cache, v_cache,
+                     num_blocks: int, H_kv: int, D: int, block_tables, bs: int = 16,
+                     k_scale: float = 1.0, v_scale: float = 1.0) -> int:
+    """pa_stage_decode_append with the ``n`` slots and context lengths
+    already in device int32 tensors (``slots``, ``lens``)."""
+    for name, t in (("slots", slots), ("lens", lens)):
+        if str(t.dtype) != "torch.int32" or not t.is_contiguous() or t.numel() < n:
+            raise PaError(PA_ERR_INVALID, f"pa_decode_append: {name} must be a contiguous int32 "
+                          "tensor of at least n entries")
+    if str(block_tables.dtype) != "torch.int32" or not block_tables.is_contiguous() or \
+            block_tables.dim() != 2 or block_tables.shape[0] < n:
+        raise PaError(PA_ERR_INVALID, "pa_decode_append: block_tables must be a contiguous "
+                      "int32 [n, max_blocks] tensor")
+    return _lib.pa_decode_append(_stream_handle(stream), _dptr(slots), _dptr(lens), n,
+                                 _dptr(k_new), _dptr(v_new), dtype_of(k_new), _dptr(k_cache),
+                                 _dptr(v_cache), dtype_of(k_cache), num_blocks, H_kv, D, bs,
+                                 k_scale, v_scale, _dptr(block_tables), block_tables.shape[1])
 
 
 def pa_decode_workspace_bytes(S: int, H_q: int, H_kv: int, D: int, max_context_len: int) -> int:

@@ -386,3 +386,27 @@ extern "C" pa_status pa_stage_decode_append(void* stream, void* dst, const void*
                                 num_blocks, H_kv, D, bs, k_scale, v_scale, &lens_offset,
                                 block_tables, max_blocks);
 }
+
+extern "C" pa_status pa_decode_append(void* stream, const int32_t* slots, const int32_t* lens,
+                                      int32_t n, const void* k_new, const void* v_new,
+                                      pa_dtype new_dt, void* k_cache, void* v_cache,
+                                      pa_dtype cache_dt, int32_t num_blocks, int32_t H_kv,
+                                      int32_t D, int32_t bs, float k_scale, float v_scale,
+                                      int32_t* block_tables, int32_t max_blocks) {
+  const char* who = "pa_decode_append";
+  CwPlan plan;
+  const pa_status chk = cw_check(who, k_new, v_new, new_dt, n, k_cache, v_cache, cache_dt,
+                                 num_blocks, H_kv, D, bs, k_scale, v_scale, &plan);
+  if (chk != PA_OK) return chk;
+  if (max_blocks < 1) return fail(PA_ERR_INVALID, "%s: max_blocks=%d < 1", who, max_blocks);
+  if (n == 0) return PA_OK;
+  if (!slots || !lens || !block_tables) return fail(PA_ERR_INVALID, "%s: NULL buffer", who);
+  TableUpkeep tu;
+  tu.tables = block_tables;
+  tu.max_blocks = max_blocks;
+  tu.lens_dev = lens;
+  // no words to stage: every work-group writes K/V (and table entries)
+  return launch_scw_types<uint64_t>(plan, D, static_cast<hipStream_t>(stream), nullptr, nullptr, 0,
+                                    slots, k_new, v_new, n, k_cache, v_cache, num_blocks, H_kv,
+                                    tu);
+}

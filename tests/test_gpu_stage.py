@@ -147,14 +147,17 @@ def test_stage_cache_write_rejects_bad_arguments():
                                     fake, fake, 1, 10, 2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
 
 
+@pytest.mark.parametrize("device_meta", [False, True], ids=["staged", "device"])
 @pytest.mark.parametrize("cache_dt,d", [("bf16", 128), ("fp8", 128), ("bf16", 64)])
-def test_stage_decode_append_keeps_device_tables(cache_dt, d):
+def test_stage_decode_append_keeps_device_tables(cache_dt, d, device_meta):
     """Decode iterations whose block tables stay on the device: after every
     iteration each row equals the allocator's table (pa_pack_batch) entry for
     entry over its context, and the cache bytes and the staged copy equal
     those of pa_stage_cache_write on the same data.  Contexts start at and
     around block boundaries; one iteration carries a slot outside the pool
-    and a length beyond the row, which leave their rows unchanged."""
+    and a length beyond the row, which leave their rows unchanged.
+    ``device``: pa_decode_append reads the slots and lengths that
+    pa_stage_cache_write staged into device memory."""
     from paged_kv_cache_host_amd.engine import _TORCH_STORAGE
     rng = np.random.default_rng(911)
     S, h_kv, steps = 37, 2, 40
@@ -179,7 +182,8 @@ def test_stage_decode_append_keeps_device_tables(cache_dt, d):
         h = host.numpy()
         g = torch.Generator(device=DEV)
         g.manual_seed(912)
-        say(f"[stage_decode_append] {cache_dt} d{d} S={S} steps={steps} max_blocks={MB}")
+        say(f"[stage_decode_append] {cache_dt} d{d} S={S} steps={steps} max_blocks={MB} "
+            f"device_meta={device_meta}")
         for it in range(steps):
             st_, done, slots = pa.pa_batch_append(pool, seqs, 1)
             assert st_ == pa.PA_OK and done == S
@@ -198,11 +202,17 @@ def test_stage_decode_append_keeps_device_tables(cache_dt, d):
             assert pa.pa_stage_cache_write(None, dsts[0], host, 4 * (2 * S + 3), 0, S, kn, vn,
                                            caches[0][0], caches[0][1], nb, h_kv, d, 16, 0.03,
                                            0.05) == 0
-            assert pa.pa_stage_decode_append(None, dsts[1], host, 4 * (2 * S + 3), 0, 4 * S, S,
-                                             kn, vn, caches[1][0], caches[1][1], nb, h_kv, d,
-                                             d_tab, 16, 0.03, 0.05) == 0
+            if device_meta:
+                assert pa.pa_decode_append(None, dsts[0][:S], dsts[0][S:2 * S], S, kn, vn,
+                                           caches[1][0], caches[1][1], nb, h_kv, d, d_tab, 16,
+                                           0.03, 0.05) == 0
+            else:
+                assert pa.pa_stage_decode_append(None, dsts[1], host, 4 * (2 * S + 3), 0, 4 * S,
+                                                 S, kn, vn, caches[1][0], caches[1][1], nb, h_kv,
+                                                 d, d_tab, 16, 0.03, 0.05) == 0
             torch.cuda.synchronize()
-            assert torch.equal(dsts[0].cpu(), dsts[1].cpu())
+            if not device_meta:
+                assert torch.equal(dsts[0].cpu(), dsts[1].cpu())
             for a, b in zip(caches[0], caches[1]):
                 assert torch.equal(a.view(torch.uint8).cpu(), b.view(torch.uint8).cpu())
             got = d_tab.cpu().numpy()

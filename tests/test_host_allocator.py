@@ -257,6 +257,31 @@ def test_stage_decode_append_argument_checks_on_host():
     assert call(nbytes=0, n=0) == 0                              # nothing to do
 
 
+def test_decode_append_argument_checks_on_host():
+    fake = 0x1000
+    lib = pa._pa._lib
+    # (stream, slots, lens, n, k, v, new_dt, kc, vc, cache_dt, num_blocks, H_kv, D, bs,
+    #  k_scale, v_scale, tables, max_blocks)
+    ok = [None, fake, fake, 4, fake, fake, 1, fake, fake, 1, 10, 2, 64, 16, 1.0, 1.0, fake, 8]
+    names = ["stream", "slots", "lens", "n", "k", "v", "new_dt", "kc", "vc", "cache_dt",
+             "num_blocks", "h_kv", "d", "bs", "k_scale", "v_scale", "tables", "max_blocks"]
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return lib.pa_decode_append(*args)
+
+    # all rejected before any HIP call
+    assert call(slots=None) == pa.PA_ERR_INVALID
+    assert call(lens=None) == pa.PA_ERR_INVALID
+    assert call(tables=None) == pa.PA_ERR_INVALID
+    assert call(max_blocks=0) == pa.PA_ERR_INVALID
+    assert call(bs=8) == pa.PA_ERR_INVALID                       # as pa_cache_write
+    assert call(d=96) == pa.PA_ERR_INVALID
+    assert call(n=0) == 0                                        # nothing to do
+
+
 def test_prefix_sharing_golden_trace_through_c_abi():
     g = json.load(open(os.path.join(GOLDEN, "prefix_sharing_trace.json")))
     st_, pool = pa.pa_pool_create(g["num_blocks"], g["block_size"], g["initial_free_order"])
