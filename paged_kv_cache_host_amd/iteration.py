@@ -340,7 +340,7 @@ class LatencyLog:
         def stats(x):
             if len(x) == 0:
                 return {"n": 0}
-            return {"n": int(len(x)), "mean_ms": float(x.mean()),
+            return {"n": int(len(x)), "mean_ms": float(x.mean()), "min_ms": float(x.min()),
                     "p50_ms": float(np.percentile(x, 50)), "p99_ms": float(np.percentile(x, 99)),
                     "max_ms": float(x.max())}
 

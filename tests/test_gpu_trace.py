@@ -189,3 +189,40 @@ def test_trace_iterations_pipelined_match_oracle(two_streams):
     say(f"    checked {checked['decode']} decode tokens, {checked['prefill']} prefill tokens, "
         f"{len(written)} cache slots, {run.totals['preempted']} preemptions, max|d| = {worst:.3g}")
     assert run.totals["preempted"] > 0 and checked["decode"] > 50 and checked["prefill"] > 500
+
+
+@pytest.mark.parametrize("mode", ["chunked", "continuous", "static", "naive"])
+def test_serve_live_clock(mode):
+    """``serve`` on a live clock: every request is released with exactly its
+    target count of output tokens, one inter-token gap per token after the
+    first, a positive time to first token (no token before its arrival),
+    and every request within targets no schedule can miss."""
+    from paged_kv_cache_host_amd.iteration import LayerIterations, serve
+
+    reqs = workloads.timed_requests(seed=21, n=24, rate_per_ms=20.0, prompt_median=40,
+                                    prompt_cap=300, out_mean=6, out_cap=40)
+    say(f"[serve, {mode}] {len(reqs)} requests, budget {BUDGET[mode]}")
+    ring = 2 * (R + BUDGET[mode])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(22)
+    kr = torch.randn((ring, H_KV, D), generator=g, device="cuda").to(torch.bfloat16)
+    vr = torch.randn((ring, H_KV, D), generator=g, device="cuda").to(torch.bfloat16)
+    qr = torch.randn((ring, H_Q, D), generator=g, device="cuda").to(torch.bfloat16)
+
+    def provider(seqs, positions):
+        n = len(seqs)
+        return kr[:n], vr[:n], qr[:n]
+
+    max_ctx = max(r[2] for r in reqs) + max(r[3] for r in reqs)
+    run = LayerIterations(400, H_Q, H_KV, D, "cuda", provider, R, BUDGET[mode],
+                          max_context=max_ctx, provider_syncs=False, mode=mode)
+    r = serve(run, reqs, ttft_slo_ms=1e9, itl_slo_ms=1e9, timeout_s=60.0)
+    run.close()
+    assert run.totals["finished"] == len(reqs)
+    assert r["output_tokens"] == sum(x[3] for x in reqs)
+    assert r["slo_met_requests"] == len(reqs)        # targets no request can miss
+    assert r["ttft"]["n"] == len(reqs) and r["ttft"]["min_ms"] > 0
+    assert r["itl"]["n"] == sum(x[3] - 1 for x in reqs)
+    assert r["itl"]["max_ms"] >= 0 and r["iterations"] > max(x[3] for x in reqs)
+    say(f"    {r['iterations']} iterations, {r['wall_s'] * 1e3:.2f} ms, "
+        f"TTFT mean {r['ttft']['mean_ms']:.3f} ms")

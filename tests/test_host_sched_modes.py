@@ -228,7 +228,7 @@ def test_timed_latency_hand_worked():
     log.step(4, [1, 0], [], [])       # request 0 is past its target here
     r = log.timed({0: 0.5, 1: 1.0}, [1.0, 2.0, 4.0, 4.5, 8.0], 2.0, 2.5, 0.01)
     assert r["ttft"]["n"] == 2 and r["ttft"]["mean_ms"] == pytest.approx(1.75)
-    assert r["ttft"]["max_ms"] == pytest.approx(3.0)
+    assert r["ttft"]["max_ms"] == pytest.approx(3.0) and r["ttft"]["min_ms"] == pytest.approx(0.5)
     assert r["itl"]["n"] == 3 and r["itl"]["max_ms"] == pytest.approx(4.0)
     assert r["itl"]["mean_ms"] == pytest.approx(7.5 / 3)
     assert r["output_tokens"] == 5 and r["slo_met_requests"] == 1
