@@ -79,6 +79,11 @@ def parse():
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode step (no mixed chunked-prefill or fp8 legs)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=32)
+    ap.add_argument("--mixed-only", action="store_true",
+                    help="only the mixed chunked-prefill leg (printed as one JSON line)")
+    ap.add_argument("--pmc-prefill-summary", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="HBM traffic of the mixed leg's prefill slices from rocprofv3 runs")
     ap.add_argument("--modes-only", action="store_true",
                     help="only the four-schedule serving comparison (printed as one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -92,6 +97,13 @@ def parse():
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     for f in ("pa_decode.hip", "pa_device.h"):
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_host_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def prefill_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("pa_prefill.hip", "pa_device.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_host_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -121,6 +133,19 @@ def traffic_from_profile(digest: str):
     if d.get("kernel_source_digest") != digest:
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def prefill_traffic_from_profile():
+    """Counter-measured HBM bytes (read + written) of the mixed leg's 64
+    prefill slices, if a PMC summary of the current prefill source is
+    committed."""
+    try:
+        d = json.load(open(os.path.join(PROFILE_DIR, "prefill_32k_slices_pmc.json")))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_digest") != prefill_source_digest():
+        return None
+    return d.get("hbm_bytes")
 
 
 def cpu_baseline(n_seqs: int):
@@ -251,6 +276,55 @@ def pmc_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_di
     }
     out["hbm_bytes_per_launch"] = out["hbm_read_bytes_per_launch"] + out["hbm_write_bytes_per_launch"]
     print(json.dumps(out, indent=1))
+
+
+def _pmc_seq(d: str, counter: str, key: str):
+    """Values of one counter for the dispatches of kernels named *key*, in
+    dispatch order."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") == counter and key in r["Kernel_Name"]:
+                rows.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    rows.sort()
+    return [v for _, v in rows]
+
+
+def pmc_prefill_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str):
+    """HBM traffic of the mixed leg's 64 prefill slices (one-stream pass of
+    ``bench.py --mixed-only``: the prefill launches are, in order, 20 warm-up
+    slices, the 64 slices of that pass, then those of the two-stream pass)
+    against their algorithmic bytes: the K/V of the prefix and the slice
+    (read once), Q and the output."""
+    key = "prefill_kernel<pa::BF16, 128>"
+    f = _pmc_seq(fetch_dir, "FETCH_SIZE", key)
+    w = _pmc_seq(write_dir, "WRITE_SIZE", key)
+    if len(f) < 84 or len(w) < 84:
+        raise SystemExit(f"expected >= 84 {key} dispatches, got {len(f)} / {len(w)}")
+    f_cal, _ = _pmc_mean(_pmc_rows(cal_fetch_dir, "FETCH_SIZE"), "neg")
+    w_cal, _ = _pmc_mean(_pmc_rows(cal_write_dir, "WRITE_SIZE"), "neg")
+    f_scale = CAL_BYTES / (f_cal * 1024.0)
+    w_scale = CAL_BYTES / (w_cal * 1024.0)
+    C = 512
+    alg_read = sum((C * c + C) * H_KV * D * 2 * 2 + C * H_Q * D * 2 for c in range(64))
+    alg_write = 64 * C * H_Q * D * 2
+    read = sum(f[20:84]) * 1024 * f_scale
+    write = sum(w[20:84]) * 1024 * w_scale
+    print(json.dumps({
+        "kernel": "prefill_kernel<BF16,128>",
+        "workload": "mixed leg, 64 causal 512-token slices of a 32768-token prompt, one stream",
+        "calibration": {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+        "hbm_read_bytes": int(read), "algorithmic_read_bytes": alg_read,
+        "read_ratio": round(read / alg_read, 3),
+        "hbm_write_bytes": int(write), "algorithmic_write_bytes": alg_write,
+        "write_ratio": round(write / alg_write, 3),
+        "hbm_bytes": int(read + write),
+        "split_partials_note": "slices whose key range is split write fp32 partials for the "
+                               "merge kernel, which the algorithmic count leaves out",
+        "kernel_source_digest": prefill_source_digest(),
+    }, indent=1))
 
 
 def _fill_random(kv, slots: np.ndarray, gen, dev, chunk: int = 1 << 16):
@@ -579,7 +653,9 @@ def mixed_leg(args, dev):
         "prefill_roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "traffic": None, "kernel": "prefill_kernel<BF16,128>",
+                             "traffic": prefill_traffic_from_profile(),
+                             "traffic_unit": "HBM bytes over the 64 slices",
+                             "kernel": "prefill_kernel<BF16,128>",
                              "kernel_us_total": round(tot_pf, 1),
                              "algorithmic_flops": flops},
         "prefill_merge_us_total": round(tm["prefill_merge"][2], 1),
@@ -1057,6 +1133,9 @@ def main():
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
         return
+    if args.pmc_prefill_summary:
+        pmc_prefill_summary(*args.pmc_prefill_summary)
+        return
 
     import torch
 
@@ -1066,6 +1145,9 @@ def main():
     K, W = args.steps, args.warmup
     if args.modes_only:
         print(json.dumps({"schedules": modes_leg(args, dev)}), flush=True)
+        return
+    if args.mixed_only:
+        print(json.dumps({"mixed": mixed_leg(args, dev)}), flush=True)
         return
 
     d = decode_leg(args, dev)
