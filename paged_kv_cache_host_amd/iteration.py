@@ -36,7 +36,7 @@ class LayerIterations:
                  cache_blocks: int | None = None, cache_dtype: str = "bf16",
                  k_scale: float = 1.0, v_scale: float = 1.0, sm_scale: float | None = None,
                  free_order=None, provider_syncs: bool = True, two_streams: bool = False,
-                 mode: str = "chunked"):
+                 mode: str = "chunked", fill_outputs: float | None = None):
         self.h_q, self.h_kv, self.d = h_q, h_kv, d
         self.dev = torch.device(device)
         self.provider = provider
@@ -44,6 +44,9 @@ class LayerIterations:
         # current stream (True) or are already in memory (False: no
         # cross-stream wait per iteration)
         self.provider_syncs = bool(provider_syncs)
+        # test aid: each iteration's output rows are set to this value on the
+        # compute stream before its kernels, so a row no kernel writes keeps it
+        self.fill_outputs = fill_outputs
         self.R, self.B = max_running, prefill_budget
         self.k_scale, self.v_scale = float(k_scale), float(v_scale)
         self.sm = sm_scale if sm_scale is not None else float(np.float32(1.0) / np.float32(np.sqrt(d)))
@@ -211,6 +214,10 @@ class LayerIterations:
                                              self.d, BLOCK, self.k_scale, self.v_scale))
         else:
             pa.check(pa.pa_stage(c, dvb, self.host_buf[X], 4 * off))
+        if self.fill_outputs is not None:
+            with torch.cuda.stream(c):
+                self.out_pf[O][:n_pt].fill_(self.fill_outputs)
+                self.out_dec[O][:n_dec].fill_(self.fill_outputs)
         if n_pf:
             pf_stream = c
             if self.side is not None:

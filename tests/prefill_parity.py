@@ -11,6 +11,7 @@ from oracle import allocator as oa
 from oracle import attention as oat
 from oracle import cache as oc
 from oracle import codecs
+from tests.parity import filled
 
 
 def _slice_rows(w):
@@ -37,7 +38,7 @@ def hip_prefill_run(w, device="cuda", free_order=None):
     max_q = max(n for _, _, n in w.slices)
     max_ctx = max(a + n for _, a, n in w.slices)
     out_dt = torch.float32 if w.q_dtype == "f32" else torch.bfloat16
-    out = torch.full((len(rows), w.h_q, w.d), float("nan"), dtype=out_dt, device=device)
+    out = filled((len(rows), w.h_q, w.d), out_dt, device)
     ws = prefill_workspace(len(w.slices), max_q, w.h_q, w.h_kv, w.d, max_ctx, device)
     kv.prefill(out, q, torch.from_numpy(cu).to(device), torch.from_numpy(start).to(device),
                torch.from_numpy(tables).to(device), max_q, max_ctx, w.sm_scale, ws)

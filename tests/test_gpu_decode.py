@@ -10,7 +10,7 @@ import torch
 
 import workloads
 from oracle import codecs
-from tests.parity import assert_close, hip_decode_run, oracle_decode_run, out_to_f64
+from tests.parity import assert_close, filled, hip_decode_run, oracle_decode_run, out_to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -192,7 +192,7 @@ def test_fp8_codes_decode_exactly():
     kv.k.fill_(0x38)
     tables, lens = kv.pack([0])
     q = torch.ones((1, h_q, d), dtype=torch.bfloat16, device=DEV)
-    out = torch.empty_like(q)
+    out = filled(q.shape, q.dtype, DEV)
     ws = decode_workspace(1, h_q, h_kv, d, 1, DEV)
     kv.decode(out, q, torch.from_numpy(tables).to(DEV), torch.from_numpy(lens).to(DEV), 1,
               1.0 / math.sqrt(d), ws)
@@ -274,7 +274,7 @@ def test_block_sizes_8_and_32(bs, cache_dt):
     else:
         k_d, v_d = k_d.view(torch.float8_e4m3fn), v_d.view(torch.float8_e4m3fn)
     q_d = torch.from_numpy(q_raw.view(np.int16)).to(DEV).view(torch.bfloat16)
-    out = torch.empty((S, h_q, d), dtype=torch.bfloat16, device=DEV)
+    out = filled((S, h_q, d), torch.bfloat16, DEV)
     ws = torch.zeros(pa.pa_decode_workspace_bytes(S, h_q, h_kv, d, max(lengths)),
                      dtype=torch.uint8, device=DEV)
     say(f"[decode bs={bs}] {cache_dt} S={S} maxL={max(lengths)} pool={nb}")

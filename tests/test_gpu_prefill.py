@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import workloads
-from tests.parity import assert_close, out_to_f64
+from tests.parity import assert_close, filled, out_to_f64
 from tests.prefill_parity import hip_prefill_run, oracle_prefill_run
 
 pytestmark = pytest.mark.gpu
@@ -131,7 +131,7 @@ def _mixed_prefix_run(chunks, sample):
         P0 = c * C
         say(f"[prefill parity] mixed-prefill chunk {c} (prefix {P0})")
         q = to_device_raw(w.prompt_q[P0:P0 + C], "bf16", dev)
-        out = torch.full((C, w.h_q, w.d), float("nan"), dtype=torch.bfloat16, device=dev)
+        out = filled((C, w.h_q, w.d), torch.bfloat16, dev)
         cu = torch.tensor([0, C], dtype=torch.int32, device=dev)
         st = torch.tensor([P0], dtype=torch.int32, device=dev)
         ws = prefill_workspace(1, C, w.h_q, w.h_kv, w.d, P0 + C, dev)
@@ -142,8 +142,6 @@ def _mixed_prefix_run(chunks, sample):
         ref = oat.prefill_chunk(codecs.decode(w.prompt_q[P0:P0 + C], "bf16"), P0, kc, vc,
                                 pool.block_table(0), w.h_kv, w.sm_scale, "bf16", rows=rows)
         err = assert_close(got, ref, "bf16", f"mixed-prefill chunk {c}")
-        if rows is not None:
-            assert not np.isnan(got).any(), "rows left unwritten"
         say(f"    max|d| = {err:.3g}")
     kv.close()
 

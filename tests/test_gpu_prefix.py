@@ -17,7 +17,7 @@ from oracle import cache as oc
 from oracle import codecs
 from paged_kv_cache_host_amd.engine import (PagedKV, decode_workspace, prefill_workspace,
                                             to_device_raw, to_host_raw)
-from tests.parity import assert_close, out_to_f64
+from tests.parity import assert_close, filled, out_to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -87,7 +87,7 @@ def test_shared_prefix_decode_and_prefill(cache_dtype):
     t_d = torch.from_numpy(tables).to(DEV)
     l_d = torch.from_numpy(lens).to(DEV)
     qd = to_device_raw(q_dec, "bf16", DEV)
-    out = torch.empty((S, H_Q, D), dtype=torch.bfloat16, device=DEV)
+    out = filled((S, H_Q, D), torch.bfloat16, DEV)
     mc = int(lens.max())
     ws = decode_workspace(S, H_Q, H_KV, D, mc, DEV)
     kv.decode(out, qd, t_d, l_d, mc, sm, ws)
@@ -106,7 +106,7 @@ def test_shared_prefix_decode_and_prefill(cache_dtype):
     row = tables[seq:seq + 1]
     cu = torch.tensor([0, n], dtype=torch.int32, device=DEV)
     st_ = torch.tensor([P], dtype=torch.int32, device=DEV)
-    outp = torch.empty((n, H_Q, D), dtype=torch.bfloat16, device=DEV)
+    outp = filled((n, H_Q, D), torch.bfloat16, DEV)
     wsp = prefill_workspace(1, n, H_Q, H_KV, D, P + n, DEV)
     kv.prefill(outp, to_device_raw(qp, "bf16", DEV), cu, st_, torch.from_numpy(row).to(DEV), n,
                P + n, sm, wsp)

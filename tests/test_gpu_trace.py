@@ -14,7 +14,7 @@ from oracle import attention as oat
 from oracle import cache as oc
 from oracle import codecs
 from oracle.scheduler import Scheduler
-from tests.parity import assert_close
+from tests.parity import SENTINEL, assert_close
 
 pytestmark = pytest.mark.gpu
 
@@ -127,7 +127,7 @@ def test_trace_iterations_match_oracle(mode):
                 to_device_raw(q, "bf16", "cuda"))
 
     run = LayerIterations(w.num_blocks, H_Q, H_KV, D, "cuda", provider, R, BUDGET[mode],
-                          max_context=max_ctx, mode=mode)
+                          max_context=max_ctx, mode=mode, fill_outputs=SENTINEL)
     results = []
     for it in range(w.iters):
         for sid, p, o in w.arrivals[it]:
@@ -167,7 +167,7 @@ def test_trace_iterations_pipelined_match_oracle(two_streams):
         return out
 
     run = LayerIterations(w.num_blocks, H_Q, H_KV, D, "cuda", provider, R, B, max_context=max_ctx,
-                          provider_syncs=False, two_streams=two_streams)
+                          provider_syncs=False, two_streams=two_streams, fill_outputs=SENTINEL)
     copies = []
     for it in range(w.iters):
         for sid, p, o in w.arrivals[it]:
