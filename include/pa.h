@@ -397,6 +397,14 @@ pa_status pa_sched_stats(const pa_sched* sched, pa_sched_accounting* out);
  * ---------------------------------------------------------------------- */
 pa_status pa_stage(void* stream, void* dst, const void* src_host, size_t bytes);
 
+/* pa_pinned_alias -- the host-side check every staging launch (pa_stage,
+ * pa_stage_cache_write, pa_stage_decode_append) makes of its source before
+ * anything is launched: src_host [host] must lie in pinned host memory
+ * (hipHostMalloc); its device-side alias is written to *src_dev [host].
+ * PA_ERR_INVALID (and *src_dev = NULL) for NULL or pageable memory.  Host
+ * only: it never launches. */
+pa_status pa_pinned_alias(const void* src_host, void** src_dev);
+
 /* ------------------------------------------------------------------------
  * pa_stage_cache_write -- pa_stage and pa_cache_write in one launch, for an
  * iteration whose slot mapping is part of the staged metadata (LESSON

@@ -91,6 +91,7 @@ _SIGS = {
     "pa_sched_step": (_i32, [_vp, C.POINTER(SchedBatchC)]),
     "pa_sched_stats": (_i32, [_vp, C.POINTER(SchedAccountingC)]),
     "pa_stage": (_i32, [_vp, _vp, _vp, _sz]),
+    "pa_pinned_alias": (_i32, [_vp, C.POINTER(_vp)]),
     "pa_stage_cache_write": (_i32, [_vp, _vp, _vp, _sz, _sz, _vp, _vp, _i32, _i32, _vp, _vp, _i32,
                                     _i32, _i32, _i32, _i32, _f32, _f32]),
     "pa_stage_decode_append": (_i32, [_vp, _vp, _vp, _sz, _sz, _sz, _vp, _vp, _i32, _i32, _vp,
@@ -428,10 +429,59 @@ def dtype_of(t) -> int:
     raise PaError(PA_ERR_INVALID, f"unsupported tensor dtype {t.dtype}")
 
 
+# Argument checks of the kernel wrappers (shapes, dtypes and extents of the
+# tensors whose pointers cross the C ABI): a tensor that is too small, of
+# the wrong integer width or strided would otherwise be read or written out
+# of bounds by a kernel that trusts its sizes.
+
+def _need(ok: bool, who: str, what: str):
+    if not ok:
+        raise PaError(PA_ERR_INVALID, f"{who}: {what}")
+
+
+def _check_i32(who: str, name: str, t, n_min: int):
+    _need(t is not None and str(t.dtype) == "torch.int32" and t.is_contiguous()
+          and t.numel() >= n_min, who,
+          f"{name} must be a contiguous int32 tensor of at least {n_min} entries")
+
+
+def _check_tables(who: str, t, rows: int):
+    _need(str(t.dtype) == "torch.int32" and t.is_contiguous() and t.dim() == 2
+          and t.shape[0] >= rows and t.shape[1] >= 1, who,
+          f"block_tables must be a contiguous int32 [>= {rows}, max_blocks] tensor")
+
+
+def _check_cache(who: str, k_cache, v_cache, num_blocks: int, H_kv: int, D: int, bs: int):
+    need = num_blocks * H_kv * D * bs
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t.is_contiguous() and t.numel() >= need, who,
+              f"{name} must be contiguous with room for {num_blocks} blocks of {H_kv} x {D} x "
+              f"{bs} elements")
+    _need(k_cache.dtype == v_cache.dtype, who, "k_cache and v_cache differ in dtype")
+
+
+def _check_rows(who: str, name: str, t, rows: int, H: int, D: int):
+    _need(t.is_contiguous() and t.dim() == 3 and t.shape[0] >= rows and t.shape[1] == H
+          and t.shape[2] == D, who, f"{name} must be a contiguous [>= {rows}, {H}, {D}] tensor")
+
+
+def pa_pinned_alias(src_host) -> tuple[int, int]:
+    """Host-only check of a staging source: (status, device alias or 0)."""
+    out = _vp()
+    st = _lib.pa_pinned_alias(src_host, C.byref(out))
+    return st, (out.value or 0)
+
+
 def pa_cache_write(stream, k_new, v_new, slot_mapping, k_cache, v_cache, num_blocks: int,
                    H_kv: int, D: int, bs: int = 16, k_scale: float = 1.0, v_scale: float = 1.0,
                    n: int | None = None) -> int:
     n = slot_mapping.numel() if n is None else n
+    who = "pa_cache_write"
+    _check_i32(who, "slot_mapping", slot_mapping, n)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t.is_contiguous() and t.numel() >= n * H_kv * D, who,
+              f"{name} must be a contiguous [>= {n}, {H_kv}, {D}] tensor")
+    _check_cache(who, k_cache, v_cache, num_blocks, H_kv, D, bs)
     return _lib.pa_cache_write(_stream_handle(stream), _dptr(k_new), _dptr(v_new),
                                dtype_of(k_new), _dptr(slot_mapping), n, _dptr(k_cache),
                                _dptr(v_cache), dtype_of(k_cache), num_blocks, H_kv, D, bs,
@@ -518,6 +568,12 @@ def pa_decode(stream, out, q, k_cache, v_cache, block_tables, context_lens, num_
               H_kv: int, max_context_len: int, sm_scale: float, k_scale: float = 1.0,
               v_scale: float = 1.0, ws=None, bs: int = 16) -> int:
     S, H_q, D = q.shape
+    who = "pa_decode"
+    _check_rows(who, "q", q, S, H_q, D)
+    _check_rows(who, "out", out, S, H_q, D)
+    _check_tables(who, block_tables, S)
+    _check_i32(who, "context_lens", context_lens, S)
+    _check_cache(who, k_cache, v_cache, num_blocks, H_kv, D, bs)
     max_blocks = block_tables.shape[1]
     return _lib.pa_decode(_stream_handle(stream), _dptr(out), dtype_of(out), _dptr(q), dtype_of(q),
                           _dptr(k_cache), _dptr(v_cache), dtype_of(k_cache), _dptr(block_tables),
@@ -535,8 +591,15 @@ def pa_prefill_chunk(stream, out, q, cu_q_lens, start_pos, k_cache, v_cache, blo
                      num_blocks: int, H_kv: int, max_q_len: int, max_context_len: int,
                      sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0, ws=None,
                      bs: int = 16) -> int:
-    _, H_q, D = q.shape
+    T, H_q, D = q.shape
     n_chunks = start_pos.numel()
+    who = "pa_prefill_chunk"
+    _check_rows(who, "q", q, T, H_q, D)
+    _check_rows(who, "out", out, T, H_q, D)
+    _check_i32(who, "cu_q_lens", cu_q_lens, n_chunks + 1)
+    _check_i32(who, "start_pos", start_pos, n_chunks)
+    _check_tables(who, block_tables, n_chunks)
+    _check_cache(who, k_cache, v_cache, num_blocks, H_kv, D, bs)
     max_blocks = block_tables.shape[1]
     return _lib.pa_prefill_chunk(_stream_handle(stream), _dptr(out), dtype_of(out), _dptr(q),
                                  dtype_of(q), _dptr(cu_q_lens), _dptr(start_pos), _dptr(k_cache),

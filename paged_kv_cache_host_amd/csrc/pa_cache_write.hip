@@ -337,12 +337,8 @@ static pa_status stage_cache_write_impl(const char* who, void* stream, void* dst
   if (bytes == 0) return PA_OK;  // and n == 0
   if (!dst || !src_host) return fail(PA_ERR_INVALID, "%s: NULL buffer", who);
   void* src_dev = nullptr;
-  hipError_t e = hipHostGetDevicePointer(&src_dev, const_cast<void*>(src_host), 0);
-  if (e != hipSuccess || !src_dev) {
-    (void)hipGetLastError();
-    return fail(PA_ERR_INVALID, "%s: source is not pinned host memory (%s)", who,
-                hipGetErrorString(e));
-  }
+  const pa_status ps = pinned_alias(who, src_host, &src_dev);
+  if (ps != PA_OK) return ps;
   const int32_t* slots_dev =
       reinterpret_cast<const int32_t*>(static_cast<const char*>(src_dev) + slot_offset);
   TableUpkeep tu;

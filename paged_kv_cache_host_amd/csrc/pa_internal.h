@@ -61,6 +61,9 @@ inline hipError_t launch(KernelId k, void (*kernel)(P...), dim3 grid, dim3 block
                        std::index_sequence_for<P...>{});
 }
 
+// pa_pinned_alias with the caller's name in the error text.
+pa_status pinned_alias(const char* who, const void* src_host, void** src_dev);
+
 // Record a printf-style message as the calling thread's last error and
 // return `st`.
 pa_status fail(pa_status st, const char* fmt, ...);

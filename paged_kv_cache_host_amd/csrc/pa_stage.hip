@@ -39,9 +39,28 @@ pa_status launch_stage(hipStream_t st, void* dst, const void* src_dev, size_t by
   return PA_OK;
 }
 
+pa_status pinned_alias(const char* who, const void* src_host, void** src_dev) {
+  *src_dev = nullptr;
+  if (!src_host) return fail(PA_ERR_INVALID, "%s: NULL source", who);
+  void* p = nullptr;
+  const hipError_t e = hipHostGetDevicePointer(&p, const_cast<void*>(src_host), 0);
+  if (e != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID, "%s: source is not pinned host memory (%s)", who,
+                hipGetErrorString(e));
+  }
+  *src_dev = p;
+  return PA_OK;
+}
+
 }  // namespace pa
 
 using namespace pa;
+
+extern "C" pa_status pa_pinned_alias(const void* src_host, void** src_dev) {
+  if (!src_dev) return fail(PA_ERR_INVALID, "pa_pinned_alias: NULL result pointer");
+  return pinned_alias("pa_pinned_alias", src_host, src_dev);
+}
 
 extern "C" pa_status pa_stage(void* stream, void* dst, const void* src_host, size_t bytes) {
   if (bytes == 0) return PA_OK;
@@ -51,12 +70,8 @@ extern "C" pa_status pa_stage(void* stream, void* dst, const void* src_host, siz
     return fail(PA_ERR_INVALID, "pa_stage: bytes=%zu and both addresses must be multiples of 4",
                 bytes);
   void* src_dev = nullptr;
-  hipError_t e = hipHostGetDevicePointer(&src_dev, const_cast<void*>(src_host), 0);
-  if (e != hipSuccess || !src_dev) {
-    (void)hipGetLastError();
-    return fail(PA_ERR_INVALID, "pa_stage: source is not pinned host memory (%s)",
-                hipGetErrorString(e));
-  }
+  const pa_status ps = pinned_alias("pa_stage", src_host, &src_dev);
+  if (ps != PA_OK) return ps;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (bytes % 8 == 0 && reinterpret_cast<uintptr_t>(dst) % 8 == 0 &&
       reinterpret_cast<uintptr_t>(src_dev) % 8 == 0)

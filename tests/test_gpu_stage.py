@@ -67,11 +67,17 @@ def test_stage_sees_every_host_rewrite():
 
 
 def test_stage_rejects_bad_sources():
+    """Pageable sources are refused by the host-only check every staging
+    launch makes first (pa_pinned_alias, which never launches); misaligned
+    pinned sources and sizes reach pa_stage itself, with real buffers on
+    both sides, so nothing outside them can be touched."""
     dev = torch.zeros(64, dtype=torch.int32, device=DEV)
     pageable = np.arange(64, dtype=np.int32)
-    st = pa._lib.pa_stage(None, dev.data_ptr(), pageable.ctypes.data, 256)
-    assert st == pa.PA_ERR_INVALID
+    st, alias = pa.pa_pinned_alias(pageable.ctypes.data)
+    assert st == pa.PA_ERR_INVALID and alias == 0
     host = torch.arange(64, dtype=torch.int32).pin_memory()
+    st, alias = pa.pa_pinned_alias(host.data_ptr())
+    assert st == pa.PA_OK and alias != 0
     assert pa._lib.pa_stage(None, dev.data_ptr(), host.data_ptr() + 2, 8) == pa.PA_ERR_INVALID
     assert pa._lib.pa_stage(None, dev.data_ptr(), host.data_ptr(), 6) == pa.PA_ERR_INVALID
     assert pa._lib.pa_stage(None, dev.data_ptr(), host.data_ptr(), 0) == 0
@@ -134,17 +140,29 @@ def test_stage_cache_write_equals_stage_then_cache_write(new_dt, cache_dt, d):
 
 
 def test_stage_cache_write_rejects_bad_arguments():
-    fake = 0x1000
+    """Every device argument is a real buffer sized for the call (10 blocks
+    of 2 KV heads x 64 dims, 8 new tokens whose slots, read from the pinned
+    buffer, lie inside the pool), so that even a launch after a failed check
+    would stay inside them; the pageable source goes to the host-only check."""
     host = torch.arange(64, dtype=torch.int32).pin_memory()
     lib = pa._lib
-    # slots past the end of the buffer, misaligned offset, non-pinned source
-    assert lib.pa_stage_cache_write(None, fake, host.data_ptr(), 64, 40, fake, fake, 1, 8, fake,
-                                    fake, 1, 10, 2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
-    assert lib.pa_stage_cache_write(None, fake, host.data_ptr(), 64, 2, fake, fake, 1, 1, fake,
-                                    fake, 1, 10, 2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
+    nb, h_kv, d, n = 10, 2, 64, 8
+    dst = torch.zeros(64 + 16, dtype=torch.int32, device=DEV)
+    kn = torch.zeros((n, h_kv, d), dtype=torch.bfloat16, device=DEV)
+    vn = torch.zeros((n, h_kv, d), dtype=torch.bfloat16, device=DEV)
+    kc = torch.zeros((nb, h_kv, d // 8, 16, 8), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros((nb, h_kv, d, 16), dtype=torch.bfloat16, device=DEV)
+    args = (kn.data_ptr(), vn.data_ptr(), 1)
+    cache = (kc.data_ptr(), vc.data_ptr(), 1, nb, h_kv, d, 16, 1.0, 1.0)
+    # 8 slots at byte 40 of a 64-byte buffer, then a misaligned slot offset
+    assert lib.pa_stage_cache_write(None, dst.data_ptr(), host.data_ptr(), 64, 40, *args, n,
+                                    *cache) == pa.PA_ERR_INVALID
+    assert lib.pa_stage_cache_write(None, dst.data_ptr(), host.data_ptr(), 64, 2, *args, 1,
+                                    *cache) == pa.PA_ERR_INVALID
+    torch.cuda.synchronize()
+    assert (dst.cpu() == 0).all() and (kc.view(torch.int16).cpu() == 0).all()
     pageable = np.zeros(64, dtype=np.int32)
-    assert lib.pa_stage_cache_write(None, fake, pageable.ctypes.data, 64, 0, fake, fake, 1, 1,
-                                    fake, fake, 1, 10, 2, 64, 16, 1.0, 1.0) == pa.PA_ERR_INVALID
+    assert pa.pa_pinned_alias(pageable.ctypes.data)[0] == pa.PA_ERR_INVALID
 
 
 @pytest.mark.parametrize("device_meta", [False, True], ids=["staged", "device"])
