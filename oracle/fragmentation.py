@@ -35,11 +35,3 @@ def contiguous_waste(lengths, reservation: int = 8192) -> float:
     total = reservation * len(lengths)
     return 0.0 if total == 0 else 1.0 - float(lengths.sum()) / total
 
-
-def pool_waste(tables_len, tokens_held, block_size: int = 16) -> float:
-    """Waste over the live sequences of a pool: ``tables_len`` blocks held per
-    sequence, ``tokens_held`` tokens each."""
-    blocks = int(np.sum(tables_len))
-    if blocks == 0:
-        return 0.0
-    return 1.0 - float(np.sum(tokens_held)) / (blocks * block_size)

@@ -22,7 +22,7 @@ def _run_golden(tr):
         got = {"finished": b.finished, "admitted": b.admitted, "preempted": b.preempted,
                "decode": [list(x) for x in b.decode],
                "prefill": [[s, a, n, list(sl)] for s, a, n, sl in b.prefill],
-               "free": pool.free_list()}
+               "free": pool.free_list(), "held": list(sch.held())}
         assert got == want, (tr["name"], it, got, want)
 
 
@@ -72,3 +72,47 @@ def test_invariants_tiny_pool_forces_preemption():
     sch = _check_invariants(num_blocks=40, iters=400, lam=0.3, budget=64, max_running=16, seed=22)
     assert sum(s.preemptions for s in sch.done + sch.running + sch.waiting) > 0
     assert len(sch.done) > 5
+
+
+
+_HELD = Scheduler.held
+
+
+def _held_mutants():
+    """Plausible mistakes in the accounting, each of which the hand-worked
+    held values must catch."""
+    def decoded_in_unwritten(self):
+        b, a, u = _HELD(self)
+        return b, a, u + sum(s.decoded for s in self.running if not s.in_prefill)
+
+    def decode_phase_only(self):
+        blocks = sum(len(self.pool.tables[s.sid]) for s in self.running if not s.in_prefill)
+        tok = sum(self.pool.lengths[s.sid] for s in self.running if not s.in_prefill)
+        return blocks, tok, 0
+
+    def written_not_assigned(self):
+        b, a, u = _HELD(self)
+        return b, a - u, u
+
+    def waiting_counted(self):
+        b, a, u = _HELD(self)
+        return b, a, u + sum(s.known for s in self.waiting)
+
+    return [decoded_in_unwritten, decode_phase_only, written_not_assigned, waiting_counted]
+
+
+def test_hand_worked_held_values_catch_accounting_mistakes(monkeypatch):
+    """Mistakes planted in the oracle's accounting (on the CPU): counting
+    decoded tokens as unwritten, dropping the prefill-phase sequences,
+    counting only written tokens as assigned, charging the waiting queue."""
+    g = json.load(open(os.path.join(GOLDEN, "scheduler_traces.json")))
+    for mutant in _held_mutants():
+        caught = False
+        with monkeypatch.context() as m:
+            m.setattr(Scheduler, "held", mutant)
+            for tr in g["traces"]:
+                try:
+                    _run_golden(tr)
+                except AssertionError:
+                    caught = True
+        assert caught, mutant.__name__
