@@ -74,6 +74,8 @@ def test_hand_worked_traces_through_c():
             got = c.step()
             del got["emits"]
             got["free"] = c.free_list()
+            a = c.stats()
+            got["held"] = [a["blocks_held"], a["tokens_held"], a["unwritten"]]
             assert got == want, (tr["name"], it, got, want)
         c.close()
 
