@@ -246,6 +246,37 @@ pa_status pa_decode(void* stream, void* out, pa_dtype out_dt, const void* q, pa_
                     float v_scale, void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc.  Same arguments, operation, kernels and results as
+ * pa_decode, without ws / ws_bytes: the workspace is a file-scope device
+ * array of PA_DECODE_SCRATCH_BYTES (64 MiB) that each GPU the library runs
+ * on holds until the process ends.  Its device address is looked up once per
+ * device (with that device current) on the first call there.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * it launches a one-wave kernel that zeroes the work counters before the
+ * decode kernels, since the array keeps the previous call's contents.
+ *
+ * Limit: the split partials of the call must fit the array less its 4 KiB
+ * counter region, i.e. pa_decode_workspace_bytes(S, H_q, H_kv, D,
+ * max_context_len) minus its counter bytes <= 64 MiB - 4 KiB (for example
+ * 128 sequences x 64 query heads x D = 128 up to 16,384 tokens of context);
+ * larger calls return PA_ERR_WORKSPACE and launch nothing.  Problems that
+ * take the fp32 path use no workspace.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (two streams, two threads) race and give wrong results;
+ * serialise them.
+ * ---------------------------------------------------------------------- */
+#define PA_DECODE_SCRATCH_BYTES (64u * 1024u * 1024u)
+pa_status pa_decode_noalloc(void* stream, void* out, pa_dtype out_dt, const void* q,
+                            pa_dtype q_dt, const void* k_cache, const void* v_cache,
+                            pa_dtype cache_dt, const int32_t* block_tables, int32_t max_blocks,
+                            int32_t num_blocks, const int32_t* context_lens, int32_t S,
+                            int32_t H_q, int32_t H_kv, int32_t D, int32_t bs,
+                            int32_t max_context_len, float sm_scale, float k_scale,
+                            float v_scale);
+
+/* ------------------------------------------------------------------------
  * Chunked-prefill attention -- LESSON "Chunked prefill": a long prompt is
  * processed as fixed-size slices (512 tokens by default), each attending
  * causally to everything before it.  Slice c holds the queries

@@ -84,6 +84,8 @@ _SIGS = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _i32,
                          _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32, _vp, _sz]),
+    "pa_decode_noalloc": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp,
+                                  _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32]),
     "pa_sched_create": (_i32, [_vp, _i32, _i32, _i32, C.POINTER(_vp)]),
     "pa_sched_create_mode": (_i32, [_vp, _i32, _i32, _i32, _i32, C.POINTER(_vp)]),
     "pa_sched_destroy": (None, [_vp]),
@@ -580,6 +582,25 @@ def pa_decode(stream, out, q, k_cache, v_cache, block_tables, context_lens, num_
                           max_blocks, num_blocks, _dptr(context_lens), S, H_q, H_kv, D, bs,
                           max_context_len, sm_scale, k_scale, v_scale, _dptr(ws),
                           0 if ws is None else ws.numel() * ws.element_size())
+
+
+def pa_decode_noalloc(stream, out, q, k_cache, v_cache, block_tables, context_lens,
+                      num_blocks: int, H_kv: int, max_context_len: int, sm_scale: float,
+                      k_scale: float = 1.0, v_scale: float = 1.0, bs: int = 16) -> int:
+    """pa_decode with the library's own per-device scratch array as its
+    workspace (no workspace argument, nothing allocated)."""
+    S, H_q, D = q.shape
+    who = "pa_decode_noalloc"
+    _check_rows(who, "q", q, S, H_q, D)
+    _check_rows(who, "out", out, S, H_q, D)
+    _check_tables(who, block_tables, S)
+    _check_i32(who, "context_lens", context_lens, S)
+    _check_cache(who, k_cache, v_cache, num_blocks, H_kv, D, bs)
+    return _lib.pa_decode_noalloc(_stream_handle(stream), _dptr(out), dtype_of(out), _dptr(q),
+                                  dtype_of(q), _dptr(k_cache), _dptr(v_cache), dtype_of(k_cache),
+                                  _dptr(block_tables), block_tables.shape[1], num_blocks,
+                                  _dptr(context_lens), S, H_q, H_kv, D, bs, max_context_len,
+                                  sm_scale, k_scale, v_scale)
 
 
 def pa_prefill_workspace_bytes(n_chunks: int, max_q_len: int, H_q: int, H_kv: int, D: int,

@@ -42,6 +42,7 @@
 #include "pa_internal.h"
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 namespace pa {
@@ -604,11 +605,11 @@ static pa_status launch_decode_mfma(hipStream_t st, void* out, const void* q, co
                                     int32_t max_blocks, int32_t num_blocks,
                                     const int32_t* context_lens, int32_t S, int32_t H_q,
                                     int32_t H_kv, int32_t max_context_len, float sm_scale,
-                                    float k_scale, float v_scale, void* ws) {
+                                    float k_scale, float v_scale, int32_t* counters,
+                                    void* partials) {
   const int32_t shift = decode_chunk_shift(S, H_kv, max_context_len);
   const int32_t n_chunks = decode_num_chunks(max_context_len, shift);
-  int32_t* counters = static_cast<int32_t*>(ws);
-  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_counter_bytes(S));
+  float* ws_ml = static_cast<float*>(partials);
   float* ws_o = ws_ml + static_cast<int64_t>(S) * H_q * n_chunks * 2;
   const float score_scale = sm_scale * kLog2e * k_scale;
   const int32_t grid = resident_work_groups<CacheT, D, BS>();
@@ -666,60 +667,79 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t S, int32_t H_q, int32_t H_kv
   return decode_counter_bytes(S) + static_cast<size_t>(S) * H_q * n_chunks * (D + 2) * sizeof(float);
 }
 
-extern "C" pa_status pa_decode(void* stream, void* out, pa_dtype out_dt, const void* q,
-                               pa_dtype q_dt, const void* k_cache, const void* v_cache,
-                               pa_dtype cache_dt, const int32_t* block_tables, int32_t max_blocks,
-                               int32_t num_blocks, const int32_t* context_lens, int32_t S,
-                               int32_t H_q, int32_t H_kv, int32_t D, int32_t bs,
-                               int32_t max_context_len, float sm_scale, float k_scale,
-                               float v_scale, void* ws, size_t ws_bytes) {
+// Validation shared by pa_decode and pa_decode_noalloc; PA_OK with *run set
+// when there is work to launch.
+static pa_status decode_check(const char* who, void* out, pa_dtype out_dt, const void* q,
+                              pa_dtype q_dt, const void* k_cache, const void* v_cache,
+                              pa_dtype cache_dt, const int32_t* block_tables, int32_t max_blocks,
+                              int32_t num_blocks, const int32_t* context_lens, int32_t S,
+                              int32_t H_q, int32_t H_kv, int32_t D, int32_t bs,
+                              int32_t max_context_len, float sm_scale, float k_scale,
+                              float v_scale, bool* run) {
+  *run = false;
   if (bs != 8 && bs != 16 && bs != 32)
-    return fail(PA_ERR_INVALID, "pa_decode: block size %d not in {8, 16, 32}", bs);
+    return fail(PA_ERR_INVALID, "%s: block size %d not in {8, 16, 32}", who, bs);
   if (S < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv != 0)
-    return fail(PA_ERR_INVALID, "pa_decode: S=%d H_q=%d H_kv=%d", S, H_q, H_kv);
-  if (D != 64 && D != 128) return fail(PA_ERR_INVALID, "pa_decode: D=%d not in {64,128}", D);
+    return fail(PA_ERR_INVALID, "%s: S=%d H_q=%d H_kv=%d", who, S, H_q, H_kv);
+  if (D != 64 && D != 128) return fail(PA_ERR_INVALID, "%s: D=%d not in {64,128}", who, D);
   if (max_blocks <= 0 || num_blocks <= 0 || max_context_len <= 0)
-    return fail(PA_ERR_INVALID, "pa_decode: max_blocks=%d num_blocks=%d max_context_len=%d",
+    return fail(PA_ERR_INVALID, "%s: max_blocks=%d num_blocks=%d max_context_len=%d", who,
                 max_blocks, num_blocks, max_context_len);
   if (static_cast<int64_t>(max_blocks) * bs > INT32_MAX)
-    return fail(PA_ERR_INVALID, "pa_decode: max_blocks=%d too large", max_blocks);
+    return fail(PA_ERR_INVALID, "%s: max_blocks=%d too large", who, max_blocks);
   const bool f32 = q_dt == PA_F32 && cache_dt == PA_F32 && out_dt == PA_F32;
   const bool bf = q_dt == PA_BF16 && out_dt == PA_BF16 &&
                   (cache_dt == PA_BF16 || cache_dt == PA_FP8_E4M3);
   if (!f32 && !bf)
-    return fail(PA_ERR_INVALID, "pa_decode: unsupported dtypes q=%d cache=%d out=%d", q_dt,
+    return fail(PA_ERR_INVALID, "%s: unsupported dtypes q=%d cache=%d out=%d", who, q_dt,
                 cache_dt, out_dt);
   if (cache_dt == PA_FP8_E4M3 &&
       (!(k_scale > 0.f) || !(v_scale > 0.f) || !__builtin_isfinite(k_scale) ||
        !__builtin_isfinite(v_scale)))
-    return fail(PA_ERR_INVALID, "pa_decode: fp8 scales must be finite and > 0");
+    return fail(PA_ERR_INVALID, "%s: fp8 scales must be finite and > 0", who);
   if (!(sm_scale > 0.f) || !__builtin_isfinite(sm_scale))
-    return fail(PA_ERR_INVALID, "pa_decode: sm_scale must be finite and > 0");
+    return fail(PA_ERR_INVALID, "%s: sm_scale must be finite and > 0", who);
   if (S == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PA_ERR_INVALID, "pa_decode: NULL buffer");
+    return fail(PA_ERR_INVALID, "%s: NULL buffer", who);
   if (S > 65535 || H_kv > 65535)
-    return fail(PA_ERR_INVALID, "pa_decode: S=%d or H_kv=%d exceeds grid limits", S, H_kv);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+    return fail(PA_ERR_INVALID, "%s: S=%d or H_kv=%d exceeds grid limits", who, S, H_kv);
+  if (!decode_uses_mfma(q_dt, cache_dt, H_q, H_kv) && bs != kBlock)
+    return fail(PA_ERR_INVALID,
+                "%s: block size %d needs the matrix-core path (bf16 queries, bf16 or fp8 "
+                "cache, at most 16 query heads per KV head)", who, bs);
+  *run = true;
+  return PA_OK;
+}
+
+// Launches a validated call; counters and partials are the workspace's two
+// regions (used by the matrix-core path only).
+static pa_status decode_dispatch(hipStream_t st, void* out, pa_dtype out_dt, const void* q,
+                                 pa_dtype q_dt, const void* k_cache, const void* v_cache,
+                                 pa_dtype cache_dt, const int32_t* block_tables,
+                                 int32_t max_blocks, int32_t num_blocks,
+                                 const int32_t* context_lens, int32_t S, int32_t H_q,
+                                 int32_t H_kv, int32_t D, int32_t bs, int32_t max_context_len,
+                                 float sm_scale, float k_scale, float v_scale,
+                                 int32_t* counters, void* partials) {
   if (decode_uses_mfma(q_dt, cache_dt, H_q, H_kv)) {
-    const size_t need = pa_decode_workspace_bytes(S, H_q, H_kv, D, max_context_len);
-    if (!ws || ws_bytes < need)
-      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace %zu bytes < %zu required", ws_bytes,
-                  need);
     auto by_bs = [&](auto cache_tag, auto d_tag, float ks, float vs) -> pa_status {
       using CT = decltype(cache_tag);
       constexpr int DD = decltype(d_tag)::value;
       if (bs == 8)
         return launch_decode_mfma<CT, DD, 8>(st, out, q, k_cache, v_cache, block_tables,
                                              max_blocks, num_blocks, context_lens, S, H_q, H_kv,
-                                             max_context_len, sm_scale, ks, vs, ws);
+                                             max_context_len, sm_scale, ks, vs, counters,
+                                             partials);
       if (bs == 32)
         return launch_decode_mfma<CT, DD, 32>(st, out, q, k_cache, v_cache, block_tables,
                                               max_blocks, num_blocks, context_lens, S, H_q, H_kv,
-                                              max_context_len, sm_scale, ks, vs, ws);
+                                              max_context_len, sm_scale, ks, vs, counters,
+                                              partials);
       return launch_decode_mfma<CT, DD, 16>(st, out, q, k_cache, v_cache, block_tables,
                                             max_blocks, num_blocks, context_lens, S, H_q, H_kv,
-                                            max_context_len, sm_scale, ks, vs, ws);
+                                            max_context_len, sm_scale, ks, vs, counters,
+                                            partials);
     };
     using D128 = std::integral_constant<int, 128>;
     using D64 = std::integral_constant<int, 64>;
@@ -728,11 +748,132 @@ extern "C" pa_status pa_decode(void* stream, void* out, pa_dtype out_dt, const v
     return D == 128 ? by_bs(FP8{}, D128{}, k_scale, v_scale)
                     : by_bs(FP8{}, D64{}, k_scale, v_scale);
   }
-  if (bs != kBlock)
-    return fail(PA_ERR_INVALID,
-                "pa_decode: block size %d needs the matrix-core path (bf16 queries, bf16 or fp8 "
-                "cache, at most 16 query heads per KV head)", bs);
   return launch_attend_generic(st, out, out_dt, q, q_dt, k_cache, v_cache, cache_dt, block_tables,
                                max_blocks, num_blocks, context_lens, nullptr, nullptr, 0, S, H_q,
                                H_kv, D, sm_scale, k_scale, v_scale);
+}
+
+extern "C" pa_status pa_decode(void* stream, void* out, pa_dtype out_dt, const void* q,
+                               pa_dtype q_dt, const void* k_cache, const void* v_cache,
+                               pa_dtype cache_dt, const int32_t* block_tables, int32_t max_blocks,
+                               int32_t num_blocks, const int32_t* context_lens, int32_t S,
+                               int32_t H_q, int32_t H_kv, int32_t D, int32_t bs,
+                               int32_t max_context_len, float sm_scale, float k_scale,
+                               float v_scale, void* ws, size_t ws_bytes) {
+  bool run = false;
+  const pa_status chk = decode_check("pa_decode", out, out_dt, q, q_dt, k_cache, v_cache,
+                                     cache_dt, block_tables, max_blocks, num_blocks, context_lens,
+                                     S, H_q, H_kv, D, bs, max_context_len, sm_scale, k_scale,
+                                     v_scale, &run);
+  if (chk != PA_OK || !run) return chk;
+  int32_t* counters = nullptr;
+  void* partials = nullptr;
+  if (decode_uses_mfma(q_dt, cache_dt, H_q, H_kv)) {
+    const size_t need = pa_decode_workspace_bytes(S, H_q, H_kv, D, max_context_len);
+    if (!ws || ws_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace %zu bytes < %zu required", ws_bytes,
+                  need);
+    counters = static_cast<int32_t*>(ws);
+    partials = static_cast<char*>(ws) + decode_counter_bytes(S);
+  }
+  return decode_dispatch(static_cast<hipStream_t>(stream), out, out_dt, q, q_dt, k_cache,
+                         v_cache, cache_dt, block_tables, max_blocks, num_blocks, context_lens, S,
+                         H_q, H_kv, D, bs, max_context_len, sm_scale, k_scale, v_scale, counters,
+                         partials);
+}
+
+// ---------------------------------------------------------------------------
+// pa_decode_noalloc: the same decode with its workspace in a file-scope device
+// array, for callers that cannot allocate device memory.  The array holds a
+// fixed counter region (kScratchCounterBytes, one pair of int32 per launch
+// batch) followed by the split partials.  Host code never passes the array's
+// name to a kernel: its device address is looked up once per device with
+// hipGetSymbolAddress and kept.
+
+namespace pa {
+
+constexpr size_t kScratchCounterBytes = 4096;  // 512 launch batches of 4096 sequences
+
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array, looked up on first use.
+static pa_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_DEVICE, "pa_decode_noalloc: no usable current device (%s)",
+                hipGetErrorString(e));
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_DEVICE, "pa_decode_noalloc: scratch address lookup failed (%s)",
+                  hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+// grid: 1; block: 64.  Zeroes n int32 words.
+__global__ __launch_bounds__(64) void zero_words_kernel(int32_t* __restrict__ p, int32_t n) {
+  for (int32_t i = threadIdx.x; i < n; i += 64) p[i] = 0;
+}
+
+}  // namespace pa
+
+extern "C" pa_status pa_decode_noalloc(void* stream, void* out, pa_dtype out_dt, const void* q,
+                                       pa_dtype q_dt, const void* k_cache, const void* v_cache,
+                                       pa_dtype cache_dt, const int32_t* block_tables,
+                                       int32_t max_blocks, int32_t num_blocks,
+                                       const int32_t* context_lens, int32_t S, int32_t H_q,
+                                       int32_t H_kv, int32_t D, int32_t bs,
+                                       int32_t max_context_len, float sm_scale, float k_scale,
+                                       float v_scale) {
+  const char* who = "pa_decode_noalloc";
+  bool run = false;
+  const pa_status chk = decode_check(who, out, out_dt, q, q_dt, k_cache, v_cache, cache_dt,
+                                     block_tables, max_blocks, num_blocks, context_lens, S, H_q,
+                                     H_kv, D, bs, max_context_len, sm_scale, k_scale, v_scale,
+                                     &run);
+  if (chk != PA_OK || !run) return chk;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!decode_uses_mfma(q_dt, cache_dt, H_q, H_kv))
+    return decode_dispatch(st, out, out_dt, q, q_dt, k_cache, v_cache, cache_dt, block_tables,
+                           max_blocks, num_blocks, context_lens, S, H_q, H_kv, D, bs,
+                           max_context_len, sm_scale, k_scale, v_scale, nullptr, nullptr);
+  const size_t need = pa_decode_workspace_bytes(S, H_q, H_kv, D, max_context_len);
+  const size_t part_need = need - decode_counter_bytes(S);
+  const size_t n_counter_words = static_cast<size_t>(decode_num_batches(S)) * 2;
+  if (part_need > PA_DECODE_SCRATCH_BYTES - kScratchCounterBytes ||
+      n_counter_words * sizeof(int32_t) > kScratchCounterBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "%s: the call needs %zu bytes of split partials, above the %zu this entry "
+                "point holds (S=%d, H_q=%d, D=%d, max_context_len=%d); use pa_decode with a "
+                "workspace", who, part_need,
+                static_cast<size_t>(PA_DECODE_SCRATCH_BYTES) - kScratchCounterBytes, S, H_q, D,
+                max_context_len);
+  void* base = nullptr;
+  const pa_status sa = scratch_address(&base);
+  if (sa != PA_OK) return sa;
+  int32_t* counters = static_cast<int32_t*>(base);
+  // the array keeps the previous call's contents: the work counters must
+  // start at zero
+  zero_words_kernel<<<dim3(1), dim3(64), 0, st>>>(counters, static_cast<int32_t>(n_counter_words));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PA_ERR_DEVICE, "%s: counter reset launch failed: %s", who, hipGetErrorString(e));
+  return decode_dispatch(st, out, out_dt, q, q_dt, k_cache, v_cache, cache_dt, block_tables,
+                         max_blocks, num_blocks, context_lens, S, H_q, H_kv, D, bs,
+                         max_context_len, sm_scale, k_scale, v_scale, counters,
+                         static_cast<char*>(base) + kScratchCounterBytes);
 }
