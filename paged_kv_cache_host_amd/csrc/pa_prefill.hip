@@ -13,10 +13,11 @@
 // bf16 queries with a bf16 or fp8 e4m3fn cache run on the matrix cores; an
 // fp32 problem runs on the generic VALU kernel.  Q K^T multiplies bf16 by
 // bf16 (v_mfma_f32_32x32x16_bf16).  P V multiplies fp16 by fp16
-// (v_mfma_f32_32x32x16_f16): the softmax weights, at most 2^8 here, keep 11
-// significant bits in fp16 against 8 in bf16, which is what keeps a slice
-// whose first rows see only a handful of keys within the output tolerance;
-// V is converted to fp16 on its way into LDS (exact for e4m3 codes and for
+// (v_mfma_f32_32x32x16_f16): the softmax weights (a lane's 32 weights of a
+// tile sum to at most kPfSafe = 2^15 before the reference is raised, so each
+// stays finite in fp16) keep 11 significant bits in fp16 against 8 in bf16,
+// which is what keeps a slice whose first rows see only a handful of keys
+// within the output tolerance; V is converted to fp16 on its way into LDS (exact for e4m3 codes and for
 // bf16 magnitudes up to 65504, larger bf16 values saturate).
 //
 // Work decomposition.  A work-group owns one KV head, up to eight of the
@@ -184,19 +185,19 @@ struct TileLoader {
   // any use before the store, so their latency overlaps the tile's compute.
   __device__ void load1(u32x4& r, int i, const CR* __restrict__ k_cache,
                         const CR* __restrict__ v_cache, int32_t ids, int32_t kvh,
-                        int32_t H_kv) const {
+                        int32_t H_kv, int32_t num_blocks) const {
     const Piece q = piece(i);
-    const int32_t bk = __builtin_amdgcn_readlane(ids, q.b);
+    const int32_t bk = safe_block(__builtin_amdgcn_readlane(ids, q.b), num_blocks);
     const CR* base = (q.v ? v_cache : k_cache) +
                      (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + q.e0 * kElems;
     r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane * kElems));
   }
   __device__ void load(u32x4* regs, const CR* __restrict__ k_cache, const CR* __restrict__ v_cache,
-                       int32_t ids, int32_t kvh, int32_t H_kv) const {
+                       int32_t ids, int32_t kvh, int32_t H_kv, int32_t num_blocks) const {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const Piece q = piece(i);
-      const int32_t bk = __builtin_amdgcn_readlane(ids, q.b);
+      const int32_t bk = safe_block(__builtin_amdgcn_readlane(ids, q.b), num_blocks);
       const CR* base = (q.v ? v_cache : k_cache) +
                        (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + q.e0 * kElems;
       regs[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane * kElems));
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
   // its K/V loads are issued: lanes 0..3 take the tile's four entries
   // (entries past the context repeat the last one), clamped into the pool.
   auto fetch_ids = [&](int t) -> int32_t {
-    return safe_block(table[min(t * 4 + (lane & 3), n_blk - 1)], num_blocks);
+    return table[min(t * 4 + (lane & 3), n_blk - 1)];
   };
 
   const Loader ld(wave, lane);
@@ -396,11 +397,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
   static_assert(kLd0 + kLdEvery * NLD < NM, "the tile loads fit the slots");
 
   u32x4 regs[NLD];
-  int32_t ids_ahead = fetch_ids(t0);
+  // block ids of the next tile to load (ids_a) and of the one after (ids_b):
+  // fetched two loads ahead, so their latency never delays a tile load
+  int32_t ids_a = fetch_ids(t0);
+  int32_t ids_b = fetch_ids(min(t0 + 1, t1 - 1));
   auto load_tile = [&](int t) {  // tiles past the range reload the last one
     const int tc = min(t, t1 - 1);
-    ld.load(regs, k_cache, v_cache, ids_ahead, kvh, geo.H_kv);
-    ids_ahead = fetch_ids(min(tc + 1, t1 - 1));
+    ld.load(regs, k_cache, v_cache, ids_a, kvh, geo.H_kv, num_blocks);
+    ids_a = ids_b;
+    ids_b = fetch_ids(min(tc + 2, t1 - 1));
   };
   auto store_tile = [&](int t) {
     ld.store(regs, stage(t), kv_end - min(t, t1 - 1) * kPfKeys);
@@ -529,9 +534,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
       if (i + PD < NM) opnd[(i + PD) % (PD + 1)] = operand(i + PD);
       if (i < NLD) ld.store1(regs[i], i, st_lds);
       if (i >= kLd0 && (i - kLd0) % kLdEvery == 0 && (i - kLd0) / kLdEvery < NLD)
-        ld.load1(regs[(i - kLd0) / kLdEvery], (i - kLd0) / kLdEvery, k_cache, v_cache, ids_ahead,
-                 kvh, geo.H_kv);
-      if (i == kLd0 + kLdEvery * NLD) ids_ahead = fetch_ids(min(t_ld + 1, t1 - 1));
+        ld.load1(regs[(i - kLd0) / kLdEvery], (i - kLd0) / kLdEvery, k_cache, v_cache, ids_a,
+                 kvh, geo.H_kv, num_blocks);
+      if (i == kLd0 + kLdEvery * NLD) {
+        ids_a = ids_b;
+        ids_b = fetch_ids(min(t_ld + 2, t1 - 1));
+      }
       if (i < NQK) {
         sn[i & 1] = mfma32x32x16(__builtin_bit_cast(bf16x8, opnd[i % (PD + 1)]), qf[i >> 1],
                                  sn[i & 1]);

@@ -379,3 +379,15 @@ def seq_token_rows(seed: int, sid: int, length: int, h_q: int, h_kv: int, d: int
     v = normal_raw(rng, (length, h_kv, d), "bf16")
     q = normal_raw(rng, (length, h_q, d), "bf16")
     return k, v, q
+
+
+def seq_token_chunk(seed: int, sid: int, chunk: int, rows: int, h_q: int, h_kv: int, d: int):
+    """K, V (raw bf16 [rows, h_kv, d]) and Q (raw bf16 [rows, h_q, d]) of
+    positions chunk*rows .. chunk*rows+rows-1 of sequence ``sid``, each chunk
+    from a stream of its own, so that long sequences are drawn piece by piece
+    and a position's data does not depend on when it is scheduled."""
+    rng = np.random.default_rng([seed, sid, chunk])
+    k = normal_raw(rng, (rows, h_kv, d), "bf16")
+    v = normal_raw(rng, (rows, h_kv, d), "bf16")
+    q = normal_raw(rng, (rows, h_q, d), "bf16")
+    return k, v, q
