@@ -14,7 +14,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PA_LIBRARY selects another build of the same library (the sanitizer build
+# of the host code that the CPU tests run under); it must exist as well
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libpa.so is not built ({LIB_PATH}); run `python -m paged_kv_cache_host_amd.build`")

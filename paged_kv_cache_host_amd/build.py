@@ -69,5 +69,64 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host code of the library (allocator, scheduler, timing) built with
+# AddressSanitizer and UndefinedBehaviorSanitizer by the ROCm clang for the
+# host only, linked with the kernels' objects of the last build() (device
+# code unsanitised).  The CPU parity tests of the host code run against it
+# with PA_LIBRARY set to its path and the clang sanitizer runtime preloaded.
+SANITIZED_SOURCES = ["pa_host.cpp", "pa_sched.cpp", "pa_timing.cpp"]
+SANITIZE = ["-fsanitize=address,undefined", "-shared-libasan", "-fno-omit-frame-pointer"]
+
+
+def host_clang() -> str:
+    p = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang++")
+    p = os.path.normpath(p)
+    if not os.path.exists(p):
+        p = "/opt/rocm/llvm/bin/clang++"
+    if not os.path.exists(p):
+        raise RuntimeError("the ROCm clang++ is required for the sanitizer build")
+    return p
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime to preload into Python."""
+    r = subprocess.run([host_clang(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True, check=True)
+    return r.stdout.strip()
+
+
+def build_sanitized(out_dir: str | None = None, verbose: bool = False) -> str:
+    out_dir = out_dir or os.path.join(BUILD_DIR, "sanitized")
+    os.makedirs(out_dir, exist_ok=True)
+    kernels = [os.path.join(BUILD_DIR, s + ".o") for s in SOURCES if s.endswith(".hip")]
+    if not all(os.path.exists(k) for k in kernels):
+        build(verbose)
+    cxx = host_clang()
+    objs = []
+    for src in SANITIZED_SOURCES:
+        obj = os.path.join(out_dir, src + ".o")
+        cmd = [cxx, "-std=c++17", "-O1", "-g", "-fPIC", *SANITIZE, "-D__HIP_PLATFORM_AMD__",
+               "-I", os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "include"),
+               "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        objs.append(obj)
+    lib = os.path.join(out_dir, "libpa_sanitized.so")
+    rocm_lib = os.path.normpath(os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..",
+                                             "lib"))
+    cmd = [cxx, "-shared", *SANITIZE, "-o", lib, *objs, *kernels, "-L", rocm_lib,
+           "-lamdhip64", f"-Wl,-rpath,{rocm_lib}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {lib}")
+    return lib
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitized" in sys.argv:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
