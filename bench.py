@@ -63,6 +63,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 H_Q, H_KV, D, BLOCK = 64, 8, 128, 16
+DECODE_EXTRA_STEPS = 4    # untimed steps after the timed ones (other kernels' timing)
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -84,6 +85,12 @@ def parse():
     ap.add_argument("--pmc-prefill-summary", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
                     help="HBM traffic of the mixed leg's prefill slices from rocprofv3 runs")
+    ap.add_argument("--trace-prefill-summary", metavar="TRACE_DIR",
+                    help="no GPU work: the mixed leg's prefill roofline from a rocprofv3 "
+                         "--kernel-trace run of bench.py --mixed-only")
+    ap.add_argument("--sq-prefill-summary", nargs="+", metavar="PMC_DIR",
+                    help="no GPU work: matrix-core / vector counters of the mixed leg's "
+                         "prefill slices from rocprofv3 --pmc runs")
     ap.add_argument("--modes-only", action="store_true",
                     help="only the four-schedule serving comparison (printed as one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -122,9 +129,9 @@ def cache_write_bytes(n_tok: int) -> int:
     return n_tok * H_KV * D * 2 * 2 * 2 + 4 * n_tok
 
 
-def traffic_from_profile(digest: str):
-    """Counter-measured HBM bytes per decode launch, if a PMC summary of the
-    current kernel source is committed."""
+def decode_pmc_from_profile(digest: str):
+    """The committed PMC summary of the decode kernel, if it was taken on the
+    current kernel source (else None)."""
     p = os.path.join(PROFILE_DIR, "decode_70b_128seq_pmc.json")
     try:
         d = json.load(open(p))
@@ -132,28 +139,98 @@ def traffic_from_profile(digest: str):
         return None
     if d.get("kernel_source_digest") != digest:
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d
 
 
-def prefill_traffic_from_profile():
-    """Counter-measured HBM bytes (read + written) of the mixed leg's 64
-    prefill slices, if a PMC summary of the current prefill source is
-    committed."""
+def prefill_pmc_from_profile():
+    """The committed PMC summary of the mixed leg's 64 prefill calls, if it
+    was taken on the current prefill source (else None)."""
     try:
         d = json.load(open(os.path.join(PROFILE_DIR, "prefill_32k_slices_pmc.json")))
     except (OSError, ValueError):
         return None
     if d.get("kernel_source_digest") != prefill_source_digest():
         return None
-    return d.get("hbm_bytes")
+    return d
+
+
+def mixed_warmup_slices(warmup: int) -> int:
+    """Prefill slices of the mixed leg's warm passes for --warmup W."""
+    return min(64, max(warmup, 1) * 4)
+
+
+def _host_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_workers() -> int:
+    """Worker processes for the parallel oracle runs: the cores this
+    process may use, at most 16 (one GPU's share of a box's cores)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+_ORACLE_JOB = {}
+
+
+def _oracle_job(part):
+    """One worker's share of an oracle call (set up in _ORACLE_JOB before the
+    workers are forked), on one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return _ORACLE_JOB["fn"](part)
+
+
+def _time_oracle(fn, parts, seconds: float):
+    """Mean wall time of fn over all parts in three configurations: one
+    thread; one process with the BLAS default threads; the parts spread over
+    worker processes of one BLAS thread each.  Returns {config: (seconds,
+    cores)}.  Runs before the GPU is initialised (the workers are forked)."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    def run(call, budget):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            call()
+            reps += 1
+            if time.perf_counter() - t0 > budget:
+                return (time.perf_counter() - t0) / reps, reps
+
+    out = {}
+    with threadpool_limits(limits=1):
+        out["1 thread"] = run(lambda: [fn(p) for p in parts], seconds / 3)[0], 1
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    out[f"{blas} BLAS threads"] = run(lambda: [fn(p) for p in parts], seconds / 3)[0], blas
+    n = min(_cpu_workers(), len(parts))
+    _ORACLE_JOB["fn"] = fn
+    with mp.get_context("fork").Pool(n) as pool:
+        pool.map(_oracle_job, parts)           # workers started and warm
+        out[f"{n} processes x 1 thread"] = \
+            run(lambda: pool.map(_oracle_job, parts), seconds / 3)[0], n
+    return out
+
+
+def _best(configs: dict, work: float, scale: float):
+    """(value, cores, config name, all) with value = work / time / scale."""
+    allv = {k: round(work / t / scale, 3) for k, (t, _) in configs.items()}
+    name = max(allv, key=allv.get)
+    return allv[name], configs[name][1], name, allv
 
 
 def cpu_baseline(n_seqs: int):
     """The oracle (numpy, fp64) on the first n_seqs sequences of the same
     workload: gather through the block tables + softmax attention, timed
-    without data generation and cache construction."""
-    from threadpoolctl import threadpool_info
-
+    without data generation and cache construction, in its best
+    configuration of the host's cores (one thread, BLAS threads, or the
+    sequences spread over worker processes)."""
     import workloads
     from oracle import allocator as oa
     from oracle import attention as oat
@@ -176,39 +253,19 @@ def cpu_baseline(n_seqs: int):
     tables = np.asarray(tables)
     lens = np.asarray(lens)
     sm = float(np.float32(1.0) / np.float32(math.sqrt(D)))
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        oat.decode(q, kc, vc, tables, lens, H_KV, sm, "bf16")
-        reps += 1
-        if time.perf_counter() - t0 > 10.0:
-            break
-    dt = (time.perf_counter() - t0) / reps
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    # the same on one thread (a shorter sample)
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):
-        t1 = time.perf_counter()
-        reps1 = 0
-        while True:
-            oat.decode(q, kc, vc, tables, lens, H_KV, sm, "bf16")
-            reps1 += 1
-            if time.perf_counter() - t1 > 5.0:
-                break
-        dt1 = (time.perf_counter() - t1) / reps1
-    model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return {"value": decode_bytes(lens) / dt / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "value_1_thread": decode_bytes(lens) / dt1 / 1e9,
+    parts = [np.arange(i, len(L), _cpu_workers()) for i in range(min(_cpu_workers(), len(L)))]
+
+    def fn(idx):
+        return oat.decode(q[idx], kc, vc, tables[idx], lens[idx], H_KV, sm, "bf16")
+
+    configs = _time_oracle(fn, parts, 24.0)
+    value, cores, name, allv = _best(configs, decode_bytes(lens), 1e9)
+    return {"value": value, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "config": name, "all_configs_gb_s": allv,
             "sample": f"first {len(L)} of the 128 sequences ({int(L.sum())} context tokens), "
-                      f"one decode launch's gather + fp64 attention, mean of {reps} runs; "
-                      f"host {model or 'unknown'}, {len(os.sched_getaffinity(0))} cores visible"}
+                      f"one decode launch's gather + fp64 attention, sequences split "
+                      f"round-robin over workers; host {_host_model()}, "
+                      f"{len(os.sched_getaffinity(0))} cores visible"}
 
 
 CAL_BYTES = 1 << 30
@@ -252,19 +309,31 @@ def _pmc_mean(rows, key: str) -> tuple[float, int]:
     return sum(vals) / len(vals), len(vals)
 
 
-def pmc_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str):
+def pmc_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str,
+                warmup: int, steps: int):
     """HBM traffic of one decode launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs (KiB per dispatch), each scaled by what the same counter reads for
-    the calibration kernel of known size."""
+    runs (KiB per dispatch) of ``bench.py --decode-only --steps K --warmup W``,
+    each scaled by what the same counter reads for the calibration kernel of
+    known size, beside the algorithmic bytes of the same launches (launch i
+    of that run attends contexts of the workload's lengths + i tokens)."""
+    import workloads
+
     f_dec, n_f = _pmc_mean(_pmc_rows(fetch_dir, "FETCH_SIZE"), "decode_kernel<pa::BF16, 128, 16>")
     w_dec, n_w = _pmc_mean(_pmc_rows(write_dir, "WRITE_SIZE"), "decode_kernel<pa::BF16, 128, 16>")
     f_cal, _ = _pmc_mean(_pmc_rows(cal_fetch_dir, "FETCH_SIZE"), "neg")
     w_cal, _ = _pmc_mean(_pmc_rows(cal_write_dir, "WRITE_SIZE"), "neg")
     f_scale = CAL_BYTES / (f_cal * 1024.0)
     w_scale = CAL_BYTES / (w_cal * 1024.0)
+    lengths, _, _ = workloads.decode_70b_layout()
+    n_launch = warmup + steps + DECODE_EXTRA_STEPS
+    if n_f != n_launch or n_w != n_launch:
+        raise SystemExit(f"expected {n_launch} decode dispatches (--warmup {warmup} --steps "
+                         f"{steps}), got {n_f} / {n_w}")
+    alg = float(np.mean([decode_bytes(lengths + i) for i in range(n_launch)]))
     out = {
         "kernel": "decode_kernel<BF16,128,16>",
-        "workload": "decode-70b-shaped, 128 seqs (bench.py default)",
+        "workload": f"decode-70b-shaped, 128 seqs: bench.py --decode-only --warmup {warmup} "
+                    f"--steps {steps} (every decode launch of the run)",
         "kernel_source_digest": kernel_source_digest(),
         "fetch_kib_per_launch_raw": round(f_dec, 1), "fetch_dispatches": n_f,
         "write_kib_per_launch_raw": round(w_dec, 1), "write_dispatches": n_w,
@@ -273,14 +342,16 @@ def pmc_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_di
                         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
         "hbm_read_bytes_per_launch": int(f_dec * 1024 * f_scale),
         "hbm_write_bytes_per_launch": int(w_dec * 1024 * w_scale),
+        "algorithmic_bytes_per_launch": int(alg),
     }
     out["hbm_bytes_per_launch"] = out["hbm_read_bytes_per_launch"] + out["hbm_write_bytes_per_launch"]
+    out["traffic_ratio"] = round(out["hbm_bytes_per_launch"] / alg, 4)
     print(json.dumps(out, indent=1))
 
 
 def _pmc_seq(d: str, counter: str, key: str):
-    """Values of one counter for the dispatches of kernels named *key*, in
-    dispatch order."""
+    """(dispatch id, value) of one counter for the dispatches of kernels named
+    *key*, in dispatch order."""
     import csv
     import glob
     rows = []
@@ -289,20 +360,34 @@ def _pmc_seq(d: str, counter: str, key: str):
             if r.get("Counter_Name") == counter and key in r["Kernel_Name"]:
                 rows.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
     rows.sort()
-    return [v for _, v in rows]
+    return rows
 
 
-def pmc_prefill_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str):
-    """HBM traffic of the mixed leg's 64 prefill slices (one-stream pass of
-    ``bench.py --mixed-only``: the prefill launches are, in order, 20 warm-up
-    slices, the 64 slices of that pass, then those of the two-stream pass)
+def _window(prefill, merge, first: int, n: int):
+    """Sum of the prefill dispatches [first, first + n) and of the merge
+    dispatches that follow one of them (before the next prefill dispatch)."""
+    ids = [i for i, _ in prefill]
+    lo = ids[first]
+    hi = ids[first + n] if first + n < len(ids) else float("inf")
+    tot = sum(v for _, v in prefill[first:first + n])
+    tot += sum(v for i, v in merge if lo < i < hi)
+    return tot
+
+
+def pmc_prefill_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str,
+                        warmup: int):
+    """HBM traffic of the mixed leg's 64 prefill calls (one-stream pass of
+    ``bench.py --mixed-only --warmup W``: the prefill launches are, in order,
+    the warm pass's slices, the 64 slices of the one-stream pass, then those
+    of the two-stream passes), prefill kernel and merge kernel together,
     against their algorithmic bytes: the K/V of the prefix and the slice
     (read once), Q and the output."""
-    key = "prefill_kernel<pa::BF16, 128>"
-    f = _pmc_seq(fetch_dir, "FETCH_SIZE", key)
-    w = _pmc_seq(write_dir, "WRITE_SIZE", key)
-    if len(f) < 84 or len(w) < 84:
-        raise SystemExit(f"expected >= 84 {key} dispatches, got {len(f)} / {len(w)}")
+    key, mkey = "prefill_kernel<pa::BF16, 128>", "prefill_merge_kernel<128>"
+    f, w = _pmc_seq(fetch_dir, "FETCH_SIZE", key), _pmc_seq(write_dir, "WRITE_SIZE", key)
+    fm, wm = _pmc_seq(fetch_dir, "FETCH_SIZE", mkey), _pmc_seq(write_dir, "WRITE_SIZE", mkey)
+    first = mixed_warmup_slices(warmup)
+    if len(f) < first + 64 or len(w) < first + 64:
+        raise SystemExit(f"expected >= {first + 64} {key} dispatches, got {len(f)} / {len(w)}")
     f_cal, _ = _pmc_mean(_pmc_rows(cal_fetch_dir, "FETCH_SIZE"), "neg")
     w_cal, _ = _pmc_mean(_pmc_rows(cal_write_dir, "WRITE_SIZE"), "neg")
     f_scale = CAL_BYTES / (f_cal * 1024.0)
@@ -310,21 +395,119 @@ def pmc_prefill_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_
     C = 512
     alg_read = sum((C * c + C) * H_KV * D * 2 * 2 + C * H_Q * D * 2 for c in range(64))
     alg_write = 64 * C * H_Q * D * 2
-    read = sum(f[20:84]) * 1024 * f_scale
-    write = sum(w[20:84]) * 1024 * w_scale
+    read = _window(f, fm, first, 64) * 1024 * f_scale
+    write = _window(w, wm, first, 64) * 1024 * w_scale
+    read_k = sum(v for _, v in f[first:first + 64]) * 1024 * f_scale
+    write_k = sum(v for _, v in w[first:first + 64]) * 1024 * w_scale
     print(json.dumps({
-        "kernel": "prefill_kernel<BF16,128>",
-        "workload": "mixed leg, 64 causal 512-token slices of a 32768-token prompt, one stream",
+        "kernel": "prefill_kernel<BF16,128> + prefill_merge_kernel<128>",
+        "workload": f"mixed leg, 64 causal 512-token slices of a 32768-token prompt, one "
+                    f"stream (bench.py --mixed-only --warmup {warmup}: prefill dispatches "
+                    f"{first}..{first + 63} and the merges that follow them)",
         "calibration": {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
         "hbm_read_bytes": int(read), "algorithmic_read_bytes": alg_read,
         "read_ratio": round(read / alg_read, 3),
         "hbm_write_bytes": int(write), "algorithmic_write_bytes": alg_write,
         "write_ratio": round(write / alg_write, 3),
         "hbm_bytes": int(read + write),
-        "split_partials_note": "slices whose key range is split write fp32 partials for the "
-                               "merge kernel, which the algorithmic count leaves out",
+        "prefill_kernel_only": {"hbm_read_bytes": int(read_k), "hbm_write_bytes": int(write_k)},
+        "split_partials_note": "slices whose key range is split write fp32 partials that the "
+                               "merge kernel reads back; the algorithmic count leaves them out",
         "kernel_source_digest": prefill_source_digest(),
     }, indent=1))
+
+
+def _trace_rows(d: str):
+    """(dispatch id, kernel name, duration ns) of a rocprofv3 --kernel-trace
+    CSV run."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                         int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
+    return rows
+
+
+def trace_prefill_summary(trace_dir: str, warmup: int):
+    """The prefill roofline of the mixed leg recomputed from a rocprofv3
+    --kernel-trace run of ``bench.py --mixed-only --warmup W``: durations of
+    the one-stream pass's 64 prefill dispatches and of the merge dispatches
+    that follow them, against the algorithmic causal flops."""
+    rows = _trace_rows(trace_dir)
+    pf = [(i, t) for i, n, t in rows if "prefill_kernel<pa::BF16, 128>" in n]
+    mg = [(i, t) for i, n, t in rows if "prefill_merge_kernel<128>" in n]
+    first = mixed_warmup_slices(warmup)
+    if len(pf) < first + 64:
+        raise SystemExit(f"expected >= {first + 64} prefill dispatches, got {len(pf)}")
+    t_pf = sum(t for _, t in pf[first:first + 64]) / 1e3
+    t_all = _window(pf, mg, first, 64) / 1e3
+    C = 512
+    flops = 4 * D * H_Q * sum(C * (c * C) + C * (C + 1) // 2 for c in range(64))
+    print(json.dumps({
+        "workload": f"mixed leg, one-stream pass (bench.py --mixed-only --warmup {warmup}: "
+                    f"prefill dispatches {first}..{first + 63} and their merges)",
+        "prefill_kernel_us_total": round(t_pf, 1), "with_merge_us_total": round(t_all, 1),
+        "algorithmic_flops": flops,
+        "achieved_tflops": round(flops / t_all / 1e6, 1),
+        "frac_of_bf16_peak": round(flops / t_all / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kernel_only_tflops": round(flops / t_pf / 1e6, 1),
+        "kernel_source_digest": prefill_source_digest(),
+    }, indent=1))
+
+
+def sq_prefill_summary(dirs, warmup: int):
+    """Matrix-core and vector-unit counters of the mixed leg's 64 one-stream
+    prefill dispatches (rocprofv3 --pmc runs of ``bench.py --mixed-only``,
+    several counter passes), summed over the window.  SQ counters are
+    aggregated over the 32 shader engines (8 XCDs x 4), GRBM_GUI_ACTIVE over
+    the 8 XCDs; a busy fraction is per SIMD (256 CUs x 4 SIMDs)."""
+    key = "prefill_kernel<pa::BF16, 128>"
+    first = mixed_warmup_slices(warmup)
+    tot = {}
+    import csv
+    import glob
+    for d in dirs:
+        rows = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if key in r["Kernel_Name"]:
+                    rows.setdefault(r["Counter_Name"], []).append(
+                        (int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        for c, v in rows.items():
+            v.sort()
+            if len(v) < first + 64:
+                raise SystemExit(f"{c}: {len(v)} dispatches")
+            tot[c] = sum(x for _, x in v[first:first + 64])
+    out = {"workload": f"mixed leg, one-stream pass, prefill dispatches {first}..{first + 63}",
+           "counters": {k: tot[k] for k in sorted(tot)}, "kernel_source_digest":
+           prefill_source_digest()}
+    simds = 256 * 4
+    if "GRBM_GUI_ACTIVE" in tot:
+        cyc = tot["GRBM_GUI_ACTIVE"] / 8
+        out["gpu_cycles"] = cyc
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in tot:
+            out["mfma_busy_frac"] = round(tot["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / cyc, 4)
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in tot and "SQ_VALU_MFMA_COEXEC_CYCLES" in tot:
+        out["valu_coexec_share_of_mfma_busy"] = round(
+            tot["SQ_VALU_MFMA_COEXEC_CYCLES"] / tot["SQ_VALU_MFMA_BUSY_CYCLES"], 4)
+    if "SQ_INSTS_MFMA" in tot and "SQ_INSTS_VALU" in tot:
+        out["valu_insts_per_mfma"] = round((tot["SQ_INSTS_VALU"] - tot["SQ_INSTS_MFMA"]) /
+                                           tot["SQ_INSTS_MFMA"], 3)
+    if "SQ_INSTS_MFMA" in tot and "SQ_INSTS_VALU_TRANS_F32" in tot:
+        out["exp_per_mfma"] = round(tot["SQ_INSTS_VALU_TRANS_F32"] / tot["SQ_INSTS_MFMA"], 3)
+    if "SQ_INSTS_MFMA" in tot and "SQ_INSTS_LDS" in tot:
+        out["lds_insts_per_mfma"] = round(tot["SQ_INSTS_LDS"] / tot["SQ_INSTS_MFMA"], 3)
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in tot and "SQ_INSTS_VALU_MFMA_MOPS_F16" in tot:
+        C = 512
+        flops = 4 * D * H_Q * sum(C * (c * C) + C * (C + 1) // 2 for c in range(64))
+        # one MOP = 256 multiply-adds = 512 flops (a 32x32x16 MFMA counts 64)
+        mops = tot["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + tot["SQ_INSTS_VALU_MFMA_MOPS_F16"]
+        out["mfma_flops_counted"] = mops * 512
+        out["mfma_flops_over_algorithmic"] = round(mops * 512 / flops, 4)
+    print(json.dumps(out, indent=1))
 
 
 def _fill_random(kv, slots: np.ndarray, gen, dev, chunk: int = 1 << 16):
@@ -367,7 +550,7 @@ def decode_leg(args, dev):
     lengths, num_blocks, free_order = workloads.decode_70b_layout()
     S = len(lengths)
     seqs = np.arange(S, dtype=np.int64)
-    EXTRA, TIME_EVERY = 4, 4
+    EXTRA, TIME_EVERY = DECODE_EXTRA_STEPS, 4
     max_ctx = int(lengths.max()) + W + K + EXTRA
     MB = -(-max_ctx // BLOCK)
     # the workload's pool (10% free) covers the growth of a default run; a
@@ -470,16 +653,24 @@ def decode_leg(args, dev):
         if i % GROUP == GROUP - 1:
             ev_group[g % 2].record(compute)
 
-    for i in range(W):
-        step(i, False)
-    torch.cuda.synchronize()
     # Kernel timing: the library attaches a pair of HIP events to a selected
     # kernel's launch on the stream it launches on (here `compute`).  Each
     # timed launch costs the stream a few microseconds, so the timed steps
     # time every TIME_EVERY-th decode launch only; a few more steps time the
-    # step's other kernels.
-    pa.check(pa.pa_timing_enable(["decode"], every=TIME_EVERY))
+    # step's other kernels.  The warm-up steps already carry the timed
+    # launches: the first launch with events attached pays a one-time set-up
+    # (measured ~0.4 ms), which must not land in the timed window.
+    pa.check(pa.pa_timing_enable(["decode", "decode_merge", "stage_cache_write"],
+                                 every=TIME_EVERY))
+    # the collector is run and frozen before the warm-up steps, not right
+    # before the timed ones: a full collection walks the whole heap and
+    # leaves the host's caches cold for the first timed step (measured
+    # ~0.25 ms of host time for that step alone)
     _settle()
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    pa.check(pa.pa_timing_enable(["decode"], every=TIME_EVERY))
     t0 = time.perf_counter()
     for i in range(K):
         step(W + i, True)
@@ -634,15 +825,24 @@ def mixed_leg(args, dev):
         kv.close()
         return wall, tm
 
-    run_pass(False, min(iters, max(args.warmup, 1) * 4), False)
+    # the warm pass carries timed launches too: the first launch with events
+    # attached pays a one-time set-up, which must not land in a timed pass
+    pa.check(pa.pa_timing_enable(["prefill", "prefill_merge"]))
+    run_pass(False, mixed_warmup_slices(args.warmup), False)
+    pa.check(pa.pa_timing_enable(False))
     wall1, tm = run_pass(True, iters, False)
-    run_pass(False, min(iters, max(args.warmup, 1) * 4), True)
+    run_pass(False, mixed_warmup_slices(args.warmup), True)
     wall, _ = run_pass(False, iters, True)
     pairs = sum(C * (c * C) + C * (C + 1) // 2 for c in range(iters))
     flops = 4 * D * H_Q * pairs
     n_pf, mean_pf, tot_pf = tm["prefill"]
     assert n_pf == iters, tm
-    achieved = flops / (tot_pf / 1e6) / 1e12
+    tot_merge = tm["prefill_merge"][2]
+    # a pa_prefill_chunk call is the prefill kernel plus, for slices whose
+    # key range is split, the merge kernel: the roofline counts both
+    achieved = flops / ((tot_pf + tot_merge) / 1e6) / 1e12
+    achieved_kernel = flops / (tot_pf / 1e6) / 1e12
+    pmc = prefill_pmc_from_profile()
     return {
         "tokens_per_s": iters * NT / wall,
         "ms_per_iteration": wall / iters * 1e3,
@@ -653,10 +853,17 @@ def mixed_leg(args, dev):
         "prefill_roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "traffic": prefill_traffic_from_profile(),
-                             "traffic_unit": "HBM bytes over the 64 slices",
+                             "time": "prefill_kernel + prefill_merge_kernel of the 64 calls",
+                             "traffic": None if pmc is None else pmc["hbm_bytes"],
+                             "traffic_unit": "HBM bytes over the 64 calls (both kernels)",
+                             "traffic_algorithmic_bytes": None if pmc is None else
+                             pmc["algorithmic_read_bytes"] + pmc["algorithmic_write_bytes"],
                              "kernel": "prefill_kernel<BF16,128>",
                              "kernel_us_total": round(tot_pf, 1),
+                             "merge_us_total": round(tot_merge, 1),
+                             "kernel_only": {"achieved": round(achieved_kernel, 1),
+                                             "frac": round(achieved_kernel /
+                                                           MFMA_BF16_PEAK_TFLOPS, 4)},
                              "algorithmic_flops": flops},
         "prefill_merge_us_total": round(tm["prefill_merge"][2], 1),
     }
@@ -1084,9 +1291,9 @@ def modes_leg(args, dev):
 
 def cpu_prefill_baseline():
     """The oracle on one 512-token slice at prefix 512 (gather + fp64 causal
-    attention of all 64 heads), as GFLOP/s on the algorithmic count."""
-    from threadpoolctl import threadpool_info
-
+    attention of all 64 heads), as GFLOP/s on the algorithmic count, in its
+    best configuration of the host's cores (the KV heads' groups spread over
+    worker processes, or threads)."""
     from oracle import allocator as oa
     from oracle import attention as oat
     from oracle import cache as oc
@@ -1105,18 +1312,20 @@ def cpu_prefill_baseline():
                    "bf16", "bf16")
     q = codecs.decode(workloads.normal_raw(rng, (C, H_Q, D), "bf16"), "bf16")
     sm = float(np.float32(1.0) / np.float32(math.sqrt(D)))
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        oat.prefill_chunk(q, P0, kc, vc, pool.block_table(0), H_KV, sm, "bf16")
-        reps += 1
-        if time.perf_counter() - t0 > 8.0:
-            break
-    dt = (time.perf_counter() - t0) / reps
+    G = H_Q // H_KV
+    table = pool.block_table(0)
+
+    def fn(kvh):
+        # the oracle on one KV head and its query heads
+        return oat.prefill_chunk(q[:, kvh * G:(kvh + 1) * G], P0, kc[:, kvh:kvh + 1],
+                                 vc[:, kvh:kvh + 1], table, 1, sm, "bf16")
+
+    configs = _time_oracle(fn, list(range(H_KV)), 24.0)
     flops = 4 * D * H_Q * (C * P0 + C * (C + 1) // 2)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": flops / dt / 1e9, "unit": "GFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one 512-token slice at prefix 512 (all 64 heads), mean of {reps} runs"}
+    value, cores, name, allv = _best(configs, flops, 1e9)
+    return {"value": value, "unit": "GFLOP/s", "cores": int(cores), "kind": "oracle",
+            "config": name, "all_configs_gflop_s": allv,
+            "sample": "one 512-token slice at prefix 512, all 64 heads (8 KV-head groups)"}
 
 
 def main():
@@ -1131,11 +1340,25 @@ def main():
         calibrate_copy()
         return
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary)
+        pmc_summary(*args.pmc_summary, args.warmup, args.steps)
         return
     if args.pmc_prefill_summary:
-        pmc_prefill_summary(*args.pmc_prefill_summary)
+        pmc_prefill_summary(*args.pmc_prefill_summary, args.warmup)
         return
+    if args.trace_prefill_summary:
+        trace_prefill_summary(args.trace_prefill_summary, args.warmup)
+        return
+    if args.sq_prefill_summary:
+        sq_prefill_summary(args.sq_prefill_summary, args.warmup)
+        return
+
+    # The CPU baselines run first: their worker processes are forked, which
+    # must happen before this process initialises the GPU.
+    cpu = cpu_pf = None
+    if not args.no_cpu_baseline and not (args.modes_only or args.mixed_only):
+        cpu = cpu_baseline(args.cpu_sample_seqs)
+        if not args.decode_only:
+            cpu_pf = cpu_prefill_baseline()
 
     import torch
 
@@ -1152,6 +1375,7 @@ def main():
 
     d = decode_leg(args, dev)
     digest = kernel_source_digest()
+    dpmc = decode_pmc_from_profile(digest)
     result = {
         "metric": "paged-attn decode HBM GB/s (% peak); mixed decode+prefill tokens/s per layer",
         "value": round(d["value"], 2),
@@ -1172,7 +1396,12 @@ def main():
                    "num_blocks": d["num_blocks"]},
         "roofline": {"bound": "hbm", "achieved": round(d["achieved"], 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(d["achieved"] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(digest), "kernel": "decode_kernel<BF16,128,16>",
+                     "traffic": None if dpmc is None else dpmc["hbm_bytes_per_launch"],
+                     "traffic_algorithmic_bytes": None if dpmc is None else
+                     dpmc["algorithmic_bytes_per_launch"],
+                     "traffic_note": "counter bytes and algorithmic bytes per launch of the "
+                                     "profiled run (its contexts differ slightly from this run's)",
+                     "kernel": "decode_kernel<BF16,128,16>",
                      "kernel_us": round(d["kernel_us"], 2),
                      "other_kernels_us": {"decode_merge_kernel": round(d["merge_us"], 2),
                                           "stage_cache_write_kernel":
@@ -1191,12 +1420,9 @@ def main():
         result["block_size"] = block_size_leg(args, dev)
         result["trace"] = trace_leg(args, dev)
         result["schedules"] = modes_leg(args, dev)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_sample_seqs)
-        if "mixed" in result:
-            result["mixed"]["cpu_baseline"] = cpu_prefill_baseline()
-    else:
-        result["cpu_baseline"] = None
+    result["cpu_baseline"] = cpu
+    if "mixed" in result and cpu_pf is not None:
+        result["mixed"]["cpu_baseline"] = cpu_pf
     print(json.dumps(result), flush=True)
 
 

@@ -527,8 +527,10 @@ pa_status pa_decode_append(void* stream, const int32_t* slots, const int32_t* le
 /* Time the kernels whose bits are set in `mask` (-1: all, 0: none): of each
  * selected kernel, the launches 0, every, 2 * every, ... counted from this
  * call (every >= 1, else PA_ERR_INVALID).  Either way the kept launches are
- * forgotten.  Call it with no timed launch of the previous recording still
- * in flight (its events are reused). */
+ * forgotten.  The events of a selected kernel's first 64 timed launches are
+ * created by this call (later ones on first use), so enable timing before,
+ * not inside, the region being timed.  Call it with no timed launch of the
+ * previous recording still in flight (its events are reused). */
 pa_status pa_timing_enable(int32_t mask, int32_t every);
 
 /* Wait for the recorded launches of `kernel` [host string] and report their

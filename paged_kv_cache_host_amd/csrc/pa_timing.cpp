@@ -25,6 +25,7 @@ namespace pa {
 namespace {
 
 constexpr int kCapacity = 4096;  // launches kept per kernel between resets
+constexpr int kReserve = 64;     // event pairs created when a kernel is selected
 
 struct Slot {
   hipEvent_t start = nullptr, stop = nullptr;
@@ -82,9 +83,24 @@ extern "C" pa_status pa_timing_enable(int32_t mask, int32_t every) {
   std::lock_guard<std::mutex> lock(g_mu);
   g_mask = mask;
   g_every = every;
-  for (auto& t : g_tracks) {
+  for (int k = 0; k < kKernelCount; ++k) {
+    Track& t = g_tracks[k];
     t.count = 0;
     t.seen = 0;
+    // the events of a selected kernel's first launches are created here,
+    // not inside the launches (and a timed region) that use them
+    if (mask & (1 << k)) {
+      while (static_cast<int>(t.slots.size()) < kReserve) {
+        Slot sl;
+        if (hipEventCreate(&sl.start) != hipSuccess) break;
+        if (hipEventCreate(&sl.stop) != hipSuccess) {
+          (void)hipEventDestroy(sl.start);
+          break;
+        }
+        t.slots.push_back(sl);
+      }
+      (void)hipGetLastError();
+    }
   }
   return PA_OK;
 }
