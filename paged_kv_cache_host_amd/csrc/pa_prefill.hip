@@ -45,10 +45,7 @@
 // quads swapped; with that permutation the 8 keys a lane holds for each
 // 16-key step of P^T are consecutive, which is what one 16-byte read of the
 // token-minor V layout supplies.
-#include <type_traits>
-
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "pa_prefill_body.h"
 
 namespace pa {
 
@@ -62,225 +59,6 @@ pa_status launch_attend_generic(hipStream_t st, void* out, pa_dtype out_dt, cons
 
 namespace {
 
-constexpr int kPfWaves = 8;                 // waves per work-group
-constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfRows = 32;                 // query positions per wave
-constexpr int kPfKeys = 64;                 // keys per LDS tile (4 blocks)
-constexpr int kPfTargetGroups = 256;        // one work-group per compute unit
-constexpr int kPfMaxSplit = 8;
-constexpr int kPfMinKeysPerSplit = 1024;
-constexpr float kPfSafe = 32768.0f;         // bound on a lane's 32 weights of one tile
-
-// LDS bytes of one stage: K [D/8 chunks][64 rows][16 B] + V [D/16][8 chunks][16 dims][16 B].
-template <int D>
-constexpr int stage_bytes() {
-  return D * kPfKeys * 2 * 2;
-}
-
-// Position of key `tok` (0..15) of a block among the 16 K rows of that block
-// in LDS: the second and third groups of four trade places.
-__device__ __forceinline__ int krow_of(int tok) {
-  const int quad = tok >> 2;
-  const int swapped = (quad == 1 || quad == 2) ? (3 - quad) : quad;
-  return (swapped << 2) | (tok & 3);
-}
-
-// V in LDS: chunk c (8 keys, 16 B) of dimension d.  The 16 dimensions
-// d0..d0+15 of one chunk are 256 contiguous bytes, so the 16 lanes of an
-// MFMA operand read that take consecutive dimensions hit distinct banks.
-__device__ __forceinline__ int v_off(int d, int c) {
-  return (((d >> 4) * (kPfKeys / 8) + c) << 8) + ((d & 15) << 4);
-}
-
-struct PfGeom {
-  int H_kv, G, hpw, psub, n_head_groups, n_pos_tiles, n_split;
-};
-
-// Work split shared by the launcher and the workspace query.
-PfGeom pf_geometry(int32_t n_chunks, int32_t max_q_len, int32_t H_q, int32_t H_kv,
-                   int32_t max_context_len) {
-  PfGeom g;
-  g.H_kv = H_kv;
-  g.G = H_q / H_kv;
-  g.hpw = g.G < kPfWaves ? g.G : kPfWaves;
-  g.psub = kPfWaves / g.hpw;
-  g.n_head_groups = (g.G + kPfWaves - 1) / kPfWaves;
-  const int pos_per_group = kPfRows * g.psub;
-  g.n_pos_tiles = (max_q_len + pos_per_group - 1) / pos_per_group;
-  const int64_t groups =
-      static_cast<int64_t>(n_chunks) * g.n_pos_tiles * H_kv * g.n_head_groups;
-  int split = groups > 0 ? static_cast<int>(kPfTargetGroups / groups) : 1;
-  const int by_keys = max_context_len / kPfMinKeysPerSplit;
-  if (split > by_keys) split = by_keys;
-  if (split > kPfMaxSplit) split = kPfMaxSplit;
-  if (split < 1) split = 1;
-  g.n_split = split;
-  return g;
-}
-
-__device__ __forceinline__ f16x8 pack_f16x8(const float* v) {
-  f16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = static_cast<_Float16>(v[i]);
-  return r;
-}
-
-// Moves one 64-key tile (4 blocks x K and V of one KV head) from the paged
-// cache into an LDS stage as 16-byte pieces spread over the work-group's
-// threads: piece p = wave * 64 + lane + i * threads.  A block-head tile has a
-// multiple of 64 pieces, so which tensor and block a piece belongs to is the
-// same for the whole wave (scalar), and every offset splits into a scalar
-// part and a lane part that does not depend on i.
-template <typename CacheT, int D>
-struct TileLoader {
-  using CR = typename CacheT::raw;
-  static constexpr int kElems = 16 / sizeof(CR);            // cache elements per piece
-  static constexpr int kPerBlock = D * kBlock / kElems;     // pieces per (block, head), K or V
-  static constexpr int kHalf = 4 * kPerBlock;               // K pieces of a tile
-  static constexpr int kPieces = 2 * kHalf;
-  static constexpr int NLD = kPieces / kPfThreads;          // pieces per thread
-  static_assert(kPieces % kPfThreads == 0, "tile pieces must divide over the threads");
-  static_assert(kPerBlock % kWave == 0, "a wave's pieces must share one block");
-  static constexpr bool kWide = sizeof(CR) == 1;            // fp8 pieces widen to two chunks
-
-  int wave;      // scalar
-  int lane;
-  int k_lane;    // LDS offset, lane part, K pieces
-  int v_lane;    // LDS offset, lane part, V pieces
-  int v_key;     // first key of the lane's V piece inside its block
-
-  __device__ TileLoader(int wave_, int lane_) : wave(wave_), lane(lane_) {
-    if (!kWide) {
-      k_lane = (lane >> 4) * (kPfKeys * 16) + krow_of(lane & 15) * 16;
-      v_lane = (lane >> 5) * 2048 + (lane & 1) * 256 + ((lane >> 1) & 15) * 16;
-      v_key = (lane & 1) * 8;
-    } else {
-      k_lane = (lane >> 4) * 2 * (kPfKeys * 16) + krow_of(lane & 15) * 16;
-      v_lane = (lane >> 4) * 2048 + (lane & 15) * 16;
-      v_key = 0;
-    }
-  }
-  // scalar description of piece i of this wave
-  struct Piece {
-    bool v;
-    int b;      // block of the tile
-    int e0;     // index of the wave's first piece inside the (block, head) tile
-  };
-  __device__ Piece piece(int i) const {
-    const int p = wave * kWave + i * kPfThreads;
-    Piece q;
-    // when the K half is a whole number of sweeps over the threads, which
-    // tensor a piece belongs to depends on i alone
-    q.v = kHalf % kPfThreads == 0 ? i * kPfThreads >= kHalf : p >= kHalf;
-    const int pp = q.v ? p - kHalf : p;
-    q.b = pp / kPerBlock;
-    q.e0 = pp % kPerBlock;
-    return q;
-  }
-
-  // ids: lanes 0..3 hold the tile's four block ids, already inside the
-  // pool.  Blocks past the context are loaded too (any valid id): their
-  // keys lie beyond `valid`, so store() zeroes their V and the causal mask
-  // drops their scores.  Loading unconditionally keeps the loads free of
-  // any use before the store, so their latency overlaps the tile's compute.
-  __device__ void load1(u32x4& r, int i, const CR* __restrict__ k_cache,
-                        const CR* __restrict__ v_cache, int32_t ids, int32_t kvh,
-                        int32_t H_kv, int32_t num_blocks) const {
-    const Piece q = piece(i);
-    const int32_t bk = safe_block(__builtin_amdgcn_readlane(ids, q.b), num_blocks);
-    const CR* base = (q.v ? v_cache : k_cache) +
-                     (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + q.e0 * kElems;
-    r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane * kElems));
-  }
-  __device__ void load(u32x4* regs, const CR* __restrict__ k_cache, const CR* __restrict__ v_cache,
-                       int32_t ids, int32_t kvh, int32_t H_kv, int32_t num_blocks) const {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const Piece q = piece(i);
-      const int32_t bk = safe_block(__builtin_amdgcn_readlane(ids, q.b), num_blocks);
-      const CR* base = (q.v ? v_cache : k_cache) +
-                       (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + q.e0 * kElems;
-      regs[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane * kElems));
-    }
-  }
-
-  // Piece i of the tile into a stage, V beyond the context not cleared.
-  __device__ void store1(const u32x4& w0, int i, uint8_t* stage) const {
-    const Piece q = piece(i);
-    u32x4 w = w0;
-    if (!kWide) {
-      if (!q.v) {
-        const int off = (q.e0 >> 4) * (kPfKeys * 16) + q.b * kBlock * 16;
-        *reinterpret_cast<u32x4*>(stage + off + k_lane) = w;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(w[j]);
-        const int off = D * kPfKeys * 2 + ((q.e0 >> 1) >> 4) * 2048 + 2 * q.b * 256;
-        *reinterpret_cast<u32x4*>(stage + off + v_lane) = w;
-      }
-    } else if (!q.v) {
-      const int off = (q.e0 >> 4) * 2 * (kPfKeys * 16) + q.b * kBlock * 16 + k_lane;
-      *reinterpret_cast<bf16x8*>(stage + off) = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
-      *reinterpret_cast<bf16x8*>(stage + off + kPfKeys * 16) = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
-    } else {
-      const int off = D * kPfKeys * 2 + (q.e0 >> 4) * 2048 + 2 * q.b * 256 + v_lane;
-      *reinterpret_cast<f16x8*>(stage + off) = fp8x8_to_f16x8(u32x2{w[0], w[1]});
-      *reinterpret_cast<f16x8*>(stage + off + 256) = fp8x8_to_f16x8(u32x2{w[2], w[3]});
-    }
-  }
-
-  // `valid` = keys of the tile that exist; V beyond them is stored as zero.
-  __device__ void store(const u32x4* regs, uint8_t* stage, int valid) const {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const Piece q = piece(i);
-      u32x4 w = regs[i];
-      if (!kWide) {
-        if (!q.v) {
-          // e = chunk * 16 + token
-          const int off = (q.e0 >> 4) * (kPfKeys * 16) + q.b * kBlock * 16;
-          *reinterpret_cast<u32x4*>(stage + off + k_lane) = w;
-        } else {
-          // e = dim * 2 + half; v_off(dim, 2 b + half)
-          if (valid < kPfKeys) {  // last tile of the range only
-            const int key0 = q.b * kBlock + v_key;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int k = key0 + 2 * j;
-              const uint32_t m = (k < valid ? 0xFFFFu : 0u) | (k + 1 < valid ? 0xFFFF0000u : 0u);
-              w[j] &= m;
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = bf16x2_to_f16x2(w[j]);
-          const int off = D * kPfKeys * 2 + ((q.e0 >> 1) >> 4) * 2048 + 2 * q.b * 256;
-          *reinterpret_cast<u32x4*>(stage + off + v_lane) = w;
-        }
-      } else if (!q.v) {
-        // e = chunk8 * 16 + token: bf16 chunks 2 chunk8, 2 chunk8 + 1
-        const int off = (q.e0 >> 4) * 2 * (kPfKeys * 16) + q.b * kBlock * 16 + k_lane;
-        *reinterpret_cast<bf16x8*>(stage + off) = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
-        *reinterpret_cast<bf16x8*>(stage + off + kPfKeys * 16) = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
-      } else {
-        // e = dim: tokens 0..7 -> chunk 2 b, 8..15 -> chunk 2 b + 1
-        f16x8 v0 = fp8x8_to_f16x8(u32x2{w[0], w[1]});
-        f16x8 v1 = fp8x8_to_f16x8(u32x2{w[2], w[3]});
-        const int key0 = q.b * kBlock;
-        if (valid < kPfKeys && key0 + kBlock > valid) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            if (key0 + j >= valid) v0[j] = static_cast<_Float16>(0.0f);
-            if (key0 + 8 + j >= valid) v1[j] = static_cast<_Float16>(0.0f);
-          }
-        }
-        const int off = D * kPfKeys * 2 + (q.e0 >> 4) * 2048 + 2 * q.b * 256 + v_lane;
-        *reinterpret_cast<f16x8*>(stage + off) = v0;
-        *reinterpret_cast<f16x8*>(stage + off + 256) = v1;  // chunk 2 b + 1
-      }
-    }
-  }
-};
-
 // grid.x = H_kv * n_head_groups * n_split * n_pos_tiles (KV head fastest, so
 // the groups sharing a KV head land on the same XCD's L2); grid.y = slices.
 template <typename CacheT, int D>
@@ -291,392 +69,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
     const typename CacheT::raw* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     int32_t max_blocks, int32_t num_blocks, int32_t H_q, PfGeom geo, float score_scale,
     float v_scale, float* __restrict__ ws_ml, float* __restrict__ ws_o, int32_t ws_rows) {
-  constexpr int NKS = D / 16;  // 16-dim MFMA steps of Q K^T
-  constexpr int NDT = D / 32;  // 32-dim tiles of O^T
-  using Loader = TileLoader<CacheT, D>;
-  constexpr int NLD = Loader::NLD;
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * stage_bytes<D>()];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int g = lane >> 5;   // which half of the wave (MFMA k-group)
-  const int col = lane & 31; // the lane's query within the wave
-
-  int x = blockIdx.x;
-  const int kvh = x % geo.H_kv;
-  x /= geo.H_kv;
-  const int hg = x % geo.n_head_groups;
-  x /= geo.n_head_groups;
-  const int split = x % geo.n_split;
-  const int pt = geo.n_pos_tiles - 1 - x / geo.n_split;  // longest rows first
-  const int c = blockIdx.y;
-
-  const int32_t q0 = cu_q_lens[c];
-  const int32_t qlen = cu_q_lens[c + 1] - q0;
-  const int32_t P0 = start_pos[c];
-  const int pos_per_group = kPfRows * geo.psub;
-  const int grp0 = pt * pos_per_group;
-  if (grp0 >= qlen) return;
-  const int grp_end = min(grp0 + pos_per_group, qlen);
-  const int32_t kv_end = P0 + grp_end;  // keys this group needs: [0, kv_end)
-
-  const int n_tiles = (kv_end + kPfKeys - 1) / kPfKeys;
-  const int per = (n_tiles + geo.n_split - 1) / geo.n_split;
-  const int t0 = split * per;
-  const int t1 = min(n_tiles, t0 + per);
-
-  // this wave's query head and positions
-  const int hi = wave % geo.hpw, ps = wave / geo.hpw;
-  const int hq_in_group = hg * kPfWaves + hi;
-  const bool active = ps < geo.psub && hq_in_group < geo.G;
-  const int head = kvh * geo.G + hq_in_group;
-  const int w0 = grp0 + ps * kPfRows;  // first position (relative to the slice)
-  const bool wave_live = active && w0 < qlen;
-  const int my_rel = min(w0 + col, qlen - 1);
-  const int32_t qpos = P0 + my_rel;   // absolute position (clamped for rows past the end)
-  const bool row_ok = wave_live && (w0 + col) < qlen;
-  const int32_t wave_last_pos = P0 + min(w0 + kPfRows, qlen) - 1;
-  const int32_t wave_first_pos = P0 + w0;
-
-  // Q fragment: query `col`, dims 16 ks + 8 g .. + 7
-  bf16x8 qf[NKS];
-  {
-    const uint16_t* qrow = q + (static_cast<int64_t>(q0 + my_rel) * H_q + head) * D + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 w = u32x4{0u, 0u, 0u, 0u};
-      if (row_ok) w = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
-      qf[ks] = __builtin_bit_cast(bf16x8, w);
-    }
-    // Settle the Q loads here: otherwise the counter bookkeeping at the loop
-    // head cannot tell them from the K/V prefetch and waits for all loads
-    // before every tile's first MFMA.
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qf[ks]));
-  }
-
-  f32x16 o[NDT];
-#pragma unroll
-  for (int n = 0; n < NDT; ++n)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) o[n][j] = 0.f;
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
-
-  const int32_t* table = block_tables + static_cast<int64_t>(c) * max_blocks;
-  const int32_t n_blk = min((kv_end + kBlock - 1) / kBlock, max_blocks);
-  // A tile's block ids are fetched by a vector load one iteration before
-  // its K/V loads are issued: lanes 0..3 take the tile's four entries
-  // (entries past the context repeat the last one), clamped into the pool.
-  auto fetch_ids = [&](int t) -> int32_t {
-    return table[min(t * 4 + (lane & 3), n_blk - 1)];
-  };
-
-  const Loader ld(wave, lane);
-  const int v_lane = v_off(col, g);
-
-  // Software pipeline inside each wave.  Iteration t enters with the fp16
-  // weights P(t-1) and the scores S(t).  One straight run of 32 MFMAs then
-  // computes S(t+1) = K(t+1) Q^T and O^T += V(t-1)^T P(t-1)^T; none of them
-  // waits for the vector work of the same iteration, which in between turns
-  // S(t) into P(t) against the current softmax reference.  Only when P(t)
-  // would leave fp16 (checked on its row sums after the run, rare) is the
-  // reference raised and P(t) formed again.  K/V tiles rotate through four
-  // LDS stages: tile t is stored during iteration t-2, read as K in
-  // iteration t-1 and as V in iteration t+1.
-  auto stage = [&](int t) { return smem + ((t - t0) & 3) * stage_bytes<D>(); };
-  constexpr int NQK = 2 * NKS;       // S MFMAs per tile
-  constexpr int NPV = 4 * NDT;       // O MFMAs per tile
-  constexpr int NM = NQK + NPV;
-  constexpr int EPS = 32 / NQK;      // exponentials per S slot
-  static_assert(EPS * NQK == 32, "32 scores per lane and tile");
-  constexpr int PD = 2;              // operand reads issued this many MFMAs ahead
-  constexpr int kLd0 = NLD;          // first slot with a tile load
-  constexpr int kLdEvery = 4;        // one tile load every this many MFMA slots
-  static_assert(kLd0 + kLdEvery * NLD < NM, "the tile loads fit the slots");
-
-  u32x4 regs[NLD];
-  // block ids of the next tile to load (ids_a) and of the one after (ids_b):
-  // fetched two loads ahead, so their latency never delays a tile load
-  int32_t ids_a = fetch_ids(t0);
-  int32_t ids_b = fetch_ids(min(t0 + 1, t1 - 1));
-  auto load_tile = [&](int t) {  // tiles past the range reload the last one
-    const int tc = min(t, t1 - 1);
-    ld.load(regs, k_cache, v_cache, ids_a, kvh, geo.H_kv, num_blocks);
-    ids_a = ids_b;
-    ids_b = fetch_ids(min(tc + 2, t1 - 1));
-  };
-  auto store_tile = [&](int t) {
-    ld.store(regs, stage(t), kv_end - min(t, t1 - 1) * kPfKeys);
-  };
-  auto zero_v_tail = [&](uint8_t* v_lds, int valid) {
-    for (int idx = tid; idx < D * 8; idx += kPfThreads) {
-      const int d = idx >> 3, c = idx & 7;
-      if (8 * c + 7 >= valid) {
-        f16x8* p = reinterpret_cast<f16x8*>(v_lds + v_off(d, c));
-        f16x8 v = *p;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (8 * c + j >= valid) v[j] = static_cast<_Float16>(0.0f);
-        *p = v;
-      }
-    }
-  };
-  auto mask_scores = [&](f32x16* s, int t) {
-    const int lim = qpos - t * kPfKeys - 8 * g;  // largest admissible key offset
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int off = 32 * h + 16 * (j >> 3) + (j & 7);
-        s[h][j] = off <= lim ? s[h][j] : -__builtin_inff();
-      }
-  };
-  // the score scale is positive, so maxima are taken on raw scores
-  // S^T of the 64 keys of a stage
-  auto qk_stage = [&](const uint8_t* k_lds, f32x16* s) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s[h][j] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            k_lds + (2 * ks + g) * (kPfKeys * 16) + (32 * h + col) * 16);
-        s[h] = mfma32x32x16(a, qf[ks], s[h]);
-      }
-    }
-  };
-  auto half_max = [&](const f32x16& s) {
-    // scores are never NaN: plain three-way maxima, no quieting
-    float m;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(s[0]), "v"(s[1]), "v"(s[2]));
-#pragma unroll
-    for (int j = 3; j < 15; j += 2)
-      asm("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(m), "v"(s[j]), "v"(s[j + 1]));
-    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(m), "v"(s[15]));
-    return m;
-  };
-  // The softmax reference m_run (log2 domain) starts at the maximum of the
-  // first tile and is raised only when a tile's weights would leave fp16:
-  // a lane whose 32 weights of a tile sum beyond kPfSafe (or overflow).
-  // Any reference gives the same normalised result; this one never lies
-  // above the running maximum, so the largest weight seen so far is >= 1.
-  float mu = 0.f;                    // reference the exponentials use
-  // lane maximum of raw scores -> the query's maximum, scaled
-  auto query_max = [&](const f32x16* s) {
-    const float mx = fmaxf(half_max(s[0]), half_max(s[1]));
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                     false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * score_scale;
-  };
-  // raise the reference to m_new (>= m_run), rescaling l and O^T
-  auto raise_to = [&](float m_new) {
-    const float alpha =
-        m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int n = 0; n < NDT; ++n)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) o[n][j] *= alpha;
-    m_run = m_new;
-    mu = m_run == -__builtin_inff() ? 0.f : m_run;
-  };
-  // fp16 weights of S (32 per lane) against mu, and their sum
-  auto weights = [&](const f32x16* s, f16x8* p) {
-    const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; e += 2) {
-      const int u = e >> 3, i8 = e & 7;
-      const f16x2 h2 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(
-                            __builtin_fmaf(s[u >> 1][8 * (u & 1) + i8], score_scale, -mu))),
-                        static_cast<_Float16>(__builtin_amdgcn_exp2f(
-                            __builtin_fmaf(s[u >> 1][8 * (u & 1) + i8 + 1], score_scale, -mu)))};
-      p[u][i8] = h2[0];
-      p[u][i8 + 1] = h2[1];
-      sum = __builtin_amdgcn_fdot2(h2, ones, sum, false);
-    }
-    return sum;
-  };
-
-  // One iteration.  sc: S(t) in, sn: S(t+1) out, pp: P(t-1) in, pn: P(t) out.
-  auto body = [&](auto masked_next, int t, f32x16* sc, f32x16* sn, const f16x8* pp, f16x8* pn) {
-    // Tile t+2 (loaded during the last iteration) goes into its stage in the
-    // first slots; the global loads of tile t+3 follow, spread over the
-    // slots so that the waves do not queue for the address unit at once,
-    // and have a whole iteration to arrive.
-    const int t_ld = min(t + 3, t1 - 1);
-    uint8_t* st_lds = stage(t + 2);
-    const uint8_t* k_lds = stage(t + 1);
-    const uint8_t* v_lds = stage(t - 1) + D * kPfKeys * 2;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sn[h][j] = 0.f;
-    // MFMA slot i < NQK: S step i (h = i & 1, ks = i >> 1); slot NQK + j: O
-    // step j (u = j / NDT, n = j % NDT)
-    auto operand = [&](int i) -> u32x4 {
-      if (i < NQK)
-        return *reinterpret_cast<const u32x4*>(k_lds + (2 * (i >> 1) + g) * (kPfKeys * 16) +
-                                                (32 * (i & 1) + col) * 16);
-      const int j = i - NQK;
-      return *reinterpret_cast<const u32x4*>(v_lds + v_lane + (j % NDT) * 4096 + (j / NDT) * 512);
-    };
-    u32x4 opnd[PD + 1];
-#pragma unroll
-    for (int i = 0; i < PD; ++i) opnd[i] = operand(i);
-    const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-    float l_tile = 0.f;
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      if (i + PD < NM) opnd[(i + PD) % (PD + 1)] = operand(i + PD);
-      if (i < NLD) ld.store1(regs[i], i, st_lds);
-      if (i >= kLd0 && (i - kLd0) % kLdEvery == 0 && (i - kLd0) / kLdEvery < NLD)
-        ld.load1(regs[(i - kLd0) / kLdEvery], (i - kLd0) / kLdEvery, k_cache, v_cache, ids_a,
-                 kvh, geo.H_kv, num_blocks);
-      if (i == kLd0 + kLdEvery * NLD) {
-        ids_a = ids_b;
-        ids_b = fetch_ids(min(t_ld + 2, t1 - 1));
-      }
-      if (i < NQK) {
-        sn[i & 1] = mfma32x32x16(__builtin_bit_cast(bf16x8, opnd[i % (PD + 1)]), qf[i >> 1],
-                                 sn[i & 1]);
-        // weights of scores e = EPS i .. (e = 8 u + i8: key 16 u + i8 of
-        // the lane's half), in pairs
-#pragma unroll
-        for (int q2 = 0; q2 < EPS; q2 += 2) {
-          const int e = EPS * i + q2;
-          const int u = e >> 3, i8 = e & 7;
-          const float w0 = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(sc[u >> 1][8 * (u & 1) + i8], score_scale, -mu));
-          const float w1 = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(sc[u >> 1][8 * (u & 1) + i8 + 1], score_scale, -mu));
-          f16x2 h2 = {static_cast<_Float16>(w0), static_cast<_Float16>(w1)};
-          // computed here, between the MFMAs, not where it is next used
-          asm volatile("" : "+v"(h2));
-          pn[u][i8] = h2[0];
-          pn[u][i8 + 1] = h2[1];
-          l_tile = __builtin_amdgcn_fdot2(h2, ones, l_tile, false);
-          asm volatile("" : "+v"(l_tile));
-        }
-      } else {
-        const int j = i - NQK;
-        o[j % NDT] = mfma32x32x16(__builtin_bit_cast(f16x8, opnd[i % (PD + 1)]), pp[j / NDT],
-                                  o[j % NDT]);
-        // S(t+1) is complete two slots after its last MFMA: mask it where
-        // it reaches the diagonal
-        if constexpr (decltype(masked_next)::value)
-          if (j == 1) mask_scores(sn, t + 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // P(t) left fp16 (rare: S(t) far above the reference): recompute S(t)
-    // from tile t's K, still in its stage, raise the reference to its
-    // maximum (O^T holds P(t-1) V(t-1) by now) and form P(t) again
-    if (__builtin_amdgcn_ballot_w64(!(l_tile <= kPfSafe)) != 0) {
-      qk_stage(stage(t), sc);
-      if (t * kPfKeys + kPfKeys - 1 > wave_first_pos) mask_scores(sc, t);
-      raise_to(fmaxf(m_run, query_max(sc)));
-      l_tile = weights(sc, pn);
-    }
-    l_run += l_tile;
-    // V of keys past the context must be zero, not stale cache bits
-    const int valid_st = kv_end - min(t + 2, t1 - 1) * kPfKeys;
-    if (valid_st < kPfKeys) zero_v_tail(st_lds + D * kPfKeys * 2, valid_st);
-    __syncthreads();
-  };
-
-  if (t0 < t1) {
-    load_tile(t0);
-    store_tile(t0);
-    load_tile(t0 + 1);
-    store_tile(t0 + 1);
-    load_tile(t0 + 2);  // stored by iteration t0
-    {
-      // iteration t0 multiplies zero weights by the V half of the stage
-      // before it: clear that half so that no stale bits become NaN
-      uint8_t* vz = stage(t0 - 1) + D * kPfKeys * 2;
-      for (int i = tid; i < D * kPfKeys * 2 / 16; i += kPfThreads)
-        *reinterpret_cast<u32x4*>(vz + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
-    f32x16 sA[2], sB[2];
-    f16x8 pA[4], pB[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pA[u][i] = static_cast<_Float16>(0.0f);
-    // S(t0) and the first reference, its maximum
-    qk_stage(stage(t0), sA);
-    if (t0 * kPfKeys + kPfKeys - 1 > wave_first_pos) mask_scores(sA, t0);
-    m_run = query_max(sA);
-    mu = m_run == -__builtin_inff() ? 0.f : m_run;
-    // iteration t masks S(t+1) when tile t+1 reaches past the wave's first
-    // position, i.e. from tile t_mask on
-    const int t_mask = (wave_first_pos + 1) / kPfKeys;
-    int t = t0;
-    for (; t + 2 < min(t_mask, t1); t += 2) {
-      body(std::false_type{}, t, sA, sB, pA, pB);
-      body(std::false_type{}, t + 1, sB, sA, pB, pA);
-    }
-    for (; t + 1 < t1; t += 2) {
-      body(std::true_type{}, t, sA, sB, pA, pB);
-      body(std::true_type{}, t + 1, sB, sA, pB, pA);
-    }
-    const f16x8* p_last = pA;
-    int t_last = t - 1;
-    if (t < t1) {
-      body(std::true_type{}, t, sA, sB, pA, pB);
-      p_last = pB;
-      t_last = t;
-    }
-    // O^T += V(last)^T P(last)^T; every owed rescale is already applied
-    const uint8_t* v_lds = stage(t_last) + D * kPfKeys * 2;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int n = 0; n < NDT; ++n) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(v_lds + v_lane + n * 4096 + u * 512);
-        o[n] = mfma32x32x16(a, p_last[u], o[n]);
-      }
-  }
-
-  if (!row_ok) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  const int64_t row = q0 + w0 + col;
-  if (geo.n_split == 1) {
-    const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
-    uint16_t* orow = out + (row * H_q + head) * D;
-#pragma unroll
-    for (int n = 0; n < NDT; ++n)
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const int d = 32 * n + 8 * jq + 4 * g;
-        u32x2 w;
-        w[0] = static_cast<uint32_t>(f32_to_bf16(o[n][4 * jq] * inv)) |
-               (static_cast<uint32_t>(f32_to_bf16(o[n][4 * jq + 1] * inv)) << 16);
-        w[1] = static_cast<uint32_t>(f32_to_bf16(o[n][4 * jq + 2] * inv)) |
-               (static_cast<uint32_t>(f32_to_bf16(o[n][4 * jq + 3] * inv)) << 16);
-        *reinterpret_cast<u32x2*>(orow + d) = w;
-      }
-  } else if (row < ws_rows) {
-    const int64_t slot = (static_cast<int64_t>(split) * ws_rows + row) * H_q + head;
-    float* po = ws_o + slot * D;
-#pragma unroll
-    for (int n = 0; n < NDT; ++n)
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const int d = 32 * n + 8 * jq + 4 * g;
-        *reinterpret_cast<f32x4*>(po + d) =
-            f32x4{o[n][4 * jq], o[n][4 * jq + 1], o[n][4 * jq + 2], o[n][4 * jq + 3]};
-      }
-    if (g == 0) {
-      ws_ml[2 * slot] = m_run;
-      ws_ml[2 * slot + 1] = l_tot;
-    }
-  }
+  prefill_block<CacheT, D, false>(smem, blockIdx.x, blockIdx.y, out, q, cu_q_lens, start_pos,
+                                  k_cache, v_cache, block_tables, max_blocks, num_blocks, H_q, geo,
+                                  score_scale, v_scale, ws_ml, ws_o, ws_rows, nullptr);
 }
 
 // Merge the key-range partials of each (row, head): D/4 threads per pair,
@@ -693,29 +89,10 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
       min(static_cast<int64_t>(cu_q_lens[n_chunks]), static_cast<int64_t>(ws_rows)) * H_q;
   if (pair >= total) return;
   const int64_t stride = static_cast<int64_t>(ws_rows) * H_q;
-  float M = -__builtin_inff();
-  for (int j = 0; j < n_split; ++j) {
-    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * (j * stride + pair));
-    if (ml.y > 0.f) M = fmaxf(M, ml.x);
-  }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  for (int j = 0; j < n_split; ++j) {
-    const int64_t slot = j * stride + pair;
-    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * slot);
-    if (!(ml.y > 0.f)) continue;
-    const float w = __builtin_amdgcn_exp2f(ml.x - M);
-    L += w * ml.y;
-    const f32x4 po = *reinterpret_cast<const f32x4*>(ws_o + slot * D + 4 * sub);
-    acc += w * po;
-  }
-  const float inv = L > 0.f ? v_scale / L : 0.f;
-  u32x2 w2;
-  w2[0] = static_cast<uint32_t>(f32_to_bf16(acc[0] * inv)) |
-          (static_cast<uint32_t>(f32_to_bf16(acc[1] * inv)) << 16);
-  w2[1] = static_cast<uint32_t>(f32_to_bf16(acc[2] * inv)) |
-          (static_cast<uint32_t>(f32_to_bf16(acc[3] * inv)) << 16);
-  *reinterpret_cast<u32x2*>(out + pair * D + 4 * sub) = w2;
+  const float M = pf_merge_max(ws_ml, pair, stride, n_split);
+  const float inv = pf_merge_inv(ws_ml, pair, stride, n_split, M, v_scale);
+  const f32x4 acc = pf_merge_dims4<D>(ws_ml, ws_o, pair, stride, n_split, M, 4 * sub);
+  *reinterpret_cast<u32x2*>(out + pair * D + 4 * sub) = pack_bf16x4(acc, inv);
 }
 
 template <typename CacheT, int D>
@@ -777,9 +154,7 @@ extern "C" size_t pa_prefill_workspace_bytes(int32_t n_chunks, int32_t max_q_len
   if (n_chunks <= 0 || max_q_len <= 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv != 0 ||
       (D != 64 && D != 128))
     return 0;
-  const PfGeom geo = pf_geometry(n_chunks, max_q_len, H_q, H_kv, max_context_len);
-  if (geo.n_split <= 1) return 0;
-  return static_cast<size_t>(geo.n_split) * n_chunks * max_q_len * H_q * (D + 2) * sizeof(float);
+  return pf_partials_bound(n_chunks, max_q_len, H_q, H_kv, D, max_context_len);
 }
 
 extern "C" pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, const void* q,
