@@ -305,6 +305,63 @@ pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, const void*
                            float k_scale, float v_scale, void* ws, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------
+ * Mixed-batch attention in one launch -- LESSON "What the scheduler looks
+ * like": an iteration runs its decode tokens and its chunked-prefill slices
+ * together as one call on the GPU.  Sequence i of the batch has the queries
+ * q[cu_q_lens[i] .. cu_q_lens[i+1]) at positions seq_lens[i] - q_len(i) ..
+ * seq_lens[i] - 1; query j sees positions 0 .. its own, inclusive ("Chunked
+ * prefill"), through row i of block_tables (ARTICLE 2.3).  The K/V of every
+ * such position must already be in the cache.
+ *
+ * The first n_decode sequences are decode rows: one query each, at rows
+ * 0 .. n_decode-1 of q and out (cu_q_lens[i] == i for i <= n_decode).  The
+ * next n_prefill sequences are prefill slices of 0 .. max_q_len queries.
+ * The results are those of pa_decode over the decode rows (context_lens =
+ * seq_lens) and pa_prefill_chunk over the slices (start_pos = seq_lens -
+ * q_len), and equal them bit for bit when both take the same key-range
+ * splits; one persistent kernel computes both, merging split ranges inside
+ * the launch.
+ *
+ * out, q [device, total_q * H_q * D, bf16], layout [total_q][H_q][D]
+ * cu_q_lens [device, n_decode + n_prefill + 1 int32], nondecreasing
+ * seq_lens [device, n_decode + n_prefill int32]: context length of each
+ *   sequence after this iteration's tokens, >= its q_len and >= 1 for a
+ *   decode row
+ * block_tables [device, (n_decode + n_prefill) * max_blocks int32]
+ * max_q_len: host-side bound of the slices' q_len; max_decode_len and
+ *   max_prefill_len: bounds of seq_lens over the decode rows and the slices
+ *   (sizing only; no device-to-host read).
+ * Types: bf16 q and out with a bf16 or fp8 e4m3fn cache, D 64 or 128,
+ *   bs 16, at most 16 query heads per KV head, n_decode <= 4096; other
+ *   problems return PA_ERR_INVALID (pa_decode and pa_prefill_chunk take
+ *   them).
+ * counters [device, n_counters int32]: at least
+ *   pa_attend_varlen_counters(...) work counters, zero-filled once before
+ *   their first use; every call leaves them zero.  An array sized for some
+ *   maxima serves every call within them.
+ * ws [device, ws_bytes]: partial results of split key ranges, at least
+ *   pa_attend_varlen_workspace_bytes(...) bytes (may be 0 and ws NULL when
+ *   that is 0); a workspace sized for some maxima serves every call within
+ *   them.  Calls that overlap in time must share neither counters nor ws.
+ * ---------------------------------------------------------------------- */
+int64_t pa_attend_varlen_counters(int32_t n_decode, int32_t n_prefill, int32_t H_q,
+                                  int32_t H_kv, int32_t max_q_len);
+
+size_t pa_attend_varlen_workspace_bytes(int32_t n_decode, int32_t n_prefill, int32_t H_q,
+                                        int32_t H_kv, int32_t D, int32_t max_q_len,
+                                        int32_t max_decode_len, int32_t max_prefill_len);
+
+pa_status pa_attend_varlen(void* stream, void* out, pa_dtype out_dt, const void* q,
+                           pa_dtype q_dt, const int32_t* cu_q_lens, const int32_t* seq_lens,
+                           int32_t n_decode, int32_t n_prefill, const void* k_cache,
+                           const void* v_cache, pa_dtype cache_dt, const int32_t* block_tables,
+                           int32_t max_blocks, int32_t num_blocks, int32_t H_q, int32_t H_kv,
+                           int32_t D, int32_t bs, int32_t max_q_len, int32_t max_decode_len,
+                           int32_t max_prefill_len, float sm_scale, float k_scale,
+                           float v_scale, int32_t* counters, int64_t n_counters, void* ws,
+                           size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
  * Iteration-level scheduler over a pool (host).
  *
  * LESSON "Continuous batching at the iteration level", "What the scheduler

@@ -21,6 +21,7 @@ enum KernelId {
   kGeneric,
   kStage,
   kStageCacheWrite,
+  kVarlen,
   kKernelCount
 };
 

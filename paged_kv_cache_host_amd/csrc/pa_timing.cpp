@@ -44,7 +44,7 @@ Track g_tracks[kKernelCount];
 
 const char* kNames[kKernelCount] = {"cache_write",   "decode",  "decode_merge",
                                     "prefill",       "prefill_merge", "generic",
-                                    "stage",         "stage_cache_write"};
+                                    "stage",         "stage_cache_write", "varlen"};
 
 }  // namespace
 

@@ -118,6 +118,29 @@ class PagedKV:
                                      self.num_blocks, self.h_kv, max_q_len, max_context_len,
                                      sm_scale, self.k_scale, self.v_scale, ws))
 
+    def attend_varlen(self, out, q, cu_q_lens, seq_lens, n_decode: int, tables, max_q_len: int,
+                      max_decode_len: int, max_prefill_len: int, sm_scale: float, bufs,
+                      stream=None):
+        """Decode rows and prefill slices in one launch; bufs = varlen_buffers(...)."""
+        counters, ws = bufs
+        pa.check(pa.pa_attend_varlen(stream, out, q, cu_q_lens, seq_lens, n_decode, self.k,
+                                     self.v, tables, self.num_blocks, self.h_kv, max_q_len,
+                                     max_decode_len, max_prefill_len, sm_scale, self.k_scale,
+                                     self.v_scale, counters, ws))
+
+
+def varlen_buffers(n_decode, n_prefill, h_q, h_kv, d, max_q_len, max_decode_len,
+                   max_prefill_len, device="cuda"):
+    """(counters, workspace) for pa_attend_varlen calls within these sizes:
+    the counters zero-filled (every call leaves them zero), the workspace
+    uninitialised (None when no call within the sizes needs one)."""
+    nc = pa.pa_attend_varlen_counters(n_decode, n_prefill, h_q, h_kv, max_q_len)
+    nb = pa.pa_attend_varlen_workspace_bytes(n_decode, n_prefill, h_q, h_kv, d, max_q_len,
+                                             max_decode_len, max_prefill_len)
+    counters = torch.zeros(max(nc, 2), dtype=torch.int32, device=device)
+    ws = torch.empty(nb, dtype=torch.uint8, device=device) if nb > 0 else None
+    return counters, ws
+
 
 def decode_workspace(S, h_q, h_kv, d, max_context_len, device="cuda") -> torch.Tensor | None:
     """Zero-filled decode workspace (its work counters must start at zero;
