@@ -708,14 +708,16 @@ def mixed_leg(args, dev):
     512-token slices; every iteration also decodes one token for each of 127
     sequences.  One iteration = host append/pack + one pa_cache_write of the
     639 new tokens + pa_prefill_chunk of the slice + pa_decode of the 127
-    sequences.  Reported as tokens/s per layer over the 64 iterations, plus
-    the prefill kernel's bf16 MFMA throughput."""
+    sequences (on one stream, or the slice on a second stream), or, in the
+    fused form, one pa_attend_varlen for both.  Reported as tokens/s per
+    layer over the 64 iterations for each form, plus the prefill kernel's
+    bf16 MFMA throughput."""
     import torch
 
     import workloads
     from paged_kv_cache_host_amd import _pa as pa
     from paged_kv_cache_host_amd.engine import (PagedKV, decode_workspace, prefill_workspace,
-                                                sm_scale_for)
+                                                sm_scale_for, varlen_buffers)
 
     P, C = 32768, 512
     iters = P // C
@@ -743,19 +745,21 @@ def mixed_leg(args, dev):
                                   for c in range(iters))), dtype=torch.uint8, device=dev)
     cu = torch.tensor([0, C], dtype=torch.int32, device=dev)
 
-    # a ring of NBUF pinned buffers [slots NT | start 1 | lens S | tables S*MB],
+    # a ring of NBUF pinned buffers [slots NT | lens S | prompt 1 | tables S*MB],
     # each with a device twin, staged once per iteration on the compute
-    # stream; one event per GROUP iterations frees them for refilling
+    # stream; one event per GROUP iterations frees them for refilling.  The
+    # prompt word is the slice's start for pa_prefill_chunk and its context
+    # length for pa_attend_varlen, whose seq_lens are then [lens | prompt].
     NBUF, GROUP = 8, 4
-    n_meta = NT + 1 + S + S * MB
+    n_meta = NT + S + 1 + S * MB
     host_buf = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True) for _ in range(NBUF)]
     dev_buf = [torch.empty(n_meta, dtype=torch.int32, device=dev) for _ in range(NBUF)]
     views = []
     for X in range(NBUF):
         h, d_ = host_buf[X].numpy(), dev_buf[X]
-        o1, o2, o3 = NT, NT + 1, NT + 1 + S
-        views.append((h[:NT], h[o1:o2], h[o2:o3], h[o3:].reshape(S, MB),
-                      d_[:NT], d_[o1:o2], d_[o2:o3], d_[o3:].view(S, MB)))
+        o1, o2, o3 = NT, NT + S, NT + S + 1
+        views.append((h[:NT], h[o2:o3], h[o1:o2], h[o3:].reshape(S, MB),
+                      d_[:NT], d_[o2:o3], d_[o1:o2], d_[o3:].view(S, MB), d_[o1:o3]))
     compute = torch.cuda.Stream(device=dev)
     # In the two-stream pass the prefill slice runs on a stream of its own
     # after the staging launch, beside the decode (the next iteration's
@@ -767,7 +771,20 @@ def mixed_leg(args, dev):
     ev_group = [torch.cuda.Event() for _ in range(2)]
     ev_group_side = [torch.cuda.Event() for _ in range(2)]
 
-    def run_pass(timed: bool, n_iters: int, two_streams: bool):
+    # the fused form: one pa_attend_varlen per iteration over [127 decode rows;
+    # the 512-row slice] (queries of both, the same values as the separate
+    # forms use, laid out together once here)
+    q_mix = torch.empty((iters, NT, H_Q, D), dtype=torch.bfloat16, device=dev)
+    for c in range(iters):
+        q_mix[c, :S] = q_dec[c % R]
+        q_mix[c, S:] = q_prompt[c * C:(c + 1) * C]
+    cu_mix = torch.tensor(list(range(S + 1)) + [S + C], dtype=torch.int32, device=dev)
+    # two sets (output, counters + workspace): in the two-stream fused form
+    # consecutive iterations run on alternate streams and may overlap
+    out_mix = [torch.empty((NT, H_Q, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    bufs_mix = [varlen_buffers(S, 1, H_Q, H_KV, D, C, max_dec, P, dev) for _ in range(2)]
+
+    def run_pass(timed: bool, n_iters: int, two_streams: bool, fused: bool = False):
         side = side_stream if two_streams else compute
         # fresh pool: decode contexts of L0-1 tokens cached, prompt blocks
         # allocated at admission (its K/V are written slice by slice)
@@ -786,12 +803,12 @@ def mixed_leg(args, dev):
         for e in ev_group_side:
             e.record(side)
         if timed:
-            pa.check(pa.pa_timing_enable(["prefill", "prefill_merge"]))
+            pa.check(pa.pa_timing_enable(["varlen"] if fused else ["prefill", "prefill_merge"]))
         _settle()
         t0 = time.perf_counter()
         for c in range(n_iters):
             X = c % NBUF
-            h_sl, h_st, h_len, h_tab, d_sl, d_st, d_len, d_tab = views[X]
+            h_sl, h_st, h_len, h_tab, d_sl, d_st, d_len, d_tab, d_seqlens = views[X]
             if c % GROUP == 0:
                 ev_group[(c // GROUP) % 2].synchronize()
                 ev_group_side[(c // GROUP) % 2].synchronize()
@@ -800,11 +817,24 @@ def mixed_leg(args, dev):
             pa.check(st)
             st, _, _ = pa.pa_pack_batch(kv.pool, dec_seqs, MB, h_tab, h_len)
             pa.check(st)
-            h_st[0] = c * C
+            h_st[0] = (c + 1) * C if fused else c * C
             r = c % R
-            pa.check(pa.pa_stage_cache_write(compute, dev_buf[X], host_buf[X], 4 * n_meta, 0, NT,
+            # fused, two streams: iteration c stages and attends on stream c % 2
+            # (iteration c+1 writes only its new tokens' slots, which iteration
+            # c does not read, so the two may overlap)
+            st_c = side if (fused and c % 2) else compute
+            pa.check(pa.pa_stage_cache_write(st_c, dev_buf[X], host_buf[X], 4 * n_meta, 0, NT,
                                              k_ring[r], v_ring[r], kv.k, kv.v, num_blocks, H_KV,
                                              D, BLOCK))
+            if fused:
+                b2 = bufs_mix[c % 2]
+                pa.check(pa.pa_attend_varlen(st_c, out_mix[c % 2], q_mix[c], cu_mix, d_seqlens, S,
+                                             kv.k, kv.v, d_tab, ptab_dev, num_blocks, H_KV, C,
+                                             max_dec, (c + 1) * C, sm, 1.0, 1.0, b2[0], b2[1]))
+                if c % GROUP == GROUP - 1:
+                    ev_group[(c // GROUP) % 2].record(compute)
+                    ev_group_side[(c // GROUP) % 2].record(side)
+                continue
             if side is not compute:
                 ev_staged[c % 2].record(compute)
                 side.wait_event(ev_staged[c % 2])
@@ -820,7 +850,7 @@ def mixed_leg(args, dev):
         wall = time.perf_counter() - t0
         tm = None
         if timed:
-            tm = _timings(pa, ("prefill", "prefill_merge"))
+            tm = _timings(pa, ("varlen",) if fused else ("prefill", "prefill_merge"))
             pa.check(pa.pa_timing_enable(False))
         kv.close()
         return wall, tm
@@ -833,6 +863,12 @@ def mixed_leg(args, dev):
     wall1, tm = run_pass(True, iters, False)
     run_pass(False, mixed_warmup_slices(args.warmup), True)
     wall, _ = run_pass(False, iters, True)
+    pa.check(pa.pa_timing_enable(["varlen"]))
+    run_pass(False, mixed_warmup_slices(args.warmup), False, fused=True)
+    pa.check(pa.pa_timing_enable(False))
+    wall_f, tm_f = run_pass(True, iters, False, fused=True)
+    run_pass(False, mixed_warmup_slices(args.warmup), True, fused=True)
+    wall_f2, _ = run_pass(False, iters, True, fused=True)
     pairs = sum(C * (c * C) + C * (C + 1) // 2 for c in range(iters))
     flops = 4 * D * H_Q * pairs
     n_pf, mean_pf, tot_pf = tm["prefill"]
@@ -848,6 +884,13 @@ def mixed_leg(args, dev):
         "ms_per_iteration": wall / iters * 1e3,
         "streams": "prefill beside decode (two streams)",
         "one_stream": {"tokens_per_s": iters * NT / wall1, "ms_per_iteration": wall1 / iters * 1e3},
+        "fused": {"tokens_per_s": iters * NT / wall_f, "ms_per_iteration": wall_f / iters * 1e3,
+                  "launch": "pa_attend_varlen: decode rows and the slice in one kernel",
+                  "kernel_us_mean": round(tm_f["varlen"][1], 1),
+                  "kernel_us_total": round(tm_f["varlen"][2], 1),
+                  "two_streams": {"tokens_per_s": iters * NT / wall_f2,
+                                  "ms_per_iteration": wall_f2 / iters * 1e3,
+                                  "streams": "consecutive iterations on alternate streams"}},
         "iterations": iters,
         "tokens_per_iteration": NT,
         "prefill_roofline": {"bound": "mfma", "achieved": round(achieved, 1),

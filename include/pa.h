@@ -310,8 +310,8 @@ pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, const void*
  * together as one call on the GPU.  Sequence i of the batch has the queries
  * q[cu_q_lens[i] .. cu_q_lens[i+1]) at positions seq_lens[i] - q_len(i) ..
  * seq_lens[i] - 1; query j sees positions 0 .. its own, inclusive ("Chunked
- * prefill"), through row i of block_tables (ARTICLE 2.3).  The K/V of every
- * such position must already be in the cache.
+ * prefill"), through the sequence's block-table row (ARTICLE 2.3).  The K/V
+ * of every such position must already be in the cache.
  *
  * The first n_decode sequences are decode rows: one query each, at rows
  * 0 .. n_decode-1 of q and out (cu_q_lens[i] == i for i <= n_decode).  The
@@ -327,10 +327,16 @@ pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, const void*
  * seq_lens [device, n_decode + n_prefill int32]: context length of each
  *   sequence after this iteration's tokens, >= its q_len and >= 1 for a
  *   decode row
- * block_tables [device, (n_decode + n_prefill) * max_blocks int32]
+ * dec_tables [device, n_decode * dec_max_blocks int32]: row i for decode
+ *   row i; pf_tables [device, n_prefill * pf_max_blocks int32]: row c for
+ *   slice c (sequence n_decode + c).  One table of every sequence with
+ *   stride max_blocks is passed as (tables, max_blocks) and
+ *   (tables + n_decode * max_blocks, max_blocks).  Either may be NULL when
+ *   its part of the batch is empty.
  * max_q_len: host-side bound of the slices' q_len; max_decode_len and
  *   max_prefill_len: bounds of seq_lens over the decode rows and the slices
- *   (sizing only; no device-to-host read).
+ *   (sizing only; no device-to-host read), within 16 * dec_max_blocks and
+ *   16 * pf_max_blocks.
  * Types: bf16 q and out with a bf16 or fp8 e4m3fn cache, D 64 or 128,
  *   bs 16, at most 16 query heads per KV head, n_decode <= 4096; other
  *   problems return PA_ERR_INVALID (pa_decode and pa_prefill_chunk take
@@ -354,8 +360,9 @@ size_t pa_attend_varlen_workspace_bytes(int32_t n_decode, int32_t n_prefill, int
 pa_status pa_attend_varlen(void* stream, void* out, pa_dtype out_dt, const void* q,
                            pa_dtype q_dt, const int32_t* cu_q_lens, const int32_t* seq_lens,
                            int32_t n_decode, int32_t n_prefill, const void* k_cache,
-                           const void* v_cache, pa_dtype cache_dt, const int32_t* block_tables,
-                           int32_t max_blocks, int32_t num_blocks, int32_t H_q, int32_t H_kv,
+                           const void* v_cache, pa_dtype cache_dt, const int32_t* dec_tables,
+                           int32_t dec_max_blocks, const int32_t* pf_tables,
+                           int32_t pf_max_blocks, int32_t num_blocks, int32_t H_q, int32_t H_kv,
                            int32_t D, int32_t bs, int32_t max_q_len, int32_t max_decode_len,
                            int32_t max_prefill_len, float sm_scale, float k_scale,
                            float v_scale, int32_t* counters, int64_t n_counters, void* ws,
@@ -578,7 +585,8 @@ pa_status pa_decode_append(void* stream, const int32_t* slots, const int32_t* le
  * 4096 launches per kernel between resets).  The events cost the stream a
  * few microseconds per timed launch.  Kernel names and their bits:
  * "cache_write" 1, "decode" 2, "decode_merge" 4, "prefill" 8,
- * "prefill_merge" 16, "generic" 32, "stage" 64, "stage_cache_write" 128.
+ * "prefill_merge" 16, "generic" 32, "stage" 64, "stage_cache_write" 128,
+ * "varlen" 256.
  * ---------------------------------------------------------------------- */
 
 /* Time the kernels whose bits are set in `mask` (-1: all, 0: none): of each

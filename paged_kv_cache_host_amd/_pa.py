@@ -112,8 +112,8 @@ _SIGS = {
     "pa_attend_varlen_counters": (_i64, [_i32, _i32, _i32, _i32, _i32]),
     "pa_attend_varlen_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_attend_varlen": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32,
-                                _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
-                                _f32, _f32, _vp, _i64, _vp, _sz]),
+                                _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                _i32, _f32, _f32, _f32, _vp, _i64, _vp, _sz]),
 }
 
 for _name, (_res, _args) in _SIGS.items():
@@ -382,7 +382,7 @@ def pa_sched_stats(sched):
 
 TIMING_BITS = {"cache_write": 1, "decode": 2, "decode_merge": 4, "prefill": 8,
                "prefill_merge": 16, "generic": 32, "stage": 64,
-               "stage_cache_write": 128}
+               "stage_cache_write": 128, "varlen": 256}
 
 
 def pa_timing_enable(enable=True, every: int = 1) -> int:
@@ -650,30 +650,38 @@ def pa_attend_varlen_workspace_bytes(n_decode: int, n_prefill: int, H_q: int, H_
 
 
 def pa_attend_varlen(stream, out, q, cu_q_lens, seq_lens, n_decode: int, k_cache, v_cache,
-                     block_tables, num_blocks: int, H_kv: int, max_q_len: int,
+                     dec_tables, pf_tables, num_blocks: int, H_kv: int, max_q_len: int,
                      max_decode_len: int, max_prefill_len: int, sm_scale: float,
                      k_scale: float = 1.0, v_scale: float = 1.0, counters=None, ws=None,
                      bs: int = 16) -> int:
-    """The decode rows (the first n_decode sequences, one query each) and the
-    prefill slices (the rest of seq_lens) of one iteration in one launch."""
+    """The decode rows (the first n_decode sequences, one query each, block
+    tables ``dec_tables``) and the prefill slices (the rest of seq_lens,
+    tables ``pf_tables``) of one iteration in one launch."""
     T, H_q, D = q.shape
     who = "pa_attend_varlen"
     n_seqs = seq_lens.numel()
+    n_pf = n_seqs - n_decode
     _need(0 <= n_decode <= n_seqs, who, f"n_decode={n_decode} must lie in [0, {n_seqs}]")
     _need(T >= n_decode, who, f"q has {T} rows, fewer than the {n_decode} decode rows")
     _check_rows(who, "q", q, T, H_q, D)
     _check_rows(who, "out", out, T, H_q, D)
     _check_i32(who, "cu_q_lens", cu_q_lens, n_seqs + 1)
     _check_i32(who, "seq_lens", seq_lens, n_seqs)
-    _check_tables(who, block_tables, n_seqs)
+    if n_decode:
+        _check_tables(who, dec_tables, n_decode)
+    if n_pf:
+        _check_tables(who, pf_tables, n_pf)
     _check_cache(who, k_cache, v_cache, num_blocks, H_kv, D, bs)
     _need(counters is None or (str(counters.dtype) == "torch.int32" and counters.is_contiguous()),
           who, "counters must be a contiguous int32 tensor")
+    dmb = dec_tables.shape[1] if n_decode else 0
+    pmb = pf_tables.shape[1] if n_pf else 0
     return _lib.pa_attend_varlen(_stream_handle(stream), _dptr(out), dtype_of(out), _dptr(q),
-                                 dtype_of(q), _dptr(cu_q_lens), _dptr(seq_lens), n_decode,
-                                 n_seqs - n_decode, _dptr(k_cache), _dptr(v_cache),
-                                 dtype_of(k_cache), _dptr(block_tables), block_tables.shape[1],
-                                 num_blocks, H_q, H_kv, D, bs, max_q_len, max_decode_len,
-                                 max_prefill_len, sm_scale, k_scale, v_scale, _dptr(counters),
+                                 dtype_of(q), _dptr(cu_q_lens), _dptr(seq_lens), n_decode, n_pf,
+                                 _dptr(k_cache), _dptr(v_cache), dtype_of(k_cache),
+                                 _dptr(dec_tables) if n_decode else None, dmb,
+                                 _dptr(pf_tables) if n_pf else None, pmb, num_blocks, H_q, H_kv,
+                                 D, bs, max_q_len, max_decode_len, max_prefill_len, sm_scale,
+                                 k_scale, v_scale, _dptr(counters),
                                  0 if counters is None else counters.numel(), _dptr(ws),
                                  0 if ws is None else ws.numel() * ws.element_size())

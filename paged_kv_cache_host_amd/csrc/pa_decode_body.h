@@ -514,23 +514,29 @@ __device__ __attribute__((always_inline)) inline void decode_work(DecodeShared<D
     }
   }
   if constexpr (kVarlen) {
-    // partials visible device-wide before the (sequence, KV head) counter
-    // moves; the last of its n_valid chunks to finish merges them
-    if (n_valid > 1) __threadfence();
+    // the last of a (sequence, KV head)'s n_valid chunks to finish merges
+    // their partials: published by every wave's stores, the barrier and
+    // one agent-scope release by thread 0 (the counter bump); the
+    // work-group completing the count acquires at agent scope before the
+    // barrier that lets its waves read them
+    if (n_valid > 1) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   }
   __syncthreads();  // LDS reads done before the next item overwrites it
   if constexpr (kVarlen) {
     if (n_valid > 1) {
       if (tid == 0) {
         const int64_t gi = static_cast<int64_t>(seq) * H_kv + kvh;
-        const int32_t prev = atomicAdd(&merge_counters[gi], 1);
+        const int32_t prev = __hip_atomic_fetch_add(&merge_counters[gi], 1, __ATOMIC_RELEASE,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
         const int32_t last = prev == n_valid - 1;
-        if (last) atomicExch(&merge_counters[gi], 0);
+        if (last) {
+          __hip_atomic_store(&merge_counters[gi], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
         sh.s_flag = last;
       }
       __syncthreads();
       if (sh.s_flag) {
-        __threadfence();
         for (int h = wave; h < G; h += kDecodeWaves)
           decode_merge_row<D>(out, ws_ml, ws_o, static_cast<int64_t>(seq) * H_q + kvh * G + h,
                               n_valid, n_chunks, lane, out_scale);

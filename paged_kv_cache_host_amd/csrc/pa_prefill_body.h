@@ -719,38 +719,93 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
     }
   }
   if constexpr (kVarlen) {
-    // the last of the group's n_split work-groups merges its partials:
-    // every partial is written (and made visible device-wide) before the
-    // group counter is bumped, and read only after it has been seen full
-    __threadfence();
+    // The last of the group's n_split work-groups merges its partials.
+    // Publication: every wave's partial stores, then the barrier, then one
+    // agent-scope release (the counter bump by thread 0: one write-back of
+    // the L2's dirty lines per work-group, nothing invalidated, so the other
+    // work-groups' K/V tiles stay cached).  The work-group that completes
+    // the count acquires at agent scope (thread 0, before the barrier that
+    // releases its waves to read the partials) and clears the counter.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();  // all waves are past the stages: word 0 is free
     int32_t* flag = reinterpret_cast<int32_t*>(smem);
     if (tid == 0) {
       const int64_t gi =
           ((static_cast<int64_t>(c) * geo.n_pos_tiles + pt) * geo.n_head_groups + hg) * geo.H_kv +
           kvh;
-      const int32_t prev = atomicAdd(&merge_counters[gi], 1);
+      const int32_t prev = __hip_atomic_fetch_add(&merge_counters[gi], 1, __ATOMIC_RELEASE,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
       const int32_t last = prev == geo.n_split - 1;
-      if (last) atomicExch(&merge_counters[gi], 0);
+      if (last) {
+        __hip_atomic_store(&merge_counters[gi], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
       *flag = last;
     }
     __syncthreads();
     const bool last = *flag != 0;
     if (!last || !ws_ok) return;
-    __threadfence();
+    // The merge of the pf_merge_* helpers (same operations in the same
+    // order, so the same bits as the merge kernel), arranged for latency:
+    // this work-group's own partial comes from its registers (the values
+    // it wrote), and each other split's 16-byte pieces are loaded together.
     const int64_t stride = static_cast<int64_t>(ws_rows) * H_q;
     const int64_t pair = wrow * H_q + head;
-    const float M = pf_merge_max(ws_ml, pair, stride, geo.n_split);
-    const float inv = pf_merge_inv(ws_ml, pair, stride, geo.n_split, M, v_scale);
+    // (m, l) of every split, loaded without branches so that the loads are
+    // in flight together (splits past n_split reread the last one and are
+    // then ignored)
+    float mj[kPfMaxSplit], lj[kPfMaxSplit];
+#pragma unroll
+    for (int j = 0; j < kPfMaxSplit; ++j) {
+      const int jj = min(j, geo.n_split - 1);
+      const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * (jj * stride + pair));
+      mj[j] = j == split ? m_run : ml.x;
+      lj[j] = j >= geo.n_split ? 0.f : (j == split ? l_tot : ml.y);
+    }
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < kPfMaxSplit; ++j)
+      if (j < geo.n_split && lj[j] > 0.f) M = fmaxf(M, mj[j]);
+    float L = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPfMaxSplit; ++j)
+      if (j < geo.n_split && lj[j] > 0.f) L += __builtin_amdgcn_exp2f(mj[j] - M) * lj[j];
+    const float inv = L > 0.f ? v_scale / L : 0.f;
+    f32x4 acc[NDT][4];
+#pragma unroll
+    for (int n = 0; n < NDT; ++n)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) acc[n][jq] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < geo.n_split; ++j) {
+      if (!(lj[j] > 0.f)) continue;
+      const float w = __builtin_amdgcn_exp2f(mj[j] - M);
+      if (j == split) {
+#pragma unroll
+        for (int n = 0; n < NDT; ++n)
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq)
+            acc[n][jq] += w * f32x4{o[n][4 * jq], o[n][4 * jq + 1], o[n][4 * jq + 2],
+                                    o[n][4 * jq + 3]};
+      } else {
+        const float* po = ws_o + (j * stride + pair) * D;
+        f32x4 v[NDT][4];
+#pragma unroll
+        for (int n = 0; n < NDT; ++n)
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq)
+            v[n][jq] = *reinterpret_cast<const f32x4*>(po + 32 * n + 8 * jq + 4 * g);
+#pragma unroll
+        for (int n = 0; n < NDT; ++n)
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) acc[n][jq] += w * v[n][jq];
+      }
+    }
     uint16_t* orow = out + (row * H_q + head) * D;
 #pragma unroll
     for (int n = 0; n < NDT; ++n)
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const int d = 32 * n + 8 * jq + 4 * g;
-        const f32x4 acc = pf_merge_dims4<D>(ws_ml, ws_o, pair, stride, geo.n_split, M, d);
-        *reinterpret_cast<u32x2*>(orow + d) = pack_bf16x4(acc, inv);
-      }
+      for (int jq = 0; jq < 4; ++jq)
+        *reinterpret_cast<u32x2*>(orow + 32 * n + 8 * jq + 4 * g) = pack_bf16x4(acc[n][jq], inv);
   }
 }
 

@@ -30,6 +30,7 @@
 #include "pa_prefill_body.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace pa {
 namespace {
@@ -46,8 +47,9 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ seq_lens,
     const typename CacheT::raw* __restrict__ k_cache,
-    const typename CacheT::raw* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    int32_t max_blocks, int32_t num_blocks, int32_t n_decode, int32_t H_q, int32_t H_kv,
+    const typename CacheT::raw* __restrict__ v_cache, const int32_t* __restrict__ dec_tables,
+    int32_t dec_max_blocks, const int32_t* __restrict__ pf_tables, int32_t pf_max_blocks,
+    int32_t num_blocks, int32_t n_decode, int32_t H_q, int32_t H_kv,
     PfGeom geo, int32_t pf_gx, int32_t pf_items, float* __restrict__ pf_ws_ml,
     float* __restrict__ pf_ws_o, int32_t pf_ws_rows, int32_t dec_chunks, int32_t dec_shift,
     float* __restrict__ dec_ws_ml, float* __restrict__ dec_ws_o, float score_scale,
@@ -58,12 +60,12 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(
   if (b < pf_items) {
     prefill_block<CacheT, D, true>(
         lds, b % pf_gx, b / pf_gx, out, q, cu_q_lens + n_decode, seq_lens + n_decode, k_cache,
-        v_cache, block_tables + static_cast<int64_t>(n_decode) * max_blocks, max_blocks,
-        num_blocks, H_q, geo, score_scale, v_scale, pf_ws_ml, pf_ws_o, pf_ws_rows, pf_merge);
+        v_cache, pf_tables, pf_max_blocks, num_blocks, H_q, geo, score_scale, v_scale, pf_ws_ml,
+        pf_ws_o, pf_ws_rows, pf_merge);
     __syncthreads();  // the stages are done before the decode lists reuse them
   }
   decode_work<CacheT, D, kBlock, true>(*reinterpret_cast<DecodeShared<D>*>(lds), out, q, k_cache,
-                                       v_cache, block_tables, max_blocks, num_blocks, seq_lens,
+                                       v_cache, dec_tables, dec_max_blocks, num_blocks, seq_lens,
                                        n_decode, H_q, H_kv, H_q / H_kv, dec_chunks, dec_shift,
                                        score_scale, v_scale, counters, dec_ws_ml, dec_ws_o,
                                        dec_merge);
@@ -128,9 +130,10 @@ int32_t device_cus() {
 template <typename CacheT, int D>
 pa_status launch_varlen(hipStream_t st, const VarlenPlan& p, void* out, const void* q,
                         const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t n_decode,
-                        const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                        int32_t max_blocks, int32_t num_blocks, int32_t H_q, int32_t H_kv,
-                        float score_scale, float v_scale, int32_t* counters, void* ws) {
+                        const void* k_cache, const void* v_cache, const int32_t* dec_tables,
+                        int32_t dec_max_blocks, const int32_t* pf_tables, int32_t pf_max_blocks,
+                        int32_t num_blocks, int32_t H_q, int32_t H_kv, float score_scale,
+                        float v_scale, int32_t* counters, void* ws) {
   int32_t* dec_merge = counters + 2;
   int32_t* pf_merge = dec_merge + static_cast<int64_t>(n_decode) * H_kv;
   char* base = static_cast<char*>(ws);
@@ -145,8 +148,9 @@ pa_status launch_varlen(hipStream_t st, const VarlenPlan& p, void* out, const vo
       launch(kVarlen, varlen_kernel<CacheT, D>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads),
              0, st, static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q), cu_q_lens,
              seq_lens, static_cast<const typename CacheT::raw*>(k_cache),
-             static_cast<const typename CacheT::raw*>(v_cache), block_tables, max_blocks,
-             num_blocks, n_decode, H_q, H_kv, p.geo, static_cast<int32_t>(p.pf_gx),
+             static_cast<const typename CacheT::raw*>(v_cache), dec_tables, dec_max_blocks,
+             pf_tables, pf_max_blocks, num_blocks, n_decode, H_q, H_kv, p.geo,
+             static_cast<int32_t>(p.pf_gx),
              static_cast<int32_t>(p.pf_items), pf_ws_ml, pf_ws_o, p.pf_ws_rows, p.dec_chunks,
              p.dec_shift, dec_ws_ml, dec_ws_o, score_scale, v_scale, counters, dec_merge,
              pf_merge);
@@ -194,8 +198,9 @@ extern "C" pa_status pa_attend_varlen(void* stream, void* out, pa_dtype out_dt, 
                                       pa_dtype q_dt, const int32_t* cu_q_lens,
                                       const int32_t* seq_lens, int32_t n_decode,
                                       int32_t n_prefill, const void* k_cache, const void* v_cache,
-                                      pa_dtype cache_dt, const int32_t* block_tables,
-                                      int32_t max_blocks, int32_t num_blocks, int32_t H_q,
+                                      pa_dtype cache_dt, const int32_t* dec_tables,
+                                      int32_t dec_max_blocks, const int32_t* pf_tables,
+                                      int32_t pf_max_blocks, int32_t num_blocks, int32_t H_q,
                                       int32_t H_kv, int32_t D, int32_t bs, int32_t max_q_len,
                                       int32_t max_decode_len, int32_t max_prefill_len,
                                       float sm_scale, float k_scale, float v_scale,
@@ -216,19 +221,21 @@ extern "C" pa_status pa_attend_varlen(void* stream, void* out, pa_dtype out_dt, 
   if (H_q / H_kv > kMaxGroup)
     return fail(PA_ERR_INVALID, "%s: %d query heads per KV head exceed %d", who, H_q / H_kv,
                 kMaxGroup);
-  if (max_blocks <= 0 || num_blocks <= 0 || max_q_len < 0 || max_decode_len < 0 ||
-      max_prefill_len < 0)
+  if (num_blocks <= 0 || max_q_len < 0 || max_decode_len < 0 || max_prefill_len < 0 ||
+      (n_decode > 0 && dec_max_blocks <= 0) || (n_prefill > 0 && pf_max_blocks <= 0))
     return fail(PA_ERR_INVALID,
-                "%s: max_blocks=%d num_blocks=%d max_q_len=%d max_decode_len=%d "
-                "max_prefill_len=%d",
-                who, max_blocks, num_blocks, max_q_len, max_decode_len, max_prefill_len);
-  const int64_t cap = 16LL * max_blocks;
-  if (max_decode_len > cap || max_prefill_len > cap ||
+                "%s: dec_max_blocks=%d pf_max_blocks=%d num_blocks=%d max_q_len=%d "
+                "max_decode_len=%d max_prefill_len=%d",
+                who, dec_max_blocks, pf_max_blocks, num_blocks, max_q_len, max_decode_len,
+                max_prefill_len);
+  if ((n_decode > 0 && max_decode_len > 16LL * dec_max_blocks) ||
+      (n_prefill > 0 && max_prefill_len > 16LL * pf_max_blocks) ||
       (n_prefill > 0 && max_prefill_len < max_q_len))
     return fail(PA_ERR_INVALID,
-                "%s: max_decode_len=%d and max_prefill_len=%d must lie within 16*max_blocks=%lld, "
-                "and max_prefill_len >= max_q_len=%d",
-                who, max_decode_len, max_prefill_len, cap, max_q_len);
+                "%s: max_decode_len=%d must lie within 16*dec_max_blocks=%lld, max_prefill_len=%d "
+                "within 16*pf_max_blocks=%lld and >= max_q_len=%d",
+                who, max_decode_len, 16LL * dec_max_blocks, max_prefill_len,
+                16LL * pf_max_blocks, max_q_len);
   if (n_decode > kMaxSeqsPerLaunch)
     return fail(PA_ERR_INVALID, "%s: %d decode rows exceed %d per launch", who, n_decode,
                 kMaxSeqsPerLaunch);
@@ -240,7 +247,8 @@ extern "C" pa_status pa_attend_varlen(void* stream, void* out, pa_dtype out_dt, 
     return fail(PA_ERR_INVALID, "%s: sm_scale must be finite and > 0", who);
   if (n_prefill > 0 && max_q_len == 0) n_prefill = 0;  // every slice is empty
   if (n_decode == 0 && n_prefill == 0) return PA_OK;
-  if (!out || !q || !cu_q_lens || !seq_lens || !k_cache || !v_cache || !block_tables)
+  if (!out || !q || !cu_q_lens || !seq_lens || !k_cache || !v_cache ||
+      (n_decode > 0 && !dec_tables) || (n_prefill > 0 && !pf_tables))
     return fail(PA_ERR_INVALID, "%s: NULL buffer", who);
   if (!counters) return fail(PA_ERR_WORKSPACE, "%s: NULL counters", who);
   if (static_cast<int64_t>(n_prefill) * max_q_len + n_decode > INT32_MAX / 64)
@@ -260,17 +268,14 @@ extern "C" pa_status pa_attend_varlen(void* stream, void* out, pa_dtype out_dt, 
   const bool fp8 = cache_dt == PA_FP8_E4M3;
   const float score_scale = sm_scale * (fp8 ? k_scale : 1.f) * kLog2e;
   const float vscale = fp8 ? v_scale : 1.f;
-  if (!fp8)
-    return D == 128 ? launch_varlen<BF16, 128>(st, p, out, q, cu_q_lens, seq_lens, n_decode,
-                                               k_cache, v_cache, block_tables, max_blocks,
-                                               num_blocks, H_q, H_kv, score_scale, vscale, counters, ws)
-                    : launch_varlen<BF16, 64>(st, p, out, q, cu_q_lens, seq_lens, n_decode,
-                                              k_cache, v_cache, block_tables, max_blocks,
-                                              num_blocks, H_q, H_kv, score_scale, vscale, counters, ws);
-  return D == 128 ? launch_varlen<FP8, 128>(st, p, out, q, cu_q_lens, seq_lens, n_decode, k_cache,
-                                            v_cache, block_tables, max_blocks, num_blocks, H_q,
-                                            H_kv, score_scale, vscale, counters, ws)
-                  : launch_varlen<FP8, 64>(st, p, out, q, cu_q_lens, seq_lens, n_decode, k_cache,
-                                           v_cache, block_tables, max_blocks, num_blocks, H_q,
-                                           H_kv, score_scale, vscale, counters, ws);
+  auto run = [&](auto cache_tag, auto d_tag) {
+    return launch_varlen<decltype(cache_tag), decltype(d_tag)::value>(
+        st, p, out, q, cu_q_lens, seq_lens, n_decode, k_cache, v_cache, dec_tables,
+        dec_max_blocks, pf_tables, pf_max_blocks, num_blocks, H_q, H_kv, score_scale, vscale,
+        counters, ws);
+  };
+  using D128 = std::integral_constant<int, 128>;
+  using D64 = std::integral_constant<int, 64>;
+  if (!fp8) return D == 128 ? run(BF16{}, D128{}) : run(BF16{}, D64{});
+  return D == 128 ? run(FP8{}, D128{}) : run(FP8{}, D64{});
 }

@@ -118,15 +118,15 @@ class PagedKV:
                                      self.num_blocks, self.h_kv, max_q_len, max_context_len,
                                      sm_scale, self.k_scale, self.v_scale, ws))
 
-    def attend_varlen(self, out, q, cu_q_lens, seq_lens, n_decode: int, tables, max_q_len: int,
-                      max_decode_len: int, max_prefill_len: int, sm_scale: float, bufs,
-                      stream=None):
+    def attend_varlen(self, out, q, cu_q_lens, seq_lens, n_decode: int, dec_tables, pf_tables,
+                      max_q_len: int, max_decode_len: int, max_prefill_len: int,
+                      sm_scale: float, bufs, stream=None):
         """Decode rows and prefill slices in one launch; bufs = varlen_buffers(...)."""
         counters, ws = bufs
         pa.check(pa.pa_attend_varlen(stream, out, q, cu_q_lens, seq_lens, n_decode, self.k,
-                                     self.v, tables, self.num_blocks, self.h_kv, max_q_len,
-                                     max_decode_len, max_prefill_len, sm_scale, self.k_scale,
-                                     self.v_scale, counters, ws))
+                                     self.v, dec_tables, pf_tables, self.num_blocks, self.h_kv,
+                                     max_q_len, max_decode_len, max_prefill_len, sm_scale,
+                                     self.k_scale, self.v_scale, counters, ws))
 
 
 def varlen_buffers(n_decode, n_prefill, h_q, h_kv, d, max_q_len, max_decode_len,

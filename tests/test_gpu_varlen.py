@@ -92,8 +92,9 @@ class Batch:
             bufs = varlen_buffers(self.n_dec, len(w.slices) - self.n_dec, w.h_q, w.h_kv, w.d,
                                   max_q, max_dec, max_pf, DEV)
         out = filled((len(self.rows), w.h_q, w.d), torch.bfloat16, DEV)
-        self.kv.attend_varlen(out, self.q, self.d_cu, self.d_lens, self.n_dec, self.tables, max_q,
-                              max_dec, max_pf, w.sm_scale, bufs)
+        nd = self.n_dec
+        self.kv.attend_varlen(out, self.q, self.d_cu, self.d_lens, nd, self.tables[:nd],
+                              self.tables[nd:], max_q, max_dec, max_pf, w.sm_scale, bufs)
         torch.cuda.synchronize()
         return to_host_raw(out, w.q_dtype), bufs
 
@@ -226,8 +227,10 @@ def test_varlen_rejects_bad_arguments():
         a = dict(n_decode=1, max_q_len=64, max_decode_len=20, max_prefill_len=64,
                  counters=counters, ws=ws)
         a.update(kw)
+        nd = min(a["n_decode"], 2)
         return pa.pa_attend_varlen(None, out, b.q, b.d_cu, b.d_lens, a["n_decode"], b.kv.k,
-                                   b.kv.v, b.tables, w.num_blocks, w.h_kv, a["max_q_len"],
+                                   b.kv.v, b.tables[:nd], b.tables[nd:], w.num_blocks, w.h_kv,
+                                   a["max_q_len"],
                                    a["max_decode_len"], a["max_prefill_len"], w.sm_scale,
                                    counters=a["counters"], ws=a["ws"])
 
