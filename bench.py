@@ -103,14 +103,14 @@ def parse():
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("pa_decode.hip", "pa_device.h"):
+    for f in ("pa_decode.hip", "pa_decode_body.h", "pa_device.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_host_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def prefill_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("pa_prefill.hip", "pa_device.h"):
+    for f in ("pa_prefill.hip", "pa_prefill_body.h", "pa_device.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_host_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

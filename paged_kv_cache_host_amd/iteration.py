@@ -27,7 +27,7 @@ import numpy as np
 import torch
 
 from . import _pa as pa
-from .engine import BLOCK, _TORCH_STORAGE
+from .engine import BLOCK, _TORCH_STORAGE, varlen_buffers
 
 
 class LayerIterations:
@@ -36,7 +36,7 @@ class LayerIterations:
                  cache_blocks: int | None = None, cache_dtype: str = "bf16",
                  k_scale: float = 1.0, v_scale: float = 1.0, sm_scale: float | None = None,
                  free_order=None, provider_syncs: bool = True, two_streams: bool = False,
-                 mode: str = "chunked", fill_outputs: float | None = None):
+                 mode: str = "chunked", fill_outputs: float | None = None, fused: bool = False):
         self.h_q, self.h_kv, self.d = h_q, h_kv, d
         self.dev = torch.device(device)
         self.provider = provider
@@ -71,7 +71,7 @@ class LayerIterations:
         # compute stream moves the used prefix.  One event per GROUP
         # iterations tells the host which buffers the kernels have read.
         T = max_running + max(prefill_budget, 1)
-        n_meta = T + max_running + 2 * max_running * mb + 2 * max_running + 1
+        n_meta = T + 2 * max_running * mb + 4 * max_running + 1
         self.NBUF, self.GROUP = 8, 4
         self.host_buf = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True)
                          for _ in range(self.NBUF)]
@@ -83,16 +83,18 @@ class LayerIterations:
                        for _ in range(2)]
         n = pa.pa_decode_workspace_bytes(max_running, h_q, h_kv, d, max_context)
         self.ws_dec = torch.zeros(max(n, 1), dtype=torch.uint8, device=self.dev)
-        # the launch's key split (hence its workspace) depends on its slice
-        # count and longest slice, through whole 32-row position tiles: cover
-        # every count and every multiple of 32 up to the budget (a slice
-        # longer than 32768 spans more than 128 position tiles and is never
-        # split) and the budget itself
+        # sized for every call with at most max_running slices of at most
+        # the budget (the query bounds every smaller call)
         top = max(prefill_budget, 1)
-        q_lens = sorted({top} | set(range(32, min(top, 32768) + 1, 32)))
-        n = max(pa.pa_prefill_workspace_bytes(c, q, h_q, h_kv, d, max_context)
-                for c in range(1, max_running + 1) for q in q_lens)
+        n = pa.pa_prefill_workspace_bytes(max_running, top, h_q, h_kv, d, max_context)
         self.ws_pf = torch.empty(max(n, 1), dtype=torch.uint8, device=self.dev)
+        # fused: one pa_attend_varlen per iteration over [decode rows; slices]
+        self.fused = bool(fused)
+        if self.fused:
+            self.out_mix = [torch.empty((T, h_q, d), dtype=out_dt, device=self.dev)
+                            for _ in range(2)]
+            self.bufs_mix = varlen_buffers(max_running, max_running, h_q, h_kv, d, top,
+                                           max_context, max_context, self.dev)
         self.compute = torch.cuda.Stream(device=self.dev)
         # two_streams: the prefill slices run on a second stream, after the
         # staging launch and beside the decode, and the compute stream waits
@@ -153,12 +155,17 @@ class LayerIterations:
         self.waste.append(float("nan") if held == 0 else 1.0 - acc["tokens_held"] / held)
         self.unwritten.append(float("nan") if held == 0 else acc["unwritten"] / held)
 
-        # token data: prefill tokens first, then decode tokens
+        # token data: prefill tokens first, then decode tokens (fused: the
+        # decode rows first, as pa_attend_varlen takes them)
         pf_pos = np.concatenate([np.arange(a, a + n) for a, n in zip(pst.tolist(), pl.tolist())]) \
             if n_pf else np.zeros(0, np.int64)
         pf_seq = np.repeat(ps, pl) if n_pf else np.zeros(0, np.int64)
-        seqs = np.concatenate([pf_seq, ds]).astype(np.int64)
-        poss = np.concatenate([pf_pos, dp]).astype(np.int64)
+        if self.fused:
+            seqs = np.concatenate([ds, pf_seq]).astype(np.int64)
+            poss = np.concatenate([dp, pf_pos]).astype(np.int64)
+        else:
+            seqs = np.concatenate([pf_seq, ds]).astype(np.int64)
+            poss = np.concatenate([pf_pos, dp]).astype(np.int64)
         n_tok = n_pt + n_dec
         h = self.host_buf[X].numpy()
         dvb = self.dev_buf[X]
@@ -171,8 +178,18 @@ class LayerIterations:
             return r
 
         h_sl, d_sl = region(n_tok)
-        h_sl[:n_pt] = b.slots()
-        h_sl[n_pt:] = dsl
+        if self.fused:
+            h_sl[:n_dec] = dsl
+            h_sl[n_dec:] = b.slots()
+            h_vl, d_vl = region(n_dec + n_pf)       # seq_lens
+            h_vl[:n_dec] = dp + 1
+            h_vl[n_dec:] = pst + pl
+            h_cu, d_cu = region(n_dec + n_pf + 1)   # cu_q_lens
+            h_cu[:n_dec + 1] = np.arange(n_dec + 1)
+            h_cu[n_dec + 1:] = n_dec + np.cumsum(pl)
+        else:
+            h_sl[:n_pt] = b.slots()
+            h_sl[n_pt:] = dsl
         mbd = mbp = 1
         if n_dec:
             max_ctx_d = int(dp.max()) + 1
@@ -192,10 +209,11 @@ class LayerIterations:
             h_pt, d_pt = region(n_pf * mbp)
             st, _, _ = pa.pa_pack_batch(self.pool, ps, mbp, h_pt.reshape(n_pf, mbp), None)
             pa.check(st)
-            h_pm, d_pm = region(2 * n_pf + 1)
-            h_pm[0] = 0
-            h_pm[1:n_pf + 1] = np.cumsum(pl)
-            h_pm[n_pf + 1:] = pst
+            if not self.fused:
+                h_pm, d_pm = region(2 * n_pf + 1)
+                h_pm[0] = 0
+                h_pm[1:n_pf + 1] = np.cumsum(pl)
+                h_pm[n_pf + 1:] = pst
         record = {"decode": (ds.copy(), dp.copy()), "prefill": (ps.copy(), pst.copy(), pl.copy())}
         k_new = v_new = q_new = None
         if n_tok:
@@ -216,8 +234,29 @@ class LayerIterations:
             pa.check(pa.pa_stage(c, dvb, self.host_buf[X], 4 * off))
         if self.fill_outputs is not None:
             with torch.cuda.stream(c):
-                self.out_pf[O][:n_pt].fill_(self.fill_outputs)
-                self.out_dec[O][:n_dec].fill_(self.fill_outputs)
+                if self.fused:
+                    self.out_mix[O][:n_tok].fill_(self.fill_outputs)
+                else:
+                    self.out_pf[O][:n_pt].fill_(self.fill_outputs)
+                    self.out_dec[O][:n_dec].fill_(self.fill_outputs)
+        if self.fused:
+            if n_tok:
+                counters, ws = self.bufs_mix
+                pa.check(pa.pa_attend_varlen(
+                    c, self.out_mix[O][:n_tok], q_new[:n_tok], d_cu, d_vl, n_dec, self.k, self.v,
+                    d_dt.view(n_dec, mbd) if n_dec else None,
+                    d_pt.view(n_pf, mbp) if n_pf else None, self.cache_blocks, self.h_kv,
+                    int(pl.max()) if n_pf else 0, int(dp.max()) + 1 if n_dec else 0,
+                    int((pst + pl).max()) if n_pf else 0, self.sm, self.k_scale, self.v_scale,
+                    counters, ws))
+            if self.it % self.GROUP == self.GROUP - 1:
+                self.ev_group[g % 2].record(c)
+            self._last = (record, self.out_mix[O][:n_dec], self.out_mix[O][n_dec:n_tok])
+            if keep is not None:
+                c.synchronize()
+                keep(record, self.out_mix[O][:n_dec].clone(), self.out_mix[O][n_dec:n_tok].clone())
+            self.it += 1
+            return n_tok
         if n_pf:
             pf_stream = c
             if self.side is not None:

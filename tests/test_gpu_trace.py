@@ -109,17 +109,20 @@ def _decode_bf16(t):
     return codecs.decode(t.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
 
 
-@pytest.mark.parametrize("mode", ["chunked", "continuous", "static", "naive"])
-def test_trace_iterations_match_oracle(mode):
+@pytest.mark.parametrize("mode,fused", [("chunked", False), ("continuous", False),
+                                        ("static", False), ("naive", False), ("chunked", True),
+                                        ("static", True)])
+def test_trace_iterations_match_oracle(mode, fused):
     """Host waits for every iteration's kernels (the ``keep`` callback); each
     of the four schedules (static batches prefill up to 12 padded prompts in
-    one launch)."""
+    one launch); ``fused``: each iteration's attention is one
+    pa_attend_varlen launch over its decode rows and slices."""
     from paged_kv_cache_host_amd.engine import to_device_raw
     from paged_kv_cache_host_amd.iteration import LayerIterations
 
     w, host_rows, max_ctx = _trace()
-    say(f"[trace parity, synchronous, {mode}] {w.name} pool={w.num_blocks} running<={R} "
-        f"budget={BUDGET[mode]}")
+    say(f"[trace parity, synchronous, {mode}, fused={fused}] {w.name} pool={w.num_blocks} "
+        f"running<={R} budget={BUDGET[mode]}")
 
     def provider(seqs, positions):
         k, v, q = host_rows(seqs, positions)
@@ -127,7 +130,7 @@ def test_trace_iterations_match_oracle(mode):
                 to_device_raw(q, "bf16", "cuda"))
 
     run = LayerIterations(w.num_blocks, H_Q, H_KV, D, "cuda", provider, R, BUDGET[mode],
-                          max_context=max_ctx, mode=mode, fill_outputs=SENTINEL)
+                          max_context=max_ctx, mode=mode, fill_outputs=SENTINEL, fused=fused)
     results = []
     for it in range(w.iters):
         for sid, p, o in w.arrivals[it]:
@@ -146,8 +149,8 @@ def test_trace_iterations_match_oracle(mode):
         assert run.totals["preempted"] > 0
 
 
-@pytest.mark.parametrize("two_streams", [False, True])
-def test_trace_iterations_pipelined_match_oracle(two_streams):
+@pytest.mark.parametrize("two_streams,fused", [(False, False), (True, False), (False, True)])
+def test_trace_iterations_pipelined_match_oracle(two_streams, fused):
     """The host runs ahead of the kernels (metadata ring, one event per group
     of iterations, provider tensors already resident): outputs are copied on
     the compute stream, the written cache slots compared byte for byte at
@@ -156,8 +159,8 @@ def test_trace_iterations_pipelined_match_oracle(two_streams):
     from paged_kv_cache_host_amd.iteration import LayerIterations
 
     w, host_rows, max_ctx = _trace()
-    say(f"[trace parity, pipelined, two_streams={two_streams}] {w.name} pool={w.num_blocks} "
-        f"running<={R} budget={B}")
+    say(f"[trace parity, pipelined, two_streams={two_streams}, fused={fused}] {w.name} "
+        f"pool={w.num_blocks} running<={R} budget={B}")
 
     def provider(seqs, positions):
         k, v, q = host_rows(seqs, positions)
@@ -167,7 +170,8 @@ def test_trace_iterations_pipelined_match_oracle(two_streams):
         return out
 
     run = LayerIterations(w.num_blocks, H_Q, H_KV, D, "cuda", provider, R, B, max_context=max_ctx,
-                          provider_syncs=False, two_streams=two_streams, fill_outputs=SENTINEL)
+                          provider_syncs=False, two_streams=two_streams, fill_outputs=SENTINEL,
+                          fused=fused)
     copies = []
     for it in range(w.iters):
         for sid, p, o in w.arrivals[it]:
