@@ -22,6 +22,9 @@ algorithmic decode bytes per launch over its mean duration from HIP events
 on its own stream (libpa's pa_timing_* facility).
 
 Secondary legs (skipped with --decode-only):
+  ``decode_step_fused`` the same step as one pa_decode_step launch (a2 and
+                 a3 in one kernel: the staging copy, the new tokens' K/V,
+                 the table entries and the attention);
   ``mixed``      the chunked-prefill iteration: a 32768-token prompt as 64
                  causal 512-token slices, each iteration also decoding one
                  token for 127 sequences; tokens/s per layer over the 64
@@ -41,7 +44,7 @@ Secondary legs (skipped with --decode-only):
                  fragmentation.
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 5] [--no-cpu-baseline]
-                       [--decode-only]
+                       [--decode-only] [--step-launch separate|fused|fused-device]
 """
 from __future__ import annotations
 
@@ -74,6 +77,12 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="decode step: the append launch on a second stream")
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--step-launch", choices=["fused", "fused-device", "separate"],
+                    default="separate",
+                    help="decode step as one pa_decode_step launch that also stages the "
+                         "metadata (fused), as pa_stage + pa_decode_step reading it from the "
+                         "device (fused-device), or as pa_stage_decode_append + pa_decode "
+                         "(separate)")
     ap.add_argument("--stage-ahead", action="store_true",
                     help="decode step: stage the metadata on a side stream ahead of the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -538,8 +547,9 @@ def _timings(pa, names):
     return out
 
 
-def decode_leg(args, dev):
-    """The headline step: one decode iteration of the decode-70b layer."""
+def decode_leg(args, dev, launch_mode: str | None = None):
+    """The headline step: one decode iteration of the decode-70b layer
+    (``launch_mode`` overrides --step-launch)."""
     import torch
 
     import workloads
@@ -609,6 +619,15 @@ def decode_leg(args, dev):
     # (pa_stage, one work-group), and pa_decode_append on the compute stream
     # reads the staged slots and lengths from device memory.
     ahead = torch.cuda.Stream(device=dev) if getattr(args, "stage_ahead", False) else None
+    # --step-launch fused: pa_decode_step stages the buffer, appends the new
+    # tokens, enters their blocks and attends, all in one launch
+    if launch_mode is None:
+        launch_mode = getattr(args, "step_launch", "separate")
+    fused = launch_mode in ("fused", "fused-device")
+    if fused and (ahead is not None or aux is not compute):
+        raise SystemExit("--step-launch fused runs on one stream (no --overlap / --stage-ahead)")
+    kname = "decode_step" if fused else "decode"
+    side = (["stage"] if launch_mode == "fused-device" else []) if fused else ["stage_cache_write"]
     ev_w = [torch.cuda.Event() for _ in range(2)]
     ev_group = [torch.cuda.Event() for _ in range(2)]
     for e in ev_group:
@@ -628,7 +647,14 @@ def decode_leg(args, dev):
         h_lens[:] = lens_host
         lens_np = lens_host
         r = i % R
-        if ahead is not None:
+        if fused:
+            if launch_mode == "fused-device":
+                pa.check(pa.pa_stage(compute, dev_buf[X], host_buf[X], 4 * n_meta))
+            src = host_buf[X] if launch_mode == "fused" else None
+            pa.check(pa.pa_decode_step(compute, dev_buf[X], src, 4 * n_meta, 0, 4 * S,
+                                       k_ring[r], v_ring[r], out, q_ring[r], kv.k, kv.v, d_tab,
+                                       num_blocks, H_KV, max_ctx, sm, 1.0, 1.0, ws))
+        elif ahead is not None:
             # the buffer is staged on the side stream as soon as it is packed
             # (during an earlier step's decode); the compute stream then only
             # scatters the new tokens and enters their blocks
@@ -646,8 +672,9 @@ def decode_leg(args, dev):
         if ahead is None and aux is not compute:
             ev_w[i % 2].record(aux)
             compute.wait_event(ev_w[i % 2])
-        pa.check(pa.pa_decode(compute, out, q_ring[r], kv.k, kv.v, d_tab, d_lens,
-                              num_blocks, H_KV, max_ctx, sm, 1.0, 1.0, ws))
+        if not fused:
+            pa.check(pa.pa_decode(compute, out, q_ring[r], kv.k, kv.v, d_tab, d_lens,
+                                  num_blocks, H_KV, max_ctx, sm, 1.0, 1.0, ws))
         if timed:
             ctx_lens.append(lens_np.copy())
         if i % GROUP == GROUP - 1:
@@ -660,8 +687,7 @@ def decode_leg(args, dev):
     # step's other kernels.  The warm-up steps already carry the timed
     # launches: the first launch with events attached pays a one-time set-up
     # (measured ~0.4 ms), which must not land in the timed window.
-    pa.check(pa.pa_timing_enable(["decode", "decode_merge", "stage_cache_write"],
-                                 every=TIME_EVERY))
+    pa.check(pa.pa_timing_enable([kname, "decode_merge"] + side, every=TIME_EVERY))
     # the collector is run and frozen before the warm-up steps, not right
     # before the timed ones: a full collection walks the whole heap and
     # leaves the host's caches cold for the first timed step (measured
@@ -670,36 +696,40 @@ def decode_leg(args, dev):
     for i in range(W):
         step(i, False)
     torch.cuda.synchronize()
-    pa.check(pa.pa_timing_enable(["decode"], every=TIME_EVERY))
+    pa.check(pa.pa_timing_enable([kname], every=TIME_EVERY))
     t0 = time.perf_counter()
     for i in range(K):
         step(W + i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    tm = _timings(pa, ("decode",))
-    assert tm["decode"][0] == len(range(0, K, TIME_EVERY)), tm
-    pa.check(pa.pa_timing_enable(["decode_merge", "stage_cache_write"]))
+    tm = _timings(pa, (kname,))
+    assert tm[kname][0] == len(range(0, K, TIME_EVERY)), tm
+    pa.check(pa.pa_timing_enable(["decode_merge"] + side))
     for i in range(EXTRA):
         step(W + K + i, False)
     torch.cuda.synchronize()
-    tm.update(_timings(pa, ("decode_merge", "stage_cache_write")))
+    tm.update(_timings(pa, ["decode_merge"] + side))
     pa.check(pa.pa_timing_enable(False))
     kv.close()
 
     dec_bytes = [decode_bytes(l) for l in ctx_lens]
     total_bytes = sum(dec_bytes) + K * cache_write_bytes(S)
-    dec_avg_s = tm["decode"][1] / 1e6
-    timed_bytes = float(np.mean(dec_bytes[::TIME_EVERY]))
+    dec_avg_s = tm[kname][1] / 1e6
+    # the fused kernel also moves the new tokens' K/V (the cache write's bytes)
+    timed_bytes = float(np.mean(dec_bytes[::TIME_EVERY])) + (cache_write_bytes(S) if fused else 0)
     return {
         "value": total_bytes / wall / 1e9,
         "wall": wall,
         "mean_context": float(np.mean([l.mean() for l in ctx_lens])),
         "num_seqs": S, "num_blocks": num_blocks,
         "achieved": timed_bytes / dec_avg_s / 1e9,
-        "timed_launches": tm["decode"][0],
+        "timed_launches": tm[kname][0],
         "kernel_us": dec_avg_s * 1e6,
-        "merge_us": tm["decode_merge"][1], "stage_cache_write_us": tm["stage_cache_write"][1],
-        "bytes_per_launch": int(sum(dec_bytes) / K),
+        "kernel": "decode_step_kernel<BF16,128>" if fused else "decode_kernel<BF16,128,16>",
+        "fused": fused,
+        "merge_us": tm["decode_merge"][1],
+        "stage_cache_write_us": None if fused else tm["stage_cache_write"][1],
+        "bytes_per_launch": int(sum(dec_bytes) / K) + (cache_write_bytes(S) if fused else 0),
     }
 
 
@@ -1444,15 +1474,28 @@ def main():
                      dpmc["algorithmic_bytes_per_launch"],
                      "traffic_note": "counter bytes and algorithmic bytes per launch of the "
                                      "profiled run (its contexts differ slightly from this run's)",
-                     "kernel": "decode_kernel<BF16,128,16>",
+                     "kernel": d["kernel"],
                      "kernel_us": round(d["kernel_us"], 2),
-                     "other_kernels_us": {"decode_merge_kernel": round(d["merge_us"], 2),
-                                          "stage_cache_write_kernel":
-                                              round(d["stage_cache_write_us"], 2)},
+                     "other_kernels_us": {"decode_merge_kernel": round(d["merge_us"], 2)} |
+                     ({} if d["fused"] else {"stage_cache_write_kernel":
+                                             round(d["stage_cache_write_us"], 2)}),
                      "algorithmic_bytes_per_launch": d["bytes_per_launch"],
                      "kernel_source_digest": digest},
     }
     if not args.decode_only:
+        # the same step as one pa_decode_step launch (metadata staged, new
+        # tokens appended, blocks entered and attention, in one kernel)
+        alt = "fused" if not d["fused"] else "separate"
+        f = decode_leg(args, dev, alt)
+        result["decode_step_" + alt] = {
+            "launch": ("pa_decode_step (staging, append, table entries and attention in one "
+                       "kernel)" if alt == "fused" else "pa_stage_decode_append + pa_decode"),
+            "value": round(f["value"], 2), "unit": "GB/s",
+            "ms_per_step": round(f["wall"] / K * 1e3, 4),
+            "kernel": f["kernel"], "kernel_us": round(f["kernel_us"], 2),
+            "achieved": round(f["achieved"], 2),
+            "frac": round(f["achieved"] / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": f["bytes_per_launch"]}
         m = mixed_leg(args, dev)
         m["workload"] = ("mixed chunked prefill: 32768-token prompt as 64 causal 512-token "
                          "slices + 127 decodes per iteration, 64/8 heads, d128, bf16")

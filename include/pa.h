@@ -579,6 +579,58 @@ pa_status pa_decode_append(void* stream, const int32_t* slots, const int32_t* le
                            int32_t* block_tables, int32_t max_blocks);
 
 /* ------------------------------------------------------------------------
+ * pa_decode_step -- one decode iteration of a batch whose block tables stay
+ * on the device, in ONE launch: pa_stage_decode_append (or pa_decode_append)
+ * followed by pa_decode.  LESSON "Continuous batching at the iteration
+ * level": the iteration's new tokens are written into the cache before
+ * attention reads it; ARTICLE 2.2: a block table grows by one entry when the
+ * next token opens a block; 2.3: attention reads the tables and context
+ * lengths from device memory.  The item of the persistent decode kernel that
+ * streams a sequence's last block writes the new token's K/V for its KV head
+ * just before reading that block, and the KV-head-0 item enters
+ *     block_tables[i * max_blocks + (lens[i] - 1) / 16] = slots[i] / 16.
+ * Outputs, cache bytes and tables equal those of the two launches.
+ *
+ * dst          [device, bytes] int32 metadata buffer holding the S slots at
+ *              byte slot_offset and the S context lengths (new token
+ *              included) at byte lens_offset, both multiples of 4 inside
+ *              bytes, else PA_ERR_INVALID.
+ * src_host     [host] pinned source of that buffer (as for pa_stage): the
+ *              launch copies its first `bytes` into dst (one work-group reads
+ *              the host; the others wait for it, with a bounded wait), so
+ *              dst holds the staged copy afterwards.  NULL: dst already holds
+ *              the metadata (for instance staged once for all the layers of
+ *              an iteration) and is only read.
+ * k_new, v_new [device, S x H_kv x D] bf16 (new_dt must be PA_BF16): token
+ *              i's K/V, row i.
+ * out, q       [device, S x H_q x D] bf16, as for pa_decode.
+ * k_cache, v_cache, cache_dt (bf16 or fp8 e4m3fn with k_scale, v_scale as
+ *              for pa_cache_write / pa_decode), num_blocks, H_kv, D (64 or
+ *              128), bs (16 only), max_context_len (>= every length; larger
+ *              lengths are attended as pa_decode attends them), sm_scale.
+ * block_tables [device, S x max_blocks] int32, row i = sequence i, updated
+ *              in place.
+ * ws           [device, ws_bytes >= pa_decode_workspace_bytes(S, H_q, H_kv,
+ *              D, max_context_len)]: the same workspace as pa_decode (its
+ *              counter words zero before the first call; the launch leaves
+ *              them zero).  Calls that overlap on one workspace race.
+ * Limits: S <= 2048, bf16 q/out/new K/V, H_q / H_kv <= 16; else
+ * PA_ERR_INVALID (use the two launches).  A token whose slot lies outside
+ * the pool, or whose length is < 1 or > max_blocks * 16, is not written and
+ * leaves its row unchanged (pa_stage_decode_append would still write a token
+ * with a valid slot and an out-of-range length); a length < 1 also leaves the
+ * output row unwritten, as pa_decode does.
+ * ---------------------------------------------------------------------- */
+pa_status pa_decode_step(void* stream, int32_t* dst, const void* src_host, size_t bytes,
+                         size_t slot_offset, size_t lens_offset, const void* k_new,
+                         const void* v_new, pa_dtype new_dt, void* out, pa_dtype out_dt,
+                         const void* q, pa_dtype q_dt, void* k_cache, void* v_cache,
+                         pa_dtype cache_dt, int32_t* block_tables, int32_t max_blocks,
+                         int32_t num_blocks, int32_t S, int32_t H_q, int32_t H_kv, int32_t D,
+                         int32_t bs, int32_t max_context_len, float sm_scale, float k_scale,
+                         float v_scale, void* ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------
  * Kernel timing (instrumentation, off by default).  Each launch of a
  * selected kernel carries a pair of HIP events attached to the launch
  * (hipExtLaunchKernel), which take that kernel's start and end times (up to
@@ -586,7 +638,7 @@ pa_status pa_decode_append(void* stream, const int32_t* slots, const int32_t* le
  * few microseconds per timed launch.  Kernel names and their bits:
  * "cache_write" 1, "decode" 2, "decode_merge" 4, "prefill" 8,
  * "prefill_merge" 16, "generic" 32, "stage" 64, "stage_cache_write" 128,
- * "varlen" 256.
+ * "varlen" 256, "decode_step" 512.
  * ---------------------------------------------------------------------- */
 
 /* Time the kernels whose bits are set in `mask` (-1: all, 0: none): of each

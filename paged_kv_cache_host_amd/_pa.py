@@ -103,6 +103,9 @@ _SIGS = {
                                        _i32]),
     "pa_decode_append": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                                  _i32, _i32, _f32, _f32, _vp, _i32]),
+    "pa_decode_step": (_i32, [_vp, _vp, _vp, _sz, _sz, _sz, _vp, _vp, _i32, _vp, _i32, _vp,
+                               _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _i32, _i32, _f32, _f32, _f32, _vp, _sz]),
     "pa_timing_enable": (_i32, [_i32, _i32]),
     "pa_timing_query": (_i32, [C.c_char_p, _i32p, C.POINTER(_f32), C.POINTER(_f32)]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -382,7 +385,7 @@ def pa_sched_stats(sched):
 
 TIMING_BITS = {"cache_write": 1, "decode": 2, "decode_merge": 4, "prefill": 8,
                "prefill_merge": 16, "generic": 32, "stage": 64,
-               "stage_cache_write": 128, "varlen": 256}
+               "stage_cache_write": 128, "varlen": 256, "decode_step": 512}
 
 
 def pa_timing_enable(enable=True, every: int = 1) -> int:
@@ -567,6 +570,43 @@ def pa_decode_append(stream, slots, lens, n: int, k_new, v_new, k_cache, v_cache
                                  _dptr(k_new), _dptr(v_new), dtype_of(k_new), _dptr(k_cache),
                                  _dptr(v_cache), dtype_of(k_cache), num_blocks, H_kv, D, bs,
                                  k_scale, v_scale, _dptr(block_tables), block_tables.shape[1])
+
+
+def pa_decode_step(stream, dst, src_host, nbytes: int, slot_offset: int, lens_offset: int,
+                   k_new, v_new, out, q, k_cache, v_cache, block_tables, num_blocks: int,
+                   H_kv: int, max_context_len: int, sm_scale: float, k_scale: float = 1.0,
+                   v_scale: float = 1.0, ws=None, bs: int = 16) -> int:
+    """One decode iteration in one launch: the S = q.shape[0] new tokens'
+    K/V (``k_new``/``v_new`` [S, H_kv, D] bf16) into their slots, their
+    blocks into ``block_tables`` (device [S, max_blocks] int32, updated in
+    place) and decode attention into ``out``.  The int32 slots and context
+    lengths sit at byte ``slot_offset`` / ``lens_offset`` of the metadata
+    buffer: ``src_host`` (pinned host tensor), staged into the device tensor
+    ``dst`` by the launch, or None when ``dst`` already holds them."""
+    S, H_q, D = q.shape
+    who = "pa_decode_step"
+    if src_host is not None:
+        if src_host.is_cuda or not src_host.is_pinned():
+            raise PaError(PA_ERR_INVALID, f"{who}: source must be a pinned host tensor")
+        if nbytes > src_host.numel() * src_host.element_size():
+            raise PaError(PA_ERR_INVALID, f"{who}: nbytes exceeds the source")
+    if nbytes > dst.numel() * dst.element_size():
+        raise PaError(PA_ERR_INVALID, f"{who}: nbytes exceeds dst")
+    _check_rows(who, "q", q, S, H_q, D)
+    _check_rows(who, "out", out, S, H_q, D)
+    _check_tables(who, block_tables, S)
+    _check_cache(who, k_cache, v_cache, num_blocks, H_kv, D, bs)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t.is_contiguous() and t.numel() >= S * H_kv * D, who,
+              f"{name} must be a contiguous [>= {S}, {H_kv}, {D}] tensor")
+    return _lib.pa_decode_step(_stream_handle(stream), _dptr(dst),
+                               None if src_host is None else src_host.data_ptr(), nbytes,
+                               slot_offset, lens_offset, _dptr(k_new), _dptr(v_new),
+                               dtype_of(k_new), _dptr(out), dtype_of(out), _dptr(q), dtype_of(q),
+                               _dptr(k_cache), _dptr(v_cache), dtype_of(k_cache),
+                               _dptr(block_tables), block_tables.shape[1], num_blocks, S, H_q,
+                               H_kv, D, bs, max_context_len, sm_scale, k_scale, v_scale,
+                               _dptr(ws), 0 if ws is None else ws.numel() * ws.element_size())
 
 
 def pa_decode_workspace_bytes(S: int, H_q: int, H_kv: int, D: int, max_context_len: int) -> int:

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["pa_host.cpp", "pa_sched.cpp", "pa_timing.cpp", "pa_cache_write.hip", "pa_decode.hip", "pa_generic.hip", "pa_prefill.hip", "pa_stage.hip", "pa_varlen.hip"]
+SOURCES = ["pa_host.cpp", "pa_sched.cpp", "pa_timing.cpp", "pa_cache_write.hip", "pa_decode.hip", "pa_generic.hip", "pa_prefill.hip", "pa_stage.hip", "pa_varlen.hip", "pa_decode_step.hip"]
 ARCH = "gfx950"
 
 

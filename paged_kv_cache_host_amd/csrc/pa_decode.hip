@@ -91,15 +91,19 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   decode_merge_row<D>(out, ws_ml, ws_o, idx, nsp, n_chunks, lane, out_scale);
 }
 
-inline int32_t decode_num_batches(int32_t S) {
-  return (S + kMaxSeqsPerLaunch - 1) / kMaxSeqsPerLaunch;
-}
-
-// Bytes of ticket counters at the front of the workspace (two int32 per
-// launch batch of up to kMaxSeqsPerLaunch sequences).
-inline size_t decode_counter_bytes(int32_t S) {
-  return (static_cast<size_t>(decode_num_batches(S)) * 2 * sizeof(int32_t) + 255) &
-         ~static_cast<size_t>(255);
+// Launches the chunk merge of a decode over S sequences (n_chunks > 1).
+pa_status launch_decode_merge(hipStream_t st, void* out, const float* ws_ml, const float* ws_o,
+                              const int32_t* context_lens, int32_t max_blocks, int32_t bs,
+                              int32_t S, int32_t H_q, int32_t D, int32_t n_chunks, int32_t shift,
+                              float out_scale) {
+  const int64_t rows = static_cast<int64_t>(S) * H_q;
+  auto* kern = D == 128 ? decode_merge_kernel<128> : decode_merge_kernel<64>;
+  hipError_t e = launch(kDecodeMerge, kern, dim3((rows + 3) / 4), dim3(256), 0, st,
+                        static_cast<uint16_t*>(out), ws_ml, ws_o, context_lens, max_blocks, bs, S,
+                        H_q, n_chunks, shift, out_scale);
+  if (e != hipSuccess)
+    return fail(PA_ERR_DEVICE, "decode merge launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
 }
 
 // Work-groups of the persistent kernel that fit on the current device at
@@ -151,14 +155,9 @@ static pa_status launch_decode_mfma(hipStream_t st, void* out, const void* q, co
     if (e != hipSuccess)
       return fail(PA_ERR_DEVICE, "pa_decode: launch failed: %s", hipGetErrorString(e));
   }
-  if (n_chunks > 1) {
-    const int64_t rows = static_cast<int64_t>(S) * H_q;
-    hipError_t e = launch(kDecodeMerge, decode_merge_kernel<D>, dim3((rows + 3) / 4), dim3(256), 0,
-                          st, static_cast<uint16_t*>(out), ws_ml, ws_o, context_lens, max_blocks,
-                          BS, S, H_q, n_chunks, shift, v_scale);
-    if (e != hipSuccess)
-      return fail(PA_ERR_DEVICE, "pa_decode: merge launch failed: %s", hipGetErrorString(e));
-  }
+  if (n_chunks > 1)
+    return launch_decode_merge(st, out, ws_ml, ws_o, context_lens, max_blocks, BS, S, H_q, D,
+                               n_chunks, shift, v_scale);
   return PA_OK;
 }
 

@@ -33,6 +33,18 @@ inline int32_t decode_num_chunks(int32_t max_context_len, int32_t shift) {
   return nblk <= 0 ? 1 : ((nblk - 1) >> shift) + 1;
 }
 
+inline int32_t decode_num_batches(int32_t S) {
+  return (S + kMaxSeqsPerLaunch - 1) / kMaxSeqsPerLaunch;
+}
+
+// Bytes of ticket counters at the front of the decode workspace (two int32
+// per launch batch of up to kMaxSeqsPerLaunch sequences, rounded up to 256
+// bytes; the fused append + decode launch keeps a third word there).
+inline size_t decode_counter_bytes(int32_t S) {
+  return (static_cast<size_t>(decode_num_batches(S)) * 2 * sizeof(int32_t) + 255) &
+         ~static_cast<size_t>(255);
+}
+
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
@@ -74,21 +86,36 @@ struct BlockRegs<FP8, D> {
 // j / 2; with BS = 8 its K rows and V quads come from blocks 2 j and
 // 2 j + 1 (lane by lane).  Table indices are clamped to the last of the
 // sequence's nphys blocks and every entry into the pool.
-template <typename CacheT, int D, int BS>
+// kOverride (the fused append + decode launch, BS = 16): table entry
+// `last_ti` (when >= 0) is taken as `last_blk` instead of being read (the
+// launch itself enters that block into the table).
+template <typename CacheT, int D, int BS, bool kOverride = false>
 __device__ __forceinline__ void load_block(BlockRegs<CacheT, D>& r,
                                            const typename CacheT::raw* __restrict__ k_cache,
                                            const typename CacheT::raw* __restrict__ v_cache,
                                            const int32_t* __restrict__ table, int32_t j,
                                            int32_t nphys, int32_t num_blocks, int32_t H_kv,
-                                           int32_t kvh, int c, int g) {
+                                           int32_t kvh, int c, int g, int32_t last_ti = -1,
+                                           int32_t last_blk = 0) {
   using R = typename CacheT::raw;
   constexpr int X = 16 / sizeof(R);
   const R* kt;
   const R* vt;
   if constexpr (BS >= kBlock) {
     constexpr int kSubs = BS / kBlock;       // sub-blocks per block
-    const int64_t tile =
-        static_cast<int64_t>(safe_block(table[min(j / kSubs, nphys - 1)], num_blocks)) * H_kv + kvh;
+    const int32_t ti = min(j / kSubs, nphys - 1);
+    int32_t e;
+    if constexpr (kOverride) {
+      // read as constant memory so that the entry is a scalar load, as in the
+      // plain launch: the entries this launch writes are never taken from
+      // the table (ti == last_ti takes last_blk)
+      using ConstI32 = const __attribute__((address_space(4))) int32_t;
+      const int32_t loaded = ((ConstI32*)table)[ti];
+      e = ti == last_ti ? last_blk : loaded;
+    } else {
+      e = table[ti];
+    }
+    const int64_t tile = static_cast<int64_t>(safe_block(e, num_blocks)) * H_kv + kvh;
     const int tok0 = kBlock * (j % kSubs);   // first token of the sub-block in its block
     kt = k_cache + tile * (BS * D) + (tok0 + c) * X;
     vt = v_cache + tile * (BS * D) + c * BS + tok0 + 4 * g;
@@ -219,19 +246,86 @@ __device__ __forceinline__ void decode_merge_row(uint16_t* __restrict__ out,
   for (int i = 0; i < D / kWave; ++i) out[idx * D + lane + kWave * i] = f32_to_bf16(acc[i] * inv);
 }
 
+// The fused append + decode launch (pa_decode_step): sequence i's new token
+// (bf16 K/V rows [S][H_kv][D], flat slot slots[i], position
+// context_lens[i] - 1) is written into the cache by the work item that
+// attends that position, for its KV head, and the KV-head-0 item enters the
+// slot's block into row i of the block tables.
+template <typename CacheT>
+struct DecodeAppend {
+  const int32_t* slots = nullptr;
+  const uint16_t* k_new = nullptr;
+  const uint16_t* v_new = nullptr;
+  typename CacheT::raw* k_cache = nullptr;
+  typename CacheT::raw* v_cache = nullptr;
+  int32_t* tables = nullptr;
+  float k_inv = 1.f, v_inv = 1.f;  // fp8: reciprocal scales
+};
+
+template <typename CacheT>
+__device__ __forceinline__ typename CacheT::raw encode_new(uint16_t x, float inv) {
+  if constexpr (sizeof(typename CacheT::raw) == 1)
+    return f32_to_e4m3_sat(bf16_to_f32(x) * inv);
+  else
+    return x;
+}
+
+// One wave's share of a new token: lane l holds dims l*E .. l*E + E - 1
+// (E = D / 64) of the token's K row and V row, bf16, packed in kw and vw.
+template <int D>
+__device__ __forceinline__ void load_new_token(const uint16_t* __restrict__ k_new,
+                                               const uint16_t* __restrict__ v_new, int64_t row,
+                                               int lane, uint32_t& kw, uint32_t& vw) {
+  if constexpr (D == 128) {
+    kw = *reinterpret_cast<const uint32_t*>(k_new + row * D + 2 * lane);
+    vw = *reinterpret_cast<const uint32_t*>(v_new + row * D + 2 * lane);
+  } else {
+    kw = k_new[row * D + lane];
+    vw = v_new[row * D + lane];
+  }
+}
+
+// Stores the wave's share of a new token into slot `off` of cache tile
+// `tile` (= block * H_kv + KV head): K [D/x][16][x], V [D][16].
+template <typename CacheT, int D>
+__device__ __forceinline__ void store_new_token(const DecodeAppend<CacheT>& ap, int64_t tile,
+                                                int off, int lane, uint32_t kw, uint32_t vw) {
+  using CR = typename CacheT::raw;
+  constexpr int X = 16 / sizeof(CR);
+  constexpr int NCH = D / X;
+  constexpr int E = D / kWave;
+  const int d = E * lane;
+  CR* kd = ap.k_cache + ((tile * NCH + d / X) * kBlock + off) * X + d % X;
+  CR* vd = ap.v_cache + (tile * D + d) * kBlock + off;
+  if constexpr (E == 2) {
+    const CR k0 = encode_new<CacheT>(static_cast<uint16_t>(kw), ap.k_inv);
+    const CR k1 = encode_new<CacheT>(static_cast<uint16_t>(kw >> 16), ap.k_inv);
+    if constexpr (sizeof(CR) == 2)
+      *reinterpret_cast<uint32_t*>(kd) = static_cast<uint32_t>(k0) | (static_cast<uint32_t>(k1) << 16);
+    else
+      *reinterpret_cast<uint16_t*>(kd) = static_cast<uint16_t>(k0 | (k1 << 8));
+    vd[0] = encode_new<CacheT>(static_cast<uint16_t>(vw), ap.v_inv);
+    vd[kBlock] = encode_new<CacheT>(static_cast<uint16_t>(vw >> 16), ap.v_inv);
+  } else {
+    kd[0] = encode_new<CacheT>(static_cast<uint16_t>(kw), ap.k_inv);
+    vd[0] = encode_new<CacheT>(static_cast<uint16_t>(vw), ap.v_inv);
+  }
+}
+
 // Persistent work-group body (the kernel's comment above describes it).
 // kVarlen (the fused decode + prefill launch): a context cut into several
 // chunks is merged in-kernel by the last of its chunks to finish
 // (merge_counters: one per (sequence, KV head), zero before and after).
-template <typename CacheT, int D, int BS, bool kVarlen>
+template <typename CacheT, int D, int BS, bool kVarlen, bool kAppend = false>
 __device__ __attribute__((always_inline)) inline void decode_work(DecodeShared<D>& sh,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
-    const typename CacheT::raw* __restrict__ k_cache,
-    const typename CacheT::raw* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    int32_t max_blocks, int32_t num_blocks, const int32_t* __restrict__ context_lens, int32_t S,
-    int32_t H_q, int32_t H_kv, int32_t G, int32_t n_chunks, int32_t chunk_shift, float score_scale,
-    float out_scale, int32_t* __restrict__ counters, float* __restrict__ ws_ml, float* __restrict__ ws_o,
-    int32_t* __restrict__ merge_counters) {
+    const typename CacheT::raw* k_cache, const typename CacheT::raw* v_cache,
+    const int32_t* block_tables, int32_t max_blocks, int32_t num_blocks,
+    const int32_t* __restrict__ context_lens, int32_t S, int32_t H_q, int32_t H_kv, int32_t G,
+    int32_t n_chunks, int32_t chunk_shift, float score_scale, float out_scale,
+    int32_t* __restrict__ counters, float* __restrict__ ws_ml, float* __restrict__ ws_o,
+    int32_t* __restrict__ merge_counters, const DecodeAppend<CacheT>& ap = {}) {
+  static_assert(!kAppend || BS == kBlock, "the fused append takes 16-token blocks");
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -344,7 +438,33 @@ __device__ __attribute__((always_inline)) inline void decode_work(DecodeShared<D
   const int32_t nphys = (L + BS - 1) / BS;            // table entries in use
   const int32_t c0 = chunk << chunk_shift;
   const int32_t b1 = (chunk == n_chunks - 1) ? nblk : min(nblk, c0 + (1 << chunk_shift));
-  const int32_t* __restrict__ table = block_tables + static_cast<int64_t>(seq) * max_blocks;
+  // (no __restrict__ on the cache and table pointers: the fused append
+  // writes through other pointers to the same memory)
+  const int32_t* table = block_tables + static_cast<int64_t>(seq) * max_blocks;
+
+  // fused append: the item that holds position L - 1 (its last chunk)
+  // writes the new token.  Only the wave with the item's last step reads
+  // that position's block (no other step's pair reaches block b1 - 1), so
+  // that wave alone stores the token's K/V, just before the step's loads:
+  // its own later loads of the same addresses see the stores, and no other
+  // wave waits.  The token's rows and its slot are loaded here and used
+  // only at that step (the slot decides the block, which that step takes
+  // from the slot instead of the table); the KV-head-0 item enters the block
+  // into the table once the item is done.
+  int32_t last_ti = -1, app_slot = -1;
+  bool app_item = false;
+  uint32_t app_k = 0, app_v = 0;
+  if constexpr (kAppend) {
+    const int32_t raw = context_lens[seq];
+    if (chunk == n_valid - 1 && raw >= 1 && raw <= max_blocks * kBlock) {
+      app_item = true;
+      last_ti = (raw - 1) / kBlock;
+      app_slot = ap.slots[seq];
+      if (wave == ((b1 - c0 + 1) / 2 - 1) % kDecodeWaves)
+        load_new_token<D>(ap.k_new, ap.v_new, static_cast<int64_t>(seq) * H_kv + kvh, lane,
+                          app_k, app_v);
+    }
+  }
 
   // Q^T operand: column c = head kvh*G + c, zero for padded columns.
   bf16x8 qb[D / 32];
@@ -462,10 +582,26 @@ __device__ __attribute__((always_inline)) inline void decode_work(DecodeShared<D
   const int32_t n_steps = (b1 - c0 + 1) / 2;
   for (int32_t st = wave; st < n_steps; st += kDecodeWaves) {
     const int32_t p = c0 + 2 * st;
+    int32_t ov_ti = -1, ov_blk = 0;  // table entry taken from the slot at this step
+    if constexpr (kAppend) {
+      if (app_item && st == n_steps - 1) {
+        const int32_t sl = __builtin_amdgcn_readfirstlane(app_slot);
+        if (sl >= 0 && sl < num_blocks * kBlock) {
+          ov_ti = last_ti;
+          ov_blk = sl / kBlock;
+          store_new_token<CacheT, D>(ap, static_cast<int64_t>(ov_blk) * H_kv + kvh, sl % kBlock,
+                                     lane, app_k, app_v);
+          // keeps the compiler from moving this step's cache loads above
+          // the stores (the loads go through another pointer)
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
+      }
+    }
     BlockRegs<CacheT, D> xa, xb;
-    load_block<CacheT, D, BS>(xa, k_cache, v_cache, table, p, nphys, num_blocks, H_kv, kvh, c, g);
-    load_block<CacheT, D, BS>(xb, k_cache, v_cache, table, min(p + 1, b1 - 1), nphys, num_blocks,
-                              H_kv, kvh, c, g);
+    load_block<CacheT, D, BS, kAppend>(xa, k_cache, v_cache, table, p, nphys, num_blocks, H_kv,
+                                       kvh, c, g, ov_ti, ov_blk);
+    load_block<CacheT, D, BS, kAppend>(xb, k_cache, v_cache, table, min(p + 1, b1 - 1), nphys,
+                                       num_blocks, H_kv, kvh, c, g, ov_ti, ov_blk);
     compute(xa, xb, p);
   }
 
@@ -473,6 +609,10 @@ __device__ __attribute__((always_inline)) inline void decode_work(DecodeShared<D
   // work-group that runs ahead takes the next item and the queue balances
   // (taking it earlier would bind it to this work-group behind a long item)
   if (tid == 0) next = atomicAdd(&counters[0], 1);
+  if constexpr (kAppend) {
+    if (app_item && kvh == 0 && tid == 0 && app_slot >= 0 && app_slot < num_blocks * kBlock)
+      ap.tables[static_cast<int64_t>(seq) * max_blocks + last_ti] = app_slot / kBlock;
+  }
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
   // lane (c, g) holds o^T[d = 16t + 4g + r][head c]; a wave without steps
@@ -547,13 +687,13 @@ __device__ __attribute__((always_inline)) inline void decode_work(DecodeShared<D
 }
 
 // The last work-group of a persistent launch to finish resets the ticket
-// counters for the next call.
-__device__ __forceinline__ void decode_finish(int32_t* __restrict__ counters) {
+// counters (and any further words of the launch's counter region, up to
+// `words`) for the next call.
+__device__ __forceinline__ void decode_finish(int32_t* __restrict__ counters, int words = 2) {
   if (threadIdx.x == 0) {
     const int32_t done = atomicAdd(&counters[1], 1);
     if (done == static_cast<int32_t>(gridDim.x) - 1) {
-      atomicExch(&counters[0], 0);
-      atomicExch(&counters[1], 0);
+      for (int w = 0; w < words; ++w) atomicExch(&counters[w], 0);
     }
   }
 }

@@ -22,6 +22,7 @@ enum KernelId {
   kStage,
   kStageCacheWrite,
   kVarlen,
+  kDecodeStep,
   kKernelCount
 };
 

@@ -44,7 +44,8 @@ Track g_tracks[kKernelCount];
 
 const char* kNames[kKernelCount] = {"cache_write",   "decode",  "decode_merge",
                                     "prefill",       "prefill_merge", "generic",
-                                    "stage",         "stage_cache_write", "varlen"};
+                                    "stage",         "stage_cache_write", "varlen",
+                                    "decode_step"};
 
 }  // namespace
 

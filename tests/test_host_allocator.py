@@ -282,6 +282,48 @@ def test_decode_append_argument_checks_on_host():
     assert call(n=0) == 0                                        # nothing to do
 
 
+def test_decode_step_argument_checks_on_host():
+    fake = 0x1000
+    lib = pa._pa._lib
+    names = ["stream", "dst", "src", "nbytes", "slot_off", "lens_off", "k", "v", "new_dt", "out",
+             "out_dt", "q", "q_dt", "kc", "vc", "cache_dt", "tables", "max_blocks", "num_blocks",
+             "S", "h_q", "h_kv", "d", "bs", "max_ctx", "sm_scale", "k_scale", "v_scale", "ws",
+             "ws_bytes"]
+    # 4 sequences, 16/2 heads, d 64, bf16 throughout; a workspace large enough
+    need = pa.pa_decode_workspace_bytes(4, 16, 2, 64, 100)
+    ok = [None, fake, fake, 32, 0, 16, fake, fake, 1, fake, 1, fake, 1, fake, fake, 1, fake, 8,
+          10, 4, 16, 2, 64, 16, 100, 0.125, 1.0, 1.0, fake, need]
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return lib.pa_decode_step(*args)
+
+    # all rejected before any HIP call
+    assert call(bs=8) == pa.PA_ERR_INVALID
+    assert call(S=2049) == pa.PA_ERR_INVALID                     # lengths kept in LDS
+    assert call(h_q=48, h_kv=2) == pa.PA_ERR_INVALID             # 24 query heads per KV head
+    assert call(d=96) == pa.PA_ERR_INVALID
+    assert call(new_dt=0) == pa.PA_ERR_INVALID                   # f32 new K/V
+    assert call(q_dt=0) == pa.PA_ERR_INVALID
+    assert call(cache_dt=0) == pa.PA_ERR_INVALID
+    assert call(cache_dt=2, k_scale=0.0) == pa.PA_ERR_INVALID    # fp8 scales
+    assert call(sm_scale=float("nan")) == pa.PA_ERR_INVALID
+    assert call(max_blocks=0) == pa.PA_ERR_INVALID
+    assert call(max_ctx=0) == pa.PA_ERR_INVALID
+    assert call(lens_off=6) == pa.PA_ERR_INVALID                 # misaligned
+    assert call(lens_off=24) == pa.PA_ERR_INVALID                # 4 lengths do not fit 32 bytes
+    assert "do not fit" in pa.pa_last_error()
+    assert call(slot_off=20) == pa.PA_ERR_INVALID
+    assert call(tables=None) == pa.PA_ERR_INVALID
+    assert call(dst=None) == pa.PA_ERR_INVALID
+    assert call(k=None) == pa.PA_ERR_INVALID
+    assert call(ws=None) == pa.PA_ERR_WORKSPACE
+    assert call(ws_bytes=need - 4) == pa.PA_ERR_WORKSPACE
+    assert call(S=0, nbytes=0) == 0                              # nothing to do
+
+
 def test_prefix_sharing_golden_trace_through_c_abi():
     g = json.load(open(os.path.join(GOLDEN, "prefix_sharing_trace.json")))
     st_, pool = pa.pa_pool_create(g["num_blocks"], g["block_size"], g["initial_free_order"])
