@@ -420,8 +420,9 @@ def pmc_prefill_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_
         "write_ratio": round(write / alg_write, 3),
         "hbm_bytes": int(read + write),
         "prefill_kernel_only": {"hbm_read_bytes": int(read_k), "hbm_write_bytes": int(write_k)},
-        "split_partials_note": "slices whose key range is split write fp32 partials that the "
-                               "merge kernel reads back; the algorithmic count leaves them out",
+        "split_partials_note": "slices whose key range is split write partial states (fp16 "
+                               "normalised outputs + fp32 (m, l)) that the merge kernel reads "
+                               "back; the algorithmic count leaves them out",
         "kernel_source_digest": prefill_source_digest(),
     }, indent=1))
 

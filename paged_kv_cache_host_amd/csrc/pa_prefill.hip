@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
     const typename CacheT::raw* __restrict__ k_cache,
     const typename CacheT::raw* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     int32_t max_blocks, int32_t num_blocks, int32_t H_q, PfGeom geo, float score_scale,
-    float v_scale, float* __restrict__ ws_ml, float* __restrict__ ws_o, int32_t ws_rows) {
+    float v_scale, float* __restrict__ ws_ml, uint16_t* __restrict__ ws_o, int32_t ws_rows) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * stage_bytes<D>()];
   prefill_block<CacheT, D, false>(smem, blockIdx.x, blockIdx.y, out, q, cu_q_lens, start_pos,
                                   k_cache, v_cache, block_tables, max_blocks, num_blocks, H_q, geo,
@@ -81,7 +81,7 @@ template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(
     uint16_t* __restrict__ out, const int32_t* __restrict__ cu_q_lens, int32_t n_chunks,
     int32_t H_q, int32_t n_split, const float* __restrict__ ws_ml,
-    const float* __restrict__ ws_o, int32_t ws_rows, float v_scale) {
+    const uint16_t* __restrict__ ws_o, int32_t ws_rows, float v_scale) {
   constexpr int T = D / 4;
   const int sub = threadIdx.x % T;
   const int64_t pair = static_cast<int64_t>(blockIdx.x) * (256 / T) + threadIdx.x / T;
@@ -109,13 +109,14 @@ pa_status launch_prefill_mfma(hipStream_t st, void* out, const void* q, const in
                 static_cast<long long>(gx), n_chunks);
   const int32_t ws_rows = n_chunks * max_q_len;
   float* ws_ml = nullptr;
-  float* ws_o = nullptr;
+  uint16_t* ws_o = nullptr;
   if (geo.n_split > 1) {
-    const size_t need = static_cast<size_t>(geo.n_split) * ws_rows * H_q * (D + 2) * sizeof(float);
+    // [normalised partial outputs, fp16][partial (m, l), fp32]
+    const size_t need = static_cast<size_t>(geo.n_split) * ws_rows * H_q * pf_slot_bytes(D);
     if (!ws || ws_bytes < need)
       return fail(PA_ERR_WORKSPACE, "pa_prefill_chunk: workspace %zu bytes < %zu", ws_bytes, need);
-    ws_o = static_cast<float*>(ws);
-    ws_ml = ws_o + static_cast<size_t>(geo.n_split) * ws_rows * H_q * D;
+    ws_o = static_cast<uint16_t*>(ws);
+    ws_ml = reinterpret_cast<float*>(ws_o + static_cast<size_t>(geo.n_split) * ws_rows * H_q * D);
   }
   hipError_t e = launch(kPrefill, prefill_kernel<CacheT, D>,
                         dim3(static_cast<uint32_t>(gx), n_chunks), dim3(kPfThreads), 0, st,

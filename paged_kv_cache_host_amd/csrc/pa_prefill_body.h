@@ -69,6 +69,13 @@ PfGeom pf_geometry(int32_t n_chunks, int32_t max_q_len, int32_t H_q, int32_t H_k
   return g;
 }
 
+// Bytes of one split partial of one (row, head): its output normalised by
+// its own weight sum as fp16 (the values are weighted means of V, which the
+// kernel already holds in fp16, so the range is V's), then (m, l) as fp32.
+inline size_t pf_slot_bytes(int32_t D) {
+  return static_cast<size_t>(D) * sizeof(uint16_t) + 2 * sizeof(float);
+}
+
 // Bytes of split partials that any launch with at most n_chunks slices of
 // at most max_q_len queries (keys up to max_context_len) can need: the
 // split count grows as the batch shrinks, so a smaller batch may need more
@@ -88,7 +95,7 @@ inline size_t pf_partials_bound(int32_t n_chunks, int32_t max_q_len, int32_t H_q
     if (tiles <= 0) break;
     best = std::max(best, s * std::min(rows_max, tiles * ppg));
   }
-  return static_cast<size_t>(best) * H_q * (D + 2) * sizeof(float);
+  return static_cast<size_t>(best) * H_q * pf_slot_bytes(D);
 }
 
 
@@ -252,8 +259,9 @@ struct TileLoader {
 // merge kernel and the fused launch's in-kernel merge (same arithmetic, so
 // the two give identical bits).  Partial j of the pair sits at
 // slot = j * stride + pair: ws_ml[2 slot] = m (base-2 running maximum),
-// ws_ml[2 slot + 1] = l (weight sum), ws_o[slot * D ..] = unnormalised
-// output; a partial with l = 0 saw no key and is skipped.
+// ws_ml[2 slot + 1] = l (weight sum), ws_o[slot * D ..] = output / l as
+// fp16; a partial with l = 0 saw no key and is skipped.  Merged:
+//   M = max_j m_j,  W_j = 2^(m_j - M) l_j,  out = sum_j W_j o_j / sum_j W_j.
 __device__ __forceinline__ float pf_merge_max(const float* __restrict__ ws_ml, int64_t pair,
                                               int64_t stride, int n_split) {
   float M = -__builtin_inff();
@@ -264,7 +272,11 @@ __device__ __forceinline__ float pf_merge_max(const float* __restrict__ ws_ml, i
   return M;
 }
 
-// v_scale / (sum of the partials' weight sums against M), or 0 if none
+__device__ __forceinline__ float pf_merge_weight(float m, float l, float M) {
+  return __builtin_amdgcn_exp2f(m - M) * l;
+}
+
+// v_scale / (sum of the partials' weights W_j), or 0 if none
 __device__ __forceinline__ float pf_merge_inv(const float* __restrict__ ws_ml, int64_t pair,
                                               int64_t stride, int n_split, float M,
                                               float v_scale) {
@@ -272,23 +284,41 @@ __device__ __forceinline__ float pf_merge_inv(const float* __restrict__ ws_ml, i
   for (int j = 0; j < n_split; ++j) {
     const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * (j * stride + pair));
     if (!(ml.y > 0.f)) continue;
-    L += __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
+    L += pf_merge_weight(ml.x, ml.y, M);
   }
   return L > 0.f ? v_scale / L : 0.f;
 }
 
-// dimensions d0 .. d0 + 3 of the merged unnormalised output
+// 4 normalised partial values as stored (fp16, round to nearest even), and
+// back (exact)
+__device__ __forceinline__ u32x2 pf_pack_f16x4(const f32x4& v) {
+  u32x2 w;
+  w[0] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[0]))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[1]))) << 16);
+  w[1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[2]))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[3]))) << 16);
+  return w;
+}
+
+__device__ __forceinline__ f32x4 pf_unpack_f16x4(u32x2 w) {
+  return f32x4{static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[0]))),
+               static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[0] >> 16))),
+               static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[1]))),
+               static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[1] >> 16)))};
+}
+
+// dimensions d0 .. d0 + 3 of sum_j W_j o_j
 template <int D>
 __device__ __forceinline__ f32x4 pf_merge_dims4(const float* __restrict__ ws_ml,
-                                                const float* __restrict__ ws_o, int64_t pair,
+                                                const uint16_t* __restrict__ ws_o, int64_t pair,
                                                 int64_t stride, int n_split, float M, int d0) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < n_split; ++j) {
     const int64_t slot = j * stride + pair;
     const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * slot);
     if (!(ml.y > 0.f)) continue;
-    const float w = __builtin_amdgcn_exp2f(ml.x - M);
-    acc += w * *reinterpret_cast<const f32x4*>(ws_o + slot * D + d0);
+    const float w = pf_merge_weight(ml.x, ml.y, M);
+    acc += w * pf_unpack_f16x4(*reinterpret_cast<const u32x2*>(ws_o + slot * D + d0));
   }
   return acc;
 }
@@ -321,7 +351,7 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
     const typename CacheT::raw* __restrict__ k_cache,
     const typename CacheT::raw* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     int32_t max_blocks, int32_t num_blocks, int32_t H_q, PfGeom geo, float score_scale,
-    float v_scale, float* __restrict__ ws_ml, float* __restrict__ ws_o, int32_t ws_rows,
+    float v_scale, float* __restrict__ ws_ml, uint16_t* __restrict__ ws_o, int32_t ws_rows,
     int32_t* __restrict__ merge_counters) {
   constexpr int NKS = D / 16;  // 16-dim MFMA steps of Q K^T
   constexpr int NDT = D / 32;  // 32-dim tiles of O^T
@@ -702,16 +732,18 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
   // split key range: this work-group's partial softmax state
   const int64_t wrow = row - rbase;   // row inside the workspace
   const bool ws_ok = row_ok && wrow < ws_rows;
+  // (the output normalised by this split's own weight sum, as fp16)
   if (ws_ok) {
+    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t slot = (static_cast<int64_t>(split) * ws_rows + wrow) * H_q + head;
-    float* po = ws_o + slot * D;
+    uint16_t* po = ws_o + slot * D;
 #pragma unroll
     for (int n = 0; n < NDT; ++n)
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
         const int d = 32 * n + 8 * jq + 4 * g;
-        *reinterpret_cast<f32x4*>(po + d) =
-            f32x4{o[n][4 * jq], o[n][4 * jq + 1], o[n][4 * jq + 2], o[n][4 * jq + 3]};
+        *reinterpret_cast<u32x2*>(po + d) = pf_pack_f16x4(
+            f32x4{o[n][4 * jq], o[n][4 * jq + 1], o[n][4 * jq + 2], o[n][4 * jq + 3]} * inv_l);
       }
     if (g == 0) {
       ws_ml[2 * slot] = m_run;
@@ -747,8 +779,8 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
     if (!last || !ws_ok) return;
     // The merge of the pf_merge_* helpers (same operations in the same
     // order, so the same bits as the merge kernel), arranged for latency:
-    // this work-group's own partial comes from its registers (the values
-    // it wrote), and each other split's 16-byte pieces are loaded together.
+    // each split's pieces (this work-group's own as it stored them) are
+    // loaded together.
     const int64_t stride = static_cast<int64_t>(ws_rows) * H_q;
     const int64_t pair = wrow * H_q + head;
     // (m, l) of every split, loaded without branches so that the loads are
@@ -759,8 +791,8 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
     for (int j = 0; j < kPfMaxSplit; ++j) {
       const int jj = min(j, geo.n_split - 1);
       const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * (jj * stride + pair));
-      mj[j] = j == split ? m_run : ml.x;
-      lj[j] = j >= geo.n_split ? 0.f : (j == split ? l_tot : ml.y);
+      mj[j] = ml.x;
+      lj[j] = j >= geo.n_split ? 0.f : ml.y;
     }
     float M = -__builtin_inff();
 #pragma unroll
@@ -769,7 +801,7 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
     float L = 0.f;
 #pragma unroll
     for (int j = 0; j < kPfMaxSplit; ++j)
-      if (j < geo.n_split && lj[j] > 0.f) L += __builtin_amdgcn_exp2f(mj[j] - M) * lj[j];
+      if (j < geo.n_split && lj[j] > 0.f) L += pf_merge_weight(mj[j], lj[j], M);
     const float inv = L > 0.f ? v_scale / L : 0.f;
     f32x4 acc[NDT][4];
 #pragma unroll
@@ -778,27 +810,18 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
       for (int jq = 0; jq < 4; ++jq) acc[n][jq] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < geo.n_split; ++j) {
       if (!(lj[j] > 0.f)) continue;
-      const float w = __builtin_amdgcn_exp2f(mj[j] - M);
-      if (j == split) {
+      const float w = pf_merge_weight(mj[j], lj[j], M);
+      const uint16_t* po = ws_o + (j * stride + pair) * D;
+      u32x2 v[NDT][4];
 #pragma unroll
-        for (int n = 0; n < NDT; ++n)
+      for (int n = 0; n < NDT; ++n)
 #pragma unroll
-          for (int jq = 0; jq < 4; ++jq)
-            acc[n][jq] += w * f32x4{o[n][4 * jq], o[n][4 * jq + 1], o[n][4 * jq + 2],
-                                    o[n][4 * jq + 3]};
-      } else {
-        const float* po = ws_o + (j * stride + pair) * D;
-        f32x4 v[NDT][4];
+        for (int jq = 0; jq < 4; ++jq)
+          v[n][jq] = *reinterpret_cast<const u32x2*>(po + 32 * n + 8 * jq + 4 * g);
 #pragma unroll
-        for (int n = 0; n < NDT; ++n)
+      for (int n = 0; n < NDT; ++n)
 #pragma unroll
-          for (int jq = 0; jq < 4; ++jq)
-            v[n][jq] = *reinterpret_cast<const f32x4*>(po + 32 * n + 8 * jq + 4 * g);
-#pragma unroll
-        for (int n = 0; n < NDT; ++n)
-#pragma unroll
-          for (int jq = 0; jq < 4; ++jq) acc[n][jq] += w * v[n][jq];
-      }
+        for (int jq = 0; jq < 4; ++jq) acc[n][jq] += w * pf_unpack_f16x4(v[n][jq]);
     }
     uint16_t* orow = out + (row * H_q + head) * D;
 #pragma unroll

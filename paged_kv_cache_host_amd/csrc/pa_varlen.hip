@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(
     int32_t dec_max_blocks, const int32_t* __restrict__ pf_tables, int32_t pf_max_blocks,
     int32_t num_blocks, int32_t n_decode, int32_t H_q, int32_t H_kv,
     PfGeom geo, int32_t pf_gx, int32_t pf_items, float* __restrict__ pf_ws_ml,
-    float* __restrict__ pf_ws_o, int32_t pf_ws_rows, int32_t dec_chunks, int32_t dec_shift,
+    uint16_t* __restrict__ pf_ws_o, int32_t pf_ws_rows, int32_t dec_chunks, int32_t dec_shift,
     float* __restrict__ dec_ws_ml, float* __restrict__ dec_ws_o, float score_scale,
     float v_scale, int32_t* __restrict__ counters, int32_t* __restrict__ dec_merge,
     int32_t* __restrict__ pf_merge) {
@@ -94,8 +94,7 @@ VarlenPlan varlen_plan(int32_t n_decode, int32_t n_prefill, int32_t H_q, int32_t
     p.pf_groups = p.pf_items / p.geo.n_split;
     p.pf_ws_rows = n_prefill * max_q_len;
     if (p.geo.n_split > 1)
-      p.pf_bytes = static_cast<size_t>(p.geo.n_split) * p.pf_ws_rows * H_q * (D + 2) *
-                   sizeof(float);
+      p.pf_bytes = static_cast<size_t>(p.geo.n_split) * p.pf_ws_rows * H_q * pf_slot_bytes(D);
   } else {
     p.geo = PfGeom{H_kv, H_q / H_kv, 1, 1, 1, 0, 1};
   }
@@ -139,8 +138,9 @@ pa_status launch_varlen(hipStream_t st, const VarlenPlan& p, void* out, const vo
   char* base = static_cast<char*>(ws);
   float* dec_ws_ml = reinterpret_cast<float*>(base);
   float* dec_ws_o = dec_ws_ml + static_cast<int64_t>(n_decode) * H_q * p.dec_chunks * 2;
-  float* pf_ws_o = reinterpret_cast<float*>(base + p.dec_bytes);
-  float* pf_ws_ml = pf_ws_o + static_cast<int64_t>(p.geo.n_split) * p.pf_ws_rows * H_q * D;
+  uint16_t* pf_ws_o = reinterpret_cast<uint16_t*>(base + p.dec_bytes);
+  float* pf_ws_ml = reinterpret_cast<float*>(
+      pf_ws_o + static_cast<int64_t>(p.geo.n_split) * p.pf_ws_rows * H_q * D);
   // decode-only work-groups: one per compute unit (the kernel's LDS admits
   // one work-group per unit), none when there are no decode rows
   const int64_t grid = p.pf_items + (n_decode > 0 ? device_cus() : 0);
