@@ -630,6 +630,14 @@ pa_status pa_decode_step(void* stream, int32_t* dst, const void* src_host, size_
                          int32_t bs, int32_t max_context_len, float sm_scale, float k_scale,
                          float v_scale, void* ws, size_t ws_bytes);
 
+/* pa_decode_step_set_spin_limit -- testing aid: the number of polls
+ * (each followed by a short sleep) a work-group of later pa_decode_step
+ * launches makes for the staged metadata before it takes no work and ends
+ * (default 65536).  A tiny limit forces that path, where work-group 0 and
+ * any work-group that did see the flag serve the whole queue; the results
+ * are the same.  polls < 1 is PA_ERR_INVALID.  Process-wide, host only. */
+pa_status pa_decode_step_set_spin_limit(int32_t polls);
+
 /* ------------------------------------------------------------------------
  * Kernel timing (instrumentation, off by default).  Each launch of a
  * selected kernel carries a pair of HIP events attached to the launch

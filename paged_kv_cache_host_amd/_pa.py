@@ -106,6 +106,7 @@ _SIGS = {
     "pa_decode_step": (_i32, [_vp, _vp, _vp, _sz, _sz, _sz, _vp, _vp, _i32, _vp, _i32, _vp,
                                _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i32, _i32, _f32, _f32, _f32, _vp, _sz]),
+    "pa_decode_step_set_spin_limit": (_i32, [_i32]),
     "pa_timing_enable": (_i32, [_i32, _i32]),
     "pa_timing_query": (_i32, [C.c_char_p, _i32p, C.POINTER(_f32), C.POINTER(_f32)]),
     "pa_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -607,6 +608,12 @@ def pa_decode_step(stream, dst, src_host, nbytes: int, slot_offset: int, lens_of
                                _dptr(block_tables), block_tables.shape[1], num_blocks, S, H_q,
                                H_kv, D, bs, max_context_len, sm_scale, k_scale, v_scale,
                                _dptr(ws), 0 if ws is None else ws.numel() * ws.element_size())
+
+
+def pa_decode_step_set_spin_limit(polls: int) -> int:
+    """Testing aid: polls a pa_decode_step work-group makes for the staged
+    metadata before it takes no work (default 65536)."""
+    return _lib.pa_decode_step_set_spin_limit(polls)
 
 
 def pa_decode_workspace_bytes(S: int, H_q: int, H_kv: int, D: int, max_context_len: int) -> int:

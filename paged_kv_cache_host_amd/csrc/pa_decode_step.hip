@@ -25,17 +25,21 @@
 // host read for the launch instead of one per work-group) and publishes the
 // copy through a flag in the workspace (agent-scope release); every other
 // work-group polls the flag (acquire) before it starts.  The poll is
-// bounded: a work-group that has not seen the flag after kStepSpins polls
+// bounded: a work-group that has not seen the flag after spin_limit polls
 // takes no work and ends (work-group 0 and the others drain the work
 // queue), so the launch ends whatever the order in which its work-groups
 // run.
 #include "pa_decode_body.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace pa {
 
 constexpr int32_t kStepSpins = 1 << 16;  // flag polls (each followed by a short sleep)
+
+// The poll limit the launches use (kStepSpins unless a test lowers it).
+static std::atomic<int32_t> g_step_spins{kStepSpins};
 // Sequences per launch: their lengths are kept in LDS (8 KiB, which keeps
 // the d = 64 kernel at two work-groups per CU).
 constexpr int32_t kStepMaxSeqs = 2048;
@@ -53,7 +57,7 @@ struct StepShared {
 template <typename CacheT, int D>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     int32_t* dst, const int32_t* src, int32_t n_words, int32_t slot_word, int32_t lens_word,
-    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, typename CacheT::raw* k_cache,
+    int32_t spin_limit, uint16_t* __restrict__ out, const uint16_t* __restrict__ q, typename CacheT::raw* k_cache,
     typename CacheT::raw* v_cache, int32_t* block_tables, int32_t max_blocks, int32_t num_blocks,
     int32_t S, int32_t H_q, int32_t H_kv, int32_t G, int32_t n_chunks, int32_t chunk_shift,
     float score_scale, float out_scale, const uint16_t* __restrict__ k_new,
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     } else {
       if (tid == 0) {
         int32_t ok = 0;
-        for (int32_t n = 0; n < kStepSpins; ++n) {
+        for (int32_t n = 0; n < spin_limit; ++n) {
           ok = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (ok) break;
           __builtin_amdgcn_s_sleep(1);
@@ -163,7 +167,9 @@ static pa_status launch_step(hipStream_t st, const StepArgs& a) {
   const float v_inv = fp8 ? 1.0f / a.v_scale : 1.f;
   hipError_t e = launch(kDecodeStep, decode_step_kernel<CacheT, D>,
                         dim3(step_work_groups<CacheT, D>()), dim3(kThreads), 0, st, a.dst, a.src,
-                        a.n_words, a.slot_word, a.lens_word, static_cast<uint16_t*>(a.out),
+                        a.n_words, a.slot_word, a.lens_word,
+                        g_step_spins.load(std::memory_order_relaxed),
+                        static_cast<uint16_t*>(a.out),
                         static_cast<const uint16_t*>(a.q),
                         static_cast<typename CacheT::raw*>(a.k_cache),
                         static_cast<typename CacheT::raw*>(a.v_cache), a.tables, a.max_blocks,
@@ -271,4 +277,10 @@ extern "C" pa_status pa_decode_step(void* stream, int32_t* dst, const void* src_
   if (cache_dt == PA_BF16)
     return D == 128 ? launch_step<BF16, 128>(st, a) : launch_step<BF16, 64>(st, a);
   return D == 128 ? launch_step<FP8, 128>(st, a) : launch_step<FP8, 64>(st, a);
+}
+
+extern "C" pa_status pa_decode_step_set_spin_limit(int32_t polls) {
+  if (polls < 1) return fail(PA_ERR_INVALID, "pa_decode_step_set_spin_limit: polls=%d < 1", polls);
+  g_step_spins.store(polls, std::memory_order_relaxed);
+  return PA_OK;
 }

@@ -256,3 +256,63 @@ def test_decode_step_workspace_serves_smaller_calls():
             assert_close(out_to_f64(to_host_raw(out, "bf16"), "bf16"), ref, "bf16",
                          f"batch {i} rep {rep}")
             assert int(ws[:64].view(torch.int32)[:3].abs().sum()) == 0
+
+
+def test_decode_step_bounded_wait_path():
+    """With the poll limit lowered to one poll, the work-groups that do not
+    see the staged metadata at once take no work and end; work-group 0 (and
+    any that did see it) serve the whole queue.  Results as the oracle's
+    over three iterations, with a context long enough to span chunks."""
+    b = StepBatch(5500, [3, 700, 2049, 16, 15, 90, 4097, 1], 16, 2, 128, "bf16", steps=3)
+    ws = decode_workspace(b.S, b.h_q, b.h_kv, 128, int(b.lengths.max()) + 3, DEV)
+    assert pa.pa_decode_step_set_spin_limit(1) == pa.PA_OK
+    try:
+        for it in range(3):
+            slots, k, v, q = b.next_tokens()
+            host, slot_off, lens_off, nbytes = _meta(b.S, slots, b.lens, pad=it)
+            dst = torch.zeros(nbytes // 4, dtype=torch.int32, device=DEV)
+            out = torch.full((b.S, b.h_q, 128), SENTINEL, dtype=torch.bfloat16, device=DEV)
+            say(f"[decode step, one poll] iteration {it}")
+            assert pa.pa_decode_step(None, dst, host, nbytes, slot_off, lens_off,
+                                     to_device_raw(k, "bf16", DEV),
+                                     to_device_raw(v, "bf16", DEV), out,
+                                     to_device_raw(q, "bf16", DEV), b.k_dev, b.v_dev, b.tab_dev,
+                                     b.nb, b.h_kv, int(b.lens.max()), b.sm, KS, VS,
+                                     ws) == pa.PA_OK
+            torch.cuda.synchronize()
+            ref, _ = b.oracle_step(slots, k, v, q)
+            assert_close(out_to_f64(to_host_raw(out, "bf16"), "bf16"), ref, "bf16",
+                         f"one poll, iteration {it}")
+            assert np.array_equal(dst.cpu().numpy(), host.numpy())
+            assert int(ws[:64].view(torch.int32)[:3].abs().sum()) == 0
+    finally:
+        assert pa.pa_decode_step_set_spin_limit(65536) == pa.PA_OK
+
+
+def test_decode_step_full_batch_wide_groups():
+    """The largest batch one launch takes (2048 sequences, lengths kept in
+    LDS) with 16 query heads per KV head and d = 64: short contexts from
+    empty up, two iterations, against the oracle."""
+    rng = np.random.default_rng(5600)
+    lengths = rng.integers(0, 48, size=2048)
+    lengths[:4] = [0, 15, 16, 47]
+    b = StepBatch(5601, lengths.tolist(), 32, 2, 64, "bf16", steps=2, extra_blocks=4)
+    ws = decode_workspace(b.S, b.h_q, b.h_kv, 64, int(b.lengths.max()) + 2, DEV)
+    for it in range(2):
+        slots, k, v, q = b.next_tokens()
+        host, slot_off, lens_off, nbytes = _meta(b.S, slots, b.lens, pad=1)
+        dst = torch.zeros(nbytes // 4, dtype=torch.int32, device=DEV)
+        out = torch.full((b.S, b.h_q, 64), SENTINEL, dtype=torch.bfloat16, device=DEV)
+        say(f"[decode step] 2048 sequences, 32/2 heads, d64, iteration {it}")
+        assert pa.pa_decode_step(None, dst, host, nbytes, slot_off, lens_off,
+                                 to_device_raw(k, "bf16", DEV), to_device_raw(v, "bf16", DEV),
+                                 out, to_device_raw(q, "bf16", DEV), b.k_dev, b.v_dev, b.tab_dev,
+                                 b.nb, b.h_kv, int(b.lens.max()), b.sm, KS, VS, ws) == pa.PA_OK
+        torch.cuda.synchronize()
+        ref, tables = b.oracle_step(slots, k, v, q)
+        assert_close(out_to_f64(to_host_raw(out, "bf16"), "bf16"), ref, "bf16",
+                     f"2048 sequences, iteration {it}")
+        got_t = b.tab_dev.cpu().numpy()
+        for s_ in range(b.S):
+            n = _blocks(b.lens[s_])
+            assert np.array_equal(got_t[s_, :n], tables[s_, :n]), (it, s_)

@@ -322,6 +322,9 @@ def test_decode_step_argument_checks_on_host():
     assert call(ws=None) == pa.PA_ERR_WORKSPACE
     assert call(ws_bytes=need - 4) == pa.PA_ERR_WORKSPACE
     assert call(S=0, nbytes=0) == 0                              # nothing to do
+    # the testing aid's limit is checked on the host
+    assert lib.pa_decode_step_set_spin_limit(0) == pa.PA_ERR_INVALID
+    assert lib.pa_decode_step_set_spin_limit(65536) == pa.PA_OK
 
 
 def test_prefix_sharing_golden_trace_through_c_abi():
