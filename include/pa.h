@@ -164,6 +164,37 @@ pa_status pa_seq_release(pa_pool* pool, int64_t seq);
 pa_status pa_seq_share(pa_pool* pool, int64_t seq, int64_t src, int32_t shared_tokens,
                        int32_t num_tokens, int32_t* shared_out);
 
+/* Prefix detection (ARTICLE 4.3: requests with the same system-prompt
+ * prefix reuse its blocks, and finding them is the scheduler's added
+ * work).  pa_seq_register_prefix declares that the K/V of positions
+ * 0 .. n_tokens-1 of `seq` are in the cache and that those positions hold
+ * the token ids tokens[0 .. n_tokens) [host]: each full block among them is
+ * registered under its content (the id of the block before it in seq's
+ * table, or none, and its block_size token ids), unless that content is
+ * already registered for another block, in which case registration stops
+ * there (lookups reach that other block).  A registered block leaves the
+ * index when the last table holding it is released.
+ * Errors (state unchanged): PA_ERR_UNKNOWN_SEQ; PA_ERR_INVALID for
+ * n_tokens outside [0, length of seq], NULL tokens, or a block of seq that
+ * is already registered under other token ids. */
+pa_status pa_seq_register_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens,
+                                 int32_t n_tokens);
+
+/* Create `seq` for a prompt of num_tokens token ids tokens [host]: its
+ * full blocks are matched from the first against the registered contents
+ * (the previous block matched, or none, and the block's token ids), every
+ * match is shared as by pa_seq_share, and the walk stops at the first block
+ * that does not match; the remaining blocks are taken fresh from the front
+ * of the free list.  *shared_out [host, optional] = tokens that live in
+ * shared blocks (their K/V are in the cache; the caller writes and
+ * prefills from there).  Errors (state unchanged): PA_ERR_EXISTS,
+ * PA_ERR_INVALID (num_tokens < 0, NULL tokens), PA_ERR_NO_BLOCKS. */
+pa_status pa_seq_create_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens,
+                               int32_t num_tokens, int32_t* shared_out);
+
+/* Number of registered blocks (-1 for a NULL pool). */
+int32_t pa_pool_num_registered(const pa_pool* pool);
+
 /* Number of sequences holding `block` (0: free) into *refs [host]. */
 pa_status pa_pool_block_refs(const pa_pool* pool, int32_t block, int32_t* refs);
 

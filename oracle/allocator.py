@@ -35,6 +35,20 @@ reuse one set of KV blocks, marked read-only).  Readings taken:
 * a block is counted once for every table that holds it and returns to the
   back of the free list when the last table holding it is released (in that
   table's order).
+
+Prefix detection (ARTICLE §4.3 names the prefix-match detection as the
+scheduler's added work; it gives no algorithm).  Readings taken:
+* a block can be found only after the caller declares its K/V computed
+  (``seq_register_prefix``); it is found by its content: the block before it
+  in the registering sequence's table (none for a first block) and its
+  ``block_size`` token ids, so a match of block i implies a match of every
+  earlier position;
+* a new sequence (``seq_create_prefix``) takes matched blocks from its first
+  full block on and stops at the first full block whose content is not
+  registered; the rest of its blocks are fresh, exactly as ``seq_share``;
+* content already registered for another block is not registered again
+  (registration of that sequence stops there); a block leaves the index when
+  it returns to the free list.
 """
 from __future__ import annotations
 
@@ -67,6 +81,8 @@ class BlockPool:
         self.tables: dict[int, list[int]] = {}
         self.lengths: dict[int, int] = {}
         self.refs = [0] * self.num_blocks   # tables holding each block
+        self.index: dict = {}               # (previous block, token ids) -> block
+        self.content: dict = {}             # block -> its key in the index
 
     # -- ARTICLE §2.2: allocate / free ---------------------------------------
     def _take(self, n: int):
@@ -81,6 +97,9 @@ class BlockPool:
         for b in ids:
             self.refs[b] -= 1
             if self.refs[b] == 0:
+                key = self.content.pop(b, None)
+                if key is not None:
+                    del self.index[key]
                 self.free.append(b)
 
     # -- sequence-level verbs -------------------------------------------------
@@ -120,6 +139,59 @@ class BlockPool:
         self.tables[seq] = head + fresh
         self.lengths[seq] = num_tokens
         return OK, n_shared * self.block_size
+
+    # -- ARTICLE §4.3: prefix detection ---------------------------------------
+    def seq_register_prefix(self, seq: int, tokens) -> int:
+        """Declare the K/V of positions 0 .. len(tokens)-1 of ``seq`` computed,
+        holding these token ids: index each full block among them by its
+        content."""
+        if seq not in self.tables:
+            return ERR_UNKNOWN_SEQ
+        tokens = [int(t) for t in tokens]
+        if len(tokens) > self.lengths[seq]:
+            return ERR_INVALID
+        table, bs = self.tables[seq], self.block_size
+        keys = []
+        for i in range(len(tokens) // bs):
+            keys.append((table[i - 1] if i else -1, tuple(tokens[i * bs:(i + 1) * bs])))
+        for b, key in zip(table, keys):
+            if b in self.content and self.content[b] != key:
+                return ERR_INVALID
+        for b, key in zip(table, keys):
+            if key in self.index:
+                if self.index[key] == b:
+                    continue
+                break
+            self.index[key] = b
+            self.content[b] = key
+        return OK
+
+    def seq_create_prefix(self, seq: int, tokens):
+        """Create ``seq`` for the prompt ``tokens``, sharing the leading full
+        blocks whose content is registered.  Returns (status, tokens that live
+        in shared blocks)."""
+        tokens = [int(t) for t in tokens]
+        if seq in self.tables:
+            return ERR_EXISTS, 0
+        bs = self.block_size
+        matched, parent = [], -1
+        for i in range(len(tokens) // bs):
+            b = self.index.get((parent, tuple(tokens[i * bs:(i + 1) * bs])))
+            if b is None:
+                break
+            matched.append(b)
+            parent = b
+        fresh = self._take(ceil_div(len(tokens), bs) - len(matched))
+        if fresh is None:
+            return ERR_NO_BLOCKS, 0
+        for b in matched:
+            self.refs[b] += 1
+        self.tables[seq] = matched + fresh
+        self.lengths[seq] = len(tokens)
+        return OK, len(matched) * bs
+
+    def num_registered(self) -> int:
+        return len(self.content)
 
     def block_refs(self, block: int) -> int:
         return self.refs[block]

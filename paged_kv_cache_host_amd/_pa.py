@@ -77,6 +77,9 @@ _SIGS = {
     "pa_seq_release": (_i32, [_vp, _i64]),
     "pa_seq_share": (_i32, [_vp, _i64, _i64, _i32, _i32, _i32p]),
     "pa_pool_block_refs": (_i32, [_vp, _i32, _i32p]),
+    "pa_seq_register_prefix": (_i32, [_vp, _i64, _i32p, _i32]),
+    "pa_seq_create_prefix": (_i32, [_vp, _i64, _i32p, _i32, _i32p]),
+    "pa_pool_num_registered": (_i32, [_vp]),
     "pa_seq_length": (_i32, [_vp, _i64, _i32p]),
     "pa_seq_block_table": (_i32, [_vp, _i64, _i32p, _i32, _i32p]),
     "pa_pack_batch": (_i32, [_vp, _i64p, _i32, _i32, _i32p, _i32p]),
@@ -228,6 +231,31 @@ def pa_seq_share(pool, seq: int, src: int, shared_tokens: int, num_tokens: int):
     out = _i32(0)
     st = _lib.pa_seq_share(pool, seq, src, shared_tokens, num_tokens, C.byref(out))
     return st, out.value
+
+
+def pa_seq_register_prefix(pool, seq: int, tokens, n_tokens: int | None = None) -> int:
+    """Register the full blocks among the first n_tokens (default: all of
+    ``tokens``) positions of ``seq`` under their token ids."""
+    t = _i32_array(tokens)
+    n = len(t) if n_tokens is None else int(n_tokens)
+    if n > len(t):
+        raise PaError(PA_ERR_INVALID, "pa_seq_register_prefix: n_tokens exceeds tokens")
+    return _lib.pa_seq_register_prefix(pool, seq, _ptr_i32(t) if len(t) else None, n)
+
+
+def pa_seq_create_prefix(pool, seq: int, tokens):
+    """Create ``seq`` for the prompt ``tokens``, sharing every leading full
+    block whose content is registered.  Returns (status, tokens that live
+    in shared blocks)."""
+    t = _i32_array(tokens)
+    out = _i32(0)
+    st = _lib.pa_seq_create_prefix(pool, seq, _ptr_i32(t) if len(t) else None, len(t),
+                                   C.byref(out))
+    return st, out.value
+
+
+def pa_pool_num_registered(pool) -> int:
+    return _lib.pa_pool_num_registered(pool)
 
 
 def pa_pool_block_refs(pool, block: int):

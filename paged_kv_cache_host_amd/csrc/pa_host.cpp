@@ -19,6 +19,17 @@
 // The free list is a ring buffer of int32 ids (capacity = pool size, so it
 // can never overflow: a block is either in the ring or held by one or more
 // tables).
+//
+// Prefix detection (ARTICLE §4.3: finding the requests that share a prefix
+// is the scheduler's added work).  A full block whose K/V the caller has
+// computed can be registered under its content: the id of the block before
+// it in the sequence (none for the first) and the token ids it holds.  A
+// new sequence created from its token ids walks its full blocks from the
+// first and takes every block whose content is registered, stopping at the
+// first that is not.  The chain through the previous block's id makes a
+// match cover all earlier positions, and keys are compared in full, so no
+// hash collision can produce a false match.  A block leaves the index when
+// the last table holding it is released.
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -39,6 +50,22 @@ struct Seq {
   int32_t len = 0;
 };
 
+// Content of a registered block: the previous block of the sequence that
+// registered it (-1 for a first block) and its token ids.
+struct BlockKey {
+  int32_t parent = -1;
+  std::vector<int32_t> tokens;
+  bool operator==(const BlockKey& o) const { return parent == o.parent && tokens == o.tokens; }
+};
+
+struct BlockKeyHash {
+  size_t operator()(const BlockKey& k) const {
+    uint64_t h = 1469598103934665603ull ^ static_cast<uint32_t>(k.parent);  // FNV-1a style mix
+    for (int32_t t : k.tokens) h = (h ^ static_cast<uint32_t>(t)) * 1099511628211ull;
+    return static_cast<size_t>(h ^ (h >> 29));
+  }
+};
+
 }  // namespace
 
 struct pa_pool {
@@ -49,6 +76,8 @@ struct pa_pool {
   int32_t count = 0;          // number of free ids
   std::vector<int32_t> refs;  // tables holding each block (0: free)
   std::unordered_map<int64_t, Seq> seqs;
+  std::unordered_map<BlockKey, int32_t, BlockKeyHash> index;  // registered content -> block
+  std::unordered_map<int32_t, BlockKey> registered;           // block -> its content
 
   int32_t at(int32_t i) const { return ring[(head + i) % num_blocks]; }
   // Take n ids from the front.  Caller has checked count >= n.
@@ -66,9 +95,20 @@ struct pa_pool {
   void give_back(const std::vector<int32_t>& ids) {
     for (int32_t b : ids) {
       if (--refs[b] > 0) continue;
+      auto r = registered.find(b);
+      if (r != registered.end()) {
+        index.erase(r->second);
+        registered.erase(r);
+      }
       ring[(head + count) % num_blocks] = b;
       ++count;
     }
+  }
+  BlockKey key_of(int32_t parent, const int32_t* tokens) const {
+    BlockKey k;
+    k.parent = parent;
+    k.tokens.assign(tokens, tokens + block_size);
+    return k;
   }
 };
 
@@ -200,6 +240,80 @@ pa_status pa_seq_share(pa_pool* pool, int64_t seq, int64_t src, int32_t shared_t
   pool->seqs.emplace(seq, std::move(s));
   if (shared_out) *shared_out = n_shared * pool->block_size;
   return PA_OK;
+}
+
+pa_status pa_seq_register_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens,
+                                 int32_t n_tokens) {
+  if (!pool) return fail(PA_ERR_INVALID, "pa_seq_register_prefix: pool is NULL");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_register_prefix: unknown sequence %lld",
+                (long long)seq);
+  const Seq& s = it->second;
+  if (n_tokens < 0 || n_tokens > s.len || (n_tokens > 0 && !tokens))
+    return fail(PA_ERR_INVALID, "pa_seq_register_prefix: n_tokens=%d outside [0, %d] or NULL",
+                n_tokens, s.len);
+  const int32_t bs = pool->block_size;
+  const int32_t n_full = n_tokens / bs;
+  // validate first (all or nothing): a block that is already registered
+  // must be registered under this content
+  for (int32_t i = 0; i < n_full; ++i) {
+    auto r = pool->registered.find(s.table[i]);
+    if (r != pool->registered.end() &&
+        !(r->second == pool->key_of(i ? s.table[i - 1] : -1, tokens + static_cast<int64_t>(i) * bs)))
+      return fail(PA_ERR_INVALID,
+                  "pa_seq_register_prefix: block %d of sequence %lld is registered with other "
+                  "token ids", i, (long long)seq);
+  }
+  for (int32_t i = 0; i < n_full; ++i) {
+    const int32_t b = s.table[i];
+    BlockKey k = pool->key_of(i ? s.table[i - 1] : -1, tokens + static_cast<int64_t>(i) * bs);
+    auto f = pool->index.find(k);
+    if (f != pool->index.end()) {
+      if (f->second == b) continue;  // this very block
+      break;  // the same content lives in another block: lookups go there
+    }
+    pool->registered.emplace(b, k);
+    pool->index.emplace(std::move(k), b);
+  }
+  return PA_OK;
+}
+
+pa_status pa_seq_create_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens,
+                               int32_t num_tokens, int32_t* shared_out) {
+  if (!pool) return fail(PA_ERR_INVALID, "pa_seq_create_prefix: pool is NULL");
+  if (num_tokens < 0 || (num_tokens > 0 && !tokens))
+    return fail(PA_ERR_INVALID, "pa_seq_create_prefix: num_tokens=%d or NULL tokens", num_tokens);
+  if (pool->seqs.count(seq))
+    return fail(PA_ERR_EXISTS, "pa_seq_create_prefix: sequence %lld exists", (long long)seq);
+  const int32_t bs = pool->block_size;
+  std::vector<int32_t> matched;
+  int32_t parent = -1;
+  for (int32_t i = 0; i < num_tokens / bs; ++i) {
+    auto f = pool->index.find(pool->key_of(parent, tokens + static_cast<int64_t>(i) * bs));
+    if (f == pool->index.end()) break;
+    matched.push_back(f->second);
+    parent = f->second;
+  }
+  const int64_t need = ceil_div64(num_tokens, bs) - static_cast<int64_t>(matched.size());
+  if (need > pool->count)
+    return fail(PA_ERR_NO_BLOCKS, "pa_seq_create_prefix: need %lld blocks, %d free",
+                (long long)need, pool->count);
+  Seq s;
+  s.table.reserve(matched.size() + static_cast<size_t>(need));
+  for (int32_t b : matched) {
+    s.table.push_back(b);
+    ++pool->refs[b];
+  }
+  pool->take(static_cast<int32_t>(need), s.table);
+  s.len = num_tokens;
+  pool->seqs.emplace(seq, std::move(s));
+  if (shared_out) *shared_out = static_cast<int32_t>(matched.size()) * bs;
+  return PA_OK;
+}
+
+int32_t pa_pool_num_registered(const pa_pool* pool) {
+  return pool ? static_cast<int32_t>(pool->registered.size()) : -1;
 }
 
 pa_status pa_pool_block_refs(const pa_pool* pool, int32_t block, int32_t* refs) {

@@ -121,3 +121,102 @@ def test_shared_prefix_decode_and_prefill(cache_dtype):
     assert pa.pa_seq_release(kv.pool, 0) == 0 and ref.seq_release(0) == oa.OK
     assert list(pa.pa_pool_free_list(kv.pool)[1]) == ref.free_list()
     kv.close()
+
+
+def test_detected_prefix_prefill_and_decode():
+    """Prefix detection (ARTICLE 4.3): requests that start with the same
+    200-token system prompt find its blocks by content.  Request 0 is
+    prefilled and its prompt registered; each later request is created from
+    its token ids, takes the matched full blocks, and writes and prefills
+    only from the first position past them (its prefill slice starts
+    there).  One request diverges inside the system prompt and shares only
+    the blocks before the divergence.  Tables, reference counts, the
+    registered count and the cache bytes equal the oracle pool's; every
+    prefill slice and a decode of all requests pass the gate against the
+    oracle.  Same tokens are taken to give the same K/V (the premise of
+    reusing them), so the K/V of a position are drawn once per distinct
+    token prefix."""
+    rng = np.random.default_rng(701)
+    sp = rng.integers(1, 50000, size=200).tolist()         # system prompt token ids
+    users = [rng.integers(1, 50000, size=n).tolist() for n in (40, 3, 77, 16)]
+    prompts = [sp + u for u in users]
+    div = sp[:100] + [7] + sp[101:]                          # diverges at position 100
+    prompts.append(div + users[0])
+    S = len(prompts)
+    nb = sum(-(-len(p) // BS) for p in prompts) + 4
+    order = rng.permutation(nb).astype(np.int32)
+    sm = float(np.float32(1.0) / np.float32(np.sqrt(D)))
+    say(f"[prefix detection] {S} requests, system prompt 200 tokens, pool {nb}")
+
+    kv = PagedKV(nb, H_KV, D, "bf16", DEV, order)
+    ref = oa.BlockPool(nb, BS, order.tolist())
+    kc, vc = oc.new_cache(nb, H_KV, BS, D, "bf16")
+    # K/V per distinct token prefix (position p of a prompt is identified by
+    # its first p+1 token ids)
+    kv_of = {}
+
+    def token_kv(prompt, p):
+        key = tuple(prompt[:p + 1])
+        if key not in kv_of:
+            kv_of[key] = (workloads.normal_raw(rng, (1, H_KV, D), "bf16"),
+                          workloads.normal_raw(rng, (1, H_KV, D), "bf16"))
+        return kv_of[key]
+
+    written = []
+    for i, prompt in enumerate(prompts):
+        st1 = pa.pa_seq_create_prefix(kv.pool, i, prompt)
+        st2 = ref.seq_create_prefix(i, prompt)
+        assert st1 == st2 and st1[0] == pa.PA_OK, (st1, st2)
+        shared = st1[1]
+        expect = 0 if i == 0 else (96 if i == S - 1 else 192)
+        assert shared == expect, (i, shared)
+        n = len(prompt) - shared
+        k_raw = np.concatenate([token_kv(prompt, p)[0] for p in range(shared, len(prompt))])
+        v_raw = np.concatenate([token_kv(prompt, p)[1] for p in range(shared, len(prompt))])
+        slots = kv.slots(i, shared, n)
+        assert list(slots) == ref.slots(i, shared, n)
+        kv.write(to_device_raw(k_raw, "bf16", DEV), to_device_raw(v_raw, "bf16", DEV),
+                 torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int32)).to(DEV))
+        oc.cache_write(kc, vc, k_raw, v_raw, list(slots), "bf16", "bf16")
+        written.append(n)
+        # the slice's prefill from the first unshared position
+        t_row, _ = kv.pack([i])
+        qp = workloads.normal_raw(rng, (n, H_Q, D), "bf16")
+        cu = torch.tensor([0, n], dtype=torch.int32, device=DEV)
+        st_ = torch.tensor([shared], dtype=torch.int32, device=DEV)
+        outp = filled((n, H_Q, D), torch.bfloat16, DEV)
+        wsp = prefill_workspace(1, n, H_Q, H_KV, D, len(prompt), DEV)
+        kv.prefill(outp, to_device_raw(qp, "bf16", DEV), cu, st_, torch.from_numpy(t_row).to(DEV),
+                   n, len(prompt), sm, wsp)
+        torch.cuda.synchronize()
+        gotp = out_to_f64(to_host_raw(outp.cpu(), "bf16"), "bf16")
+        wantp = oat.prefill_chunk(codecs.decode(qp, "bf16"), shared, kc, vc,
+                                  np.asarray(ref.block_table(i)), H_KV, sm, "bf16")
+        err = assert_close(gotp, wantp, "bf16", f"request {i} prefill from {shared}")
+        say(f"    request {i}: shared {shared}, wrote {n}, prefill max|d| = {err:.3g}")
+        # its prompt is now computed: register it for the next requests
+        assert pa.pa_seq_register_prefix(kv.pool, i, prompt) == ref.seq_register_prefix(i, prompt)
+        assert pa.pa_pool_num_registered(kv.pool) == ref.num_registered()
+
+    for b in range(nb):
+        assert pa.pa_pool_block_refs(kv.pool, b)[1] == ref.block_refs(b)
+    assert sum(written) < sum(len(p) for p in prompts) - 3 * 192
+    tables, lens = kv.pack(list(range(S)))
+    rt, rl = ref.pack(list(range(S)), tables.shape[1])
+    assert tables.tolist() == rt and lens.tolist() == rl
+    assert np.array_equal(to_host_raw(kv.k, "bf16"), kc) and \
+        np.array_equal(to_host_raw(kv.v, "bf16"), vc), "cache bytes differ"
+
+    q_dec = workloads.normal_raw(rng, (S, H_Q, D), "bf16")
+    out = filled((S, H_Q, D), torch.bfloat16, DEV)
+    mc = int(lens.max())
+    ws = decode_workspace(S, H_Q, H_KV, D, mc, DEV)
+    kv.decode(out, to_device_raw(q_dec, "bf16", DEV), torch.from_numpy(tables).to(DEV),
+              torch.from_numpy(lens).to(DEV), mc, sm, ws)
+    torch.cuda.synchronize()
+    got = out_to_f64(to_host_raw(out.cpu(), "bf16"), "bf16")
+    want = oat.decode(codecs.decode(q_dec, "bf16"), kc, vc, np.asarray(rt), np.asarray(rl), H_KV,
+                      sm, "bf16")
+    err = assert_close(got, want, "bf16", "detected-prefix decode")
+    say(f"    decode max|d| = {err:.3g}")
+    kv.close()

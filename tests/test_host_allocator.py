@@ -358,6 +358,84 @@ def test_prefix_sharing_golden_trace_through_c_abi():
         pa.pa_pool_destroy(pool)
 
 
+def test_prefix_detection_golden_trace_through_c_abi():
+    """tests/golden/prefix_detection_trace.json (hand-worked, ARTICLE 4.3)
+    through the C ABI."""
+    g = json.load(open(os.path.join(GOLDEN, "prefix_detection_trace.json")))
+    st_, pool = pa.pa_pool_create(g["num_blocks"], g["block_size"], g["initial_free_order"])
+    assert st_ == pa.PA_OK
+    try:
+        for step in g["steps"]:
+            if step["op"] == "create_prefix":
+                s, shared = pa.pa_seq_create_prefix(pool, step["seq"], step["tokens"])
+                if s == pa.PA_OK and "shared_out" in step:
+                    assert shared == step["shared_out"], step
+            elif step["op"] == "register":
+                s = pa.pa_seq_register_prefix(pool, step["seq"], step["tokens"])
+            else:
+                s = pa.pa_seq_release(pool, step["seq"])
+            assert s == step["status"], (step, pa.pa_last_error())
+            assert _state(pool) == step["free"], step
+            assert pa.pa_pool_num_registered(pool) == step["registered"], step
+            if "table" in step:
+                assert list(pa.pa_seq_block_table(pool, step["seq"])[1]) == step["table"]
+            if "refs" in step:
+                assert [pa.pa_pool_block_refs(pool, b)[1] for b in range(g["num_blocks"])] == \
+                    step["refs"]
+    finally:
+        pa.pa_pool_destroy(pool)
+
+
+detect_ops = st.lists(st.tuples(st.sampled_from(["create", "register", "append", "release"]),
+                                st.integers(0, 7), st.lists(st.integers(0, 1), max_size=40),
+                                st.integers(0, 40)), max_size=80)
+
+
+@settings(max_examples=300, deadline=None)
+@given(detect_ops, st.integers(0, 40), st.randoms(use_true_random=False))
+def test_prefix_detection_bit_exact_against_oracle(oplist, nblocks, rnd):
+    """Random create-from-tokens / register / append / release sequences
+    over a two-letter token alphabet (so that contents repeat and match):
+    statuses, shared counts, tables, lengths, free list, reference counts
+    and the number of registered blocks equal the oracle's after every
+    operation."""
+    order = list(range(nblocks))
+    rnd.shuffle(order)
+    ref = oa.BlockPool(nblocks, 4, order)
+    st_, pool = pa.pa_pool_create(nblocks, 4, order)
+    assert st_ == pa.PA_OK
+    toks = {}   # token ids of every live sequence
+    try:
+        for op, seq, tokens, n in oplist:
+            if op == "create":
+                r1 = pa.pa_seq_create_prefix(pool, seq, tokens)
+                r2 = ref.seq_create_prefix(seq, tokens)
+                assert r1 == r2
+                if r1[0] == pa.PA_OK:
+                    toks[seq] = list(tokens)
+            elif op == "register":
+                t = toks.get(seq, [])[:n]
+                assert pa.pa_seq_register_prefix(pool, seq, t) == ref.seq_register_prefix(seq, t)
+            elif op == "append":
+                s1, _ = pa.pa_seq_append(pool, seq, n % 9)
+                s2, _ = ref.seq_append(seq, n % 9)
+                assert s1 == s2
+                if s1 == pa.PA_OK:
+                    toks[seq] += [rnd.randint(0, 1) for _ in range(n % 9)]
+            else:
+                assert pa.pa_seq_release(pool, seq) == ref.seq_release(seq)
+                toks.pop(seq, None)
+            assert _state(pool) == ref.free_list()
+            assert pa.pa_pool_num_registered(pool) == ref.num_registered()
+            for b in range(nblocks):
+                assert pa.pa_pool_block_refs(pool, b)[1] == ref.block_refs(b)
+            for s, t in ref.tables.items():
+                assert list(pa.pa_seq_block_table(pool, s)[1]) == t
+                assert pa.pa_seq_length(pool, s)[1] == ref.lengths[s]
+    finally:
+        pa.pa_pool_destroy(pool)
+
+
 share_ops = st.lists(st.tuples(st.sampled_from(["create", "append", "release", "share"]),
                                st.integers(0, 6), st.integers(0, 6), st.integers(0, 90),
                                st.integers(0, 90)), max_size=80)

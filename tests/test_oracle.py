@@ -150,6 +150,113 @@ def test_prefix_sharing_hand_worked_trace():
             assert [pool.block_refs(b) for b in range(g["num_blocks"])] == step["refs"], step
 
 
+def run_detection_step(pool, step):
+    """(status, tokens in shared blocks or None) of one step."""
+    if step["op"] == "create_prefix":
+        return pool.seq_create_prefix(step["seq"], step["tokens"])
+    if step["op"] == "register":
+        return pool.seq_register_prefix(step["seq"], step["tokens"]), None
+    return pool.seq_release(step["seq"]), None
+
+
+def check_detection_trace(pool_cls):
+    """Runs tests/golden/prefix_detection_trace.json (hand-worked) on a pool
+    class with the oracle's interface; returns the first mismatch or None."""
+    g = json.load(open(os.path.join(GOLDEN, "prefix_detection_trace.json")))
+    pool = pool_cls(g["num_blocks"], g["block_size"], g["initial_free_order"])
+    for i, step in enumerate(g["steps"]):
+        status, shared = run_detection_step(pool, step)
+        if status != step["status"]:
+            return i, "status"
+        if status == oa.OK and "shared_out" in step and shared != step["shared_out"]:
+            return i, "shared tokens"
+        if pool.free_list() != step["free"]:
+            return i, "free list"
+        if pool.num_registered() != step["registered"]:
+            return i, "registered"
+        if "table" in step and pool.block_table(step["seq"]) != step["table"]:
+            return i, "table"
+        if "refs" in step and [pool.block_refs(b) for b in range(g["num_blocks"])] != step["refs"]:
+            return i, "refs"
+    return None
+
+
+def test_prefix_detection_hand_worked_trace():
+    """ARTICLE 4.3 (prefix reuse, detection left to the scheduler): the
+    oracle's detection against a trace worked by hand."""
+    assert check_detection_trace(oa.BlockPool) is None
+
+
+class _NoParent(oa.BlockPool):
+    """Planted mistake: a block is found by its token ids alone."""
+
+    def seq_create_prefix(self, seq, tokens):
+        saved = self.index
+        self.index = {(-1, k[1]): b for k, b in saved.items()}
+        self._chain_off = True
+        try:
+            tokens = [int(t) for t in tokens]
+            if seq in self.tables:
+                return oa.ERR_EXISTS, 0
+            bs, matched = self.block_size, []
+            for i in range(len(tokens) // bs):
+                b = self.index.get((-1, tuple(tokens[i * bs:(i + 1) * bs])))
+                if b is None:
+                    break
+                matched.append(b)
+            fresh = self._take(oa.ceil_div(len(tokens), bs) - len(matched))
+            if fresh is None:
+                return oa.ERR_NO_BLOCKS, 0
+            for b in matched:
+                self.refs[b] += 1
+            self.tables[seq] = matched + fresh
+            self.lengths[seq] = len(tokens)
+            return oa.OK, len(matched) * bs
+        finally:
+            self.index = saved
+
+
+class _KeepsFreed(oa.BlockPool):
+    """Planted mistake: freed blocks stay in the index."""
+
+    def _give_back(self, ids):
+        saved = dict(self.content), dict(self.index)
+        super()._give_back(ids)
+        self.content, self.index = saved
+
+
+class _NoStop(oa.BlockPool):
+    """Planted mistake: the walk skips an unmatched block and goes on."""
+
+    def seq_create_prefix(self, seq, tokens):
+        tokens = [int(t) for t in tokens]
+        if seq in self.tables:
+            return oa.ERR_EXISTS, 0
+        bs, table, parent, shared = self.block_size, [], -1, 0
+        n = oa.ceil_div(len(tokens), bs)
+        for i in range(n):
+            b = self.index.get((parent, tuple(tokens[i * bs:(i + 1) * bs])))
+            table.append(b)
+            parent = b if b is not None else parent
+        fresh = self._take(sum(b is None for b in table))
+        if fresh is None:
+            return oa.ERR_NO_BLOCKS, 0
+        it = iter(fresh)
+        table = [b if b is not None else next(it) for b in table]
+        for b in table:
+            if b not in fresh:
+                self.refs[b] += 1
+                shared += bs
+        self.tables[seq] = table
+        self.lengths[seq] = len(tokens)
+        return oa.OK, shared
+
+
+@pytest.mark.parametrize("cls", [_NoParent, _KeepsFreed, _NoStop])
+def test_prefix_detection_trace_catches_planted_mistakes(cls):
+    assert check_detection_trace(cls) is not None
+
+
 share_ops = st.lists(st.tuples(st.sampled_from(["create", "append", "release", "share"]),
                                st.integers(0, 5), st.integers(0, 5), st.integers(0, 70),
                                st.integers(0, 70)), max_size=60)
