@@ -122,15 +122,25 @@ struct TileLoader {
   int k_lane;    // LDS offset, lane part, K pieces
   int v_lane;    // LDS offset, lane part, V pieces
   int v_key;     // first key of the lane's V piece inside its block
+  int k_ge;      // cache elements from the wave's first K piece to the lane's
+  int v_ge;      // same for V
 
   __device__ TileLoader(int wave_, int lane_) : wave(wave_), lane(lane_) {
     if (!kWide) {
-      k_lane = (lane >> 4) * (kPfKeys * 16) + krow_of(lane & 15) * 16;
-      v_lane = (lane >> 5) * 2048 + (lane & 1) * 256 + ((lane >> 1) & 15) * 16;
-      v_key = (lane & 1) * 8;
+      // Each 16 lanes write 256 contiguous LDS bytes: a lane loads the K
+      // token (of the 16 of its chunk) or the V dimension and half whose
+      // LDS slot is its own, rather than writing its piece to a scattered
+      // slot.  The 16 lanes still read one contiguous 256-byte run.
+      k_lane = (lane >> 4) * (kPfKeys * 16) + (lane & 15) * 16;
+      k_ge = ((lane & ~15) + krow_of(lane & 15)) * kElems;
+      v_lane = (lane >> 5) * 2048 + ((lane >> 4) & 1) * 256 + (lane & 15) * 16;
+      v_ge = (2 * ((lane & 15) + 16 * (lane >> 5)) + ((lane >> 4) & 1)) * kElems;
+      v_key = ((lane >> 4) & 1) * 8;
     } else {
       k_lane = (lane >> 4) * 2 * (kPfKeys * 16) + krow_of(lane & 15) * 16;
+      k_ge = lane * kElems;
       v_lane = (lane >> 4) * 2048 + (lane & 15) * 16;
+      v_ge = lane * kElems;
       v_key = 0;
     }
   }
@@ -164,7 +174,7 @@ struct TileLoader {
     const int32_t bk = safe_block(__builtin_amdgcn_readlane(ids, q.b), num_blocks);
     const CR* base = (q.v ? v_cache : k_cache) +
                      (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + q.e0 * kElems;
-    r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane * kElems));
+    r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (q.v ? v_ge : k_ge)));
   }
   __device__ void load(u32x4* regs, const CR* __restrict__ k_cache, const CR* __restrict__ v_cache,
                        int32_t ids, int32_t kvh, int32_t H_kv, int32_t num_blocks) const {
@@ -174,7 +184,7 @@ struct TileLoader {
       const int32_t bk = safe_block(__builtin_amdgcn_readlane(ids, q.b), num_blocks);
       const CR* base = (q.v ? v_cache : k_cache) +
                        (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + q.e0 * kElems;
-      regs[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane * kElems));
+      regs[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (q.v ? v_ge : k_ge)));
     }
   }
 
@@ -450,8 +460,8 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
   constexpr int NQK = 2 * NKS;       // S MFMAs per tile
   constexpr int NPV = 4 * NDT;       // O MFMAs per tile
   constexpr int NM = NQK + NPV;
-  constexpr int EPS = 32 / NQK;      // exponentials per S slot
-  static_assert(EPS * NQK == 32, "32 scores per lane and tile");
+  constexpr int WPS = 32 / NM;       // weights formed per MFMA slot
+  static_assert(WPS * NM == 32, "32 scores per lane and tile");
   constexpr int PD = 2;              // operand reads issued this many MFMAs ahead
   constexpr int kLd0 = NLD;          // first slot with a tile load
   constexpr int kLdEvery = 4;        // one tile load every this many MFMA slots
@@ -590,6 +600,7 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
     for (int i = 0; i < PD; ++i) opnd[i] = operand(i);
     const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
     float l_tile = 0.f;
+    float w_even = 0.f;  // first weight of a pair whose second is still to come
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       if (i + PD < NM) opnd[(i + PD) % (PD + 1)] = operand(i + PD);
@@ -604,24 +615,6 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
       if (i < NQK) {
         sn[i & 1] = mfma32x32x16(__builtin_bit_cast(bf16x8, opnd[i % (PD + 1)]), qf[i >> 1],
                                  sn[i & 1]);
-        // weights of scores e = EPS i .. (e = 8 u + i8: key 16 u + i8 of
-        // the lane's half), in pairs
-#pragma unroll
-        for (int q2 = 0; q2 < EPS; q2 += 2) {
-          const int e = EPS * i + q2;
-          const int u = e >> 3, i8 = e & 7;
-          const float w0 = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(sc[u >> 1][8 * (u & 1) + i8], score_scale, -mu));
-          const float w1 = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(sc[u >> 1][8 * (u & 1) + i8 + 1], score_scale, -mu));
-          f16x2 h2 = {static_cast<_Float16>(w0), static_cast<_Float16>(w1)};
-          // computed here, between the MFMAs, not where it is next used
-          asm volatile("" : "+v"(h2));
-          pn[u][i8] = h2[0];
-          pn[u][i8 + 1] = h2[1];
-          l_tile = __builtin_amdgcn_fdot2(h2, ones, l_tile, false);
-          asm volatile("" : "+v"(l_tile));
-        }
       } else {
         const int j = i - NQK;
         o[j % NDT] = mfma32x32x16(__builtin_bit_cast(f16x8, opnd[i % (PD + 1)]), pp[j / NDT],
@@ -630,6 +623,29 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
         // it reaches the diagonal
         if constexpr (decltype(masked_next)::value)
           if (j == 1) mask_scores(sn, t + 1);
+      }
+      // weights of S(t) spread evenly over all the slots: slot i forms
+      // e = WPS i .. WPS i + WPS - 1 (e = 8 u + i8: key 16 u + i8 of the
+      // lane's half); a pair goes to fp16 and into the row sum once its
+      // second weight exists.  Each value is pinned to its slot (empty asm),
+      // not left to sink to where it is next used.
+#pragma unroll
+      for (int q2 = 0; q2 < WPS; ++q2) {
+        const int e = WPS * i + q2;
+        const int u = e >> 3, i8 = e & 7;
+        float w = __builtin_amdgcn_exp2f(
+            __builtin_fmaf(sc[u >> 1][8 * (u & 1) + i8], score_scale, -mu));
+        if (e & 1) {
+          f16x2 h2 = {static_cast<_Float16>(w_even), static_cast<_Float16>(w)};
+          asm volatile("" : "+v"(h2));
+          pn[u][i8 - 1] = h2[0];
+          pn[u][i8] = h2[1];
+          l_tile = __builtin_amdgcn_fdot2(h2, ones, l_tile, false);
+          asm volatile("" : "+v"(l_tile));
+        } else {
+          asm volatile("" : "+v"(w));
+          w_even = w;
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
