@@ -36,7 +36,8 @@ Secondary legs (skipped with --decode-only):
   ``fp8_prefill`` the 64 slices of the 32768-token prompt with an e4m3fn
                  cache: prefill kernel TFLOP/s;
   ``prefix_sharing`` 128 sequences behind one shared 1024-token prompt:
-                 blocks held and decode kernel time, shared vs private;
+                 blocks held and decode kernel time: shared by naming the
+                 owner, private, and found from the token ids (detected);
   ``block_size`` the decode-70b contexts with 8/16/32-token blocks: decode
                  kernel GB/s, and the trace's fragmentation per block size;
   ``trace``      1000 continuous-batching iterations (libpa scheduler +
@@ -1135,10 +1136,13 @@ def fp8_prefill_leg(args, dev):
 def prefix_leg(args, dev):
     """Prefix sharing (ARTICLE 4.3): 128 sequences that start with the same
     1024-token system prompt, followed by their own lognormal contexts
-    (decode-70b lengths).  The same decode batch runs over two pools: one
+    (decode-70b lengths).  The same decode batch runs over three pools: one
     where every sequence holds the prompt's 64 blocks through pa_seq_share,
-    one where each holds a private copy.  Reports the blocks held and the
-    decode kernel time of both on the same algorithmic bytes."""
+    one where each holds a private copy, and one where the prompt's owner
+    registers its computed blocks by content and every other sequence is
+    created from its token ids alone (pa_seq_create_prefix finds the 64
+    blocks).  Reports the blocks held and the decode kernel time of each on
+    the same algorithmic bytes."""
     import torch
 
     import workloads
@@ -1155,11 +1159,34 @@ def prefix_leg(args, dev):
     q = torch.randn((S, H_Q, D), generator=gen, device=dev).to(torch.bfloat16)
     out = torch.empty((S, H_Q, D), dtype=torch.bfloat16, device=dev)
     res = {}
-    for mode in ("shared", "private"):
+    # token ids (detected pool): one prompt, then each sequence's own ids,
+    # drawn apart from the prompt's so that only the prompt's blocks match
+    ids_rng = np.random.default_rng(11)
+    prompt_ids = ids_rng.integers(0, 32000, PFX).astype(np.int32)
+    own_ids = [ids_rng.integers(32000, 64000, int(n)).astype(np.int32) for n in own]
+    for mode in ("shared", "private", "detected"):
         nb = int(np.sum(-(-lens // BLOCK))) + PFX // BLOCK + 8
         order = np.random.default_rng(7).permutation(nb).astype(np.int32)
         kv = PagedKV(nb, H_KV, D, "bf16", dev, order)
-        if mode == "shared":
+        if mode == "detected":
+            st, _ = pa.pa_seq_create_prefix(kv.pool, S, prompt_ids)     # the prompt's owner
+            pa.check(st)
+            _fill_random(kv, kv.slots(S, 0, PFX), gen, dev)
+            torch.cuda.synchronize()                           # its K/V are in the cache
+            pa.check(pa.pa_seq_register_prefix(kv.pool, S, prompt_ids))
+            fill, found = [], []
+            for s in range(S):
+                st, shared = pa.pa_seq_create_prefix(
+                    kv.pool, s, np.concatenate([prompt_ids, own_ids[s]]))
+                pa.check(st)
+                found.append(shared)
+                fill.append(kv.slots(s, shared, int(lens[s]) - shared))
+            _fill_random(kv, np.concatenate(fill), gen, dev)
+            if min(found) != PFX or max(found) != PFX:
+                raise RuntimeError(f"prefix detection found {min(found)}..{max(found)} of "
+                                   f"the {PFX} prompt tokens")
+            registered = pa.pa_pool_num_registered(kv.pool)
+        elif mode == "shared":
             pa.check(kv.create(S, PFX))                       # the prompt's owner
             _fill_random(kv, kv.slots(S, 0, PFX), gen, dev)
             fill = []
@@ -1198,6 +1225,8 @@ def prefix_leg(args, dev):
                        "lengths, 64/8 heads, d128, bf16; decode kernel on algorithmic bytes")
     res["algorithmic_bytes_per_launch"] = int(nbytes)
     res["blocks_saved"] = res["private"]["blocks_held"] - res["shared"]["blocks_held"]
+    res["detected"]["registered_blocks"] = int(registered)
+    res["detected"]["prompt_tokens_found_per_sequence"] = PFX
     return res
 
 
