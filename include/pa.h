@@ -192,6 +192,13 @@ pa_status pa_seq_register_prefix(pa_pool* pool, int64_t seq, const int32_t* toke
 pa_status pa_seq_create_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens,
                                int32_t num_tokens, int32_t* shared_out);
 
+/* The lookup of pa_seq_create_prefix without its effects [host]: tokens
+ * (a multiple of block_size) of the leading full blocks of tokens[0 ..
+ * num_tokens) whose content is registered, into *matched_out.  Errors:
+ * PA_ERR_INVALID (NULL pool or matched_out, num_tokens < 0, NULL tokens). */
+pa_status pa_pool_match_prefix(const pa_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                               int32_t* matched_out);
+
 /* Number of registered blocks (-1 for a NULL pool). */
 int32_t pa_pool_num_registered(const pa_pool* pool);
 
@@ -459,6 +466,7 @@ typedef struct pa_sched_accounting {
   int32_t running, waiting;
   int64_t finished, preemptions;
   int64_t blocks_held, tokens_held, unwritten;
+  int64_t prefix_hit_tokens;  /* prompt tokens found shared at admission, in total */
 } pa_sched_accounting;
 
 /* block_size must equal the pool's.  PA_ERR_INVALID on bad sizes.  The
@@ -501,6 +509,18 @@ void pa_sched_destroy(pa_sched* sched);
 /* Queue a request (prompt_len >= 1 tokens, target >= 1 output tokens);
  * PA_ERR_EXISTS if the id was ever added. */
 pa_status pa_sched_add(pa_sched* sched, int64_t seq, int32_t prompt_len, int32_t target);
+/* Queue a request with its prompt's token ids (ids[prompt_len], host,
+ * copied), for prefix caching (ARTICLE 4.3; PA_SCHED_CHUNKED only, else
+ * PA_ERR_INVALID).  Its admission shares the leading full blocks of
+ * ids[0 .. prompt_len-1) that the pool has registered by content
+ * (pa_seq_create_prefix; the last prompt token is always computed), needs
+ * free blocks only for the rest, and prefills from the shared count on; a
+ * re-admission after preemption does the same and then grows to every
+ * token it knows.  Its own full prompt blocks are registered
+ * (pa_seq_register_prefix) at the start of the step after the one whose
+ * slices complete them, once their K/V are in the cache. */
+pa_status pa_sched_add_prompt(pa_sched* sched, int64_t seq, int32_t prompt_len, int32_t target,
+                              const int32_t* ids);
 pa_status pa_sched_step(pa_sched* sched, pa_sched_batch* batch);
 pa_status pa_sched_stats(const pa_sched* sched, pa_sched_accounting* out);
 

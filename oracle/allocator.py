@@ -190,6 +190,20 @@ class BlockPool:
         self.lengths[seq] = len(tokens)
         return OK, len(matched) * bs
 
+    def match_prefix(self, tokens) -> int:
+        """Tokens of the leading full blocks of ``tokens`` whose content is
+        registered (the walk of ``seq_create_prefix``, nothing taken)."""
+        tokens = [int(t) for t in tokens]
+        bs = self.block_size
+        n, parent = 0, -1
+        for i in range(len(tokens) // bs):
+            b = self.index.get((parent, tuple(tokens[i * bs:(i + 1) * bs])))
+            if b is None:
+                break
+            n += 1
+            parent = b
+        return n * bs
+
     def num_registered(self) -> int:
         return len(self.content)
 

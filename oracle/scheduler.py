@@ -51,6 +51,19 @@ without chunking), read as follows:
   reached its target keeps decoding padding until every member has, and the
   batch leaves together;
 * ``naive``: ``static`` with one request per batch.
+
+Prefix caching (ARTICLE §4.3 names prefix sharing and the detection of a
+shared prefix, not its mechanics; ``chunked`` only), read as follows: a
+request may carry its prompt's token ids; at admission the leading full
+blocks of the prompt without its last token are looked up by content (the
+allocator's index: the block before and the block's ids), the request fits
+if the free list holds the blocks it needs beyond those, it is created
+sharing them, and its prefill starts after them (the last prompt token is
+always computed: its slice yields the first output token); a re-admitted
+request does the same for its prompt and then grows to every token it
+knows.  A sequence's full prompt blocks are registered at the start of the
+step after the one whose slices complete them (their K/V are then in the
+cache).
 """
 from __future__ import annotations
 
@@ -70,6 +83,8 @@ class Seq:
     in_prefill: bool = True
     preemptions: int = 0
     padding: int = 0          # static batches: padding tokens before the output
+    ids: list | None = None   # the prompt's token ids (prefix caching)
+    reg_blocks: int = 0       # leading blocks of the current table registered
 
     def cached_len(self) -> int:
         if self.in_prefill:
@@ -101,17 +116,29 @@ class Scheduler:
         self.waiting: list[Seq] = []
         self.running: list[Seq] = []
         self.done: list[Seq] = []
+        self.prefix_hits = 0      # prompt tokens found shared at admission
 
     def add(self, sid: int, prompt_len: int, target: int):
         if prompt_len < 1 or target < 1:
             raise ValueError("prompt and target must be positive")
         self.waiting.append(Seq(sid, prompt_len, target, known=prompt_len))
 
+    def add_prompt(self, sid: int, prompt_len: int, target: int, ids):
+        """A request with its prompt's token ids (prefix caching)."""
+        if self.mode != "chunked":
+            raise ValueError("prefix caching needs the chunked schedule")
+        ids = [int(t) for t in ids]
+        if len(ids) != prompt_len:
+            raise ValueError("one token id per prompt position")
+        self.add(sid, prompt_len, target)
+        self.waiting[-1].ids = ids
+
     def _preempt(self, s: Seq):
         self.pool.seq_release(s.sid)
         s.preemptions += 1
         s.in_prefill = True
         s.prefilled = 0
+        s.reg_blocks = 0
         s.known = s.prompt_len + s.padding + s.decoded
         self.waiting.append(s)
 
@@ -142,10 +169,42 @@ class Scheduler:
         self.running.append(s)
         out.admitted.append(s.sid)
 
+    def _admit_prefix(self, out: Batch, s: Seq) -> bool:
+        """Admission of a request with token ids; False if it does not fit."""
+        bs = self.pool.block_size
+        head = s.ids[:s.prompt_len - 1]          # the last prompt token is always computed
+        matched = self.pool.match_prefix(head)
+        if self.pool.num_free() < ceil_div(s.known, bs) - matched // bs:
+            return False
+        st, shared = self.pool.seq_create_prefix(s.sid, head)
+        assert st == OK and shared == matched
+        st, _ = self.pool.seq_append(s.sid, s.known - len(head))
+        assert st == OK
+        s.prefilled = shared
+        s.reg_blocks = shared // bs
+        self.prefix_hits += shared
+        self.waiting.pop(0)
+        self.running.append(s)
+        out.admitted.append(s.sid)
+        return True
+
+    def _register_computed(self):
+        """(1') Prompt blocks completed by the last step's slices (their K/V
+        are in the cache now) join the allocator's index."""
+        bs = self.pool.block_size
+        for s in self.running:
+            if s.ids is None:
+                continue
+            nb = min(s.prefilled, s.prompt_len) // bs
+            if nb > s.reg_blocks:
+                assert self.pool.seq_register_prefix(s.sid, s.ids[:nb * bs]) == OK
+                s.reg_blocks = nb
+
     def step(self) -> Batch:
         out = Batch()
         bs = self.pool.block_size
         static = self.mode in ("static", "naive")
+        self._register_computed()
         # (2) release finished sequences; a static batch only all at once
         over = [not s.in_prefill and s.decoded >= s.target for s in self.running]
         if static and not all(over):
@@ -180,6 +239,10 @@ class Scheduler:
         if self.mode == "chunked":
             while self.waiting and len(self.running) < self.max_running:
                 s = self.waiting[0]
+                if s.ids is not None:
+                    if not self._admit_prefix(out, s):
+                        break
+                    continue
                 if self.pool.num_free() < ceil_div(s.known, bs):
                     break
                 self._admit(out, s)

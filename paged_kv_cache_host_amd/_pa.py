@@ -59,7 +59,8 @@ class SchedBatchC(C.Structure):
 class SchedAccountingC(C.Structure):
     """``pa_sched_accounting`` of include/pa.h."""
     _fields_ = [("running", _i32), ("waiting", _i32), ("finished", _i64), ("preemptions", _i64),
-                ("blocks_held", _i64), ("tokens_held", _i64), ("unwritten", _i64)]
+                ("blocks_held", _i64), ("tokens_held", _i64), ("unwritten", _i64),
+                ("prefix_hit_tokens", _i64)]
 
 
 _SIGS = {
@@ -79,6 +80,7 @@ _SIGS = {
     "pa_pool_block_refs": (_i32, [_vp, _i32, _i32p]),
     "pa_seq_register_prefix": (_i32, [_vp, _i64, _i32p, _i32]),
     "pa_seq_create_prefix": (_i32, [_vp, _i64, _i32p, _i32, _i32p]),
+    "pa_pool_match_prefix": (_i32, [_vp, _i32p, _i32, _i32p]),
     "pa_pool_num_registered": (_i32, [_vp]),
     "pa_seq_length": (_i32, [_vp, _i64, _i32p]),
     "pa_seq_block_table": (_i32, [_vp, _i64, _i32p, _i32, _i32p]),
@@ -95,6 +97,7 @@ _SIGS = {
     "pa_sched_create_mode": (_i32, [_vp, _i32, _i32, _i32, _i32, C.POINTER(_vp)]),
     "pa_sched_destroy": (None, [_vp]),
     "pa_sched_add": (_i32, [_vp, _i64, _i32, _i32]),
+    "pa_sched_add_prompt": (_i32, [_vp, _i64, _i32, _i32, _i32p]),
     "pa_sched_step": (_i32, [_vp, C.POINTER(SchedBatchC)]),
     "pa_sched_stats": (_i32, [_vp, C.POINTER(SchedAccountingC)]),
     "pa_stage": (_i32, [_vp, _vp, _vp, _sz]),
@@ -254,6 +257,15 @@ def pa_seq_create_prefix(pool, seq: int, tokens):
     return st, out.value
 
 
+def pa_pool_match_prefix(pool, tokens):
+    """Returns (status, tokens of the leading full blocks of ``tokens``
+    whose content is registered); changes nothing."""
+    t = _i32_array(tokens)
+    out = _i32(0)
+    st = _lib.pa_pool_match_prefix(pool, _ptr_i32(t) if len(t) else None, len(t), C.byref(out))
+    return st, out.value
+
+
 def pa_pool_num_registered(pool) -> int:
     return _lib.pa_pool_num_registered(pool)
 
@@ -340,6 +352,15 @@ def pa_sched_destroy(sched) -> None:
 
 def pa_sched_add(sched, seq: int, prompt_len: int, target: int) -> int:
     return _lib.pa_sched_add(sched, seq, prompt_len, target)
+
+
+def pa_sched_add_prompt(sched, seq: int, target: int, ids) -> int:
+    """Queue a request with its prompt's token ids (prefix caching); the
+    prompt length is len(ids)."""
+    t = _i32_array(ids)
+    if len(t) < 1:
+        raise PaError(PA_ERR_INVALID, "pa_sched_add_prompt: empty prompt")
+    return _lib.pa_sched_add_prompt(sched, seq, len(t), target, _ptr_i32(t))
 
 
 class SchedBatch:

@@ -312,6 +312,23 @@ pa_status pa_seq_create_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens
   return PA_OK;
 }
 
+pa_status pa_pool_match_prefix(const pa_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                               int32_t* matched_out) {
+  if (!pool || !matched_out) return fail(PA_ERR_INVALID, "pa_pool_match_prefix: NULL argument");
+  if (num_tokens < 0 || (num_tokens > 0 && !tokens))
+    return fail(PA_ERR_INVALID, "pa_pool_match_prefix: num_tokens=%d or NULL tokens", num_tokens);
+  const int32_t bs = pool->block_size;
+  int32_t parent = -1, n = 0;
+  for (int32_t i = 0; i < num_tokens / bs; ++i) {
+    auto f = pool->index.find(pool->key_of(parent, tokens + static_cast<int64_t>(i) * bs));
+    if (f == pool->index.end()) break;
+    parent = f->second;
+    ++n;
+  }
+  *matched_out = n * bs;
+  return PA_OK;
+}
+
 int32_t pa_pool_num_registered(const pa_pool* pool) {
   return pool ? static_cast<int32_t>(pool->registered.size()) : -1;
 }

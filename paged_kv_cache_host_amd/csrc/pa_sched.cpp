@@ -37,11 +37,23 @@
 //    one finishes, and the batch is released together.
 //  * NAIVE: STATIC with batches of one request.
 //
+// Prefix caching (ARTICLE §4.3; CHUNKED only): a request may carry its
+// prompt's token ids.  Its admission then looks up the leading full blocks
+// of the prompt, all but its last token (that token is always computed, so
+// a fully cached prompt still runs the slice that yields its first output
+// token), among the blocks the pool has registered by content; it needs
+// fresh blocks only for the rest, and its prefill starts after the shared
+// tokens.  A block is registered at the start of the step after the one
+// that handed out its last prompt position as prefill: by then the caller
+// has written its K/V.  Registration stops where another block already
+// holds the same content, and freed blocks leave the index (pa_host.cpp).
+//
 // The pool is driven through its public C calls only.
 #include <algorithm>
 #include <cstdint>
 #include <deque>
 #include <new>
+#include <unordered_map>
 #include <unordered_set>
 #include <vector>
 
@@ -60,6 +72,8 @@ struct SSeq {
   int32_t decoded;    // output tokens produced
   bool in_prefill;
   int32_t preemptions;
+  bool has_ids;       // the prompt's token ids are known (prefix caching)
+  int32_t reg_blocks; // leading blocks of the current table registered so far
 };
 
 }  // namespace
@@ -73,8 +87,10 @@ struct pa_sched {
   std::deque<SSeq> waiting;
   std::vector<SSeq> running;
   std::unordered_set<int64_t> known_ids;
+  std::unordered_map<int64_t, std::vector<int32_t>> prompt_ids;  // requests with ids
   int64_t n_done = 0;
   int64_t preemptions = 0;
+  int64_t prefix_hits = 0;  // prompt tokens found in registered blocks at admission
 };
 
 using pa::fail;
@@ -121,7 +137,20 @@ pa_status pa_sched_add(pa_sched* s, int64_t seq, int32_t prompt_len, int32_t tar
   if (s->known_ids.count(seq)) return fail(PA_ERR_EXISTS, "pa_sched_add: sequence %lld exists",
                                            static_cast<long long>(seq));
   s->known_ids.insert(seq);
-  s->waiting.push_back(SSeq{seq, prompt_len, target, 0, prompt_len, 0, 0, true, 0});
+  s->waiting.push_back(SSeq{seq, prompt_len, target, 0, prompt_len, 0, 0, true, 0, false, 0});
+  return PA_OK;
+}
+
+pa_status pa_sched_add_prompt(pa_sched* s, int64_t seq, int32_t prompt_len, int32_t target,
+                              const int32_t* ids) {
+  if (!s) return fail(PA_ERR_INVALID, "pa_sched_add_prompt: NULL scheduler");
+  if (s->mode != PA_SCHED_CHUNKED)
+    return fail(PA_ERR_INVALID, "pa_sched_add_prompt: prefix caching needs the chunked mode");
+  if (!ids) return fail(PA_ERR_INVALID, "pa_sched_add_prompt: NULL token ids");
+  const pa_status st = pa_sched_add(s, seq, prompt_len, target);
+  if (st != PA_OK) return st;
+  s->waiting.back().has_ids = true;
+  s->prompt_ids.emplace(seq, std::vector<int32_t>(ids, ids + prompt_len));
   return PA_OK;
 }
 
@@ -144,6 +173,17 @@ pa_status pa_sched_step(pa_sched* s, pa_sched_batch* b) {
   b->n_finished = b->n_admitted = b->n_preempted = 0;
   pa_pool* pool = s->pool;
 
+  // prompt blocks whose K/V the last step's slices completed join the index
+  for (SSeq& q : s->running) {
+    if (!q.has_ids) continue;
+    const int32_t nb = std::min(q.prefilled, q.prompt) / s->block_size;
+    if (nb <= q.reg_blocks) continue;
+    const pa_status st =
+        pa_seq_register_prefix(pool, q.id, s->prompt_ids[q.id].data(), nb * s->block_size);
+    if (st != PA_OK) return st;
+    q.reg_blocks = nb;
+  }
+
   const bool batched = s->mode == PA_SCHED_STATIC || s->mode == PA_SCHED_NAIVE;
   // finished sequences leave and free their blocks; a static batch leaves
   // only as a whole
@@ -158,6 +198,7 @@ pa_status pa_sched_step(pa_sched* s, pa_sched_batch* b) {
         if (pa_seq_release(pool, q.id) != PA_OK) return PA_ERR_UNKNOWN_SEQ;
         b->finished[b->n_finished++] = q.id;
         ++s->n_done;
+        if (q.has_ids) s->prompt_ids.erase(q.id);
       } else {
         s->running[w++] = q;
       }
@@ -182,6 +223,7 @@ pa_status pa_sched_step(pa_sched* s, pa_sched_batch* b) {
         ++s->preemptions;
         q.in_prefill = true;
         q.prefilled = 0;
+        q.reg_blocks = 0;
         q.known = q.prompt + q.pad + q.decoded;
         s->waiting.push_back(q);
         b->preempted[b->n_preempted++] = q.id;
@@ -233,6 +275,29 @@ pa_status pa_sched_step(pa_sched* s, pa_sched_batch* b) {
   if (!batched) {
     while (!s->waiting.empty() && static_cast<int32_t>(s->running.size()) < R) {
       SSeq q = s->waiting.front();
+      if (q.has_ids) {
+        // shared: leading full blocks of the prompt but its last token
+        const int32_t* ids = s->prompt_ids[q.id].data();
+        const int32_t m_len = q.prompt - 1;
+        int32_t matched = 0;
+        st = pa_pool_match_prefix(pool, ids, m_len, &matched);
+        if (st != PA_OK) return st;
+        if (pa_pool_num_free(pool) <
+            ceil_div32(q.known, s->block_size) - matched / s->block_size)
+          break;
+        int32_t shared = 0;
+        st = pa_seq_create_prefix(pool, q.id, ids, m_len, &shared);
+        if (st != PA_OK) return st;
+        st = pa_seq_append(pool, q.id, q.known - m_len, nullptr);
+        if (st != PA_OK) return st;
+        q.prefilled = shared;
+        q.reg_blocks = shared / s->block_size;
+        s->prefix_hits += shared;
+        s->waiting.pop_front();
+        s->running.push_back(q);
+        b->admitted[b->n_admitted++] = q.id;
+        continue;
+      }
       if (pa_pool_num_free(pool) < ceil_div32(q.known, s->block_size)) break;
       // a whole prompt must fit what is left of the iteration's budget
       if (s->mode == PA_SCHED_CONTINUOUS && q.known > left && left < s->budget) break;
@@ -282,6 +347,7 @@ pa_status pa_sched_stats(const pa_sched* s, pa_sched_accounting* out) {
   out->waiting = static_cast<int32_t>(s->waiting.size());
   out->finished = s->n_done;
   out->preemptions = s->preemptions;
+  out->prefix_hit_tokens = s->prefix_hits;
   out->blocks_held = 0;
   out->tokens_held = 0;
   out->unwritten = 0;

@@ -125,8 +125,16 @@ class LayerIterations:
         except Exception:
             pass
 
-    def add(self, seq: int, prompt_len: int, target: int):
-        pa.check(pa.pa_sched_add(self.sched, seq, prompt_len, target))
+    def add(self, seq: int, prompt_len: int, target: int, ids=None):
+        """Queue a request; with its prompt's token ids (``ids``, prompt_len
+        of them) the scheduler shares the leading prompt blocks an earlier
+        request already computed (prefix caching, chunked schedule)."""
+        if ids is None:
+            pa.check(pa.pa_sched_add(self.sched, seq, prompt_len, target))
+        else:
+            if len(ids) != prompt_len:
+                raise ValueError("one token id per prompt position")
+            pa.check(pa.pa_sched_add_prompt(self.sched, seq, target, ids))
 
     def step(self, keep=None):
         """One iteration.  ``keep``: optional callback(record) receiving the

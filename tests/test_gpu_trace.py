@@ -52,10 +52,11 @@ def _trace():
     return w, host_rows, n_rows
 
 
-def _replay(w, host_rows, sm, results, mode="chunked"):
+def _replay(w, host_rows, sm, results, mode="chunked", ids=None):
     """Run the oracle's scheduler, cache scatter and attention over the same
     trace and compare every iteration's record and outputs (``results[it]``
-    = (record, decode output, prefill output), decoded to float)."""
+    = (record, decode output, prefill output), decoded to float).  ``ids``:
+    prompt token ids per request (prefix caching)."""
     pool = oa.BlockPool(w.num_blocks, 16)
     sch = Scheduler(pool, R, BUDGET[mode], mode=mode)
     kc, vc = oc.new_cache(w.num_blocks, H_KV, 16, D, "bf16")
@@ -64,7 +65,10 @@ def _replay(w, host_rows, sm, results, mode="chunked"):
     written = set()
     for it in range(w.iters):
         for sid, p, o in w.arrivals[it]:
-            sch.add(sid, p, o)
+            if ids is not None:
+                sch.add_prompt(sid, p, o, ids[sid])
+            else:
+                sch.add(sid, p, o)
         rec, dec, pf = results[it]
         ob = sch.step()
         ds, dp = rec["decode"]
@@ -102,6 +106,8 @@ def _replay(w, host_rows, sm, results, mode="chunked"):
             ref = oat.decode(codecs.decode(q, "bf16"), kc, vc, tables, lens, H_KV, sm, "bf16")
             worst = max(worst, assert_close(dec, ref, "bf16", f"iteration {it} decode"))
             checked["decode"] += len(seqs)
+    if ids is not None:
+        checked["prefix_hits"] = sch.prefix_hits
     return checked, worst, kc, vc, sorted(written)
 
 
@@ -230,3 +236,81 @@ def test_serve_live_clock(mode):
     assert r["itl"]["max_ms"] >= 0 and r["iterations"] > max(x[3] for x in reqs)
     say(f"    {r['iterations']} iterations, {r['wall_s'] * 1e3:.2f} ms, "
         f"TTFT mean {r['ttft']['mean_ms']:.3f} ms")
+
+
+def _prefix_trace():
+    """The trace above with every prompt behind one of three system prefixes
+    (40, 64 and 100 tokens) and its own tokens after it.  A prefix's token
+    rows are the same for every request that starts with it, as its K/V
+    would be; prompt token ids are the prefix's ids, then the request's."""
+    from types import SimpleNamespace
+    base = workloads.trace(seed=SEED + 1, iters=80, lam=0.5, prompt_median=40, prompt_sigma=0.8,
+                           prompt_cap=300, out_mean=30, num_blocks=80)
+    rng = np.random.default_rng(SEED)
+    plens = [40, 64, 100]
+    pids = [rng.integers(0, 30000, n).astype(np.int32) for n in plens]
+    arrivals, ids, src = [], {}, {}
+    for row in base.arrivals:
+        out = []
+        for sid, p, o in row:
+            k = int(rng.integers(0, 3))
+            ids[sid] = np.concatenate([pids[k], rng.integers(30000, 60000, p).astype(np.int32)])
+            src[sid] = (k, plens[k])
+            out.append((sid, plens[k] + p, o))
+        arrivals.append(out)
+    w = SimpleNamespace(arrivals=arrivals, iters=base.iters, num_blocks=base.num_blocks,
+                        name=base.name + " behind 3 shared prefixes")
+    n_rows = max(p for row in arrivals for _, p, _ in row) + \
+        max(o for row in arrivals for _, _, o in row)
+    prefix_rows = [workloads.seq_token_rows(SEED, 100000 + k, n, H_Q, H_KV, D)
+                   for k, n in enumerate(plens)]
+    rows = {sid: workloads.seq_token_rows(SEED, sid, n_rows, H_Q, H_KV, D)
+            for row in arrivals for sid, _, _ in row}
+
+    def row_of(s, p):
+        k, n = src[s]
+        return (prefix_rows[k], p) if p < n else (rows[s], p)
+
+    def host_rows(seqs, positions):
+        got = [row_of(s, p) for s, p in zip(seqs, positions)]
+        return tuple(np.stack([r[j][p] for r, p in got]) for j in range(3))
+
+    return w, host_rows, n_rows, ids
+
+
+def test_trace_prefix_caching_matches_oracle():
+    """Prefix caching through whole iterations: requests queued with their
+    prompt token ids share the prompt blocks earlier requests computed, and
+    prefill only after them.  Schedule, cache and every decode and prefill
+    output against the oracle's scheduler (same readings) and fp64
+    attention over the same cache."""
+    from paged_kv_cache_host_amd.engine import to_device_raw
+    from paged_kv_cache_host_amd.iteration import LayerIterations
+
+    w, host_rows, max_ctx, ids = _prefix_trace()
+    say(f"[trace parity, prefix caching] {w.name} pool={w.num_blocks} running<={R} budget={B}")
+
+    def provider(seqs, positions):
+        k, v, q = host_rows(seqs, positions)
+        return (to_device_raw(k, "bf16", "cuda"), to_device_raw(v, "bf16", "cuda"),
+                to_device_raw(q, "bf16", "cuda"))
+
+    run = LayerIterations(w.num_blocks, H_Q, H_KV, D, "cuda", provider, R, B,
+                          max_context=max_ctx, fill_outputs=SENTINEL)
+    results = []
+    for it in range(w.iters):
+        for sid, p, o in w.arrivals[it]:
+            run.add(sid, p, o, ids=ids[sid])
+
+        def keep(rec, out_dec, out_pf):
+            results.append((rec, _decode_bf16(out_dec), _decode_bf16(out_pf)))
+
+        run.step(keep)
+    hits = run.acc["prefix_hit_tokens"]
+    run.close()
+    checked, worst, _, _, _ = _replay(w, host_rows, run.sm, results, ids=ids)
+    say(f"    checked {checked['decode']} decode tokens, {checked['prefill']} prefill tokens, "
+        f"{hits} prompt tokens found shared, {run.totals['preempted']} preemptions, "
+        f"max|d| = {worst:.3g}")
+    assert hits == checked["prefix_hits"] and hits > 200
+    assert checked["decode"] > 50 and checked["prefill"] > 300

@@ -18,15 +18,19 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 class CSide:
-    def __init__(self, num_blocks, max_running, budget, free_order=None, mode="chunked"):
-        st, self.pool = pa.pa_pool_create(num_blocks, 16, free_order)
+    def __init__(self, num_blocks, max_running, budget, free_order=None, mode="chunked",
+                 block_size=16):
+        st, self.pool = pa.pa_pool_create(num_blocks, block_size, free_order)
         pa.check(st)
-        st, self.sch = pa.pa_sched_create_mode(self.pool, mode, max_running, budget, 16)
+        st, self.sch = pa.pa_sched_create_mode(self.pool, mode, max_running, budget, block_size)
         pa.check(st)
         self.b = pa.SchedBatch(max_running, budget)
 
     def add(self, sid, p, o):
         pa.check(pa.pa_sched_add(self.sch, sid, p, o))
+
+    def add_prompt(self, sid, o, ids):
+        pa.check(pa.pa_sched_add_prompt(self.sch, sid, o, ids))
 
     def step(self):
         pa.check(pa.pa_sched_step(self.sch, self.b))
@@ -197,3 +201,85 @@ def test_latency_log_matches_oracle_token_times():
     sm = log.summary(0.5)
     assert sm["ttft"]["n"] == len(want_ttft)
     assert abs(sm["itl"]["mean_ms"] - 0.5 * np.mean(want_gaps)) < 1e-9
+
+
+# -- prefix caching (ARTICLE §4.3) ------------------------------------------
+
+def test_prefix_trace_through_c():
+    """The hand-worked prefix-caching trace (tests/golden/prefix_sched_trace.json)
+    through the C scheduler: batches, accounting, free list, registered
+    blocks and the tokens found shared."""
+    tr = json.load(open(os.path.join(GOLDEN, "prefix_sched_trace.json")))
+    c = CSide(tr["num_blocks"], tr["max_running"], tr["prefill_budget"],
+              block_size=tr["block_size"])
+    for it, want in enumerate(tr["iterations"]):
+        for sid, o, ids in tr["arrivals"].get(str(it), []):
+            c.add_prompt(sid, o, ids)
+        got = c.step()
+        got["free"] = c.free_list()
+        a = c.stats()
+        got["held"] = [a["blocks_held"], a["tokens_held"], a["unwritten"]]
+        got["registered"] = pa.pa_pool_num_registered(c.pool)
+        got["prefix_hits"] = a["prefix_hit_tokens"]
+        assert got == want, (it, got, want)
+    c.close()
+
+
+@pytest.mark.parametrize("seed,num_blocks,lam,out_max", [(1, 24, 0.6, 80), (2, 30, 0.8, 120),
+                                                          (3, 64, 1.0, 40), (4, 20, 1.0, 60)])
+def test_prefix_caching_c_matches_oracle(seed, num_blocks, lam, out_max):
+    """Seeded traces whose prompts start with one of a few system prefixes
+    (some requests without token ids), preempting on the small pools: the C
+    scheduler and the oracle agree bit for bit on every step."""
+    rng = np.random.default_rng(seed)
+    bs = 16
+    prefixes = [rng.integers(0, 1000, n).tolist() for n in (17, 40, 64, 100)]
+    pool = BlockPool(num_blocks, bs)
+    o = Scheduler(pool, 8, 48)
+    c = CSide(num_blocks, 8, 48)
+    sid = 0
+    for it in range(300):
+        for _ in range(rng.poisson(lam)):
+            ids = prefixes[rng.integers(0, 4)] + rng.integers(1000, 2000, rng.integers(1, 40)).tolist()
+            tgt = int(rng.integers(1, out_max))
+            if rng.random() < 0.15:
+                o.add(sid, len(ids), tgt)
+                c.add(sid, len(ids), tgt)
+            else:
+                o.add_prompt(sid, len(ids), tgt, ids)
+                c.add_prompt(sid, tgt, ids)
+            sid += 1
+        want = _oracle_batch(o.step())
+        got = c.step()
+        assert got == want, (seed, it, got, want)
+        a = c.stats()
+        assert [a["blocks_held"], a["tokens_held"], a["unwritten"]] == list(o.held()), (seed, it)
+        assert a["prefix_hit_tokens"] == o.prefix_hits, (seed, it)
+        assert pa.pa_pool_num_registered(c.pool) == pool.num_registered(), (seed, it)
+        assert c.free_list() == pool.free_list(), (seed, it)
+    assert o.prefix_hits > 0
+    c.close()
+
+
+def test_sched_add_prompt_rejects():
+    st, pool = pa.pa_pool_create(8, 16, None)
+    pa.check(st)
+    for mode in ("continuous", "static", "naive"):
+        st, sch = pa.pa_sched_create_mode(pool, mode, 4, 64, 16)
+        pa.check(st)
+        assert pa.pa_sched_add_prompt(sch, 1, 2, [1, 2, 3]) == pa.PA_ERR_INVALID
+        pa.pa_sched_destroy(sch)
+    st, sch = pa.pa_sched_create_mode(pool, "chunked", 4, 64, 16)
+    pa.check(st)
+    assert pa.pa_sched_add_prompt(sch, 1, 2, [1, 2, 3]) == pa.PA_OK
+    assert pa.pa_sched_add_prompt(sch, 1, 2, [1, 2, 3]) == pa.PA_ERR_EXISTS
+    assert pa.pa_sched_add(sch, 1, 3, 2) == pa.PA_ERR_EXISTS
+    assert pa.pa_sched_add_prompt(sch, 2, 0, [1, 2, 3]) == pa.PA_ERR_INVALID   # target 0
+    with pytest.raises(pa.PaError):
+        pa.pa_sched_add_prompt(sch, 3, 2, [])
+    assert pa._lib.pa_sched_add_prompt(sch, 4, 3, 2, None) == pa.PA_ERR_INVALID
+    pa.pa_sched_destroy(sch)
+    st, m = pa.pa_pool_match_prefix(pool, [1, 2, 3])
+    assert st == pa.PA_OK and m == 0
+    assert pa._lib.pa_pool_match_prefix(pool, None, 4, None) == pa.PA_ERR_INVALID
+    pa.pa_pool_destroy(pool)
