@@ -38,6 +38,9 @@ Secondary legs (skipped with --decode-only):
   ``prefix_sharing`` 128 sequences behind one shared 1024-token prompt:
                  blocks held and decode kernel time: shared by naming the
                  owner, private, and found from the token ids (detected);
+  ``prefix_trace`` 1000 iterations of requests behind 8 shared system
+                 prompts, with and without their token ids: prefill tokens
+                 computed, prompt tokens found shared, output tokens/s;
   ``block_size`` the decode-70b contexts with 8/16/32-token blocks: decode
                  kernel GB/s, and the trace's fragmentation per block size;
   ``trace``      1000 continuous-batching iterations (libpa scheduler +
@@ -1230,6 +1233,66 @@ def prefix_leg(args, dev):
     return res
 
 
+def prefix_trace_leg(args, dev):
+    """Prefix caching in the serving loop: 1000 iterations of requests behind
+    one of 8 shared system prompts (512-2048 tokens) plus their own tokens,
+    run twice over the same arrivals: requests queued with their prompt's
+    token ids (the scheduler shares the prompt blocks earlier requests
+    computed and prefills after them) and without.  Reports prefill tokens
+    computed, prompt tokens found shared, output tokens and their rate."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_host_amd.iteration import LayerIterations
+
+    arrivals, num_blocks = workloads.prefix_trace()
+    iters, R, B = len(arrivals), 256, 512
+    max_ctx = max(p + o for row in arrivals for _, p, o, _ in row)
+    ring_n = 8 * (R + B)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    k_ring = torch.randn((ring_n, H_KV, D), generator=gen, device=dev).to(torch.bfloat16)
+    v_ring = torch.randn((ring_n, H_KV, D), generator=gen, device=dev).to(torch.bfloat16)
+    q_ring = torch.randn((ring_n, H_Q, D), generator=gen, device=dev).to(torch.bfloat16)
+    pos = [0]
+
+    def provider(seqs, positions):
+        n = len(seqs)
+        a = pos[0] if pos[0] + n <= ring_n else 0
+        pos[0] = a + n
+        return k_ring[a:a + n], v_ring[a:a + n], q_ring[a:a + n]
+
+    res = {}
+    for mode in ("cached", "uncached"):
+        run = LayerIterations(num_blocks, H_Q, H_KV, D, dev, provider, R, B, max_context=max_ctx,
+                              provider_syncs=False)
+        torch.cuda.synchronize()
+        _settle()
+        t0 = time.perf_counter()
+        for it in range(iters):
+            for sid, p_, o, ids in arrivals[it]:
+                run.add(sid, p_, o, ids=ids if mode == "cached" else None)
+            run.step()
+        run.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        res[mode] = {"ms_per_iteration": round(wall / iters * 1e3, 4),
+                     "prefill_tokens": run.totals["prefill_tokens"],
+                     "prompt_tokens_found_shared": int(run.acc["prefix_hit_tokens"]),
+                     "output_tokens": run.totals["decode_tokens"],
+                     "output_tokens_per_s": round(run.totals["decode_tokens"] / wall, 1),
+                     "finished": run.totals["finished"],
+                     "preemptions": run.totals["preempted"]}
+        run.close()
+        del run
+        torch.cuda.empty_cache()
+    res["workload"] = (f"prefix trace: {iters} iterations, Poisson(0.5) arrivals, prompts = one of 8 "
+                       "system prompts (512-2048 tokens) + lognormal own tokens (median 256, "
+                       "sigma 1, cap 8192), geometric outputs (mean 256), <=256 running, "
+                       "512-token prefill budget, 64/8 heads, d128, bf16, one layer")
+    return res
+
+
 def trace_leg(args, dev):
     """The continuous-batching trace: Poisson arrivals, lognormal prompts,
     geometric outputs, 256 running, 512-token prefill budget, 1000
@@ -1533,6 +1596,7 @@ def main():
         result["fp8_decode"] = fp8_leg(args, dev)
         result["fp8_prefill"] = fp8_prefill_leg(args, dev)
         result["prefix_sharing"] = prefix_leg(args, dev)
+        result["prefix_trace"] = prefix_trace_leg(args, dev)
         result["block_size"] = block_size_leg(args, dev)
         result["trace"] = trace_leg(args, dev)
         result["schedules"] = modes_leg(args, dev)

@@ -285,6 +285,35 @@ def trace(seed: int = 5, iters: int = 1000, lam: float = 0.5, prompt_median: flo
     return TraceWorkload(f"trace-{iters}it-lam{lam}", iters, arrivals, num_blocks, None)
 
 
+def prefix_trace(seed: int = 9, iters: int = 1000, lam: float = 0.5, n_system: int = 8,
+                 system_min: int = 512, system_max: int = 2048, user_median: float = 256.0,
+                 user_sigma: float = 1.0, user_cap: int = 8192, out_mean: float = 256.0,
+                 num_blocks: int = 200_000):
+    """Requests behind shared system prompts: Poisson arrivals (``lam`` per
+    iteration); each prompt is one of ``n_system`` system prompts (token
+    ids drawn once, lengths uniform in [system_min, system_max]) followed by
+    the request's own tokens (lognormal length, median 256, sigma 1.0, cap
+    8192, ids drawn apart from the system prompts'); geometric outputs (mean
+    256).  Returns (arrivals [[(id, prompt_len, output_len, ids)] per
+    iteration], num_blocks)."""
+    rng = np.random.default_rng(seed)
+    systems = [rng.integers(0, 50000, int(rng.integers(system_min, system_max + 1))).astype(np.int32)
+               for _ in range(n_system)]
+    arrivals = []
+    sid = 0
+    for _ in range(iters):
+        row = []
+        for _ in range(int(rng.poisson(lam))):
+            u = int(min(user_cap, math.ceil(rng.lognormal(math.log(user_median), user_sigma))))
+            ids = np.concatenate([systems[int(rng.integers(0, n_system))],
+                                  rng.integers(50000, 100000, max(1, u)).astype(np.int32)])
+            o = int(rng.geometric(1.0 / out_mean))
+            row.append((sid, len(ids), o, ids))
+            sid += 1
+        arrivals.append(row)
+    return arrivals, num_blocks
+
+
 def timed_requests(seed: int = 7, n: int = 256, rate_per_ms: float = 2.0,
                    prompt_median: float = 512.0, prompt_sigma: float = 1.2,
                    prompt_cap: int = 8192, out_mean: float = 64.0, out_cap: int = 512):
