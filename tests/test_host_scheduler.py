@@ -283,3 +283,32 @@ def test_sched_add_prompt_rejects():
     assert st == pa.PA_OK and m == 0
     assert pa._lib.pa_pool_match_prefix(pool, None, 4, None) == pa.PA_ERR_INVALID
     pa.pa_pool_destroy(pool)
+
+
+def test_prefix_caching_edges_c_and_oracle():
+    """Edge prompts, C against the oracle and against counts worked by hand
+    (16-token blocks): a 32-token prompt computed, then the same 32 tokens
+    again (the last token is always computed, so one block is shared), a
+    one-token prompt (nothing to match), and 17 tokens starting with the
+    same 16 (one block shared)."""
+    base = list(range(100, 132))
+    reqs = [(0, 0, 10, base), (3, 1, 1, base), (3, 2, 1, [7]), (3, 3, 1, base[:16] + [5])]
+    pool = BlockPool(16, 16)
+    o = Scheduler(pool, 4, 32)
+    c = CSide(16, 4, 32)
+    hits = []
+    for it in range(8):
+        for when, sid, tgt, ids in reqs:
+            if when == it:
+                o.add_prompt(sid, len(ids), tgt, ids)
+                c.add_prompt(sid, tgt, ids)
+        want = _oracle_batch(o.step())
+        got = c.step()
+        assert got == want, (it, got, want)
+        hits.append(c.stats()["prefix_hit_tokens"])
+        assert hits[-1] == o.prefix_hits
+    # request 0 computes its 32 tokens in step 0, is registered at step 1
+    # and still runs at step 3 (10 output tokens): request 1 shares 16 (not
+    # 32), request 2 none, request 3 16
+    assert hits[2] == 0 and hits[3] == 32 and hits[-1] == 32
+    c.close()
