@@ -386,7 +386,8 @@ def test_prefix_detection_golden_trace_through_c_abi():
         pa.pa_pool_destroy(pool)
 
 
-detect_ops = st.lists(st.tuples(st.sampled_from(["create", "register", "append", "release"]),
+detect_ops = st.lists(st.tuples(st.sampled_from(["create", "register", "append", "release",
+                                                 "match"]),
                                 st.integers(0, 7), st.lists(st.integers(0, 1), max_size=40),
                                 st.integers(0, 40)), max_size=80)
 
@@ -394,8 +395,9 @@ detect_ops = st.lists(st.tuples(st.sampled_from(["create", "register", "append",
 @settings(max_examples=300, deadline=None)
 @given(detect_ops, st.integers(0, 40), st.randoms(use_true_random=False))
 def test_prefix_detection_bit_exact_against_oracle(oplist, nblocks, rnd):
-    """Random create-from-tokens / register / append / release sequences
-    over a two-letter token alphabet (so that contents repeat and match):
+    """Random create-from-tokens / register / append / release / lookup
+    sequences over a two-letter token alphabet (so that contents repeat and
+    match):
     statuses, shared counts, tables, lengths, free list, reference counts
     and the number of registered blocks equal the oracle's after every
     operation."""
@@ -416,6 +418,9 @@ def test_prefix_detection_bit_exact_against_oracle(oplist, nblocks, rnd):
             elif op == "register":
                 t = toks.get(seq, [])[:n]
                 assert pa.pa_seq_register_prefix(pool, seq, t) == ref.seq_register_prefix(seq, t)
+            elif op == "match":
+                st1, m1 = pa.pa_pool_match_prefix(pool, tokens)
+                assert st1 == pa.PA_OK and m1 == ref.match_prefix(tokens)
             elif op == "append":
                 s1, _ = pa.pa_seq_append(pool, seq, n % 9)
                 s2, _ = ref.seq_append(seq, n % 9)
