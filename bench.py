@@ -1286,6 +1286,36 @@ def prefix_trace_leg(args, dev):
         run.close()
         del run
         torch.cuda.empty_cache()
+    # the host side alone (ARTICLE 4.3 / 5: weigh what match detection adds
+    # to the scheduler): the C scheduler over the same arrivals, no kernels,
+    # with and without the token ids; best of three passes each
+    from paged_kv_cache_host_amd import _pa as pa
+    host = {}
+    for mode in ("cached", "uncached"):
+        best = None
+        for _ in range(3):
+            st_, pool = pa.pa_pool_create(num_blocks, BLOCK, None)
+            pa.check(st_)
+            st_, sch = pa.pa_sched_create(pool, R, B, BLOCK)
+            pa.check(st_)
+            b = pa.SchedBatch(R, B)
+            t0 = time.perf_counter()
+            for it in range(iters):
+                for sid, p_, o, ids in arrivals[it]:
+                    if mode == "cached":
+                        pa.check(pa.pa_sched_add_prompt(sch, sid, o, ids))
+                    else:
+                        pa.check(pa.pa_sched_add(sch, sid, p_, o))
+                pa.check(pa.pa_sched_step(sch, b))
+            dt = time.perf_counter() - t0
+            pa.pa_sched_destroy(sch)
+            pa.pa_pool_destroy(pool)
+            best = dt if best is None else min(best, dt)
+        host[mode] = round(best / iters * 1e6, 2)
+    res["host_us_per_iteration"] = {**host, "note": (
+        "C scheduler alone (requests queued + pa_sched_step, through the ctypes binding), "
+        "no kernels; cached = with the prompts' token ids (lookups at admission, "
+        "registration of computed blocks)")}
     res["workload"] = (f"prefix trace: {iters} iterations, Poisson(0.5) arrivals, prompts = one of 8 "
                        "system prompts (512-2048 tokens) + lognormal own tokens (median 256, "
                        "sigma 1, cap 8192), geometric outputs (mean 256), <=256 running, "

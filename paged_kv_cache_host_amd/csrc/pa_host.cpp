@@ -30,6 +30,7 @@
 // match cover all earlier positions, and keys are compared in full, so no
 // hash collision can produce a false match.  A block leaves the index when
 // the last table holding it is released.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -55,16 +56,14 @@ struct Seq {
 struct BlockKey {
   int32_t parent = -1;
   std::vector<int32_t> tokens;
-  bool operator==(const BlockKey& o) const { return parent == o.parent && tokens == o.tokens; }
 };
 
-struct BlockKeyHash {
-  size_t operator()(const BlockKey& k) const {
-    uint64_t h = 1469598103934665603ull ^ static_cast<uint32_t>(k.parent);  // FNV-1a style mix
-    for (int32_t t : k.tokens) h = (h ^ static_cast<uint32_t>(t)) * 1099511628211ull;
-    return static_cast<size_t>(h ^ (h >> 29));
-  }
-};
+// FNV-1a style mix of a content, computed in place (no key object).
+inline uint64_t content_hash(int32_t parent, const int32_t* tokens, int32_t n) {
+  uint64_t h = 1469598103934665603ull ^ static_cast<uint32_t>(parent);
+  for (int32_t i = 0; i < n; ++i) h = (h ^ static_cast<uint32_t>(tokens[i])) * 1099511628211ull;
+  return h ^ (h >> 29);
+}
 
 }  // namespace
 
@@ -76,8 +75,11 @@ struct pa_pool {
   int32_t count = 0;          // number of free ids
   std::vector<int32_t> refs;  // tables holding each block (0: free)
   std::unordered_map<int64_t, Seq> seqs;
-  std::unordered_map<BlockKey, int32_t, BlockKeyHash> index;  // registered content -> block
-  std::unordered_map<int32_t, BlockKey> registered;           // block -> its content
+  // Registered contents: block -> its content, and content hash -> the
+  // blocks registered under that hash (lookups compare the stored content,
+  // so a hash collision never matches a different content).
+  std::unordered_map<int32_t, BlockKey> registered;
+  std::unordered_multimap<uint64_t, int32_t> index;
 
   int32_t at(int32_t i) const { return ring[(head + i) % num_blocks]; }
   // Take n ids from the front.  Caller has checked count >= n.
@@ -95,20 +97,38 @@ struct pa_pool {
   void give_back(const std::vector<int32_t>& ids) {
     for (int32_t b : ids) {
       if (--refs[b] > 0) continue;
-      auto r = registered.find(b);
-      if (r != registered.end()) {
-        index.erase(r->second);
-        registered.erase(r);
-      }
+      unregister(b);
       ring[(head + count) % num_blocks] = b;
       ++count;
     }
   }
-  BlockKey key_of(int32_t parent, const int32_t* tokens) const {
-    BlockKey k;
-    k.parent = parent;
-    k.tokens.assign(tokens, tokens + block_size);
-    return k;
+  bool holds(int32_t b, int32_t parent, const int32_t* tokens) const {
+    auto r = registered.find(b);
+    return r != registered.end() && r->second.parent == parent &&
+           std::equal(r->second.tokens.begin(), r->second.tokens.end(), tokens);
+  }
+  // The block registered under this content, or -1.
+  int32_t find(int32_t parent, const int32_t* tokens) const {
+    auto range = index.equal_range(content_hash(parent, tokens, block_size));
+    for (auto it = range.first; it != range.second; ++it)
+      if (holds(it->second, parent, tokens)) return it->second;
+    return -1;
+  }
+  void add(int32_t b, int32_t parent, const int32_t* tokens) {
+    registered.emplace(b, BlockKey{parent, std::vector<int32_t>(tokens, tokens + block_size)});
+    index.emplace(content_hash(parent, tokens, block_size), b);
+  }
+  void unregister(int32_t b) {
+    auto r = registered.find(b);
+    if (r == registered.end()) return;
+    auto range = index.equal_range(content_hash(r->second.parent, r->second.tokens.data(),
+                                                block_size));
+    for (auto it = range.first; it != range.second; ++it)
+      if (it->second == b) {
+        index.erase(it);
+        break;
+      }
+    registered.erase(r);
   }
 };
 
@@ -258,23 +278,23 @@ pa_status pa_seq_register_prefix(pa_pool* pool, int64_t seq, const int32_t* toke
   // validate first (all or nothing): a block that is already registered
   // must be registered under this content
   for (int32_t i = 0; i < n_full; ++i) {
-    auto r = pool->registered.find(s.table[i]);
-    if (r != pool->registered.end() &&
-        !(r->second == pool->key_of(i ? s.table[i - 1] : -1, tokens + static_cast<int64_t>(i) * bs)))
+    const int32_t b = s.table[i];
+    if (pool->registered.count(b) &&
+        !pool->holds(b, i ? s.table[i - 1] : -1, tokens + static_cast<int64_t>(i) * bs))
       return fail(PA_ERR_INVALID,
                   "pa_seq_register_prefix: block %d of sequence %lld is registered with other "
                   "token ids", i, (long long)seq);
   }
   for (int32_t i = 0; i < n_full; ++i) {
     const int32_t b = s.table[i];
-    BlockKey k = pool->key_of(i ? s.table[i - 1] : -1, tokens + static_cast<int64_t>(i) * bs);
-    auto f = pool->index.find(k);
-    if (f != pool->index.end()) {
-      if (f->second == b) continue;  // this very block
+    const int32_t parent = i ? s.table[i - 1] : -1;
+    const int32_t* t = tokens + static_cast<int64_t>(i) * bs;
+    const int32_t f = pool->find(parent, t);
+    if (f >= 0) {
+      if (f == b) continue;  // this very block
       break;  // the same content lives in another block: lookups go there
     }
-    pool->registered.emplace(b, k);
-    pool->index.emplace(std::move(k), b);
+    pool->add(b, parent, t);
   }
   return PA_OK;
 }
@@ -290,10 +310,10 @@ pa_status pa_seq_create_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens
   std::vector<int32_t> matched;
   int32_t parent = -1;
   for (int32_t i = 0; i < num_tokens / bs; ++i) {
-    auto f = pool->index.find(pool->key_of(parent, tokens + static_cast<int64_t>(i) * bs));
-    if (f == pool->index.end()) break;
-    matched.push_back(f->second);
-    parent = f->second;
+    const int32_t f = pool->find(parent, tokens + static_cast<int64_t>(i) * bs);
+    if (f < 0) break;
+    matched.push_back(f);
+    parent = f;
   }
   const int64_t need = ceil_div64(num_tokens, bs) - static_cast<int64_t>(matched.size());
   if (need > pool->count)
@@ -320,9 +340,9 @@ pa_status pa_pool_match_prefix(const pa_pool* pool, const int32_t* tokens, int32
   const int32_t bs = pool->block_size;
   int32_t parent = -1, n = 0;
   for (int32_t i = 0; i < num_tokens / bs; ++i) {
-    auto f = pool->index.find(pool->key_of(parent, tokens + static_cast<int64_t>(i) * bs));
-    if (f == pool->index.end()) break;
-    parent = f->second;
+    const int32_t f = pool->find(parent, tokens + static_cast<int64_t>(i) * bs);
+    if (f < 0) break;
+    parent = f;
     ++n;
   }
   *matched_out = n * bs;
