@@ -194,10 +194,30 @@ pa_status pa_seq_create_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens
 
 /* The lookup of pa_seq_create_prefix without its effects [host]: tokens
  * (a multiple of block_size) of the leading full blocks of tokens[0 ..
- * num_tokens) whose content is registered, into *matched_out.  Errors:
- * PA_ERR_INVALID (NULL pool or matched_out, num_tokens < 0, NULL tokens). */
+ * num_tokens) whose content is registered, into *matched_out, and how many
+ * of those blocks are retained rather than held (they are counted as free,
+ * so a caller checking the fit subtracts them), into *retained_out
+ * (optional).  Errors: PA_ERR_INVALID (NULL pool or matched_out,
+ * num_tokens < 0, NULL tokens). */
 pa_status pa_pool_match_prefix(const pa_pool* pool, const int32_t* tokens, int32_t num_tokens,
-                               int32_t* matched_out);
+                               int32_t* matched_out, int32_t* retained_out);
+
+/* Prefix retention [host; off by default, which is ARTICLE 2.2's plain FIFO
+ * pool]: with enable != 0, a registered block that its last holder releases
+ * is retained (still found by its content) instead of joining the free
+ * list; retained blocks count as free, fresh blocks are taken from the free
+ * list first and only then from the retained blocks, oldest release first,
+ * each leaving the index as it is taken, and a block that
+ * pa_seq_create_prefix finds while retained comes back into use.
+ * pa_pool_free_list lists the free list, then the retained blocks in that
+ * order.  Turning it off moves the retained blocks, oldest first, to the
+ * back of the free list and out of the index.  PA_ERR_INVALID for a NULL
+ * pool.  Keeping a prefix after its last request has finished is an
+ * extension beyond the pages (their reuse is among running requests). */
+pa_status pa_pool_set_prefix_retention(pa_pool* pool, int32_t enable);
+
+/* Retained blocks (-1 for a NULL pool). */
+int32_t pa_pool_num_retained(const pa_pool* pool);
 
 /* Number of registered blocks (-1 for a NULL pool). */
 int32_t pa_pool_num_registered(const pa_pool* pool);

@@ -49,10 +49,21 @@ scheduler's added work; it gives no algorithm).  Readings taken:
 * content already registered for another block is not registered again
   (registration of that sequence stops there); a block leaves the index when
   it returns to the free list.
+
+Prefix retention (an extension, off by default: the pages reuse a prefix
+among running requests).  Read as follows: a registered block whose last
+holder lets go is retained, still found by its content, instead of joining
+the free list; retained blocks count as free; fresh blocks are taken from the
+free list first and then from the retained blocks, oldest release first,
+each leaving the index as it is taken; a lookup that finds a retained block
+brings it back into use; the free list as listed is the free list followed
+by the retained blocks in that order; turning retention off moves the
+retained blocks, oldest first, to the back of the free list and out of the
+index.
 """
 from __future__ import annotations
 
-from collections import deque
+from collections import OrderedDict, deque
 
 OK = 0
 ERR_INVALID = -1
@@ -83,12 +94,26 @@ class BlockPool:
         self.refs = [0] * self.num_blocks   # tables holding each block
         self.index: dict = {}               # (previous block, token ids) -> block
         self.content: dict = {}             # block -> its key in the index
+        self.retain = False                 # prefix retention
+        self.retained = OrderedDict()       # retained blocks, oldest release first
 
     # -- ARTICLE §2.2: allocate / free ---------------------------------------
+    def _unregister(self, b: int):
+        key = self.content.pop(b, None)
+        if key is not None:
+            del self.index[key]
+
     def _take(self, n: int):
-        if len(self.free) < n:
+        if self.num_free() < n:
             return None
-        ids = [self.free.popleft() for _ in range(n)]
+        ids = []
+        for _ in range(n):
+            if self.free:
+                b = self.free.popleft()
+            else:
+                b, _ = self.retained.popitem(last=False)
+                self._unregister(b)
+            ids.append(b)
         for b in ids:
             self.refs[b] = 1
         return ids
@@ -97,14 +122,27 @@ class BlockPool:
         for b in ids:
             self.refs[b] -= 1
             if self.refs[b] == 0:
-                key = self.content.pop(b, None)
-                if key is not None:
-                    del self.index[key]
+                if self.retain and b in self.content:
+                    self.retained[b] = None
+                    continue
+                self._unregister(b)
                 self.free.append(b)
+
+    def set_prefix_retention(self, on: bool):
+        self.retain = bool(on)
+        if not self.retain:
+            for b in list(self.retained):
+                self._unregister(b)
+                self.free.append(b)
+            self.retained.clear()
+        return OK
+
+    def num_retained(self) -> int:
+        return len(self.retained)
 
     # -- sequence-level verbs -------------------------------------------------
     def num_free(self) -> int:
-        return len(self.free)
+        return len(self.free) + len(self.retained)
 
     def seq_create(self, seq: int, num_tokens: int) -> int:
         if num_tokens < 0:
@@ -181,28 +219,36 @@ class BlockPool:
                 break
             matched.append(b)
             parent = b
-        fresh = self._take(ceil_div(len(tokens), bs) - len(matched))
-        if fresh is None:
+        # matched blocks nobody holds (retained) come back into use: they
+        # are not available as fresh blocks
+        idle = [b for b in matched if self.refs[b] == 0]
+        if ceil_div(len(tokens), bs) - len(matched) > self.num_free() - len(idle):
             return ERR_NO_BLOCKS, 0
+        for b in idle:
+            del self.retained[b]
+        fresh = self._take(ceil_div(len(tokens), bs) - len(matched))
+        assert fresh is not None
         for b in matched:
             self.refs[b] += 1
         self.tables[seq] = matched + fresh
         self.lengths[seq] = len(tokens)
         return OK, len(matched) * bs
 
-    def match_prefix(self, tokens) -> int:
+    def match_prefix(self, tokens, with_retained: bool = False):
         """Tokens of the leading full blocks of ``tokens`` whose content is
-        registered (the walk of ``seq_create_prefix``, nothing taken)."""
+        registered (the walk of ``seq_create_prefix``, nothing taken)[, and
+        how many of those blocks are retained rather than held]."""
         tokens = [int(t) for t in tokens]
         bs = self.block_size
-        n, parent = 0, -1
+        n, idle, parent = 0, 0, -1
         for i in range(len(tokens) // bs):
             b = self.index.get((parent, tuple(tokens[i * bs:(i + 1) * bs])))
             if b is None:
                 break
             n += 1
+            idle += self.refs[b] == 0
             parent = b
-        return n * bs
+        return (n * bs, idle) if with_retained else n * bs
 
     def num_registered(self) -> int:
         return len(self.content)
@@ -258,4 +304,5 @@ class BlockPool:
         return tables, lens
 
     def free_list(self) -> list[int]:
-        return list(self.free)
+        """The free list, then the retained blocks, oldest release first."""
+        return list(self.free) + list(self.retained)

@@ -173,8 +173,10 @@ class Scheduler:
         """Admission of a request with token ids; False if it does not fit."""
         bs = self.pool.block_size
         head = s.ids[:s.prompt_len - 1]          # the last prompt token is always computed
-        matched = self.pool.match_prefix(head)
-        if self.pool.num_free() < ceil_div(s.known, bs) - matched // bs:
+        matched, idle = self.pool.match_prefix(head, with_retained=True)
+        # matched blocks that are retained rather than held count as free but
+        # come back into use: they are not fresh blocks
+        if self.pool.num_free() - idle < ceil_div(s.known, bs) - matched // bs:
             return False
         st, shared = self.pool.seq_create_prefix(s.sid, head)
         assert st == OK and shared == matched

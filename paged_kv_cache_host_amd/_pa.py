@@ -80,7 +80,9 @@ _SIGS = {
     "pa_pool_block_refs": (_i32, [_vp, _i32, _i32p]),
     "pa_seq_register_prefix": (_i32, [_vp, _i64, _i32p, _i32]),
     "pa_seq_create_prefix": (_i32, [_vp, _i64, _i32p, _i32, _i32p]),
-    "pa_pool_match_prefix": (_i32, [_vp, _i32p, _i32, _i32p]),
+    "pa_pool_match_prefix": (_i32, [_vp, _i32p, _i32, _i32p, _i32p]),
+    "pa_pool_set_prefix_retention": (_i32, [_vp, _i32]),
+    "pa_pool_num_retained": (_i32, [_vp]),
     "pa_pool_num_registered": (_i32, [_vp]),
     "pa_seq_length": (_i32, [_vp, _i64, _i32p]),
     "pa_seq_block_table": (_i32, [_vp, _i64, _i32p, _i32, _i32p]),
@@ -257,13 +259,23 @@ def pa_seq_create_prefix(pool, seq: int, tokens):
     return st, out.value
 
 
-def pa_pool_match_prefix(pool, tokens):
+def pa_pool_match_prefix(pool, tokens, with_retained: bool = False):
     """Returns (status, tokens of the leading full blocks of ``tokens``
-    whose content is registered); changes nothing."""
+    whose content is registered[, how many of those blocks are retained]);
+    changes nothing."""
     t = _i32_array(tokens)
-    out = _i32(0)
-    st = _lib.pa_pool_match_prefix(pool, _ptr_i32(t) if len(t) else None, len(t), C.byref(out))
-    return st, out.value
+    out, ret = _i32(0), _i32(0)
+    st = _lib.pa_pool_match_prefix(pool, _ptr_i32(t) if len(t) else None, len(t), C.byref(out),
+                                   C.byref(ret))
+    return (st, out.value, ret.value) if with_retained else (st, out.value)
+
+
+def pa_pool_set_prefix_retention(pool, enable: bool) -> int:
+    return _lib.pa_pool_set_prefix_retention(pool, 1 if enable else 0)
+
+
+def pa_pool_num_retained(pool) -> int:
+    return _lib.pa_pool_num_retained(pool)
 
 
 def pa_pool_num_registered(pool) -> int:

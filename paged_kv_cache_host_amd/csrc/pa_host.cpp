@@ -34,6 +34,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <iterator>
+#include <list>
 #include <new>
 #include <string>
 #include <unordered_map>
@@ -82,21 +84,51 @@ struct pa_pool {
   std::unordered_multimap<uint64_t, int32_t> index;
 
   int32_t at(int32_t i) const { return ring[(head + i) % num_blocks]; }
-  // Take n ids from the front.  Caller has checked count >= n.
+  // Prefix retention (off by default): a registered block whose last holder
+  // lets go waits here, oldest first, still findable by its content, instead
+  // of joining the free list; fresh blocks come from the free list first and
+  // only then from the front of this list (leaving the index).
+  bool retain = false;
+  std::list<int32_t> lru;
+  std::unordered_map<int32_t, std::list<int32_t>::iterator> lru_pos;
+
+  int32_t available() const { return count + static_cast<int32_t>(lru.size()); }
+  // Take n ids: the front of the free list, then the oldest retained blocks.
+  // Caller has checked available() >= n.
   void take(int32_t n, std::vector<int32_t>& dst) {
     for (int32_t i = 0; i < n; ++i) {
-      const int32_t b = ring[head];
+      int32_t b;
+      if (count > 0) {
+        b = ring[head];
+        head = head + 1 == num_blocks ? 0 : head + 1;
+        --count;
+      } else {
+        b = lru.front();
+        lru.pop_front();
+        lru_pos.erase(b);
+        unregister(b);
+      }
       dst.push_back(b);
       refs[b] = 1;
-      head = head + 1 == num_blocks ? 0 : head + 1;
     }
-    count -= n;
+  }
+  // A retained block found by a lookup goes back into use.
+  void revive(int32_t b) {
+    auto it = lru_pos.find(b);
+    lru.erase(it->second);
+    lru_pos.erase(it);
   }
   // Drop one reference to each id, in order; ids nobody holds any more go to
-  // the back of the free list.
+  // the back of the free list (retained instead when retention is on and
+  // the block is registered).
   void give_back(const std::vector<int32_t>& ids) {
     for (int32_t b : ids) {
       if (--refs[b] > 0) continue;
+      if (retain && registered.count(b)) {
+        lru.push_back(b);
+        lru_pos.emplace(b, std::prev(lru.end()));
+        continue;
+      }
       unregister(b);
       ring[(head + count) % num_blocks] = b;
       ++count;
@@ -197,7 +229,7 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* 
 
 void pa_pool_destroy(pa_pool* pool) { delete pool; }
 
-int32_t pa_pool_num_free(const pa_pool* pool) { return pool ? pool->count : -1; }
+int32_t pa_pool_num_free(const pa_pool* pool) { return pool ? pool->available() : -1; }
 
 int32_t pa_pool_num_seqs(const pa_pool* pool) {
   return pool ? static_cast<int32_t>(pool->seqs.size()) : -1;
@@ -205,11 +237,13 @@ int32_t pa_pool_num_seqs(const pa_pool* pool) {
 
 pa_status pa_pool_free_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n) {
   if (!pool || !n) return fail(PA_ERR_INVALID, "pa_pool_free_list: NULL argument");
-  *n = pool->count;
-  if (cap < pool->count || (pool->count > 0 && !out))
+  *n = pool->available();
+  if (cap < pool->available() || (pool->available() > 0 && !out))
     return fail(PA_ERR_INVALID, "pa_pool_free_list: capacity %d < %d free blocks", cap,
-                pool->count);
+                pool->available());
   for (int32_t i = 0; i < pool->count; ++i) out[i] = pool->at(i);
+  int32_t k = pool->count;
+  for (int32_t b : pool->lru) out[k++] = b;  // retained blocks, in eviction order
   return PA_OK;
 }
 
@@ -219,9 +253,9 @@ pa_status pa_seq_create(pa_pool* pool, int64_t seq, int32_t num_tokens) {
   if (pool->seqs.count(seq))
     return fail(PA_ERR_EXISTS, "pa_seq_create: sequence %lld exists", (long long)seq);
   int64_t need = ceil_div64(num_tokens, pool->block_size);
-  if (need > pool->count)
+  if (need > pool->available())
     return fail(PA_ERR_NO_BLOCKS, "pa_seq_create: need %lld blocks, %d free", (long long)need,
-                pool->count);
+                pool->available());
   Seq s;
   s.table.reserve(static_cast<size_t>(need));
   pool->take(static_cast<int32_t>(need), s.table);
@@ -245,9 +279,9 @@ pa_status pa_seq_share(pa_pool* pool, int64_t seq, int64_t src, int32_t shared_t
                 shared_tokens, from.len, num_tokens);
   const int32_t n_shared = shared_tokens / pool->block_size;
   const int64_t need = ceil_div64(num_tokens, pool->block_size) - n_shared;
-  if (need > pool->count)
+  if (need > pool->available())
     return fail(PA_ERR_NO_BLOCKS, "pa_seq_share: need %lld blocks, %d free", (long long)need,
-                pool->count);
+                pool->available());
   Seq s;
   s.table.reserve(static_cast<size_t>(n_shared + need));
   for (int32_t i = 0; i < n_shared; ++i) {
@@ -315,15 +349,19 @@ pa_status pa_seq_create_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens
     matched.push_back(f);
     parent = f;
   }
+  // matched blocks that nobody holds (retained) come back into use and are
+  // not available as fresh blocks
+  int32_t idle = 0;
+  for (int32_t b : matched) idle += pool->refs[b] == 0;
   const int64_t need = ceil_div64(num_tokens, bs) - static_cast<int64_t>(matched.size());
-  if (need > pool->count)
+  if (need > pool->available() - idle)
     return fail(PA_ERR_NO_BLOCKS, "pa_seq_create_prefix: need %lld blocks, %d free",
-                (long long)need, pool->count);
+                (long long)need, pool->available() - idle);
   Seq s;
   s.table.reserve(matched.size() + static_cast<size_t>(need));
   for (int32_t b : matched) {
     s.table.push_back(b);
-    ++pool->refs[b];
+    if (pool->refs[b]++ == 0) pool->revive(b);
   }
   pool->take(static_cast<int32_t>(need), s.table);
   s.len = num_tokens;
@@ -333,20 +371,42 @@ pa_status pa_seq_create_prefix(pa_pool* pool, int64_t seq, const int32_t* tokens
 }
 
 pa_status pa_pool_match_prefix(const pa_pool* pool, const int32_t* tokens, int32_t num_tokens,
-                               int32_t* matched_out) {
+                               int32_t* matched_out, int32_t* retained_out) {
   if (!pool || !matched_out) return fail(PA_ERR_INVALID, "pa_pool_match_prefix: NULL argument");
   if (num_tokens < 0 || (num_tokens > 0 && !tokens))
     return fail(PA_ERR_INVALID, "pa_pool_match_prefix: num_tokens=%d or NULL tokens", num_tokens);
   const int32_t bs = pool->block_size;
-  int32_t parent = -1, n = 0;
+  int32_t parent = -1, n = 0, idle = 0;
   for (int32_t i = 0; i < num_tokens / bs; ++i) {
     const int32_t f = pool->find(parent, tokens + static_cast<int64_t>(i) * bs);
     if (f < 0) break;
+    idle += pool->refs[f] == 0;
     parent = f;
     ++n;
   }
   *matched_out = n * bs;
+  if (retained_out) *retained_out = idle;
   return PA_OK;
+}
+
+pa_status pa_pool_set_prefix_retention(pa_pool* pool, int32_t enable) {
+  if (!pool) return fail(PA_ERR_INVALID, "pa_pool_set_prefix_retention: pool is NULL");
+  pool->retain = enable != 0;
+  if (!pool->retain) {
+    // retained blocks join the free list, oldest first, and leave the index
+    for (int32_t b : pool->lru) {
+      pool->unregister(b);
+      pool->ring[(pool->head + pool->count) % pool->num_blocks] = b;
+      ++pool->count;
+    }
+    pool->lru.clear();
+    pool->lru_pos.clear();
+  }
+  return PA_OK;
+}
+
+int32_t pa_pool_num_retained(const pa_pool* pool) {
+  return pool ? static_cast<int32_t>(pool->lru.size()) : -1;
 }
 
 int32_t pa_pool_num_registered(const pa_pool* pool) {
@@ -371,9 +431,9 @@ pa_status pa_seq_append(pa_pool* pool, int64_t seq, int32_t n_new, int32_t* slot
   int64_t new_len = static_cast<int64_t>(s.len) + n_new;
   if (new_len > INT32_MAX) return fail(PA_ERR_INVALID, "pa_seq_append: length overflow");
   int64_t need = ceil_div64(new_len, pool->block_size) - static_cast<int64_t>(s.table.size());
-  if (need > pool->count)
+  if (need > pool->available())
     return fail(PA_ERR_NO_BLOCKS, "pa_seq_append: need %lld blocks, %d free", (long long)need,
-                pool->count);
+                pool->available());
   if (need > 0) pool->take(static_cast<int32_t>(need), s.table);
   const int32_t bs = pool->block_size;
   if (slots_out) {

@@ -279,10 +279,12 @@ pa_status pa_sched_step(pa_sched* s, pa_sched_batch* b) {
         // shared: leading full blocks of the prompt but its last token
         const int32_t* ids = s->prompt_ids[q.id].data();
         const int32_t m_len = q.prompt - 1;
-        int32_t matched = 0;
-        st = pa_pool_match_prefix(pool, ids, m_len, &matched);
+        int32_t matched = 0, idle = 0;
+        st = pa_pool_match_prefix(pool, ids, m_len, &matched, &idle);
         if (st != PA_OK) return st;
-        if (pa_pool_num_free(pool) <
+        // (matched blocks that are retained rather than held count as free
+        // but come back into use: they are not fresh blocks)
+        if (pa_pool_num_free(pool) - idle <
             ceil_div32(q.known, s->block_size) - matched / s->block_size)
           break;
         int32_t shared = 0;

@@ -52,12 +52,13 @@ def _trace():
     return w, host_rows, n_rows
 
 
-def _replay(w, host_rows, sm, results, mode="chunked", ids=None):
+def _replay(w, host_rows, sm, results, mode="chunked", ids=None, retain=False):
     """Run the oracle's scheduler, cache scatter and attention over the same
     trace and compare every iteration's record and outputs (``results[it]``
     = (record, decode output, prefill output), decoded to float).  ``ids``:
     prompt token ids per request (prefix caching)."""
     pool = oa.BlockPool(w.num_blocks, 16)
+    pool.set_prefix_retention(retain)
     sch = Scheduler(pool, R, BUDGET[mode], mode=mode)
     kc, vc = oc.new_cache(w.num_blocks, H_KV, 16, D, "bf16")
     checked = {"decode": 0, "prefill": 0}
@@ -238,14 +239,14 @@ def test_serve_live_clock(mode):
         f"TTFT mean {r['ttft']['mean_ms']:.3f} ms")
 
 
-def _prefix_trace():
+def _prefix_trace(lam=0.5, iters=80, out_mean=30):
     """The trace above with every prompt behind one of three system prefixes
     (40, 64 and 100 tokens) and its own tokens after it.  A prefix's token
     rows are the same for every request that starts with it, as its K/V
     would be; prompt token ids are the prefix's ids, then the request's."""
     from types import SimpleNamespace
-    base = workloads.trace(seed=SEED + 1, iters=80, lam=0.5, prompt_median=40, prompt_sigma=0.8,
-                           prompt_cap=300, out_mean=30, num_blocks=80)
+    base = workloads.trace(seed=SEED + 1, iters=iters, lam=lam, prompt_median=40,
+                           prompt_sigma=0.8, prompt_cap=300, out_mean=out_mean, num_blocks=80)
     rng = np.random.default_rng(SEED)
     plens = [40, 64, 100]
     pids = [rng.integers(0, 30000, n).astype(np.int32) for n in plens]
@@ -278,17 +279,23 @@ def _prefix_trace():
     return w, host_rows, n_rows, ids
 
 
-def test_trace_prefix_caching_matches_oracle():
+@pytest.mark.parametrize("retain,lam,iters,out_mean,min_hits", [(False, 0.5, 80, 30, 200),
+                                                                 (True, 0.1, 160, 10, 500)])
+def test_trace_prefix_caching_matches_oracle(retain, lam, iters, out_mean, min_hits):
     """Prefix caching through whole iterations: requests queued with their
     prompt token ids share the prompt blocks earlier requests computed, and
-    prefill only after them.  Schedule, cache and every decode and prefill
-    output against the oracle's scheduler (same readings) and fp64
-    attention over the same cache."""
+    prefill only after them; with ``retain`` (sparser arrivals) the pool
+    keeps finished requests' prompt blocks findable, so later requests also
+    attend blocks brought back from retention.  Schedule, cache and every
+    decode and prefill output against the oracle's scheduler (same
+    readings) and fp64 attention over the same cache."""
+    from paged_kv_cache_host_amd import _pa as pa
     from paged_kv_cache_host_amd.engine import to_device_raw
     from paged_kv_cache_host_amd.iteration import LayerIterations
 
-    w, host_rows, max_ctx, ids = _prefix_trace()
-    say(f"[trace parity, prefix caching] {w.name} pool={w.num_blocks} running<={R} budget={B}")
+    w, host_rows, max_ctx, ids = _prefix_trace(lam, iters, out_mean)
+    say(f"[trace parity, prefix caching, retain={retain}] {w.name} pool={w.num_blocks} "
+        f"running<={R} budget={B}")
 
     def provider(seqs, positions):
         k, v, q = host_rows(seqs, positions)
@@ -297,6 +304,7 @@ def test_trace_prefix_caching_matches_oracle():
 
     run = LayerIterations(w.num_blocks, H_Q, H_KV, D, "cuda", provider, R, B,
                           max_context=max_ctx, fill_outputs=SENTINEL)
+    pa.check(pa.pa_pool_set_prefix_retention(run.pool, retain))
     results = []
     for it in range(w.iters):
         for sid, p, o in w.arrivals[it]:
@@ -308,9 +316,10 @@ def test_trace_prefix_caching_matches_oracle():
         run.step(keep)
     hits = run.acc["prefix_hit_tokens"]
     run.close()
-    checked, worst, _, _, _ = _replay(w, host_rows, run.sm, results, ids=ids)
+    checked, worst, _, _, _ = _replay(w, host_rows, run.sm, results, ids=ids, retain=retain)
     say(f"    checked {checked['decode']} decode tokens, {checked['prefill']} prefill tokens, "
         f"{hits} prompt tokens found shared, {run.totals['preempted']} preemptions, "
         f"max|d| = {worst:.3g}")
-    assert hits == checked["prefix_hits"] and hits > 200
+    # (with retention the sparse trace finds 768 prompt tokens, 160 without)
+    assert hits == checked["prefix_hits"] and hits > min_hits
     assert checked["decode"] > 50 and checked["prefill"] > 300

@@ -477,3 +477,104 @@ def test_prefix_sharing_bit_exact_against_oracle(oplist, nblocks, rnd):
                 assert pa.pa_seq_length(pool, s)[1] == ref.lengths[s]
     finally:
         pa.pa_pool_destroy(pool)
+
+
+def test_prefix_retention_golden_trace_through_c_abi():
+    """tests/golden/prefix_retention_trace.json (hand-worked) through the C
+    allocator: statuses, shared and matched counts, tables, free list,
+    registered and retained counts, reference counts."""
+    g = json.load(open(os.path.join(GOLDEN, "prefix_retention_trace.json")))
+    st_, pool = pa.pa_pool_create(g["num_blocks"], g["block_size"], g["initial_free_order"])
+    assert st_ == pa.PA_OK
+    try:
+        for i, step in enumerate(g["steps"]):
+            op = step["op"]
+            res = {}
+            if op == "retention":
+                res["status"] = pa.pa_pool_set_prefix_retention(pool, step["on"])
+            elif op == "create_prefix":
+                res["status"], res["shared_out"] = pa.pa_seq_create_prefix(pool, step["seq"],
+                                                                           step["tokens"])
+            elif op == "register":
+                res["status"] = pa.pa_seq_register_prefix(pool, step["seq"], step["tokens"])
+            elif op == "release":
+                res["status"] = pa.pa_seq_release(pool, step["seq"])
+            elif op == "create":
+                res["status"] = pa.pa_seq_create(pool, step["seq"], step["n"])
+            else:
+                res["status"], res["matched"], res["matched_retained"] = \
+                    pa.pa_pool_match_prefix(pool, step["tokens"], with_retained=True)
+            res["free"] = _state(pool)
+            res["registered"] = pa.pa_pool_num_registered(pool)
+            res["retained"] = pa.pa_pool_num_retained(pool)
+            if "table" in step:
+                res["table"] = list(pa.pa_seq_block_table(pool, step["seq"])[1])
+            if "refs" in step:
+                res["refs"] = [pa.pa_pool_block_refs(pool, b)[1] for b in range(g["num_blocks"])]
+            for k, v in step.items():
+                if k in res and not (k == "shared_out" and res["status"] != pa.PA_OK):
+                    assert res[k] == v, (i, op, k, res[k], v)
+    finally:
+        pa.pa_pool_destroy(pool)
+
+
+retain_ops = st.lists(st.tuples(st.sampled_from(["create", "register", "append", "release",
+                                                 "match", "plain", "retain_on", "retain_off"]),
+                                st.integers(0, 7), st.lists(st.integers(0, 1), max_size=40),
+                                st.integers(0, 40)), max_size=80)
+
+
+@settings(max_examples=300, deadline=None)
+@given(retain_ops, st.integers(0, 40), st.randoms(use_true_random=False))
+def test_prefix_retention_bit_exact_against_oracle(oplist, nblocks, rnd):
+    """Random sequences of the detection operations, plain creates and
+    retention switched on and off, over a two-letter token alphabet: every
+    status, count, table, the free list (retained blocks after it) and the
+    reference counts equal the oracle's after every operation."""
+    order = list(range(nblocks))
+    rnd.shuffle(order)
+    ref = oa.BlockPool(nblocks, 4, order)
+    st_, pool = pa.pa_pool_create(nblocks, 4, order)
+    assert st_ == pa.PA_OK
+    ref.set_prefix_retention(True)
+    assert pa.pa_pool_set_prefix_retention(pool, True) == pa.PA_OK
+    toks = {}
+    try:
+        for op, seq, tokens, n in oplist:
+            if op == "create":
+                r1 = pa.pa_seq_create_prefix(pool, seq, tokens)
+                assert r1 == ref.seq_create_prefix(seq, tokens)
+                if r1[0] == pa.PA_OK:
+                    toks[seq] = list(tokens)
+            elif op == "plain":
+                s1 = pa.pa_seq_create(pool, seq, n)
+                assert s1 == ref.seq_create(seq, n)
+                if s1 == pa.PA_OK:
+                    toks[seq] = [rnd.randint(0, 1) for _ in range(n)]
+            elif op == "register":
+                t = toks.get(seq, [])[:n]
+                assert pa.pa_seq_register_prefix(pool, seq, t) == ref.seq_register_prefix(seq, t)
+            elif op == "match":
+                st1, m1, r1 = pa.pa_pool_match_prefix(pool, tokens, with_retained=True)
+                assert st1 == pa.PA_OK and (m1, r1) == ref.match_prefix(tokens, with_retained=True)
+            elif op == "append":
+                s1, _ = pa.pa_seq_append(pool, seq, n % 9)
+                assert s1 == ref.seq_append(seq, n % 9)[0]
+                if s1 == pa.PA_OK:
+                    toks[seq] += [rnd.randint(0, 1) for _ in range(n % 9)]
+            elif op == "release":
+                assert pa.pa_seq_release(pool, seq) == ref.seq_release(seq)
+                toks.pop(seq, None)
+            else:
+                on = op == "retain_on"
+                assert pa.pa_pool_set_prefix_retention(pool, on) == ref.set_prefix_retention(on)
+            assert _state(pool) == ref.free_list()
+            assert pa.pa_pool_num_free(pool) == ref.num_free()
+            assert pa.pa_pool_num_registered(pool) == ref.num_registered()
+            assert pa.pa_pool_num_retained(pool) == ref.num_retained()
+            for b in range(nblocks):
+                assert pa.pa_pool_block_refs(pool, b)[1] == ref.block_refs(b)
+            for s, t in ref.tables.items():
+                assert list(pa.pa_seq_block_table(pool, s)[1]) == t
+    finally:
+        pa.pa_pool_destroy(pool)

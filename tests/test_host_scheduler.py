@@ -225,18 +225,24 @@ def test_prefix_trace_through_c():
     c.close()
 
 
-@pytest.mark.parametrize("seed,num_blocks,lam,out_max", [(1, 24, 0.6, 80), (2, 30, 0.8, 120),
-                                                          (3, 64, 1.0, 40), (4, 20, 1.0, 60)])
-def test_prefix_caching_c_matches_oracle(seed, num_blocks, lam, out_max):
+@pytest.mark.parametrize("seed,num_blocks,lam,out_max,retain",
+                         [(1, 24, 0.6, 80, False), (2, 30, 0.8, 120, False),
+                          (3, 64, 1.0, 40, False), (4, 20, 1.0, 60, False),
+                          (1, 24, 0.6, 80, True), (3, 64, 0.3, 40, True), (5, 40, 0.2, 30, True)])
+def test_prefix_caching_c_matches_oracle(seed, num_blocks, lam, out_max, retain):
     """Seeded traces whose prompts start with one of a few system prefixes
-    (some requests without token ids), preempting on the small pools: the C
-    scheduler and the oracle agree bit for bit on every step."""
+    (some requests without token ids), preempting on the small pools, with
+    and without prefix retention in the pool: the C scheduler and the oracle
+    agree bit for bit on every step."""
     rng = np.random.default_rng(seed)
     bs = 16
     prefixes = [rng.integers(0, 1000, n).tolist() for n in (17, 40, 64, 100)]
     pool = BlockPool(num_blocks, bs)
     o = Scheduler(pool, 8, 48)
     c = CSide(num_blocks, 8, 48)
+    if retain:
+        pool.set_prefix_retention(True)
+        pa.check(pa.pa_pool_set_prefix_retention(c.pool, True))
     sid = 0
     for it in range(300):
         for _ in range(rng.poisson(lam)):
@@ -256,6 +262,7 @@ def test_prefix_caching_c_matches_oracle(seed, num_blocks, lam, out_max):
         assert [a["blocks_held"], a["tokens_held"], a["unwritten"]] == list(o.held()), (seed, it)
         assert a["prefix_hit_tokens"] == o.prefix_hits, (seed, it)
         assert pa.pa_pool_num_registered(c.pool) == pool.num_registered(), (seed, it)
+        assert pa.pa_pool_num_retained(c.pool) == pool.num_retained(), (seed, it)
         assert c.free_list() == pool.free_list(), (seed, it)
     assert o.prefix_hits > 0
     c.close()
@@ -281,7 +288,7 @@ def test_sched_add_prompt_rejects():
     pa.pa_sched_destroy(sch)
     st, m = pa.pa_pool_match_prefix(pool, [1, 2, 3])
     assert st == pa.PA_OK and m == 0
-    assert pa._lib.pa_pool_match_prefix(pool, None, 4, None) == pa.PA_ERR_INVALID
+    assert pa._lib.pa_pool_match_prefix(pool, None, 4, None, None) == pa.PA_ERR_INVALID
     pa.pa_pool_destroy(pool)
 
 

@@ -539,3 +539,139 @@ def test_paged_waste_closed_form_and_exercise():
     assert 0.003 < paged < 0.007          # about 7.5 wasted tokens of ~1508 held
     assert abs(contiguous - (1 - L.mean() / 8192)) < 1e-12
     assert 0.80 < contiguous < 0.83
+
+
+# -- prefix retention (an extension beyond the pages; off by default) --------
+
+def run_retention_step(pool, step):
+    """The observable results of one step of prefix_retention_trace.json."""
+    op = step["op"]
+    res = {}
+    if op == "retention":
+        res["status"] = pool.set_prefix_retention(step["on"])
+    elif op == "create_prefix":
+        res["status"], res["shared_out"] = pool.seq_create_prefix(step["seq"], step["tokens"])
+    elif op == "register":
+        res["status"] = pool.seq_register_prefix(step["seq"], step["tokens"])
+    elif op == "release":
+        res["status"] = pool.seq_release(step["seq"])
+    elif op == "create":
+        res["status"] = pool.seq_create(step["seq"], step["n"])
+    else:
+        res["status"] = oa.OK
+        res["matched"], res["matched_retained"] = pool.match_prefix(step["tokens"],
+                                                                     with_retained=True)
+    return res
+
+
+def check_retention_trace(pool_cls):
+    """Runs tests/golden/prefix_retention_trace.json (hand-worked) on a pool
+    class with the oracle's interface; returns the first mismatch or None."""
+    g = json.load(open(os.path.join(GOLDEN, "prefix_retention_trace.json")))
+    pool = pool_cls(g["num_blocks"], g["block_size"], g["initial_free_order"])
+    for i, step in enumerate(g["steps"]):
+        try:
+            res = run_retention_step(pool, step)
+        except AssertionError:
+            return i, "raised"
+        res["free"] = pool.free_list()
+        res["registered"] = pool.num_registered()
+        res["retained"] = pool.num_retained()
+        if "table" in step:
+            res["table"] = pool.block_table(step["seq"])
+        if "refs" in step:
+            res["refs"] = [pool.block_refs(b) for b in range(g["num_blocks"])]
+        for k, v in step.items():
+            if k in res and res[k] != v and not (k == "shared_out" and res["status"] != oa.OK):
+                return i, k
+    return None
+
+
+def test_prefix_retention_hand_worked_trace():
+    assert check_retention_trace(oa.BlockPool) is None
+
+
+class _NoRevive(oa.BlockPool):
+    """Planted mistake: a retained block found by a lookup is used but stays
+    in the retained list."""
+
+    def seq_create_prefix(self, seq, tokens):
+        saved = dict(self.retained)
+        st, shared = super().seq_create_prefix(seq, tokens)
+        if st == oa.OK:
+            for b in saved:
+                if b in self.tables[seq] and b not in self.retained:
+                    self.retained[b] = None
+        return st, shared
+
+
+class _EvictNewest(oa.BlockPool):
+    """Planted mistake: the most recently retained block is evicted first."""
+
+    def _take(self, n):
+        if self.num_free() < n:
+            return None
+        ids = []
+        for _ in range(n):
+            if self.free:
+                b = self.free.popleft()
+            else:
+                b, _ = self.retained.popitem(last=True)
+                self._unregister(b)
+            ids.append(b)
+        for b in ids:
+            self.refs[b] = 1
+        return ids
+
+
+class _RetainedFirst(oa.BlockPool):
+    """Planted mistake: fresh blocks come from the retained blocks first."""
+
+    def _take(self, n):
+        if self.num_free() < n:
+            return None
+        ids = []
+        for _ in range(n):
+            if self.retained:
+                b, _ = self.retained.popitem(last=False)
+                self._unregister(b)
+            else:
+                b = self.free.popleft()
+            ids.append(b)
+        for b in ids:
+            self.refs[b] = 1
+        return ids
+
+
+class _RevivedCountFree(oa.BlockPool):
+    """Planted mistake: the fit check counts the matched retained blocks as
+    fresh blocks too."""
+
+    def seq_create_prefix(self, seq, tokens):
+        tokens = [int(t) for t in tokens]
+        if seq in self.tables:
+            return oa.ERR_EXISTS, 0
+        bs, matched, parent = self.block_size, [], -1
+        for i in range(len(tokens) // bs):
+            b = self.index.get((parent, tuple(tokens[i * bs:(i + 1) * bs])))
+            if b is None:
+                break
+            matched.append(b)
+            parent = b
+        if oa.ceil_div(len(tokens), bs) - len(matched) > self.num_free():
+            return oa.ERR_NO_BLOCKS, 0
+        for b in matched:
+            if self.refs[b] == 0:
+                del self.retained[b]
+        fresh = self._take(oa.ceil_div(len(tokens), bs) - len(matched))
+        assert fresh is not None
+        for b in matched:
+            self.refs[b] += 1
+        self.tables[seq] = matched + fresh
+        self.lengths[seq] = len(tokens)
+        return oa.OK, len(matched) * bs
+
+
+def test_prefix_retention_trace_catches_planted_mistakes():
+    for cls in (_NoRevive, _EvictNewest, _RetainedFirst, _RevivedCountFree):
+        assert check_retention_trace(cls) is not None, cls.__name__
