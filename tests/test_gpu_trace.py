@@ -52,7 +52,8 @@ def _trace():
     return w, host_rows, n_rows
 
 
-def _replay(w, host_rows, sm, results, mode="chunked", ids=None, retain=False):
+def _replay(w, host_rows, sm, results, mode="chunked", ids=None, retain=False, cache="bf16",
+            scale=1.0):
     """Run the oracle's scheduler, cache scatter and attention over the same
     trace and compare every iteration's record and outputs (``results[it]``
     = (record, decode output, prefill output), decoded to float).  ``ids``:
@@ -60,7 +61,7 @@ def _replay(w, host_rows, sm, results, mode="chunked", ids=None, retain=False):
     pool = oa.BlockPool(w.num_blocks, 16)
     pool.set_prefix_retention(retain)
     sch = Scheduler(pool, R, BUDGET[mode], mode=mode)
-    kc, vc = oc.new_cache(w.num_blocks, H_KV, 16, D, "bf16")
+    kc, vc = oc.new_cache(w.num_blocks, H_KV, 16, D, cache)
     checked = {"decode": 0, "prefill": 0}
     worst = 0.0
     written = set()
@@ -80,18 +81,18 @@ def _replay(w, host_rows, sm, results, mode="chunked", ids=None, retain=False):
         # oracle: write this iteration's tokens, then attend
         for s, a, n, slots in ob.prefill:
             k, v, _ = host_rows([s] * n, list(range(a, a + n)))
-            oc.cache_write(kc, vc, k, v, slots, "bf16", "bf16")
+            oc.cache_write(kc, vc, k, v, slots, "bf16", cache, scale, scale)
             written.update(int(x) for x in slots)
         for s, p, slot in ob.decode:
             k, v, _ = host_rows([s], [p])
-            oc.cache_write(kc, vc, k, v, [slot], "bf16", "bf16")
+            oc.cache_write(kc, vc, k, v, [slot], "bf16", cache, scale, scale)
             written.add(int(slot))
         off = 0
         for s, a, n, _ in ob.prefill:
             _, _, q = host_rows([s] * n, list(range(a, a + n)))
             ref = oat.prefill_chunk(codecs.decode(q, "bf16"), a, kc, vc, pool.block_table(s),
-                                    H_KV, sm, "bf16")
-            worst = max(worst, assert_close(pf[off:off + n], ref, "bf16",
+                                    H_KV, sm, cache, scale, scale)
+            worst = max(worst, assert_close(pf[off:off + n], ref, cache,
                                             f"iteration {it} prefill seq {s}"))
             off += n
             checked["prefill"] += n
@@ -104,8 +105,9 @@ def _replay(w, host_rows, sm, results, mode="chunked", ids=None, retain=False):
                 t = pool.block_table(s)
                 tables[i, :len(t)] = t
             lens = np.array([p + 1 for _, p, _ in ob.decode])
-            ref = oat.decode(codecs.decode(q, "bf16"), kc, vc, tables, lens, H_KV, sm, "bf16")
-            worst = max(worst, assert_close(dec, ref, "bf16", f"iteration {it} decode"))
+            ref = oat.decode(codecs.decode(q, "bf16"), kc, vc, tables, lens, H_KV, sm, cache,
+                             scale, scale)
+            worst = max(worst, assert_close(dec, ref, cache, f"iteration {it} decode"))
             checked["decode"] += len(seqs)
     if ids is not None:
         checked["prefix_hits"] = sch.prefix_hits
@@ -279,9 +281,10 @@ def _prefix_trace(lam=0.5, iters=80, out_mean=30):
     return w, host_rows, n_rows, ids
 
 
-@pytest.mark.parametrize("retain,lam,iters,out_mean,min_hits", [(False, 0.5, 80, 30, 200),
-                                                                 (True, 0.1, 160, 10, 500)])
-def test_trace_prefix_caching_matches_oracle(retain, lam, iters, out_mean, min_hits):
+@pytest.mark.parametrize("retain,lam,iters,out_mean,min_hits,cache",
+                         [(False, 0.5, 80, 30, 200, "bf16"), (True, 0.1, 160, 10, 500, "bf16"),
+                          (False, 0.5, 80, 30, 200, "fp8")])
+def test_trace_prefix_caching_matches_oracle(retain, lam, iters, out_mean, min_hits, cache):
     """Prefix caching through whole iterations: requests queued with their
     prompt token ids share the prompt blocks earlier requests computed, and
     prefill only after them; with ``retain`` (sparser arrivals) the pool
@@ -294,8 +297,9 @@ def test_trace_prefix_caching_matches_oracle(retain, lam, iters, out_mean, min_h
     from paged_kv_cache_host_amd.iteration import LayerIterations
 
     w, host_rows, max_ctx, ids = _prefix_trace(lam, iters, out_mean)
-    say(f"[trace parity, prefix caching, retain={retain}] {w.name} pool={w.num_blocks} "
-        f"running<={R} budget={B}")
+    scale = (4.9 / 448.0) if cache == "fp8" else 1.0   # e4m3 scale of N(0,1) rows
+    say(f"[trace parity, prefix caching, retain={retain}, {cache}] {w.name} "
+        f"pool={w.num_blocks} running<={R} budget={B}")
 
     def provider(seqs, positions):
         k, v, q = host_rows(seqs, positions)
@@ -303,7 +307,8 @@ def test_trace_prefix_caching_matches_oracle(retain, lam, iters, out_mean, min_h
                 to_device_raw(q, "bf16", "cuda"))
 
     run = LayerIterations(w.num_blocks, H_Q, H_KV, D, "cuda", provider, R, B,
-                          max_context=max_ctx, fill_outputs=SENTINEL)
+                          max_context=max_ctx, fill_outputs=SENTINEL, cache_dtype=cache,
+                          k_scale=scale, v_scale=scale)
     pa.check(pa.pa_pool_set_prefix_retention(run.pool, retain))
     results = []
     for it in range(w.iters):
@@ -316,7 +321,8 @@ def test_trace_prefix_caching_matches_oracle(retain, lam, iters, out_mean, min_h
         run.step(keep)
     hits = run.acc["prefix_hit_tokens"]
     run.close()
-    checked, worst, _, _, _ = _replay(w, host_rows, run.sm, results, ids=ids, retain=retain)
+    checked, worst, _, _, _ = _replay(w, host_rows, run.sm, results, ids=ids, retain=retain,
+                                      cache=cache, scale=scale)
     say(f"    checked {checked['decode']} decode tokens, {checked['prefill']} prefill tokens, "
         f"{hits} prompt tokens found shared, {run.totals['preempted']} preemptions, "
         f"max|d| = {worst:.3g}")
