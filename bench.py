@@ -41,6 +41,8 @@ Secondary legs (skipped with --decode-only):
   ``prefix_trace`` 1000 iterations of requests behind 8 shared system
                  prompts, with and without their token ids: prefill tokens
                  computed, prompt tokens found shared, output tokens/s;
+  ``preemption`` short prompts, long outputs, a small pool, running caps
+                 32..256: preemptions, recomputed prefill, output tokens/s;
   ``block_size`` the decode-70b contexts with 8/16/32-token blocks: decode
                  kernel GB/s, and the trace's fragmentation per block size;
   ``trace``      1000 continuous-batching iterations (libpa scheduler +
@@ -1354,6 +1356,76 @@ def prefix_trace_leg(args, dev):
     return res
 
 
+def preemption_leg(args, dev):
+    """ARTICLE 4.2: frequent preemption wastes work on recomputation, and the
+    pages advise a reasonable cap on concurrent sequences.  1000 iterations
+    of short prompts (lognormal median 200, cap 4096) with long outputs
+    (geometric, mean 800) on a 2048-block pool, so that admitted sequences
+    outgrow the pool, at running caps of 32, 64, 128 and 256: preemptions,
+    prefill tokens (recomputation included), output tokens, their rate and
+    the iteration time, kernels included."""
+    import torch
+
+    import workloads
+    from paged_kv_cache_host_amd.iteration import LayerIterations
+
+    w = workloads.trace(seed=5, iters=1000, lam=0.5, prompt_median=200, prompt_cap=4096,
+                        out_mean=800, num_blocks=2048)
+    B = 512
+    max_ctx = max(p + o for row in w.arrivals for _, p, o in row)
+    ring_n = 8 * (256 + B)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(8)
+    k_ring = torch.randn((ring_n, H_KV, D), generator=gen, device=dev).to(torch.bfloat16)
+    v_ring = torch.randn((ring_n, H_KV, D), generator=gen, device=dev).to(torch.bfloat16)
+    q_ring = torch.randn((ring_n, H_Q, D), generator=gen, device=dev).to(torch.bfloat16)
+    pos = [0]
+
+    def provider(seqs, positions):
+        n = len(seqs)
+        a = pos[0] if pos[0] + n <= ring_n else 0
+        pos[0] = a + n
+        return k_ring[a:a + n], v_ring[a:a + n], q_ring[a:a + n]
+
+    res = {}
+    # untimed warm-up: the first iterations of a fresh driver carry one-time
+    # set-up (library kernels' first launches, allocator caches)
+    run = LayerIterations(w.num_blocks, H_Q, H_KV, D, dev, provider, 64, B,
+                          max_context=max_ctx, provider_syncs=False)
+    for it in range(100):
+        for sid, p_, o in w.arrivals[it]:
+            run.add(sid, p_, o)
+        run.step()
+    run.synchronize()
+    run.close()
+    del run
+    for R in (32, 64, 128, 256):
+        run = LayerIterations(w.num_blocks, H_Q, H_KV, D, dev, provider, R, B,
+                              max_context=max_ctx, provider_syncs=False)
+        torch.cuda.synchronize()
+        _settle()
+        t0 = time.perf_counter()
+        for it in range(w.iters):
+            for sid, p_, o in w.arrivals[it]:
+                run.add(sid, p_, o)
+            run.step()
+        run.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        res[f"max_running_{R}"] = {
+            "preemptions": run.totals["preempted"], "prefill_tokens": run.totals["prefill_tokens"],
+            "output_tokens": run.totals["decode_tokens"], "finished": run.totals["finished"],
+            "ms_per_iteration": round(wall / w.iters * 1e3, 4),
+            "output_tokens_per_s": round(run.totals["decode_tokens"] / wall, 1)}
+        run.close()
+        del run
+        torch.cuda.empty_cache()
+    res["workload"] = ("preemption: 1000 iterations, Poisson(0.5) arrivals, lognormal prompts "
+                       "(median 200, sigma 1, cap 4096), geometric outputs (mean 800), pool 2048 "
+                       "blocks, 512-token prefill budget, 64/8 heads, d128, bf16, one layer")
+    return res
+
+
 def trace_leg(args, dev):
     """The continuous-batching trace: Poisson arrivals, lognormal prompts,
     geometric outputs, 256 running, 512-token prefill budget, 1000
@@ -1658,6 +1730,7 @@ def main():
         result["fp8_prefill"] = fp8_prefill_leg(args, dev)
         result["prefix_sharing"] = prefix_leg(args, dev)
         result["prefix_trace"] = prefix_trace_leg(args, dev)
+        result["preemption"] = preemption_leg(args, dev)
         result["block_size"] = block_size_leg(args, dev)
         result["trace"] = trace_leg(args, dev)
         result["schedules"] = modes_leg(args, dev)
