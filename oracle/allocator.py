@@ -53,7 +53,9 @@ scheduler's added work; it gives no algorithm).  Readings taken:
 Prefix retention (an extension, off by default: the pages reuse a prefix
 among running requests).  Read as follows: a registered block whose last
 holder lets go is retained, still found by its content, instead of joining
-the free list; retained blocks count as free; fresh blocks are taken from the
+the free list (the blocks one release retains enter deepest first, i.e. in
+reverse table order, so a chain is evicted from its tail); retained blocks
+count as free; fresh blocks are taken from the
 free list first and then from the retained blocks, oldest release first,
 each leaving the index as it is taken; a lookup that finds a retained block
 brings it back into use; the free list as listed is the free list followed
@@ -119,14 +121,17 @@ class BlockPool:
         return ids
 
     def _give_back(self, ids):
+        kept = []
         for b in ids:
             self.refs[b] -= 1
             if self.refs[b] == 0:
                 if self.retain and b in self.content:
-                    self.retained[b] = None
+                    kept.append(b)
                     continue
                 self._unregister(b)
                 self.free.append(b)
+        for b in reversed(kept):      # deepest first: chains are evicted from the tail
+            self.retained[b] = None
 
     def set_prefix_retention(self, on: bool):
         self.retain = bool(on)

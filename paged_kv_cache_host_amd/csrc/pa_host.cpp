@@ -119,14 +119,17 @@ struct pa_pool {
     lru_pos.erase(it);
   }
   // Drop one reference to each id, in order; ids nobody holds any more go to
-  // the back of the free list (retained instead when retention is on and
-  // the block is registered).
+  // the back of the free list, in that order.  With retention on, the
+  // registered ones are retained instead, deepest first (reverse table
+  // order), so that a chain is evicted from its tail and its head, through
+  // which every lookup enters it, stays findable longest.
   void give_back(const std::vector<int32_t>& ids) {
+    auto at = lru.end();  // each retained block goes in front of the last one
     for (int32_t b : ids) {
       if (--refs[b] > 0) continue;
       if (retain && registered.count(b)) {
-        lru.push_back(b);
-        lru_pos.emplace(b, std::prev(lru.end()));
+        at = lru.insert(at, b);
+        lru_pos[b] = at;
         continue;
       }
       unregister(b);

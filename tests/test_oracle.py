@@ -672,6 +672,21 @@ class _RevivedCountFree(oa.BlockPool):
         return oa.OK, len(matched) * bs
 
 
+class _RetainInTableOrder(oa.BlockPool):
+    """Planted mistake: a release retains its blocks in table order, so the
+    head of a chain is evicted first and strands the rest."""
+
+    def _give_back(self, ids):
+        for b in ids:
+            self.refs[b] -= 1
+            if self.refs[b] == 0:
+                if self.retain and b in self.content:
+                    self.retained[b] = None
+                    continue
+                self._unregister(b)
+                self.free.append(b)
+
+
 def test_prefix_retention_trace_catches_planted_mistakes():
-    for cls in (_NoRevive, _EvictNewest, _RetainedFirst, _RevivedCountFree):
+    for cls in (_NoRevive, _EvictNewest, _RetainedFirst, _RevivedCountFree, _RetainInTableOrder):
         assert check_retention_trace(cls) is not None, cls.__name__
