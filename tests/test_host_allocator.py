@@ -12,6 +12,7 @@ from hypothesis import given, settings, strategies as st
 import paged_kv_cache_host_amd as pa
 import paged_kv_cache_host_amd._pa  # noqa: F401  (pa._pa: library path and handle)
 from oracle import allocator as oa
+from tests.prefix_truth import run_with_truth, seeded_cases
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = os.path.join(ROOT, "tests", "golden")
@@ -578,3 +579,46 @@ def test_prefix_retention_bit_exact_against_oracle(oplist, nblocks, rnd):
                 assert list(pa.pa_seq_block_table(pool, s)[1]) == t
     finally:
         pa.pa_pool_destroy(pool)
+
+
+class _CPoolView:
+    """The C allocator behind the interface tests/prefix_truth.py drives."""
+
+    def __init__(self, num_blocks, block_size):
+        st_, self.pool = pa.pa_pool_create(num_blocks, block_size, None)
+        assert st_ == pa.PA_OK
+        self.block_size = block_size
+
+    def seq_create_prefix(self, seq, tokens):
+        return pa.pa_seq_create_prefix(self.pool, seq, tokens)
+
+    def block_table(self, seq):
+        return list(pa.pa_seq_block_table(self.pool, seq)[1])
+
+    def free_list(self):
+        return _state(self.pool)
+
+    def seq_append(self, seq, n):
+        return pa.pa_seq_append(self.pool, seq, n)
+
+    def seq_register_prefix(self, seq, tokens):
+        return pa.pa_seq_register_prefix(self.pool, seq, tokens)
+
+    def seq_release(self, seq):
+        return pa.pa_seq_release(self.pool, seq)
+
+    def set_prefix_retention(self, on):
+        assert pa.pa_pool_set_prefix_retention(self.pool, on) == pa.PA_OK
+
+
+def test_prefix_blocks_hold_their_own_prefix_through_c_abi():
+    """The oracle's 6000 seeded random runs (prompts, appends, registrations,
+    releases, retention switched on and off, pools small enough that retained
+    blocks are evicted all the time) through the C allocator: no sequence is
+    ever handed a block computed under a different prefix."""
+    for ops, nblocks in seeded_cases():
+        view = _CPoolView(nblocks, 2)
+        try:
+            run_with_truth(view, ops, check_index=False)
+        finally:
+            pa.pa_pool_destroy(view.pool)

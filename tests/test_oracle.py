@@ -19,6 +19,7 @@ from oracle import attention as oat
 from oracle import cache as oc
 from oracle import codecs
 from oracle import fragmentation as ofr
+from tests.prefix_truth import run_with_truth, seeded_cases
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -690,3 +691,38 @@ class _RetainInTableOrder(oa.BlockPool):
 def test_prefix_retention_trace_catches_planted_mistakes():
     for cls in (_NoRevive, _EvictNewest, _RetainedFirst, _RevivedCountFree, _RetainInTableOrder):
         assert check_retention_trace(cls) is not None, cls.__name__
+
+
+def test_retention_never_shares_a_block_computed_under_another_prefix():
+    """Two blocks, 2-token blocks: the prompt a a b b is computed, registered
+    and released with retention on; the next prompt (c c) needs one fresh
+    block, which must be the retained tail (b b), not the head (a a).  Taking
+    the head leaves the tail's key naming the head's id, which c c then
+    occupies, so c c b b would be handed the b b block computed after a a."""
+    ops = [("retention", True), ("create", 1, [0, 0, 1, 1]), ("register", 1, 4),
+           ("release", 1), ("create", 2, [2, 2]), ("register", 2, 4),
+           ("create", 3, [2, 2, 1, 1])]
+    run_with_truth(oa.BlockPool(2, 2), ops)
+    for cls in (_RetainInTableOrder, _EvictNewest):
+        with pytest.raises(AssertionError):
+            run_with_truth(cls(2, 2), ops)
+
+
+def test_prefix_blocks_always_hold_their_own_prefix():
+    """6000 seeded random runs: prompts over a two-letter alphabet, appends,
+    registrations of any computed prefix, releases and retention switched on
+    and off, on pools small enough that retained blocks are evicted all the
+    time.  No sequence is ever handed a block computed under a different
+    prefix; the same runs on the two planted eviction-order mistakes fail
+    (each in roughly one run of a hundred and fifty)."""
+    cases = seeded_cases()
+    for ops, nblocks in cases:
+        run_with_truth(oa.BlockPool(nblocks, 2), ops)
+    for cls in (_RetainInTableOrder, _EvictNewest):
+        failed = 0
+        for ops, nblocks in cases:
+            try:
+                run_with_truth(cls(nblocks, 2), ops)
+            except AssertionError:
+                failed += 1
+        assert failed > 0, cls.__name__
