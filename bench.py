@@ -1057,6 +1057,53 @@ def block_size_leg(args, dev):
                         "achieved_GBps": round(nbytes / (k_us / 1e6) / 1e9, 1),
                         "frac": round(nbytes / (k_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
                         "blocks_held": need}
+    # chunked prefill from caches of each block size: slices 15, 31, 47 and 63
+    # of the 32768-token prompt (512 positions each, against their prefix)
+    from paged_kv_cache_host_amd.engine import prefill_workspace
+    P, C, picks = 32768, 512, (15, 31, 47, 63)
+    qp = torch.randn((C, H_Q, D), generator=gen, device=dev).to(torch.bfloat16)
+    op = torch.empty((C, H_Q, D), dtype=torch.bfloat16, device=dev)
+    wsp = prefill_workspace(1, C, H_Q, H_KV, D, P, dev)
+    cu = torch.tensor([0, C], dtype=torch.int32, device=dev)
+    for bs in (8, 16, 32):
+        nb = P // bs + 64
+        order = np.random.default_rng(60 + bs).permutation(nb).astype(np.int32)
+        st, pool = pa.pa_pool_create(nb, bs, order)
+        pa.check(st)
+        pa.check(pa.pa_seq_create(pool, 0, P))
+        st, tables, _ = pa.pa_pack_batch(pool, [0], P // bs)
+        pa.check(st)
+        pa.pa_pool_destroy(pool)
+        k = torch.randn((nb, H_KV, D // 8, bs, 8), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((nb, H_KV, D, bs), generator=gen, device=dev).to(torch.bfloat16)
+        t_d = torch.from_numpy(tables).to(dev)
+        starts = {c: torch.tensor([c * C], dtype=torch.int32, device=dev) for c in picks}
+
+        def call(c):
+            pa.check(pa.pa_prefill_chunk(None, op, qp, cu, starts[c], k, v, t_d, nb, H_KV, C,
+                                         (c + 1) * C, sm, ws=wsp, bs=bs))
+        for _ in range(3):
+            for c in picks:
+                call(c)
+        torch.cuda.synchronize()
+        pa.check(pa.pa_timing_enable(["prefill", "prefill_merge"]))
+        reps = 5
+        for _ in range(reps):
+            for c in picks:
+                call(c)
+        torch.cuda.synchronize()
+        tm = _timings(pa, ("prefill", "prefill_merge"))
+        pa.check(pa.pa_timing_enable(False))
+        del k, v
+        torch.cuda.empty_cache()
+        flops = reps * sum(4.0 * D * H_Q * (C * c * C + C * (C + 1) / 2) for c in picks)
+        kern = tm["prefill"][2]
+        whole = kern + tm["prefill_merge"][2]
+        res[str(bs)]["prefill_slices_15_31_47_63"] = {
+            "kernel_us_per_pass": round(kern / reps, 1),
+            "with_merge_us_per_pass": round(whole / reps, 1),
+            "TFLOPs_kernel": round(flops / (kern / 1e6) / 1e12, 1),
+            "frac_bf16_peak_with_merge": round(flops / (whole / 1e6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     # fragmentation of the continuous-batching trace per block size
     w = workloads.trace()
     for bs in (8, 16, 32):
@@ -1081,7 +1128,9 @@ def block_size_leg(args, dev):
         res[str(bs)]["trace_internal_waste_mean"] = round(float(np.mean(waste)), 5)
         res[str(bs)]["trace_internal_waste_max"] = round(float(np.max(waste)), 5)
     return {"workload": "decode-70b contexts (128 seqs, 64/8 heads, d128, bf16) with 8/16/32-token "
-                        "blocks; trace fragmentation with the same block sizes",
+                        "blocks; slices 15/31/47/63 of the 32768-token prompt (512 positions, "
+                        "64/8 heads, d128, bf16) prefilled from the same block sizes; trace "
+                        "fragmentation with the same block sizes",
             "by_block_size": res}
 
 

@@ -52,7 +52,8 @@
  *   (f32, f32, f32), (bf16, bf16, bf16) or (bf16, fp8, bf16).  pa_decode
  *   also takes bs 8 or 32 (ARTICLE 4.1: the block size trades fragmentation
  *   against per-block overhead) with bf16 queries, a bf16 or fp8 cache and at
- *   most 16 query heads per KV head.
+ *   most 16 query heads per KV head; pa_prefill_chunk takes bs 8 or 32 with
+ *   bf16 queries and a bf16 or fp8 cache.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -348,7 +349,10 @@ pa_status pa_decode_noalloc(void* stream, void* out, pa_dtype out_dt, const void
  * start_pos [device, n_chunks int32], >= 0
  * block_tables [device, n_chunks * max_blocks int32]
  * max_q_len: host-side bound of the slice lengths; max_context_len: bound
- *   of start_pos[c] + q_len(c).
+ *   of start_pos[c] + q_len(c), at most bs * max_blocks.
+ * bs: tokens per block, 16, or 8 / 32 with bf16 queries and a bf16 or fp8
+ *   cache (the kernel's unit stays a 16-token sub-block: one block, half of
+ *   a 32-token block, or two 8-token blocks).
  * ws as for pa_decode, sized by pa_prefill_workspace_bytes.
  * ---------------------------------------------------------------------- */
 size_t pa_prefill_workspace_bytes(int32_t n_chunks, int32_t max_q_len, int32_t H_q,

@@ -16,8 +16,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kBlock = 16;  // tokens per block of the cache write and prefill paths; decode also
-                             // takes 8- and 32-token blocks (templated on the size)
+constexpr int kBlock = 16;  // tokens per block of the cache write and fused paths; decode and
+                             // prefill also take 8- and 32-token blocks (templated on the size)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Storage tags: the element type of a buffer as the kernels see it.

@@ -61,7 +61,7 @@ namespace {
 
 // grid.x = H_kv * n_head_groups * n_split * n_pos_tiles (KV head fastest, so
 // the groups sharing a KV head land on the same XCD's L2); grid.y = slices.
-template <typename CacheT, int D>
+template <typename CacheT, int D, int BS>
 __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ start_pos,
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(
     int32_t max_blocks, int32_t num_blocks, int32_t H_q, PfGeom geo, float score_scale,
     float v_scale, float* __restrict__ ws_ml, uint16_t* __restrict__ ws_o, int32_t ws_rows) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * stage_bytes<D>()];
-  prefill_block<CacheT, D, false>(smem, blockIdx.x, blockIdx.y, out, q, cu_q_lens, start_pos,
+  prefill_block<CacheT, D, false, BS>(smem, blockIdx.x, blockIdx.y, out, q, cu_q_lens, start_pos,
                                   k_cache, v_cache, block_tables, max_blocks, num_blocks, H_q, geo,
                                   score_scale, v_scale, ws_ml, ws_o, ws_rows, nullptr);
 }
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
   *reinterpret_cast<u32x2*>(out + pair * D + 4 * sub) = pack_bf16x4(acc, inv);
 }
 
-template <typename CacheT, int D>
+template <typename CacheT, int D, int BS>
 pa_status launch_prefill_mfma(hipStream_t st, void* out, const void* q, const int32_t* cu_q_lens,
                               const int32_t* start_pos, const void* k_cache, const void* v_cache,
                               const int32_t* block_tables, int32_t max_blocks, int32_t num_blocks,
@@ -118,7 +118,7 @@ pa_status launch_prefill_mfma(hipStream_t st, void* out, const void* q, const in
     ws_o = static_cast<uint16_t*>(ws);
     ws_ml = reinterpret_cast<float*>(ws_o + static_cast<size_t>(geo.n_split) * ws_rows * H_q * D);
   }
-  hipError_t e = launch(kPrefill, prefill_kernel<CacheT, D>,
+  hipError_t e = launch(kPrefill, prefill_kernel<CacheT, D, BS>,
                         dim3(static_cast<uint32_t>(gx), n_chunks), dim3(kPfThreads), 0, st,
                         static_cast<uint16_t*>(out),
                         static_cast<const uint16_t*>(q), cu_q_lens, start_pos,
@@ -167,7 +167,8 @@ extern "C" pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, 
                                       int32_t H_kv, int32_t D, int32_t bs, int32_t max_q_len,
                                       int32_t max_context_len, float sm_scale, float k_scale,
                                       float v_scale, void* ws, size_t ws_bytes) {
-  if (bs != kBlock) return fail(PA_ERR_INVALID, "pa_prefill_chunk: block size %d != 16", bs);
+  if (bs != 8 && bs != 16 && bs != 32)
+    return fail(PA_ERR_INVALID, "pa_prefill_chunk: block size %d not in {8, 16, 32}", bs);
   if (n_chunks < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv != 0)
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: n_chunks=%d H_q=%d H_kv=%d", n_chunks, H_q,
                 H_kv);
@@ -176,10 +177,11 @@ extern "C" pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, 
   if (max_blocks <= 0 || num_blocks <= 0 || max_q_len < 0)
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: max_blocks=%d num_blocks=%d max_q_len=%d",
                 max_blocks, num_blocks, max_q_len);
-  if (max_context_len < max_q_len || static_cast<int64_t>(max_context_len) > 16LL * max_blocks)
+  if (max_context_len < max_q_len ||
+      static_cast<int64_t>(max_context_len) > static_cast<int64_t>(bs) * max_blocks)
     return fail(PA_ERR_INVALID,
-                "pa_prefill_chunk: max_context_len=%d must lie in [max_q_len=%d, 16*max_blocks=%lld]",
-                max_context_len, max_q_len, 16LL * max_blocks);
+                "pa_prefill_chunk: max_context_len=%d must lie in [max_q_len=%d, bs*max_blocks=%lld]",
+                max_context_len, max_q_len, static_cast<long long>(bs) * max_blocks);
   const bool f32 = q_dt == PA_F32 && cache_dt == PA_F32 && out_dt == PA_F32;
   const bool bf = q_dt == PA_BF16 && out_dt == PA_BF16 &&
                   (cache_dt == PA_BF16 || cache_dt == PA_FP8_E4M3);
@@ -198,6 +200,10 @@ extern "C" pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, 
   if (static_cast<int64_t>(n_chunks) * max_q_len > INT32_MAX / 64)
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: too many query rows");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!prefill_uses_mfma(q_dt, cache_dt) && bs != kBlock)
+    return fail(PA_ERR_INVALID,
+                "pa_prefill_chunk: block size %d needs the matrix-core path (bf16 queries, bf16 or "
+                "fp8 cache)", bs);
   if (!prefill_uses_mfma(q_dt, cache_dt)) {
     // slice lengths live on the device: launch max_q_len rows per slice and
     // let the rows past each slice's end exit
@@ -210,24 +216,21 @@ extern "C" pa_status pa_prefill_chunk(void* stream, void* out, pa_dtype out_dt, 
   const float kscale = cache_dt == PA_FP8_E4M3 ? k_scale : 1.f;
   const float vscale = cache_dt == PA_FP8_E4M3 ? v_scale : 1.f;
   const float score_scale = sm_scale * kscale * kLog2e;
-  if (cache_dt == PA_BF16) {
-    if (D == 128)
-      return launch_prefill_mfma<BF16, 128>(st, out, q, cu_q_lens, start_pos, k_cache, v_cache,
-                                            block_tables, max_blocks, num_blocks, n_chunks, H_q,
-                                            H_kv, max_q_len, max_context_len, score_scale, vscale,
-                                            ws, ws_bytes);
-    return launch_prefill_mfma<BF16, 64>(st, out, q, cu_q_lens, start_pos, k_cache, v_cache,
-                                         block_tables, max_blocks, num_blocks, n_chunks, H_q, H_kv,
-                                         max_q_len, max_context_len, score_scale, vscale, ws,
-                                         ws_bytes);
-  }
-  if (D == 128)
-    return launch_prefill_mfma<FP8, 128>(st, out, q, cu_q_lens, start_pos, k_cache, v_cache,
-                                         block_tables, max_blocks, num_blocks, n_chunks, H_q, H_kv,
-                                         max_q_len, max_context_len, score_scale, vscale, ws,
-                                         ws_bytes);
-  return launch_prefill_mfma<FP8, 64>(st, out, q, cu_q_lens, start_pos, k_cache, v_cache,
-                                      block_tables, max_blocks, num_blocks, n_chunks, H_q, H_kv,
-                                      max_q_len, max_context_len, score_scale, vscale, ws,
-                                      ws_bytes);
+  auto run = [&](auto cache_tag, auto d_tag, auto bs_tag) {
+    using C = decltype(cache_tag);
+    return launch_prefill_mfma<C, decltype(d_tag)::value, decltype(bs_tag)::value>(
+        st, out, q, cu_q_lens, start_pos, k_cache, v_cache, block_tables, max_blocks, num_blocks,
+        n_chunks, H_q, H_kv, max_q_len, max_context_len, score_scale, vscale, ws, ws_bytes);
+  };
+  auto by_bs = [&](auto cache_tag, auto d_tag) {
+    if (bs == 8) return run(cache_tag, d_tag, std::integral_constant<int, 8>{});
+    if (bs == 32) return run(cache_tag, d_tag, std::integral_constant<int, 32>{});
+    return run(cache_tag, d_tag, std::integral_constant<int, 16>{});
+  };
+  auto by_d = [&](auto cache_tag) {
+    if (D == 128) return by_bs(cache_tag, std::integral_constant<int, 128>{});
+    return by_bs(cache_tag, std::integral_constant<int, 64>{});
+  };
+  if (cache_dt == PA_BF16) return by_d(BF16{});
+  return by_d(FP8{});
 }

@@ -99,50 +99,69 @@ inline size_t pf_partials_bound(int32_t n_chunks, int32_t max_q_len, int32_t H_q
 }
 
 
-// Moves one 64-key tile (4 blocks x K and V of one KV head) from the paged
-// cache into an LDS stage as 16-byte pieces spread over the work-group's
-// threads: piece p = wave * 64 + lane + i * threads.  A block-head tile has a
-// multiple of 64 pieces, so which tensor and block a piece belongs to is the
-// same for the whole wave (scalar), and every offset splits into a scalar
-// part and a lane part that does not depend on i.
-template <typename CacheT, int D>
+// Moves one 64-key tile (four 16-key sub-blocks x K and V of one KV head)
+// from the paged cache into an LDS stage as 16-byte pieces spread over the
+// work-group's threads: piece p = wave * 64 + lane + i * threads.  A
+// sub-block-head tile has a multiple of 64 pieces, so which tensor and
+// sub-block a piece belongs to is the same for the whole wave (scalar), and
+// every offset splits into a scalar part and a lane part that does not depend
+// on i.  BS is the cache's block size: a 16-key sub-block is one block (16),
+// half of one (32: the half at 16 (b & 1) keys), or two (8: its first eight
+// keys in one block, the last eight in the next, chosen lane by lane).
+template <typename CacheT, int D, int BS>
 struct TileLoader {
   using CR = typename CacheT::raw;
   static constexpr int kElems = 16 / sizeof(CR);            // cache elements per piece
-  static constexpr int kPerBlock = D * kBlock / kElems;     // pieces per (block, head), K or V
+  static constexpr int kPerBlock = D * 16 / kElems;        // pieces per (sub-block, head), K or V
   static constexpr int kHalf = 4 * kPerBlock;               // K pieces of a tile
   static constexpr int kPieces = 2 * kHalf;
   static constexpr int NLD = kPieces / kPfThreads;          // pieces per thread
   static_assert(kPieces % kPfThreads == 0, "tile pieces must divide over the threads");
   static_assert(kPerBlock % kWave == 0, "a wave's pieces must share one block");
   static constexpr bool kWide = sizeof(CR) == 1;            // fp8 pieces widen to two chunks
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static constexpr int kX = kElems;                         // K's innermost run (16 bytes)
 
   int wave;      // scalar
   int lane;
   int k_lane;    // LDS offset, lane part, K pieces
   int v_lane;    // LDS offset, lane part, V pieces
-  int v_key;     // first key of the lane's V piece inside its block
+  int v_key;     // first key of the lane's V piece inside its sub-block
   int k_ge;      // cache elements from the wave's first K piece to the lane's
   int v_ge;      // same for V
+  bool k_hi;     // 8-key blocks: the lane's K piece is in the sub-block's second block
+  bool v_hi;     // same for V (a 16-key fp8 V piece straddles both: not used)
 
+  // The cache holds K as [block][head][D / kX][BS][kX] and V as
+  // [block][head][D][BS].  In a sub-block, K piece e = chunk * 16 + key
+  // (one key's kX elements of one chunk) and V piece e = dim * 2 + half (8
+  // keys of one dimension; fp8: e = dim, all 16 keys).
   __device__ TileLoader(int wave_, int lane_) : wave(wave_), lane(lane_) {
+    constexpr int R = BS < 16 ? BS : 16;   // keys of a sub-block inside one block
+    int k_key, v_dim, v_half;
     if (!kWide) {
       // Each 16 lanes write 256 contiguous LDS bytes: a lane loads the K
-      // token (of the 16 of its chunk) or the V dimension and half whose
+      // key (of the 16 of its chunk) or the V dimension and half whose
       // LDS slot is its own, rather than writing its piece to a scattered
-      // slot.  The 16 lanes still read one contiguous 256-byte run.
+      // slot.  The 16 lanes still read contiguous runs of the cache.
       k_lane = (lane >> 4) * (kPfKeys * 16) + (lane & 15) * 16;
-      k_ge = ((lane & ~15) + krow_of(lane & 15)) * kElems;
+      k_key = krow_of(lane & 15);
       v_lane = (lane >> 5) * 2048 + ((lane >> 4) & 1) * 256 + (lane & 15) * 16;
-      v_ge = (2 * ((lane & 15) + 16 * (lane >> 5)) + ((lane >> 4) & 1)) * kElems;
-      v_key = ((lane >> 4) & 1) * 8;
+      v_dim = (lane & 15) + 16 * (lane >> 5);
+      v_half = (lane >> 4) & 1;
+      v_key = v_half * 8;
     } else {
       k_lane = (lane >> 4) * 2 * (kPfKeys * 16) + krow_of(lane & 15) * 16;
-      k_ge = lane * kElems;
+      k_key = lane & 15;
       v_lane = (lane >> 4) * 2048 + (lane & 15) * 16;
-      v_ge = lane * kElems;
+      v_dim = lane;
+      v_half = 0;
       v_key = 0;
     }
+    k_hi = BS == 8 && k_key >= 8;
+    v_hi = BS == 8 && !kWide && v_half;
+    k_ge = ((lane >> 4) * BS + k_key % R) * kX;
+    v_ge = v_dim * BS + (BS == 8 ? 0 : v_half * 8);
   }
   // scalar description of piece i of this wave
   struct Piece {
@@ -162,7 +181,18 @@ struct TileLoader {
     return q;
   }
 
-  // ids: lanes 0..3 hold the tile's four block ids, already inside the
+  // Entries of the block table a tile reads: lanes 0..n-1 of `ids` hold
+  // them (BS 16: one per sub-block; 32: one per two; 8: two per sub-block).
+  static constexpr int kIdsPerTile = kPfKeys / BS;
+
+  // Scalar part of piece q's offset inside its block, in cache elements.
+  __device__ static int scalar_off(const Piece& q) {
+    const int half = BS == 32 ? (q.b & 1) * 16 : 0;
+    if (!q.v) return ((q.e0 >> 4) * BS + half) * kX;
+    return (kWide ? q.e0 : q.e0 >> 1) * BS + half;
+  }
+
+  // ids: the tile's table entries (see kIdsPerTile), already inside the
   // pool.  Blocks past the context are loaded too (any valid id): their
   // keys lie beyond `valid`, so store() zeroes their V and the causal mask
   // drops their scores.  Loading unconditionally keeps the loads free of
@@ -171,21 +201,34 @@ struct TileLoader {
                         const CR* __restrict__ v_cache, int32_t ids, int32_t kvh,
                         int32_t H_kv, int32_t num_blocks) const {
     const Piece q = piece(i);
-    const int32_t bk = safe_block(__builtin_amdgcn_readlane(ids, q.b), num_blocks);
-    const CR* base = (q.v ? v_cache : k_cache) +
-                     (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + q.e0 * kElems;
-    r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (q.v ? v_ge : k_ge)));
+    const CR* cache = q.v ? v_cache : k_cache;
+    const int off = scalar_off(q) + (q.v ? v_ge : k_ge);
+    if constexpr (BS != 8) {
+      const int32_t bk = safe_block(__builtin_amdgcn_readlane(ids, BS == 16 ? q.b : q.b >> 1),
+                                    num_blocks);
+      const CR* base = cache + (static_cast<int64_t>(bk) * H_kv + kvh) * (D * BS);
+      r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+    } else {
+      const int32_t b0 = safe_block(__builtin_amdgcn_readlane(ids, 2 * q.b), num_blocks);
+      const int32_t b1 = safe_block(__builtin_amdgcn_readlane(ids, 2 * q.b + 1), num_blocks);
+      const CR* base0 = cache + (static_cast<int64_t>(b0) * H_kv + kvh) * (D * BS);
+      const CR* base1 = cache + (static_cast<int64_t>(b1) * H_kv + kvh) * (D * BS);
+      if (kWide && q.v) {
+        // 16 keys of one dimension: eight bytes from each block
+        const u32x2 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base0 + off));
+        const u32x2 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base1 + off));
+        r = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        const bool second = q.v ? v_hi : k_hi;
+        r = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>((second ? base1 : base0) + off));
+      }
+    }
   }
   __device__ void load(u32x4* regs, const CR* __restrict__ k_cache, const CR* __restrict__ v_cache,
                        int32_t ids, int32_t kvh, int32_t H_kv, int32_t num_blocks) const {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const Piece q = piece(i);
-      const int32_t bk = safe_block(__builtin_amdgcn_readlane(ids, q.b), num_blocks);
-      const CR* base = (q.v ? v_cache : k_cache) +
-                       (static_cast<int64_t>(bk) * H_kv + kvh) * (D * kBlock) + q.e0 * kElems;
-      regs[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (q.v ? v_ge : k_ge)));
-    }
+    for (int i = 0; i < NLD; ++i) load1(regs[i], i, k_cache, v_cache, ids, kvh, H_kv, num_blocks);
   }
 
   // Piece i of the tile into a stage, V beyond the context not cleared.
@@ -194,7 +237,7 @@ struct TileLoader {
     u32x4 w = w0;
     if (!kWide) {
       if (!q.v) {
-        const int off = (q.e0 >> 4) * (kPfKeys * 16) + q.b * kBlock * 16;
+        const int off = (q.e0 >> 4) * (kPfKeys * 16) + q.b * 16 * 16;
         *reinterpret_cast<u32x4*>(stage + off + k_lane) = w;
       } else {
 #pragma unroll
@@ -203,7 +246,7 @@ struct TileLoader {
         *reinterpret_cast<u32x4*>(stage + off + v_lane) = w;
       }
     } else if (!q.v) {
-      const int off = (q.e0 >> 4) * 2 * (kPfKeys * 16) + q.b * kBlock * 16 + k_lane;
+      const int off = (q.e0 >> 4) * 2 * (kPfKeys * 16) + q.b * 16 * 16 + k_lane;
       *reinterpret_cast<bf16x8*>(stage + off) = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
       *reinterpret_cast<bf16x8*>(stage + off + kPfKeys * 16) = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
     } else {
@@ -222,12 +265,12 @@ struct TileLoader {
       if (!kWide) {
         if (!q.v) {
           // e = chunk * 16 + token
-          const int off = (q.e0 >> 4) * (kPfKeys * 16) + q.b * kBlock * 16;
+          const int off = (q.e0 >> 4) * (kPfKeys * 16) + q.b * 16 * 16;
           *reinterpret_cast<u32x4*>(stage + off + k_lane) = w;
         } else {
           // e = dim * 2 + half; v_off(dim, 2 b + half)
           if (valid < kPfKeys) {  // last tile of the range only
-            const int key0 = q.b * kBlock + v_key;
+            const int key0 = q.b * 16 + v_key;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int k = key0 + 2 * j;
@@ -242,15 +285,15 @@ struct TileLoader {
         }
       } else if (!q.v) {
         // e = chunk8 * 16 + token: bf16 chunks 2 chunk8, 2 chunk8 + 1
-        const int off = (q.e0 >> 4) * 2 * (kPfKeys * 16) + q.b * kBlock * 16 + k_lane;
+        const int off = (q.e0 >> 4) * 2 * (kPfKeys * 16) + q.b * 16 * 16 + k_lane;
         *reinterpret_cast<bf16x8*>(stage + off) = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
         *reinterpret_cast<bf16x8*>(stage + off + kPfKeys * 16) = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
       } else {
         // e = dim: tokens 0..7 -> chunk 2 b, 8..15 -> chunk 2 b + 1
         f16x8 v0 = fp8x8_to_f16x8(u32x2{w[0], w[1]});
         f16x8 v1 = fp8x8_to_f16x8(u32x2{w[2], w[3]});
-        const int key0 = q.b * kBlock;
-        if (valid < kPfKeys && key0 + kBlock > valid) {
+        const int key0 = q.b * 16;
+        if (valid < kPfKeys && key0 + 16 > valid) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             if (key0 + j >= valid) v0[j] = static_cast<_Float16>(0.0f);
@@ -353,7 +396,7 @@ __device__ __forceinline__ u32x2 pack_bf16x4(const f32x4& acc, float inv) {
 // zero, and when the key range is split the last of a group's work-groups
 // to finish merges the group's partials (merge_counters: one per group,
 // zero before and after).
-template <typename CacheT, int D, bool kVarlen>
+template <typename CacheT, int D, bool kVarlen, int BS>
 __device__ __attribute__((always_inline)) inline void prefill_block(
     uint8_t* __restrict__ smem, int x, const int c,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
@@ -365,7 +408,7 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
     int32_t* __restrict__ merge_counters) {
   constexpr int NKS = D / 16;  // 16-dim MFMA steps of Q K^T
   constexpr int NDT = D / 32;  // 32-dim tiles of O^T
-  using Loader = TileLoader<CacheT, D>;
+  using Loader = TileLoader<CacheT, D, BS>;
   constexpr int NLD = Loader::NLD;
 
   const int tid = threadIdx.x;
@@ -436,12 +479,14 @@ __device__ __attribute__((always_inline)) inline void prefill_block(
   float l_run = 0.f;
 
   const int32_t* table = block_tables + static_cast<int64_t>(c) * max_blocks;
-  const int32_t n_blk = min((kv_end + kBlock - 1) / kBlock, max_blocks);
+  const int32_t n_blk = min((kv_end + BS - 1) / BS, max_blocks);
   // A tile's block ids are fetched by a vector load one iteration before
-  // its K/V loads are issued: lanes 0..3 take the tile's four entries
-  // (entries past the context repeat the last one), clamped into the pool.
+  // its K/V loads are issued: lanes 0..n-1 take the tile's n entries
+  // (entries past the context repeat the last one); each is clamped into
+  // the pool where it is used.
   auto fetch_ids = [&](int t) -> int32_t {
-    return table[min(t * 4 + (lane & 3), n_blk - 1)];
+    constexpr int n = Loader::kIdsPerTile;
+    return table[min(t * n + (lane & (n - 1)), n_blk - 1)];
   };
 
   const Loader ld(wave, lane);

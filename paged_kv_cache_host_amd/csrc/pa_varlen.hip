@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void varlen_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[varlen_lds_bytes<D>()];
   const int32_t b = blockIdx.x;
   if (b < pf_items) {
-    prefill_block<CacheT, D, true>(
+    prefill_block<CacheT, D, true, kBlock>(
         lds, b % pf_gx, b / pf_gx, out, q, cu_q_lens + n_decode, seq_lens + n_decode, k_cache,
         v_cache, pf_tables, pf_max_blocks, num_blocks, H_q, geo, score_scale, v_scale, pf_ws_ml,
         pf_ws_o, pf_ws_rows, pf_merge);

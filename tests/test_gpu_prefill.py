@@ -189,3 +189,104 @@ def test_zero_work_calls_are_no_ops():
                                0.125, 1.0, 1.0, None) == 0
     torch.cuda.synchronize()
     kv.close()
+
+
+@pytest.mark.parametrize("bs,cache_dt,d", [(8, "bf16", 128), (32, "bf16", 128), (8, "fp8", 128),
+                                           (32, "fp8", 128), (8, "bf16", 64), (32, "fp8", 64)])
+def test_block_sizes_8_and_32(bs, cache_dt, d):
+    """pa_prefill_chunk over caches of 8- and 32-token blocks (ARTICLE 4.1):
+    the C allocator's tables for that block size equal the oracle's; the cache
+    is scattered here by layout alone (its bytes equal the oracle's scatter);
+    outputs within tolerance of the oracle.  Prompts of 1, 9, 17 and 33
+    tokens, slices starting off block boundaries, a 188-row tail and two
+    slices of a 2500-token prompt (key ranges split over work-groups)."""
+    import torch
+
+    from oracle import allocator as oa
+    from oracle import attention as oat
+    from oracle import cache as oc
+    from oracle import codecs
+    import paged_kv_cache_host_amd._pa as pa
+    from paged_kv_cache_host_amd.engine import prefill_workspace
+    dev = "cuda"
+    rng = np.random.default_rng(2300 + bs + d + len(cache_dt))
+    prompts = [1, 9, 17, 33, 700, 2500]
+    slices = [(0, 0, 1), (1, 0, 9), (2, 3, 14), (3, 16, 17), (4, 512, 188), (5, 1024, 512),
+              (5, 1988, 512)]
+    S, h_q, h_kv = len(prompts), 16, 2
+    nb = sum(-(-P // bs) for P in prompts) + 5
+    order = rng.permutation(nb).astype(np.int32)
+    ntok = sum(prompts)
+    if cache_dt == "bf16":
+        k_raw = workloads.normal_raw(rng, (ntok, h_kv, d), "bf16")
+        v_raw = workloads.normal_raw(rng, (ntok, h_kv, d), "bf16")
+        ks = vs = 1.0
+    else:   # e4m3fn codes, NaN codes (0x7F, 0xFF) excluded
+        k_raw = rng.integers(0, 0x7F, size=(ntok, h_kv, d)).astype(np.uint8) | \
+            (rng.integers(0, 2, size=(ntok, h_kv, d)).astype(np.uint8) << 7)
+        v_raw = rng.integers(0, 0x7F, size=(ntok, h_kv, d)).astype(np.uint8) | \
+            (rng.integers(0, 2, size=(ntok, h_kv, d)).astype(np.uint8) << 7)
+        ks, vs = 0.01, 0.02
+    T = sum(n for _, _, n in slices)
+    q_raw = workloads.normal_raw(rng, (T, h_q, d), "bf16")
+    # host side: the C allocator with this block size
+    st_, pool = pa.pa_pool_create(nb, bs, order)
+    assert st_ == pa.PA_OK
+    try:
+        slots = []
+        for s, P in enumerate(prompts):
+            assert pa.pa_seq_create(pool, s, P) == pa.PA_OK
+            st_, sl = pa.pa_seq_slots(pool, s, 0, P)
+            assert st_ == pa.PA_OK
+            slots.append(np.asarray(sl, dtype=np.int64))
+        mb = max(-(-P // bs) for P in prompts)
+        st_, tables, _ = pa.pa_pack_batch(pool, np.array([s for s, _, _ in slices]), mb)
+        assert st_ == pa.PA_OK
+    finally:
+        pa.pa_pool_destroy(pool)
+    slots = np.concatenate(slots)
+    opool = oa.BlockPool(nb, bs, order.tolist())
+    for s, P in enumerate(prompts):
+        assert opool.seq_create(s, P) == oa.OK
+    o_slots = np.concatenate([np.asarray(opool.slots(s, 0, P)) for s, P in enumerate(prompts)])
+    assert np.array_equal(o_slots, slots)
+    for i, (s, _, _) in enumerate(slices):
+        t = opool.block_table(s)
+        assert list(tables[i, :len(t)]) == list(t)
+    # the device cache, scattered by layout only
+    x = 8 if cache_dt == "bf16" else 16
+    sdt = np.uint16 if cache_dt == "bf16" else np.uint8
+    kc = np.zeros((nb, h_kv, d // x, bs, x), dtype=sdt)
+    vc = np.zeros((nb, h_kv, d, bs), dtype=sdt)
+    kc[slots // bs, :, :, slots % bs, :] = k_raw.reshape(ntok, h_kv, d // x, x)
+    vc[slots // bs, :, :, slots % bs] = v_raw
+    okc, ovc = oc.new_cache(nb, h_kv, bs, d, cache_dt)
+    oc.cache_write(okc, ovc, k_raw, v_raw, slots, cache_dt, cache_dt)
+    assert np.array_equal(okc, kc) and np.array_equal(ovc, vc)
+    sm = float(np.float32(1.0) / np.float32(np.sqrt(d)))
+    q64 = codecs.decode(q_raw, "bf16")
+    cu = np.concatenate([[0], np.cumsum([n for _, _, n in slices])]).astype(np.int32)
+    ref = np.concatenate([oat.prefill_chunk(q64[cu[i]:cu[i + 1]], a, okc, ovc,
+                                            opool.block_table(s), h_kv, sm, cache_dt, ks, vs)
+                          for i, (s, a, _) in enumerate(slices)])
+    if cache_dt == "bf16":
+        k_d = torch.from_numpy(kc.view(np.int16)).to(dev).view(torch.bfloat16)
+        v_d = torch.from_numpy(vc.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        k_d = torch.from_numpy(kc).to(dev).view(torch.float8_e4m3fn)
+        v_d = torch.from_numpy(vc).to(dev).view(torch.float8_e4m3fn)
+    q_d = torch.from_numpy(q_raw.view(np.int16)).to(dev).view(torch.bfloat16)
+    start = np.array([a for _, a, _ in slices], dtype=np.int32)
+    max_q = max(n for _, _, n in slices)
+    max_ctx = max(a + n for _, a, n in slices)
+    out = filled((T, h_q, d), torch.bfloat16, dev)
+    ws = prefill_workspace(len(slices), max_q, h_q, h_kv, d, max_ctx, dev)
+    say(f"[prefill bs={bs}] {cache_dt} d={d} slices={slices} pool={nb}")
+    assert pa.pa_prefill_chunk(None, out, q_d, torch.from_numpy(cu).to(dev),
+                               torch.from_numpy(start).to(dev), k_d, v_d,
+                               torch.from_numpy(tables).to(dev), nb, h_kv, max_q, max_ctx, sm,
+                               ks, vs, ws, bs=bs) == 0
+    torch.cuda.synchronize()
+    got = codecs.decode(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    err = assert_close(got, ref, cache_dt, f"prefill bs={bs} {cache_dt} d={d}")
+    say(f"    max|d| = {err:.3g}")
