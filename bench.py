@@ -397,7 +397,7 @@ def pmc_prefill_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_
     of the two-stream passes), prefill kernel and merge kernel together,
     against their algorithmic bytes: the K/V of the prefix and the slice
     (read once), Q and the output."""
-    key, mkey = "prefill_kernel<pa::BF16, 128>", "prefill_merge_kernel<128>"
+    key, mkey = "prefill_kernel<pa::BF16, 128, 16>", "prefill_merge_kernel<128>"
     f, w = _pmc_seq(fetch_dir, "FETCH_SIZE", key), _pmc_seq(write_dir, "WRITE_SIZE", key)
     fm, wm = _pmc_seq(fetch_dir, "FETCH_SIZE", mkey), _pmc_seq(write_dir, "WRITE_SIZE", mkey)
     first = mixed_warmup_slices(warmup)
@@ -415,7 +415,7 @@ def pmc_prefill_summary(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_
     read_k = sum(v for _, v in f[first:first + 64]) * 1024 * f_scale
     write_k = sum(v for _, v in w[first:first + 64]) * 1024 * w_scale
     print(json.dumps({
-        "kernel": "prefill_kernel<BF16,128> + prefill_merge_kernel<128>",
+        "kernel": "prefill_kernel<BF16,128,16> + prefill_merge_kernel<128>",
         "workload": f"mixed leg, 64 causal 512-token slices of a 32768-token prompt, one "
                     f"stream (bench.py --mixed-only --warmup {warmup}: prefill dispatches "
                     f"{first}..{first + 63} and the merges that follow them)",
@@ -453,7 +453,7 @@ def trace_prefill_summary(trace_dir: str, warmup: int):
     the one-stream pass's 64 prefill dispatches and of the merge dispatches
     that follow them, against the algorithmic causal flops."""
     rows = _trace_rows(trace_dir)
-    pf = [(i, t) for i, n, t in rows if "prefill_kernel<pa::BF16, 128>" in n]
+    pf = [(i, t) for i, n, t in rows if "prefill_kernel<pa::BF16, 128, 16>" in n]
     mg = [(i, t) for i, n, t in rows if "prefill_merge_kernel<128>" in n]
     first = mixed_warmup_slices(warmup)
     if len(pf) < first + 64:
@@ -480,7 +480,7 @@ def sq_prefill_summary(dirs, warmup: int):
     several counter passes), summed over the window.  SQ counters are
     aggregated over the 32 shader engines (8 XCDs x 4), GRBM_GUI_ACTIVE over
     the 8 XCDs; a busy fraction is per SIMD (256 CUs x 4 SIMDs)."""
-    key = "prefill_kernel<pa::BF16, 128>"
+    key = "prefill_kernel<pa::BF16, 128, 16>"
     first = mixed_warmup_slices(warmup)
     tot = {}
     import csv
@@ -938,7 +938,7 @@ def mixed_leg(args, dev):
                              "traffic_unit": "HBM bytes over the 64 calls (both kernels)",
                              "traffic_algorithmic_bytes": None if pmc is None else
                              pmc["algorithmic_read_bytes"] + pmc["algorithmic_write_bytes"],
-                             "kernel": "prefill_kernel<BF16,128>",
+                             "kernel": "prefill_kernel<BF16,128,16>",
                              "kernel_us_total": round(tot_pf, 1),
                              "merge_us_total": round(tot_merge, 1),
                              "kernel_only": {"achieved": round(achieved_kernel, 1),
@@ -1181,7 +1181,7 @@ def fp8_prefill_leg(args, dev):
             "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
             "peak_note": "the e4m3fn K/V are widened to bf16 / fp16 for the matrix cores, "
                          "so the contraction runs at the dense bf16 peak",
-            "kernel": "prefill_kernel<FP8,128>",
+            "kernel": "prefill_kernel<FP8,128,16>",
             "kernel_us_total": round(tm["prefill"][2], 1),
             "prefill_merge_us_total": round(tm["prefill_merge"][2], 1),
             "algorithmic_flops": flops}
