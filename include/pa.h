@@ -53,7 +53,7 @@
  *   also takes bs 8 or 32 (ARTICLE 4.1: the block size trades fragmentation
  *   against per-block overhead) with bf16 queries, a bf16 or fp8 cache and at
  *   most 16 query heads per KV head; pa_prefill_chunk takes bs 8 or 32 with
- *   bf16 queries and a bf16 or fp8 cache.
+ *   bf16 queries and a bf16 or fp8 cache; pa_cache_write takes bs 8 or 32.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -266,6 +266,8 @@ pa_status pa_validate_tables(const int32_t* block_tables, const int32_t* context
  * 1/scale computed once in fp32 on the host, one fp32 multiply, round to
  * nearest even, magnitudes above 448 saturated to 448, NaN kept as NaN.
  * k_scale / v_scale are ignored for other caches.
+ * bs: tokens per block, 8, 16 or 32 (any of the type pairs above); the
+ *   staged forms below take 16.
  * ---------------------------------------------------------------------- */
 pa_status pa_cache_write(void* stream, const void* k_new, const void* v_new, pa_dtype new_dt,
                          const int32_t* slot_mapping, int32_t n, void* k_cache, void* v_cache,

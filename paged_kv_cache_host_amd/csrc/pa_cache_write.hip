@@ -40,7 +40,7 @@ __device__ __forceinline__ uint8_t encode<BF16, FP8>(uint16_t x, float inv_scale
 // KV head h.  HOST_SLOTS: the slot mapping lies in pinned host memory and is
 // read with system-scope loads (the fused staging kernel); otherwise it is
 // device memory.
-template <typename NewT, typename CacheT, int D, bool HOST_SLOTS>
+template <typename NewT, typename CacheT, int D, bool HOST_SLOTS, int BS>
 __device__ __forceinline__ void cw_tile(int bx, int h, const typename NewT::raw* __restrict__ k_new,
                                         const typename NewT::raw* __restrict__ v_new,
                                         const int32_t* __restrict__ slots, int32_t n,
@@ -65,7 +65,7 @@ __device__ __forceinline__ void cw_tile(int bx, int h, const typename NewT::raw*
       else
         sl = slots[t];
     }
-    if (sl >= num_blocks * kBlock) sl = -1;
+    if (sl >= num_blocks * BS) sl = -1;
     slot_s[tid] = sl;
   }
   // stage V rows of the 16 tokens
@@ -81,9 +81,9 @@ __device__ __forceinline__ void cw_tile(int bx, int h, const typename NewT::raw*
     const int32_t sl = slot_s[tt];
     if (sl < 0) continue;
     const int64_t t = t0 + tt;
-    const int32_t blk = sl / kBlock, off = sl % kBlock;
+    const int32_t blk = sl / BS, off = sl % BS;
     const NR* src = k_new + (t * H_kv + h) * D + ch * X;
-    CR* dst = k_cache + ((static_cast<int64_t>(blk) * H_kv + h) * NCH + ch) * (kBlock * X) + off * X;
+    CR* dst = k_cache + ((static_cast<int64_t>(blk) * H_kv + h) * NCH + ch) * (BS * X) + off * X;
 #pragma unroll
     for (int j = 0; j < X; ++j) dst[j] = encode<NewT, CacheT>(src[j], k_inv);
   }
@@ -92,21 +92,21 @@ __device__ __forceinline__ void cw_tile(int bx, int h, const typename NewT::raw*
     const int tt = i & 15, d = i >> 4;
     const int32_t sl = slot_s[tt];
     if (sl < 0) continue;
-    const int32_t blk = sl / kBlock, off = sl % kBlock;
-    v_cache[((static_cast<int64_t>(blk) * H_kv + h) * D + d) * kBlock + off] =
+    const int32_t blk = sl / BS, off = sl % BS;
+    v_cache[((static_cast<int64_t>(blk) * H_kv + h) * D + d) * BS + off] =
         encode<NewT, CacheT>(v_s[tt][d], v_inv);
   }
 }
 
 // grid: (ceil(n / 16), H_kv); block: 256 threads.
-template <typename NewT, typename CacheT, int D>
+template <typename NewT, typename CacheT, int D, int BS>
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const typename NewT::raw* __restrict__ k_new, const typename NewT::raw* __restrict__ v_new,
     const int32_t* __restrict__ slots, int32_t n, typename CacheT::raw* __restrict__ k_cache,
     typename CacheT::raw* __restrict__ v_cache, int32_t num_blocks, int32_t H_kv, float k_inv,
     float v_inv) {
-  cw_tile<NewT, CacheT, D, false>(blockIdx.x, blockIdx.y, k_new, v_new, slots, n, k_cache,
-                                  v_cache, num_blocks, H_kv, k_inv, v_inv);
+  cw_tile<NewT, CacheT, D, false, BS>(blockIdx.x, blockIdx.y, k_new, v_new, slots, n, k_cache,
+                                      v_cache, num_blocks, H_kv, k_inv, v_inv);
 }
 
 // grid: stage groups + ceil(n / 16) * H_kv; block: 256 threads.  The first
@@ -143,16 +143,16 @@ __global__ __launch_bounds__(256) void stage_cache_write_kernel(
         tables[t * max_blocks + (len - 1) / kBlock] = sl / kBlock;
     }
   }
-  cw_tile<NewT, CacheT, D, true>(r % ntb, r / ntb, k_new, v_new, slots_host, n, k_cache, v_cache,
-                                 num_blocks, H_kv, k_inv, v_inv);
+  cw_tile<NewT, CacheT, D, true, kBlock>(r % ntb, r / ntb, k_new, v_new, slots_host, n, k_cache,
+                                         v_cache, num_blocks, H_kv, k_inv, v_inv);
 }
 
-template <typename NewT, typename CacheT, int D>
+template <typename NewT, typename CacheT, int D, int BS>
 static pa_status launch_cw(hipStream_t st, const void* k_new, const void* v_new,
                            const int32_t* slots, int32_t n, void* k_cache, void* v_cache,
                            int32_t num_blocks, int32_t H_kv, float k_inv, float v_inv) {
   dim3 grid((n + 15) / 16, H_kv);
-  hipError_t e = launch(kCacheWrite, cache_write_kernel<NewT, CacheT, D>, grid, dim3(256), 0, st,
+  hipError_t e = launch(kCacheWrite, cache_write_kernel<NewT, CacheT, D, BS>, grid, dim3(256), 0, st,
                         static_cast<const typename NewT::raw*>(k_new),
                         static_cast<const typename NewT::raw*>(v_new), slots, n,
                         static_cast<typename CacheT::raw*>(k_cache),
@@ -163,16 +163,31 @@ static pa_status launch_cw(hipStream_t st, const void* k_new, const void* v_new,
   return PA_OK;
 }
 
+template <typename NewT, typename CacheT, int BS>
+static pa_status launch_cw_d(hipStream_t st, const void* k_new, const void* v_new,
+                             const int32_t* slots, int32_t n, void* k_cache, void* v_cache,
+                             int32_t num_blocks, int32_t H_kv, int32_t D, float k_inv,
+                             float v_inv) {
+  if (D == 128)
+    return launch_cw<NewT, CacheT, 128, BS>(st, k_new, v_new, slots, n, k_cache, v_cache,
+                                            num_blocks, H_kv, k_inv, v_inv);
+  return launch_cw<NewT, CacheT, 64, BS>(st, k_new, v_new, slots, n, k_cache, v_cache, num_blocks,
+                                         H_kv, k_inv, v_inv);
+}
+
 template <typename NewT, typename CacheT>
 static pa_status launch_cache_write(hipStream_t st, const void* k_new, const void* v_new,
                                     const int32_t* slots, int32_t n, void* k_cache, void* v_cache,
-                                    int32_t num_blocks, int32_t H_kv, int32_t D, float k_inv,
-                                    float v_inv) {
-  if (D == 128)
-    return launch_cw<NewT, CacheT, 128>(st, k_new, v_new, slots, n, k_cache, v_cache, num_blocks,
-                                        H_kv, k_inv, v_inv);
-  return launch_cw<NewT, CacheT, 64>(st, k_new, v_new, slots, n, k_cache, v_cache, num_blocks,
-                                     H_kv, k_inv, v_inv);
+                                    int32_t num_blocks, int32_t H_kv, int32_t D, int32_t bs,
+                                    float k_inv, float v_inv) {
+  if (bs == 8)
+    return launch_cw_d<NewT, CacheT, 8>(st, k_new, v_new, slots, n, k_cache, v_cache, num_blocks,
+                                        H_kv, D, k_inv, v_inv);
+  if (bs == 32)
+    return launch_cw_d<NewT, CacheT, 32>(st, k_new, v_new, slots, n, k_cache, v_cache,
+                                         num_blocks, H_kv, D, k_inv, v_inv);
+  return launch_cw_d<NewT, CacheT, 16>(st, k_new, v_new, slots, n, k_cache, v_cache, num_blocks,
+                                       H_kv, D, k_inv, v_inv);
 }
 
 // Argument checks shared by pa_cache_write and pa_stage_cache_write (all but
@@ -186,12 +201,14 @@ struct CwPlan {
 static pa_status cw_check(const char* who, const void* k_new, const void* v_new, pa_dtype new_dt,
                           int32_t n, void* k_cache, void* v_cache, pa_dtype cache_dt,
                           int32_t num_blocks, int32_t H_kv, int32_t D, int32_t bs, float k_scale,
-                          float v_scale, CwPlan* plan) {
-  if (bs != kBlock) return fail(PA_ERR_INVALID, "%s: block size %d != 16", who, bs);
+                          float v_scale, CwPlan* plan, bool any_bs = false) {
+  if (any_bs ? (bs != 8 && bs != 16 && bs != 32) : bs != kBlock)
+    return fail(PA_ERR_INVALID, "%s: block size %d not in %s", who, bs,
+                any_bs ? "{8, 16, 32}" : "{16}");
   if (n < 0 || H_kv <= 0 || num_blocks < 0)
     return fail(PA_ERR_INVALID, "%s: n=%d H_kv=%d num_blocks=%d", who, n, H_kv, num_blocks);
   if (D != 64 && D != 128) return fail(PA_ERR_INVALID, "%s: D=%d not in {64,128}", who, D);
-  if (static_cast<int64_t>(num_blocks) * kBlock > INT32_MAX)
+  if (static_cast<int64_t>(num_blocks) * bs > INT32_MAX)
     return fail(PA_ERR_INVALID, "%s: num_blocks=%d overflows int32 slots", who, num_blocks);
   if (H_kv > 65535) return fail(PA_ERR_INVALID, "%s: H_kv=%d too large", who, H_kv);
   if (n > 0 && (!k_new || !v_new || !k_cache || !v_cache))
@@ -287,19 +304,19 @@ extern "C" pa_status pa_cache_write(void* stream, const void* k_new, const void*
                                     float k_scale, float v_scale) {
   CwPlan plan;
   const pa_status chk = cw_check("pa_cache_write", k_new, v_new, new_dt, n, k_cache, v_cache,
-                                 cache_dt, num_blocks, H_kv, D, bs, k_scale, v_scale, &plan);
+                                 cache_dt, num_blocks, H_kv, D, bs, k_scale, v_scale, &plan, true);
   if (chk != PA_OK) return chk;
   if (n == 0) return PA_OK;
   if (!slot_mapping) return fail(PA_ERR_INVALID, "pa_cache_write: NULL buffer");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.combo == 0)
     return launch_cache_write<F32, F32>(st, k_new, v_new, slot_mapping, n, k_cache, v_cache,
-                                        num_blocks, H_kv, D, 1.f, 1.f);
+                                        num_blocks, H_kv, D, bs, 1.f, 1.f);
   if (plan.combo == 1)
     return launch_cache_write<BF16, BF16>(st, k_new, v_new, slot_mapping, n, k_cache, v_cache,
-                                          num_blocks, H_kv, D, 1.f, 1.f);
+                                          num_blocks, H_kv, D, bs, 1.f, 1.f);
   return launch_cache_write<BF16, FP8>(st, k_new, v_new, slot_mapping, n, k_cache, v_cache,
-                                       num_blocks, H_kv, D, plan.k_inv, plan.v_inv);
+                                       num_blocks, H_kv, D, bs, plan.k_inv, plan.v_inv);
 }
 
 namespace pa {

@@ -16,8 +16,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kBlock = 16;  // tokens per block of the cache write and fused paths; decode and
-                             // prefill also take 8- and 32-token blocks (templated on the size)
+constexpr int kBlock = 16;  // tokens per block of the staged and fused paths; decode, prefill
+                             // and the cache write also take 8- and 32-token blocks (templated)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Storage tags: the element type of a buffer as the kernels see it.

@@ -286,3 +286,70 @@ def test_block_sizes_8_and_32(bs, cache_dt):
     got = codecs.decode(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
     err = assert_close(got, ref, cache_dt, f"bs={bs} {cache_dt}")
     say(f"    max|d| = {err:.3g}")
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("new_dt,cache_dt,d", [("f32", "f32", 64), ("bf16", "bf16", 128),
+                                               ("bf16", "fp8", 128)])
+def test_cache_write_block_sizes_8_and_32(bs, new_dt, cache_dt, d):
+    """pa_cache_write into caches of 8- and 32-token blocks: slots from the C
+    allocator with that block size (equal to the oracle allocator's), cache
+    bytes bit-exact against the oracle's scatter (fp8: quantised with the
+    per-tensor scales), every other byte of the cache left as it was."""
+    from oracle import allocator as oa
+    from oracle import cache as oc
+    import paged_kv_cache_host_amd._pa as pa
+    rng = np.random.default_rng(2500 + bs + d + len(cache_dt))
+    lengths = [1, 7, 8, 9, 31, 33, 100, 257]
+    h_kv = 2
+    nb = sum(-(-L // bs) for L in lengths) + 5
+    order = rng.permutation(nb).astype(np.int32)
+    st_, pool = pa.pa_pool_create(nb, bs, order)
+    assert st_ == pa.PA_OK
+    try:
+        slots = []
+        for s, L in enumerate(lengths):
+            assert pa.pa_seq_create(pool, s, L) == pa.PA_OK
+            slots.append(np.asarray(pa.pa_seq_slots(pool, s, 0, L)[1], dtype=np.int64))
+    finally:
+        pa.pa_pool_destroy(pool)
+    slots = np.concatenate(slots)
+    opool = oa.BlockPool(nb, bs, order.tolist())
+    for s, L in enumerate(lengths):
+        assert opool.seq_create(s, L) == oa.OK
+    assert np.array_equal(np.concatenate([opool.slots(s, 0, L) for s, L in enumerate(lengths)]),
+                          slots)
+    n = len(slots)
+    k_raw = workloads.normal_raw(rng, (n, h_kv, d), new_dt)
+    v_raw = workloads.normal_raw(rng, (n, h_kv, d), new_dt)
+    ks, vs = (0.05, 0.03) if cache_dt == "fp8" else (1.0, 1.0)
+    okc, ovc = oc.new_cache(nb, h_kv, bs, d, cache_dt)
+    oc.cache_write(okc, ovc, k_raw, v_raw, slots, new_dt, cache_dt, ks, vs)
+    x = 16 // {"f32": 4, "bf16": 2, "fp8": 1}[cache_dt]
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[cache_dt]
+    raw_np = {"f32": np.int32, "bf16": np.int16, "fp8": np.uint8}[cache_dt]
+    raw_t = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8}[cache_dt]
+    # the cache starts as a recognisable byte pattern, so stray writes show
+    pattern = 0x3C if cache_dt == "fp8" else (0x3C3C if cache_dt == "bf16" else 0x3C3C3C3C)
+    kc = torch.full(okc.shape, pattern, dtype=raw_t, device=DEV).view(tdt)
+    vc = torch.full(ovc.shape, pattern, dtype=raw_t, device=DEV).view(tdt)
+
+    def dev_raw(a):
+        if new_dt == "f32":
+            return torch.from_numpy(a.view(np.float32)).to(DEV)
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    say(f"[cache_write bs={bs}] {new_dt}->{cache_dt} d={d} n={n} pool={nb}")
+    assert pa.pa_cache_write(None, dev_raw(k_raw), dev_raw(v_raw),
+                             torch.from_numpy(slots.astype(np.int32)).to(DEV), kc, vc, nb, h_kv,
+                             d, bs=bs, k_scale=ks, v_scale=vs) == pa.PA_OK
+    torch.cuda.synchronize()
+    got_k = kc.view(raw_t).cpu().numpy().view(okc.dtype)
+    got_v = vc.view(raw_t).cpu().numpy().view(ovc.dtype)
+    fill = np.array([pattern], dtype=raw_np).view(okc.dtype)[0]
+    held = np.zeros(nb * bs, dtype=bool)
+    held[slots] = True
+    k_mask = held.reshape(nb, 1, 1, bs, 1).repeat(h_kv, 1).repeat(d // x, 2).repeat(x, 4)
+    v_mask = held.reshape(nb, 1, 1, bs).repeat(h_kv, 1).repeat(d, 2)
+    assert np.array_equal(got_k[k_mask], okc[k_mask])
+    assert np.array_equal(got_v[v_mask], ovc[v_mask])
+    assert np.all(got_k[~k_mask] == fill) and np.all(got_v[~v_mask] == fill)
